@@ -1,0 +1,317 @@
+"""CPU oracle for the FLASH gated attention unit with mixed chunk attention.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain float64 statement of
+what the layer computes.  Only the test suite, the package's smoke check and the
+benchmark's CPU-baseline leg may import it.  It shares no code with the HIP
+library: no kernels, headers, helpers or constants, and it imports nothing from
+the package.
+
+Sources ("Transformer Quality in Linear Time", Hua, Dai, Liu, Le, and two
+summaries of it; Su Jianlin's blog post "FLASH: Possibly the Most Interesting
+Efficient Transformer Design in Recent Times"):
+
+* GAU output O = (U * (A V)) W_o with U, V = SiLU(X W_u), SiLU(X W_v):
+  blog, "Gated Attention" (GLU and GAU equations); paper summary (wikillm),
+  "Method", eq. 1-3.
+* Z = SiLU(X W_z) and the four per-dimension scale+offset heads:
+  blog, "Weak Attention" (the relu^2 attention equation); wikillm, "Method",
+  "Mixed chunk attention"; papercache, section 3.2 "Preparation".
+* Intra-chunk attention relu^2(Q K^T + b) V with a causal lower-triangular mask:
+  blog, "Mixed Chunking" (the V_quad equation); wikillm, "Method" step 1 and the
+  FLASH block pseudocode (Code 8 rewrite).
+* Inter-chunk linear attention, a plain sum over all chunks (non-causal, eq. 7)
+  or over strictly earlier chunks (causal, eq. 8): wikillm, "Method" steps 2-3;
+  blog, "Mixed Chunking".
+* O_g = [U_g * (V_quad_g + V_lin_g)] W_o: wikillm, "Method" step 4; blog,
+  "Mixed Chunking" (final equation).
+* Relative-position bias as a Toeplitz matrix of a 2n-1 vector:
+  papercache, appendix D, Code 4 (the n < 512 branch).
+
+Readings where the pages are silent or disagree (each is also listed in the
+design notes):
+
+* Scaling.  The equations put no factor on Q K^T or on the chunk summaries; the
+  listing divides Q K^T by C and K_lin^T V by C.  Both are parameters here:
+  ``quad_scale`` multiplies Q K^T before the bias is added (inside relu^2), and
+  ``lin_scale`` multiplies each chunk summary K_lin^T V.  The listing's reading
+  is quad_scale = lin_scale = 1/C.
+* Bias index: b[i, j] = w[C - 1 + j - i] (key position minus query position),
+  obtained by carrying out Code 4's pad / tile / slice / reshape / slice steps.
+* The causal mask keeps j <= i (diagonal included) and is applied after relu^2.
+* SiLU on U, V and Z.  No RoPE, no dense-layer biases, no segment masks.
+* Non-causal: every chunk (its own included) feeds the linear term.
+
+parity pinned: every function here is checked in tests/test_oracle.py against
+brute force, closed forms or invariants that do not reuse its code.
+"""
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# elementwise pieces
+# --------------------------------------------------------------------------
+
+def silu(x):
+    """SiLU / Swish, x * sigmoid(x), in float64.
+
+    Blog, "Gated Attention": the paper applies Swish (SiLU) to both U and V;
+    wikillm, "Paper vs code" (Activation): Code 6 and Code 8 apply SiLU to U, V
+    and Z.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def scale_offset(z, gamma, beta):
+    """Per-dimension affine head Z * gamma + beta (like LayerNorm's gamma, beta).
+
+    Blog, "Weak Attention" (Q and K are simple affine transforms of Z);
+    papercache section 2 (per-dimension scale and offset).
+    """
+    return np.asarray(z, np.float64) * np.asarray(gamma, np.float64) + np.asarray(beta, np.float64)
+
+
+def relu_squared(x):
+    """relu(x)**2, the attention activation (blog, "Weak Attention"; eq. 5)."""
+    r = np.maximum(np.asarray(x, np.float64), 0.0)
+    return r * r
+
+
+def toeplitz_bias(w, n):
+    """n x n relative-position bias built from a learned 2n-1 vector.
+
+    papercache, appendix D, Code 4 (n < 512 branch).  Carrying out that
+    listing's steps (pad by n zeros, tile n times, drop the last n, reshape to
+    n x (3n-2), keep the middle n columns) gives b[i, j] = w[n - 1 + j - i].
+    """
+    w = np.asarray(w, dtype=np.float64)
+    if w.shape != (2 * n - 1,):
+        raise ValueError("relative-position vector must have length 2n-1")
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    return w[n - 1 + j - i]
+
+
+def causal_mask(n):
+    """Lower-triangular 0/1 mask, diagonal included (wikillm, Code 8 rewrite)."""
+    return np.tril(np.ones((n, n), dtype=np.float64))
+
+
+# --------------------------------------------------------------------------
+# the layer, chunked form (the steps in the order of the FLASH block)
+# --------------------------------------------------------------------------
+
+def _as64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def projections(X, W_u, W_v, W_z):
+    """U, V, Z = SiLU(X W_u), SiLU(X W_v), SiLU(X W_z).
+
+    One dense layer of width 2e+s followed by SiLU, split into U, V and the
+    shared base Z (wikillm, FLASH block pseudocode; blog, "Gated Attention").
+    Weights are in the pages' orientation: W_u, W_v are d x e, W_z is d x s.
+    """
+    X = _as64(X)
+    H = X @ np.concatenate([_as64(W_u), _as64(W_v), _as64(W_z)], axis=1)
+    e = np.shape(W_u)[1]
+    return silu(H[..., :e]), silu(H[..., e:2 * e]), silu(H[..., 2 * e:])
+
+
+def heads(Z, gamma, beta):
+    """The four heads Q_quad, K_quad, Q_lin, K_lin from Z.
+
+    gamma, beta have shape (4, s) in that order (wikillm, "Mixed chunk
+    attention": four heads are derived from Z; papercache 3.2 "Preparation").
+    """
+    gamma = _as64(gamma)
+    beta = _as64(beta)
+    return tuple(scale_offset(Z, gamma[h], beta[h]) for h in range(4))
+
+
+def flash_forward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
+                  quad_scale=None, lin_scale=None, return_intermediates=False):
+    """Forward pass of one FLASH layer (GAU with mixed chunk attention).
+
+    X: (B, T, d).  W_u, W_v: (d, e).  W_z: (d, s).  W_o: (e, d).
+    gamma, beta: (4, s).  relpos: (2C-1,).  T must be a multiple of C.
+    quad_scale / lin_scale default to 1/C (the listing's reading).
+
+    Steps, in the order of the FLASH block (wikillm pseudocode; blog "Mixed
+    Chunking"; papercache 3.2):
+      1. U, V, Z from one SiLU projection; four scale+offset heads from Z.
+      2. Split the sequence into G = T / C non-overlapping chunks.
+      3. Per chunk: kernel = relu^2(Q_quad K_quad^T * quad_scale + bias),
+         lower-triangular masked when causal; quad = kernel @ V.
+      4. Per chunk summary S_g = lin_scale * K_lin_g^T V_g  (s x e).
+      5. Causal: P_g = sum_{h<g} S_h (exclusive prefix, eq. 8); otherwise
+         P_g = sum over all h (eq. 7).
+      6. lin = Q_lin_g P_g;  out = U * (quad + lin);  O = out @ W_o.
+    """
+    X = _as64(X)
+    B, T, d = X.shape
+    if T % C != 0:
+        raise ValueError("T must be a multiple of C")
+    G = T // C
+    if quad_scale is None:
+        quad_scale = 1.0 / C
+    if lin_scale is None:
+        lin_scale = 1.0 / C
+
+    U, V, Z = projections(X, W_u, W_v, W_z)
+    e = U.shape[-1]
+    s = Z.shape[-1]
+    Qq, Kq, Ql, Kl = heads(Z, gamma, beta)
+
+    def chunks(a):
+        return a.reshape(B, G, C, a.shape[-1])
+
+    Ug, Vg, Qqg, Kqg, Qlg, Klg = map(chunks, (U, V, Qq, Kq, Ql, Kl))
+
+    # step 3: local squared-ReLU attention inside each chunk
+    scores = (Qqg @ Kqg.swapaxes(-1, -2)) * quad_scale + toeplitz_bias(relpos, C)
+    kernel = relu_squared(scores)
+    if causal:
+        kernel = kernel * causal_mask(C)
+    quad = kernel @ Vg
+
+    # step 4: one s x e summary per chunk
+    S = (Klg.swapaxes(-1, -2) @ Vg) * lin_scale
+
+    # step 5: chunk-level sum, exclusive prefix when causal
+    if causal:
+        incl = np.cumsum(S, axis=1)
+        P = np.concatenate([np.zeros_like(S[:, :1]), incl[:, :-1]], axis=1)
+    else:
+        P = np.broadcast_to(S.sum(axis=1, keepdims=True), S.shape)
+
+    # step 6: linear term, gate, output projection
+    lin = Qlg @ P
+    Y = Ug * (quad + lin)
+    O = (Y.reshape(B, T, e)) @ _as64(W_o)
+    if not return_intermediates:
+        return O
+    flat = lambda a: a.reshape(B, T, a.shape[-1])
+    return O, {
+        "U": U, "V": V, "Z": Z, "Q_quad": Qq, "K_quad": Kq, "Q_lin": Ql, "K_lin": Kl,
+        "quad": flat(quad), "S": S, "P": np.array(P), "lin": flat(lin), "Y": flat(Y),
+        "kernel": kernel,
+    }
+
+
+# --------------------------------------------------------------------------
+# the same layer as one T x T operator, built token by token (tiny T only)
+# --------------------------------------------------------------------------
+
+def flash_forward_bruteforce(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
+                             quad_scale=None, lin_scale=None):
+    """The layer as O = (U * (A V)) W_o with the full T x T matrix A.
+
+    A per-token double loop builds A[t, tau] (blog, "Gated Attention" GAU
+    equation; "Mixed Chunking" notes that the chunked global part is exactly
+    linear attention on the full matrices):
+      * same chunk (and tau <= t when causal):
+          relu^2(q_quad_t . k_quad_tau * quad_scale + w[C-1 + (tau mod C) - (t mod C)])
+      * plus q_lin_t . k_lin_tau * lin_scale when chunk(tau) < chunk(t)
+        (causal), or for every tau (non-causal, own chunk included).
+    Every product is written out per token; nothing is shared with
+    ``flash_forward`` beyond the SiLU definition.  Pure Python loops: keep
+    T small.
+    """
+    X = _as64(X)
+    B, T, d = X.shape
+    if T % C != 0:
+        raise ValueError("T must be a multiple of C")
+    if quad_scale is None:
+        quad_scale = 1.0 / C
+    if lin_scale is None:
+        lin_scale = 1.0 / C
+    W_u, W_v, W_z, W_o = map(_as64, (W_u, W_v, W_z, W_o))
+    gamma, beta, w = _as64(gamma), _as64(beta), _as64(relpos)
+    e = W_u.shape[1]
+    out = np.zeros((B, T, d))
+    for b in range(B):
+        u = np.zeros((T, e)); v = np.zeros((T, e))
+        qq = [None] * T; kq = [None] * T; ql = [None] * T; kl = [None] * T
+        for t in range(T):
+            x = X[b, t]
+            u[t] = silu(x @ W_u)
+            v[t] = silu(x @ W_v)
+            z = silu(x @ W_z)
+            qq[t] = z * gamma[0] + beta[0]
+            kq[t] = z * gamma[1] + beta[1]
+            ql[t] = z * gamma[2] + beta[2]
+            kl[t] = z * gamma[3] + beta[3]
+        A = np.zeros((T, T))
+        for t in range(T):
+            for tau in range(T):
+                a = 0.0
+                same = (t // C) == (tau // C)
+                if same and (tau <= t or not causal):
+                    sc = float(np.dot(qq[t], kq[tau])) * quad_scale + w[C - 1 + (tau % C) - (t % C)]
+                    a += max(sc, 0.0) ** 2
+                if (not causal) or (tau // C) < (t // C):
+                    a += float(np.dot(ql[t], kl[tau])) * lin_scale
+                A[t, tau] = a
+        out[b] = (u * (A @ v)) @ W_o
+    return out
+
+
+# --------------------------------------------------------------------------
+# references used by the invariant tests and by the stack configuration
+# --------------------------------------------------------------------------
+
+def glu(X, W_u, W_v, W_o):
+    """GLU feed-forward O = (SiLU(X W_u) * SiLU(X W_v)) W_o.
+
+    Blog, "Gated Attention" (GLU equation); the GAU reduces to it when A = I.
+    """
+    X = _as64(X)
+    return (silu(X @ _as64(W_u)) * silu(X @ _as64(W_v))) @ _as64(W_o)
+
+
+def linear_attention_recurrence(Q, K, V, scale):
+    """Causal token-level linear attention through the running cache
+    M_t = M_{t-1} + k_t v_t^T, output q_t M_{t-1} (strictly earlier tokens).
+
+    papercache 3.1 (linear attention, the incremental form M_t).  Used to pin
+    the chunked form at C = 1, where every chunk is one token.
+    Q, K: (T, s); V: (T, e).
+    """
+    Q, K, V = _as64(Q), _as64(K), _as64(V)
+    T, s = Q.shape
+    e = V.shape[1]
+    M = np.zeros((s, e))
+    out = np.zeros((T, e))
+    for t in range(T):
+        out[t] = Q[t] @ M
+        M = M + scale * np.outer(K[t], V[t])
+    return out
+
+
+def rms_norm(x, eps=1e-6):
+    """Pre-norm for the layer stack: x / sqrt(mean(x^2) + eps) over the last axis.
+
+    The listings put a norm before each block and add the shortcut after it
+    (wikillm, gau_block / flash_block pseudocode); the norm's body (Code 5) is
+    missing from the pages, so this is ScaleNorm with its gain fixed at sqrt(d),
+    which is an RMS norm.
+    """
+    x = _as64(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def flash_stack_forward(X, layers, C, causal, quad_scale=None, lin_scale=None):
+    """A stack of FLASH layers with pre-norm and residual adds:
+    x <- x + flash_forward(rms_norm(x), layer weights).
+
+    ``layers`` is a list of dicts with keys W_u, W_v, W_z, W_o, gamma, beta,
+    relpos (pages' orientation, as for flash_forward).
+    """
+    x = _as64(X).copy()
+    for L in layers:
+        x = x + flash_forward(rms_norm(x), L["W_u"], L["W_v"], L["W_z"], L["W_o"],
+                              L["gamma"], L["beta"], L["relpos"], C, causal,
+                              quad_scale, lin_scale)
+    return x

@@ -1,0 +1,275 @@
+"""Pins for the CPU oracle: brute force, closed forms, invariants and the
+hand-worked Code 4 fixture.  CPU only."""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import gau_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tiny(B, T, d, e, s, C, seed, beta_scale=0.3, w_scale=0.5):
+    rng = np.random.default_rng(seed)
+    return dict(
+        X=rng.standard_normal((B, T, d)),
+        W_u=rng.standard_normal((d, e)) / np.sqrt(d),
+        W_v=rng.standard_normal((d, e)) / np.sqrt(d),
+        W_z=rng.standard_normal((d, s)) / np.sqrt(d),
+        W_o=rng.standard_normal((e, d)) / np.sqrt(e),
+        gamma=1.0 + 0.5 * rng.standard_normal((4, s)),
+        beta=beta_scale * rng.standard_normal((4, s)),
+        relpos=w_scale * rng.standard_normal(2 * C - 1),
+    )
+
+
+def _run(fn, p, C, causal, **kw):
+    return fn(p["X"], p["W_u"], p["W_v"], p["W_z"], p["W_o"], p["gamma"], p["beta"],
+              p["relpos"], C, causal, **kw)
+
+
+# ---------------------------------------------------------------- Code 4
+
+def _read_golden_toeplitz():
+    mats, cur, n = {}, None, None
+    with open(os.path.join(GOLDEN, "toeplitz_code4.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("n="):
+                n = int(line[2:])
+                cur = mats.setdefault(n, [])
+            else:
+                cur.append([int(v) for v in line.split()])
+    return {k: np.array(v) for k, v in mats.items()}
+
+
+def test_toeplitz_matches_hand_worked_code4():
+    for n, idx in _read_golden_toeplitz().items():
+        w = np.arange(2 * n - 1, dtype=np.float64) * 10.0 + 1.0   # distinct entries
+        np.testing.assert_array_equal(orc.toeplitz_bias(w, n), w[idx])
+
+
+def _code4_steps(w, n):
+    """Code 4's n < 512 branch carried out with numpy array operations."""
+    t = np.pad(w, (0, n))                 # pad(w, [[0, n]])
+    t = np.tile(t, n)                     # tile(t, [n])
+    t = t[:-n]                            # t[..., :-n]
+    t = t.reshape(n, 3 * n - 2)           # reshape(t, [n, 3n-2])
+    r = (2 * n - 1) // 2
+    return t[:, r:t.shape[1] - r]         # t[..., r:-r]
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 7, 64, 256])
+def test_toeplitz_matches_code4_steps(n):
+    w = np.random.default_rng(n).standard_normal(2 * n - 1)
+    np.testing.assert_array_equal(orc.toeplitz_bias(w, n), _code4_steps(w, n))
+
+
+# ---------------------------------------------------------------- elementwise
+
+def test_silu_fixture_values():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "silu_values.txt"))
+            if l.strip() and not l.startswith("#")]
+    for x, y in rows:
+        assert orc.silu(float(x)) == pytest.approx(float(y), rel=1e-15, abs=1e-300)
+
+
+def test_silu_odd_part_identity():
+    x = np.linspace(-30, 30, 1001)
+    np.testing.assert_allclose(orc.silu(x) - orc.silu(-x), x, rtol=0, atol=1e-13)
+    assert orc.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+
+
+def test_relu_squared_and_mask():
+    np.testing.assert_array_equal(orc.relu_squared(np.array([-2.0, 0.0, 3.0])), [0.0, 0.0, 9.0])
+    m = orc.causal_mask(3)
+    np.testing.assert_array_equal(m, [[1, 0, 0], [1, 1, 0], [1, 1, 1]])
+
+
+def test_rms_norm_closed_form():
+    x = np.array([[3.0, 4.0]])
+    np.testing.assert_allclose(orc.rms_norm(x, eps=0.0), x / math.sqrt(12.5), rtol=1e-15)
+    y = orc.rms_norm(np.random.default_rng(0).standard_normal((5, 64)), eps=0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("B,T,C", [(2, 12, 4), (1, 8, 1), (1, 8, 8), (1, 9, 3), (2, 10, 5)])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("scales", [(None, None), (1.0, 1.0), (0.7, 1.9)])
+def test_chunked_equals_bruteforce(B, T, C, causal, scales):
+    p = _tiny(B, T, d=5, e=6, s=4, C=C, seed=B * 100 + T * 10 + C)
+    qs, ls = scales
+    got = _run(orc.flash_forward, p, C, causal, quad_scale=qs, lin_scale=ls)
+    ref = _run(orc.flash_forward_bruteforce, p, C, causal, quad_scale=qs, lin_scale=ls)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_bruteforce_sees_clipping_and_bias():
+    """The random tiny cases must exercise relu's clipping and the bias
+    direction, or the brute-force comparison would not pin them."""
+    p = _tiny(1, 12, 5, 6, 4, 4, seed=3)
+    _, im = _run(orc.flash_forward, p, 4, True, return_intermediates=True)
+    Qq = im["Q_quad"].reshape(1, 3, 4, 4)
+    Kq = im["K_quad"].reshape(1, 3, 4, 4)
+    sc = (Qq @ Kq.swapaxes(-1, -2)) / 4 + orc.toeplitz_bias(p["relpos"], 4)
+    low = sc[..., np.tril_indices(4)[0], np.tril_indices(4)[1]]
+    assert (low < 0).any() and (low > 0).any()
+    # a flipped bias index (w[C-1+i-j]) gives a different answer
+    flipped = dict(p, relpos=p["relpos"][::-1].copy())
+    a = _run(orc.flash_forward, p, 4, True)
+    b = _run(orc.flash_forward, flipped, 4, True)
+    assert np.max(np.abs(a - b)) > 1e-6
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_identity_attention_reduces_to_glu(causal):
+    """gamma = beta = 0 for all heads and w = one-hot at C-1 make
+    relu^2(bias) the identity and the linear term zero, so the GAU is a GLU
+    (blog, "Gated Attention": A = I reduces the GAU to the GLU)."""
+    C = 4
+    p = _tiny(2, 12, 5, 6, 4, C, seed=7)
+    p["gamma"][:] = 0.0
+    p["beta"][:] = 0.0
+    p["relpos"][:] = 0.0
+    p["relpos"][C - 1] = 1.0
+    got = _run(orc.flash_forward, p, C, causal, quad_scale=0.3, lin_scale=0.9)
+    ref = orc.glu(p["X"], p["W_u"], p["W_v"], p["W_o"])
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-14)
+
+
+def test_full_chunk_causal_has_no_linear_term():
+    """C = T: one chunk, so the exclusive prefix is zero and FLASH is the
+    quadratic GAU (papercache C.3: chunk size equal to the context length)."""
+    p = _tiny(2, 8, 5, 6, 4, 8, seed=11)
+    O, im = _run(orc.flash_forward, p, 8, True, return_intermediates=True)
+    assert np.all(im["P"] == 0.0) and np.all(im["lin"] == 0.0)
+    # quadratic GAU over the whole sequence, from the GAU equation directly
+    U, V, _ = orc.projections(p["X"], p["W_u"], p["W_v"], p["W_z"])
+    A = im["kernel"][:, 0]
+    np.testing.assert_allclose(O, (U * (A @ V)) @ p["W_o"], rtol=1e-13, atol=1e-14)
+
+
+def test_unit_chunks_match_token_recurrence():
+    """C = 1: the linear part is token-level causal linear attention through
+    the running cache M_t (papercache 3.1 and C.3)."""
+    T = 9
+    p = _tiny(1, T, 5, 6, 4, 1, seed=13)
+    _, im = _run(orc.flash_forward, p, 1, True, quad_scale=0.8, lin_scale=0.6,
+                 return_intermediates=True)
+    ref_lin = orc.linear_attention_recurrence(im["Q_lin"][0], im["K_lin"][0], im["V"][0], 0.6)
+    np.testing.assert_allclose(im["lin"][0], ref_lin, rtol=1e-12, atol=1e-13)
+    diag = np.sum(im["Q_quad"][0] * im["K_quad"][0], axis=-1) * 0.8 + p["relpos"][0]
+    np.testing.assert_allclose(im["quad"][0], (np.maximum(diag, 0) ** 2)[:, None] * im["V"][0],
+                               rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("C", [1, 2, 4, 8])
+def test_noncausal_linear_term_is_full_linear_attention(C):
+    """Eq. 7 equals linear attention on the full matrices, whatever C is
+    (blog, "Mixed Chunking")."""
+    p = _tiny(2, 8, 5, 6, 4, C, seed=17)
+    _, im = _run(orc.flash_forward, p, C, False, lin_scale=0.25, return_intermediates=True)
+    full = im["Q_lin"] @ (im["K_lin"].swapaxes(-1, -2) @ im["V"]) * 0.25
+    np.testing.assert_allclose(im["lin"], full, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("t", [0, 3, 4, 7, 10])
+def test_causal_output_ignores_future_tokens_bitwise(t):
+    p = _tiny(2, 12, 5, 6, 4, 4, seed=19)
+    a = _run(orc.flash_forward, p, 4, True)
+    q = dict(p)
+    q["X"] = p["X"].copy()
+    q["X"][:, t + 1:] += np.random.default_rng(t).standard_normal(q["X"][:, t + 1:].shape)
+    b = _run(orc.flash_forward, q, 4, True)
+    np.testing.assert_array_equal(a[:, :t + 1], b[:, :t + 1])
+    if t + 1 < 12:
+        assert np.max(np.abs(a[:, t + 1:] - b[:, t + 1:])) > 0
+
+
+def test_noncausal_output_sees_future_tokens():
+    p = _tiny(1, 12, 5, 6, 4, 4, seed=23)
+    a = _run(orc.flash_forward, p, 4, False)
+    q = dict(p)
+    q["X"] = p["X"].copy()
+    q["X"][:, 11] += 1.0
+    b = _run(orc.flash_forward, q, 4, False)
+    assert np.max(np.abs(a[:, 0] - b[:, 0])) > 0
+
+
+def test_batch_rows_are_independent():
+    p = _tiny(3, 8, 5, 6, 4, 4, seed=29)
+    full = _run(orc.flash_forward, p, 4, True)
+    for b in range(3):
+        q = dict(p, X=p["X"][b:b + 1])
+        np.testing.assert_allclose(_run(orc.flash_forward, q, 4, True)[0], full[b],
+                                   rtol=1e-13, atol=1e-14)
+
+
+def test_scale_placement():
+    """quad_scale multiplies Q K^T inside relu^2: with a zero bias the local
+    term scales with its square; lin_scale multiplies the linear term once."""
+    p = _tiny(1, 8, 5, 6, 4, 4, seed=31)
+    p["relpos"][:] = 0.0
+    _, a = _run(orc.flash_forward, p, 4, True, quad_scale=1.0, lin_scale=1.0,
+                return_intermediates=True)
+    _, b = _run(orc.flash_forward, p, 4, True, quad_scale=3.0, lin_scale=5.0,
+                return_intermediates=True)
+    np.testing.assert_allclose(b["quad"], 9.0 * a["quad"], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(b["lin"], 5.0 * a["lin"], rtol=1e-13, atol=1e-14)
+    assert np.max(np.abs(a["quad"])) > 0 and np.max(np.abs(a["lin"])) > 0
+
+
+def test_local_only_and_global_only_isolation():
+    """LocalOnly / GlobalOnly ablations (wikillm, "Ablation variants"): zero
+    Q_lin removes the global part; zero Q_quad with a non-positive bias
+    removes the local part."""
+    C = 4
+    p = _tiny(1, 12, 5, 6, 4, C, seed=37)
+    loc = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in p.items()}
+    loc["gamma"][2] = 0.0
+    loc["beta"][2] = 0.0
+    O, im = _run(orc.flash_forward, loc, C, True, return_intermediates=True)
+    assert np.all(im["lin"] == 0.0)
+    np.testing.assert_allclose(O, (im["U"] * im["quad"]) @ p["W_o"], rtol=1e-13, atol=1e-14)
+    glo = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in p.items()}
+    glo["gamma"][0] = 0.0
+    glo["beta"][0] = 0.0
+    glo["relpos"] = -np.abs(glo["relpos"])
+    O, im = _run(orc.flash_forward, glo, C, True, return_intermediates=True)
+    assert np.all(im["quad"] == 0.0)
+    np.testing.assert_allclose(O, (im["U"] * im["lin"]) @ p["W_o"], rtol=1e-13, atol=1e-14)
+
+
+def test_exclusive_prefix_order():
+    """P_0 = 0 and P_g - P_{g-1} = S_{g-1} (eq. 8 sums h = 1..g-1)."""
+    p = _tiny(1, 16, 5, 6, 4, 4, seed=41)
+    _, im = _run(orc.flash_forward, p, 4, True, return_intermediates=True)
+    P, S = im["P"], im["S"]
+    assert np.all(P[:, 0] == 0)
+    np.testing.assert_allclose(P[:, 1:] - P[:, :-1], S[:, :-1], rtol=1e-12, atol=1e-14)
+
+
+def test_stack_first_layer_matches_single_layer():
+    C = 4
+    layers = [{k: v for k, v in _tiny(1, 8, 6, 8, 4, C, seed=50 + l).items() if k != "X"}
+              for l in range(2)]
+    X = np.random.default_rng(5).standard_normal((1, 8, 6))
+    out1 = orc.flash_stack_forward(X, layers[:1], C, True)
+    L = layers[0]
+    ref = X + orc.flash_forward(orc.rms_norm(X), L["W_u"], L["W_v"], L["W_z"], L["W_o"],
+                                L["gamma"], L["beta"], L["relpos"], C, True)
+    np.testing.assert_allclose(out1, ref, rtol=1e-14, atol=1e-14)
+    out2 = orc.flash_stack_forward(X, layers, C, True)
+    L = layers[1]
+    ref2 = out1 + orc.flash_forward(orc.rms_norm(out1), L["W_u"], L["W_v"], L["W_z"], L["W_o"],
+                                    L["gamma"], L["beta"], L["relpos"], C, True)
+    np.testing.assert_allclose(out2, ref2, rtol=1e-13, atol=1e-13)
