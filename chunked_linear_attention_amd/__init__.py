@@ -1,0 +1,69 @@
+"""MI355X-native forward pass of the FLASH gated attention unit with mixed
+chunk attention ("Transformer Quality in Linear Time").
+
+The computation lives in libgau.so: hand-written HIP kernels for gfx950 behind
+the C ABI declared in include/gau.h.  This package is the thin Python binding
+(ctypes; PyTorch tensors supply device memory and the HIP stream), the build
+script, and the seeded synthetic input generator.
+"""
+
+import numpy as np
+
+from . import inputs  # noqa: F401
+from ._lib import (  # noqa: F401
+    GAU_BF16, GAU_F32, STAGE_ATTN, STAGE_OUT, STAGE_PROJ, STAGE_SCAN, STAGE_STATE, EXPORTS,
+    GauError, forward, forward_stages, load, make_config, stack_forward, stack_workspace_bytes,
+    status_string, workspace_bytes, workspace_layout,
+)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def device_tensor(a, dtype, device="cuda"):
+    """numpy float32 array -> contiguous device tensor of `dtype` (bf16 values
+    are taken as exact bf16 bit patterns via round-to-nearest-even)."""
+    torch = _torch()
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == torch.bfloat16:
+        bits = inputs.bf16_bits(a).view(np.int16)
+        return torch.from_numpy(bits).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def device_layer(inp, dtype, device="cuda"):
+    """Upload one layer's inputs (numpy, pages' orientation) in the ABI layout:
+    weights output-major (W transposed on the host), scale/offset/relpos fp32."""
+    torch = _torch()
+    out = {}
+    if "X" in inp:
+        out["X"] = device_tensor(inp["X"], dtype, device)
+    for k in ("W_u", "W_v", "W_z", "W_o"):
+        out[k] = device_tensor(np.ascontiguousarray(inp[k].T), dtype, device)
+    out["scale"] = device_tensor(inp["gamma"], torch.float32, device)
+    out["offset"] = device_tensor(inp["beta"], torch.float32, device)
+    out["relpos"] = device_tensor(inp["relpos"], torch.float32, device)
+    return out
+
+
+def gau_forward(X, W_u, W_v, W_z, W_o, scale, offset, relpos, C, causal,
+                quad_scale=None, lin_scale=None, out=None, workspace=None, stream=None):
+    """O = FLASH layer forward of X [B, T, d] (weights output-major).
+
+    Allocates O and the workspace with torch.empty when not given; all
+    arithmetic runs in libgau's kernels on the current (or given) stream.
+    """
+    torch = _torch()
+    B, T, d = X.shape
+    e = W_u.shape[0]
+    s = W_z.shape[0]
+    dt = GAU_BF16 if X.dtype == torch.bfloat16 else GAU_F32
+    cfg = make_config(B, T, d, e, s, C, causal, dt, quad_scale, lin_scale)
+    if out is None:
+        out = torch.empty_like(X)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(cfg), 1), dtype=torch.uint8, device=X.device)
+    forward(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, out, workspace, stream)
+    return out

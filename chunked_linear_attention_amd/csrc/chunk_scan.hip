@@ -1,0 +1,91 @@
+// Chunk-level sum of the linear-attention states.
+//   causal:     P_g = sum_{h<g} S_h  (exclusive prefix, eq. 8: h = 1..g-1)
+//   non-causal: P   = sum_h S_h      (eq. 7, one total per sequence)
+// Pages: wikillm "Method" steps 2-3 and the FLASH block pseudocode
+// (exclusive_cumsum over the chunk axis, or sum); Su's post, "Mixed
+// Chunking" (cumulative-sum form for the decoder).  The chunking reduces the
+// sequential dependency from T token steps to G chunk steps (wikillm
+// "Method" step 4; papercache 3.2.1).
+//
+// Every one of the B * e * s state entries is an independent G-step sum.  A
+// thread owns four consecutive entries (one 16-byte vector) and walks the G
+// chunks in order g = 0..G-1, so each output is a true exclusive prefix summed
+// in a fixed order (never an inclusive sum minus the own term), which keeps the
+// causal outputs independent of later chunks bit for bit.  Sums are fp32; P is
+// stored in the layer's element type, the precision its consumer (an MFMA
+// operand) takes it in.  HBM bound: it reads S once and writes P once.
+#include "gau_device.h"
+#include "gau_launch.h"
+
+namespace gau {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void put4(void* dst, const f32x4_t& v);
+template <>
+__device__ __forceinline__ void put4<float>(void* dst, const f32x4_t& v) {
+    *(f32x4_t*)dst = v;
+}
+template <>
+__device__ __forceinline__ void put4<bf16>(void* dst, const f32x4_t& v) {
+    u32x2_t w;
+    w.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    w.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    *(u32x2_t*)dst = w;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void chunk_scan_kernel(ScanParams p) {
+    const int per_b = p.es / 4;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= per_b * p.B) return;
+    const int b = idx / per_b;
+    const int v = idx - b * per_b;
+    const size_t stride = (size_t)p.es;  // elements between consecutive chunks
+    const f32x4_t* __restrict__ S = (const f32x4_t*)(p.S + (size_t)b * p.G * stride) + v;
+    char* __restrict__ P = (char*)p.P;
+    constexpr int EB = Elem<T>::kBytes;
+    f32x4_t run = {0.f, 0.f, 0.f, 0.f};
+    if (p.causal) {
+        char* out = P + ((size_t)b * p.G * stride + (size_t)v * 4) * EB;
+        int g = 0;
+        for (; g + 4 <= p.G; g += 4) {
+            const f32x4_t s0 = S[(size_t)(g + 0) * (stride / 4)];
+            const f32x4_t s1 = S[(size_t)(g + 1) * (stride / 4)];
+            const f32x4_t s2 = S[(size_t)(g + 2) * (stride / 4)];
+            const f32x4_t s3 = S[(size_t)(g + 3) * (stride / 4)];
+            put4<T>(out + (size_t)(g + 0) * stride * EB, run);
+            run += s0;
+            put4<T>(out + (size_t)(g + 1) * stride * EB, run);
+            run += s1;
+            put4<T>(out + (size_t)(g + 2) * stride * EB, run);
+            run += s2;
+            put4<T>(out + (size_t)(g + 3) * stride * EB, run);
+            run += s3;
+        }
+        for (; g < p.G; ++g) {
+            const f32x4_t s0 = S[(size_t)g * (stride / 4)];
+            put4<T>(out + (size_t)g * stride * EB, run);
+            run += s0;
+        }
+    } else {
+        for (int g = 0; g < p.G; ++g) run += S[(size_t)g * (stride / 4)];
+        put4<T>(P + ((size_t)b * stride + (size_t)v * 4) * EB, run);
+    }
+}
+
+template <typename T>
+hipError_t launch(const ScanParams& p, hipStream_t st) {
+    const long threads = (long)p.B * (p.es / 4);
+    const int blocks = (int)((threads + 255) / 256);
+    hipLaunchKernelGGL(chunk_scan_kernel<T>, dim3(blocks), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_scan(const ScanParams& p, bool bf16_storage, hipStream_t st) {
+    return bf16_storage ? launch<bf16>(p, st) : launch<float>(p, st);
+}
+
+}  // namespace gau

@@ -1,0 +1,83 @@
+// Host-side launch interface between the C ABI (gau_api.hip) and the kernel
+// translation units.  Internal to libgau; not exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gau {
+
+// Fused projection + SiLU + scale/offset heads.
+struct ProjParams {
+    const void* X;      // [M, d]
+    const void* W_u;    // [e, d]  (W_u transposed)
+    const void* W_v;    // [e, d]
+    const void* W_z;    // [s, d]
+    const float* scale;   // [4, s]
+    const float* offset;  // [4, s]
+    void* U;    // [M, e]
+    void* Vt;   // [B, e, T]
+    void* Qq;   // [M, s]
+    void* Kq;   // [M, s]
+    void* Ql;   // [M, s]
+    void* Klt;  // [B, s, T]
+    int M, T, d, e, s;
+};
+
+// Per-chunk state S_g^T = lin_scale * V_g^T K_lin_g, [B, G, e, s] fp32.
+struct StateParams {
+    const void* Vt;   // [B, e, T]
+    const void* Klt;  // [B, s, T]
+    float* S;         // [B, G, e, s]
+    int B, T, e, s, C;
+    float lin_scale;
+};
+
+// Exclusive prefix over chunks (causal) or the total (non-causal).
+struct ScanParams {
+    const float* S;  // [B, G, e, s]
+    void* P;         // [B, G, e, s] causal, [B, 1, e, s] otherwise
+    int B, G, es;    // es = e * s
+    int causal;
+};
+
+// Intra-chunk relu^2 attention + linear term + U gate: Y = U * (quad + lin).
+struct AttnParams {
+    const void* Qq;   // [M, s]
+    const void* Kq;   // [M, s]
+    const void* Ql;   // [M, s]
+    const void* Vt;   // [B, e, T]
+    const void* P;    // [B, G or 1, e, s]
+    const void* U;    // [M, e]
+    const float* relpos;  // [2C-1]
+    void* Y;          // [M, e]
+    int B, T, e, s, C;
+    int causal;
+    float quad_scale;
+};
+
+// Output projection O = Y W_o (optionally O = residual + Y W_o in fp32).
+struct OutParams {
+    const void* Y;     // [M, e]
+    const void* W_o;   // [d, e]  (W_o transposed)
+    void* O;           // [M, d]  element type of the layer, or fp32 when residual
+    const float* residual;  // [M, d] fp32 or nullptr
+    int M, d, e;
+};
+
+// Row RMS normalisation for the layer stack: Xn = bf16(x / sqrt(mean(x^2) + eps)).
+struct NormParams {
+    const float* x;  // [M, d]
+    void* xn;        // [M, d] layer element type
+    int M, d;
+    float eps;
+};
+
+hipError_t launch_proj_gemm(const ProjParams& p, bool bf16_storage, hipStream_t st);
+hipError_t launch_chunk_state(const StateParams& p, bool bf16_storage, hipStream_t st);
+hipError_t launch_chunk_scan(const ScanParams& p, bool bf16_storage, hipStream_t st);
+hipError_t launch_chunk_attn(const AttnParams& p, bool bf16_storage, hipStream_t st);
+hipError_t launch_out_gemm(const OutParams& p, bool bf16_storage, hipStream_t st);
+hipError_t launch_rms_norm(const NormParams& p, bool bf16_storage, hipStream_t st);
+
+}  // namespace gau

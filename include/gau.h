@@ -1,0 +1,195 @@
+/*
+ * gau.h -- C ABI of libgau, the forward pass of the FLASH gated attention unit
+ * (GAU) with mixed chunk attention, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed ("Transformer Quality in Linear Time", Hua, Dai, Liu, Le;
+ * equations as summarised on the wikillm page, section "Method", and in Su
+ * Jianlin's post "FLASH: Possibly the Most Interesting Efficient Transformer
+ * Design in Recent Times", sections "Gated Attention" and "Mixed Chunking"):
+ *
+ *   U = SiLU(X W_u),  V = SiLU(X W_v),  Z = SiLU(X W_z)        (GAU, eq. 1-4)
+ *   Q_quad, K_quad, Q_lin, K_lin = Z * gamma_h + beta_h, h = 0..3
+ *   per chunk g of C tokens (G = T / C chunks):
+ *     V_quad_g = relu^2(quad_scale * Q_quad_g K_quad_g^T + Bias) V_g
+ *                Bias[i][j] = relpos[C-1 + j - i]   (papercache page,
+ *                appendix D, Code 4, branch n < 512); causal: entries with
+ *                key j > query i are zeroed after relu^2
+ *     S_g      = lin_scale * K_lin_g^T V_g                      (s x e)
+ *     P_g      = sum_{h<g} S_h   (causal, eq. 8)
+ *              = sum_{h}   S_h   (non-causal, eq. 7)
+ *     V_lin_g  = Q_lin_g P_g
+ *   O_g = [U_g * (V_quad_g + V_lin_g)] W_o         (display after eq. 8)
+ *
+ * The listing (Code 8 as rewritten on the wikillm page) divides Q K^T by C and
+ * each chunk summary by C; the equations use no factor.  Both factors are
+ * arguments here (gau_config.quad_scale, gau_config.lin_scale); the listing's
+ * reading is quad_scale = lin_scale = 1/C.  No RoPE, no dense-layer biases.
+ *
+ * Conventions for every entry point:
+ *  - Every pointer is caller-owned device memory (HBM of the current HIP
+ *    device) unless stated otherwise.  The library allocates nothing, keeps no
+ *    global state and may be called from several host threads at once.
+ *  - Work is queued on `stream` (a hipStream_t; NULL is the default stream)
+ *    and the call returns without synchronising.
+ *  - Arguments are checked before anything is queued.  A non-OK status means
+ *    nothing was queued and no output was touched, except GAU_ERR_HIP, which
+ *    reports a failed launch (outputs then are unspecified).
+ *  - All pointers must be 16-byte aligned.  Outputs must not alias inputs.
+ *  - Matrix layouts are row-major.  Weight matrices W in R^{in x out} (the
+ *    pages' orientation, X W) are passed output-major: element (i, o) of W at
+ *    offset o * in + i, i.e. an out x in row-major array (W transposed).
+ */
+#ifndef GAU_H
+#define GAU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GAU_OK = 0,
+    GAU_ERR_NULL = 1,       /* a required pointer is NULL                        */
+    GAU_ERR_SHAPE = 2,      /* unsupported shape (see gau_config)                */
+    GAU_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned                  */
+    GAU_ERR_DTYPE = 4,      /* dtype is not GAU_F32 or GAU_BF16                  */
+    GAU_ERR_WORKSPACE = 5,  /* workspace smaller than gau_workspace_bytes()      */
+    GAU_ERR_HIP = 6         /* a kernel launch failed                            */
+} gau_status;
+
+typedef enum {
+    GAU_F32 = 0,   /* fp32 storage, fp32 MFMA arithmetic                         */
+    GAU_BF16 = 1   /* bf16 storage, bf16 MFMA with fp32 accumulation             */
+} gau_dtype;
+
+/*
+ * Layer shape and options.
+ *   B batch, T tokens per sequence, d model width, e expanded width,
+ *   s shared (attention) width, C chunk length; G = T / C.
+ * Supported: B, T >= 0 (B*T == 0 is a no-op); T % C == 0 (the chunking splits
+ *   the sequence into whole chunks, wikillm "Method", papercache 3.2);
+ *   C in {64, 128, 256, 512}; d % 128 == 0; e % 256 == 0; s in {128, 256}.
+ *   Otherwise GAU_ERR_SHAPE.
+ */
+typedef struct {
+    int64_t B, T, d, e, s, C;
+    int32_t causal;      /* 1: lower-triangular in-chunk mask and exclusive chunk
+                            prefix (eq. 8); 0: full in-chunk attention and the
+                            sum over all chunks (eq. 7)                          */
+    int32_t dtype;       /* gau_dtype of X, W_*, O and the stored intermediates  */
+    float quad_scale;    /* multiplies Q_quad K_quad^T before the bias is added  */
+    float lin_scale;     /* multiplies every chunk summary K_lin^T V             */
+} gau_config;
+
+/*
+ * Byte offsets, inside the workspace, of the intermediates gau_forward leaves
+ * there (valid after the stream has reached the end of the call).  "dt" is the
+ * element type selected by gau_config.dtype.
+ *   U       [B*T, e]      dt    SiLU(X W_u)
+ *   Vt      [B, e, T]     dt    SiLU(X W_v), transposed per sequence
+ *   Q_quad  [B*T, s]      dt
+ *   K_quad  [B*T, s]      dt
+ *   Q_lin   [B*T, s]      dt
+ *   K_lin_t [B, s, T]     dt    K_lin transposed per sequence
+ *   S       [B, G, e, s]  fp32  S_g transposed (element (b,g,c,k) = S_g[k][c])
+ *   P       [B, G', e, s] dt    P_g transposed; G' = G if causal, else 1
+ *   Y       [B*T, e]      dt    U * (V_quad + V_lin)
+ *   total   bytes needed (== gau_workspace_bytes)
+ */
+typedef struct {
+    size_t U, Vt, Q_quad, K_quad, Q_lin, K_lin_t, S, P, Y, total;
+} gau_ws_layout;
+
+/* Workspace bytes gau_forward needs for cfg (0 if cfg is invalid). */
+size_t gau_workspace_bytes(const gau_config* cfg);
+
+/* Fills *out with the workspace layout for cfg.  GAU_ERR_NULL / _SHAPE /
+ * _DTYPE as gau_forward. */
+gau_status gau_workspace_layout(const gau_config* cfg, gau_ws_layout* out);
+
+/*
+ * One FLASH layer forward: O = GAU(X).
+ *   X       [B, T, d]   dt   input activations
+ *   W_u     [e, d]      dt   W_u transposed (output-major, see above)
+ *   W_v     [e, d]      dt
+ *   W_z     [s, d]      dt
+ *   W_o     [d, e]      dt   W_o transposed
+ *   scale   [4, s]      fp32 gamma of Q_quad, K_quad, Q_lin, K_lin (in order)
+ *   offset  [4, s]      fp32 beta, same order
+ *   relpos  [2C-1]      fp32 relative-position vector, Bias[i][j] = relpos[C-1+j-i]
+ *   O       [B, T, d]   dt   output
+ *   workspace, workspace_bytes: device scratch of at least gau_workspace_bytes
+ *   stream  hipStream_t (may be NULL)
+ */
+gau_status gau_forward(const gau_config* cfg,
+                       const void* X, const void* W_u, const void* W_v,
+                       const void* W_z, const void* W_o,
+                       const float* scale, const float* offset, const float* relpos,
+                       void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The five kernels gau_forward queues, in order.  gau_forward_stages runs a
+ * contiguous range of them (for stage-wise tests and per-kernel timing); the
+ * stages communicate only through the workspace.
+ *   GAU_STAGE_PROJ   U, Vt, Q_quad, K_quad, Q_lin, K_lin_t from X (SiLU projection
+ *                    and the four scale+offset heads; wikillm "Method", Su's post
+ *                    "Gated Attention" and "Weak Attention")
+ *   GAU_STAGE_STATE  S_g = lin_scale * K_lin_g^T V_g for every chunk (eq. 7-8)
+ *   GAU_STAGE_SCAN   P_g = exclusive prefix over chunks (causal, eq. 8) or total (eq. 7)
+ *   GAU_STAGE_ATTN   Y = U * (relu^2(quad_scale Q_quad K_quad^T + Bias) V + Q_lin P)
+ *                    per chunk (wikillm "Method" steps 1-4; papercache appendix D, Code 4)
+ *   GAU_STAGE_OUT    O = Y W_o
+ * Arguments, checks and status codes as gau_forward (every pointer is
+ * checked, also those the selected stages do not read).  A stage reads the
+ * workspace regions earlier stages wrote, so a range that does not start at
+ * GAU_STAGE_PROJ needs them there already.  first > last or a stage number
+ * outside 0..4 gives GAU_ERR_SHAPE.
+ */
+enum {
+    GAU_STAGE_PROJ = 0,
+    GAU_STAGE_STATE = 1,
+    GAU_STAGE_SCAN = 2,
+    GAU_STAGE_ATTN = 3,
+    GAU_STAGE_OUT = 4
+};
+
+gau_status gau_forward_stages(const gau_config* cfg, int first_stage, int last_stage,
+                              const void* X, const void* W_u, const void* W_v,
+                              const void* W_z, const void* W_o,
+                              const float* scale, const float* offset, const float* relpos,
+                              void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * A stack of n_layers FLASH layers with pre-norm and residual adds, the block
+ * structure of the listings (wikillm, FLASH block pseudocode: norm, block,
+ * add the shortcut):
+ *   for l in 0..n_layers-1:  X <- X + gau_forward(rms_norm(X); layer l)
+ * rms_norm(x) = x / sqrt(mean(x^2) + 1e-6) per token row; the norm's body
+ * (Code 5) is missing from the pages, and this is ScaleNorm with its gain fixed
+ * at sqrt(d).  The normalised activations are stored in cfg->dtype; the
+ * residual stream stays fp32.
+ *   X        [B, T, d] fp32, updated in place
+ *   W_u .. relpos: host arrays of n_layers device pointers, each as for
+ *            gau_forward
+ *   workspace: at least gau_stack_workspace_bytes(cfg) bytes
+ * Every layer uses cfg (quad_scale, lin_scale, causal, dtype).
+ */
+size_t gau_stack_workspace_bytes(const gau_config* cfg);
+
+gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X,
+                             const void* const* W_u, const void* const* W_v,
+                             const void* const* W_z, const void* const* W_o,
+                             const float* const* scale, const float* const* offset,
+                             const float* const* relpos,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* gau_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GAU_H */

@@ -1,0 +1,77 @@
+"""Helpers for the GPU parity tests: run libgau on seeded inputs and read its
+outputs and workspace intermediates back to the host."""
+
+import numpy as np
+import torch
+
+import chunked_linear_attention_amd as g
+from chunked_linear_attention_amd import inputs
+from oracle import gau_oracle as orc
+
+BF16_TOL = 2e-2   # max|err| <= 2e-2 * max|ref|, bf16 storage with fp32 accumulation
+F32_TOL = 1e-4    # max|err| <= 1e-4 * max|ref|, fp32
+
+
+def tol_for(dtype):
+    return BF16_TOL if dtype == "bf16" else F32_TOL
+
+
+def torch_dtype(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def run_layer(inp, B, T, d, e, s, C, causal, dtype, quad_scale=None, lin_scale=None, stream=None):
+    """Forward on the GPU; returns (O as float64 numpy, workspace tensor, cfg, layout)."""
+    tdt = torch_dtype(dtype)
+    dev = g.device_layer(inp, tdt)
+    cfg = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32,
+                        quad_scale, lin_scale)
+    ws = torch.empty(g.workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    O = torch.empty((B, T, d), dtype=tdt, device="cuda")
+    g.forward(cfg, dev["X"], dev["W_u"], dev["W_v"], dev["W_z"], dev["W_o"], dev["scale"],
+              dev["offset"], dev["relpos"], O, ws, stream)
+    torch.cuda.synchronize()
+    return O.float().cpu().numpy().astype(np.float64), ws, cfg, g.workspace_layout(cfg)
+
+
+def ws_array(ws, layout, name, shape, dtype):
+    """A workspace region as a float64 numpy array of `shape`."""
+    n = int(np.prod(shape))
+    if name == "S":
+        tdt, eb = torch.float32, 4
+    else:
+        tdt, eb = torch_dtype(dtype), (2 if dtype == "bf16" else 4)
+    off = layout[name]
+    t = ws[off:off + n * eb].view(tdt).reshape(shape)
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def oracle_layer(inp, C, causal, quad_scale=None, lin_scale=None, intermediates=False):
+    return orc.flash_forward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"],
+                             inp["beta"], inp["relpos"], C, causal, quad_scale, lin_scale,
+                             return_intermediates=intermediates)
+
+
+def rel_err(got, ref):
+    """max|got - ref| / max|ref|."""
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def assert_close(got, ref, tol, what=""):
+    err = rel_err(got, ref)
+    assert err <= tol, f"{what}: max|err|/max|ref| = {err:.3e} > {tol:.1e}"
+    return err
+
+
+def chunk_errors(got, ref, C):
+    """Per-chunk max|err| / max|ref| (diagnostic; not the gate)."""
+    B, T, _ = ref.shape
+    G = T // C
+    e = np.abs(got - ref).reshape(B, G, -1).max(axis=(0, 2))
+    r = np.abs(ref).reshape(B, G, -1).max(axis=(0, 2))
+    return e / np.maximum(r, 1e-300)
+
+
+def make(B, T, d, e, s, C, dtype, seed):
+    """Seeded inputs with the workloads' recipe at a given shape."""
+    return inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=seed, dtype=dtype)

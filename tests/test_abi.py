@@ -1,0 +1,118 @@
+"""Host-side checks of libgau's C ABI: the library loads, exports every symbol
+include/gau.h declares, and rejects bad arguments before touching a GPU.
+CPU only: no call here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_linear_attention_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "gau.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gau_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = g.load()
+    decl = _declared()
+    assert decl, "no declarations found"
+    assert set(decl) == set(g.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def _cfg(**kw):
+    base = dict(B=2, T=512, d=256, e=512, s=128, C=128, causal=True, dtype=g.GAU_BF16)
+    base.update(kw)
+    return g.make_config(**base)
+
+
+def test_workspace_layout_sizes():
+    cfg = _cfg()
+    L = g.workspace_layout(cfg)
+    M, e, s, B, G = 2 * 512, 512, 128, 2, 4
+    assert L["Vt"] - L["U"] >= M * e * 2
+    assert L["P"] - L["S"] >= B * G * e * s * 4
+    assert L["Y"] - L["P"] >= B * G * e * s * 2
+    assert L["total"] == g.workspace_bytes(cfg)
+    for k, v in L.items():
+        assert v % 256 == 0, k
+    nc = g.workspace_layout(_cfg(causal=False))
+    assert nc["Y"] - nc["P"] < L["Y"] - L["P"]          # one total per sequence
+    f32 = g.workspace_layout(_cfg(dtype=g.GAU_F32))
+    assert f32["total"] > L["total"]
+
+
+@pytest.mark.parametrize("bad", [dict(T=500), dict(C=32), dict(C=96), dict(d=200), dict(e=384),
+                                 dict(s=64), dict(s=192), dict(B=-1)])
+def test_bad_shapes_rejected(bad):
+    cfg = _cfg(**bad)
+    assert g.workspace_bytes(cfg) == 0
+    with pytest.raises(g.GauError) as ei:
+        g.workspace_layout(cfg)
+    assert ei.value.status == 2
+
+
+def test_bad_dtype_rejected():
+    cfg = _cfg()
+    cfg.dtype = 7
+    with pytest.raises(g.GauError) as ei:
+        g.workspace_layout(cfg)
+    assert ei.value.status == 4
+
+
+def _call_forward(cfg, ptrs, ws_bytes):
+    lib = g.load()
+    return lib.gau_forward(ctypes.byref(cfg), *[ctypes.c_void_p(p) if p else None for p in ptrs],
+                           ctypes.c_size_t(ws_bytes), None)
+
+
+def test_forward_argument_checks_without_gpu():
+    cfg = _cfg()
+    good = [4096 * (i + 1) for i in range(10)]       # fake, aligned, never dereferenced
+    ws = g.workspace_bytes(cfg)
+    assert _call_forward(cfg, [None] + good[1:], ws) == 1           # NULL X
+    assert _call_forward(cfg, good[:8] + [None, good[9]], ws) == 1  # NULL O
+    bad = list(good)
+    bad[3] += 8
+    assert _call_forward(cfg, bad, ws) == 3                         # misaligned W_z
+    assert _call_forward(cfg, good, ws - 1) == 5                    # workspace too small
+    assert _call_forward(_cfg(T=500), good, ws) == 2
+    empty = _cfg(B=0)
+    assert _call_forward(empty, [None] * 10, 0) == 0                # B*T == 0: nothing to do
+
+
+def test_stage_range_checks():
+    lib = g.load()
+    cfg = _cfg()
+    good = [ctypes.c_void_p(4096 * (i + 1)) for i in range(10)]
+    ws = ctypes.c_size_t(g.workspace_bytes(cfg))
+    for first, last in [(-1, 4), (0, 5), (3, 2)]:
+        assert lib.gau_forward_stages(ctypes.byref(cfg), first, last, *good, ws, None) == 2
+
+
+def test_stack_argument_checks():
+    lib = g.load()
+    cfg = _cfg()
+    arr = (ctypes.c_void_p * 1)(4096)
+    pp = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    ws = g.stack_workspace_bytes(cfg)
+    assert ws > g.workspace_bytes(cfg)
+    assert lib.gau_stack_forward(ctypes.byref(cfg), 1, None, *[pp] * 7, ctypes.c_void_p(4096),
+                                 ctypes.c_size_t(ws), None) == 1
+    assert lib.gau_stack_forward(ctypes.byref(cfg), 1, ctypes.c_void_p(4096), *[pp] * 7,
+                                 ctypes.c_void_p(4096), ctypes.c_size_t(ws - 1), None) == 5
+    assert lib.gau_stack_forward(ctypes.byref(cfg), 0, None, *[pp] * 7, None, 0, None) == 0
+
+
+def test_status_strings():
+    for code in range(7):
+        assert g.status_string(code)
+    assert g.status_string(99) == "unknown status"

@@ -1,0 +1,174 @@
+"""GPU parity: libgau (through its C ABI) against the float64 CPU oracle on the
+same seeded inputs.  Gate: max|err| <= 1e-4 * max|ref| (fp32) and
+<= 2e-2 * max|ref| (bf16 storage, fp32 accumulation), on the output and on
+every stored intermediate."""
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_linear_attention_amd as g
+from chunked_linear_attention_amd import inputs
+from oracle import gau_oracle as orc
+
+from _gpu import (assert_close, chunk_errors, make, oracle_layer, run_layer, tol_for, ws_array,
+                  torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+
+def _stagewise(ws, L, im, B, T, e, s, C, causal, dtype):
+    tol = tol_for(dtype)
+    G = T // C
+    assert_close(ws_array(ws, L, "U", (B, T, e), dtype), im["U"], tol, "U")
+    assert_close(ws_array(ws, L, "Vt", (B, e, T), dtype), im["V"].transpose(0, 2, 1), tol, "Vt")
+    assert_close(ws_array(ws, L, "Q_quad", (B, T, s), dtype), im["Q_quad"], tol, "Q_quad")
+    assert_close(ws_array(ws, L, "K_quad", (B, T, s), dtype), im["K_quad"], tol, "K_quad")
+    assert_close(ws_array(ws, L, "Q_lin", (B, T, s), dtype), im["Q_lin"], tol, "Q_lin")
+    assert_close(ws_array(ws, L, "K_lin_t", (B, s, T), dtype), im["K_lin"].transpose(0, 2, 1), tol, "K_lin_t")
+    assert_close(ws_array(ws, L, "S", (B, G, e, s), dtype), im["S"].transpose(0, 1, 3, 2), tol, "S")
+    Gp = G if causal else 1
+    P = ws_array(ws, L, "P", (B, Gp, e, s), dtype)
+    refP = im["P"].transpose(0, 1, 3, 2)[:, :Gp]
+    if causal:
+        assert np.all(P[:, 0] == 0.0), "P_0 must be exactly zero"
+    if np.max(np.abs(refP)) > 0:
+        assert_close(P, refP, tol, "P")
+    assert_close(ws_array(ws, L, "Y", (B, T, e), dtype), im["Y"], tol, "Y")
+
+
+SMALL = [
+    # B, T, d, e, s, C, dtype, causal
+    (1, 256, 128, 256, 128, 64, "f32", True),
+    (1, 256, 128, 256, 128, 64, "f32", False),
+    (2, 512, 256, 512, 128, 128, "bf16", True),
+    (2, 512, 256, 512, 128, 128, "bf16", False),
+    (1, 320, 128, 256, 128, 64, "bf16", True),     # 320 rows: two full 128-row tiles + a ragged 64
+    (1, 320, 128, 256, 128, 64, "f32", True),
+    (1, 1024, 256, 512, 128, 512, "bf16", True),   # C = 512
+    (1, 1024, 256, 512, 128, 512, "bf16", False),
+    (1, 512, 256, 512, 256, 256, "bf16", True),    # s = 256
+    (1, 256, 128, 256, 256, 128, "f32", False),
+    (3, 128, 128, 256, 128, 128, "bf16", True),    # C = T: one chunk per sequence
+    (2, 192, 384, 768, 128, 64, "bf16", True),     # d, e not powers of two
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}".format(
+    *c[:7], "causal" if c[7] else "full"))
+def test_layer_matches_oracle(case):
+    B, T, d, e, s, C, dtype, causal = case
+    inp = make(B, T, d, e, s, C, dtype, seed=B * 7919 + T + C)
+    O, ws, cfg, L = run_layer(inp, B, T, d, e, s, C, causal, dtype)
+    ref, im = oracle_layer(inp, C, causal, intermediates=True)
+    _stagewise(ws, L, im, B, T, e, s, C, causal, dtype)
+    assert_close(O, ref, tol_for(dtype), "O")
+
+
+def test_tiny_fp32_workload():
+    cfg, inp = inputs.workload_inputs("layer_fp32_B1_T256_d128_C64")
+    O, *_ = run_layer(inp, cfg["B"], cfg["T"], cfg["d"], cfg["e"], cfg["s"], cfg["C"], cfg["causal"],
+                      cfg["dtype"])
+    ref = oracle_layer(inp, cfg["C"], cfg["causal"])
+    assert_close(O, ref, 1e-4, "O")
+
+
+@pytest.mark.parametrize("scales", [(1.0, 1.0), (0.05, 0.3)])
+def test_equation_scaling_reading(scales):
+    qs, ls = scales
+    B, T, d, e, s, C = 1, 512, 256, 512, 128, 128
+    inp = make(B, T, d, e, s, C, "bf16", seed=5)
+    O, *_ = run_layer(inp, B, T, d, e, s, C, True, "bf16", qs, ls)
+    assert_close(O, oracle_layer(inp, C, True, qs, ls), 2e-2, "O")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_identity_attention_is_glu(dtype):
+    """gamma = beta = 0 and relpos = one-hot at C-1: the layer is a GLU."""
+    B, T, d, e, s, C = 1, 256, 128, 256, 128, 64
+    inp = make(B, T, d, e, s, C, dtype, seed=9)
+    inp["gamma"][:] = 0
+    inp["beta"][:] = 0
+    inp["relpos"][:] = 0
+    inp["relpos"][C - 1] = 1.0
+    O, *_ = run_layer(inp, B, T, d, e, s, C, True, dtype)
+    ref = orc.glu(inp["X"], inp["W_u"], inp["W_v"], inp["W_o"])
+    assert_close(O, ref, tol_for(dtype), "O vs GLU")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_causal_output_ignores_future_bitwise(dtype):
+    B, T, d, e, s, C = 2, 512, 256, 512, 128, 128
+    inp = make(B, T, d, e, s, C, dtype, seed=21)
+    a, *_ = run_layer(inp, B, T, d, e, s, C, True, dtype)
+    for t in (127, 200):
+        q = dict(inp)
+        q["X"] = inp["X"].copy()
+        q["X"][:, t + 1:] = np.random.default_rng(t).standard_normal(q["X"][:, t + 1:].shape)
+        if dtype == "bf16":
+            q["X"] = inputs.round_bf16(q["X"].astype(np.float32))
+        b, *_ = run_layer(q, B, T, d, e, s, C, True, dtype)
+        np.testing.assert_array_equal(a[:, :t + 1], b[:, :t + 1])
+        assert np.max(np.abs(a[:, t + 1:] - b[:, t + 1:])) > 0
+
+
+def test_runs_are_bitwise_deterministic():
+    B, T, d, e, s, C = 2, 512, 256, 512, 128, 128
+    inp = make(B, T, d, e, s, C, "bf16", seed=33)
+    a, *_ = run_layer(inp, B, T, d, e, s, C, True, "bf16")
+    b, *_ = run_layer(inp, B, T, d, e, s, C, True, "bf16")
+    np.testing.assert_array_equal(a, b)
+
+
+def test_local_only_and_global_only_components():
+    """The quadratic and linear parts, each alone, meet the same tolerance
+    (the global gate alone would not see an error in a small part)."""
+    B, T, d, e, s, C = 1, 1024, 256, 512, 128, 256
+    base = make(B, T, d, e, s, C, "bf16", seed=41)
+    loc = {k: v.copy() for k, v in base.items()}
+    loc["gamma"][2] = 0
+    loc["beta"][2] = 0
+    O, *_ = run_layer(loc, B, T, d, e, s, C, True, "bf16")
+    assert_close(O, oracle_layer(loc, C, True), 2e-2, "LocalOnly")
+    glo = {k: v.copy() for k, v in base.items()}
+    glo["gamma"][0] = 0
+    glo["beta"][0] = 0
+    glo["relpos"] = -np.abs(glo["relpos"]) - 0.01
+    O, *_ = run_layer(glo, B, T, d, e, s, C, True, "bf16")
+    assert_close(O, oracle_layer(glo, C, True), 2e-2, "GlobalOnly")
+
+
+def test_batch_rows_independent_on_gpu():
+    B, T, d, e, s, C = 3, 256, 128, 256, 128, 64
+    inp = make(B, T, d, e, s, C, "bf16", seed=45)
+    full, *_ = run_layer(inp, B, T, d, e, s, C, True, "bf16")
+    one = dict(inp, X=inp["X"][1:2].copy())
+    row, *_ = run_layer(one, 1, T, d, e, s, C, True, "bf16")
+    np.testing.assert_array_equal(full[1:2], row)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+FULL = ["layer_bf16_B8_T1024_d768_C256", "layer_bf16_B4_T4096_d768_C256",
+        "layer_bf16_B4_T4096_d768_C256_noncausal", "layer_bf16_B2_T8192_d768_C512",
+        "layer_bf16_B2_T8192_d768_C256"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    """The benchmark's launch configuration at full size.  The oracle checks
+    batch row 0 (rows are independent: pinned in the oracle tests and checked
+    on the GPU above) and, for B <= 2, every row."""
+    cfg, inp = inputs.workload_inputs(name)
+    B, T, d, e, s, C = (cfg[k] for k in ("B", "T", "d", "e", "s", "C"))
+    O, *_ = run_layer(inp, B, T, d, e, s, C, cfg["causal"], "bf16")
+    assert np.all(np.isfinite(O))
+    rows = range(B) if B <= 2 else [0]
+    if B > 2 and B * T <= 8192:
+        rows = range(B)
+    for b in rows:
+        one = dict(inp, X=inp["X"][b:b + 1])
+        ref = oracle_layer(one, C, cfg["causal"])
+        err = assert_close(O[b:b + 1], ref, 2e-2, f"{name} row {b}")
+        ce = chunk_errors(O[b:b + 1], ref, C)
+        print(f"{name} row {b}: global {err:.2e}, worst per-chunk {ce.max():.2e}")
