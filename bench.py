@@ -1,0 +1,220 @@
+"""Benchmark of the FLASH layer forward (GAU with mixed chunk attention) on one
+MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one full forward of the layer (all five kernels) over one batch of
+seeded synthetic input, B=2 sequences of T=8192 tokens, d=768, e=1536, s=128,
+chunk C=256, bf16 storage with fp32 accumulation, causal.  Inputs are resident
+in HBM before the timed region starts.  Prints one JSON line.
+
+Per-kernel durations come from HIP events recorded between the stages on the
+stream the kernels run on, inside the timed region.  The roofline object is for
+the dominant kernel (the fused projection GEMM): its algorithmic FLOPs per
+launch divided by its average duration, against the dense bf16 MFMA peak.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4 SIMDs x 1024 dense bf16 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "GAU/FLASH layer fwd tokens/sec at d=768 T=8192 C=256; % bf16 MFMA peak"
+STAGES = ["proj_gemm", "chunk_state", "chunk_scan", "chunk_attn", "out_gemm"]
+
+
+def algorithmic_flops(B, T, d, e, s, C, causal=True):
+    """Algorithmic FLOPs of one layer forward, per stage.
+
+    Dense GEMMs count 2 FLOP per multiply-add.  The intra-chunk score and value
+    products count the causal lower triangle with its diagonal, C(C+1)/2 pairs
+    per chunk (the full C^2 when non-causal)."""
+    M = B * T
+    pairs = C * (C + 1) / 2 if causal else C * C
+    G = T // C
+    return {
+        "proj_gemm": 2.0 * M * d * (2 * e + s),
+        "chunk_state": 2.0 * M * s * e,
+        "chunk_scan": 0.0,
+        "chunk_attn": 2.0 * B * G * pairs * (s + e) + 2.0 * M * s * e,
+        "out_gemm": 2.0 * M * e * d,
+    }
+
+
+def algorithmic_bytes(B, T, d, e, s, C, causal=True, eb=2):
+    """Minimum HBM bytes each stage must move with this decomposition."""
+    M = B * T
+    G = T // C
+    Gp = G if causal else 1
+    st = B * G * e * s
+    return {
+        "proj_gemm": M * d * eb + (2 * e + s) * d * eb + M * (2 * e + 4 * s) * eb,
+        "chunk_state": M * (e + s) * eb + st * 4,
+        "chunk_scan": st * 4 + B * Gp * e * s * eb,
+        "chunk_attn": M * (3 * s + 2 * e) * eb + B * Gp * e * s * eb + M * e * eb,
+        "out_gemm": M * e * eb + e * d * eb + M * d * eb,
+    }
+
+
+def source_hash(name):
+    path = os.path.join(ROOT, "chunked_linear_attention_amd", "csrc", name + ".hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel source has changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_B2_T8192_d768_C256_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg, inp, min_s=10.0, max_passes=20):
+    """The float64 oracle, as it stands, on the host cores: whole sequences of
+    the timed workload, one after another, repeated until at least min_s of
+    CPU work has been timed."""
+    from oracle import gau_oracle as orc
+    done, t0 = 0, time.perf_counter()
+    while True:
+        b = done % cfg["B"]
+        orc.flash_forward(inp["X"][b:b + 1], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"],
+                          inp["beta"], inp["relpos"], cfg["C"], cfg["causal"])
+        done += 1
+        dt = time.perf_counter() - t0
+        if (dt >= min_s and done % cfg["B"] == 0) or done >= max_passes * cfg["B"]:
+            break
+    return {"value": done * cfg["T"] / dt, "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{done} sequences of T={cfg['T']} ({done // cfg['B']} passes over the B={cfg['B']} "
+                      f"timed workload), float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunked_linear_attention_amd as g
+    from chunked_linear_attention_amd import inputs
+
+    name = inputs.HEADLINE
+    cfg, inp = inputs.workload_inputs(name)
+    B, T, d, e, s, C = (cfg[k] for k in ("B", "T", "d", "e", "s", "C"))
+    causal = cfg["causal"]
+    torch.cuda.set_device(0)
+    dev = g.device_layer(inp, torch.bfloat16)
+    gc = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16)
+    ws = torch.empty(g.workspace_bytes(gc), dtype=torch.uint8, device="cuda")
+    O = torch.empty((B, T, d), dtype=torch.bfloat16, device="cuda")
+    args_l = (dev["X"], dev["W_u"], dev["W_v"], dev["W_z"], dev["W_o"], dev["scale"], dev["offset"],
+              dev["relpos"], O, ws)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs is None:
+            g.forward(gc, *args_l, stream=stream)
+            return
+        for i in range(5):
+            evs[i].record(stream)
+            g.forward_stages(gc, i, i, *args_l, stream=stream)
+        evs[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_stage = {n: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(K)]))
+                 for i, n in enumerate(STAGES)}  # ms
+    # the same K steps as single gau_forward calls (no events between kernels)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall_plain = time.perf_counter() - t1
+
+    tokens = B * T
+    ms_per_step = wall * 1e3 / K
+    value = tokens * K / wall
+    flops = algorithmic_flops(B, T, d, e, s, C, causal)
+    bytes_ = algorithmic_bytes(B, T, d, e, s, C, causal)
+    layer_flops = sum(flops.values())
+    dom = "proj_gemm"
+    achieved = flops[dom] / (per_stage[dom] * 1e-3) / 1e12
+    traffic = measured_traffic(dom)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, random-init weights)",
+        "config": {"workload": name, "B": B, "T": T, "d": d, "e": e, "s": s, "C": C,
+                   "causal": causal, "global_batch": B, "seq_len": T},
+        "layer_frac_of_bf16_peak": layer_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "layer_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "algorithmic_flops_per_launch": flops[dom]},
+        "kernels_us": {n: per_stage[n] * 1e3 for n in STAGES},
+        "kernels_gbs": {n: bytes_[n] / (per_stage[n] * 1e-3) / 1e9 for n in STAGES},
+        "kernels_tflops": {n: flops[n] / (per_stage[n] * 1e-3) / 1e12 for n in STAGES},
+        "ms_per_step_without_stage_events": wall_plain * 1e3 / K,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,324 @@
+// Block-level NT GEMM core for gfx950:  C[BM x BN] += A[BM x K] . B[BN x K]^T
+// with A and B row-major and K contiguous.  Used by the projection and output
+// GEMMs of the layer.
+//
+// Design (MI355X / CDNA4):
+//  * 32x32x16 bf16 MFMA (v_mfma_f32_32x32x16_bf16; fp32: four
+//    v_mfma_f32_32x32x2_f32 per 16-byte fragment), fp32 accumulation.  Each of
+//    the WGM x WGN waves owns a (BM/WGM) x (BN/WGN) sub-tile.
+//  * K advances in chunks of 128 bytes (64 bf16 / 32 fp32).  Global memory is
+//    copied straight into LDS with global_load_lds_dwordx4 (no VGPR staging),
+//    double-buffered: the copy of chunk k+1 is in flight while chunk k is
+//    multiplied, and one barrier per chunk separates the two.
+//  * LDS rows are 128 bytes without padding; the eight 16-byte pieces of row r
+//    are stored XOR-permuted by (r & 7), so the 32 rows read by one MFMA
+//    fragment load hit distinct banks, and every wave's direct copy still
+//    writes 1 KiB of consecutive LDS (the permutation is applied to the global
+//    addresses instead).
+//
+// Fragment layout of v_mfma_f32_32x32x16_bf16 (lane l; verified on gfx950):
+//   A: row l % 32, 16 bytes of K at byte 16 * (l / 32) of a 32-byte K step;
+//   B: column l % 32, same K bytes; accumulator (16 floats): column l % 32,
+//   row 8 * (r / 4) + 4 * (l / 32) + r % 4.
+// For fp32 the fragment's four floats feed four K=2 MFMAs (slot t of lane
+// group h stands for K index 4h + t in both operands).
+#pragma once
+
+#include "gau_device.h"
+
+namespace gau {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void mma32(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b, bf16) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b, float) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima so they do not wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Direct global -> LDS copy of one 128-byte K chunk of a ROWS-row operand
+// tile.  The tile is moved as 1 KiB wave pieces (8 rows); wave w of NW takes
+// pieces w, w + NW, ...  Each lane's source pointer (row clamped to the rows
+// that exist, piece XOR-permuted by the row) is computed once; a chunk only
+// adds its K offset.
+template <int ROWS, int NW>
+struct DmaOperand {
+    static constexpr int kLoads = ROWS / 8 / NW;
+    static_assert(ROWS % (8 * NW) == 0, "pieces must split evenly over the waves");
+    const char* src[kLoads];
+
+    __device__ __forceinline__ void init(const char* g, size_t pitch, int rows_valid, int wave, int lane) {
+        const int sub = lane >> 3;           // row inside the 8-row piece
+        const int piece = (lane & 7) ^ sub;  // logical 16-byte piece this lane fetches
+#pragma unroll
+        for (int jj = 0; jj < kLoads; ++jj) {
+            int r = (wave + jj * NW) * 8 + sub;
+            r = r < rows_valid ? r : rows_valid - 1;
+            src[jj] = g + (size_t)r * pitch + piece * 16;
+        }
+    }
+    // Issue the copy of K chunk `kc` into `lds_tile`.
+    __device__ __forceinline__ void issue(char* lds_tile, int kc, int wave) const {
+#pragma unroll
+        for (int jj = 0; jj < kLoads; ++jj)
+            __builtin_amdgcn_global_load_lds((glb_ptr_t)(src[jj] + (size_t)kc * 128),
+                                             (lds_ptr_t)(lds_tile + (wave + jj * NW) * 1024), 16, 0, 0);
+    }
+};
+
+// The hardware dispatches workgroup b to XCD b % 8, and each XCD has its own
+// L2.  xcd_remap turns the dispatch index into a logical tile index such that
+// each XCD receives a contiguous range of logical tiles (so neighbouring tiles,
+// which share operand rows, share one L2).  Bijective for any count.
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+    constexpr int kXcd = 8;
+    const int x = b % kXcd, q = nb / kXcd, r = nb % kXcd;
+    return x * q + (x < r ? x : r) + b / kXcd;
+}
+
+// LDS byte offset of logical 16-byte piece c of row r in a swizzled tile.
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+template <typename T, int BM, int BN, int WGM, int WGN>
+struct GemmCore {
+    static constexpr int NW = WGM * WGN;
+    static constexpr int NT = NW * kWave;
+    static constexpr int WTM = BM / WGM;  // wave tile
+    static constexpr int WTN = BN / WGN;
+    static constexpr int MB = WTM / 32;
+    static constexpr int NB = WTN / 32;
+    static constexpr int KELEMS = 128 / Elem<T>::kBytes;  // K elements per chunk
+    static constexpr int A_BYTES = BM * 128;
+    static constexpr int STAGE_BYTES = (BM + BN) * 128;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "tile shape");
+    static_assert(BM % 8 == 0 && BN % 8 == 0, "tile rows");
+    static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "pieces must split evenly over waves");
+
+    __device__ static __forceinline__ void zero(f32x16_t (&acc)[MB][NB]) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
+
+    // Fragments of one 32-byte K step (ks = 0..3 inside a 128-byte chunk).
+    __device__ static __forceinline__ void load_frags(u32x4_t (&fa)[MB], u32x4_t (&fb)[NB], const char* ta,
+                                                      const char* tb, int ks, int fr, int fh) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) fa[i] = *(const u32x4_t*)(ta + swz(i * 32 + fr, 2 * ks + fh));
+#pragma unroll
+        for (int j = 0; j < NB; ++j) fb[j] = *(const u32x4_t*)(tb + swz(j * 32 + fr, 2 * ks + fh));
+    }
+
+    __device__ static __forceinline__ void mma_step(f32x16_t (&acc)[MB][NB], const u32x4_t (&fa)[MB],
+                                                    const u32x4_t (&fb)[NB]) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) mma32(acc[i][j], fa[i], fb[j], T());
+    }
+
+    // Scheduling pattern for one K step: NMFMA MFMAs, each followed by one LDS
+    // read while any remain (NREAD) and one DMA load while any remain (NVMEM).
+    template <int NMFMA, int NREAD, int NVMEM>
+    __device__ static __forceinline__ void sched_step() {
+        constexpr int n0 = NREAD > NVMEM ? NREAD : NVMEM;
+        constexpr int n = n0 < NMFMA ? n0 : NMFMA;
+#pragma unroll
+        for (int x = 0; x < n; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+            if (x < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            if (x < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // DMA load
+        }
+        if constexpr (NMFMA > n) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - n, 0);
+    }
+
+    // One K step of a chunk: read the fragments of step KS+1 (if any), issue
+    // the next chunk's DMA (ISSUE, step 0 only), multiply step KS.
+    template <int KS, bool ISSUE>
+    __device__ static __forceinline__ void step(f32x16_t (&acc)[MB][NB], u32x4_t (&fa)[2][MB],
+                                                u32x4_t (&fb)[2][NB], const char* ta, const char* tb,
+                                                const DmaOperand<BM, NW>& da, const DmaOperand<BN, NW>& db,
+                                                char* nxt, int kc_next, int wave, int fr, int fh) {
+        constexpr int NL = DmaOperand<BM, NW>::kLoads + DmaOperand<BN, NW>::kLoads;
+        if constexpr (KS < 3) load_frags(fa[(KS + 1) & 1], fb[(KS + 1) & 1], ta, tb, KS + 1, fr, fh);
+        if constexpr (ISSUE && KS == 0) {
+            da.issue(nxt, kc_next, wave);
+            db.issue(nxt + A_BYTES, kc_next, wave);
+        }
+        mma_step(acc, fa[KS & 1], fb[KS & 1]);
+        sched_step<MB * NB, (KS < 3 ? MB + NB : 0), ((ISSUE && KS == 0) ? NL : 0)>();
+    }
+
+    // One 128-byte K chunk from LDS (four K steps; fragments double-buffered
+    // in registers).  With ISSUE the DMA copy of the next chunk is spread over
+    // the first step's MFMAs.
+    template <bool ISSUE>
+    __device__ static __forceinline__ void chunk(f32x16_t (&acc)[MB][NB], u32x4_t (&fa)[2][MB],
+                                                 u32x4_t (&fb)[2][NB], const char* ta, const char* tb,
+                                                 const DmaOperand<BM, NW>& da, const DmaOperand<BN, NW>& db,
+                                                 char* nxt, int kc_next, int wave, int fr, int fh) {
+        step<0, ISSUE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh);
+        step<1, ISSUE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh);
+        step<2, ISSUE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh);
+        step<3, ISSUE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh);
+    }
+
+    // acc += A . B^T over K elements (a multiple of KELEMS).  Double-buffered
+    // LDS stages; one barrier per chunk, after the wave's copy of the next
+    // chunk has landed.
+    __device__ static __forceinline__ void run(f32x16_t (&acc)[MB][NB], const char* __restrict__ a,
+                                               size_t pitch_a, int rows_a, const char* __restrict__ b,
+                                               size_t pitch_b, int rows_b, int K, char* lds) {
+        const int tid = threadIdx.x;
+        const int wave = tid / kWave;
+        const int lane = tid % kWave;
+        const int wm = wave / WGN, wn = wave % WGN;
+        const int nk = K / KELEMS;
+        const int fr = lane & 31;  // fragment row
+        const int fh = lane >> 5;  // fragment K half
+
+        DmaOperand<BM, NW> da;
+        DmaOperand<BN, NW> db;
+        da.init(a, pitch_a, rows_a, wave, lane);
+        db.init(b, pitch_b, rows_b, wave, lane);
+        da.issue(lds, 0, wave);
+        db.issue(lds + A_BYTES, 0, wave);
+        wait_vmcnt<0>();
+        __syncthreads();
+
+        u32x4_t fa[2][MB], fb[2][NB];
+        const int oa = (wm * WTM) * 128, ob = A_BYTES + (wn * WTN) * 128;
+        load_frags(fa[0], fb[0], lds + oa, lds + ob, 0, fr, fh);
+
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            char* cur = lds + (kt & 1) * STAGE_BYTES;
+            char* nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
+            chunk<true>(acc, fa, fb, cur + oa, cur + ob, da, db, nxt, kt + 1, wave, fr, fh);
+            wait_vmcnt<0>();
+            __syncthreads();
+            load_frags(fa[0], fb[0], nxt + oa, nxt + ob, 0, fr, fh);
+        }
+        {
+            char* cur = lds + ((nk - 1) & 1) * STAGE_BYTES;
+            chunk<false>(acc, fa, fb, cur + oa, cur + ob, da, db, nullptr, 0, wave, fr, fh);
+        }
+        __syncthreads();  // LDS free for the epilogue
+    }
+
+    // Apply f to every accumulator element in place: acc = f(row, col, acc).
+    template <typename F>
+    __device__ static __forceinline__ void transform(f32x16_t (&acc)[MB][NB], F&& f) {
+        const int wave = threadIdx.x / kWave;
+        const int lane = threadIdx.x % kWave;
+        const int wm = wave / WGN, wn = wave % WGN;
+        const int c = lane & 31;
+        const int h = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = f(wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3), wn * WTN + j * 32 + c,
+                                     acc[i][j][r]);
+    }
+
+    // Store the block tile through LDS with 16-byte global stores.
+    //   TRANSPOSED = false: staged rows are tile rows; dst(row, col) gives the
+    //     global address of element (row, col..col+V-1) or nullptr to skip.
+    //   TRANSPOSED = true: staged rows are tile columns; dst(col, row) gives
+    //     the address of elements (row..row+V-1, col).
+    // val(row, col, acc) gives the value stored (in OutT); emit(d, v) writes
+    // one staged 16-byte vector v to d (a plain store by default).  When the staged
+    // tile does not fit in LDS at once it is staged in passes of one wave row
+    // (or column) of the wave grid.  Begins and ends with a barrier.
+    struct PlainEmit {
+        __device__ __forceinline__ void operator()(char* d, const u32x4_t& v) const { *(u32x4_t*)d = v; }
+    };
+
+    template <typename OutT, bool TRANSPOSED, typename V, typename D, typename E = PlainEmit>
+    __device__ static __forceinline__ void store(const f32x16_t (&acc)[MB][NB], char* lds, int lds_bytes, V&& val,
+                                                 D&& dst, E&& emit = E()) {
+        constexpr int EB = Elem<OutT>::kBytes;
+        constexpr int SROWS = TRANSPOSED ? BN : BM;  // staged rows
+        constexpr int SCOLS = TRANSPOSED ? BM : BN;  // elements per staged row
+        constexpr int PITCH = SCOLS * EB + 16;
+        constexpr int NG = TRANSPOSED ? WGN : WGM;   // wave groups along the staged rows
+        const int npass = SROWS * PITCH <= lds_bytes ? 1 : NG;
+        const int prows = SROWS / npass;
+        const int wave = threadIdx.x / kWave;
+        const int lane = threadIdx.x % kWave;
+        const int wm = wave / WGN, wn = wave % WGN;
+        const int c = lane & 31;
+        const int h = lane >> 5;
+        const int mygroup = TRANSPOSED ? wn : wm;
+        constexpr int VPR = SCOLS * EB / 16;  // 16-byte vectors per staged row
+        for (int pass = 0; pass < npass; ++pass) {
+            __syncthreads();
+            if (npass == 1 || mygroup == pass) {
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int row = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                            const int col = wn * WTN + j * 32 + c;
+                            const float x = val(row, col, acc[i][j][r]);
+                            if (TRANSPOSED)
+                                Elem<OutT>::put(lds + (col - pass * prows) * PITCH + row * EB, x);
+                            else
+                                Elem<OutT>::put(lds + (row - pass * prows) * PITCH + col * EB, x);
+                        }
+            }
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < prows * VPR; idx += NT) {
+                const int srow = idx / VPR;
+                const int v = idx % VPR;
+                char* d = dst(pass * prows + srow, v * (16 / EB));
+                if (d) emit(d, *(const u32x4_t*)(lds + srow * PITCH + v * 16));
+            }
+        }
+    }
+
+    // f(row, col, value) for every accumulator element; row/col relative to
+    // the block tile.
+    template <typename F>
+    __device__ static __forceinline__ void for_each(const f32x16_t (&acc)[MB][NB], F&& f) {
+        const int wave = threadIdx.x / kWave;
+        const int lane = threadIdx.x % kWave;
+        const int wm = wave / WGN, wn = wave % WGN;
+        const int c = lane & 31;
+        const int h = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    f(wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3), wn * WTN + j * 32 + c, acc[i][j][r]);
+    }
+};
+
+}  // namespace gau

@@ -4,77 +4,81 @@
 // epilogue also adds the layer's shortcut in fp32 (the skip connection the
 // listings add after each block: wikillm, FLASH block pseudocode).
 //
-// An NT GEMM: A = Y [M, e], B = W_o^T [d, e], K = e.
-#include "gau_device.h"
+// An NT GEMM on the shared core: A = Y [M, e], B = W_o^T [d, e], K = e,
+// 256 x 256 output tiles (d need only be a multiple of 128: the last column
+// tile may be half full).
 #include "gau_launch.h"
+#include "gemm_core.h"
 
 namespace gau {
 namespace {
 
-constexpr int BM = 128, BN = 128;
+constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4;
 
 template <typename T>
-__global__ __launch_bounds__(256) void out_gemm_kernel(OutParams p) {
+struct OutTile {
+    using G = GemmCore<T, BM, BN, WGM, WGN>;
+    // fp32 staging (residual output or fp32 layer) in two passes of 128 rows
+    static constexpr int STAGE = BM / WGM * (BN * 4 + 16);
+    static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
+};
+
+template <typename T>
+__global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     extern __shared__ __align__(16) char lds[];
-    using G = GemmNT<T, BM, BN>;
+    using G = typename OutTile<T>::G;
     constexpr int EB = Elem<T>::kBytes;
-    const int ntiles = p.d / BN;
-    const int nt = blockIdx.x % ntiles;
-    const int mt = blockIdx.x / ntiles;
+    const int ntiles = (p.d + BN - 1) / BN;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int nt = bid % ntiles;
+    const int mt = bid / ntiles;
     const int m0 = mt * BM, n0 = nt * BN;
     const size_t pitch = (size_t)p.e * EB;
     const int rows_a = min(BM, p.M - m0);
+    const int rows_b = min(BN, p.d - n0);
 
-    f32x4_t acc[G::MB][G::NB];
+    f32x16_t acc[G::MB][G::NB];
+    G::zero(acc);
     G::run(acc, (const char*)p.Y + (size_t)m0 * pitch, pitch, rows_a, (const char*)p.W_o + (size_t)n0 * pitch, pitch,
-           BN, p.e, lds);
+           rows_b, p.e, lds);
 
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave >> 1, wn = wave & 1;
-    __syncthreads();
+    constexpr int LDS = OutTile<T>::LDS;
+    const int M = p.M, d = p.d;
+    auto ident = [](int, int, float v) { return v; };
     if (p.residual == nullptr) {
-        constexpr int PITCH = BN * EB + 16;
-        for_each_acc(acc, lane, [&](int r, int c, float v) {
-            Elem<T>::put(lds + (wm * (BM / 2) + r) * PITCH + (wn * (BN / 2) + c) * EB, v);
-        });
-        __syncthreads();
-        constexpr int VPR = BN * EB / 16;
         char* O = (char*)p.O;
-        for (int idx = tid; idx < BM * VPR; idx += 256) {
-            const int row = idx / VPR, v = idx % VPR;
-            if (m0 + row < p.M)
-                *(u32x4_t*)(O + ((size_t)(m0 + row) * p.d + n0) * EB + v * 16) =
-                    *(const u32x4_t*)(lds + row * PITCH + v * 16);
-        }
-    } else {
-        constexpr int PITCH = BN * 4 + 16;
-        for_each_acc(acc, lane, [&](int r, int c, float v) {
-            *(float*)(lds + (wm * (BM / 2) + r) * PITCH + (wn * (BN / 2) + c) * 4) = v;
+        G::template store<T, false>(acc, lds, LDS, ident, [&](int row, int col) -> char* {
+            const int m = m0 + row, n = n0 + col;
+            return (m < M && n < d) ? O + ((size_t)m * d + n) * EB : nullptr;
         });
-        __syncthreads();
-        constexpr int VPR = BN * 4 / 16;
+    } else {
+        // O = residual + Y W_o (fp32): stage the product, then add the residual
+        // while storing (each 16-byte vector is read and written by one thread).
         float* O = (float*)p.O;
-        for (int idx = tid; idx < BM * VPR; idx += 256) {
-            const int row = idx / VPR, v = idx % VPR;
-            if (m0 + row < p.M) {
-                const size_t off = (size_t)(m0 + row) * p.d + n0 + v * 4;
-                f32x4_t x = *(const f32x4_t*)(p.residual + off);
-                x += *(const f32x4_t*)(lds + row * PITCH + v * 16);
-                *(f32x4_t*)(O + off) = x;
-            }
-        }
+        const float* R = p.residual;
+        G::template store<float, false>(
+            acc, lds, LDS, ident,
+            [&](int row, int col) -> char* {
+                const int m = m0 + row, n = n0 + col;
+                return (m < M && n < d) ? (char*)(O + (size_t)m * d + n) : nullptr;
+            },
+            [&](char* dp, const u32x4_t& v) {
+                const size_t off = (size_t)((float*)dp - O);
+                f32x4_t x = *(const f32x4_t*)(R + off);
+                x += __builtin_bit_cast(f32x4_t, v);
+                *(f32x4_t*)dp = x;
+            });
     }
 }
 
 template <typename T>
 hipError_t launch(const OutParams& p, hipStream_t st) {
-    using G = GemmNT<T, BM, BN>;
-    constexpr int STAGE = BM * (BN * 4 + 16);
-    constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
-    const int blocks = (p.d / BN) * ((p.M + BM - 1) / BM);
+    constexpr int LDS = OutTile<T>::LDS;
+    static_assert(LDS <= 160 * 1024, "output GEMM LDS over budget");
+    const int blocks = ((p.d + BN - 1) / BN) * ((p.M + BM - 1) / BM);
     hipError_t e = allow_lds(out_gemm_kernel<T>, LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(out_gemm_kernel<T>, dim3(blocks), dim3(256), LDS, st, p);
+    hipLaunchKernelGGL(out_gemm_kernel<T>, dim3(blocks), dim3(512), LDS, st, p);
     return hipGetLastError();
 }
 

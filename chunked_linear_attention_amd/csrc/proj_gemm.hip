@@ -14,123 +14,95 @@
 //   kernels read tokens contiguously); Q_quad, K_quad, Q_lin [M, s] row-major;
 //   K_lin_t [B, s, T] transposed.  M = B*T.
 //
-// Grid: one block per (128 rows) x (128 columns of the concatenated 2e+s
-// outputs).  e and s are multiples of 128, so a block's columns lie in exactly
-// one of the U, V and Z sections and its epilogue branch is uniform.
-#include "gau_device.h"
+// Tiling: 256 x 256 output tiles (GemmCore, 8 waves), the tiles of each
+// section (U: e/256, V: e/256, Z: one tile of s <= 256 columns) laid side by
+// side along N; tiles are assigned to XCDs in contiguous ranges.  A block's
+// columns lie in exactly one section, so its epilogue branch is uniform.
 #include "gau_launch.h"
+#include "gemm_core.h"
 
 namespace gau {
 
 namespace {
 
-constexpr int BM = 128, BN = 128;
-
-// Stage a BM x BN tile (values from `val(row, col)`) into LDS and store it to
-// global memory, row-major (rows = tokens) or transposed (rows = features).
-template <typename T, bool TRANSPOSED, typename V, typename D>
-__device__ __forceinline__ void stage_and_store(char* lds, V&& val, D&& dst_row, const f32x4_t (&acc)[BM / 32][BN / 32],
-                                                int wm, int wn, int lane, int tid) {
-    constexpr int EB = Elem<T>::kBytes;
-    constexpr int ROWS = TRANSPOSED ? BN : BM;
-    constexpr int COLS = TRANSPOSED ? BM : BN;
-    constexpr int PITCH = COLS * EB + 16;
-    __syncthreads();
-    for_each_acc(acc, lane, [&](int r, int c, float v) {
-        const int row = wm * (BM / 2) + r;
-        const int col = wn * (BN / 2) + c;
-        const float x = val(row, col, v);
-        if (TRANSPOSED)
-            Elem<T>::put(lds + col * PITCH + row * EB, x);
-        else
-            Elem<T>::put(lds + row * PITCH + col * EB, x);
-    });
-    __syncthreads();
-    constexpr int VPR = COLS * EB / 16;  // 16-byte vectors per staged row
-    for (int idx = tid; idx < ROWS * VPR; idx += 256) {
-        const int row = idx / VPR;
-        const int v = idx % VPR;
-        char* d = dst_row(row, v * 16 / EB);
-        if (d) *(u32x4_t*)d = *(const u32x4_t*)(lds + row * PITCH + v * 16);
-    }
-}
+constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4;
 
 template <typename T>
-__global__ __launch_bounds__(256) void proj_gemm_kernel(ProjParams p) {
+struct ProjTile {
+    using G = GemmCore<T, BM, BN, WGM, WGN>;
+    static constexpr int EB = Elem<T>::kBytes;
+    static constexpr int STAGE = (BM * (BN * EB + 16) > 160 * 1024 - 1024) ? BM / WGM * (BN * EB + 16)
+                                                                           : BM * (BN * EB + 16);
+    static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
+};
+
+template <typename T>
+__global__ __launch_bounds__(512) void proj_gemm_kernel(ProjParams p) {
     extern __shared__ __align__(16) char lds[];
-    using G = GemmNT<T, BM, BN>;
-    const int n_tiles = (2 * p.e + p.s) / BN;
-    const int nt = blockIdx.x % n_tiles;
-    const int mt = blockIdx.x / n_tiles;
-    const int m0 = mt * BM;
-    const int n0 = nt * BN;
-    int section, c0;
-    const char* w;
-    if (n0 < p.e) {
-        section = 0; c0 = n0; w = (const char*)p.W_u;
-    } else if (n0 < 2 * p.e) {
-        section = 1; c0 = n0 - p.e; w = (const char*)p.W_v;
-    } else {
-        section = 2; c0 = n0 - 2 * p.e; w = (const char*)p.W_z;
-    }
+    using G = typename ProjTile<T>::G;
     constexpr int EB = Elem<T>::kBytes;
+    const int ntu = p.e / BN;              // tiles per U or V section
+    const int ntiles = 2 * ntu + 1;        // + one Z tile
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int nt = bid % ntiles;
+    const int mt = bid / ntiles;
+    const int m0 = mt * BM;
+    int section, c0, rows_b;
+    const char* w;
+    if (nt < ntu) {
+        section = 0; c0 = nt * BN; w = (const char*)p.W_u; rows_b = BN;
+    } else if (nt < 2 * ntu) {
+        section = 1; c0 = (nt - ntu) * BN; w = (const char*)p.W_v; rows_b = BN;
+    } else {
+        section = 2; c0 = 0; w = (const char*)p.W_z; rows_b = p.s;
+    }
     const size_t pitch = (size_t)p.d * EB;
     const int rows_a = min(BM, p.M - m0);
 
-    f32x4_t acc[G::MB][G::NB];
-    G::run(acc, (const char*)p.X + (size_t)m0 * pitch, pitch, rows_a, w + (size_t)c0 * pitch, pitch, BN, p.d, lds);
+    f32x16_t acc[G::MB][G::NB];
+    G::zero(acc);
+    G::run(acc, (const char*)p.X + (size_t)m0 * pitch, pitch, rows_a, w + (size_t)c0 * pitch, pitch, rows_b, p.d,
+           lds);
+    G::transform(acc, [](int, int, float v) { return silu(v); });
 
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave >> 1, wn = wave & 1;
+    constexpr int LDS = ProjTile<T>::LDS;
     const int M = p.M, T_ = p.T;
-
+    auto ident = [](int, int, float v) { return v; };
     if (section == 0) {
         char* U = (char*)p.U;
-        stage_and_store<T, false>(
-            lds, [&](int, int, float v) { return silu(v); },
-            [&](int row, int col) -> char* {
-                const int m = m0 + row;
-                return m < M ? U + ((size_t)m * p.e + c0 + col) * EB : nullptr;
-            },
-            acc, wm, wn, lane, tid);
+        G::template store<T, false>(acc, lds, LDS, ident, [&](int row, int col) -> char* {
+            const int m = m0 + row;
+            return m < M ? U + ((size_t)m * p.e + c0 + col) * EB : nullptr;
+        });
     } else if (section == 1) {
         char* Vt = (char*)p.Vt;
-        stage_and_store<T, true>(
-            lds, [&](int, int, float v) { return silu(v); },
-            [&](int frow, int tcol) -> char* {
-                const int m = m0 + tcol;
-                if (m >= M) return nullptr;
-                const int b = m / T_, t = m - b * T_;
-                return Vt + (((size_t)b * p.e + c0 + frow) * T_ + t) * EB;
-            },
-            acc, wm, wn, lane, tid);
+        G::template store<T, true>(acc, lds, LDS, ident, [&](int frow, int tcol) -> char* {
+            const int m = m0 + tcol;
+            if (m >= M) return nullptr;
+            const int b = m / T_, t = m - b * T_;
+            return Vt + (((size_t)b * p.e + c0 + frow) * T_ + t) * EB;
+        });
     } else {
-        // Z = SiLU(H_z); head h = Z * gamma[h] + beta[h].  Heads 0..2 are
-        // stored row-major, head 3 (K_lin) transposed.
+        // head h = Z * gamma[h] + beta[h]; heads 0..2 row-major, head 3 (K_lin) transposed
+        const int s = p.s;
         for (int h = 0; h < 4; ++h) {
-            const float* gam = p.scale + h * p.s + c0;
-            const float* bet = p.offset + h * p.s + c0;
-            auto val = [&](int, int col, float v) { return silu(v) * gam[col] + bet[col]; };
+            const float* gam = p.scale + h * s;
+            const float* bet = p.offset + h * s;
+            auto val = [&](int, int col, float z) { return col < s ? z * gam[col] + bet[col] : 0.f; };
             if (h < 3) {
                 char* dst = (char*)(h == 0 ? p.Qq : h == 1 ? p.Kq : p.Ql);
-                stage_and_store<T, false>(
-                    lds, val,
-                    [&](int row, int col) -> char* {
-                        const int m = m0 + row;
-                        return m < M ? dst + ((size_t)m * p.s + c0 + col) * EB : nullptr;
-                    },
-                    acc, wm, wn, lane, tid);
+                G::template store<T, false>(acc, lds, LDS, val, [&](int row, int col) -> char* {
+                    const int m = m0 + row;
+                    return (m < M && col < s) ? dst + ((size_t)m * s + col) * EB : nullptr;
+                });
             } else {
                 char* Klt = (char*)p.Klt;
-                stage_and_store<T, true>(
-                    lds, val,
-                    [&](int frow, int tcol) -> char* {
-                        const int m = m0 + tcol;
-                        if (m >= M) return nullptr;
-                        const int b = m / T_, t = m - b * T_;
-                        return Klt + (((size_t)b * p.s + c0 + frow) * T_ + t) * EB;
-                    },
-                    acc, wm, wn, lane, tid);
+                G::template store<T, true>(acc, lds, LDS, val, [&](int frow, int tcol) -> char* {
+                    const int m = m0 + tcol;
+                    if (m >= M || frow >= s) return nullptr;
+                    const int b = m / T_, t = m - b * T_;
+                    return Klt + (((size_t)b * s + frow) * T_ + t) * EB;
+                });
             }
         }
     }
@@ -138,17 +110,13 @@ __global__ __launch_bounds__(256) void proj_gemm_kernel(ProjParams p) {
 
 template <typename T>
 hipError_t launch(const ProjParams& p, hipStream_t st) {
-    using G = GemmNT<T, BM, BN>;
-    constexpr int EB = Elem<T>::kBytes;
-    constexpr int STAGE_T = BN * (BM * EB + 16);  // transposed staging (largest)
-    constexpr int STAGE_R = BM * (BN * EB + 16);
-    constexpr int LDS = G::LDS_BYTES > STAGE_T ? (G::LDS_BYTES > STAGE_R ? G::LDS_BYTES : STAGE_R)
-                                               : (STAGE_T > STAGE_R ? STAGE_T : STAGE_R);
-    const int n_tiles = (2 * p.e + p.s) / BN;
+    constexpr int LDS = ProjTile<T>::LDS;
+    static_assert(LDS <= 160 * 1024, "projection GEMM LDS over budget");
+    const int ntiles = 2 * (p.e / BN) + 1;
     const int m_tiles = (p.M + BM - 1) / BM;
     hipError_t e = allow_lds(proj_gemm_kernel<T>, LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(proj_gemm_kernel<T>, dim3(n_tiles * m_tiles), dim3(256), LDS, st, p);
+    hipLaunchKernelGGL(proj_gemm_kernel<T>, dim3(ntiles * m_tiles), dim3(512), LDS, st, p);
     return hipGetLastError();
 }
 
