@@ -54,8 +54,11 @@ template <> struct Elem<float> {
     __device__ static __forceinline__ float get(const void* p) { return *(const float*)p; }
 };
 
-// SiLU(x) = x * sigmoid(x) = x / (1 + exp(-x)), evaluated in fp32.
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU(x) = x * sigmoid(x) = x / (1 + exp(-x)), evaluated in fp32 with the
+// hardware exponential and reciprocal (v_exp_f32, v_rcp_f32; about 1 ulp
+// each).  For x below about -88, exp(-x) overflows to +inf and the result is
+// x * 0 = -0, the correctly rounded limit.
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // ------------------------------------------------------------------ MFMA
 

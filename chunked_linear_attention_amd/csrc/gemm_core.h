@@ -302,6 +302,62 @@ struct GemmCore {
         }
     }
 
+    // Store the block tile through LDS with the accumulator's column index as
+    // the staged row: staged element (col, row) = val(row, col, acc).  Each
+    // lane holds four consecutive accumulator rows of one column, so every LDS
+    // write is one packed 4-element store (8 bytes for bf16).  dst(srow, scol)
+    // gives the global address of staged elements (srow, scol..scol+V-1) or
+    // nullptr; the caller picks the operand order so that the staged rows are
+    // the rows of the global layout.  Passes as in store().
+    template <typename OutT, typename V, typename D, typename E = PlainEmit>
+    __device__ static __forceinline__ void store_packed(const f32x16_t (&acc)[MB][NB], char* lds, int lds_bytes,
+                                                        V&& val, D&& dst, E&& emit = E()) {
+        constexpr int EB = Elem<OutT>::kBytes;
+        constexpr int SROWS = BN, SCOLS = BM;
+        constexpr int PITCH = SCOLS * EB + 16;
+        const int npass = SROWS * PITCH <= lds_bytes ? 1 : WGN;
+        const int prows = SROWS / npass;
+        const int wave = threadIdx.x / kWave;
+        const int lane = threadIdx.x % kWave;
+        const int wm = wave / WGN, wn = wave % WGN;
+        const int c = lane & 31;
+        const int h = lane >> 5;
+        constexpr int VPR = SCOLS * EB / 16;
+        for (int pass = 0; pass < npass; ++pass) {
+            __syncthreads();
+            if (npass == 1 || wn == pass) {
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const int row0 = wm * WTM + i * 32 + 8 * g4 + 4 * h;
+                            const int col = wn * WTN + j * 32 + c;
+                            float x[4];
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) x[t] = val(row0 + t, col, acc[i][j][4 * g4 + t]);
+                            char* q = lds + (col - pass * prows) * PITCH + row0 * EB;
+                            if constexpr (EB == 2) {
+                                u32x2_t w;
+                                w.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+                                w.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+                                *(u32x2_t*)q = w;
+                            } else {
+                                *(f32x4_t*)q = f32x4_t{x[0], x[1], x[2], x[3]};
+                            }
+                        }
+            }
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < prows * VPR; idx += NT) {
+                const int srow = idx / VPR;
+                const int v = idx % VPR;
+                char* d = dst(pass * prows + srow, v * (16 / EB));
+                if (d) emit(d, *(const u32x4_t*)(lds + srow * PITCH + v * 16));
+            }
+        }
+    }
+
     // f(row, col, value) for every accumulator element; row/col relative to
     // the block tile.
     template <typename F>

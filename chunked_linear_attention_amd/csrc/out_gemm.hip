@@ -28,27 +28,29 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     extern __shared__ __align__(16) char lds[];
     using G = typename OutTile<T>::G;
     constexpr int EB = Elem<T>::kBytes;
-    const int ntiles = (p.d + BN - 1) / BN;
+    const int ntiles = (p.d + BM - 1) / BM;  // feature tiles (acc rows)
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int nt = bid % ntiles;
     const int mt = bid / ntiles;
-    const int m0 = mt * BM, n0 = nt * BN;
+    const int m0 = mt * BN, n0 = nt * BM;  // token offset, feature offset
     const size_t pitch = (size_t)p.e * EB;
-    const int rows_a = min(BM, p.M - m0);
-    const int rows_b = min(BN, p.d - n0);
+    const int rows_y = min(BN, p.M - m0);
+    const int rows_w = min(BM, p.d - n0);
 
+    // acc = tile^T: rows = output features (W_o^T rows), columns = tokens, so
+    // the packed epilogue writes run along the token-major rows of O.
     f32x16_t acc[G::MB][G::NB];
     G::zero(acc);
-    G::run(acc, (const char*)p.Y + (size_t)m0 * pitch, pitch, rows_a, (const char*)p.W_o + (size_t)n0 * pitch, pitch,
-           rows_b, p.e, lds);
+    G::run(acc, (const char*)p.W_o + (size_t)n0 * pitch, pitch, rows_w, (const char*)p.Y + (size_t)m0 * pitch, pitch,
+           rows_y, p.e, lds);
 
     constexpr int LDS = OutTile<T>::LDS;
     const int M = p.M, d = p.d;
     auto ident = [](int, int, float v) { return v; };
     if (p.residual == nullptr) {
         char* O = (char*)p.O;
-        G::template store<T, false>(acc, lds, LDS, ident, [&](int row, int col) -> char* {
-            const int m = m0 + row, n = n0 + col;
+        G::template store_packed<T>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
+            const int m = m0 + tok, n = n0 + feat;
             return (m < M && n < d) ? O + ((size_t)m * d + n) * EB : nullptr;
         });
     } else {
@@ -56,10 +58,10 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
         // while storing (each 16-byte vector is read and written by one thread).
         float* O = (float*)p.O;
         const float* R = p.residual;
-        G::template store<float, false>(
+        G::template store_packed<float>(
             acc, lds, LDS, ident,
-            [&](int row, int col) -> char* {
-                const int m = m0 + row, n = n0 + col;
+            [&](int tok, int feat) -> char* {
+                const int m = m0 + tok, n = n0 + feat;
                 return (m < M && n < d) ? (char*)(O + (size_t)m * d + n) : nullptr;
             },
             [&](char* dp, const u32x4_t& v) {
@@ -75,7 +77,7 @@ template <typename T>
 hipError_t launch(const OutParams& p, hipStream_t st) {
     constexpr int LDS = OutTile<T>::LDS;
     static_assert(LDS <= 160 * 1024, "output GEMM LDS over budget");
-    const int blocks = ((p.d + BN - 1) / BN) * ((p.M + BM - 1) / BM);
+    const int blocks = ((p.d + BM - 1) / BM) * ((p.M + BN - 1) / BN);
     hipError_t e = allow_lds(out_gemm_kernel<T>, LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(out_gemm_kernel<T>, dim3(blocks), dim3(512), LDS, st, p);

@@ -57,51 +57,62 @@ __global__ __launch_bounds__(512) void proj_gemm_kernel(ProjParams p) {
         section = 2; c0 = 0; w = (const char*)p.W_z; rows_b = p.s;
     }
     const size_t pitch = (size_t)p.d * EB;
-    const int rows_a = min(BM, p.M - m0);
+    const int rows_x = min(BM, p.M - m0);
+    const char* xt = (const char*)p.X + (size_t)m0 * pitch;
+    const char* wt = w + (size_t)c0 * pitch;
 
+    // Operand order per section, so that the accumulator's columns run along
+    // the rows of the stored layout (packed epilogue writes): U and the heads
+    // are token-major, so the weights are the A operand and the tokens the B
+    // operand (acc = tile^T); Vt is feature-major, so the tokens are A.
     f32x16_t acc[G::MB][G::NB];
     G::zero(acc);
-    G::run(acc, (const char*)p.X + (size_t)m0 * pitch, pitch, rows_a, w + (size_t)c0 * pitch, pitch, rows_b, p.d,
-           lds);
+    const bool tok_a = section == 1;
+    G::run(acc, tok_a ? xt : wt, pitch, tok_a ? rows_x : rows_b, tok_a ? wt : xt, pitch, tok_a ? rows_b : rows_x,
+           p.d, lds);
     G::transform(acc, [](int, int, float v) { return silu(v); });
 
     constexpr int LDS = ProjTile<T>::LDS;
     const int M = p.M, T_ = p.T;
     auto ident = [](int, int, float v) { return v; };
     if (section == 0) {
+        // acc rows = features, columns = tokens
         char* U = (char*)p.U;
-        G::template store<T, false>(acc, lds, LDS, ident, [&](int row, int col) -> char* {
-            const int m = m0 + row;
-            return m < M ? U + ((size_t)m * p.e + c0 + col) * EB : nullptr;
+        G::template store_packed<T>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
+            const int m = m0 + tok;
+            return m < M ? U + ((size_t)m * p.e + c0 + feat) * EB : nullptr;
         });
     } else if (section == 1) {
+        // acc rows = tokens, columns = features
         char* Vt = (char*)p.Vt;
-        G::template store<T, true>(acc, lds, LDS, ident, [&](int frow, int tcol) -> char* {
-            const int m = m0 + tcol;
+        G::template store_packed<T>(acc, lds, LDS, ident, [&](int feat, int tok) -> char* {
+            const int m = m0 + tok;
             if (m >= M) return nullptr;
             const int b = m / T_, t = m - b * T_;
-            return Vt + (((size_t)b * p.e + c0 + frow) * T_ + t) * EB;
+            return Vt + (((size_t)b * p.e + c0 + feat) * T_ + t) * EB;
         });
     } else {
-        // head h = Z * gamma[h] + beta[h]; heads 0..2 row-major, head 3 (K_lin) transposed
+        // acc rows = features of Z (s of them valid), columns = tokens.
+        // head h = Z * gamma[h] + beta[h]; heads 0..2 token-major, head 3
+        // (K_lin) feature-major.
         const int s = p.s;
         for (int h = 0; h < 4; ++h) {
             const float* gam = p.scale + h * s;
             const float* bet = p.offset + h * s;
-            auto val = [&](int, int col, float z) { return col < s ? z * gam[col] + bet[col] : 0.f; };
+            auto val = [&](int feat, int, float z) { return feat < s ? z * gam[feat] + bet[feat] : 0.f; };
             if (h < 3) {
                 char* dst = (char*)(h == 0 ? p.Qq : h == 1 ? p.Kq : p.Ql);
-                G::template store<T, false>(acc, lds, LDS, val, [&](int row, int col) -> char* {
-                    const int m = m0 + row;
-                    return (m < M && col < s) ? dst + ((size_t)m * s + col) * EB : nullptr;
+                G::template store_packed<T>(acc, lds, LDS, val, [&](int tok, int feat) -> char* {
+                    const int m = m0 + tok;
+                    return (m < M && feat < s) ? dst + ((size_t)m * s + feat) * EB : nullptr;
                 });
             } else {
                 char* Klt = (char*)p.Klt;
-                G::template store<T, true>(acc, lds, LDS, val, [&](int frow, int tcol) -> char* {
-                    const int m = m0 + tcol;
-                    if (m >= M || frow >= s) return nullptr;
+                G::template store<T, false>(acc, lds, LDS, val, [&](int feat, int tok) -> char* {
+                    const int m = m0 + tok;
+                    if (m >= M || feat >= s) return nullptr;
                     const int b = m / T_, t = m - b * T_;
-                    return Klt + (((size_t)b * s + frow) * T_ + t) * EB;
+                    return Klt + (((size_t)b * s + feat) * T_ + t) * EB;
                 });
             }
         }
