@@ -3,7 +3,7 @@ MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-A step is one full forward of the layer (all five kernels) over one batch of
+A step is one full forward of the layer (all six kernels) over one batch of
 seeded synthetic input, B=2 sequences of T=8192 tokens, d=768, e=1536, s=128,
 chunk C=256, bf16 storage with fp32 accumulation, causal.  Inputs are resident
 in HBM before the timed region starts.  Prints one JSON line.
@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4 SIMDs x 1024 dense bf16 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 METRIC = "GAU/FLASH layer fwd tokens/sec at d=768 T=8192 C=256; % bf16 MFMA peak"
-STAGES = ["proj_gemm", "chunk_state", "chunk_scan", "chunk_attn", "out_gemm"]
+STAGES = ["proj_gemm", "chunk_scores", "chunk_state", "chunk_scan", "chunk_attn", "out_gemm"]
 
 
 def algorithmic_flops(B, T, d, e, s, C, causal=True):
@@ -43,9 +43,10 @@ def algorithmic_flops(B, T, d, e, s, C, causal=True):
     G = T // C
     return {
         "proj_gemm": 2.0 * M * d * (2 * e + s),
+        "chunk_scores": 2.0 * B * G * pairs * s,
         "chunk_state": 2.0 * M * s * e,
         "chunk_scan": 0.0,
-        "chunk_attn": 2.0 * B * G * pairs * (s + e) + 2.0 * M * s * e,
+        "chunk_attn": 2.0 * B * G * pairs * e + 2.0 * M * s * e,
         "out_gemm": 2.0 * M * e * d,
     }
 
@@ -56,11 +57,13 @@ def algorithmic_bytes(B, T, d, e, s, C, causal=True, eb=2):
     G = T // C
     Gp = G if causal else 1
     st = B * G * e * s
+    pairs = C * (C + 1) // 2 if causal else C * C
     return {
         "proj_gemm": M * d * eb + (2 * e + s) * d * eb + M * (2 * e + 4 * s) * eb,
+        "chunk_scores": 2 * M * s * eb + B * G * pairs * eb,
         "chunk_state": M * (e + s) * eb + st * 4,
         "chunk_scan": st * 4 + B * Gp * e * s * eb,
-        "chunk_attn": M * (3 * s + 2 * e) * eb + B * Gp * e * s * eb + M * e * eb,
+        "chunk_attn": B * G * pairs * eb + M * (s + 2 * e) * eb + B * Gp * e * s * eb + M * e * eb,
         "out_gemm": M * e * eb + e * d * eb + M * d * eb,
     }
 
@@ -148,17 +151,17 @@ def main():
         if evs is None:
             g.forward(gc, *args_l, stream=stream)
             return
-        for i in range(5):
+        for i in range(len(STAGES)):
             evs[i].record(stream)
             g.forward_stages(gc, i, i, *args_l, stream=stream)
-        evs[5].record(stream)
+        evs[len(STAGES)].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     K = args.steps
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):

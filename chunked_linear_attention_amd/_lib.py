@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, "libgau.so")
 GAU_F32 = 0
 GAU_BF16 = 1
 
-STAGE_PROJ, STAGE_STATE, STAGE_SCAN, STAGE_ATTN, STAGE_OUT = range(5)
+STAGE_PROJ, STAGE_SCORES, STAGE_STATE, STAGE_SCAN, STAGE_ATTN, STAGE_OUT = range(6)
 
 STATUS = {
     0: "GAU_OK", 1: "GAU_ERR_NULL", 2: "GAU_ERR_SHAPE", 3: "GAU_ERR_ALIGN",
@@ -39,7 +39,7 @@ class GauConfig(ctypes.Structure):
 
 class GauWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("U", "Vt", "Q_quad", "K_quad", "Q_lin", "K_lin_t", "S", "P", "Y", "total")]
+                ("U", "Vt", "Q_quad", "K_quad", "Q_lin", "K_lin_t", "S", "P", "A", "Y", "total")]
 
 
 class GauError(RuntimeError):

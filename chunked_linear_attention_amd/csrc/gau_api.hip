@@ -52,6 +52,7 @@ void layout(const gau_config* c, gau_ws_layout* L) {
     L->K_lin_t = take(M * c->s * eb);
     L->S = take((size_t)c->B * G * es * 4);
     L->P = take((size_t)c->B * Gp * es * eb);
+    L->A = take(M * (size_t)c->C * eb);
     L->Y = take(M * c->e * eb);
     L->total = off;
 }
@@ -102,10 +103,15 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
                 e = gau::launch_chunk_scan(p, bf, st);
                 break;
             }
+            case GAU_STAGE_SCORES: {
+                gau::ScoresParams p{ws + L.Q_quad, ws + L.K_quad, a.relpos, ws + L.A, (int)c->B, (int)c->T,
+                                    (int)c->s, (int)c->C, c->causal ? 1 : 0, c->quad_scale};
+                e = gau::launch_chunk_scores(p, bf, st);
+                break;
+            }
             case GAU_STAGE_ATTN: {
-                gau::AttnParams p{ws + L.Q_quad, ws + L.K_quad, ws + L.Q_lin, ws + L.Vt, ws + L.P, ws + L.U,
-                                  a.relpos, ws + L.Y, (int)c->B, (int)c->T, (int)c->e, (int)c->s, (int)c->C,
-                                  c->causal ? 1 : 0, c->quad_scale};
+                gau::AttnParams p{ws + L.A, ws + L.Q_lin, ws + L.Vt, ws + L.P, ws + L.U, ws + L.Y, (int)c->B,
+                                  (int)c->T, (int)c->e, (int)c->s, (int)c->C, c->causal ? 1 : 0};
                 e = gau::launch_chunk_attn(p, bf, st);
                 break;
             }

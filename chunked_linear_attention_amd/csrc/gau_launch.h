@@ -41,19 +41,29 @@ struct ScanParams {
     int causal;
 };
 
-// Intra-chunk relu^2 attention + linear term + U gate: Y = U * (quad + lin).
-struct AttnParams {
+// Per-chunk attention weights A_g = relu^2(quad_scale Q_quad K_quad^T + Bias),
+// causal-masked, [B*G, C, C] (query-major); causal: only the key tiles at or
+// below the diagonal are written (the consumer reads no others).
+struct ScoresParams {
     const void* Qq;   // [M, s]
     const void* Kq;   // [M, s]
+    const float* relpos;  // [2C-1]
+    void* A;          // [B*G, C, C]
+    int B, T, s, C;
+    int causal;
+    float quad_scale;
+};
+
+// Per chunk: Y = U * (A_g V_g + Q_lin_g P_g), one GEMM with K = keys then s.
+struct AttnParams {
+    const void* A;    // [B*G, C, C]
     const void* Ql;   // [M, s]
     const void* Vt;   // [B, e, T]
     const void* P;    // [B, G or 1, e, s]
     const void* U;    // [M, e]
-    const float* relpos;  // [2C-1]
     void* Y;          // [M, e]
     int B, T, e, s, C;
     int causal;
-    float quad_scale;
 };
 
 // Output projection O = Y W_o (optionally O = residual + Y W_o in fp32).
@@ -76,6 +86,7 @@ struct NormParams {
 hipError_t launch_proj_gemm(const ProjParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_chunk_state(const StateParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_chunk_scan(const ScanParams& p, bool bf16_storage, hipStream_t st);
+hipError_t launch_chunk_scores(const ScoresParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_chunk_attn(const AttnParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_out_gemm(const OutParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_rms_norm(const NormParams& p, bool bf16_storage, hipStream_t st);

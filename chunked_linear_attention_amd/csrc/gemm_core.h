@@ -53,32 +53,47 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
+// One segment of a K-major operand: `chunks` K chunks of 128 bytes starting at
+// `base` (first row of the tile), rows `pitch` bytes apart.
+struct KSeg {
+    const char* base;
+    size_t pitch;
+    int chunks;
+};
+
 // Direct global -> LDS copy of one 128-byte K chunk of a ROWS-row operand
-// tile.  The tile is moved as 1 KiB wave pieces (8 rows); wave w of NW takes
-// pieces w, w + NW, ...  Each lane's source pointer (row clamped to the rows
-// that exist, piece XOR-permuted by the row) is computed once; a chunk only
+// tile whose K axis is the concatenation of two segments (the second may be
+// empty).  The tile is moved as 1 KiB wave pieces (8 rows); wave w of NW takes
+// pieces w, w + NW, ...  Each lane's source pointers (row clamped to the rows
+// that exist, piece XOR-permuted by the row) are computed once; a chunk only
 // adds its K offset.
 template <int ROWS, int NW>
 struct DmaOperand {
     static constexpr int kLoads = ROWS / 8 / NW;
     static_assert(ROWS % (8 * NW) == 0, "pieces must split evenly over the waves");
-    const char* src[kLoads];
+    const char* src0[kLoads];
+    const char* src1[kLoads];
+    int n0;
 
-    __device__ __forceinline__ void init(const char* g, size_t pitch, int rows_valid, int wave, int lane) {
+    __device__ __forceinline__ void init(const KSeg& s0, const KSeg& s1, int rows_valid, int wave, int lane) {
         const int sub = lane >> 3;           // row inside the 8-row piece
         const int piece = (lane & 7) ^ sub;  // logical 16-byte piece this lane fetches
+        n0 = s0.chunks;
 #pragma unroll
         for (int jj = 0; jj < kLoads; ++jj) {
             int r = (wave + jj * NW) * 8 + sub;
             r = r < rows_valid ? r : rows_valid - 1;
-            src[jj] = g + (size_t)r * pitch + piece * 16;
+            src0[jj] = s0.base + (size_t)r * s0.pitch + piece * 16;
+            src1[jj] = s1.base + (size_t)r * s1.pitch + piece * 16;
         }
     }
     // Issue the copy of K chunk `kc` into `lds_tile`.
     __device__ __forceinline__ void issue(char* lds_tile, int kc, int wave) const {
+        const bool first = kc < n0;
+        const size_t off = (size_t)(first ? kc : kc - n0) * 128;
 #pragma unroll
         for (int jj = 0; jj < kLoads; ++jj)
-            __builtin_amdgcn_global_load_lds((glb_ptr_t)(src[jj] + (size_t)kc * 128),
+            __builtin_amdgcn_global_load_lds((glb_ptr_t)((first ? src0[jj] : src1[jj]) + off),
                                              (lds_ptr_t)(lds_tile + (wave + jj * NW) * 1024), 16, 0, 0);
     }
 };
@@ -184,24 +199,25 @@ struct GemmCore {
         step<3, ISSUE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh);
     }
 
-    // acc += A . B^T over K elements (a multiple of KELEMS).  Double-buffered
-    // LDS stages; one barrier per chunk, after the wave's copy of the next
-    // chunk has landed.
-    __device__ static __forceinline__ void run(f32x16_t (&acc)[MB][NB], const char* __restrict__ a,
-                                               size_t pitch_a, int rows_a, const char* __restrict__ b,
-                                               size_t pitch_b, int rows_b, int K, char* lds) {
+    // acc += A . B^T where A's and B's K axes are the concatenations
+    // a0|a1 and b0|b1 (a0.chunks == b0.chunks, a1.chunks == b1.chunks).
+    // Double-buffered LDS stages; one barrier per chunk, after the wave's copy
+    // of the next chunk has landed.  Ends with a barrier (LDS free).
+    __device__ static __forceinline__ void run_segs(f32x16_t (&acc)[MB][NB], const KSeg& a0, const KSeg& a1,
+                                                    int rows_a, const KSeg& b0, const KSeg& b1, int rows_b,
+                                                    char* lds) {
         const int tid = threadIdx.x;
         const int wave = tid / kWave;
         const int lane = tid % kWave;
         const int wm = wave / WGN, wn = wave % WGN;
-        const int nk = K / KELEMS;
+        const int nk = a0.chunks + a1.chunks;
         const int fr = lane & 31;  // fragment row
         const int fh = lane >> 5;  // fragment K half
 
         DmaOperand<BM, NW> da;
         DmaOperand<BN, NW> db;
-        da.init(a, pitch_a, rows_a, wave, lane);
-        db.init(b, pitch_b, rows_b, wave, lane);
+        da.init(a0, a1, rows_a, wave, lane);
+        db.init(b0, b1, rows_b, wave, lane);
         da.issue(lds, 0, wave);
         db.issue(lds + A_BYTES, 0, wave);
         wait_vmcnt<0>();
@@ -224,6 +240,37 @@ struct GemmCore {
             chunk<false>(acc, fa, fb, cur + oa, cur + ob, da, db, nullptr, 0, wave, fr, fh);
         }
         __syncthreads();  // LDS free for the epilogue
+    }
+
+    // acc += A . B^T over K elements (a multiple of KELEMS), one segment each.
+    __device__ static __forceinline__ void run(f32x16_t (&acc)[MB][NB], const char* a, size_t pitch_a, int rows_a,
+                                               const char* b, size_t pitch_b, int rows_b, int K, char* lds) {
+        const int nk = K / KELEMS;
+        run_segs(acc, KSeg{a, pitch_a, nk}, KSeg{a, pitch_a, 0}, rows_a, KSeg{b, pitch_b, nk}, KSeg{b, pitch_b, 0},
+                 rows_b, lds);
+    }
+
+    // Apply f4(row0, col, v) to groups of four consecutive accumulator rows of
+    // one column (the elements a lane holds together); v is modified in place.
+    template <typename F>
+    __device__ static __forceinline__ void transform4(f32x16_t (&acc)[MB][NB], F&& f4) {
+        const int wave = threadIdx.x / kWave;
+        const int lane = threadIdx.x % kWave;
+        const int wm = wave / WGN, wn = wave % WGN;
+        const int c = lane & 31;
+        const int h = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    float v[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                                  acc[i][j][4 * g4 + 3]};
+                    f4(wm * WTM + i * 32 + 8 * g4 + 4 * h, wn * WTN + j * 32 + c, v);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) acc[i][j][4 * g4 + t] = v[t];
+                }
     }
 
     // Apply f to every accumulator element in place: acc = f(row, col, acc).

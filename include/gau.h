@@ -95,11 +95,15 @@ typedef struct {
  *   K_lin_t [B, s, T]     dt    K_lin transposed per sequence
  *   S       [B, G, e, s]  fp32  S_g transposed (element (b,g,c,k) = S_g[k][c])
  *   P       [B, G', e, s] dt    P_g transposed; G' = G if causal, else 1
+ *   A       [B*G, C, C]   dt    per-chunk attention weights
+ *                               relu^2(quad_scale Q_quad K_quad^T + Bias), masked,
+ *                               query-major; causal: key blocks above the diagonal
+ *                               (128 wide, 64 when C = 64) are not written
  *   Y       [B*T, e]      dt    U * (V_quad + V_lin)
  *   total   bytes needed (== gau_workspace_bytes)
  */
 typedef struct {
-    size_t U, Vt, Q_quad, K_quad, Q_lin, K_lin_t, S, P, Y, total;
+    size_t U, Vt, Q_quad, K_quad, Q_lin, K_lin_t, S, P, A, Y, total;
 } gau_ws_layout;
 
 /* Workspace bytes gau_forward needs for cfg (0 if cfg is invalid). */
@@ -130,29 +134,31 @@ gau_status gau_forward(const gau_config* cfg,
                        void* O, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The five kernels gau_forward queues, in order.  gau_forward_stages runs a
+ * The six kernels gau_forward queues, in order.  gau_forward_stages runs a
  * contiguous range of them (for stage-wise tests and per-kernel timing); the
  * stages communicate only through the workspace.
  *   GAU_STAGE_PROJ   U, Vt, Q_quad, K_quad, Q_lin, K_lin_t from X (SiLU projection
  *                    and the four scale+offset heads; wikillm "Method", Su's post
  *                    "Gated Attention" and "Weak Attention")
+ *   GAU_STAGE_SCORES A_g = relu^2(quad_scale Q_quad K_quad^T + Bias), causal-masked,
+ *                    per chunk (wikillm "Method" step 1, eq. 5; papercache appendix D, Code 4)
  *   GAU_STAGE_STATE  S_g = lin_scale * K_lin_g^T V_g for every chunk (eq. 7-8)
  *   GAU_STAGE_SCAN   P_g = exclusive prefix over chunks (causal, eq. 8) or total (eq. 7)
- *   GAU_STAGE_ATTN   Y = U * (relu^2(quad_scale Q_quad K_quad^T + Bias) V + Q_lin P)
- *                    per chunk (wikillm "Method" steps 1-4; papercache appendix D, Code 4)
+ *   GAU_STAGE_ATTN   Y = U * (A_g V_g + Q_lin P_g) per chunk (wikillm "Method" steps 2-4)
  *   GAU_STAGE_OUT    O = Y W_o
  * Arguments, checks and status codes as gau_forward (every pointer is
  * checked, also those the selected stages do not read).  A stage reads the
  * workspace regions earlier stages wrote, so a range that does not start at
  * GAU_STAGE_PROJ needs them there already.  first > last or a stage number
- * outside 0..4 gives GAU_ERR_SHAPE.
+ * outside 0..5 gives GAU_ERR_SHAPE.
  */
 enum {
     GAU_STAGE_PROJ = 0,
-    GAU_STAGE_STATE = 1,
-    GAU_STAGE_SCAN = 2,
-    GAU_STAGE_ATTN = 3,
-    GAU_STAGE_OUT = 4
+    GAU_STAGE_SCORES = 1,
+    GAU_STAGE_STATE = 2,
+    GAU_STAGE_SCAN = 3,
+    GAU_STAGE_ATTN = 4,
+    GAU_STAGE_OUT = 5
 };
 
 gau_status gau_forward_stages(const gau_config* cfg, int first_stage, int last_stage,

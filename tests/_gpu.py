@@ -26,7 +26,7 @@ def run_layer(inp, B, T, d, e, s, C, causal, dtype, quad_scale=None, lin_scale=N
     dev = g.device_layer(inp, tdt)
     cfg = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32,
                         quad_scale, lin_scale)
-    ws = torch.empty(g.workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(g.workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
     O = torch.empty((B, T, d), dtype=tdt, device="cuda")
     g.forward(cfg, dev["X"], dev["W_u"], dev["W_v"], dev["W_z"], dev["W_o"], dev["scale"],
               dev["offset"], dev["relpos"], O, ws, stream)

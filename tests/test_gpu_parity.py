@@ -34,6 +34,14 @@ def _stagewise(ws, L, im, B, T, e, s, C, causal, dtype):
         assert np.all(P[:, 0] == 0.0), "P_0 must be exactly zero"
     if np.max(np.abs(refP)) > 0:
         assert_close(P, refP, tol, "P")
+    A = ws_array(ws, L, "A", (B * G, C, C), dtype)
+    refA = im["kernel"].reshape(B * G, C, C)
+    if causal:  # key tiles above the diagonal are not written (and not read)
+        ts = 128 if C >= 128 else 64
+        t = np.arange(C) // ts
+        keep = t[None, :] <= t[:, None]
+        A, refA = A[:, keep], refA[:, keep]
+    assert_close(A, refA, tol, "A")
     assert_close(ws_array(ws, L, "Y", (B, T, e), dtype), im["Y"], tol, "Y")
 
 
