@@ -4,29 +4,31 @@
 // epilogue also adds the layer's shortcut in fp32 (the skip connection the
 // listings add after each block: wikillm, FLASH block pseudocode).
 //
-// An NT GEMM on the shared core: A = Y [M, e], B = W_o^T [d, e], K = e,
-// 256 x 256 output tiles (d need only be a multiple of 128: the last column
-// tile may be half full).
+// An NT GEMM on the shared core, K = e: A operand = W_o^T rows (output
+// features), B operand = Y rows (tokens).  Tiles are BF features x 256 tokens
+// with BF chosen per d (256, 192 or 128, dividing d) so that the grid is as
+// close as possible to whole rounds over the 256 CUs: d = 768 takes 192, which
+// gives 4 x 64 = 256 blocks at B*T = 16384.
 #include "gau_launch.h"
 #include "gemm_core.h"
 
 namespace gau {
 namespace {
 
-constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4;
+constexpr int BN = 256, WGM = 2, WGN = 4;  // tokens per tile, wave grid
 
-template <typename T>
+template <typename T, int BM>
 struct OutTile {
     using G = GemmCore<T, BM, BN, WGM, WGN>;
-    // fp32 staging (residual output or fp32 layer) in two passes of 128 rows
-    static constexpr int STAGE = BM / WGM * (BN * 4 + 16);
+    // staging of one pass of the epilogue in the worst case (fp32, WGN passes)
+    static constexpr int STAGE = BN / WGN * (BM * 4 + 16);
     static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
 };
 
-template <typename T>
+template <typename T, int BM>
 __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     extern __shared__ __align__(16) char lds[];
-    using G = typename OutTile<T>::G;
+    using G = typename OutTile<T, BM>::G;
     constexpr int EB = Elem<T>::kBytes;
     const int ntiles = (p.d + BM - 1) / BM;  // feature tiles (acc rows)
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     G::run(acc, (const char*)p.W_o + (size_t)n0 * pitch, pitch, rows_w, (const char*)p.Y + (size_t)m0 * pitch, pitch,
            rows_y, p.e, lds);
 
-    constexpr int LDS = OutTile<T>::LDS;
+    constexpr int LDS = OutTile<T, BM>::LDS;
     const int M = p.M, d = p.d;
     auto ident = [](int, int, float v) { return v; };
     if (p.residual == nullptr) {
@@ -73,21 +75,49 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     }
 }
 
-template <typename T>
+template <typename T, int BM>
 hipError_t launch(const OutParams& p, hipStream_t st) {
-    constexpr int LDS = OutTile<T>::LDS;
+    constexpr int LDS = OutTile<T, BM>::LDS;
     static_assert(LDS <= 160 * 1024, "output GEMM LDS over budget");
     const int blocks = ((p.d + BM - 1) / BM) * ((p.M + BN - 1) / BN);
-    hipError_t e = allow_lds(out_gemm_kernel<T>, LDS);
+    hipError_t e = allow_lds(out_gemm_kernel<T, BM>, LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(out_gemm_kernel<T>, dim3(blocks), dim3(512), LDS, st, p);
+    hipLaunchKernelGGL((out_gemm_kernel<T, BM>), dim3(blocks), dim3(512), LDS, st, p);
     return hipGetLastError();
+}
+
+// Feature-tile width for d: the candidate (dividing d) with the least
+// rounds-times-tile-width over 256 CUs, the larger tile on ties.
+int feature_tile(int d, int M) {
+    const int cand[3] = {256, 192, 128};
+    int best = 128;
+    long best_cost = -1;
+    const int mt = (M + BN - 1) / BN;
+    for (int bf : cand) {
+        if (d % bf) continue;
+        const long blocks = (long)(d / bf) * mt;
+        const long cost = (blocks + 255) / 256 * bf;
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = bf;
+        }
+    }
+    return best;
+}
+
+template <typename T>
+hipError_t dispatch(const OutParams& p, hipStream_t st) {
+    switch (feature_tile(p.d, p.M)) {
+        case 256: return launch<T, 256>(p, st);
+        case 192: return launch<T, 192>(p, st);
+        default: return launch<T, 128>(p, st);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_out_gemm(const OutParams& p, bool bf16_storage, hipStream_t st) {
-    return bf16_storage ? launch<bf16>(p, st) : launch<float>(p, st);
+    return bf16_storage ? dispatch<bf16>(p, st) : dispatch<float>(p, st);
 }
 
 }  // namespace gau

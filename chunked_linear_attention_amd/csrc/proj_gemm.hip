@@ -14,10 +14,12 @@
 //   kernels read tokens contiguously); Q_quad, K_quad, Q_lin [M, s] row-major;
 //   K_lin_t [B, s, T] transposed.  M = B*T.
 //
-// Tiling: 256 x 256 output tiles (GemmCore, 8 waves), the tiles of each
-// section (U: e/256, V: e/256, Z: one tile of s <= 256 columns) laid side by
-// side along N; tiles are assigned to XCDs in contiguous ranges.  A block's
-// columns lie in exactly one section, so its epilogue branch is uniform.
+// Two kernels on the shared MFMA core: U and V with 256 x 256 tiles (the
+// e/256 tiles of each section side by side along N, so a block's columns lie
+// in one section and its epilogue branch is uniform), and Z with its four
+// heads with 128 x 128 tiles (s is small, and a separate launch keeps the U/V
+// grid a whole number of rounds over the 256 CUs for the usual widths).
+// Tiles are assigned to XCDs in contiguous ranges.
 #include "gau_launch.h"
 #include "gemm_core.h"
 
@@ -36,53 +38,45 @@ struct ProjTile {
     static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
 };
 
+// U and V: 256 x 256 tiles; the e/256 tiles of U and of V side by side.
 template <typename T>
-__global__ __launch_bounds__(512) void proj_gemm_kernel(ProjParams p) {
+__global__ __launch_bounds__(512) void proj_uv_kernel(ProjParams p) {
     extern __shared__ __align__(16) char lds[];
     using G = typename ProjTile<T>::G;
     constexpr int EB = Elem<T>::kBytes;
-    const int ntu = p.e / BN;              // tiles per U or V section
-    const int ntiles = 2 * ntu + 1;        // + one Z tile
+    const int ntu = p.e / BN;  // tiles per section
+    const int ntiles = 2 * ntu;
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int nt = bid % ntiles;
     const int mt = bid / ntiles;
     const int m0 = mt * BM;
-    int section, c0, rows_b;
-    const char* w;
-    if (nt < ntu) {
-        section = 0; c0 = nt * BN; w = (const char*)p.W_u; rows_b = BN;
-    } else if (nt < 2 * ntu) {
-        section = 1; c0 = (nt - ntu) * BN; w = (const char*)p.W_v; rows_b = BN;
-    } else {
-        section = 2; c0 = 0; w = (const char*)p.W_z; rows_b = p.s;
-    }
+    const bool is_v = nt >= ntu;
+    const int c0 = (is_v ? nt - ntu : nt) * BN;
     const size_t pitch = (size_t)p.d * EB;
     const int rows_x = min(BM, p.M - m0);
     const char* xt = (const char*)p.X + (size_t)m0 * pitch;
-    const char* wt = w + (size_t)c0 * pitch;
+    const char* wt = (const char*)(is_v ? p.W_v : p.W_u) + (size_t)c0 * pitch;
 
     // Operand order per section, so that the accumulator's columns run along
-    // the rows of the stored layout (packed epilogue writes): U and the heads
-    // are token-major, so the weights are the A operand and the tokens the B
-    // operand (acc = tile^T); Vt is feature-major, so the tokens are A.
+    // the rows of the stored layout (packed epilogue writes): U is token-major,
+    // so the weights are the A operand and the tokens the B operand
+    // (acc = tile^T); Vt is feature-major, so the tokens are A.
     f32x16_t acc[G::MB][G::NB];
     G::zero(acc);
-    const bool tok_a = section == 1;
-    G::run(acc, tok_a ? xt : wt, pitch, tok_a ? rows_x : rows_b, tok_a ? wt : xt, pitch, tok_a ? rows_b : rows_x,
-           p.d, lds);
+    G::run(acc, is_v ? xt : wt, pitch, is_v ? rows_x : BN, is_v ? wt : xt, pitch, is_v ? BN : rows_x, p.d, lds);
     G::transform(acc, [](int, int, float v) { return silu(v); });
 
     constexpr int LDS = ProjTile<T>::LDS;
     const int M = p.M, T_ = p.T;
     auto ident = [](int, int, float v) { return v; };
-    if (section == 0) {
+    if (!is_v) {
         // acc rows = features, columns = tokens
         char* U = (char*)p.U;
         G::template store_packed<T>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
             const int m = m0 + tok;
             return m < M ? U + ((size_t)m * p.e + c0 + feat) * EB : nullptr;
         });
-    } else if (section == 1) {
+    } else {
         // acc rows = tokens, columns = features
         char* Vt = (char*)p.Vt;
         G::template store_packed<T>(acc, lds, LDS, ident, [&](int feat, int tok) -> char* {
@@ -91,50 +85,97 @@ __global__ __launch_bounds__(512) void proj_gemm_kernel(ProjParams p) {
             const int b = m / T_, t = m - b * T_;
             return Vt + (((size_t)b * p.e + c0 + feat) * T_ + t) * EB;
         });
-    } else {
-        // acc rows = features of Z (s of them valid), columns = tokens.
-        // head h = Z * gamma[h] + beta[h]; heads 0..2 token-major, head 3
-        // (K_lin) feature-major.
-        const int s = p.s;
-        for (int h = 0; h < 4; ++h) {
-            const float* gam = p.scale + h * s;
-            const float* bet = p.offset + h * s;
-            auto val = [&](int feat, int, float z) { return feat < s ? z * gam[feat] + bet[feat] : 0.f; };
-            if (h < 3) {
-                char* dst = (char*)(h == 0 ? p.Qq : h == 1 ? p.Kq : p.Ql);
-                G::template store_packed<T>(acc, lds, LDS, val, [&](int tok, int feat) -> char* {
-                    const int m = m0 + tok;
-                    return (m < M && feat < s) ? dst + ((size_t)m * s + feat) * EB : nullptr;
-                });
-            } else {
-                char* Klt = (char*)p.Klt;
-                G::template store<T, false>(acc, lds, LDS, val, [&](int feat, int tok) -> char* {
-                    const int m = m0 + tok;
-                    if (m >= M || feat >= s) return nullptr;
-                    const int b = m / T_, t = m - b * T_;
-                    return Klt + (((size_t)b * s + feat) * T_ + t) * EB;
-                });
-            }
+    }
+}
+
+// Z = SiLU(X W_z) and its four heads: 128 x 128 tiles (features x tokens).
+constexpr int ZF = 128, ZT = 128;
+
+template <typename T>
+struct ZTile {
+    using G = GemmCore<T, ZF, ZT, 2, 2>;
+    static constexpr int EB = Elem<T>::kBytes;
+    static constexpr int STAGE = ZT * (ZF * EB + 16) > ZF * (ZT * EB + 16) ? ZT * (ZF * EB + 16)
+                                                                          : ZF * (ZT * EB + 16);
+    static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void proj_z_kernel(ProjParams p) {
+    extern __shared__ __align__(16) char lds[];
+    using G = typename ZTile<T>::G;
+    constexpr int EB = Elem<T>::kBytes;
+    const int nf = p.s / ZF;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int ft = bid % nf;
+    const int mt = bid / nf;
+    const int m0 = mt * ZT, f0 = ft * ZF;
+    const size_t pitch = (size_t)p.d * EB;
+    const int rows_x = min(ZT, p.M - m0);
+
+    // acc rows = features of Z, columns = tokens
+    f32x16_t acc[G::MB][G::NB];
+    G::zero(acc);
+    G::run(acc, (const char*)p.W_z + (size_t)f0 * pitch, pitch, ZF, (const char*)p.X + (size_t)m0 * pitch, pitch,
+           rows_x, p.d, lds);
+    G::transform(acc, [](int, int, float v) { return silu(v); });
+
+    // head h = Z * gamma[h] + beta[h]; heads 0..2 token-major, head 3 (K_lin)
+    // feature-major
+    constexpr int LDS = ZTile<T>::LDS;
+    const int M = p.M, T_ = p.T, s = p.s;
+    for (int h = 0; h < 4; ++h) {
+        const float* gam = p.scale + h * s + f0;
+        const float* bet = p.offset + h * s + f0;
+        auto val = [&](int feat, int, float z) { return z * gam[feat] + bet[feat]; };
+        if (h < 3) {
+            char* dst = (char*)(h == 0 ? p.Qq : h == 1 ? p.Kq : p.Ql);
+            G::template store_packed<T>(acc, lds, LDS, val, [&](int tok, int feat) -> char* {
+                const int m = m0 + tok;
+                return m < M ? dst + ((size_t)m * s + f0 + feat) * EB : nullptr;
+            });
+        } else {
+            char* Klt = (char*)p.Klt;
+            G::template store<T, false>(acc, lds, LDS, val, [&](int feat, int tok) -> char* {
+                const int m = m0 + tok;
+                if (m >= M) return nullptr;
+                const int b = m / T_, t = m - b * T_;
+                return Klt + (((size_t)b * s + f0 + feat) * T_ + t) * EB;
+            });
         }
     }
 }
 
 template <typename T>
-hipError_t launch(const ProjParams& p, hipStream_t st) {
+hipError_t launch_z(const ProjParams& p, hipStream_t st) {
+    constexpr int LDS = ZTile<T>::LDS;
+    static_assert(LDS <= 160 * 1024, "Z projection LDS over budget");
+    const int blocks = (p.s / ZF) * ((p.M + ZT - 1) / ZT);
+    hipError_t e = allow_lds(proj_z_kernel<T>, LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(proj_z_kernel<T>, dim3(blocks), dim3(256), LDS, st, p);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_uv(const ProjParams& p, hipStream_t st) {
     constexpr int LDS = ProjTile<T>::LDS;
     static_assert(LDS <= 160 * 1024, "projection GEMM LDS over budget");
-    const int ntiles = 2 * (p.e / BN) + 1;
-    const int m_tiles = (p.M + BM - 1) / BM;
-    hipError_t e = allow_lds(proj_gemm_kernel<T>, LDS);
+    const int blocks = 2 * (p.e / BN) * ((p.M + BM - 1) / BM);
+    hipError_t e = allow_lds(proj_uv_kernel<T>, LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(proj_gemm_kernel<T>, dim3(ntiles * m_tiles), dim3(512), LDS, st, p);
+    hipLaunchKernelGGL(proj_uv_kernel<T>, dim3(blocks), dim3(512), LDS, st, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_proj_gemm(const ProjParams& p, bool bf16_storage, hipStream_t st) {
-    return bf16_storage ? launch<bf16>(p, st) : launch<float>(p, st);
+hipError_t launch_proj_z(const ProjParams& p, bool bf16_storage, hipStream_t st) {
+    return bf16_storage ? launch_z<bf16>(p, st) : launch_z<float>(p, st);
+}
+
+hipError_t launch_proj_uv(const ProjParams& p, bool bf16_storage, hipStream_t st) {
+    return bf16_storage ? launch_uv<bf16>(p, st) : launch_uv<float>(p, st);
 }
 
 }  // namespace gau
