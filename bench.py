@@ -2,6 +2,9 @@
 MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--copy-calibration]
+    python bench.py --summarize-stats STATS_CSV --command CMD --out FILE.md
+    python bench.py --summarize-traffic FETCH_CSV WRITE_CSV --command CMD
 
 A step is one full forward of the layer (all six kernels) over one batch of
 seeded synthetic input, B=2 sequences of T=8192 tokens, d=768, e=1536, s=128,
@@ -109,7 +112,7 @@ def blas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(cfg, inp, min_s=10.0, max_passes=20):
+def cpu_baseline(cfg, inp, min_s=12.0, max_passes=100):
     """The float64 oracle, as it stands, on the host cores: whole sequences of
     the timed workload, one after another, repeated until at least min_s of
     CPU work has been timed."""
@@ -129,13 +132,112 @@ def cpu_baseline(cfg, inp, min_s=10.0, max_passes=20):
                       f"timed workload), float64 numpy, {dt:.1f} s"}
 
 
+# Size of the calibration copy (bytes read = bytes written).
+COPY_BYTES = 256 << 20
+PROFILE_TAG = "B2_T8192_d768_C256"
+
+
+def copy_calibration(torch):
+    """Three plain device-to-device copies of COPY_BYTES (torch's copy_ of a
+    contiguous tensor runs the HIP runtime's copyBuffer blit kernel): the HBM
+    counters of a kernel whose traffic is known exactly."""
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _short(name):
+    n = name.replace("void gau::(anonymous namespace)::", "")
+    return n.split("(")[0]
+
+
+def summarize_stats(csv_path, command, out):
+    """Markdown summary of a rocprofv3 --stats kernel table."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = ["# rocprofv3 kernel statistics: FLASH layer forward, B=2 T=8192 d=768 e=1536 s=128 C=256, "
+             "bf16, causal", "", "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---:|---:|---:|---:|---:|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _counter_rows(csv_path, counter):
+    """(kernel name, grid size, value) per dispatch from a rocprofv3 --pmc csv."""
+    import csv
+    return [(r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]))
+            for r in csv.DictReader(open(csv_path)) if r["Counter_Name"] == counter]
+
+
+def summarize_traffic(fetch_csv, write_csv, command):
+    """HBM bytes per launch of the dominant kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by the reading of the same
+    counter for the calibration copy of COPY_BYTES."""
+    out = {}
+    for csv_path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        rows = _counter_rows(csv_path, counter)
+        blits = [r for r in rows if r[0] == "__amd_rocclr_copyBuffer"]
+        big = max(g for _, g, _ in blits) if blits else 0
+        copy = [v for _, g, v in blits if g == big]
+        dom = [v for k, _, v in rows if f"{DOMINANT}_kernel<gau::bf16>" in k]
+        if len(copy) != 3 or not dom:
+            raise SystemExit(f"{csv_path}: expected 3 calibration copies and {DOMINANT} dispatches")
+        kib_copy, kib_dom = sum(copy) / len(copy), sum(dom) / len(dom)
+        factor = kib_copy * 1024.0 / COPY_BYTES  # counter bytes per true byte
+        out[counter] = {"kib_per_dispatch": kib_dom, "copy_kib_per_dispatch": kib_copy,
+                        "scale": factor, "bytes_per_launch": kib_dom * 1024.0 / factor,
+                        "dispatches": len(dom)}
+    total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    cfg = dict(B=2, T=8192, d=768, e=1536, s=128, C=256)
+    algo = algorithmic_bytes(**cfg)[DOMINANT]
+    rec = {"kernel": DOMINANT, "workload": "layer_bf16_" + PROFILE_TAG, "source_sha256_16": source_hash(DOMINANT),
+           "hbm_bytes_per_launch": total, "algorithmic_bytes_per_launch": algo, "counters": out,
+           "calibration": f"torch device copy of {COPY_BYTES} bytes (read {COPY_BYTES}, write {COPY_BYTES})",
+           "command": command}
+    base = os.path.join(ROOT, "profiles", f"{DOMINANT}_{PROFILE_TAG}_traffic")
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# HBM traffic of `{DOMINANT}` (U/V projection GEMM), FLASH layer B=2 T=8192 d=768 e=1536 "
+             "s=128 C=256, bf16", "", "Commands (from the repository root, one MI355X; one counter per run):",
+             "", "```", command, "```", "",
+             "| counter | KiB / dispatch | calibration copy KiB / dispatch | scale (counter B per true B) | "
+             "bytes / launch |", "|---|---:|---:|---:|---:|"]
+    for c, v in out.items():
+        lines.append(f"| {c} | {v['kib_per_dispatch']:.0f} | {v['copy_kib_per_dispatch']:.0f} | "
+                     f"{v['scale']:.4f} | {v['bytes_per_launch'] / 1e6:.2f} MB |")
+    lines += ["", f"Total {total / 1e6:.2f} MB per launch against {algo / 1e6:.2f} MB algorithmic "
+              f"(ratio {total / algo:.2f}).", ""]
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the measurement, run the copy that calibrates the HBM counters")
+    ap.add_argument("--summarize-stats", metavar="STATS_CSV")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--command", default="")
+    ap.add_argument("--out")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.command, args.out)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.command)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
@@ -243,7 +345,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp)
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
+    if args.copy_calibration:
+        copy_calibration(torch)
 
 
 if __name__ == "__main__":

@@ -92,7 +92,7 @@ hipError_t launch_t(const AttnParams& p, hipStream_t st) {
     constexpr int LDS = AttnTile<T, BQ>::LDS;
     static_assert(LDS <= 160 * 1024, "chunk kernel LDS over budget");
     const int blocks = (p.e / BF) * (p.C / BQ) * p.B * (p.T / p.C);
-    hipError_t e = allow_lds(chunk_attn_kernel<T, BQ>, LDS);
+    hipError_t e = allow_lds<chunk_attn_kernel<T, BQ>>(LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_attn_kernel<T, BQ>), dim3(blocks), dim3(256), LDS, st, p);
     return hipGetLastError();

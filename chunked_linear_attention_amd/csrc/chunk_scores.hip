@@ -76,7 +76,7 @@ hipError_t launch_t(const ScoresParams& p, hipStream_t st) {
     const int nt = p.C / TS;
     const int npairs = p.causal ? nt * (nt + 1) / 2 : nt * nt;
     const int blocks = npairs * p.B * (p.T / p.C);
-    hipError_t e = allow_lds(chunk_scores_kernel<T, TS>, LDS);
+    hipError_t e = allow_lds<chunk_scores_kernel<T, TS>>(LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_scores_kernel<T, TS>), dim3(blocks), dim3(256), LDS, st, p);
     return hipGetLastError();

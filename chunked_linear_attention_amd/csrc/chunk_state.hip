@@ -59,7 +59,7 @@ hipError_t launch(const StateParams& p, hipStream_t st) {
     constexpr int LDS = StateTile<T>::LDS;
     static_assert(LDS <= 160 * 1024, "state GEMM LDS over budget");
     const int blocks = (p.e / BE) * (p.s / BS) * p.B * (p.T / p.C);
-    hipError_t e = allow_lds(chunk_state_kernel<T>, LDS);
+    hipError_t e = allow_lds<chunk_state_kernel<T>>(LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(chunk_state_kernel<T>, dim3(blocks), dim3(256), LDS, st, p);
     return hipGetLastError();

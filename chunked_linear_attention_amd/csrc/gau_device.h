@@ -216,11 +216,12 @@ __device__ __forceinline__ void for_each_acc(const f32x4_t (&acc)[MB][NB], int l
             for (int r = 0; r < 4; ++r) f(i * 16 + 4 * q + r, j * 16 + c, acc[i][j][r]);
 }
 
-// Allow a kernel more than the default dynamic LDS (once per instantiation).
-template <typename K>
-inline hipError_t allow_lds(K kernel, int bytes) {
+// Allow kernel `Kernel` more than the default dynamic LDS (the attribute is set
+// once per kernel).
+template <auto Kernel>
+inline hipError_t allow_lds(int bytes) {
     static const hipError_t err =
-        hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        hipFuncSetAttribute((const void*)Kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     return err;
 }
 

@@ -8,11 +8,17 @@
 //    the WGM x WGN waves owns a (BM/WGM) x (BN/WGN) sub-tile.
 //  * K advances in chunks of 128 bytes (64 bf16 / 32 fp32).  Global memory is
 //    copied straight into LDS with global_load_lds_dwordx4 (no VGPR staging),
-//    double-buffered: the copy of chunk k+1 is in flight while chunk k is
-//    multiplied, and one barrier per chunk separates the two.
+//    through a ring of NS stages (NS = 2 for the large tiles, more for small
+//    tiles whose blocks would otherwise wait on one copy at a time): the
+//    copies of the next NS-1 chunks are in flight while one chunk is
+//    multiplied, and one barrier per chunk separates them.
 //  * LDS rows are 128 bytes without padding; the eight 16-byte pieces of row r
-//    are stored XOR-permuted by (r & 7), so the 32 rows read by one MFMA
-//    fragment load hit distinct banks, and every wave's direct copy still
+//    are stored XOR-permuted by ((r >> 1) & 7).  The LDS serves a 16-byte
+//    read for 16 lanes per cycle (a 256-byte bank window, two rows), so the
+//    16 rows a fragment load touches per cycle must fall in distinct bank
+//    groups: the pair of rows sharing a window differs in r & 1, and the
+//    eight pairs differ in (r >> 1) & 7 (measured on gfx950: 188 B/clk/CU
+//    against 117 for an (r & 7) permutation).  Every wave's direct copy still
 //    writes 1 KiB of consecutive LDS (the permutation is applied to the global
 //    addresses instead).
 //
@@ -76,13 +82,13 @@ struct DmaOperand {
     int n0;
 
     __device__ __forceinline__ void init(const KSeg& s0, const KSeg& s1, int rows_valid, int wave, int lane) {
-        const int sub = lane >> 3;           // row inside the 8-row piece
-        const int piece = (lane & 7) ^ sub;  // logical 16-byte piece this lane fetches
+        const int sub = lane >> 3;  // row inside the 8-row piece
         n0 = s0.chunks;
 #pragma unroll
         for (int jj = 0; jj < kLoads; ++jj) {
-            int r = (wave + jj * NW) * 8 + sub;
-            r = r < rows_valid ? r : rows_valid - 1;
+            const int row = (wave + jj * NW) * 8 + sub;
+            const int piece = (lane & 7) ^ ((row >> 1) & 7);  // logical 16-byte piece this lane fetches
+            const int r = row < rows_valid ? row : rows_valid - 1;
             src0[jj] = s0.base + (size_t)r * s0.pitch + piece * 16;
             src1[jj] = s1.base + (size_t)r * s1.pitch + piece * 16;
         }
@@ -109,9 +115,9 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 }
 
 // LDS byte offset of logical 16-byte piece c of row r in a swizzled tile.
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-template <typename T, int BM, int BN, int WGM, int WGN>
+template <typename T, int BM, int BN, int WGM, int WGN, int NS = 2>
 struct GemmCore {
     static constexpr int NW = WGM * WGN;
     static constexpr int NT = NW * kWave;
@@ -122,7 +128,9 @@ struct GemmCore {
     static constexpr int KELEMS = 128 / Elem<T>::kBytes;  // K elements per chunk
     static constexpr int A_BYTES = BM * 128;
     static constexpr int STAGE_BYTES = (BM + BN) * 128;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+    static constexpr int LOADS = (BM / 8) / NW + (BN / 8) / NW;  // DMA loads per wave per chunk
+    static_assert(NS >= 2 && (NS - 2) * LOADS < 64, "stages / vmcnt range");
     static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "tile shape");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "tile rows");
     static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "pieces must split evenly over waves");
@@ -199,10 +207,28 @@ struct GemmCore {
         step<3, ISSUE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh);
     }
 
+    // Wait until this wave's copy of the current chunk has landed, given that
+    // the copies of `ahead` later chunks (issued after it) may be in flight.
+    __device__ static __forceinline__ void wait_chunk(int ahead) {
+        switch (ahead) {
+            case 0: wait_vmcnt<0>(); break;
+            case 1: wait_vmcnt<(NS > 2 ? 1 : 0) * LOADS>(); break;
+            case 2: wait_vmcnt<(NS > 3 ? 2 : 0) * LOADS>(); break;
+            case 3: wait_vmcnt<(NS > 4 ? 3 : 0) * LOADS>(); break;
+            default: wait_vmcnt<(NS > 5 ? 4 : 0) * LOADS>(); break;
+        }
+    }
+
     // acc += A . B^T where A's and B's K axes are the concatenations
     // a0|a1 and b0|b1 (a0.chunks == b0.chunks, a1.chunks == b1.chunks).
-    // Double-buffered LDS stages; one barrier per chunk, after the wave's copy
-    // of the next chunk has landed.  Ends with a barrier (LDS free).
+    //
+    // A ring of NS LDS stages, NS-1 chunk copies in flight.  Iteration kt:
+    // issue the copy of chunk kt+NS-1 into the stage chunk kt-1 used (free
+    // since the barrier that ended iteration kt-1), spread over the first K
+    // step's MFMAs; multiply chunk kt (fragments register-double-buffered);
+    // then wait for this wave's copy of chunk kt+1 (the later ones may still
+    // fly), barrier, and read chunk kt+1's first fragments.  Ends with a
+    // barrier (LDS free for the epilogue).
     __device__ static __forceinline__ void run_segs(f32x16_t (&acc)[MB][NB], const KSeg& a0, const KSeg& a1,
                                                     int rows_a, const KSeg& b0, const KSeg& b1, int rows_b,
                                                     char* lds) {
@@ -218,26 +244,43 @@ struct GemmCore {
         DmaOperand<BN, NW> db;
         da.init(a0, a1, rows_a, wave, lane);
         db.init(b0, b1, rows_b, wave, lane);
-        da.issue(lds, 0, wave);
-        db.issue(lds + A_BYTES, 0, wave);
-        wait_vmcnt<0>();
+#pragma unroll
+        for (int c = 0; c < NS - 1; ++c)
+            if (c < nk) {
+                da.issue(lds + c * STAGE_BYTES, c, wave);
+                db.issue(lds + c * STAGE_BYTES + A_BYTES, c, wave);
+            }
+        wait_chunk(min(NS - 2, nk - 1));
         __syncthreads();
 
         u32x4_t fa[2][MB], fb[2][NB];
         const int oa = (wm * WTM) * 128, ob = A_BYTES + (wn * WTN) * 128;
         load_frags(fa[0], fb[0], lds + oa, lds + ob, 0, fr, fh);
 
-        for (int kt = 0; kt + 1 < nk; ++kt) {
-            char* cur = lds + (kt & 1) * STAGE_BYTES;
-            char* nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
-            chunk<true>(acc, fa, fb, cur + oa, cur + ob, da, db, nxt, kt + 1, wave, fr, fh);
-            wait_vmcnt<0>();
+        // main loop: chunks whose iteration still issues a copy
+        int stage = 0;
+        int kt = 0;
+        for (; kt + NS - 1 < nk; ++kt) {
+            char* cur = lds + stage * STAGE_BYTES;
+            char* dst = lds + (stage == 0 ? NS - 1 : stage - 1) * STAGE_BYTES;
+            chunk<true>(acc, fa, fb, cur + oa, cur + ob, da, db, dst, kt + NS - 1, wave, fr, fh);
+            wait_chunk(min(NS - 2, nk - 2 - kt));
             __syncthreads();
-            load_frags(fa[0], fb[0], nxt + oa, nxt + ob, 0, fr, fh);
+            stage = stage + 1 == NS ? 0 : stage + 1;
+            char* n = lds + stage * STAGE_BYTES;
+            load_frags(fa[0], fb[0], n + oa, n + ob, 0, fr, fh);
         }
-        {
-            char* cur = lds + ((nk - 1) & 1) * STAGE_BYTES;
+        // tail: the last NS-1 chunks (all copies issued)
+        for (; kt < nk; ++kt) {
+            char* cur = lds + stage * STAGE_BYTES;
             chunk<false>(acc, fa, fb, cur + oa, cur + ob, da, db, nullptr, 0, wave, fr, fh);
+            if (kt + 1 < nk) {
+                wait_chunk(min(NS - 2, nk - 2 - kt));
+                __syncthreads();
+                stage = stage + 1 == NS ? 0 : stage + 1;
+                char* n = lds + stage * STAGE_BYTES;
+                load_frags(fa[0], fb[0], n + oa, n + ob, 0, fr, fh);
+            }
         }
         __syncthreads();  // LDS free for the epilogue
     }

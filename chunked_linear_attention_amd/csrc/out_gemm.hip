@@ -80,7 +80,7 @@ hipError_t launch(const OutParams& p, hipStream_t st) {
     constexpr int LDS = OutTile<T, BM>::LDS;
     static_assert(LDS <= 160 * 1024, "output GEMM LDS over budget");
     const int blocks = ((p.d + BM - 1) / BM) * ((p.M + BN - 1) / BN);
-    hipError_t e = allow_lds(out_gemm_kernel<T, BM>, LDS);
+    hipError_t e = allow_lds<out_gemm_kernel<T, BM>>(LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((out_gemm_kernel<T, BM>), dim3(blocks), dim3(512), LDS, st, p);
     return hipGetLastError();

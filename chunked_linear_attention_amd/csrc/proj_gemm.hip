@@ -17,7 +17,7 @@
 // Two kernels on the shared MFMA core: U and V with 256 x 256 tiles (the
 // e/256 tiles of each section side by side along N, so a block's columns lie
 // in one section and its epilogue branch is uniform), and Z with its four
-// heads with 128 x 128 tiles (s is small, and a separate launch keeps the U/V
+// heads with 128 x 64 tiles (s is small, and a separate launch keeps the U/V
 // grid a whole number of rounds over the 256 CUs for the usual widths).
 // Tiles are assigned to XCDs in contiguous ranges.
 #include "gau_launch.h"
@@ -88,12 +88,15 @@ __global__ __launch_bounds__(512) void proj_uv_kernel(ProjParams p) {
     }
 }
 
-// Z = SiLU(X W_z) and its four heads: 128 x 128 tiles (features x tokens).
-constexpr int ZF = 128, ZT = 128;
+// Z = SiLU(X W_z) and its four heads: 128 features x 64 tokens per block
+// (B*T/64 blocks fill the CUs), with a 4-stage copy ring: the K loop over d
+// is a dependent chain of d/64 chunk copies per block, so several must be in
+// flight at once.
+constexpr int ZF = 128, ZT = 64, ZNS = 4;
 
 template <typename T>
 struct ZTile {
-    using G = GemmCore<T, ZF, ZT, 2, 2>;
+    using G = GemmCore<T, ZF, ZT, 2, 2, ZNS>;
     static constexpr int EB = Elem<T>::kBytes;
     static constexpr int STAGE = ZT * (ZF * EB + 16) > ZF * (ZT * EB + 16) ? ZT * (ZF * EB + 16)
                                                                           : ZF * (ZT * EB + 16);
@@ -151,7 +154,7 @@ hipError_t launch_z(const ProjParams& p, hipStream_t st) {
     constexpr int LDS = ZTile<T>::LDS;
     static_assert(LDS <= 160 * 1024, "Z projection LDS over budget");
     const int blocks = (p.s / ZF) * ((p.M + ZT - 1) / ZT);
-    hipError_t e = allow_lds(proj_z_kernel<T>, LDS);
+    hipError_t e = allow_lds<proj_z_kernel<T>>(LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(proj_z_kernel<T>, dim3(blocks), dim3(256), LDS, st, p);
     return hipGetLastError();
@@ -162,7 +165,7 @@ hipError_t launch_uv(const ProjParams& p, hipStream_t st) {
     constexpr int LDS = ProjTile<T>::LDS;
     static_assert(LDS <= 160 * 1024, "projection GEMM LDS over budget");
     const int blocks = 2 * (p.e / BN) * ((p.M + BM - 1) / BM);
-    hipError_t e = allow_lds(proj_uv_kernel<T>, LDS);
+    hipError_t e = allow_lds<proj_uv_kernel<T>>(LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(proj_uv_kernel<T>, dim3(blocks), dim3(512), LDS, st, p);
     return hipGetLastError();
