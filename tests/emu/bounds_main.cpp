@@ -1,0 +1,134 @@
+// Bounds check of every kernel launch of the library on the CPU emulation:
+// each operand in its own exact-size heap buffer (AddressSanitizer reports any
+// access outside), for the shapes the tests and the benchmark use.
+#include <chrono>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "gau.h"
+#include "gau_launch.h"
+
+using namespace gau;
+
+static void* buf(size_t n) {
+    void* p = malloc(n ? n : 1);
+    memset(p, 0, n ? n : 1);
+    return p;
+}
+
+struct Cfg {
+    int B, T, d, e, s, C;
+    bool bf;
+    bool causal;
+};
+
+static double now() {
+    return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+#define CHECK(x)                                                        \
+    do {                                                                \
+        if ((x) != hipSuccess) {                                        \
+            fprintf(stderr, "launch failed: %s\n", #x);                 \
+            exit(1);                                                    \
+        }                                                               \
+    } while (0)
+
+static void run(const Cfg& c, const std::string& only) {
+    const size_t eb = c.bf ? 2 : 4;
+    const size_t M = (size_t)c.B * c.T;
+    const int G = c.T / c.C;
+    const int Gp = c.causal ? G : 1;
+    fprintf(stderr, "config B%d T%d d%d e%d s%d C%d %s %s\n", c.B, c.T, c.d, c.e, c.s, c.C, c.bf ? "bf16" : "f32",
+            c.causal ? "causal" : "full");
+    void* X = buf(M * c.d * eb);
+    void* Wu = buf((size_t)c.e * c.d * eb);
+    void* Wv = buf((size_t)c.e * c.d * eb);
+    void* Wz = buf((size_t)c.s * c.d * eb);
+    void* Wo = buf((size_t)c.d * c.e * eb);
+    float* sc = (float*)buf(4 * c.s * 4);
+    float* of = (float*)buf(4 * c.s * 4);
+    float* rp = (float*)buf((2 * c.C - 1) * 4);
+    void* U = buf(M * c.e * eb);
+    void* Vt = buf(M * c.e * eb);
+    void* Qq = buf(M * c.s * eb);
+    void* Kq = buf(M * c.s * eb);
+    void* Ql = buf(M * c.s * eb);
+    void* Klt = buf(M * c.s * eb);
+    float* S = (float*)buf((size_t)c.B * G * c.e * c.s * 4);
+    void* P = buf((size_t)c.B * Gp * c.e * c.s * eb);
+    void* A = buf(M * c.C * eb);
+    void* Y = buf(M * c.e * eb);
+    void* O = buf(M * c.d * eb);
+    float* Of = (float*)buf(M * c.d * 4);
+    auto t = [&](const char* name, auto fn) {
+        if (!only.empty() && only != name) return;
+        double t0 = now();
+        fn();
+        fprintf(stderr, "  %-12s ok (%.1f s)\n", name, now() - t0);
+    };
+    ProjParams pp{X, Wu, Wv, Wz, sc, of, U, Vt, Qq, Kq, Ql, Klt, (int)M, c.T, c.d, c.e, c.s};
+    t("proj_z", [&] { CHECK(launch_proj_z(pp, c.bf, nullptr)); });
+    t("proj_uv", [&] { CHECK(launch_proj_uv(pp, c.bf, nullptr)); });
+    ScoresParams sp{Qq, Kq, rp, A, c.B, c.T, c.s, c.C, c.causal ? 1 : 0, 1.0f / c.C};
+    t("chunk_scores", [&] { CHECK(launch_chunk_scores(sp, c.bf, nullptr)); });
+    StateParams stp{Vt, Klt, S, c.B, c.T, c.e, c.s, c.C, 1.0f / c.C};
+    t("chunk_state", [&] { CHECK(launch_chunk_state(stp, c.bf, nullptr)); });
+    ScanParams scp{S, P, c.B, G, c.e * c.s, c.causal ? 1 : 0};
+    t("chunk_scan", [&] { CHECK(launch_chunk_scan(scp, c.bf, nullptr)); });
+    AttnParams ap{A, Ql, Vt, P, U, Y, c.B, c.T, c.e, c.s, c.C, c.causal ? 1 : 0};
+    t("chunk_attn", [&] { CHECK(launch_chunk_attn(ap, c.bf, nullptr)); });
+    OutParams op{Y, Wo, O, nullptr, (int)M, c.d, c.e};
+    t("out_gemm", [&] { CHECK(launch_out_gemm(op, c.bf, nullptr)); });
+    OutParams opr{Y, Wo, Of, Of, (int)M, c.d, c.e};
+    t("out_residual", [&] { CHECK(launch_out_gemm(opr, c.bf, nullptr)); });
+    NormParams np{Of, X, (int)M, c.d, 1e-6f};
+    t("rms_norm", [&] { CHECK(launch_rms_norm(np, c.bf, nullptr)); });
+    // the whole layer through the C ABI, one workspace
+    t("gau_forward", [&] {
+        gau_config cfg{c.B, c.T, c.d, c.e, c.s, c.C, c.causal ? 1 : 0, c.bf ? GAU_BF16 : GAU_F32, 1.0f / c.C,
+                       1.0f / c.C};
+        const size_t wsb = gau_workspace_bytes(&cfg);
+        void* ws = buf(wsb);
+        int st = gau_forward(&cfg, X, Wu, Wv, Wz, Wo, sc, of, rp, O, ws, wsb, nullptr);
+        if (st != GAU_OK) {
+            fprintf(stderr, "gau_forward status %d\n", st);
+            exit(1);
+        }
+        free(ws);
+    });
+    for (void* p : {X, Wu, Wv, Wz, Wo, (void*)sc, (void*)of, (void*)rp, U, Vt, Qq, Kq, Ql, Klt, (void*)S, P, A, Y, O,
+                    (void*)Of})
+        free(p);
+}
+
+int main(int argc, char** argv) {
+    // B, T, d, e, s, C, bf16, causal
+    std::vector<Cfg> small = {
+        {1, 256, 128, 256, 128, 64, false, true},   {1, 256, 128, 256, 128, 64, false, false},
+        {2, 512, 256, 512, 128, 128, true, true},   {2, 512, 256, 512, 128, 128, true, false},
+        {1, 320, 128, 256, 128, 64, true, true},    {1, 320, 128, 256, 128, 64, false, true},
+        {1, 1024, 256, 512, 128, 512, true, true},  {1, 1024, 256, 512, 128, 512, true, false},
+        {1, 512, 256, 512, 256, 256, true, true},   {1, 256, 128, 256, 256, 128, false, false},
+        {3, 128, 128, 256, 128, 128, true, true},   {2, 192, 384, 768, 128, 64, true, true},
+        {1, 1024, 256, 512, 128, 256, true, true},  {2, 512, 1024, 2048, 128, 256, true, true},
+        {1, 64, 128, 256, 128, 64, true, true},     {1, 64, 128, 256, 128, 64, false, false},
+    };
+    std::vector<Cfg> full = {
+        {8, 1024, 768, 1536, 128, 256, true, true}, {4, 4096, 768, 1536, 128, 256, true, true},
+        {4, 4096, 768, 1536, 128, 256, true, false}, {2, 8192, 768, 1536, 128, 512, true, true},
+        {2, 8192, 768, 1536, 128, 256, true, true},
+    };
+    const std::string which = argc > 1 ? argv[1] : "small";
+    const std::string only = argc > 2 ? argv[2] : "";
+    if (which == "small" || which == "all")
+        for (auto& c : small) run(c, only);
+    if (which == "full" || which == "all")
+        for (auto& c : full) run(c, only);
+    if (which == "headline") run(full.back(), only);
+    fprintf(stderr, "all launches in bounds\n");
+    return 0;
+}

@@ -1,0 +1,125 @@
+"""The library's kernel sources on the CPU emulation (tests/emu): every access
+in bounds, and the results of the emulated kernels equal to the oracle's.
+
+The emulation compiles the same .hip sources for the host, so these tests
+check the kernels' addressing, barriers, copy waits and MFMA operand layouts
+without a GPU.  They do not replace the GPU parity tests: the compiler's
+device code and the hardware are not exercised.
+"""
+
+import ctypes
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "emu"))
+
+emu_build = pytest.importorskip("emu_build", reason="tests/emu is not present")
+
+from chunked_linear_attention_amd import inputs  # noqa: E402
+from chunked_linear_attention_amd._lib import GauConfig, GauWsLayout  # noqa: E402
+from oracle import gau_oracle as orc  # noqa: E402
+
+pytestmark = pytest.mark.skipif(not emu_build.available(), reason="host clang++ of ROCm not found")
+
+
+@pytest.fixture(scope="module")
+def emu():
+    emu_build.build()
+    lib = ctypes.CDLL(emu_build.LIB)
+    P = ctypes.c_void_p
+    lib.gau_workspace_bytes.restype = ctypes.c_size_t
+    lib.gau_workspace_bytes.argtypes = [ctypes.POINTER(GauConfig)]
+    lib.gau_workspace_layout.argtypes = [ctypes.POINTER(GauConfig), ctypes.POINTER(GauWsLayout)]
+    lib.gau_forward.argtypes = [ctypes.POINTER(GauConfig)] + [P] * 9 + [P, ctypes.c_size_t, P]
+    lib.gau_forward.restype = ctypes.c_int
+    lib.emu_set_mode.argtypes = [ctypes.c_int, ctypes.c_int]
+    return lib
+
+
+def _bounds(which):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")
+    r = subprocess.run([emu_build.BOUNDS, which], capture_output=True, text=True, env=env, timeout=900)
+    assert r.returncode == 0 and "all launches in bounds" in r.stderr, r.stderr[-4000:]
+
+
+def test_every_launch_in_bounds_at_test_shapes(emu):
+    """All kernels at the shapes the parity tests use (ragged tiles, every C
+    and s, fp32 and bf16, causal and not): each operand in its own exact-size
+    buffer under AddressSanitizer."""
+    _bounds("small")
+
+
+def test_every_launch_in_bounds_at_benchmark_shape(emu):
+    """The same at B=2, T=8192, d=768, e=1536, s=128, C=256."""
+    _bounds("headline")
+
+
+CASES = [
+    # B, T, d, e, s, C, dtype, causal
+    (1, 256, 128, 256, 128, 64, "f32", True),
+    (1, 256, 128, 256, 128, 64, "f32", False),
+    (1, 320, 128, 256, 128, 64, "bf16", True),
+    (2, 256, 256, 512, 128, 128, "bf16", True),
+    (1, 512, 128, 256, 256, 256, "bf16", False),
+    (1, 512, 128, 256, 128, 512, "bf16", True),
+]
+
+
+def _host(a, bf):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return inputs.bf16_bits(a) if bf else a
+
+
+@pytest.mark.parametrize("late", [0, 1], ids=["dma_at_issue", "dma_at_wait"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}".format(
+    *c[:7], "causal" if c[7] else "full"))
+def test_emulated_kernels_match_oracle(emu, case, late):
+    B, T, d, e, s, C, dtype, causal = case
+    bf = dtype == "bf16"
+    emu.emu_set_mode(1, late)
+    inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=B * 31 + T + C, dtype=dtype)
+    cfg = GauConfig(B, T, d, e, s, C, 1 if causal else 0, 1 if bf else 0, 1.0 / C, 1.0 / C)
+    X = _host(inp["X"], bf)
+    W = {k: _host(np.ascontiguousarray(inp[k].T), bf) for k in ("W_u", "W_v", "W_z", "W_o")}
+    sc, of, rp = (np.ascontiguousarray(inp[k], np.float32) for k in ("gamma", "beta", "relpos"))
+    O = np.zeros((B, T, d), np.uint16 if bf else np.float32)
+    wsb = emu.gau_workspace_bytes(ctypes.byref(cfg))
+    raw = np.zeros(wsb + 256, np.uint8)
+    ws = raw[(-raw.ctypes.data) % 256:][:wsb]
+    ptr = lambda a: ctypes.c_void_p(a.ctypes.data)
+    st = emu.gau_forward(ctypes.byref(cfg), ptr(X), ptr(W["W_u"]), ptr(W["W_v"]), ptr(W["W_z"]), ptr(W["W_o"]),
+                         ptr(sc), ptr(of), ptr(rp), ptr(O), ptr(ws), wsb, None)
+    assert st == 0
+    L = GauWsLayout()
+    assert emu.gau_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == 0
+    ref, im = orc.flash_forward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"],
+                                inp["beta"], inp["relpos"], C, causal, return_intermediates=True)
+    conv = inputs.bf16_bits_to_f32 if bf else (lambda a: a)
+    eb = 2 if bf else 4
+
+    def region(name, shape, f32=False):
+        n = int(np.prod(shape))
+        o = getattr(L, name)
+        if f32:
+            return ws[o:o + 4 * n].view(np.float32).reshape(shape).astype(np.float64)
+        return conv(ws[o:o + eb * n].view(np.uint16 if bf else np.float32).reshape(shape)).astype(np.float64)
+
+    tol = 2e-2 if bf else 1e-4
+    G = T // C
+    checks = {
+        "U": (region("U", (B, T, e)), im["U"]),
+        "Vt": (region("Vt", (B, e, T)), im["V"].transpose(0, 2, 1)),
+        "Q_quad": (region("Q_quad", (B, T, s)), im["Q_quad"]),
+        "K_lin_t": (region("K_lin_t", (B, s, T)), im["K_lin"].transpose(0, 2, 1)),
+        "S": (region("S", (B, G, e, s), True), im["S"].transpose(0, 1, 3, 2)),
+        "Y": (region("Y", (B, T, e)), im["Y"]),
+        "O": (conv(O).astype(np.float64), ref),
+    }
+    for name, (got, want) in checks.items():
+        assert np.all(np.isfinite(got)), name
+        err = np.max(np.abs(got - want)) / np.max(np.abs(want))
+        assert err <= tol, f"{name}: {err:.3e} > {tol}"
