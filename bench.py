@@ -11,7 +11,7 @@ seeded synthetic input, B=2 sequences of T=8192 tokens, d=768, e=1536, s=128,
 chunk C=256, bf16 storage with fp32 accumulation, causal.  Inputs are resident
 in HBM before the timed region starts.  Prints one JSON line.
 
-Inside the timed region the dominant kernel (the U/V projection GEMM) is
+Inside the timed region the dominant kernel (the projection GEMM) is
 bracketed by HIP events on the stream the kernels run on; the roofline object
 is its algorithmic FLOPs per launch divided by that average duration, against
 the dense bf16 MFMA peak.  Per-stage times (kernels_us) come from a separate
@@ -33,8 +33,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4 SIMDs x 1024 dense bf16 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 METRIC = "GAU/FLASH layer fwd tokens/sec at d=768 T=8192 C=256; % bf16 MFMA peak"
-STAGES = ["proj_z", "proj_uv", "chunk_scores", "chunk_state", "chunk_scan", "chunk_attn", "out_gemm"]
-DOMINANT = "proj_uv"
+STAGES = ["proj", "chunk_scores", "chunk_state", "chunk_scan", "chunk_attn", "out_gemm"]
+DOMINANT = "proj"
 
 
 def algorithmic_flops(B, T, d, e, s, C, causal=True):
@@ -47,8 +47,7 @@ def algorithmic_flops(B, T, d, e, s, C, causal=True):
     pairs = C * (C + 1) / 2 if causal else C * C
     G = T // C
     return {
-        "proj_z": 2.0 * M * d * s,
-        "proj_uv": 2.0 * M * d * 2 * e,
+        "proj": 2.0 * M * d * (2 * e + s),
         "chunk_scores": 2.0 * B * G * pairs * s,
         "chunk_state": 2.0 * M * s * e,
         "chunk_scan": 0.0,
@@ -65,8 +64,7 @@ def algorithmic_bytes(B, T, d, e, s, C, causal=True, eb=2):
     st = B * G * e * s
     pairs = C * (C + 1) // 2 if causal else C * C
     return {
-        "proj_z": M * d * eb + s * d * eb + 4 * M * s * eb,
-        "proj_uv": M * d * eb + 2 * e * d * eb + 2 * M * e * eb,
+        "proj": M * d * eb + (2 * e + s) * d * eb + 2 * M * e * eb + 4 * M * s * eb,
         "chunk_scores": 2 * M * s * eb + B * G * pairs * eb,
         "chunk_state": M * (e + s) * eb + st * 4,
         "chunk_scan": st * 4 + B * Gp * e * s * eb,
@@ -75,7 +73,7 @@ def algorithmic_bytes(B, T, d, e, s, C, causal=True, eb=2):
     }
 
 
-SOURCES = {"proj_uv": "proj_gemm", "proj_z": "proj_gemm"}
+SOURCES = {"proj": "proj_gemm"}
 
 
 def source_hash(name):
@@ -204,7 +202,7 @@ def summarize_traffic(fetch_csv, write_csv, command):
     base = os.path.join(ROOT, "profiles", f"{DOMINANT}_{PROFILE_TAG}_traffic")
     with open(base + ".json", "w") as f:
         json.dump(rec, f, indent=1)
-    lines = [f"# HBM traffic of `{DOMINANT}` (U/V projection GEMM), FLASH layer B=2 T=8192 d=768 e=1536 "
+    lines = [f"# HBM traffic of `{DOMINANT}` (projection GEMM: U, V, Z heads), FLASH layer B=2 T=8192 d=768 e=1536 "
              "s=128 C=256, bf16", "", "Commands (from the repository root, one MI355X; one counter per run):",
              "", "```", command, "```", "",
              "| counter | KiB / dispatch | calibration copy KiB / dispatch | scale (counter B per true B) | "

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, "libgau.so")
 GAU_F32 = 0
 GAU_BF16 = 1
 
-STAGE_PROJ_Z, STAGE_PROJ_UV, STAGE_SCORES, STAGE_STATE, STAGE_SCAN, STAGE_ATTN, STAGE_OUT = range(7)
+STAGE_PROJ, STAGE_SCORES, STAGE_STATE, STAGE_SCAN, STAGE_ATTN, STAGE_OUT = range(6)
 
 STATUS = {
     0: "GAU_OK", 1: "GAU_ERR_NULL", 2: "GAU_ERR_SHAPE", 3: "GAU_ERR_ALIGN",

@@ -29,8 +29,8 @@ __device__ __forceinline__ void put4<float>(void* dst, const f32x4_t& v) {
 template <>
 __device__ __forceinline__ void put4<bf16>(void* dst, const f32x4_t& v) {
     u32x2_t w;
-    w.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
-    w.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    w.x = pack_bf16x2(v.x, v.y);
+    w.y = pack_bf16x2(v.z, v.w);
     *(u32x2_t*)dst = w;
 }
 

@@ -84,12 +84,11 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
     for (int stage = first; stage <= last; ++stage) {
         hipError_t e = hipSuccess;
         switch (stage) {
-            case GAU_STAGE_PROJ_Z:
-            case GAU_STAGE_PROJ_UV: {
+            case GAU_STAGE_PROJ: {
                 gau::ProjParams p{a.X, a.W_u, a.W_v, a.W_z, a.scale, a.offset, ws + L.U, ws + L.Vt,
                                   ws + L.Q_quad, ws + L.K_quad, ws + L.Q_lin, ws + L.K_lin_t,
                                   M, (int)c->T, (int)c->d, (int)c->e, (int)c->s};
-                e = stage == GAU_STAGE_PROJ_Z ? gau::launch_proj_z(p, bf, st) : gau::launch_proj_uv(p, bf, st);
+                e = gau::launch_proj(p, bf, st);
                 break;
             }
             case GAU_STAGE_STATE: {
@@ -154,7 +153,7 @@ gau_status gau_forward_stages(const gau_config* cfg, int first_stage, int last_s
                               void* workspace, size_t workspace_bytes, void* stream) {
     gau_status s = check_config(cfg);
     if (s != GAU_OK) return s;
-    if (first_stage < GAU_STAGE_PROJ_Z || last_stage > GAU_STAGE_OUT || first_stage > last_stage) return GAU_ERR_SHAPE;
+    if (first_stage < GAU_STAGE_PROJ || last_stage > GAU_STAGE_OUT || first_stage > last_stage) return GAU_ERR_SHAPE;
     if (cfg->B * cfg->T == 0) return GAU_OK;
     const LayerPtrs a{X, W_u, W_v, W_z, W_o, scale, offset, relpos};
     if ((s = check_layer_ptrs(a)) != GAU_OK) return s;
@@ -167,7 +166,7 @@ gau_status gau_forward_stages(const gau_config* cfg, int first_stage, int last_s
 gau_status gau_forward(const gau_config* cfg, const void* X, const void* W_u, const void* W_v, const void* W_z,
                        const void* W_o, const float* scale, const float* offset, const float* relpos, void* O,
                        void* workspace, size_t workspace_bytes, void* stream) {
-    return gau_forward_stages(cfg, GAU_STAGE_PROJ_Z, GAU_STAGE_OUT, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O,
+    return gau_forward_stages(cfg, GAU_STAGE_PROJ, GAU_STAGE_OUT, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O,
                               workspace, workspace_bytes, stream);
 }
 
@@ -203,7 +202,7 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X, cons
         gau::NormParams np{X, xn, (int)(cfg->B * cfg->T), (int)cfg->d, 1e-6f};
         if (gau::launch_rms_norm(np, bf, st) != hipSuccess) return GAU_ERR_HIP;
         const LayerPtrs a{xn, W_u[l], W_v[l], W_z[l], W_o[l], scale[l], offset[l], relpos[l]};
-        if ((s = run_stages(cfg, GAU_STAGE_PROJ_Z, GAU_STAGE_OUT, a, X, X, ws, st)) != GAU_OK) return s;
+        if ((s = run_stages(cfg, GAU_STAGE_PROJ, GAU_STAGE_OUT, a, X, X, ws, st)) != GAU_OK) return s;
     }
     return GAU_OK;
 }

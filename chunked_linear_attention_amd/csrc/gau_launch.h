@@ -83,8 +83,7 @@ struct NormParams {
     float eps;
 };
 
-hipError_t launch_proj_z(const ProjParams& p, bool bf16_storage, hipStream_t st);   // Z and the heads
-hipError_t launch_proj_uv(const ProjParams& p, bool bf16_storage, hipStream_t st);  // U and Vt
+hipError_t launch_proj(const ProjParams& p, bool bf16_storage, hipStream_t st);  // U, Vt, Z heads
 hipError_t launch_chunk_state(const StateParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_chunk_scan(const ScanParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_chunk_scores(const ScoresParams& p, bool bf16_storage, hipStream_t st);

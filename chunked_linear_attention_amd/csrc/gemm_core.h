@@ -430,8 +430,8 @@ struct GemmCore {
                             char* q = lds + (col - pass * prows) * PITCH + row0 * EB;
                             if constexpr (EB == 2) {
                                 u32x2_t w;
-                                w.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
-                                w.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+                                w.x = pack_bf16x2(x[0], x[1]);
+                                w.y = pack_bf16x2(x[2], x[3]);
                                 *(u32x2_t*)q = w;
                             } else {
                                 *(f32x4_t*)q = f32x4_t{x[0], x[1], x[2], x[3]};

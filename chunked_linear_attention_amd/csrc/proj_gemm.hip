@@ -14,12 +14,15 @@
 //   kernels read tokens contiguously); Q_quad, K_quad, Q_lin [M, s] row-major;
 //   K_lin_t [B, s, T] transposed.  M = B*T.
 //
-// Two kernels on the shared MFMA core: U and V with 256 x 256 tiles (the
+// One launch, two kinds of blocks on the shared MFMA core.  The first
+// (s/128) * ceil(M/256) blocks each form a 128-feature x 256-token tile of Z
+// and write its four heads; the rest form the 256 x 256 tiles of U and V (the
 // e/256 tiles of each section side by side along N, so a block's columns lie
-// in one section and its epilogue branch is uniform), and Z with its four
-// heads with 128 x 64 tiles (s is small, and a separate launch keeps the U/V
-// grid a whole number of rounds over the 256 CUs for the usual widths).
-// Tiles are assigned to XCDs in contiguous ranges.
+// in one section and its epilogue branch is uniform).  The Z blocks are
+// dispatched first and cost half a U/V tile each, so the launch is about an
+// eighth of a round longer than U and V alone instead of a second launch of
+// small, latency-bound blocks.  U/V tiles are assigned to XCDs in contiguous
+// ranges.
 #include "gau_launch.h"
 #include "gemm_core.h"
 
@@ -27,26 +30,27 @@ namespace gau {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4;
+constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4;  // U/V tiles, wave grid
+constexpr int ZF = 128, ZT = 256;                    // Z tiles: features x tokens
 
 template <typename T>
 struct ProjTile {
     using G = GemmCore<T, BM, BN, WGM, WGN>;
+    using GZ = GemmCore<T, ZF, ZT, WGM, WGN>;
     static constexpr int EB = Elem<T>::kBytes;
     static constexpr int STAGE = (BM * (BN * EB + 16) > 160 * 1024 - 1024) ? BM / WGM * (BN * EB + 16)
                                                                            : BM * (BN * EB + 16);
-    static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
+    static constexpr int CORE = G::LDS_BYTES > GZ::LDS_BYTES ? G::LDS_BYTES : GZ::LDS_BYTES;
+    static constexpr int LDS = CORE > STAGE ? CORE : STAGE;
 };
 
-// U and V: 256 x 256 tiles; the e/256 tiles of U and of V side by side.
+// U and V: one 256 x 256 tile (logical index bid over the U/V tiles).
 template <typename T>
-__global__ __launch_bounds__(512) void proj_uv_kernel(ProjParams p) {
-    extern __shared__ __align__(16) char lds[];
+__device__ __forceinline__ void uv_tile(const ProjParams& p, int bid, char* lds) {
     using G = typename ProjTile<T>::G;
     constexpr int EB = Elem<T>::kBytes;
     const int ntu = p.e / BN;  // tiles per section
     const int ntiles = 2 * ntu;
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int nt = bid % ntiles;
     const int mt = bid / ntiles;
     const int m0 = mt * BM;
@@ -88,30 +92,16 @@ __global__ __launch_bounds__(512) void proj_uv_kernel(ProjParams p) {
     }
 }
 
-// Z = SiLU(X W_z) and its four heads: 128 features x 64 tokens per block
-// (B*T/64 blocks fill the CUs), with a 4-stage copy ring: the K loop over d
-// is a dependent chain of d/64 chunk copies per block, so several must be in
-// flight at once.
-constexpr int ZF = 128, ZT = 64, ZNS = 4;
-
+// Z = SiLU(X W_z) for 128 features x 256 tokens (tile index zb), and its four
+// heads h = Z * gamma[h] + beta[h]: Q_quad, K_quad, Q_lin token-major, K_lin
+// feature-major.
 template <typename T>
-struct ZTile {
-    using G = GemmCore<T, ZF, ZT, 2, 2, ZNS>;
-    static constexpr int EB = Elem<T>::kBytes;
-    static constexpr int STAGE = ZT * (ZF * EB + 16) > ZF * (ZT * EB + 16) ? ZT * (ZF * EB + 16)
-                                                                          : ZF * (ZT * EB + 16);
-    static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
-};
-
-template <typename T>
-__global__ __launch_bounds__(256) void proj_z_kernel(ProjParams p) {
-    extern __shared__ __align__(16) char lds[];
-    using G = typename ZTile<T>::G;
+__device__ __forceinline__ void z_tile(const ProjParams& p, int zb, char* lds) {
+    using G = typename ProjTile<T>::GZ;
     constexpr int EB = Elem<T>::kBytes;
     const int nf = p.s / ZF;
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int ft = bid % nf;
-    const int mt = bid / nf;
+    const int ft = zb % nf;
+    const int mt = zb / nf;
     const int m0 = mt * ZT, f0 = ft * ZF;
     const size_t pitch = (size_t)p.d * EB;
     const int rows_x = min(ZT, p.M - m0);
@@ -123,9 +113,7 @@ __global__ __launch_bounds__(256) void proj_z_kernel(ProjParams p) {
            rows_x, p.d, lds);
     G::transform(acc, [](int, int, float v) { return silu(v); });
 
-    // head h = Z * gamma[h] + beta[h]; heads 0..2 token-major, head 3 (K_lin)
-    // feature-major
-    constexpr int LDS = ZTile<T>::LDS;
+    constexpr int LDS = ProjTile<T>::LDS;
     const int M = p.M, T_ = p.T, s = p.s;
     for (int h = 0; h < 4; ++h) {
         const float* gam = p.scale + h * s + f0;
@@ -150,35 +138,32 @@ __global__ __launch_bounds__(256) void proj_z_kernel(ProjParams p) {
 }
 
 template <typename T>
-hipError_t launch_z(const ProjParams& p, hipStream_t st) {
-    constexpr int LDS = ZTile<T>::LDS;
-    static_assert(LDS <= 160 * 1024, "Z projection LDS over budget");
-    const int blocks = (p.s / ZF) * ((p.M + ZT - 1) / ZT);
-    hipError_t e = allow_lds<proj_z_kernel<T>>(LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(proj_z_kernel<T>, dim3(blocks), dim3(256), LDS, st, p);
-    return hipGetLastError();
+__global__ __launch_bounds__(512) void proj_kernel(ProjParams p) {
+    extern __shared__ __align__(16) char lds[];
+    const int nz = (p.s / ZF) * ((p.M + ZT - 1) / ZT);
+    const int b = blockIdx.x;
+    if (b < nz)
+        z_tile<T>(p, b, lds);
+    else
+        uv_tile<T>(p, xcd_remap(b - nz, gridDim.x - nz), lds);
 }
 
 template <typename T>
-hipError_t launch_uv(const ProjParams& p, hipStream_t st) {
+hipError_t launch_t(const ProjParams& p, hipStream_t st) {
     constexpr int LDS = ProjTile<T>::LDS;
-    static_assert(LDS <= 160 * 1024, "projection GEMM LDS over budget");
-    const int blocks = 2 * (p.e / BN) * ((p.M + BM - 1) / BM);
-    hipError_t e = allow_lds<proj_uv_kernel<T>>(LDS);
+    static_assert(LDS <= 160 * 1024, "projection LDS over budget");
+    const int mtiles = (p.M + BM - 1) / BM;
+    const int blocks = (p.s / ZF) * ((p.M + ZT - 1) / ZT) + 2 * (p.e / BN) * mtiles;
+    hipError_t e = allow_lds<proj_kernel<T>>(LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(proj_uv_kernel<T>, dim3(blocks), dim3(512), LDS, st, p);
+    hipLaunchKernelGGL(proj_kernel<T>, dim3(blocks), dim3(512), LDS, st, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_proj_z(const ProjParams& p, bool bf16_storage, hipStream_t st) {
-    return bf16_storage ? launch_z<bf16>(p, st) : launch_z<float>(p, st);
-}
-
-hipError_t launch_proj_uv(const ProjParams& p, bool bf16_storage, hipStream_t st) {
-    return bf16_storage ? launch_uv<bf16>(p, st) : launch_uv<float>(p, st);
+hipError_t launch_proj(const ProjParams& p, bool bf16_storage, hipStream_t st) {
+    return bf16_storage ? launch_t<bf16>(p, st) : launch_t<float>(p, st);
 }
 
 }  // namespace gau

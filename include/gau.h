@@ -134,12 +134,12 @@ gau_status gau_forward(const gau_config* cfg,
                        void* O, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The seven kernels gau_forward queues, in order.  gau_forward_stages runs a
+ * The six kernels gau_forward queues, in order.  gau_forward_stages runs a
  * contiguous range of them (for stage-wise tests and per-kernel timing); the
  * stages communicate only through the workspace.
- *   GAU_STAGE_PROJ_Z  Z = SiLU(X W_z) and its four scale+offset heads Q_quad, K_quad,
- *                     Q_lin, K_lin_t (Su's post "Weak Attention"; wikillm "Method")
- *   GAU_STAGE_PROJ_UV U = SiLU(X W_u), Vt = SiLU(X W_v)^T (Su's post "Gated Attention")
+ *   GAU_STAGE_PROJ   U = SiLU(X W_u), Vt = SiLU(X W_v)^T (Su's post "Gated Attention"),
+ *                    Z = SiLU(X W_z) and its four scale+offset heads Q_quad, K_quad,
+ *                    Q_lin, K_lin_t (Su's post "Weak Attention"; wikillm "Method")
  *   GAU_STAGE_SCORES A_g = relu^2(quad_scale Q_quad K_quad^T + Bias), causal-masked,
  *                    per chunk (wikillm "Method" step 1, eq. 5; papercache appendix D, Code 4)
  *   GAU_STAGE_STATE  S_g = lin_scale * K_lin_g^T V_g for every chunk (eq. 7-8)
@@ -149,17 +149,16 @@ gau_status gau_forward(const gau_config* cfg,
  * Arguments, checks and status codes as gau_forward (every pointer is
  * checked, also those the selected stages do not read).  A stage reads the
  * workspace regions earlier stages wrote, so a range that does not start at
- * GAU_STAGE_PROJ_Z needs them there already.  first > last or a stage number
- * outside 0..6 gives GAU_ERR_SHAPE.
+ * GAU_STAGE_PROJ needs them there already.  first > last or a stage number
+ * outside 0..5 gives GAU_ERR_SHAPE.
  */
 enum {
-    GAU_STAGE_PROJ_Z = 0,
-    GAU_STAGE_PROJ_UV = 1,
-    GAU_STAGE_SCORES = 2,
-    GAU_STAGE_STATE = 3,
-    GAU_STAGE_SCAN = 4,
-    GAU_STAGE_ATTN = 5,
-    GAU_STAGE_OUT = 6
+    GAU_STAGE_PROJ = 0,
+    GAU_STAGE_SCORES = 1,
+    GAU_STAGE_STATE = 2,
+    GAU_STAGE_SCAN = 3,
+    GAU_STAGE_ATTN = 4,
+    GAU_STAGE_OUT = 5
 };
 
 gau_status gau_forward_stages(const gau_config* cfg, int first_stage, int last_stage,

@@ -71,8 +71,7 @@ static void run(const Cfg& c, const std::string& only) {
         fprintf(stderr, "  %-12s ok (%.1f s)\n", name, now() - t0);
     };
     ProjParams pp{X, Wu, Wv, Wz, sc, of, U, Vt, Qq, Kq, Ql, Klt, (int)M, c.T, c.d, c.e, c.s};
-    t("proj_z", [&] { CHECK(launch_proj_z(pp, c.bf, nullptr)); });
-    t("proj_uv", [&] { CHECK(launch_proj_uv(pp, c.bf, nullptr)); });
+    t("proj", [&] { CHECK(launch_proj(pp, c.bf, nullptr)); });
     ScoresParams sp{Qq, Kq, rp, A, c.B, c.T, c.s, c.C, c.causal ? 1 : 0, 1.0f / c.C};
     t("chunk_scores", [&] { CHECK(launch_chunk_scores(sp, c.bf, nullptr)); });
     StateParams stp{Vt, Klt, S, c.B, c.T, c.e, c.s, c.C, 1.0f / c.C};

@@ -29,8 +29,10 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
-CSRC = os.path.join(ROOT, "chunked_linear_attention_amd", "csrc")
-OUT = os.path.join(HERE, "_build")
+# The sources and the build folder can be redirected (EMU_CSRC, EMU_OUT) to
+# check a modified copy of the kernels before it is adopted.
+CSRC = os.environ.get("EMU_CSRC", os.path.join(ROOT, "chunked_linear_attention_amd", "csrc"))
+OUT = os.environ.get("EMU_OUT", os.path.join(HERE, "_build"))
 CXX = "/opt/rocm/llvm/bin/clang++"
 UNITS = ["proj_gemm", "chunk_attn", "chunk_scan", "chunk_scores", "chunk_state", "out_gemm", "rms_norm", "gau_api"]
 BOUNDS = os.path.join(OUT, "emu_bounds")
@@ -55,7 +57,8 @@ def _inputs():
 
 
 def _generate(gen):
-    """Copy the kernel sources, rewriting the LDS declarations only."""
+    """Copy the kernel sources, rewriting the LDS declarations (and dropping
+    AMDGPU occupancy attributes) only."""
     csrc = os.path.join(gen, "pkg", "csrc")
     os.makedirs(csrc, exist_ok=True)
     os.makedirs(os.path.join(gen, "include"), exist_ok=True)
@@ -68,6 +71,8 @@ def _generate(gen):
         s = re.sub(r"extern __shared__ __align__\(16\) char lds\[\];", "char* lds = ::emu::lds_base();", s)
         s = re.sub(r"__shared__\s+(\w+)\s+(\w+)\[(\w+)\];",
                    r"\1* \2 = (\1*)::emu::static_shared(__LINE__, sizeof(\1) * (\3));", s)
+        # AMDGPU occupancy attributes have no meaning on the host
+        s = re.sub(r"__attribute__\(\(amdgpu_[a-z_]+\([^)]*\)\)\)", "", s)
         if "__shared__" in s:
             raise RuntimeError(f"{f}: LDS declaration the emulation build does not rewrite")
         with open(os.path.join(csrc, f), "w") as fh:
