@@ -66,8 +66,8 @@ def algorithmic_bytes(B, T, d, e, s, C, causal=True, eb=2):
     return {
         "proj": M * d * eb + (2 * e + s) * d * eb + 2 * M * e * eb + 4 * M * s * eb,
         "chunk_scores": 2 * M * s * eb + B * G * pairs * eb,
-        "chunk_state": M * (e + s) * eb + st * 4,
-        "chunk_scan": st * 4 + B * Gp * e * s * eb,
+        "chunk_state": M * (e + s) * eb + st * eb,
+        "chunk_scan": st * eb + B * Gp * e * s * eb,
         "chunk_attn": B * G * pairs * eb + M * (s + 2 * e) * eb + B * Gp * e * s * eb + M * e * eb,
         "out_gemm": M * e * eb + e * d * eb + M * d * eb,
     }

@@ -11,14 +11,27 @@
 // thread owns four consecutive entries (one 16-byte vector) and walks the G
 // chunks in order g = 0..G-1, so each output is a true exclusive prefix summed
 // in a fixed order (never an inclusive sum minus the own term), which keeps the
-// causal outputs independent of later chunks bit for bit.  Sums are fp32; P is
-// stored in the layer's element type, the precision its consumer (an MFMA
-// operand) takes it in.  HBM bound: it reads S once and writes P once.
+// causal outputs independent of later chunks bit for bit.  S and P are in the
+// layer's element type (P's consumer is an MFMA operand of that type); the
+// sums are fp32.  HBM bound: it reads S once and writes P once.
 #include "gau_device.h"
 #include "gau_launch.h"
 
 namespace gau {
 namespace {
+
+template <typename T>
+__device__ __forceinline__ f32x4_t get4(const void* src);
+template <>
+__device__ __forceinline__ f32x4_t get4<float>(const void* src) {
+    return *(const f32x4_t*)src;
+}
+template <>
+__device__ __forceinline__ f32x4_t get4<bf16>(const void* src) {
+    const u32x2_t w = *(const u32x2_t*)src;
+    return f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                   __uint_as_float(w.y & 0xFFFF0000u)};
+}
 
 template <typename T>
 __device__ __forceinline__ void put4(void* dst, const f32x4_t& v);
@@ -42,34 +55,35 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanParams p) {
     const int b = idx / per_b;
     const int v = idx - b * per_b;
     const size_t stride = (size_t)p.es;  // elements between consecutive chunks
-    const f32x4_t* __restrict__ S = (const f32x4_t*)(p.S + (size_t)b * p.G * stride) + v;
-    char* __restrict__ P = (char*)p.P;
     constexpr int EB = Elem<T>::kBytes;
+    const char* __restrict__ S = (const char*)p.S + ((size_t)b * p.G * stride + (size_t)v * 4) * EB;
+    char* __restrict__ P = (char*)p.P;
+    const size_t cstride = stride * EB;  // bytes between consecutive chunks
     f32x4_t run = {0.f, 0.f, 0.f, 0.f};
     if (p.causal) {
         char* out = P + ((size_t)b * p.G * stride + (size_t)v * 4) * EB;
         int g = 0;
         for (; g + 4 <= p.G; g += 4) {
-            const f32x4_t s0 = S[(size_t)(g + 0) * (stride / 4)];
-            const f32x4_t s1 = S[(size_t)(g + 1) * (stride / 4)];
-            const f32x4_t s2 = S[(size_t)(g + 2) * (stride / 4)];
-            const f32x4_t s3 = S[(size_t)(g + 3) * (stride / 4)];
-            put4<T>(out + (size_t)(g + 0) * stride * EB, run);
+            const f32x4_t s0 = get4<T>(S + (size_t)(g + 0) * cstride);
+            const f32x4_t s1 = get4<T>(S + (size_t)(g + 1) * cstride);
+            const f32x4_t s2 = get4<T>(S + (size_t)(g + 2) * cstride);
+            const f32x4_t s3 = get4<T>(S + (size_t)(g + 3) * cstride);
+            put4<T>(out + (size_t)(g + 0) * cstride, run);
             run += s0;
-            put4<T>(out + (size_t)(g + 1) * stride * EB, run);
+            put4<T>(out + (size_t)(g + 1) * cstride, run);
             run += s1;
-            put4<T>(out + (size_t)(g + 2) * stride * EB, run);
+            put4<T>(out + (size_t)(g + 2) * cstride, run);
             run += s2;
-            put4<T>(out + (size_t)(g + 3) * stride * EB, run);
+            put4<T>(out + (size_t)(g + 3) * cstride, run);
             run += s3;
         }
         for (; g < p.G; ++g) {
-            const f32x4_t s0 = S[(size_t)g * (stride / 4)];
-            put4<T>(out + (size_t)g * stride * EB, run);
+            const f32x4_t s0 = get4<T>(S + (size_t)g * cstride);
+            put4<T>(out + (size_t)g * cstride, run);
             run += s0;
         }
     } else {
-        for (int g = 0; g < p.G; ++g) run += S[(size_t)g * (stride / 4)];
+        for (int g = 0; g < p.G; ++g) run += get4<T>(S + (size_t)g * cstride);
         put4<T>(P + ((size_t)b * stride + (size_t)v * 4) * EB, run);
     }
 }

@@ -1,5 +1,7 @@
 // Per-chunk linear-attention state: S_g = lin_scale * K_lin_g^T V_g (s x e),
-// stored transposed as S_g^T ([e, s], fp32).
+// accumulated in fp32 and stored transposed as S_g^T ([e, s]) in the layer's
+// element type: the prefix sums over chunks are formed in fp32 and handed to
+// an MFMA in that same element type, so a wider store would only add traffic.
 //
 // Pages: the chunk summary K_lin_h^T V_h that the global (linear) part sums
 // over chunks (wikillm "Method", eq. 7 and 8; Su's post, "Mixed Chunking");
@@ -22,7 +24,7 @@ constexpr int BS = 128, BE = 128;  // state dims x features per block
 template <typename T>
 struct StateTile {
     using G = GemmCore<T, BS, BE, 2, 2>;
-    static constexpr int STAGE = BE * (BS * 4 + 16);
+    static constexpr int STAGE = BE * (BS * Elem<T>::kBytes + 16);
     static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
 };
 
@@ -48,10 +50,10 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(StateParams p) {
     G::run(acc, kl, pitch, BS, vt, pitch, BE, p.C, lds);
 
     const float ls = p.lin_scale;
-    float* S = p.S + ((size_t)chunk * p.e + e0) * p.s + s0;
+    char* S = (char*)p.S + (((size_t)chunk * p.e + e0) * p.s + s0) * EB;
     const int s = p.s;
-    G::template store_packed<float>(acc, lds, StateTile<T>::LDS, [&](int, int, float v) { return v * ls; },
-                                    [&](int f, int k) -> char* { return (char*)(S + (size_t)f * s + k); });
+    G::template store_packed<T>(acc, lds, StateTile<T>::LDS, [&](int, int, float v) { return v * ls; },
+                                [&](int f, int k) -> char* { return S + ((size_t)f * s + k) * EB; });
 }
 
 template <typename T>

@@ -50,7 +50,7 @@ void layout(const gau_config* c, gau_ws_layout* L) {
     L->K_quad = take(M * c->s * eb);
     L->Q_lin = take(M * c->s * eb);
     L->K_lin_t = take(M * c->s * eb);
-    L->S = take((size_t)c->B * G * es * 4);
+    L->S = take((size_t)c->B * G * es * eb);
     L->P = take((size_t)c->B * Gp * es * eb);
     L->A = take(M * (size_t)c->C * eb);
     L->Y = take(M * c->e * eb);
@@ -92,13 +92,13 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
                 break;
             }
             case GAU_STAGE_STATE: {
-                gau::StateParams p{ws + L.Vt, ws + L.K_lin_t, (float*)(ws + L.S), (int)c->B, (int)c->T,
+                gau::StateParams p{ws + L.Vt, ws + L.K_lin_t, ws + L.S, (int)c->B, (int)c->T,
                                    (int)c->e, (int)c->s, (int)c->C, c->lin_scale};
                 e = gau::launch_chunk_state(p, bf, st);
                 break;
             }
             case GAU_STAGE_SCAN: {
-                gau::ScanParams p{(const float*)(ws + L.S), ws + L.P, (int)c->B, G, (int)(c->e * c->s),
+                gau::ScanParams p{ws + L.S, ws + L.P, (int)c->B, G, (int)(c->e * c->s),
                                   c->causal ? 1 : 0};
                 e = gau::launch_chunk_scan(p, bf, st);
                 break;

@@ -24,18 +24,19 @@ struct ProjParams {
     int M, T, d, e, s;
 };
 
-// Per-chunk state S_g^T = lin_scale * V_g^T K_lin_g, [B, G, e, s] fp32.
+// Per-chunk state S_g^T = lin_scale * V_g^T K_lin_g, [B, G, e, s] in the
+// layer's element type (fp32 accumulation).
 struct StateParams {
     const void* Vt;   // [B, e, T]
     const void* Klt;  // [B, s, T]
-    float* S;         // [B, G, e, s]
+    void* S;          // [B, G, e, s]
     int B, T, e, s, C;
     float lin_scale;
 };
 
 // Exclusive prefix over chunks (causal) or the total (non-causal).
 struct ScanParams {
-    const float* S;  // [B, G, e, s]
+    const void* S;   // [B, G, e, s], element type of the layer
     void* P;         // [B, G, e, s] causal, [B, 1, e, s] otherwise
     int B, G, es;    // es = e * s
     int causal;

@@ -93,7 +93,7 @@ typedef struct {
  *   K_quad  [B*T, s]      dt
  *   Q_lin   [B*T, s]      dt
  *   K_lin_t [B, s, T]     dt    K_lin transposed per sequence
- *   S       [B, G, e, s]  fp32  S_g transposed (element (b,g,c,k) = S_g[k][c])
+ *   S       [B, G, e, s]  dt    S_g transposed (element (b,g,c,k) = S_g[k][c])
  *   P       [B, G', e, s] dt    P_g transposed; G' = G if causal, else 1
  *   A       [B*G, C, C]   dt    per-chunk attention weights
  *                               relu^2(quad_scale Q_quad K_quad^T + Bias), masked,

@@ -37,10 +37,7 @@ def run_layer(inp, B, T, d, e, s, C, causal, dtype, quad_scale=None, lin_scale=N
 def ws_array(ws, layout, name, shape, dtype):
     """A workspace region as a float64 numpy array of `shape`."""
     n = int(np.prod(shape))
-    if name == "S":
-        tdt, eb = torch.float32, 4
-    else:
-        tdt, eb = torch_dtype(dtype), (2 if dtype == "bf16" else 4)
+    tdt, eb = torch_dtype(dtype), (2 if dtype == "bf16" else 4)
     off = layout[name]
     t = ws[off:off + n * eb].view(tdt).reshape(shape)
     return t.float().cpu().numpy().astype(np.float64)

@@ -101,11 +101,9 @@ def test_emulated_kernels_match_oracle(emu, case, late):
     conv = inputs.bf16_bits_to_f32 if bf else (lambda a: a)
     eb = 2 if bf else 4
 
-    def region(name, shape, f32=False):
+    def region(name, shape):
         n = int(np.prod(shape))
         o = getattr(L, name)
-        if f32:
-            return ws[o:o + 4 * n].view(np.float32).reshape(shape).astype(np.float64)
         return conv(ws[o:o + eb * n].view(np.uint16 if bf else np.float32).reshape(shape)).astype(np.float64)
 
     tol = 2e-2 if bf else 1e-4
@@ -115,7 +113,7 @@ def test_emulated_kernels_match_oracle(emu, case, late):
         "Vt": (region("Vt", (B, e, T)), im["V"].transpose(0, 2, 1)),
         "Q_quad": (region("Q_quad", (B, T, s)), im["Q_quad"]),
         "K_lin_t": (region("K_lin_t", (B, s, T)), im["K_lin"].transpose(0, 2, 1)),
-        "S": (region("S", (B, G, e, s), True), im["S"].transpose(0, 1, 3, 2)),
+        "S": (region("S", (B, G, e, s)), im["S"].transpose(0, 1, 3, 2)),
         "Y": (region("Y", (B, T, e)), im["Y"]),
         "O": (conv(O).astype(np.float64), ref),
     }
