@@ -117,7 +117,12 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 // LDS byte offset of logical 16-byte piece c of row r in a swizzled tile.
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int NS = 2>
+// GemmCore<T, BM, BN, WGM, WGN, NS, ZR>: with ZR > 0 the core can also form a
+// side product: ZR more rows of A-type operand (K-major like A, copied into
+// each stage after B) times the B tile, accumulated per wave into ZR x 32
+// outputs (run_with_side).  Wave (wm, wn) multiplies the side rows by its own
+// B fragment wm, so the 2 x WGN waves cover the B tile's columns once.
+template <typename T, int BM, int BN, int WGM, int WGN, int NS = 2, int ZR = 0>
 struct GemmCore {
     static constexpr int NW = WGM * WGN;
     static constexpr int NT = NW * kWave;
@@ -127,9 +132,16 @@ struct GemmCore {
     static constexpr int NB = WTN / 32;
     static constexpr int KELEMS = 128 / Elem<T>::kBytes;  // K elements per chunk
     static constexpr int A_BYTES = BM * 128;
-    static constexpr int STAGE_BYTES = (BM + BN) * 128;
+    static constexpr int Z_OFF = (BM + BN) * 128;  // side rows inside a stage
+    static constexpr int STAGE_BYTES = (BM + BN + ZR) * 128;
     static constexpr int LDS_BYTES = NS * STAGE_BYTES;
     static constexpr int LOADS = (BM / 8) / NW + (BN / 8) / NW;  // DMA loads per wave per chunk
+    static constexpr int ZMB = ZR > 0 ? ZR / 32 : 1;  // side row blocks per wave
+    static constexpr int ZPIECES = ZR / 8;            // 1 KiB wave pieces of the side rows
+    // NS = 2: every wait is for all of a wave's copies, so the waves that copy
+    // a side piece may issue one more load per chunk than the others.
+    static_assert(ZR == 0 || (ZR % 32 == 0 && WGM == 2 && WTN == 64 && NS == 2 && ZPIECES <= NW),
+                  "side operand layout");
     static_assert(NS >= 2 && (NS - 2) * LOADS < 64, "stages / vmcnt range");
     static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "tile shape");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "tile rows");
@@ -176,35 +188,75 @@ struct GemmCore {
         if constexpr (NMFMA > n) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - n, 0);
     }
 
+    // Side product state of one wave (used when ZR > 0 and `on`): the side
+    // accumulators, their double-buffered fragments, and this lane's copy
+    // source (waves below ZPIECES each copy one 1 KiB piece of the side rows).
+    struct Side {
+        f32x16_t acc[ZMB];
+        u32x4_t fz[2][ZMB];
+        const char* src;
+        int wm;
+        bool on;
+    };
+
+    __device__ static __forceinline__ void load_side(Side& sd, int buf, const char* tz, int ks, int fr, int fh) {
+#pragma unroll
+        for (int i = 0; i < ZMB; ++i) sd.fz[buf][i] = *(const u32x4_t*)(tz + swz(i * 32 + fr, 2 * ks + fh));
+    }
+
+    // Copy side rows of K chunk kc into the stage at `stage_base`: wave w <
+    // ZPIECES copies rows 8w .. 8w+7 of the ZR x 128-byte side tile.
+    __device__ static __forceinline__ void issue_side(const Side& sd, char* stage_base, int kc, int wave, int) {
+        if (wave < ZPIECES)
+            __builtin_amdgcn_global_load_lds((glb_ptr_t)(sd.src + (size_t)kc * 128),
+                                             (lds_ptr_t)(stage_base + Z_OFF + wave * 1024), 16, 0, 0);
+    }
+
     // One K step of a chunk: read the fragments of step KS+1 (if any), issue
-    // the next chunk's DMA (ISSUE, step 0 only), multiply step KS.
-    template <int KS, bool ISSUE>
+    // the next chunk's DMA (ISSUE, step 0 only), multiply step KS.  SIDE adds
+    // the side product (fragments from tz) when sd.on.
+    template <int KS, bool ISSUE, bool SIDE>
     __device__ static __forceinline__ void step(f32x16_t (&acc)[MB][NB], u32x4_t (&fa)[2][MB],
                                                 u32x4_t (&fb)[2][NB], const char* ta, const char* tb,
                                                 const DmaOperand<BM, NW>& da, const DmaOperand<BN, NW>& db,
-                                                char* nxt, int kc_next, int wave, int fr, int fh) {
+                                                char* nxt, int kc_next, int wave, int fr, int fh, Side& sd,
+                                                const char* tz, int lane) {
         constexpr int NL = DmaOperand<BM, NW>::kLoads + DmaOperand<BN, NW>::kLoads;
         if constexpr (KS < 3) load_frags(fa[(KS + 1) & 1], fb[(KS + 1) & 1], ta, tb, KS + 1, fr, fh);
+        if constexpr (SIDE && KS < 3) {
+            if (sd.on) load_side(sd, (KS + 1) & 1, tz, KS + 1, fr, fh);
+        }
         if constexpr (ISSUE && KS == 0) {
             da.issue(nxt, kc_next, wave);
             db.issue(nxt + A_BYTES, kc_next, wave);
+            if constexpr (SIDE) {
+                if (sd.on) issue_side(sd, nxt, kc_next, wave, lane);
+            }
         }
         mma_step(acc, fa[KS & 1], fb[KS & 1]);
+        if constexpr (SIDE) {
+            if (sd.on) {
+                const u32x4_t& bsel = sd.wm == 0 ? fb[KS & 1][0] : fb[KS & 1][1];
+#pragma unroll
+                for (int i = 0; i < ZMB; ++i) mma32(sd.acc[i], sd.fz[KS & 1][i], bsel, T());
+            }
+        }
         sched_step<MB * NB, (KS < 3 ? MB + NB : 0), ((ISSUE && KS == 0) ? NL : 0)>();
     }
 
     // One 128-byte K chunk from LDS (four K steps; fragments double-buffered
     // in registers).  With ISSUE the DMA copy of the next chunk is spread over
     // the first step's MFMAs.
-    template <bool ISSUE>
+    template <bool ISSUE, bool SIDE>
     __device__ static __forceinline__ void chunk(f32x16_t (&acc)[MB][NB], u32x4_t (&fa)[2][MB],
                                                  u32x4_t (&fb)[2][NB], const char* ta, const char* tb,
                                                  const DmaOperand<BM, NW>& da, const DmaOperand<BN, NW>& db,
-                                                 char* nxt, int kc_next, int wave, int fr, int fh) {
-        step<0, ISSUE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh);
-        step<1, ISSUE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh);
-        step<2, ISSUE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh);
-        step<3, ISSUE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh);
+                                                 char* nxt, int kc_next, int wave, int fr, int fh, Side& sd,
+                                                 const char* tz, int lane) {
+        step<0, ISSUE, SIDE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh, sd, tz, lane);
+        step<1, ISSUE, SIDE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh, sd, tz, lane);
+        step<2, ISSUE, SIDE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh, sd, tz, lane);
+        step<3, ISSUE, SIDE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh, sd, tz, lane);
     }
 
     // Wait until this wave's copy of the current chunk has landed, given that
@@ -220,7 +272,8 @@ struct GemmCore {
     }
 
     // acc += A . B^T where A's and B's K axes are the concatenations
-    // a0|a1 and b0|b1 (a0.chunks == b0.chunks, a1.chunks == b1.chunks).
+    // a0|a1 and b0|b1 (a0.chunks == b0.chunks, a1.chunks == b1.chunks); with
+    // SIDE and sd.on also the side product.
     //
     // A ring of NS LDS stages, NS-1 chunk copies in flight.  Iteration kt:
     // issue the copy of chunk kt+NS-1 into the stage chunk kt-1 used (free
@@ -229,9 +282,10 @@ struct GemmCore {
     // then wait for this wave's copy of chunk kt+1 (the later ones may still
     // fly), barrier, and read chunk kt+1's first fragments.  Ends with a
     // barrier (LDS free for the epilogue).
-    __device__ static __forceinline__ void run_segs(f32x16_t (&acc)[MB][NB], const KSeg& a0, const KSeg& a1,
+    template <bool SIDE>
+    __device__ static __forceinline__ void run_impl(f32x16_t (&acc)[MB][NB], const KSeg& a0, const KSeg& a1,
                                                     int rows_a, const KSeg& b0, const KSeg& b1, int rows_b,
-                                                    char* lds) {
+                                                    char* lds, Side& sd) {
         const int tid = threadIdx.x;
         const int wave = tid / kWave;
         const int lane = tid % kWave;
@@ -249,6 +303,9 @@ struct GemmCore {
             if (c < nk) {
                 da.issue(lds + c * STAGE_BYTES, c, wave);
                 db.issue(lds + c * STAGE_BYTES + A_BYTES, c, wave);
+                if constexpr (SIDE) {
+                    if (sd.on) issue_side(sd, lds + c * STAGE_BYTES, c, wave, lane);
+                }
             }
         wait_chunk(min(NS - 2, nk - 1));
         __syncthreads();
@@ -256,6 +313,9 @@ struct GemmCore {
         u32x4_t fa[2][MB], fb[2][NB];
         const int oa = (wm * WTM) * 128, ob = A_BYTES + (wn * WTN) * 128;
         load_frags(fa[0], fb[0], lds + oa, lds + ob, 0, fr, fh);
+        if constexpr (SIDE) {
+            if (sd.on) load_side(sd, 0, lds + Z_OFF, 0, fr, fh);
+        }
 
         // main loop: chunks whose iteration still issues a copy
         int stage = 0;
@@ -263,26 +323,42 @@ struct GemmCore {
         for (; kt + NS - 1 < nk; ++kt) {
             char* cur = lds + stage * STAGE_BYTES;
             char* dst = lds + (stage == 0 ? NS - 1 : stage - 1) * STAGE_BYTES;
-            chunk<true>(acc, fa, fb, cur + oa, cur + ob, da, db, dst, kt + NS - 1, wave, fr, fh);
+            chunk<true, SIDE>(acc, fa, fb, cur + oa, cur + ob, da, db, dst, kt + NS - 1, wave, fr, fh, sd,
+                              cur + Z_OFF, lane);
             wait_chunk(min(NS - 2, nk - 2 - kt));
             __syncthreads();
             stage = stage + 1 == NS ? 0 : stage + 1;
             char* n = lds + stage * STAGE_BYTES;
             load_frags(fa[0], fb[0], n + oa, n + ob, 0, fr, fh);
+            if constexpr (SIDE) {
+                if (sd.on) load_side(sd, 0, n + Z_OFF, 0, fr, fh);
+            }
         }
         // tail: the last NS-1 chunks (all copies issued)
         for (; kt < nk; ++kt) {
             char* cur = lds + stage * STAGE_BYTES;
-            chunk<false>(acc, fa, fb, cur + oa, cur + ob, da, db, nullptr, 0, wave, fr, fh);
+            chunk<false, SIDE>(acc, fa, fb, cur + oa, cur + ob, da, db, nullptr, 0, wave, fr, fh, sd, cur + Z_OFF,
+                               lane);
             if (kt + 1 < nk) {
                 wait_chunk(min(NS - 2, nk - 2 - kt));
                 __syncthreads();
                 stage = stage + 1 == NS ? 0 : stage + 1;
                 char* n = lds + stage * STAGE_BYTES;
                 load_frags(fa[0], fb[0], n + oa, n + ob, 0, fr, fh);
+                if constexpr (SIDE) {
+                    if (sd.on) load_side(sd, 0, n + Z_OFF, 0, fr, fh);
+                }
             }
         }
         __syncthreads();  // LDS free for the epilogue
+    }
+
+    __device__ static __forceinline__ void run_segs(f32x16_t (&acc)[MB][NB], const KSeg& a0, const KSeg& a1,
+                                                    int rows_a, const KSeg& b0, const KSeg& b1, int rows_b,
+                                                    char* lds) {
+        Side none;
+        none.on = false;
+        run_impl<false>(acc, a0, a1, rows_a, b0, b1, rows_b, lds, none);
     }
 
     // acc += A . B^T over K elements (a multiple of KELEMS), one segment each.
@@ -291,6 +367,32 @@ struct GemmCore {
         const int nk = K / KELEMS;
         run_segs(acc, KSeg{a, pitch_a, nk}, KSeg{a, pitch_a, 0}, rows_a, KSeg{b, pitch_b, nk}, KSeg{b, pitch_b, 0},
                  rows_b, lds);
+    }
+
+    // As run(), plus (when `on`, block-uniform) the side product of the ZR rows
+    // at z (K-major, rows z_pitch bytes apart, all present) with the B tile:
+    // sd.acc[i] (16 floats per lane) holds side rows i*32 + 8*(r/4) + 4*(l/32)
+    // + r%4 (lane l, register r) times B-tile column wn*64 + wm*32 + l%32.
+    __device__ static __forceinline__ void run_with_side(f32x16_t (&acc)[MB][NB], Side& sd, const char* a,
+                                                         size_t pitch_a, int rows_a, const char* b, size_t pitch_b,
+                                                         int rows_b, int K, const char* z, size_t z_pitch, bool on,
+                                                         char* lds) {
+        static_assert(ZR > 0, "core without side rows");
+        const int nk = K / KELEMS;
+        const int wave = threadIdx.x / kWave;
+        const int lane = threadIdx.x % kWave;
+        sd.on = on;
+        sd.wm = wave / WGN;
+#pragma unroll
+        for (int i = 0; i < ZMB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sd.acc[i][r] = 0.f;
+        // lane's 16-byte piece: row 8*wave + lane/8 (waves below ZPIECES),
+        // physical piece lane % 8, logical piece (lane % 8) ^ perm(row)
+        const int row = (wave < ZPIECES ? wave : 0) * 8 + (lane >> 3);
+        sd.src = z + (size_t)row * z_pitch + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
+        run_impl<true>(acc, KSeg{a, pitch_a, nk}, KSeg{a, pitch_a, 0}, rows_a, KSeg{b, pitch_b, nk},
+                       KSeg{b, pitch_b, 0}, rows_b, lds, sd);
     }
 
     // Apply f4(row0, col, v) to groups of four consecutive accumulator rows of

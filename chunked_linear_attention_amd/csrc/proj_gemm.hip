@@ -22,7 +22,8 @@
 // dispatched first and cost half a U/V tile each, so the launch is about an
 // eighth of a round longer than U and V alone instead of a second launch of
 // small, latency-bound blocks.  U/V tiles are assigned to XCDs in contiguous
-// ranges.
+// ranges (the 2e/256 column tiles of one token tile together, so they share
+// the X tile in one L2).
 #include "gau_launch.h"
 #include "gemm_core.h"
 
@@ -32,10 +33,14 @@ namespace {
 
 constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4;  // U/V tiles, wave grid
 constexpr int ZF = 128, ZT = 256;                    // Z tiles: features x tokens
+constexpr int ZHOSTS = 4;                            // U tiles that carry a Z slice
 
-template <typename T>
+// ZR = 0: Z in tiles of its own; ZR = s / ZHOSTS: each of the first ZHOSTS U
+// tiles of a token tile also forms ZR features of Z (the GEMM core's side
+// product, sharing the tile's X chunks and B fragments).
+template <typename T, int ZR>
 struct ProjTile {
-    using G = GemmCore<T, BM, BN, WGM, WGN>;
+    using G = GemmCore<T, BM, BN, WGM, WGN, 2, ZR>;
     using GZ = GemmCore<T, ZF, ZT, WGM, WGN>;
     static constexpr int EB = Elem<T>::kBytes;
     static constexpr int STAGE = (BM * (BN * EB + 16) > 160 * 1024 - 1024) ? BM / WGM * (BN * EB + 16)
@@ -44,10 +49,104 @@ struct ProjTile {
     static constexpr int LDS = CORE > STAGE ? CORE : STAGE;
 };
 
-// U and V: one 256 x 256 tile (logical index bid over the U/V tiles).
-template <typename T>
+// Epilogue of a Z slice formed as a side product: ZR features f0.. of Z for the
+// 256 tokens m0.. .  Applies SiLU and the four heads and stores Q_quad, K_quad,
+// Q_lin (token-major) and K_lin_t (feature-major) through LDS, all four heads
+// in one staging pass when they fit, else one head per pass.
+template <typename T, int ZR, typename Side>
+__device__ __forceinline__ void z_side_epilogue(const ProjParams& p, Side& sd, int m0, int f0, char* lds,
+                                                int lds_bytes) {
+    constexpr int EB = Elem<T>::kBytes;
+    constexpr int ZMB = ZR / 32;
+    constexpr int NT = WGM * WGN * kWave;
+    constexpr int TP = ZR * EB + 16;  // token-major staging pitch
+    constexpr int FP = BN * EB + 16;  // feature-major staging pitch
+    constexpr int HEAD_T = BN * TP;   // bytes of one token-major head
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int c = lane & 31, h = lane >> 5;
+    const int tok = wn * 64 + wm * 32 + c;  // B-tile column this lane's side outputs belong to
+    const int M = p.M, T_ = p.T, s = p.s;
+    const bool one_pass = 3 * HEAD_T + ZR * FP <= lds_bytes;
+#pragma unroll
+    for (int i = 0; i < ZMB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sd.acc[i][r] = silu(sd.acc[i][r]);
+
+    // stage head hd (token-major heads at hd * HEAD_T when one_pass, else at 0;
+    // K_lin after the three token-major heads, or at 0)
+    auto stage_head = [&](int hd, char* base) {
+        const f32x4_t* gam = (const f32x4_t*)(p.scale + hd * s + f0);
+        const f32x4_t* bet = (const f32x4_t*)(p.offset + hd * s + f0);
+#pragma unroll
+        for (int i = 0; i < ZMB; ++i)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int zr0 = i * 32 + 8 * g4 + 4 * h;  // four consecutive Z features
+                const f32x4_t gm = gam[zr0 / 4], bt = bet[zr0 / 4];
+                const float v0 = sd.acc[i][4 * g4 + 0] * gm.x + bt.x, v1 = sd.acc[i][4 * g4 + 1] * gm.y + bt.y;
+                const float v2 = sd.acc[i][4 * g4 + 2] * gm.z + bt.z, v3 = sd.acc[i][4 * g4 + 3] * gm.w + bt.w;
+                if (hd < 3) {
+                    char* q = base + tok * TP + zr0 * EB;
+                    if constexpr (EB == 2) {
+                        *(u32x2_t*)q = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+                    } else {
+                        *(f32x4_t*)q = f32x4_t{v0, v1, v2, v3};
+                    }
+                } else {
+                    char* q = base + zr0 * FP + tok * EB;
+                    Elem<T>::put(q, v0);
+                    Elem<T>::put(q + FP, v1);
+                    Elem<T>::put(q + 2 * FP, v2);
+                    Elem<T>::put(q + 3 * FP, v3);
+                }
+            }
+    };
+    auto store_head = [&](int hd, const char* base) {
+        if (hd < 3) {
+            char* dst = (char*)(hd == 0 ? p.Qq : hd == 1 ? p.Kq : p.Ql);
+            constexpr int VPR = ZR * EB / 16;  // 16-byte vectors per token row
+            for (int idx = threadIdx.x; idx < BN * VPR; idx += NT) {
+                const int t = idx / VPR, v = idx - t * VPR;
+                const int m = m0 + t;
+                if (m < M)
+                    *(u32x4_t*)(dst + ((size_t)m * s + f0) * EB + v * 16) = *(const u32x4_t*)(base + t * TP + v * 16);
+            }
+        } else {
+            char* Klt = (char*)p.Klt;
+            constexpr int VPR = BN * EB / 16;  // 16-byte vectors per feature row
+            constexpr int TPV = 16 / EB;       // tokens per vector
+            for (int idx = threadIdx.x; idx < ZR * VPR; idx += NT) {
+                const int zr = idx / VPR, v = idx - zr * VPR;
+                const int m = m0 + v * TPV;
+                if (m < M) {
+                    const int b = m / T_, t = m - b * T_;
+                    *(u32x4_t*)(Klt + (((size_t)b * s + f0 + zr) * T_ + t) * EB) =
+                        *(const u32x4_t*)(base + zr * FP + v * 16);
+                }
+            }
+        }
+    };
+    if (one_pass) {
+        __syncthreads();
+        for (int hd = 0; hd < 4; ++hd) stage_head(hd, lds + hd * HEAD_T);
+        __syncthreads();
+        for (int hd = 0; hd < 4; ++hd) store_head(hd, lds + hd * HEAD_T);
+    } else {
+        for (int hd = 0; hd < 4; ++hd) {
+            __syncthreads();
+            stage_head(hd, lds);
+            __syncthreads();
+            store_head(hd, lds);
+        }
+    }
+}
+
+// U and V: one 256 x 256 tile (logical index bid over the U/V tiles); with
+// ZR > 0 the first ZHOSTS U tiles of each token tile also form a Z slice.
+template <typename T, int ZR>
 __device__ __forceinline__ void uv_tile(const ProjParams& p, int bid, char* lds) {
-    using G = typename ProjTile<T>::G;
+    using G = typename ProjTile<T, ZR>::G;
     constexpr int EB = Elem<T>::kBytes;
     const int ntu = p.e / BN;  // tiles per section
     const int ntiles = 2 * ntu;
@@ -67,10 +166,21 @@ __device__ __forceinline__ void uv_tile(const ProjParams& p, int bid, char* lds)
     // (acc = tile^T); Vt is feature-major, so the tokens are A.
     f32x16_t acc[G::MB][G::NB];
     G::zero(acc);
-    G::run(acc, is_v ? xt : wt, pitch, is_v ? rows_x : BN, is_v ? wt : xt, pitch, is_v ? BN : rows_x, p.d, lds);
+    typename G::Side sd;
+    const bool side = ZR > 0 && !is_v && nt < ZHOSTS;
+    bool ran = false;
+    if constexpr (ZR > 0) {
+        if (side) {  // block-uniform: the side product has a main loop of its own
+            G::run_with_side(acc, sd, wt, pitch, BN, xt, pitch, rows_x, p.d,
+                             (const char*)p.W_z + (size_t)(nt * ZR) * pitch, pitch, true, lds);
+            ran = true;
+        }
+    }
+    if (!ran)
+        G::run(acc, is_v ? xt : wt, pitch, is_v ? rows_x : BN, is_v ? wt : xt, pitch, is_v ? BN : rows_x, p.d, lds);
     G::transform(acc, [](int, int, float v) { return silu(v); });
 
-    constexpr int LDS = ProjTile<T>::LDS;
+    constexpr int LDS = ProjTile<T, ZR>::LDS;
     const int M = p.M, T_ = p.T;
     auto ident = [](int, int, float v) { return v; };
     if (!is_v) {
@@ -80,6 +190,9 @@ __device__ __forceinline__ void uv_tile(const ProjParams& p, int bid, char* lds)
             const int m = m0 + tok;
             return m < M ? U + ((size_t)m * p.e + c0 + feat) * EB : nullptr;
         });
+        if constexpr (ZR > 0) {
+            if (side) z_side_epilogue<T, ZR>(p, sd, m0, nt * ZR, lds, LDS);
+        }
     } else {
         // acc rows = tokens, columns = features
         char* Vt = (char*)p.Vt;
@@ -97,7 +210,7 @@ __device__ __forceinline__ void uv_tile(const ProjParams& p, int bid, char* lds)
 // feature-major.
 template <typename T>
 __device__ __forceinline__ void z_tile(const ProjParams& p, int zb, char* lds) {
-    using G = typename ProjTile<T>::GZ;
+    using G = typename ProjTile<T, 0>::GZ;
     constexpr int EB = Elem<T>::kBytes;
     const int nf = p.s / ZF;
     const int ft = zb % nf;
@@ -113,7 +226,7 @@ __device__ __forceinline__ void z_tile(const ProjParams& p, int zb, char* lds) {
            rows_x, p.d, lds);
     G::transform(acc, [](int, int, float v) { return silu(v); });
 
-    constexpr int LDS = ProjTile<T>::LDS;
+    constexpr int LDS = ProjTile<T, 0>::LDS;
     const int M = p.M, T_ = p.T, s = p.s;
     for (int h = 0; h < 4; ++h) {
         const float* gam = p.scale + h * s + f0;
@@ -137,33 +250,42 @@ __device__ __forceinline__ void z_tile(const ProjParams& p, int zb, char* lds) {
     }
 }
 
-template <typename T>
+template <typename T, int ZR>
 __global__ __launch_bounds__(512) void proj_kernel(ProjParams p) {
     extern __shared__ __align__(16) char lds[];
-    const int nz = (p.s / ZF) * ((p.M + ZT - 1) / ZT);
+    const int nz = ZR > 0 ? 0 : (p.s / ZF) * ((p.M + ZT - 1) / ZT);
     const int b = blockIdx.x;
     if (b < nz)
         z_tile<T>(p, b, lds);
     else
-        uv_tile<T>(p, xcd_remap(b - nz, gridDim.x - nz), lds);
+        uv_tile<T, ZR>(p, xcd_remap(b - nz, gridDim.x - nz), lds);
 }
 
-template <typename T>
+template <typename T, int ZR>
 hipError_t launch_t(const ProjParams& p, hipStream_t st) {
-    constexpr int LDS = ProjTile<T>::LDS;
+    constexpr int LDS = ProjTile<T, ZR>::LDS;
     static_assert(LDS <= 160 * 1024, "projection LDS over budget");
     const int mtiles = (p.M + BM - 1) / BM;
-    const int blocks = (p.s / ZF) * ((p.M + ZT - 1) / ZT) + 2 * (p.e / BN) * mtiles;
-    hipError_t e = allow_lds<proj_kernel<T>>(LDS);
+    const int nz = ZR > 0 ? 0 : (p.s / ZF) * ((p.M + ZT - 1) / ZT);
+    const int blocks = nz + 2 * (p.e / BN) * mtiles;
+    hipError_t e = allow_lds<proj_kernel<T, ZR>>(LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(proj_kernel<T>, dim3(blocks), dim3(512), LDS, st, p);
+    hipLaunchKernelGGL((proj_kernel<T, ZR>), dim3(blocks), dim3(512), LDS, st, p);
     return hipGetLastError();
+}
+
+// Z as side products of U tiles when there are ZHOSTS U tiles per token tile,
+// in tiles of its own otherwise.
+template <typename T>
+hipError_t dispatch(const ProjParams& p, hipStream_t st) {
+    if (p.e / BN >= ZHOSTS) return p.s == 128 ? launch_t<T, 128 / ZHOSTS>(p, st) : launch_t<T, 256 / ZHOSTS>(p, st);
+    return launch_t<T, 0>(p, st);
 }
 
 }  // namespace
 
 hipError_t launch_proj(const ProjParams& p, bool bf16_storage, hipStream_t st) {
-    return bf16_storage ? launch_t<bf16>(p, st) : launch_t<float>(p, st);
+    return bf16_storage ? dispatch<bf16>(p, st) : dispatch<float>(p, st);
 }
 
 }  // namespace gau

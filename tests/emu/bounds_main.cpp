@@ -115,6 +115,8 @@ int main(int argc, char** argv) {
         {3, 128, 128, 256, 128, 128, true, true},   {2, 192, 384, 768, 128, 64, true, true},
         {1, 1024, 256, 512, 128, 256, true, true},  {2, 512, 1024, 2048, 128, 256, true, true},
         {1, 64, 128, 256, 128, 64, true, true},     {1, 64, 128, 256, 128, 64, false, false},
+        {1, 256, 128, 1024, 128, 64, false, true},  {1, 512, 256, 1024, 256, 128, true, true},
+        {1, 320, 128, 1024, 256, 64, false, false}, {2, 256, 128, 1280, 128, 128, true, true},
     };
     std::vector<Cfg> full = {
         {8, 1024, 768, 1536, 128, 256, true, true}, {4, 4096, 768, 1536, 128, 256, true, true},

@@ -66,6 +66,8 @@ CASES = [
     (2, 256, 256, 512, 128, 128, "bf16", True),
     (1, 512, 128, 256, 256, 256, "bf16", False),
     (1, 512, 128, 256, 128, 512, "bf16", True),
+    (1, 256, 128, 1024, 128, 64, "f32", True),      # Z formed inside the U tiles (s = 128)
+    (1, 256, 128, 1024, 256, 128, "bf16", False),   # Z formed inside the U tiles (s = 256)
 ]
 
 

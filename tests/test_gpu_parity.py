@@ -59,6 +59,9 @@ SMALL = [
     (1, 256, 128, 256, 256, 128, "f32", False),
     (3, 128, 128, 256, 128, 128, "bf16", True),    # C = T: one chunk per sequence
     (2, 192, 384, 768, 128, 64, "bf16", True),     # d, e not powers of two
+    (1, 256, 128, 1024, 128, 64, "f32", True),     # e >= 1024: Z formed inside the U tiles
+    (1, 320, 256, 1024, 256, 64, "bf16", False),   # ... with s = 256 and a ragged row tile
+    (2, 256, 128, 1280, 128, 128, "bf16", True),
 ]
 
 
