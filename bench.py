@@ -184,7 +184,7 @@ def summarize_traffic(fetch_csv, write_csv, command):
         blits = [r for r in rows if r[0] == "__amd_rocclr_copyBuffer"]
         big = max(g for _, g, _ in blits) if blits else 0
         copy = [v for _, g, v in blits if g == big]
-        dom = [v for k, _, v in rows if f"{DOMINANT}_kernel<gau::bf16>" in k]
+        dom = [v for k, _, v in rows if f"{DOMINANT}_kernel<gau::bf16" in k]
         if len(copy) != 3 or not dom:
             raise SystemExit(f"{csv_path}: expected 3 calibration copies and {DOMINANT} dispatches")
         kib_copy, kib_dom = sum(copy) / len(copy), sum(dom) / len(dom)
