@@ -14,25 +14,41 @@
 // so the local and global terms accumulate into the same registers.  A causal
 // query tile reads only the keys up to its last query (later keys are masked
 // to zero).  The gate multiplies the fp32 accumulator by U in the epilogue,
-// which stores Y token-major.
+// which stores Y token-major; the block's U values are loaded into registers
+// before the main loop, so their latency overlaps the chunk copies instead of
+// adding one more round trip after them.
 #include "gau_launch.h"
 #include "gemm_core.h"
 
 namespace gau {
 namespace {
 
-constexpr int BF = 128;  // features per block (accumulator rows)
+constexpr int BF = 128;         // features per block (accumulator rows)
+constexpr int WGM = 2, WGN = 2;  // wave grid
 
 template <typename T, int BQ>
 struct AttnTile {
-    using G = GemmCore<T, BF, BQ, 2, 2>;
+    using G = GemmCore<T, BF, BQ, WGM, WGN>;
     static constexpr int EB = Elem<T>::kBytes;
     static constexpr int STAGE = BQ * (BF * EB + 16);
     static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
 };
 
+// The gate values of one lane: for each accumulator block (i, j) and group
+// g4 of four rows, four consecutive features of one token of U.
+template <typename T>
+struct GateVec;
+template <>
+struct GateVec<bf16> {
+    using type = u32x2_t;
+};
+template <>
+struct GateVec<float> {
+    using type = f32x4_t;
+};
+
 template <typename T, int BQ>
-__global__ __launch_bounds__(256) void chunk_attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(WGM * WGN * kWave) void chunk_attn_kernel(AttnParams p) {
     extern __shared__ __align__(16) char lds[];
     using G = typename AttnTile<T, BQ>::G;
     constexpr int EB = Elem<T>::kBytes;
@@ -56,30 +72,52 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(AttnParams p) {
     const KSeg b0{(const char*)p.A + ((size_t)chunk * p.C + q0) * p.C * EB, (size_t)p.C * EB, keys / KELEMS};
     const KSeg b1{(const char*)p.Ql + (tok0 + q0) * p.s * EB, (size_t)p.s * EB, p.s / KELEMS};
 
+    // gate: acc rows are features f0 + row, columns are queries q0 + col; the
+    // four rows a lane holds are four consecutive features of one token of U
+    // (the accumulator layout of the MFMA core, as in transform4)
+    const char* U = (const char*)p.U + ((tok0 + q0) * p.e + f0) * EB;
+    const size_t pitch_e = (size_t)p.e * EB;
+    using GV = typename GateVec<T>::type;
+    GV gate[G::MB][G::NB][4];
+    {
+        const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+        const int wm = wave / WGN, wn = wave % WGN;
+        const int c = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+            for (int j = 0; j < G::NB; ++j)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int row0 = wm * G::WTM + i * 32 + 8 * g4 + 4 * h;
+                    const int col = wn * G::WTN + j * 32 + c;
+                    gate[i][j][g4] = *(const GV*)(U + (size_t)col * pitch_e + (size_t)row0 * EB);
+                }
+    }
+
     f32x16_t acc[G::MB][G::NB];
     G::zero(acc);
     G::run_segs(acc, a0, a1, BF, b0, b1, BQ, lds);
 
-    // gate: acc rows are features f0 + row, columns are queries q0 + col; the
-    // four rows a lane holds are four consecutive features of one token of U
-    const char* U = (const char*)p.U + ((tok0 + q0) * p.e + f0) * EB;
-    const size_t pitch_e = (size_t)p.e * EB;
-    G::transform4(acc, [&](int row0, int col, float (&v)[4]) {
-        const char* u = U + (size_t)col * pitch_e + (size_t)row0 * EB;
-        if constexpr (EB == 2) {
-            const u32x2_t w = *(const u32x2_t*)u;
-            v[0] *= __uint_as_float(w.x << 16);
-            v[1] *= __uint_as_float(w.x & 0xFFFF0000u);
-            v[2] *= __uint_as_float(w.y << 16);
-            v[3] *= __uint_as_float(w.y & 0xFFFF0000u);
-        } else {
-            const f32x4_t w = *(const f32x4_t*)u;
-            v[0] *= w.x;
-            v[1] *= w.y;
-            v[2] *= w.z;
-            v[3] *= w.w;
-        }
-    });
+#pragma unroll
+    for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < G::NB; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const GV w = gate[i][j][g4];
+                if constexpr (EB == 2) {
+                    acc[i][j][4 * g4 + 0] *= __uint_as_float(w.x << 16);
+                    acc[i][j][4 * g4 + 1] *= __uint_as_float(w.x & 0xFFFF0000u);
+                    acc[i][j][4 * g4 + 2] *= __uint_as_float(w.y << 16);
+                    acc[i][j][4 * g4 + 3] *= __uint_as_float(w.y & 0xFFFF0000u);
+                } else {
+                    acc[i][j][4 * g4 + 0] *= w.x;
+                    acc[i][j][4 * g4 + 1] *= w.y;
+                    acc[i][j][4 * g4 + 2] *= w.z;
+                    acc[i][j][4 * g4 + 3] *= w.w;
+                }
+            }
 
     char* Y = (char*)p.Y + ((tok0 + q0) * p.e + f0) * EB;
     auto ident = [](int, int, float v) { return v; };
@@ -94,7 +132,7 @@ hipError_t launch_t(const AttnParams& p, hipStream_t st) {
     const int blocks = (p.e / BF) * (p.C / BQ) * p.B * (p.T / p.C);
     hipError_t e = allow_lds<chunk_attn_kernel<T, BQ>>(LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_attn_kernel<T, BQ>), dim3(blocks), dim3(256), LDS, st, p);
+    hipLaunchKernelGGL((chunk_attn_kernel<T, BQ>), dim3(blocks), dim3(WGM * WGN * kWave), LDS, st, p);
     return hipGetLastError();
 }
 

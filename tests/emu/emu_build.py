@@ -73,6 +73,9 @@ def _generate(gen):
                    r"\1* \2 = (\1*)::emu::static_shared(__LINE__, sizeof(\1) * (\3));", s)
         # AMDGPU occupancy attributes have no meaning on the host
         s = re.sub(r"__attribute__\(\(amdgpu_[a-z_]+\([^)]*\)\)\)", "", s)
+        # inline assembly has no host meaning: refuse rather than miscompile
+        if re.search(r"\b(__)?asm(__)?\s*(volatile\s*|__volatile__\s*)?\(", s):
+            raise RuntimeError(f"{f}: inline assembly the emulation build does not rewrite")
         if "__shared__" in s:
             raise RuntimeError(f"{f}: LDS declaration the emulation build does not rewrite")
         with open(os.path.join(csrc, f), "w") as fh:
