@@ -301,6 +301,15 @@ def main():
     torch.cuda.synchronize()
     per_stage = {n: float(np.mean([stage_ev[k][i].elapsed_time(stage_ev[k][i + 1]) for k in range(K)]))
                  for i, n in enumerate(STAGES)}  # ms
+    # scores and states as the forward runs them: one launch for both
+    i_sc = STAGES.index("chunk_scores")
+    pair_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in pair_ev:
+        a.record(stream)
+        g.forward_stages(gc, i_sc, i_sc + 1, *args_l, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    pair_ms = float(np.mean([a.elapsed_time(b) for a, b in pair_ev]))
     t1 = time.perf_counter()
     for _ in range(K):
         step()
@@ -339,6 +348,7 @@ def main():
         "kernels_us": {n: per_stage[n] * 1e3 for n in STAGES},
         "kernels_gbs": {n: bytes_[n] / (per_stage[n] * 1e-3) / 1e9 for n in STAGES},
         "kernels_tflops": {n: flops[n] / (per_stage[n] * 1e-3) / 1e12 for n in STAGES},
+        "kernels_us_combined": {"chunk_scores+chunk_state": pair_ms * 1e3},
         "ms_per_step_single_call": wall_plain * 1e3 / K,
     }
     if not args.no_cpu_baseline:

@@ -72,6 +72,11 @@ gau_status check_layer_ptrs(const LayerPtrs& a) {
     return GAU_OK;
 }
 
+gau::StateParams state_params(const gau_config* c, const gau_ws_layout& L, char* ws) {
+    return gau::StateParams{ws + L.Vt, ws + L.K_lin_t, ws + L.S, (int)c->B, (int)c->T,
+                            (int)c->e, (int)c->s, (int)c->C, c->lin_scale};
+}
+
 // Stages first..last of one layer.  `residual` != nullptr makes the output
 // stage write O = residual + Y W_o in fp32.
 gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs& a, void* O, const float* residual,
@@ -92,9 +97,7 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
                 break;
             }
             case GAU_STAGE_STATE: {
-                gau::StateParams p{ws + L.Vt, ws + L.K_lin_t, ws + L.S, (int)c->B, (int)c->T,
-                                   (int)c->e, (int)c->s, (int)c->C, c->lin_scale};
-                e = gau::launch_chunk_state(p, bf, st);
+                e = gau::launch_chunk_state(state_params(c, L, ws), bf, st);
                 break;
             }
             case GAU_STAGE_SCAN: {
@@ -104,9 +107,14 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
                 break;
             }
             case GAU_STAGE_SCORES: {
-                gau::ScoresParams p{ws + L.Q_quad, ws + L.K_quad, a.relpos, ws + L.A, (int)c->B, (int)c->T,
-                                    (int)c->s, (int)c->C, c->causal ? 1 : 0, c->quad_scale};
-                e = gau::launch_chunk_scores(p, bf, st);
+                const gau::ScoresParams p{ws + L.Q_quad, ws + L.K_quad, a.relpos, ws + L.A, (int)c->B, (int)c->T,
+                                          (int)c->s, (int)c->C, c->causal ? 1 : 0, c->quad_scale};
+                if (last >= GAU_STAGE_STATE) {  // both: one launch, the state stage is done with it
+                    e = gau::launch_chunk_scores_state(p, state_params(c, L, ws), bf, st);
+                    ++stage;
+                } else {
+                    e = gau::launch_chunk_scores(p, bf, st);
+                }
                 break;
             }
             case GAU_STAGE_ATTN: {

@@ -88,6 +88,9 @@ hipError_t launch_proj(const ProjParams& p, bool bf16_storage, hipStream_t st); 
 hipError_t launch_chunk_state(const StateParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_chunk_scan(const ScanParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_chunk_scores(const ScoresParams& p, bool bf16_storage, hipStream_t st);
+// Scores and states in one launch (the forward pass's stages 1 and 2).
+hipError_t launch_chunk_scores_state(const ScoresParams& ps, const StateParams& pt, bool bf16_storage,
+                                     hipStream_t st);
 hipError_t launch_chunk_attn(const AttnParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_out_gemm(const OutParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_rms_norm(const NormParams& p, bool bf16_storage, hipStream_t st);

@@ -58,7 +58,7 @@ static void run(const Cfg& c, const std::string& only) {
     void* Kq = buf(M * c.s * eb);
     void* Ql = buf(M * c.s * eb);
     void* Klt = buf(M * c.s * eb);
-    float* S = (float*)buf((size_t)c.B * G * c.e * c.s * 4);
+    void* S = buf((size_t)c.B * G * c.e * c.s * eb);
     void* P = buf((size_t)c.B * Gp * c.e * c.s * eb);
     void* A = buf(M * c.C * eb);
     void* Y = buf(M * c.e * eb);
@@ -76,6 +76,7 @@ static void run(const Cfg& c, const std::string& only) {
     t("chunk_scores", [&] { CHECK(launch_chunk_scores(sp, c.bf, nullptr)); });
     StateParams stp{Vt, Klt, S, c.B, c.T, c.e, c.s, c.C, 1.0f / c.C};
     t("chunk_state", [&] { CHECK(launch_chunk_state(stp, c.bf, nullptr)); });
+    t("chunk_scores_state", [&] { CHECK(launch_chunk_scores_state(sp, stp, c.bf, nullptr)); });
     ScanParams scp{S, P, c.B, G, c.e * c.s, c.causal ? 1 : 0};
     t("chunk_scan", [&] { CHECK(launch_chunk_scan(scp, c.bf, nullptr)); });
     AttnParams ap{A, Ql, Vt, P, U, Y, c.B, c.T, c.e, c.s, c.C, c.causal ? 1 : 0};
