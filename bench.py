@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4 SIMDs x 1024 dense bf16 FLOP/clk x 2.4 GHz
+PEAK_FP32_TFLOPS = 157.3    # dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "GAU/FLASH layer fwd tokens/sec at d=768 T=8192 C=256; % bf16 MFMA peak"
 STAGES = ["proj", "chunk_scores", "chunk_state", "chunk_scan", "chunk_attn", "out_gemm"]
@@ -218,6 +219,66 @@ def summarize_traffic(fetch_csv, write_csv, command):
     print(json.dumps(rec))
 
 
+def sweep(steps, warmup):
+    """Forward throughput of every named workload (single layers causal and
+    not, C = 256 and 512, the 24-layer stack), one single-call forward per
+    step, inputs resident in HBM.  One JSON line per workload; not the
+    headline line."""
+    import torch
+    import chunked_linear_attention_amd as g
+    from chunked_linear_attention_amd import inputs
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    for name, wl in inputs.WORKLOADS.items():
+        B, T, d, e, s, C = (wl[k] for k in ("B", "T", "d", "e", "s", "C"))
+        causal = wl["causal"]
+        bf = wl["dtype"] == "bf16"
+        tdt = torch.bfloat16 if bf else torch.float32
+        gc = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if bf else g.GAU_F32)
+        layer_flops = sum(algorithmic_flops(B, T, d, e, s, C, causal).values())
+        if "layers" in wl:
+            X, layers = inputs.make_stack_inputs(**wl)
+            dev = [g.device_layer(L, tdt) for L in layers]
+            x0 = torch.from_numpy(np.ascontiguousarray(X, dtype=np.float32)).cuda()
+            x = x0.clone()
+            ws = torch.empty(g.stack_workspace_bytes(gc), dtype=torch.uint8, device="cuda")
+            n_layers = len(layers)
+
+            def fwd():
+                x.copy_(x0)  # the residual stream is updated in place
+                g.stack_forward(gc, x, dev, ws, stream=stream)
+        else:
+            inp = inputs.make_layer_inputs(**wl)
+            dev = g.device_layer(inp, tdt)
+            ws = torch.empty(g.workspace_bytes(gc), dtype=torch.uint8, device="cuda")
+            O = torch.empty((B, T, d), dtype=tdt, device="cuda")
+            args_l = (dev["X"], dev["W_u"], dev["W_v"], dev["W_z"], dev["W_o"], dev["scale"], dev["offset"],
+                      dev["relpos"], O, ws)
+            n_layers = 1
+
+            def fwd():
+                g.forward(gc, *args_l, stream=stream)
+        for _ in range(warmup):
+            fwd()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fwd()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / steps
+        flops = layer_flops * n_layers
+        peak = PEAK_BF16_TFLOPS if bf else PEAK_FP32_TFLOPS
+        print(json.dumps({"sweep": name, "tokens_per_s": B * T / sec, "ms_per_forward": sec * 1e3,
+                          "layers": n_layers, "tflops": flops / sec / 1e12,
+                          "frac_of_peak": flops / sec / 1e12 / peak,
+                          "peak": f"{'bf16' if bf else 'fp32'} {peak} TFLOP/s",
+                          "note": "stack: includes the copy that restores the input" if n_layers > 1 else ""}),
+              flush=True)
+        del dev, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +291,8 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="")
     ap.add_argument("--out")
+    ap.add_argument("--sweep", action="store_true",
+                    help="throughput of every named workload (one JSON line each) instead of the headline line")
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.command, args.out)
@@ -241,6 +304,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep(args.steps, args.warmup)
+        return
 
     import torch
     import chunked_linear_attention_amd as g
