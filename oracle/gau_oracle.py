@@ -25,7 +25,12 @@ Efficient Transformer Design in Recent Times"):
 * O_g = [U_g * (V_quad_g + V_lin_g)] W_o: wikillm, "Method" step 4; blog,
   "Mixed Chunking" (final equation).
 * Relative-position bias as a Toeplitz matrix of a 2n-1 vector:
-  papercache, appendix D, Code 4 (the n < 512 branch).
+  papercache, appendix D, Code 4 (the n < 512 branch); for n >= 512 the same
+  listing builds it from two RoPE-rotated vectors (einsum of the rotated
+  rows), which ``rope_toeplitz`` carries out.
+* Rotary position embedding on the four heads, positions counted over the
+  whole sequence: wikillm, FLASH block pseudocode (the Code 8 rewrite) and
+  "Paper vs code"; Su's post credits the paper's use of RoPE.
 
 Readings where the pages are silent or disagree (each is also listed in the
 design notes):
@@ -38,7 +43,15 @@ design notes):
 * Bias index: b[i, j] = w[C - 1 + j - i] (key position minus query position),
   obtained by carrying out Code 4's pad / tile / slice / reshape / slice steps.
 * The causal mask keeps j <= i (diagonal included) and is applied after relu^2.
-* SiLU on U, V and Z.  No RoPE, no dense-layer biases, no segment masks.
+* SiLU on U, V and Z.  No dense-layer biases, no segment masks.  RoPE is
+  optional (off in the layer's plain form, which has no RoPE argument).
+* RoPE itself is not printed on the pages.  ``rope`` rotates the pairs
+  (x_i, x_{i+s/2}) by t * theta_i with theta_i = 10000^(-i/(s/2)): the
+  frequency schedule and the [first half | second half] layout of the
+  sinusoid helper the pages do print (papercache, appendix D, other
+  pseudocode, _get_scaledsin).  parity unpinned for this convention choice:
+  the pins fix the rotation's defining properties, not which pairing the
+  authors' hidden helper used.
 * Non-causal: every chunk (its own included) feeds the linear term.
 
 parity pinned: every function here is checked in tests/test_oracle.py against
@@ -119,6 +132,43 @@ def projections(X, W_u, W_v, W_z):
     return silu(H[..., :e]), silu(H[..., e:2 * e]), silu(H[..., 2 * e:])
 
 
+def rope_frequencies(s):
+    """theta_i = 10000^(-i / (s/2)), i = 0 .. s/2-1 (the inverse frequencies
+    of the pages' sinusoid helper, papercache appendix D, _get_scaledsin)."""
+    half = s // 2
+    return 10000.0 ** (-(np.arange(half, dtype=np.float64) / half))
+
+
+def rope(x, positions):
+    """Rotary position embedding over the last axis of x (..., T, s):
+    the pair (x_i, x_{i+s/2}) at position p is rotated by the angle
+    p * theta_i:  (x_i cos - x_{i+s/2} sin, x_{i+s/2} cos + x_i sin)."""
+    x = _as64(x)
+    s = x.shape[-1]
+    half = s // 2
+    ang = _as64(positions)[:, None] * rope_frequencies(s)[None, :]   # (T, s/2)
+    c, sn = np.cos(ang), np.sin(ang)
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * sn, hi * c + lo * sn], axis=-1)
+
+
+def rope_toeplitz(a, b, n):
+    """The n >= 512 branch of Code 4 (papercache, appendix D): tile the
+    vectors a and b over n positions, rotate each row by its position, and
+    take t[m, k] = rope(a)_m . rope(b)_k."""
+    a = np.tile(_as64(a)[None, :], (n, 1))
+    b = np.tile(_as64(b)[None, :], (n, 1))
+    pos = np.arange(n)
+    return rope(a, pos) @ rope(b, pos).T
+
+
+def rope_relpos(a, b, n):
+    """The 2n-1 vector w of that Toeplitz matrix, t[i, j] = w[n-1 + j - i]
+    (read off its first row and first column)."""
+    t = rope_toeplitz(a, b, n)
+    return np.concatenate([t[::-1, 0][:-1], t[0, :]])
+
+
 def heads(Z, gamma, beta):
     """The four heads Q_quad, K_quad, Q_lin, K_lin from Z.
 
@@ -131,12 +181,14 @@ def heads(Z, gamma, beta):
 
 
 def flash_forward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
-                  quad_scale=None, lin_scale=None, return_intermediates=False):
+                  quad_scale=None, lin_scale=None, return_intermediates=False, use_rope=False):
     """Forward pass of one FLASH layer (GAU with mixed chunk attention).
 
     X: (B, T, d).  W_u, W_v: (d, e).  W_z: (d, s).  W_o: (e, d).
     gamma, beta: (4, s).  relpos: (2C-1,).  T must be a multiple of C.
     quad_scale / lin_scale default to 1/C (the listing's reading).
+    use_rope rotates the four heads by their position in the sequence (0 ..
+    T-1, not restarted per chunk: wikillm, FLASH block pseudocode).
 
     Steps, in the order of the FLASH block (wikillm pseudocode; blog "Mixed
     Chunking"; papercache 3.2):
@@ -163,6 +215,9 @@ def flash_forward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
     e = U.shape[-1]
     s = Z.shape[-1]
     Qq, Kq, Ql, Kl = heads(Z, gamma, beta)
+    if use_rope:
+        pos = np.arange(T)
+        Qq, Kq, Ql, Kl = (rope(h, pos) for h in (Qq, Kq, Ql, Kl))
 
     def chunks(a):
         return a.reshape(B, G, C, a.shape[-1])
@@ -205,7 +260,7 @@ def flash_forward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
 # --------------------------------------------------------------------------
 
 def flash_forward_bruteforce(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
-                             quad_scale=None, lin_scale=None):
+                             quad_scale=None, lin_scale=None, use_rope=False):
     """The layer as O = (U * (A V)) W_o with the full T x T matrix A.
 
     A per-token double loop builds A[t, tau] (blog, "Gated Attention" GAU
@@ -215,6 +270,8 @@ def flash_forward_bruteforce(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, caus
           relu^2(q_quad_t . k_quad_tau * quad_scale + w[C-1 + (tau mod C) - (t mod C)])
       * plus q_lin_t . k_lin_tau * lin_scale when chunk(tau) < chunk(t)
         (causal), or for every tau (non-causal, own chunk included).
+    With use_rope, each head vector of token t is rotated pair by pair,
+    (h_i, h_{i+s/2}) by the angle t * 10000^(-i/(s/2)), written out here.
     Every product is written out per token; nothing is shared with
     ``flash_forward`` beyond the SiLU definition.  Pure Python loops: keep
     T small.
@@ -243,6 +300,14 @@ def flash_forward_bruteforce(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, caus
             kq[t] = z * gamma[1] + beta[1]
             ql[t] = z * gamma[2] + beta[2]
             kl[t] = z * gamma[3] + beta[3]
+            if use_rope:
+                for hv in (qq[t], kq[t], ql[t], kl[t]):
+                    half = hv.shape[0] // 2
+                    for i in range(half):
+                        ang = t * 10000.0 ** (-i / half)
+                        x0, x1 = hv[i], hv[i + half]
+                        hv[i] = x0 * np.cos(ang) - x1 * np.sin(ang)
+                        hv[i + half] = x1 * np.cos(ang) + x0 * np.sin(ang)
         A = np.zeros((T, T))
         for t in range(T):
             for tau in range(T):

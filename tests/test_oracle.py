@@ -273,3 +273,90 @@ def test_stack_first_layer_matches_single_layer():
     ref2 = out1 + orc.flash_forward(orc.rms_norm(out1), L["W_u"], L["W_v"], L["W_z"], L["W_o"],
                                     L["gamma"], L["beta"], L["relpos"], C, True)
     np.testing.assert_allclose(out2, ref2, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_frequencies_match_the_printed_sinusoid_helper():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "rope_frequencies_s8.txt"))
+            if l.strip() and not l.startswith("#")]
+    want = np.array([float(v) for _, v in rows])
+    np.testing.assert_allclose(orc.rope_frequencies(8), want, rtol=1e-14)
+
+
+def test_rope_position_zero_is_identity_and_norms_are_kept():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((3, 9, 16))
+    np.testing.assert_array_equal(orc.rope(x[:, :1], [0.0]), x[:, :1])
+    y = orc.rope(x, np.arange(9) * 37.0)
+    half = 8
+    np.testing.assert_allclose(y[..., :half] ** 2 + y[..., half:] ** 2,
+                               x[..., :half] ** 2 + x[..., half:] ** 2, rtol=1e-12)
+
+
+def test_rope_basis_vector_turns_by_position_times_frequency():
+    """e_i at position p becomes cos(p theta_i) e_i + sin(p theta_i) e_{i+s/2}
+    (the pair (i, i+s/2) is one plane; theta from the golden fixture)."""
+    s, theta = 8, [1.0, 0.1, 0.01, 0.001]
+    for i in range(4):
+        for p in (1.0, 5.0, 123.0):
+            x = np.zeros((1, s))
+            x[0, i] = 1.0
+            y = orc.rope(x, [p])[0]
+            want = np.zeros(s)
+            want[i] = math.cos(p * theta[i])
+            want[i + 4] = math.sin(p * theta[i])
+            np.testing.assert_allclose(y, want, atol=1e-13)
+
+
+def test_rope_scores_depend_on_the_offset_only():
+    """rope(q, m) . rope(k, n) is a function of n - m (shift both by any D)."""
+    rng = np.random.default_rng(8)
+    q, k = rng.standard_normal((2, 6, 32))
+    m = rng.integers(0, 5000, 6).astype(float)
+    n = rng.integers(0, 5000, 6).astype(float)
+    base = np.sum(orc.rope(q, m) * orc.rope(k, n), axis=-1)
+    for D in (1.0, 250.0, 4097.0):
+        shifted = np.sum(orc.rope(q, m + D) * orc.rope(k, n + D), axis=-1)
+        np.testing.assert_allclose(shifted, base, rtol=1e-9, atol=1e-9)
+
+
+def test_rope_rotations_compose():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((5, 12))
+    a = rng.uniform(0, 900, 5)
+    b = rng.uniform(0, 900, 5)
+    np.testing.assert_allclose(orc.rope(orc.rope(x, a), b), orc.rope(x, a + b), atol=1e-10)
+
+
+@pytest.mark.parametrize("B,T,C", [(2, 12, 4), (1, 9, 3)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunked_with_rope_equals_bruteforce(B, T, C, causal):
+    """The four heads rotated by their position in the whole sequence (the
+    brute force rotates each token's head vectors pair by pair itself)."""
+    p = _tiny(B, T, d=5, e=6, s=4, C=C, seed=B * 31 + T)
+    got = _run(orc.flash_forward, p, C, causal, use_rope=True)
+    ref = _run(orc.flash_forward_bruteforce, p, C, causal, use_rope=True)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+    plain = _run(orc.flash_forward, p, C, causal)
+    assert np.max(np.abs(got - plain)) > 1e-3  # the rotation changes the result
+
+
+def test_rope_toeplitz_is_toeplitz_with_closed_form_diagonals():
+    """Code 4's n >= 512 branch depends only on the key minus query offset;
+    for a = e_0 and b = e_0 or e_{half} the diagonals are cos(d) and -sin(d)
+    (theta_0 = 1)."""
+    rng = np.random.default_rng(10)
+    a, b = rng.standard_normal((2, 16))
+    t = orc.rope_toeplitz(a, b, 12)
+    for dd in range(-11, 12):
+        diag = np.diagonal(t, offset=dd)
+        np.testing.assert_allclose(diag, diag[0], rtol=1e-10, atol=1e-10)
+    w = orc.rope_relpos(a, b, 12)
+    i, j = np.meshgrid(np.arange(12), np.arange(12), indexing="ij")
+    np.testing.assert_allclose(w[12 - 1 + j - i], t, atol=1e-12)
+    e0 = np.zeros(16); e0[0] = 1.0
+    eh = np.zeros(16); eh[8] = 1.0
+    d = np.arange(-11, 12)
+    np.testing.assert_allclose(orc.rope_relpos(e0, e0, 12), np.cos(d), atol=1e-12)
+    np.testing.assert_allclose(orc.rope_relpos(e0, eh, 12), -np.sin(d), atol=1e-12)
