@@ -235,7 +235,7 @@ def sweep(steps, warmup):
         causal = wl["causal"]
         bf = wl["dtype"] == "bf16"
         tdt = torch.bfloat16 if bf else torch.float32
-        gc = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if bf else g.GAU_F32)
+        gc = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if bf else g.GAU_F32, rope=wl.get("rope", False))
         layer_flops = sum(algorithmic_flops(B, T, d, e, s, C, causal).values())
         if "layers" in wl:
             X, layers = inputs.make_stack_inputs(**wl)

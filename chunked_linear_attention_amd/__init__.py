@@ -12,7 +12,7 @@ import numpy as np
 from . import inputs  # noqa: F401
 from ._lib import (  # noqa: F401
     GAU_BF16, GAU_F32, STAGE_ATTN, STAGE_OUT, STAGE_PROJ, STAGE_SCAN, STAGE_SCORES, STAGE_STATE, EXPORTS,
-    GauError, forward, forward_stages, load, make_config, stack_forward, stack_workspace_bytes,
+    GauError, forward, forward_stages, load, make_config, rope_relpos, stack_forward, stack_workspace_bytes,
     status_string, workspace_bytes, workspace_layout,
 )
 
@@ -49,7 +49,7 @@ def device_layer(inp, dtype, device="cuda"):
 
 
 def gau_forward(X, W_u, W_v, W_z, W_o, scale, offset, relpos, C, causal,
-                quad_scale=None, lin_scale=None, out=None, workspace=None, stream=None):
+                quad_scale=None, lin_scale=None, out=None, workspace=None, stream=None, rope=False):
     """O = FLASH layer forward of X [B, T, d] (weights output-major).
 
     Allocates O and the workspace with torch.empty when not given; all
@@ -60,7 +60,7 @@ def gau_forward(X, W_u, W_v, W_z, W_o, scale, offset, relpos, C, causal,
     e = W_u.shape[0]
     s = W_z.shape[0]
     dt = GAU_BF16 if X.dtype == torch.bfloat16 else GAU_F32
-    cfg = make_config(B, T, d, e, s, C, causal, dt, quad_scale, lin_scale)
+    cfg = make_config(B, T, d, e, s, C, causal, dt, quad_scale, lin_scale, rope)
     if out is None:
         out = torch.empty_like(X)
     if workspace is None:

@@ -26,7 +26,7 @@ STATUS = {
 # Every symbol include/gau.h declares.
 EXPORTS = (
     "gau_workspace_bytes", "gau_workspace_layout", "gau_forward", "gau_forward_stages",
-    "gau_stack_workspace_bytes", "gau_stack_forward", "gau_status_string",
+    "gau_stack_workspace_bytes", "gau_stack_forward", "gau_rope_relpos", "gau_status_string",
 )
 
 
@@ -34,7 +34,7 @@ class GauConfig(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("d", ctypes.c_int64),
                 ("e", ctypes.c_int64), ("s", ctypes.c_int64), ("C", ctypes.c_int64),
                 ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("quad_scale", ctypes.c_float), ("lin_scale", ctypes.c_float)]
+                ("quad_scale", ctypes.c_float), ("lin_scale", ctypes.c_float), ("rope", ctypes.c_int32)]
 
 
 class GauWsLayout(ctypes.Structure):
@@ -76,17 +76,20 @@ def load():
     PP = ctypes.POINTER(ctypes.c_void_p)
     lib.gau_stack_forward.argtypes = [cfgp, ctypes.c_int, P] + [PP] * 7 + [P, ctypes.c_size_t, P]
     lib.gau_stack_forward.restype = ctypes.c_int
+    lib.gau_rope_relpos.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, P, P]
+    lib.gau_rope_relpos.restype = ctypes.c_int
     lib.gau_status_string.argtypes = [ctypes.c_int]
     lib.gau_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
 
-def make_config(B, T, d, e, s, C, causal, dtype, quad_scale=None, lin_scale=None):
-    """gau_config; quad_scale / lin_scale default to 1/C (the listing's reading)."""
+def make_config(B, T, d, e, s, C, causal, dtype, quad_scale=None, lin_scale=None, rope=False):
+    """gau_config; quad_scale / lin_scale default to 1/C (the listing's reading);
+    rope rotates the four heads by position."""
     return GauConfig(B, T, d, e, s, C, 1 if causal else 0, dtype,
                      (1.0 / C) if quad_scale is None else float(quad_scale),
-                     (1.0 / C) if lin_scale is None else float(lin_scale))
+                     (1.0 / C) if lin_scale is None else float(lin_scale), 1 if rope else 0)
 
 
 def workspace_bytes(cfg):
@@ -201,3 +204,18 @@ def stack_forward(cfg, X, layers, workspace, stream=None):
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if st != 0:
         raise GauError(st, "gau_stack_forward")
+
+
+def rope_relpos(a, b, n, out=None, stream=None):
+    """gau_rope_relpos: the 2n-1 bias vector of Code 4's RoPE branch from the
+    fp32 device vectors a and b (same length)."""
+    import torch
+    _check(a, "a", torch.float32)
+    _check(b, "b", torch.float32, a.numel())
+    if out is None:
+        out = torch.empty(2 * n - 1, dtype=torch.float32, device=a.device)
+    _check(out, "out", torch.float32, 2 * n - 1)
+    st = load().gau_rope_relpos(_ptr(a), _ptr(b), n, a.numel(), _ptr(out), _stream(stream))
+    if st != 0:
+        raise GauError(st, "gau_rope_relpos")
+    return out

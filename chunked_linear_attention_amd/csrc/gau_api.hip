@@ -25,6 +25,7 @@ gau_status check_config(const gau_config* c) {
     if (c->d <= 0 || c->d % 128 != 0) return GAU_ERR_SHAPE;
     if (c->e <= 0 || c->e % 256 != 0) return GAU_ERR_SHAPE;
     if (!(c->s == 128 || c->s == 256)) return GAU_ERR_SHAPE;
+    if (c->rope != 0 && c->rope != 1) return GAU_ERR_SHAPE;
     // 32-bit index arithmetic inside the kernels
     const int64_t M = c->B * c->T;
     if (M > (int64_t)1 << 30 || c->d > 65536 || c->e > 65536) return GAU_ERR_SHAPE;
@@ -94,6 +95,11 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
                                   ws + L.Q_quad, ws + L.K_quad, ws + L.Q_lin, ws + L.K_lin_t,
                                   M, (int)c->T, (int)c->d, (int)c->e, (int)c->s};
                 e = gau::launch_proj(p, bf, st);
+                if (e == hipSuccess && c->rope) {
+                    const gau::RopeParams r{ws + L.Q_quad, ws + L.K_quad, ws + L.Q_lin, ws + L.K_lin_t, (int)c->B,
+                                            (int)c->T, M, (int)c->s};
+                    e = gau::launch_rope_heads(r, bf, st);
+                }
                 break;
             }
             case GAU_STAGE_STATE: {
@@ -212,6 +218,15 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X, cons
         const LayerPtrs a{xn, W_u[l], W_v[l], W_z[l], W_o[l], scale[l], offset[l], relpos[l]};
         if ((s = run_stages(cfg, GAU_STAGE_PROJ, GAU_STAGE_OUT, a, X, X, ws, st)) != GAU_OK) return s;
     }
+    return GAU_OK;
+}
+
+gau_status gau_rope_relpos(const float* a, const float* b, int64_t n, int64_t dim, float* relpos, void* stream) {
+    if (!a || !b || !relpos) return GAU_ERR_NULL;
+    if (n < 1 || n > (1 << 20) || dim <= 0 || dim % 2 != 0 || dim > 65536) return GAU_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(relpos)) return GAU_ERR_ALIGN;
+    if (gau::launch_rope_relpos(a, b, (int)n, (int)dim, relpos, (hipStream_t)stream) != hipSuccess)
+        return GAU_ERR_HIP;
     return GAU_OK;
 }
 

@@ -85,6 +85,18 @@ struct NormParams {
 };
 
 hipError_t launch_proj(const ProjParams& p, bool bf16_storage, hipStream_t st);  // U, Vt, Z heads
+// Rotary position embedding of the four heads, in place.
+struct RopeParams {
+    void* Qq;   // [M, s]
+    void* Kq;   // [M, s]
+    void* Ql;   // [M, s]
+    void* Klt;  // [B, s, T]
+    int B, T, M, s;
+};
+
+hipError_t launch_rope_heads(const RopeParams& p, bool bf16_storage, hipStream_t st);
+// w[n-1 + d] = a . rope(b, d), d = -(n-1) .. n-1 (a, b: [dim] fp32; w: [2n-1])
+hipError_t launch_rope_relpos(const float* a, const float* b, int n, int dim, float* relpos, hipStream_t st);
 hipError_t launch_chunk_state(const StateParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_chunk_scan(const ScanParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_chunk_scores(const ScoresParams& p, bool bf16_storage, hipStream_t st);

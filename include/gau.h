@@ -23,7 +23,16 @@
  * The listing (Code 8 as rewritten on the wikillm page) divides Q K^T by C and
  * each chunk summary by C; the equations use no factor.  Both factors are
  * arguments here (gau_config.quad_scale, gau_config.lin_scale); the listing's
- * reading is quad_scale = lin_scale = 1/C.  No RoPE, no dense-layer biases.
+ * reading is quad_scale = lin_scale = 1/C.  No dense-layer biases.
+ *
+ * Optional rotary position embedding (gau_config.rope = 1): the listing rotates
+ * the four heads after the scale+offset, by each token's position in its
+ * sequence (0 .. T-1, not restarted per chunk; wikillm, FLASH block
+ * pseudocode and "Paper vs code").  The rotation is not printed on the pages;
+ * here the pair (h_i, h_{i+s/2}) at position t turns by t * theta_i with
+ * theta_i = 10000^(-i/(s/2)), the frequency schedule and half-split layout of
+ * the sinusoid helper the pages do print (papercache, appendix D,
+ * _get_scaledsin).
  *
  * Conventions for every entry point:
  *  - Every pointer is caller-owned device memory (HBM of the current HIP
@@ -81,6 +90,8 @@ typedef struct {
     int32_t dtype;       /* gau_dtype of X, W_*, O and the stored intermediates  */
     float quad_scale;    /* multiplies Q_quad K_quad^T before the bias is added  */
     float lin_scale;     /* multiplies every chunk summary K_lin^T V             */
+    int32_t rope;        /* 1: rotate the four heads by position (see above);
+                            0: no rotation; anything else is GAU_ERR_SHAPE      */
 } gau_config;
 
 /*
@@ -190,6 +201,20 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X,
                              const float* const* scale, const float* const* offset,
                              const float* const* relpos,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The relative-position bias of chunk length n built from RoPE-rotated vectors
+ * (the n >= 512 branch of papercache, appendix D, Code 4): the Toeplitz matrix
+ * rope(a)_m . rope(b)_k depends only on k - m, so it is carried by
+ *   relpos[n-1 + d] = a . rope(b, d),   d = -(n-1) .. n-1,
+ * the vector gau_forward takes as `relpos` (Bias[i][j] = relpos[C-1+j-i]).
+ * rope(b, d) turns the pairs (b_i, b_{i+dim/2}) by d * 10000^(-i/(dim/2)).
+ *   a, b    [dim] fp32 device arrays (Code 4 uses dim = 128)
+ *   relpos  [2n-1] fp32 device array, written
+ * n >= 1, dim even and > 0 (else GAU_ERR_SHAPE); NULL pointers GAU_ERR_NULL;
+ * pointers 16-byte aligned (GAU_ERR_ALIGN).  Queued on `stream`.
+ */
+gau_status gau_rope_relpos(const float* a, const float* b, int64_t n, int64_t dim, float* relpos, void* stream);
 
 /* Static description of a status code. */
 const char* gau_status_string(int status);

@@ -72,6 +72,12 @@ static void run(const Cfg& c, const std::string& only) {
     };
     ProjParams pp{X, Wu, Wv, Wz, sc, of, U, Vt, Qq, Kq, Ql, Klt, (int)M, c.T, c.d, c.e, c.s};
     t("proj", [&] { CHECK(launch_proj(pp, c.bf, nullptr)); });
+    RopeParams rop{Qq, Kq, Ql, Klt, c.B, c.T, (int)M, c.s};
+    t("rope_heads", [&] { CHECK(launch_rope_heads(rop, c.bf, nullptr)); });
+    float* ra = (float*)buf(128 * 4);
+    float* rb = (float*)buf(128 * 4);
+    float* rw = (float*)buf((2 * c.C - 1) * 4);
+    t("rope_relpos", [&] { CHECK(launch_rope_relpos(ra, rb, c.C, 128, rw, nullptr)); });
     ScoresParams sp{Qq, Kq, rp, A, c.B, c.T, c.s, c.C, c.causal ? 1 : 0, 1.0f / c.C};
     t("chunk_scores", [&] { CHECK(launch_chunk_scores(sp, c.bf, nullptr)); });
     StateParams stp{Vt, Klt, S, c.B, c.T, c.e, c.s, c.C, 1.0f / c.C};
@@ -101,7 +107,7 @@ static void run(const Cfg& c, const std::string& only) {
         free(ws);
     });
     for (void* p : {X, Wu, Wv, Wz, Wo, (void*)sc, (void*)of, (void*)rp, U, Vt, Qq, Kq, Ql, Klt, (void*)S, P, A, Y, O,
-                    (void*)Of})
+                    (void*)Of, (void*)ra, (void*)rb, (void*)rw})
         free(p);
 }
 

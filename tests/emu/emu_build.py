@@ -35,7 +35,7 @@ CSRC = os.environ.get("EMU_CSRC", os.path.join(ROOT, "chunked_linear_attention_a
 OUT = os.environ.get("EMU_OUT", os.path.join(HERE, "_build"))
 CXX = "/opt/rocm/llvm/bin/clang++"
 UNITS = ["proj_gemm", "chunk_attn", "chunk_scan", "chunk_scores", "chunk_state", "chunk_scores_state", "out_gemm",
-         "rms_norm", "gau_api"]
+         "rope", "rms_norm", "gau_api"]
 BOUNDS = os.path.join(OUT, "emu_bounds")
 LIB = os.path.join(OUT, "libgau_emu.so")
 
@@ -74,10 +74,7 @@ def _generate(gen):
                    r"\1* \2 = (\1*)::emu::static_shared(__LINE__, sizeof(\1) * (\3));", s)
         # AMDGPU occupancy attributes have no meaning on the host
         s = re.sub(r"__attribute__\(\(amdgpu_[a-z_]+\([^)]*\)\)\)", "", s)
-        # the fence-free barrier: a block barrier of the emulation (which, like
-        # the hardware barrier, does not complete pending LDS copies)
-        s = s.replace('asm volatile("s_waitcnt lgkmcnt(0)\\n\\ts_barrier" ::: "memory");', "__syncthreads();")
-        # any other inline assembly has no host meaning: refuse rather than miscompile
+        # inline assembly has no host meaning: refuse rather than miscompile
         if re.search(r"\b(__)?asm(__)?\s*(volatile\s*|__volatile__\s*)?\(", s):
             raise RuntimeError(f"{f}: inline assembly the emulation build does not rewrite")
         if "__shared__" in s:

@@ -60,6 +60,25 @@ def test_bad_shapes_rejected(bad):
     assert ei.value.status == 2
 
 
+def test_bad_rope_flag_rejected():
+    cfg = _cfg()
+    cfg.rope = 2
+    assert g.workspace_bytes(cfg) == 0
+    cfg.rope = 1
+    assert g.workspace_bytes(cfg) == g.workspace_bytes(_cfg())
+
+
+def test_rope_relpos_argument_checks_without_gpu():
+    lib = g.load()
+    P = ctypes.c_void_p
+    a, b, w = P(4096), P(8192), P(12288)
+    assert lib.gau_rope_relpos(None, b, 64, 128, w, None) == 1
+    assert lib.gau_rope_relpos(a, b, 64, 128, None, None) == 1
+    assert lib.gau_rope_relpos(a, b, 0, 128, w, None) == 2
+    assert lib.gau_rope_relpos(a, b, 64, 127, w, None) == 2
+    assert lib.gau_rope_relpos(P(4100), b, 64, 128, w, None) == 3
+
+
 def test_bad_dtype_rejected():
     cfg = _cfg()
     cfg.dtype = 7

@@ -68,6 +68,8 @@ CASES = [
     (1, 512, 128, 256, 128, 512, "bf16", True),
     (1, 256, 128, 1024, 128, 64, "f32", True),      # Z formed inside the U tiles (s = 128)
     (1, 256, 128, 1024, 256, 128, "bf16", False),   # Z formed inside the U tiles (s = 256)
+    (1, 256, 128, 256, 128, 64, "f32", True, True),   # heads rotated by position (RoPE)
+    (1, 256, 128, 1024, 256, 128, "bf16", True, True),
 ]
 
 
@@ -77,14 +79,15 @@ def _host(a, bf):
 
 
 @pytest.mark.parametrize("late", [0, 1], ids=["dma_at_issue", "dma_at_wait"])
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}".format(
-    *c[:7], "causal" if c[7] else "full"))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}{}".format(
+    *c[:7], "causal" if c[7] else "full", "_rope" if len(c) > 8 and c[8] else ""))
 def test_emulated_kernels_match_oracle(emu, case, late):
-    B, T, d, e, s, C, dtype, causal = case
+    B, T, d, e, s, C, dtype, causal = case[:8]
+    rope = len(case) > 8 and case[8]
     bf = dtype == "bf16"
     emu.emu_set_mode(1, late)
     inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=B * 31 + T + C, dtype=dtype)
-    cfg = GauConfig(B, T, d, e, s, C, 1 if causal else 0, 1 if bf else 0, 1.0 / C, 1.0 / C)
+    cfg = GauConfig(B, T, d, e, s, C, 1 if causal else 0, 1 if bf else 0, 1.0 / C, 1.0 / C, 1 if rope else 0)
     X = _host(inp["X"], bf)
     W = {k: _host(np.ascontiguousarray(inp[k].T), bf) for k in ("W_u", "W_v", "W_z", "W_o")}
     sc, of, rp = (np.ascontiguousarray(inp[k], np.float32) for k in ("gamma", "beta", "relpos"))
@@ -99,7 +102,7 @@ def test_emulated_kernels_match_oracle(emu, case, late):
     L = GauWsLayout()
     assert emu.gau_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == 0
     ref, im = orc.flash_forward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"],
-                                inp["beta"], inp["relpos"], C, causal, return_intermediates=True)
+                                inp["beta"], inp["relpos"], C, causal, return_intermediates=True, use_rope=rope)
     conv = inputs.bf16_bits_to_f32 if bf else (lambda a: a)
     eb = 2 if bf else 4
 

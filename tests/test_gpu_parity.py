@@ -76,6 +76,39 @@ def test_layer_matches_oracle(case):
     assert_close(O, ref, tol_for(dtype), "O")
 
 
+ROPE = [
+    # B, T, d, e, s, C, dtype, causal: heads rotated by position (Z tiles, Z in U tiles, s = 256)
+    (1, 512, 128, 256, 128, 128, "f32", True),
+    (2, 256, 128, 1024, 128, 64, "bf16", True),
+    (1, 320, 256, 1024, 256, 64, "bf16", False),
+    (1, 1024, 256, 512, 128, 512, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", ROPE, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}".format(
+    *c[:7], "causal" if c[7] else "full"))
+def test_layer_with_rope_matches_oracle(case):
+    B, T, d, e, s, C, dtype, causal = case
+    inp = make(B, T, d, e, s, C, dtype, seed=B * 613 + T + C)
+    O, ws, cfg, L = run_layer(inp, B, T, d, e, s, C, causal, dtype, rope=True)
+    ref, im = oracle_layer(inp, C, causal, intermediates=True, rope=True)
+    _stagewise(ws, L, im, B, T, e, s, C, causal, dtype)
+    assert_close(O, ref, tol_for(dtype), "O")
+
+
+@pytest.mark.parametrize("n", [64, 512, 1024])
+def test_rope_relpos_matches_code4_toeplitz(n):
+    """The 2n-1 vector from the kernel against the oracle's Toeplitz matrix
+    of Code 4's RoPE branch (first row and column)."""
+    rng = np.random.default_rng(n)
+    a = (0.3 * rng.standard_normal(128)).astype(np.float32)
+    b = (0.3 * rng.standard_normal(128)).astype(np.float32)
+    w = g.rope_relpos(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), n)
+    torch.cuda.synchronize()
+    ref = orc.rope_relpos(a, b, n)
+    assert_close(w.cpu().numpy().astype(np.float64), ref, 1e-5, "relpos")
+
+
 def test_tiny_fp32_workload():
     cfg, inp = inputs.workload_inputs("layer_fp32_B1_T256_d128_C64")
     O, *_ = run_layer(inp, cfg["B"], cfg["T"], cfg["d"], cfg["e"], cfg["s"], cfg["C"], cfg["causal"],
