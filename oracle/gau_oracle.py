@@ -324,6 +324,64 @@ def flash_forward_bruteforce(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, caus
 
 
 # --------------------------------------------------------------------------
+# incremental (token-by-token) causal decoding
+# --------------------------------------------------------------------------
+
+def flash_decode(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, quad_scale=None, lin_scale=None,
+                 use_rope=False):
+    """Causal decoding one token at a time with a constant-size state.
+
+    The chunk-level recurrence of the causal layer (wikillm, "Method" steps
+    2-4; Su's post, "Mixed Chunking": the decoder's linear part as a
+    cumulative sum over chunks; papercache 3.1, the incremental form of linear
+    attention): the state is P, the sum of the summaries K_lin^T V of the
+    chunks already completed (s x e), plus the current chunk's keys and
+    values.  Token t at slot j = t mod C of its chunk:
+      quad = sum over the chunk's slots tau <= j of
+             relu^2(q_quad . k_quad_tau * quad_scale + w[C-1 + tau - j]) v_tau
+      lin  = q_lin P;   o_t = (u * (quad + lin)) W_o
+    and when j = C-1 the chunk's summary lin_scale * sum_tau k_lin_tau v_tau^T
+    is added to P.  X may have any length T (no multiple of C needed).
+    """
+    X = _as64(X)
+    B, T, d = X.shape
+    if quad_scale is None:
+        quad_scale = 1.0 / C
+    if lin_scale is None:
+        lin_scale = 1.0 / C
+    W_u, W_v, W_z, W_o = map(_as64, (W_u, W_v, W_z, W_o))
+    gamma, beta, w = _as64(gamma), _as64(beta), _as64(relpos)
+    e, s = W_u.shape[1], W_z.shape[1]
+    out = np.zeros((B, T, d))
+    for b in range(B):
+        P = np.zeros((s, e))
+        kq_c, v_c, kl_c = [], [], []
+        for t in range(T):
+            x = X[b, t]
+            u = silu(x @ W_u)
+            v = silu(x @ W_v)
+            z = silu(x @ W_z)
+            qq, kq, ql, kl = (z * gamma[h] + beta[h] for h in range(4))
+            if use_rope:
+                qq, kq, ql, kl = (rope(h[None, :], [t])[0] for h in (qq, kq, ql, kl))
+            j = t % C
+            if j == 0:
+                kq_c, v_c, kl_c = [], [], []
+            kq_c.append(kq)
+            v_c.append(v)
+            kl_c.append(kl)
+            quad = np.zeros(e)
+            for tau in range(j + 1):
+                sc = float(qq @ kq_c[tau]) * quad_scale + w[C - 1 + tau - j]
+                quad += max(sc, 0.0) ** 2 * v_c[tau]
+            lin = ql @ P
+            out[b, t] = (u * (quad + lin)) @ W_o
+            if j == C - 1:
+                P = P + lin_scale * sum(np.outer(kl_c[tau], v_c[tau]) for tau in range(C))
+    return out
+
+
+# --------------------------------------------------------------------------
 # references used by the invariant tests and by the stack configuration
 # --------------------------------------------------------------------------
 

@@ -360,3 +360,27 @@ def test_rope_toeplitz_is_toeplitz_with_closed_form_diagonals():
     d = np.arange(-11, 12)
     np.testing.assert_allclose(orc.rope_relpos(e0, e0, 12), np.cos(d), atol=1e-12)
     np.testing.assert_allclose(orc.rope_relpos(e0, eh, 12), -np.sin(d), atol=1e-12)
+
+
+# ---------------------------------------------------------------- decoding
+
+@pytest.mark.parametrize("B,T,C", [(2, 12, 4), (1, 9, 3), (1, 8, 8), (2, 10, 1)])
+@pytest.mark.parametrize("use_rope", [False, True])
+def test_token_by_token_decoding_equals_the_causal_layer(B, T, C, use_rope):
+    """The constant-state recurrence reproduces the parallel chunked form
+    (and so the brute-force T x T operator) token for token."""
+    p = _tiny(B, T, d=5, e=6, s=4, C=C, seed=B * 53 + T * 7 + C)
+    got = orc.flash_decode(p["X"], p["W_u"], p["W_v"], p["W_z"], p["W_o"], p["gamma"], p["beta"],
+                           p["relpos"], C, use_rope=use_rope)
+    ref = _run(orc.flash_forward, p, C, True, use_rope=use_rope)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_decoding_a_ragged_prefix_matches_the_layer_prefix():
+    """Decoding the first 7 tokens (not a multiple of C) gives the first 7
+    outputs of the full causal layer."""
+    p = _tiny(1, 12, d=5, e=6, s=4, C=4, seed=77)
+    full = _run(orc.flash_forward, p, 4, True)
+    got = orc.flash_decode(p["X"][:, :7], p["W_u"], p["W_v"], p["W_z"], p["W_o"], p["gamma"], p["beta"],
+                           p["relpos"], 4)
+    np.testing.assert_allclose(got, full[:, :7], rtol=1e-11, atol=1e-12)
