@@ -279,6 +279,60 @@ def sweep(steps, warmup):
         torch.cuda.empty_cache()
 
 
+def decode_bytes(B, d, e, s, C, eb=2):
+    """Algorithmic HBM bytes of one decoding step averaged over a chunk: every
+    weight once, and per sequence the fp32 state P, the chunk cache rows read
+    so far (on average (C+1)/2 slots) and the step's own rows written."""
+    weights = (2 * e + s) * d * eb + e * d * eb
+    per_seq = s * e * 4 + (C + 1) / 2 * (e + s) * eb + (e + 2 * s) * eb + 2 * d * eb
+    return weights + B * per_seq
+
+
+def decode_bench(steps, warmup, batches=(1, 2, 8, 32, 128)):
+    """Incremental decoding at the headline layer's shape (d=768, e=1536,
+    s=128, C=256, bf16): one JSON line per batch size, timed over `steps`
+    consecutive positions (a whole chunk by default, so the state update at
+    the chunk's end is included)."""
+    import torch
+    import chunked_linear_attention_amd as g
+    from chunked_linear_attention_amd import inputs
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    wl = inputs.WORKLOADS[inputs.HEADLINE]
+    d, e, s, C = (wl[k] for k in ("d", "e", "s", "C"))
+    for B in batches:
+        inp = inputs.make_layer_inputs(B=B, T=steps + warmup, d=d, e=e, s=s, C=C, seed=wl["seed"])
+        dev = g.device_layer(inp, torch.bfloat16)
+        T = ((steps + warmup + C - 1) // C) * C
+        cfg = g.make_config(B, T, d, e, s, C, True, g.GAU_BF16)
+        ws = torch.empty(g.decode_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+        xs = [dev["X"][:, t].contiguous() for t in range(steps + warmup)]
+        o = torch.empty((B, d), dtype=torch.bfloat16, device="cuda")
+        w = (dev["W_u"], dev["W_v"], dev["W_z"], dev["W_o"], dev["scale"], dev["offset"], dev["relpos"])
+
+        def run(t0, n):
+            for t in range(t0, t0 + n):
+                g.decode_step(cfg, t % T, xs[t], *w, o, ws, stream=stream)
+
+        g.decode_reset(cfg, ws, stream=stream)
+        run(0, warmup)
+        g.decode_reset(cfg, ws, stream=stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(0, steps)
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / steps
+        byt = decode_bytes(B, d, e, s, C)
+        print(json.dumps({"decode": f"layer_bf16_d{d}_e{e}_s{s}_C{C}", "batch": B, "steps": steps,
+                          "us_per_step": sec * 1e6, "tokens_per_s": B / sec,
+                          "roofline": {"bound": "hbm", "achieved": byt / sec / 1e9, "peak": PEAK_HBM_GBS,
+                                       "unit": "GB/s", "frac": byt / sec / 1e9 / PEAK_HBM_GBS,
+                                       "algorithmic_bytes_per_step": byt}}), flush=True)
+        del dev, ws, xs
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,6 +345,8 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="")
     ap.add_argument("--out")
+    ap.add_argument("--decode", action="store_true",
+                    help="incremental decoding throughput per batch size (one JSON line each)")
     ap.add_argument("--sweep", action="store_true",
                     help="throughput of every named workload (one JSON line each) instead of the headline line")
     args = ap.parse_args()
@@ -307,6 +363,9 @@ def main():
 
     if args.sweep:
         sweep(args.steps, args.warmup)
+        return
+    if args.decode:
+        decode_bench(args.steps if args.steps != 100 else 256, args.warmup)
         return
 
     import torch

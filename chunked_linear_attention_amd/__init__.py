@@ -12,7 +12,8 @@ import numpy as np
 from . import inputs  # noqa: F401
 from ._lib import (  # noqa: F401
     GAU_BF16, GAU_F32, STAGE_ATTN, STAGE_OUT, STAGE_PROJ, STAGE_SCAN, STAGE_SCORES, STAGE_STATE, EXPORTS,
-    GauError, forward, forward_stages, load, make_config, rope_relpos, stack_forward, stack_workspace_bytes,
+    GauError, decode_reset, decode_step, decode_workspace_bytes, forward, forward_stages, load, make_config,
+    rope_relpos, stack_forward, stack_workspace_bytes,
     status_string, workspace_bytes, workspace_layout,
 )
 

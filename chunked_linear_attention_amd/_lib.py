@@ -26,7 +26,8 @@ STATUS = {
 # Every symbol include/gau.h declares.
 EXPORTS = (
     "gau_workspace_bytes", "gau_workspace_layout", "gau_forward", "gau_forward_stages",
-    "gau_stack_workspace_bytes", "gau_stack_forward", "gau_rope_relpos", "gau_status_string",
+    "gau_stack_workspace_bytes", "gau_stack_forward", "gau_decode_workspace_bytes", "gau_decode_reset",
+    "gau_decode_step", "gau_rope_relpos", "gau_status_string",
 )
 
 
@@ -76,6 +77,12 @@ def load():
     PP = ctypes.POINTER(ctypes.c_void_p)
     lib.gau_stack_forward.argtypes = [cfgp, ctypes.c_int, P] + [PP] * 7 + [P, ctypes.c_size_t, P]
     lib.gau_stack_forward.restype = ctypes.c_int
+    lib.gau_decode_workspace_bytes.argtypes = [cfgp]
+    lib.gau_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.gau_decode_reset.argtypes = [cfgp, P, ctypes.c_size_t, P]
+    lib.gau_decode_reset.restype = ctypes.c_int
+    lib.gau_decode_step.argtypes = [cfgp, ctypes.c_int64] + layer
+    lib.gau_decode_step.restype = ctypes.c_int
     lib.gau_rope_relpos.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, P, P]
     lib.gau_rope_relpos.restype = ctypes.c_int
     lib.gau_status_string.argtypes = [ctypes.c_int]
@@ -141,10 +148,11 @@ def _torch_dtype(cfg):
     return torch.bfloat16 if cfg.dtype == GAU_BF16 else torch.float32
 
 
-def _check_layer(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O):
+def _check_layer(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O, T=None):
     import torch
     dt = _torch_dtype(cfg)
-    B, T, d, e, s, C = cfg.B, cfg.T, cfg.d, cfg.e, cfg.s, cfg.C
+    B, d, e, s, C = cfg.B, cfg.d, cfg.e, cfg.s, cfg.C
+    T = cfg.T if T is None else T
     _check(X, "X", dt, B * T * d)
     _check(W_u, "W_u", dt, e * d)
     _check(W_v, "W_v", dt, e * d)
@@ -219,3 +227,28 @@ def rope_relpos(a, b, n, out=None, stream=None):
     if st != 0:
         raise GauError(st, "gau_rope_relpos")
     return out
+
+
+def decode_workspace_bytes(cfg):
+    return load().gau_decode_workspace_bytes(ctypes.byref(cfg))
+
+
+def decode_reset(cfg, workspace, stream=None):
+    """gau_decode_reset: clear the decoding state (before position 0)."""
+    _check(workspace, "workspace")
+    st = load().gau_decode_reset(ctypes.byref(cfg), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    if st != 0:
+        raise GauError(st, "gau_decode_reset")
+
+
+def decode_step(cfg, t, x, W_u, W_v, W_z, W_o, scale, offset, relpos, o, workspace, stream=None):
+    """gau_decode_step: o [B, d] = the causal layer's outputs at position t for
+    the tokens x [B, d], advancing the state in ``workspace``."""
+    _check_layer(cfg, x, W_u, W_v, W_z, W_o, scale, offset, relpos, o, T=1)
+    _check(workspace, "workspace")
+    st = load().gau_decode_step(
+        ctypes.byref(cfg), int(t), _ptr(x), _ptr(W_u), _ptr(W_v), _ptr(W_z), _ptr(W_o), _ptr(scale), _ptr(offset),
+        _ptr(relpos), _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise GauError(st, "gau_decode_step")

@@ -1,0 +1,319 @@
+// Incremental causal decoding: one new token of each of B sequences per call,
+// with a constant-size state per sequence.
+//
+// Pages: the chunk-level recurrence of the causal layer (wikillm, "Method"
+// steps 2-4), the decoder's linear part as a cumulative sum over chunks (Su's
+// post, "Mixed Chunking") and the incremental form of linear attention
+// (papercache 3.1).  The state: P, the sum of the summaries
+// lin_scale * K_lin^T V of the chunks already completed (s x e, fp32), and
+// the current chunk's K_quad, V and K_lin rows (C slots, the layer's element
+// type).  Token t at slot j = t mod C:
+//   u, v, z = SiLU(x W_u), SiLU(x W_v), SiLU(x W_z); four heads from z
+//   (rotated by t with RoPE on); K_quad, V, K_lin stored in slot j;
+//   quad = sum_{tau <= j} relu^2(q_quad . k_quad_tau * quad_scale + w[C-1 + tau - j]) v_tau
+//   y = u * (quad + q_lin P);  o = y W_o
+// and at j = C-1 the chunk's summary is added to P.
+//
+// Three launches per step (a fourth at a chunk's end), all memory-bound: the
+// projection and output GEMVs read every weight once per tile of 8 tokens
+// (one half wave per weight row), the attention kernel reads the chunk's
+// cached rows and P.
+#include "gau_device.h"
+#include "gau_launch.h"
+
+namespace gau {
+namespace {
+
+constexpr int BT = 8;  // tokens per pass over a weight row
+
+template <typename T>
+__device__ __forceinline__ void ld2(const char* p, float& a, float& b);
+template <>
+__device__ __forceinline__ void ld2<bf16>(const char* p, float& a, float& b) {
+    const uint32_t w = *(const uint32_t*)p;
+    a = __uint_as_float(w << 16);
+    b = __uint_as_float(w & 0xFFFF0000u);
+}
+template <>
+__device__ __forceinline__ void ld2<float>(const char* p, float& a, float& b) {
+    const u32x2_t v = *(const u32x2_t*)p;
+    a = __uint_as_float(v.x);
+    b = __uint_as_float(v.y);
+}
+
+template <typename T>
+__device__ __forceinline__ float ld1(const char* p);
+template <>
+__device__ __forceinline__ float ld1<bf16>(const char* p) {
+    return __uint_as_float((uint32_t)(*(const uint16_t*)p) << 16);
+}
+template <>
+__device__ __forceinline__ float ld1<float>(const char* p) {
+    return *(const float*)p;
+}
+
+// Four consecutive elements as floats.
+template <typename T>
+__device__ __forceinline__ void ld4(const char* p, float (&v)[4]) {
+    float a, b, c, d;
+    ld2<T>(p, a, b);
+    ld2<T>(p + 2 * Elem<T>::kBytes, c, d);
+    v[0] = a, v[1] = b, v[2] = c, v[3] = d;
+}
+
+// Sum over the 32 lanes of a half wave.
+__device__ __forceinline__ float half_sum(float v) {
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+constexpr int RL = 32;  // lanes per weight row
+
+// acc[bb] = row . x[b0 + bb] for the tokens of one tile.  row: K elements of
+// type WT; x: B rows of K elements of type XT.  The row is read in 4-element
+// groups strided over the RL lanes of its half wave (up to 8 groups per lane
+// in flight), each multiplied with the same group of every token's x.
+template <typename WT, typename XT>
+__device__ __forceinline__ void row_dots(const char* row, const char* x, int K, int B, int b0, int rl,
+                                         float (&acc)[BT]) {
+    constexpr int WB = Elem<WT>::kBytes, XB = Elem<XT>::kBytes;
+    constexpr int U = 8;
+#pragma unroll
+    for (int bb = 0; bb < BT; ++bb) acc[bb] = 0.f;
+    const int groups = K / 4;
+    for (int g0 = rl; g0 < groups; g0 += RL * U) {
+        float w[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int gi = g0 + u * RL;
+            if (gi < groups) {
+                ld4<WT>(row + (size_t)gi * 4 * WB, w[u]);
+            } else {
+                w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int bb = 0; bb < BT; ++bb) {
+            if (b0 + bb >= B) break;
+            const char* xb = x + (size_t)(b0 + bb) * K * XB;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int gi = g0 + u * RL;
+                if (gi < groups) {
+                    float xv[4];
+                    ld4<XT>(xb + (size_t)gi * 4 * XB, xv);
+                    acc[bb] += w[u][0] * xv[0] + w[u][1] * xv[1] + w[u][2] * xv[2] + w[u][3] * xv[3];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int bb = 0; bb < BT; ++bb) acc[bb] = half_sum(acc[bb]);
+}
+
+// u, v (into the cache slot) and z: one half wave per row of W_u | W_v | W_z.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_proj_kernel(DecodeParams p) {
+    constexpr int EB = Elem<T>::kBytes;
+    const int lane = threadIdx.x % RL;
+    const int f = blockIdx.x * 8 + threadIdx.x / RL;
+    const int N = 2 * p.e + p.s;
+    if (f >= N) return;
+    const size_t pitch = (size_t)p.d * EB;
+    const char* row = f < p.e       ? (const char*)p.W_u + (size_t)f * pitch
+                      : f < 2 * p.e ? (const char*)p.W_v + (size_t)(f - p.e) * pitch
+                                    : (const char*)p.W_z + (size_t)(f - 2 * p.e) * pitch;
+    for (int b0 = 0; b0 < p.B; b0 += BT) {
+        float acc[BT];
+        row_dots<T, T>(row, (const char*)p.x, p.d, p.B, b0, lane, acc);
+        if (lane != 0) continue;
+#pragma unroll
+        for (int bb = 0; bb < BT; ++bb) {
+            const int b = b0 + bb;
+            if (b >= p.B) break;
+            const float h = silu(acc[bb]);
+            if (f < p.e)
+                p.u[(size_t)b * p.e + f] = h;
+            else if (f < 2 * p.e)
+                Elem<T>::put((char*)p.V + (((size_t)b * p.C + p.j) * p.e + (f - p.e)) * EB, h);
+            else
+                p.z[(size_t)b * p.s + (f - 2 * p.e)] = h;
+        }
+    }
+}
+
+// The value x takes once stored in T (the cache holds the heads in the
+// layer's element type, as the forward's workspace does).
+template <typename T>
+__device__ __forceinline__ float as_stored(float x);
+template <>
+__device__ __forceinline__ float as_stored<bf16>(float x) {
+    return __uint_as_float((uint32_t)f32_to_bf16(x) << 16);
+}
+template <>
+__device__ __forceinline__ float as_stored<float>(float x) {
+    return x;
+}
+
+// The token's four heads, and y = u * (quad + q_lin P) for 64 of its
+// features.  Every block of the token forms the heads from z (s/2 pairs,
+// turned by position t with RoPE on) into LDS, uses its own K_quad for the
+// score of slot j, and the first block writes K_quad and K_lin into the
+// cache slot.  The 256 threads then form 4 groups that split the sums over
+// the chunk slots and the state rows.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
+    constexpr int EB = Elem<T>::kBytes;
+    constexpr int FT = 64;
+    constexpr int PARTS = 2 * 4 * FT;  // [quad | lin][group][feature]
+    __shared__ float alpha[512];
+    __shared__ float qq[256];
+    __shared__ float ql[256];
+    __shared__ float kq[256];
+    __shared__ float part[PARTS];
+    const int ftiles = (p.e + FT - 1) / FT;
+    const int b = blockIdx.x / ftiles;
+    const int ft = blockIdx.x - b * ftiles;
+    const int f0 = ft * FT;
+    const int tid = threadIdx.x;
+    const int j = p.j;
+    const int half = p.s / 2;
+    for (int i = tid; i < half; i += 256) {
+        const float zl = p.z[(size_t)b * p.s + i], zh = p.z[(size_t)b * p.s + i + half];
+        double c = 1.0, sn = 0.0;
+        if (p.rope) sincos((double)p.t * rope_theta(i, half), &sn, &c);
+        for (int h = 0; h < 4; ++h) {
+            const float* g = p.scale + h * p.s;
+            const float* o = p.offset + h * p.s;
+            const double lo = (double)(zl * g[i] + o[i]), hi = (double)(zh * g[i + half] + o[i + half]);
+            const float rl = as_stored<T>((float)(lo * c - hi * sn)), rh = as_stored<T>((float)(hi * c + lo * sn));
+            float* dst = h == 0 ? qq : h == 1 ? kq : h == 2 ? ql : nullptr;
+            if (dst) {
+                dst[i] = rl;
+                dst[i + half] = rh;
+            }
+            if (ft == 0 && (h == 1 || h == 3)) {
+                char* k = (char*)(h == 1 ? p.Kq : p.Kl) + (((size_t)b * p.C + j) * p.s) * EB;
+                Elem<T>::put(k + (size_t)i * EB, rl);
+                Elem<T>::put(k + (size_t)(i + half) * EB, rh);
+            }
+        }
+    }
+    __syncthreads();
+    // scores of the chunk's slots 0 .. j (slot j from this block's own K_quad)
+    for (int tau = tid; tau <= j; tau += 256) {
+        float acc = 0.f;
+        if (tau == j) {
+            for (int i = 0; i < p.s; ++i) acc += qq[i] * kq[i];
+        } else {
+            const char* k = (const char*)p.Kq + (((size_t)b * p.C + tau) * p.s) * EB;
+            for (int i = 0; i < p.s; i += 2) {
+                float k0, k1;
+                ld2<T>(k + (size_t)i * EB, k0, k1);
+                acc += qq[i] * k0 + qq[i + 1] * k1;
+            }
+        }
+        const float x = acc * p.qs + p.relpos[p.C - 1 + tau - j];
+        alpha[tau] = x > 0.f ? x * x : 0.f;
+    }
+    __syncthreads();
+    const int g = tid / FT, fl = tid % FT;
+    const int f = f0 + fl;
+    float quad = 0.f, lin = 0.f;
+    if (f < p.e) {
+        const char* V = (const char*)p.V + ((size_t)b * p.C * p.e + f) * EB;
+        for (int tau = g; tau <= j; tau += 4) quad += alpha[tau] * ld1<T>(V + (size_t)tau * p.e * EB);
+        const float* P = p.P + (size_t)b * p.s * p.e + f;
+        for (int i = g; i < p.s; i += 4) lin += ql[i] * P[(size_t)i * p.e];
+    }
+    part[g * FT + fl] = quad;
+    part[4 * FT + g * FT + fl] = lin;
+    __syncthreads();
+    if (g == 0 && f < p.e) {
+        float q = 0.f, l = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {  // fixed order: 0, 1, 2, 3
+            q += part[k * FT + fl];
+            l += part[4 * FT + k * FT + fl];
+        }
+        p.y[(size_t)b * p.e + f] = p.u[(size_t)b * p.e + f] * (q + l);
+    }
+}
+
+// o = y W_o: one half wave per row of W_o^T ([d, e], row n contiguous over e).
+template <typename T>
+__global__ __launch_bounds__(256) void decode_out_kernel(DecodeParams p) {
+    constexpr int EB = Elem<T>::kBytes;
+    const int lane = threadIdx.x % RL;
+    const int n = blockIdx.x * 8 + threadIdx.x / RL;
+    if (n >= p.d) return;
+    const char* row = (const char*)p.W_o + (size_t)n * p.e * EB;
+    for (int b0 = 0; b0 < p.B; b0 += BT) {
+        float acc[BT];
+        row_dots<T, float>(row, (const char*)p.y, p.e, p.B, b0, lane, acc);
+        if (lane != 0) continue;
+#pragma unroll
+        for (int bb = 0; bb < BT; ++bb) {
+            if (b0 + bb >= p.B) break;
+            Elem<T>::put((char*)p.o + ((size_t)(b0 + bb) * p.d + n) * EB, acc[bb]);
+        }
+    }
+}
+
+// P += lin_scale * sum_tau k_lin_tau v_tau^T over the completed chunk's C
+// slots: one thread per state entry (i, f), slots in order.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_state_kernel(DecodeParams p) {
+    constexpr int EB = Elem<T>::kBytes;
+    const int ftiles = (p.e + 255) / 256;
+    const int blk = blockIdx.x;
+    const int b = blk / (p.s * ftiles);
+    const int r = blk - b * p.s * ftiles;
+    const int i = r / ftiles;
+    const int f = (r - i * ftiles) * 256 + threadIdx.x;
+    if (f >= p.e) return;
+    const char* kl = (const char*)p.Kl + ((size_t)b * p.C * p.s + i) * EB;
+    const char* v = (const char*)p.V + ((size_t)b * p.C * p.e + f) * EB;
+    float acc = 0.f;
+    for (int tau = 0; tau < p.C; ++tau)
+        acc += ld1<T>(kl + (size_t)tau * p.s * EB) * ld1<T>(v + (size_t)tau * p.e * EB);
+    p.P[((size_t)b * p.s + i) * p.e + f] += p.ls * acc;
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* x, size_t n) {
+    const size_t k = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (k < n) x[k] = 0.f;
+}
+
+template <typename T>
+hipError_t step(const DecodeParams& p, hipStream_t st) {
+    const unsigned proj_blocks = (unsigned)((2 * p.e + p.s + 7) / 8);
+    hipLaunchKernelGGL(decode_proj_kernel<T>, dim3(proj_blocks), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_attn_kernel<T>, dim3((unsigned)(p.B * ((p.e + 63) / 64))), dim3(256), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_out_kernel<T>, dim3((unsigned)((p.d + 7) / 8)), dim3(256), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.j == p.C - 1) {
+        hipLaunchKernelGGL(decode_state_kernel<T>, dim3((unsigned)(p.B * p.s * ((p.e + 255) / 256))), dim3(256), 0,
+                           st, p);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const DecodeParams& p, bool bf16_storage, hipStream_t st) {
+    return bf16_storage ? step<bf16>(p, st) : step<float>(p, st);
+}
+
+hipError_t launch_fill_zero(float* x, size_t n, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, n);
+    return hipGetLastError();
+}
+
+}  // namespace gau

@@ -73,6 +73,31 @@ gau_status check_layer_ptrs(const LayerPtrs& a) {
     return GAU_OK;
 }
 
+// Decoding workspace: the state (P fp32, the chunk cache in the element type)
+// and the per-step fp32 scratch.
+struct DecodeLayout {
+    size_t P, Kq, V, Kl, u, z, y, total;
+};
+
+void decode_layout(const gau_config* c, DecodeLayout* D) {
+    const size_t eb = elem_bytes(c->dtype);
+    const size_t B = (size_t)c->B, C = (size_t)c->C, e = (size_t)c->e, s = (size_t)c->s;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    D->P = take(B * s * e * 4);
+    D->Kq = take(B * C * s * eb);
+    D->V = take(B * C * e * eb);
+    D->Kl = take(B * C * s * eb);
+    D->u = take(B * e * 4);
+    D->z = take(B * s * 4);
+    D->y = take(B * e * 4);
+    D->total = off;
+}
+
 gau::StateParams state_params(const gau_config* c, const gau_ws_layout& L, char* ws) {
     return gau::StateParams{ws + L.Vt, ws + L.K_lin_t, ws + L.S, (int)c->B, (int)c->T,
                             (int)c->e, (int)c->s, (int)c->C, c->lin_scale};
@@ -218,6 +243,52 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X, cons
         const LayerPtrs a{xn, W_u[l], W_v[l], W_z[l], W_o[l], scale[l], offset[l], relpos[l]};
         if ((s = run_stages(cfg, GAU_STAGE_PROJ, GAU_STAGE_OUT, a, X, X, ws, st)) != GAU_OK) return s;
     }
+    return GAU_OK;
+}
+
+size_t gau_decode_workspace_bytes(const gau_config* cfg) {
+    if (check_config(cfg) != GAU_OK || !cfg->causal) return 0;
+    DecodeLayout D;
+    decode_layout(cfg, &D);
+    return D.total;
+}
+
+gau_status gau_decode_reset(const gau_config* cfg, void* workspace, size_t workspace_bytes, void* stream) {
+    gau_status s = check_config(cfg);
+    if (s != GAU_OK) return s;
+    if (!cfg->causal) return GAU_ERR_SHAPE;
+    if (cfg->B == 0) return GAU_OK;
+    if (!workspace) return GAU_ERR_NULL;
+    if (!aligned16(workspace)) return GAU_ERR_ALIGN;
+    DecodeLayout D;
+    decode_layout(cfg, &D);
+    if (workspace_bytes < D.total) return GAU_ERR_WORKSPACE;
+    const size_t n = (size_t)cfg->B * cfg->s * cfg->e;
+    if (gau::launch_fill_zero((float*)((char*)workspace + D.P), n, (hipStream_t)stream) != hipSuccess)
+        return GAU_ERR_HIP;
+    return GAU_OK;
+}
+
+gau_status gau_decode_step(const gau_config* cfg, int64_t t, const void* x, const void* W_u, const void* W_v,
+                           const void* W_z, const void* W_o, const float* scale, const float* offset,
+                           const float* relpos, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+    gau_status s = check_config(cfg);
+    if (s != GAU_OK) return s;
+    if (!cfg->causal || t < 0 || t >= cfg->T) return GAU_ERR_SHAPE;
+    if (cfg->B == 0) return GAU_OK;
+    const LayerPtrs a{x, W_u, W_v, W_z, W_o, scale, offset, relpos};
+    if ((s = check_layer_ptrs(a)) != GAU_OK) return s;
+    if (!o || !workspace) return GAU_ERR_NULL;
+    if (!aligned16(o) || !aligned16(workspace)) return GAU_ERR_ALIGN;
+    DecodeLayout D;
+    decode_layout(cfg, &D);
+    if (workspace_bytes < D.total) return GAU_ERR_WORKSPACE;
+    char* ws = (char*)workspace;
+    const gau::DecodeParams p{x, W_u, W_v, W_z, W_o, scale, offset, relpos, o,
+                              (float*)(ws + D.P), ws + D.Kq, ws + D.V, ws + D.Kl,
+                              (float*)(ws + D.u), (float*)(ws + D.z), (float*)(ws + D.y), (int)cfg->B, (int)cfg->d, (int)cfg->e, (int)cfg->s, (int)cfg->C,
+                              (int)t, (int)(t % cfg->C), cfg->rope, cfg->quad_scale, cfg->lin_scale};
+    if (gau::launch_decode_step(p, cfg->dtype == GAU_BF16, (hipStream_t)stream) != hipSuccess) return GAU_ERR_HIP;
     return GAU_OK;
 }
 

@@ -95,6 +95,29 @@ struct RopeParams {
 };
 
 hipError_t launch_rope_heads(const RopeParams& p, bool bf16_storage, hipStream_t st);
+
+// One incremental decoding step (causal): token t, chunk slot j = t mod C.
+struct DecodeParams {
+    const void* x;      // [B, d]  the new tokens
+    const void* W_u;    // [e, d]
+    const void* W_v;    // [e, d]
+    const void* W_z;    // [s, d]
+    const void* W_o;    // [d, e]
+    const float* scale;   // [4, s]
+    const float* offset;  // [4, s]
+    const float* relpos;  // [2C-1]
+    void* o;            // [B, d]
+    float* P;           // [B, s, e] fp32 state: completed chunks' summaries
+    void* Kq;           // [B, C, s] chunk cache
+    void* V;            // [B, C, e]
+    void* Kl;           // [B, C, s]
+    float *u, *z, *y;   // [B, e], [B, s], [B, e] scratch
+    int B, d, e, s, C, t, j, rope;
+    float qs, ls;
+};
+
+hipError_t launch_decode_step(const DecodeParams& p, bool bf16_storage, hipStream_t st);
+hipError_t launch_fill_zero(float* x, size_t n, hipStream_t st);
 // w[n-1 + d] = a . rope(b, d), d = -(n-1) .. n-1 (a, b: [dim] fp32; w: [2n-1])
 hipError_t launch_rope_relpos(const float* a, const float* b, int n, int dim, float* relpos, hipStream_t st);
 hipError_t launch_chunk_state(const StateParams& p, bool bf16_storage, hipStream_t st);

@@ -26,8 +26,6 @@
 namespace gau {
 namespace {
 
-__device__ __forceinline__ double theta(int i, int half) { return pow(10000.0, -(double)i / (double)half); }
-
 template <typename T>
 __device__ __forceinline__ void get4(const char* p, double (&v)[4]);
 template <>
@@ -79,7 +77,7 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(RopeParams p) {
     const double t = (double)(m % p.T);
     double c[4], s[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sincos(t * theta(i0 + k, half), &s[k], &c[k]);
+    for (int k = 0; k < 4; ++k) sincos(t * rope_theta(i0 + k, half), &s[k], &c[k]);
     void* heads[3] = {p.Qq, p.Kq, p.Ql};
 #pragma unroll
     for (int h = 0; h < 3; ++h) {
@@ -106,7 +104,7 @@ __global__ __launch_bounds__(256) void rope_cols_kernel(RopeParams p) {
     const long r = idx - (long)b * half * tg;
     const int i = (int)(r / tg);
     const int t0 = (int)(r - (long)i * tg) * 4;
-    const double th = theta(i, half);
+    const double th = rope_theta(i, half);
     double c[4], s[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) sincos((double)(t0 + k) * th, &s[k], &c[k]);
@@ -132,7 +130,7 @@ __global__ __launch_bounds__(256) void rope_relpos_kernel(const float* a, const 
     double acc = 0.0;
     for (int i = 0; i < half; ++i) {
         double sn, cs;
-        sincos(d * theta(i, half), &sn, &cs);
+        sincos(d * rope_theta(i, half), &sn, &cs);
         const double ai = a[i], ah = a[i + half], bi = b[i], bh = b[i + half];
         acc += cs * (ai * bi + ah * bh) + sn * (ah * bi - ai * bh);
     }

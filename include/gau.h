@@ -203,6 +203,44 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Incremental causal decoding: one new token of each of the B sequences per
+ * call, with a constant-size state per sequence (the chunk-level recurrence
+ * of the causal layer: wikillm, "Method" steps 2-4; Su's post, "Mixed
+ * Chunking", the decoder's cumulative sum over chunks; papercache 3.1, the
+ * incremental form of linear attention).  Token t at slot j = t mod C of its
+ * chunk:
+ *   u, v, z = SiLU(x W_u), SiLU(x W_v), SiLU(x W_z); the four heads of z
+ *     (rotated by position t when cfg->rope = 1)
+ *   quad = sum_{tau = 0..j} relu^2(quad_scale q_quad . k_quad_tau + relpos[C-1 + tau - j]) v_tau
+ *   o_t  = [u * (quad + q_lin P)] W_o
+ * over the current chunk's cached k_quad, v, k_lin rows, where P is the sum of
+ * lin_scale * K_lin^T V over the chunks already completed; when j = C-1 the
+ * chunk's summary is added to P.  Calling it for t = 0, 1, 2, ... gives the
+ * causal gau_forward's outputs token by token.
+ *
+ * cfg: as gau_forward with causal = 1 (else GAU_ERR_SHAPE); cfg->T bounds the
+ *   positions (0 <= t < T); B is the number of sequences decoded together.
+ * workspace: at least gau_decode_workspace_bytes(cfg) bytes of device memory
+ *   holding the state (P as [B, s, e] fp32; the chunk's K_quad and K_lin rows
+ *   [B, C, s] and V rows [B, C, e] in cfg->dtype) and per-step scratch.  It
+ *   must be reset (gau_decode_reset) before t = 0, and each call must follow
+ *   the call for t - 1 on the same workspace (not checked: the library keeps
+ *   no position).
+ *   x  [B, d] dt  the tokens at position t;  o [B, d] dt  their outputs.
+ *   W_u .. relpos as gau_forward.
+ * Checks and status codes as gau_forward; 0 is returned for an invalid cfg by
+ * gau_decode_workspace_bytes.  B == 0 is a no-op.
+ */
+size_t gau_decode_workspace_bytes(const gau_config* cfg);
+
+gau_status gau_decode_reset(const gau_config* cfg, void* workspace, size_t workspace_bytes, void* stream);
+
+gau_status gau_decode_step(const gau_config* cfg, int64_t t, const void* x,
+                           const void* W_u, const void* W_v, const void* W_z, const void* W_o,
+                           const float* scale, const float* offset, const float* relpos,
+                           void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The relative-position bias of chunk length n built from RoPE-rotated vectors
  * (the n >= 512 branch of papercache, appendix D, Code 4): the Toeplitz matrix
  * rope(a)_m . rope(b)_k depends only on k - m, so it is carried by

@@ -78,6 +78,26 @@ static void run(const Cfg& c, const std::string& only) {
     float* rb = (float*)buf(128 * 4);
     float* rw = (float*)buf((2 * c.C - 1) * 4);
     t("rope_relpos", [&] { CHECK(launch_rope_relpos(ra, rb, c.C, 128, rw, nullptr)); });
+    // one decoding step at the first slot of a chunk and one at its last
+    // (which also adds the chunk's summary to the state)
+    void* dx = buf((size_t)c.B * c.d * eb);
+    void* dO = buf((size_t)c.B * c.d * eb);
+    float* dP = (float*)buf((size_t)c.B * c.s * c.e * 4);
+    void* dKq = buf((size_t)c.B * c.C * c.s * eb);
+    void* dV = buf((size_t)c.B * c.C * c.e * eb);
+    void* dKl = buf((size_t)c.B * c.C * c.s * eb);
+    float* du = (float*)buf((size_t)c.B * c.e * 4);
+    float* dz = (float*)buf((size_t)c.B * c.s * 4);
+    float* dy = (float*)buf((size_t)c.B * c.e * 4);
+    if (c.causal) {
+        for (int pos : {0, c.C - 1}) {
+            DecodeParams dp{dx, Wu, Wv, Wz, Wo, sc, of, rp, dO, dP, dKq, dV, dKl, du, dz, dy,
+                            c.B, c.d, c.e, c.s, c.C, pos, pos % c.C, 1, 1.0f / c.C, 1.0f / c.C};
+            t(pos == 0 ? "decode_step_j0" : "decode_step_jlast",
+              [&] { CHECK(launch_decode_step(dp, c.bf, nullptr)); });
+        }
+        t("fill_zero", [&] { CHECK(launch_fill_zero(dP, (size_t)c.B * c.s * c.e, nullptr)); });
+    }
     ScoresParams sp{Qq, Kq, rp, A, c.B, c.T, c.s, c.C, c.causal ? 1 : 0, 1.0f / c.C};
     t("chunk_scores", [&] { CHECK(launch_chunk_scores(sp, c.bf, nullptr)); });
     StateParams stp{Vt, Klt, S, c.B, c.T, c.e, c.s, c.C, 1.0f / c.C};
@@ -107,7 +127,8 @@ static void run(const Cfg& c, const std::string& only) {
         free(ws);
     });
     for (void* p : {X, Wu, Wv, Wz, Wo, (void*)sc, (void*)of, (void*)rp, U, Vt, Qq, Kq, Ql, Klt, (void*)S, P, A, Y, O,
-                    (void*)Of, (void*)ra, (void*)rb, (void*)rw})
+                    (void*)Of, (void*)ra, (void*)rb, (void*)rw, dx, dO, (void*)dP, dKq, dV, dKl, (void*)du,
+                    (void*)dz, (void*)dy})
         free(p);
 }
 

@@ -79,6 +79,28 @@ def test_rope_relpos_argument_checks_without_gpu():
     assert lib.gau_rope_relpos(P(4100), b, 64, 128, w, None) == 3
 
 
+def test_decode_argument_checks_without_gpu():
+    lib = g.load()
+    cfg = _cfg()
+    ws = g.decode_workspace_bytes(cfg)
+    assert ws > 0 and g.decode_workspace_bytes(_cfg(causal=False)) == 0
+    good = [ctypes.c_void_p(4096 * (i + 1)) for i in range(10)]
+    call = lambda c, t, ptrs, n: lib.gau_decode_step(ctypes.byref(c), t, *ptrs, ctypes.c_size_t(n), None)
+    assert call(_cfg(causal=False), 0, good, ws) == 2       # decoding is causal only
+    assert call(cfg, -1, good, ws) == 2
+    assert call(cfg, cfg.T, good, ws) == 2                  # positions 0 .. T-1
+    assert call(cfg, 0, good, ws - 1) == 5
+    assert call(cfg, 0, [None] + good[1:], ws) == 1
+    bad = list(good)
+    bad[8] = ctypes.c_void_p(4096 * 9 + 4)
+    assert call(cfg, 0, bad, ws) == 3                       # misaligned o
+    assert call(_cfg(B=0), 0, [None] * 10, 0) == 0          # nothing to decode
+    P = ctypes.c_void_p
+    assert lib.gau_decode_reset(ctypes.byref(_cfg(causal=False)), P(4096), ctypes.c_size_t(ws), None) == 2
+    assert lib.gau_decode_reset(ctypes.byref(cfg), P(4096), ctypes.c_size_t(ws - 1), None) == 5
+    assert lib.gau_decode_reset(ctypes.byref(cfg), None, ctypes.c_size_t(ws), None) == 1
+
+
 def test_bad_dtype_rejected():
     cfg = _cfg()
     cfg.dtype = 7

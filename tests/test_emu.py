@@ -126,3 +126,39 @@ def test_emulated_kernels_match_oracle(emu, case, late):
         assert np.all(np.isfinite(got)), name
         err = np.max(np.abs(got - want)) / np.max(np.abs(want))
         assert err <= tol, f"{name}: {err:.3e} > {tol}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_emulated_decoding_matches_the_causal_layer(emu, dtype):
+    """gau_decode_step on the emulation for 70 tokens (one chunk end, C = 64)
+    against the oracle's causal layer."""
+    B, T, d, e, s, C = 2, 128, 128, 256, 128, 64
+    steps = 70
+    bf = dtype == "bf16"
+    emu.emu_set_mode(1, 1)
+    P = ctypes.c_void_p
+    emu.gau_decode_workspace_bytes.restype = ctypes.c_size_t
+    emu.gau_decode_workspace_bytes.argtypes = [ctypes.POINTER(GauConfig)]
+    emu.gau_decode_reset.argtypes = [ctypes.POINTER(GauConfig), P, ctypes.c_size_t, P]
+    emu.gau_decode_step.argtypes = [ctypes.POINTER(GauConfig), ctypes.c_int64] + [P] * 10 + [ctypes.c_size_t, P]
+    inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=41, dtype=dtype)
+    cfg = GauConfig(B, T, d, e, s, C, 1, 1 if bf else 0, 1.0 / C, 1.0 / C, 1)
+    W = {k: _host(np.ascontiguousarray(inp[k].T), bf) for k in ("W_u", "W_v", "W_z", "W_o")}
+    sc, of, rp = (np.ascontiguousarray(inp[k], np.float32) for k in ("gamma", "beta", "relpos"))
+    wsb = emu.gau_decode_workspace_bytes(ctypes.byref(cfg))
+    raw = np.full(wsb + 256, 0xFF, np.uint8)
+    ws = raw[(-raw.ctypes.data) % 256:][:wsb]
+    ptr = lambda a: P(a.ctypes.data)
+    assert emu.gau_decode_reset(ctypes.byref(cfg), ptr(ws), wsb, None) == 0
+    conv = inputs.bf16_bits_to_f32 if bf else (lambda a: a)
+    got = np.zeros((B, steps, d))
+    for t in range(steps):
+        x = _host(np.ascontiguousarray(inp["X"][:, t]), bf)
+        o = np.zeros((B, d), np.uint16 if bf else np.float32)
+        assert emu.gau_decode_step(ctypes.byref(cfg), t, ptr(x), ptr(W["W_u"]), ptr(W["W_v"]), ptr(W["W_z"]),
+                                   ptr(W["W_o"]), ptr(sc), ptr(of), ptr(rp), ptr(o), ptr(ws), wsb, None) == 0
+        got[:, t] = conv(o)
+    ref = orc.flash_forward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"], inp["beta"],
+                            inp["relpos"], C, True, use_rope=True)[:, :steps]
+    err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+    assert err <= (2e-2 if bf else 1e-4), err
