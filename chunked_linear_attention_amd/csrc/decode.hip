@@ -201,17 +201,33 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
         }
     }
     __syncthreads();
-    // scores of the chunk's slots 0 .. j (slot j from this block's own K_quad)
+    // scores of the chunk's slots 0 .. j (slot j from this block's own K_quad):
+    // one thread per slot, its K_quad row read as 16-byte vectors all in flight
     for (int tau = tid; tau <= j; tau += 256) {
         float acc = 0.f;
         if (tau == j) {
             for (int i = 0; i < p.s; ++i) acc += qq[i] * kq[i];
         } else {
             const char* k = (const char*)p.Kq + (((size_t)b * p.C + tau) * p.s) * EB;
-            for (int i = 0; i < p.s; i += 2) {
-                float k0, k1;
-                ld2<T>(k + (size_t)i * EB, k0, k1);
-                acc += qq[i] * k0 + qq[i + 1] * k1;
+            constexpr int VE = 16 / EB;  // elements per vector
+            for (int i0 = 0; i0 < p.s; i0 += 8 * VE) {  // s is a multiple of 128
+                u32x4_t w[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) w[u] = *(const u32x4_t*)(k + (size_t)(i0 + u * VE) * EB);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = i0 + u * VE;
+                    if constexpr (EB == 2) {
+                        const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc += qq[i + 2 * q] * __uint_as_float(ww[q] << 16) +
+                                   qq[i + 2 * q + 1] * __uint_as_float(ww[q] & 0xFFFF0000u);
+                    } else {
+                        acc += qq[i] * __uint_as_float(w[u].x) + qq[i + 1] * __uint_as_float(w[u].y) +
+                               qq[i + 2] * __uint_as_float(w[u].z) + qq[i + 3] * __uint_as_float(w[u].w);
+                    }
+                }
             }
         }
         const float x = acc * p.qs + p.relpos[p.C - 1 + tau - j];
@@ -223,9 +239,24 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
     float quad = 0.f, lin = 0.f;
     if (f < p.e) {
         const char* V = (const char*)p.V + ((size_t)b * p.C * p.e + f) * EB;
-        for (int tau = g; tau <= j; tau += 4) quad += alpha[tau] * ld1<T>(V + (size_t)tau * p.e * EB);
+        const size_t vs = (size_t)p.e * EB;
+        int tau = g;
+        for (; tau + 28 <= j; tau += 32) {  // eight independent loads in flight
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = ld1<T>(V + (size_t)(tau + 4 * u) * vs);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) quad += alpha[tau + 4 * u] * v[u];
+        }
+        for (; tau <= j; tau += 4) quad += alpha[tau] * ld1<T>(V + (size_t)tau * vs);
         const float* P = p.P + (size_t)b * p.s * p.e + f;
-        for (int i = g; i < p.s; i += 4) lin += ql[i] * P[(size_t)i * p.e];
+        for (int i = g; i < p.s; i += 32) {  // s is a multiple of 128
+            float w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w[u] = P[(size_t)(i + 4 * u) * p.e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) lin += ql[i + 4 * u] * w[u];
+        }
     }
     part[g * FT + fl] = quad;
     part[4 * FT + g * FT + fl] = lin;
@@ -262,23 +293,50 @@ __global__ __launch_bounds__(256) void decode_out_kernel(DecodeParams p) {
 }
 
 // P += lin_scale * sum_tau k_lin_tau v_tau^T over the completed chunk's C
-// slots: one thread per state entry (i, f), slots in order.
+// slots: a 64 x 64 tile of (state row i, feature f) per block, the slots in
+// steps of 16 staged through LDS, each thread 4 x 4 entries (rows ty + 16 r,
+// features tx + 16 c), slots summed in order.
 template <typename T>
 __global__ __launch_bounds__(256) void decode_state_kernel(DecodeParams p) {
     constexpr int EB = Elem<T>::kBytes;
-    const int ftiles = (p.e + 255) / 256;
+    constexpr int TI = 64, TF = 64, TK = 16;
+    constexpr int KT = TK * TI, VT = TK * TF;
+    __shared__ float kt[KT];
+    __shared__ float vt[VT];
+    const int itiles = p.s / TI, ftiles = (p.e + TF - 1) / TF;
     const int blk = blockIdx.x;
-    const int b = blk / (p.s * ftiles);
-    const int r = blk - b * p.s * ftiles;
-    const int i = r / ftiles;
-    const int f = (r - i * ftiles) * 256 + threadIdx.x;
-    if (f >= p.e) return;
-    const char* kl = (const char*)p.Kl + ((size_t)b * p.C * p.s + i) * EB;
-    const char* v = (const char*)p.V + ((size_t)b * p.C * p.e + f) * EB;
-    float acc = 0.f;
-    for (int tau = 0; tau < p.C; ++tau)
-        acc += ld1<T>(kl + (size_t)tau * p.s * EB) * ld1<T>(v + (size_t)tau * p.e * EB);
-    p.P[((size_t)b * p.s + i) * p.e + f] += p.ls * acc;
+    const int b = blk / (itiles * ftiles);
+    const int r = blk - b * itiles * ftiles;
+    const int i0 = (r / ftiles) * TI, f0 = (r % ftiles) * TF;
+    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+    const char* kl = (const char*)p.Kl + (size_t)b * p.C * p.s * EB;
+    const char* v = (const char*)p.V + (size_t)b * p.C * p.e * EB;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < p.C; k0 += TK) {
+        __syncthreads();
+        for (int x = tid; x < KT; x += 256) {  // [slot][row]
+            const int kk = x / TI, ii = x % TI;
+            kt[x] = ld1<T>(kl + ((size_t)(k0 + kk) * p.s + i0 + ii) * EB);
+        }
+        for (int x = tid; x < VT; x += 256) {  // [slot][feature]
+            const int kk = x / TF, ff = x % TF;
+            vt[x] = f0 + ff < p.e ? ld1<T>(v + ((size_t)(k0 + kk) * p.e + f0 + ff) * EB) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < TK; ++kk)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) acc[rr][cc] += kt[kk * TI + ty + 16 * rr] * vt[kk * TF + tx + 16 * cc];
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const int f = f0 + tx + 16 * cc;
+            if (f < p.e) p.P[((size_t)b * p.s + i0 + ty + 16 * rr) * p.e + f] += p.ls * acc[rr][cc];
+        }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* x, size_t n) {
@@ -297,8 +355,8 @@ hipError_t step(const DecodeParams& p, hipStream_t st) {
     hipLaunchKernelGGL(decode_out_kernel<T>, dim3((unsigned)((p.d + 7) / 8)), dim3(256), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.j == p.C - 1) {
-        hipLaunchKernelGGL(decode_state_kernel<T>, dim3((unsigned)(p.B * p.s * ((p.e + 255) / 256))), dim3(256), 0,
-                           st, p);
+        hipLaunchKernelGGL(decode_state_kernel<T>, dim3((unsigned)(p.B * (p.s / 64) * ((p.e + 63) / 64))), dim3(256),
+                           0, st, p);
         e = hipGetLastError();
     }
     return e;
