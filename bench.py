@@ -288,7 +288,45 @@ def decode_bytes(B, d, e, s, C, eb=2):
     return weights + B * per_seq
 
 
-def decode_bench(steps, warmup, batches=(1, 2, 8, 32, 128)):
+DECODE_BATCHES = (1, 2, 8, 32, 128)
+
+
+def summarize_decode_trace(trace_csv, command, out, steps=256, warmup=20):
+    """Markdown table of the decoding kernels per batch size from a rocprofv3
+    --kernel-trace of `bench.py --decode` (dispatches in launch order: for each
+    batch size, warmup + steps decoding steps)."""
+    import csv
+    import re
+    rows = [r for r in csv.DictReader(open(trace_csv)) if "decode_" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = {}
+    idx, cnt = 0, 0
+    for r in rows:
+        name = re.search(r"(decode_\w+)_kernel", r["Kernel_Name"]).group(1)
+        if name == "decode_proj":
+            cnt += 1
+            if cnt > steps + warmup:
+                idx, cnt = idx + 1, 1
+        per.setdefault((DECODE_BATCHES[idx], name), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    kernels = ["decode_proj", "decode_attn", "decode_out", "decode_state"]
+    lines = ["# rocprofv3 kernel trace: incremental decoding, d=768 e=1536 s=128 C=256, bf16", "",
+             "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
+             "Average duration per launch (us) by batch size B; decode_state runs once per chunk "
+             f"({steps} steps per batch size, {warmup} warm-up steps before them).", "",
+             "| B | " + " | ".join(f"`{k}`" for k in kernels) + " |",
+             "|---:|" + "---:|" * len(kernels)]
+    for B in DECODE_BATCHES:
+        cells = []
+        for k in kernels:
+            v = per.get((B, k), [])
+            cells.append(f"{sum(v) / len(v):.1f}" if v else "-")
+        lines.append(f"| {B} | " + " | ".join(cells) + " |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def decode_bench(steps, warmup, batches=DECODE_BATCHES):
     """Incremental decoding at the headline layer's shape (d=768, e=1536,
     s=128, C=256, bf16): one JSON line per batch size, timed over `steps`
     consecutive positions (a whole chunk by default, so the state update at
@@ -345,6 +383,7 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="")
     ap.add_argument("--out")
+    ap.add_argument("--summarize-decode-trace", metavar="TRACE_CSV")
     ap.add_argument("--decode", action="store_true",
                     help="incremental decoding throughput per batch size (one JSON line each)")
     ap.add_argument("--sweep", action="store_true",
@@ -352,6 +391,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.command, args.out)
+        return
+    if args.summarize_decode_trace:
+        summarize_decode_trace(args.summarize_decode_trace, args.command, args.out)
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.command)
