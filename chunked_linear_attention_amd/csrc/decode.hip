@@ -14,17 +14,20 @@
 //   y = u * (quad + q_lin P);  o = y W_o
 // and at j = C-1 the chunk's summary is added to P.
 //
-// Three launches per step (a fourth at a chunk's end), all memory-bound: the
-// projection and output GEMVs read every weight once per tile of 8 tokens
-// (one half wave per weight row), the attention kernel reads the chunk's
-// cached rows and P.
+// Three launches per step (a fourth at a chunk's end).  Up to MFMA_MIN_B - 1
+// tokens the projection and output products are GEMVs that read every
+// weight once per tile of 8 tokens (one half wave per weight row); from
+// MFMA_MIN_B on they run on the shared MFMA core as GEMMs with 64-token
+// tiles.  The attention kernel reads the chunk's cached rows and P.
 #include "gau_device.h"
 #include "gau_launch.h"
+#include "gemm_core.h"
 
 namespace gau {
 namespace {
 
-constexpr int BT = 8;  // tokens per pass over a weight row
+constexpr int BT = 8;           // tokens per pass over a weight row (GEMV)
+constexpr int MFMA_MIN_B = 3;   // batch from which the products use the MFMA core (measured)
 
 template <typename T>
 __device__ __forceinline__ void ld2(const char* p, float& a, float& b);
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
             q += part[k * FT + fl];
             l += part[4 * FT + k * FT + fl];
         }
-        p.y[(size_t)b * p.e + f] = p.u[(size_t)b * p.e + f] * (q + l);
+        Elem<T>::put((char*)p.y + ((size_t)b * p.e + f) * EB, p.u[(size_t)b * p.e + f] * (q + l));
     }
 }
 
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(256) void decode_out_kernel(DecodeParams p) {
     const char* row = (const char*)p.W_o + (size_t)n * p.e * EB;
     for (int b0 = 0; b0 < p.B; b0 += BT) {
         float acc[BT];
-        row_dots<T, float>(row, (const char*)p.y, p.e, p.B, b0, lane, acc);
+        row_dots<T, T>(row, (const char*)p.y, p.e, p.B, b0, lane, acc);
         if (lane != 0) continue;
 #pragma unroll
         for (int bb = 0; bb < BT; ++bb) {
@@ -339,6 +342,58 @@ __global__ __launch_bounds__(256) void decode_state_kernel(DecodeParams p) {
         }
 }
 
+// The projection as a GEMM for larger batches: 64 rows of W_u | W_v | W_z
+// (the tile lies in one of them: e and s are multiples of 64) times 64
+// tokens, K = d; epilogue as decode_proj_kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_proj_mfma_kernel(DecodeParams p) {
+    extern __shared__ __align__(16) char lds[];
+    using G = GemmCore<T, 64, 64, 2, 2>;
+    constexpr int EB = Elem<T>::kBytes;
+    const int ntiles = (2 * p.e + p.s) / 64;
+    const int nt = blockIdx.x % ntiles, bt = blockIdx.x / ntiles;
+    const int f0 = nt * 64, b0 = bt * 64;
+    const size_t pitch = (size_t)p.d * EB;
+    const char* w = f0 < p.e       ? (const char*)p.W_u + (size_t)f0 * pitch
+                    : f0 < 2 * p.e ? (const char*)p.W_v + (size_t)(f0 - p.e) * pitch
+                                   : (const char*)p.W_z + (size_t)(f0 - 2 * p.e) * pitch;
+    f32x16_t acc[G::MB][G::NB];
+    G::zero(acc);
+    G::run(acc, w, pitch, 64, (const char*)p.x + (size_t)b0 * pitch, pitch, min(64, p.B - b0), p.d, lds);
+    G::for_each(acc, [&](int row, int col, float v) {
+        const int f = f0 + row, b = b0 + col;
+        if (b >= p.B) return;
+        const float h = silu(v);
+        if (f < p.e)
+            p.u[(size_t)b * p.e + f] = h;
+        else if (f < 2 * p.e)
+            Elem<T>::put((char*)p.V + (((size_t)b * p.C + p.j) * p.e + (f - p.e)) * EB, h);
+        else
+            p.z[(size_t)b * p.s + (f - 2 * p.e)] = h;
+    });
+}
+
+// o = y W_o as a GEMM for larger batches: 32 rows of W_o^T times 64 tokens,
+// K = e (two waves).
+template <typename T>
+__global__ __launch_bounds__(128) void decode_out_mfma_kernel(DecodeParams p) {
+    extern __shared__ __align__(16) char lds[];
+    using G = GemmCore<T, 32, 64, 1, 2>;
+    constexpr int EB = Elem<T>::kBytes;
+    const int ntiles = p.d / 32;
+    const int nt = blockIdx.x % ntiles, bt = blockIdx.x / ntiles;
+    const int n0 = nt * 32, b0 = bt * 64;
+    const size_t pitch = (size_t)p.e * EB;
+    f32x16_t acc[G::MB][G::NB];
+    G::zero(acc);
+    G::run(acc, (const char*)p.W_o + (size_t)n0 * pitch, pitch, 32, (const char*)p.y + (size_t)b0 * pitch, pitch,
+           min(64, p.B - b0), p.e, lds);
+    G::for_each(acc, [&](int row, int col, float v) {
+        const int b = b0 + col;
+        if (b < p.B) Elem<T>::put((char*)p.o + ((size_t)b * p.d + n0 + row) * EB, v);
+    });
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* x, size_t n) {
     const size_t k = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (k < n) x[k] = 0.f;
@@ -346,13 +401,25 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* x, size_t n) {
 
 template <typename T>
 hipError_t step(const DecodeParams& p, hipStream_t st) {
-    const unsigned proj_blocks = (unsigned)((2 * p.e + p.s + 7) / 8);
-    hipLaunchKernelGGL(decode_proj_kernel<T>, dim3(proj_blocks), dim3(256), 0, st, p);
+    const bool mfma = p.B >= MFMA_MIN_B;
+    const unsigned btiles = (unsigned)((p.B + 63) / 64);
+    if (mfma) {
+        constexpr int LDS = GemmCore<T, 64, 64, 2, 2>::LDS_BYTES;
+        hipLaunchKernelGGL(decode_proj_mfma_kernel<T>, dim3((unsigned)((2 * p.e + p.s) / 64) * btiles), dim3(256),
+                           LDS, st, p);
+    } else {
+        hipLaunchKernelGGL(decode_proj_kernel<T>, dim3((unsigned)((2 * p.e + p.s + 7) / 8)), dim3(256), 0, st, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_attn_kernel<T>, dim3((unsigned)(p.B * ((p.e + 63) / 64))), dim3(256), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_out_kernel<T>, dim3((unsigned)((p.d + 7) / 8)), dim3(256), 0, st, p);
+    if (mfma) {
+        constexpr int LDS = GemmCore<T, 32, 64, 1, 2>::LDS_BYTES;
+        hipLaunchKernelGGL(decode_out_mfma_kernel<T>, dim3((unsigned)(p.d / 32) * btiles), dim3(128), LDS, st, p);
+    } else {
+        hipLaunchKernelGGL(decode_out_kernel<T>, dim3((unsigned)((p.d + 7) / 8)), dim3(256), 0, st, p);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.j == p.C - 1) {
         hipLaunchKernelGGL(decode_state_kernel<T>, dim3((unsigned)(p.B * (p.s / 64) * ((p.e + 63) / 64))), dim3(256),

@@ -94,7 +94,7 @@ void decode_layout(const gau_config* c, DecodeLayout* D) {
     D->Kl = take(B * C * s * eb);
     D->u = take(B * e * 4);
     D->z = take(B * s * 4);
-    D->y = take(B * e * 4);
+    D->y = take(B * e * eb);
     D->total = off;
 }
 
@@ -286,7 +286,7 @@ gau_status gau_decode_step(const gau_config* cfg, int64_t t, const void* x, cons
     char* ws = (char*)workspace;
     const gau::DecodeParams p{x, W_u, W_v, W_z, W_o, scale, offset, relpos, o,
                               (float*)(ws + D.P), ws + D.Kq, ws + D.V, ws + D.Kl,
-                              (float*)(ws + D.u), (float*)(ws + D.z), (float*)(ws + D.y), (int)cfg->B, (int)cfg->d, (int)cfg->e, (int)cfg->s, (int)cfg->C,
+                              (float*)(ws + D.u), (float*)(ws + D.z), ws + D.y, (int)cfg->B, (int)cfg->d, (int)cfg->e, (int)cfg->s, (int)cfg->C,
                               (int)t, (int)(t % cfg->C), cfg->rope, cfg->quad_scale, cfg->lin_scale};
     if (gau::launch_decode_step(p, cfg->dtype == GAU_BF16, (hipStream_t)stream) != hipSuccess) return GAU_ERR_HIP;
     return GAU_OK;

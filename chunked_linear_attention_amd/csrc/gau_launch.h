@@ -111,7 +111,8 @@ struct DecodeParams {
     void* Kq;           // [B, C, s] chunk cache
     void* V;            // [B, C, e]
     void* Kl;           // [B, C, s]
-    float *u, *z, *y;   // [B, e], [B, s], [B, e] scratch
+    float *u, *z;       // [B, e], [B, s] fp32 scratch
+    void* y;            // [B, e] element type scratch (the gated attention output)
     int B, d, e, s, C, t, j, rope;
     float qs, ls;
 };

@@ -88,7 +88,7 @@ static void run(const Cfg& c, const std::string& only) {
     void* dKl = buf((size_t)c.B * c.C * c.s * eb);
     float* du = (float*)buf((size_t)c.B * c.e * 4);
     float* dz = (float*)buf((size_t)c.B * c.s * 4);
-    float* dy = (float*)buf((size_t)c.B * c.e * 4);
+    void* dy = buf((size_t)c.B * c.e * eb);
     if (c.causal) {
         for (int pos : {0, c.C - 1}) {
             DecodeParams dp{dx, Wu, Wv, Wz, Wo, sc, of, rp, dO, dP, dKq, dV, dKl, du, dz, dy,
@@ -128,7 +128,7 @@ static void run(const Cfg& c, const std::string& only) {
     });
     for (void* p : {X, Wu, Wv, Wz, Wo, (void*)sc, (void*)of, (void*)rp, U, Vt, Qq, Kq, Ql, Klt, (void*)S, P, A, Y, O,
                     (void*)Of, (void*)ra, (void*)rb, (void*)rw, dx, dO, (void*)dP, dKq, dV, dKl, (void*)du,
-                    (void*)dz, (void*)dy})
+                    (void*)dz, dy})
         free(p);
 }
 
@@ -145,6 +145,8 @@ int main(int argc, char** argv) {
         {1, 64, 128, 256, 128, 64, true, true},     {1, 64, 128, 256, 128, 64, false, false},
         {1, 256, 128, 1024, 128, 64, false, true},  {1, 512, 256, 1024, 256, 128, true, true},
         {1, 320, 128, 1024, 256, 64, false, false}, {2, 256, 128, 1280, 128, 128, true, true},
+        // batches that decode on the MFMA core (one ragged and two token tiles)
+        {17, 64, 128, 256, 128, 64, true, true},     {70, 64, 128, 512, 256, 64, false, true},
     };
     std::vector<Cfg> full = {
         {8, 1024, 768, 1536, 128, 256, true, true}, {4, 4096, 768, 1536, 128, 256, true, true},

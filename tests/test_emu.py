@@ -128,12 +128,12 @@ def test_emulated_kernels_match_oracle(emu, case, late):
         assert err <= tol, f"{name}: {err:.3e} > {tol}"
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_emulated_decoding_matches_the_causal_layer(emu, dtype):
-    """gau_decode_step on the emulation for 70 tokens (one chunk end, C = 64)
-    against the oracle's causal layer."""
-    B, T, d, e, s, C = 2, 128, 128, 256, 128, 64
-    steps = 70
+@pytest.mark.parametrize("dtype,B", [("f32", 2), ("bf16", 2), ("bf16", 18)])
+def test_emulated_decoding_matches_the_causal_layer(emu, dtype, B):
+    """gau_decode_step on the emulation for 66 tokens (one chunk end, C = 64)
+    against the oracle's causal layer; B = 18 takes the MFMA products (from B = 3 on)."""
+    T, d, e, s, C = 128, 128, 256, 128, 64
+    steps = 66
     bf = dtype == "bf16"
     emu.emu_set_mode(1, 1)
     P = ctypes.c_void_p

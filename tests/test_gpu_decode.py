@@ -42,6 +42,8 @@ CASES = [
     (1, 256, 128, 1024, 256, 128, "bf16", 256, True),  # s = 256, RoPE
     (3, 192, 128, 256, 128, 64, "bf16", 130, False),   # stop inside a chunk
     (9, 128, 128, 256, 128, 64, "f32", 128, True),     # B > 8: two token tiles per weight row
+    (20, 128, 128, 256, 128, 64, "bf16", 128, False),  # B >= 3: the products on the MFMA core
+    (70, 128, 256, 512, 256, 64, "f32", 70, True),     # ... two token tiles, the second ragged
 ]
 
 
