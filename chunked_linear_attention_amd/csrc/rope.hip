@@ -16,10 +16,12 @@
 // w[n-1 + d] = a . rope(b, d) carries it, and the layer takes it as its
 // relpos argument unchanged.
 //
-// Angles are formed and turned in fp64 (t * theta_i reaches about 10^4 rad at
-// the sequence lengths here, where fp32 would lose 4 decimal digits of the
-// angle); the heads are read and written in the layer's element type.
-// Memory-bound elementwise passes: 16-byte-aligned 4-element vectors.
+// Angles t * theta_i reach about 10^4 rad at the sequence lengths here, where
+// an fp32 product would lose 4 decimal digits: they are formed in fp64 and
+// reduced to [-pi, pi] there, and only the reduced angle's cosine and sine
+// are fp32.  The heads are read and written in the layer's element type: two
+// memory-bound passes, one over the three token-major heads and one over
+// K_lin_t, each with coalesced 4-element vectors.
 #include "gau_device.h"
 #include "gau_launch.h"
 
@@ -63,12 +65,28 @@ __device__ __forceinline__ void turn(double (&lo)[4], double (&hi)[4], const dou
     }
 }
 
+// cos and sin of t * theta: the angle formed in fp64 and reduced to
+// [-pi, pi] there, the reduced angle's cosine and sine in fp32 (about 1 ulp).
+__device__ __forceinline__ void turn_cs(double t, double theta, double& c, double& s) {
+    constexpr double kTwoPi = 6.283185307179586476925287;
+    const double a = t * theta;
+    const float r = (float)(a - kTwoPi * rint(a / kTwoPi));
+    float sf, cf;
+    sincosf(r, &sf, &cf);
+    c = cf;
+    s = sf;
+}
+
 // Token-major heads Q_quad, K_quad, Q_lin [M, s]: one thread per token and
-// four consecutive pair indices i0 .. i0+3.
+// four consecutive pair indices i0 .. i0+3 (consecutive threads along the
+// row).  The block's pair frequencies come from an LDS table (fp64).
 template <typename T>
 __global__ __launch_bounds__(256) void rope_rows_kernel(RopeParams p) {
     constexpr int EB = Elem<T>::kBytes;
+    __shared__ double theta[128];
     const int half = p.s / 2;
+    for (int i = threadIdx.x; i < half; i += 256) theta[i] = rope_theta(i, half);
+    __syncthreads();
     const int groups = half / 4;
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (long)p.M * groups) return;
@@ -77,7 +95,7 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(RopeParams p) {
     const double t = (double)(m % p.T);
     double c[4], s[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sincos(t * rope_theta(i0 + k, half), &s[k], &c[k]);
+    for (int k = 0; k < 4; ++k) turn_cs(t, theta[i0 + k], c[k], s[k]);
     void* heads[3] = {p.Qq, p.Kq, p.Ql};
 #pragma unroll
     for (int h = 0; h < 3; ++h) {
@@ -92,7 +110,7 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(RopeParams p) {
 }
 
 // K_lin_t [B, s, T]: one thread per sequence, pair index i and four
-// consecutive tokens t0 .. t0+3.
+// consecutive tokens t0 .. t0+3 (consecutive threads along the tokens).
 template <typename T>
 __global__ __launch_bounds__(256) void rope_cols_kernel(RopeParams p) {
     constexpr int EB = Elem<T>::kBytes;
@@ -104,10 +122,10 @@ __global__ __launch_bounds__(256) void rope_cols_kernel(RopeParams p) {
     const long r = idx - (long)b * half * tg;
     const int i = (int)(r / tg);
     const int t0 = (int)(r - (long)i * tg) * 4;
-    const double th = rope_theta(i, half);
+    const double th = rope_theta(i, half);  // uniform over most of the block
     double c[4], s[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sincos((double)(t0 + k) * th, &s[k], &c[k]);
+    for (int k = 0; k < 4; ++k) turn_cs((double)(t0 + k), th, c[k], s[k]);
     char* base = (char*)p.Klt + ((size_t)b * p.s * p.T + t0) * EB;
     char* lo_p = base + (size_t)i * p.T * EB;
     char* hi_p = base + (size_t)(i + half) * p.T * EB;
