@@ -181,7 +181,8 @@ def heads(Z, gamma, beta):
 
 
 def flash_forward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
-                  quad_scale=None, lin_scale=None, return_intermediates=False, use_rope=False):
+                  quad_scale=None, lin_scale=None, return_intermediates=False, use_rope=False,
+                  parts="both"):
     """Forward pass of one FLASH layer (GAU with mixed chunk attention).
 
     X: (B, T, d).  W_u, W_v: (d, e).  W_z: (d, s).  W_o: (e, d).
@@ -189,6 +190,10 @@ def flash_forward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
     quad_scale / lin_scale default to 1/C (the listing's reading).
     use_rope rotates the four heads by their position in the sequence (0 ..
     T-1, not restarted per chunk: wikillm, FLASH block pseudocode).
+    parts = "local" keeps only the quadratic in-chunk term and "global" only
+    the linear cross-chunk term (the LocalOnly / GlobalOnly ablation
+    variants: wikillm, "Ablation variants"; Su's post reports both fall well
+    short of the full model).
 
     Steps, in the order of the FLASH block (wikillm pseudocode; blog "Mixed
     Chunking"; papercache 3.2):
@@ -243,6 +248,12 @@ def flash_forward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
 
     # step 6: linear term, gate, output projection
     lin = Qlg @ P
+    if parts == "local":
+        lin = np.zeros_like(lin)
+    elif parts == "global":
+        quad = np.zeros_like(quad)
+    elif parts != "both":
+        raise ValueError("parts must be 'both', 'local' or 'global'")
     Y = Ug * (quad + lin)
     O = (Y.reshape(B, T, e)) @ _as64(W_o)
     if not return_intermediates:

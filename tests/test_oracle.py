@@ -384,3 +384,26 @@ def test_decoding_a_ragged_prefix_matches_the_layer_prefix():
     got = orc.flash_decode(p["X"][:, :7], p["W_u"], p["W_v"], p["W_z"], p["W_o"], p["gamma"], p["beta"],
                            p["relpos"], 4)
     np.testing.assert_allclose(got, full[:, :7], rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_parts_local_and_global_match_the_ablation_by_weights(causal):
+    """parts="local" equals the layer whose Q_lin head is zero, and
+    parts="global" the layer whose Q_quad head is zero with a negative bias
+    (relu clips every score): the ablations expressed through the inputs."""
+    C = 4
+    p = _tiny(2, 12, 5, 6, 4, C, seed=38)
+    loc = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in p.items()}
+    loc["gamma"][2] = 0.0
+    loc["beta"][2] = 0.0
+    np.testing.assert_allclose(_run(orc.flash_forward, p, C, causal, parts="local"),
+                               _run(orc.flash_forward_bruteforce, loc, C, causal), rtol=1e-11, atol=1e-12)
+    glo = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in p.items()}
+    glo["gamma"][0] = 0.0
+    glo["beta"][0] = 0.0
+    glo["relpos"] = -np.abs(glo["relpos"]) - 0.1
+    np.testing.assert_allclose(_run(orc.flash_forward, p, C, causal, parts="global"),
+                               _run(orc.flash_forward_bruteforce, glo, C, causal), rtol=1e-11, atol=1e-12)
+    full = _run(orc.flash_forward, p, C, causal)
+    both = _run(orc.flash_forward, p, C, causal, parts="local") + _run(orc.flash_forward, p, C, causal, parts="global")
+    np.testing.assert_allclose(both, full, rtol=1e-11, atol=1e-12)   # the output is linear in (quad + lin)
