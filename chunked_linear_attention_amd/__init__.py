@@ -11,7 +11,7 @@ import numpy as np
 
 from . import inputs  # noqa: F401
 from ._lib import (  # noqa: F401
-    GAU_BF16, GAU_F32, STAGE_ATTN, STAGE_OUT, STAGE_PROJ, STAGE_SCAN, STAGE_SCORES, STAGE_STATE, EXPORTS,
+    GAU_BF16, GAU_F32, GAU_FULL, GAU_GLOBAL_ONLY, GAU_LOCAL_ONLY, STAGE_ATTN, STAGE_OUT, STAGE_PROJ, STAGE_SCAN, STAGE_SCORES, STAGE_STATE, EXPORTS,
     GauError, decode_reset, decode_step, decode_workspace_bytes, forward, forward_stages, load, make_config,
     rope_relpos, stack_forward, stack_workspace_bytes,
     status_string, workspace_bytes, workspace_layout,
@@ -50,7 +50,8 @@ def device_layer(inp, dtype, device="cuda"):
 
 
 def gau_forward(X, W_u, W_v, W_z, W_o, scale, offset, relpos, C, causal,
-                quad_scale=None, lin_scale=None, out=None, workspace=None, stream=None, rope=False):
+                quad_scale=None, lin_scale=None, out=None, workspace=None, stream=None, rope=False,
+                parts="both"):
     """O = FLASH layer forward of X [B, T, d] (weights output-major).
 
     Allocates O and the workspace with torch.empty when not given; all
@@ -61,7 +62,7 @@ def gau_forward(X, W_u, W_v, W_z, W_o, scale, offset, relpos, C, causal,
     e = W_u.shape[0]
     s = W_z.shape[0]
     dt = GAU_BF16 if X.dtype == torch.bfloat16 else GAU_F32
-    cfg = make_config(B, T, d, e, s, C, causal, dt, quad_scale, lin_scale, rope)
+    cfg = make_config(B, T, d, e, s, C, causal, dt, quad_scale, lin_scale, rope, parts)
     if out is None:
         out = torch.empty_like(X)
     if workspace is None:

@@ -35,7 +35,12 @@ class GauConfig(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("d", ctypes.c_int64),
                 ("e", ctypes.c_int64), ("s", ctypes.c_int64), ("C", ctypes.c_int64),
                 ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("quad_scale", ctypes.c_float), ("lin_scale", ctypes.c_float), ("rope", ctypes.c_int32)]
+                ("quad_scale", ctypes.c_float), ("lin_scale", ctypes.c_float), ("rope", ctypes.c_int32),
+                ("ablation", ctypes.c_int32)]
+
+# gau_config.ablation values
+GAU_FULL, GAU_LOCAL_ONLY, GAU_GLOBAL_ONLY = 0, 1, 2
+_PARTS = {"both": GAU_FULL, "local": GAU_LOCAL_ONLY, "global": GAU_GLOBAL_ONLY}
 
 
 class GauWsLayout(ctypes.Structure):
@@ -91,12 +96,13 @@ def load():
     return lib
 
 
-def make_config(B, T, d, e, s, C, causal, dtype, quad_scale=None, lin_scale=None, rope=False):
+def make_config(B, T, d, e, s, C, causal, dtype, quad_scale=None, lin_scale=None, rope=False, parts="both"):
     """gau_config; quad_scale / lin_scale default to 1/C (the listing's reading);
-    rope rotates the four heads by position."""
+    rope rotates the four heads by position; parts "local" / "global" keeps
+    only that term (the LocalOnly / GlobalOnly variants)."""
     return GauConfig(B, T, d, e, s, C, 1 if causal else 0, dtype,
                      (1.0 / C) if quad_scale is None else float(quad_scale),
-                     (1.0 / C) if lin_scale is None else float(lin_scale), 1 if rope else 0)
+                     (1.0 / C) if lin_scale is None else float(lin_scale), 1 if rope else 0, _PARTS[parts])
 
 
 def workspace_bytes(cfg):

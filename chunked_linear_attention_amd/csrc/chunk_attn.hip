@@ -67,10 +67,11 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void chunk_attn_kernel(AttnParam
     const size_t pidx = p.causal ? (size_t)chunk : (size_t)b;
 
     const KSeg a0{(const char*)p.Vt + (((size_t)b * p.e + f0) * p.T + (size_t)g * p.C) * EB, (size_t)p.T * EB,
-                  keys / KELEMS};
-    const KSeg a1{(const char*)p.P + (pidx * p.e + f0) * p.s * EB, (size_t)p.s * EB, p.s / KELEMS};
-    const KSeg b0{(const char*)p.A + ((size_t)chunk * p.C + q0) * p.C * EB, (size_t)p.C * EB, keys / KELEMS};
-    const KSeg b1{(const char*)p.Ql + (tok0 + q0) * p.s * EB, (size_t)p.s * EB, p.s / KELEMS};
+                  p.local ? keys / KELEMS : 0};
+    const KSeg a1{(const char*)p.P + (pidx * p.e + f0) * p.s * EB, (size_t)p.s * EB, p.global ? p.s / KELEMS : 0};
+    const KSeg b0{(const char*)p.A + ((size_t)chunk * p.C + q0) * p.C * EB, (size_t)p.C * EB,
+                  p.local ? keys / KELEMS : 0};
+    const KSeg b1{(const char*)p.Ql + (tok0 + q0) * p.s * EB, (size_t)p.s * EB, p.global ? p.s / KELEMS : 0};
 
     // gate: acc rows are features f0 + row, columns are queries q0 + col; the
     // four rows a lane holds are four consecutive features of one token of U

@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
     __syncthreads();
     // scores of the chunk's slots 0 .. j (slot j from this block's own K_quad):
     // one thread per slot, its K_quad row read as 16-byte vectors all in flight
-    for (int tau = tid; tau <= j; tau += 256) {
+    for (int tau = tid; tau <= (p.local ? j : -1); tau += 256) {
         float acc = 0.f;
         if (tau == j) {
             for (int i = 0; i < p.s; ++i) acc += qq[i] * kq[i];
@@ -243,17 +243,18 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
     if (f < p.e) {
         const char* V = (const char*)p.V + ((size_t)b * p.C * p.e + f) * EB;
         const size_t vs = (size_t)p.e * EB;
+        const int jl = p.local ? j : -1;  // last slot of the local term
         int tau = g;
-        for (; tau + 28 <= j; tau += 32) {  // eight independent loads in flight
+        for (; tau + 28 <= jl; tau += 32) {  // eight independent loads in flight
             float v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = ld1<T>(V + (size_t)(tau + 4 * u) * vs);
 #pragma unroll
             for (int u = 0; u < 8; ++u) quad += alpha[tau + 4 * u] * v[u];
         }
-        for (; tau <= j; tau += 4) quad += alpha[tau] * ld1<T>(V + (size_t)tau * vs);
+        for (; tau <= jl; tau += 4) quad += alpha[tau] * ld1<T>(V + (size_t)tau * vs);
         const float* P = p.P + (size_t)b * p.s * p.e + f;
-        for (int i = g; i < p.s; i += 32) {  // s is a multiple of 128
+        for (int i = g; i < (p.global ? p.s : 0); i += 32) {  // s is a multiple of 128
             float w[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) w[u] = P[(size_t)(i + 4 * u) * p.e];
@@ -421,7 +422,7 @@ hipError_t step(const DecodeParams& p, hipStream_t st) {
         hipLaunchKernelGGL(decode_out_kernel<T>, dim3((unsigned)((p.d + 7) / 8)), dim3(256), 0, st, p);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (p.j == p.C - 1) {
+    if (p.j == p.C - 1 && p.global) {
         hipLaunchKernelGGL(decode_state_kernel<T>, dim3((unsigned)(p.B * (p.s / 64) * ((p.e + 63) / 64))), dim3(256),
                            0, st, p);
         e = hipGetLastError();

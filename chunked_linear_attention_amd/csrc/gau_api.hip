@@ -26,6 +26,8 @@ gau_status check_config(const gau_config* c) {
     if (c->e <= 0 || c->e % 256 != 0) return GAU_ERR_SHAPE;
     if (!(c->s == 128 || c->s == 256)) return GAU_ERR_SHAPE;
     if (c->rope != 0 && c->rope != 1) return GAU_ERR_SHAPE;
+    if (c->ablation != GAU_FULL && c->ablation != GAU_LOCAL_ONLY && c->ablation != GAU_GLOBAL_ONLY)
+        return GAU_ERR_SHAPE;
     // 32-bit index arithmetic inside the kernels
     const int64_t M = c->B * c->T;
     if (M > (int64_t)1 << 30 || c->d > 65536 || c->e > 65536) return GAU_ERR_SHAPE;
@@ -112,6 +114,7 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
     const bool bf = c->dtype == GAU_BF16;
     const int M = (int)(c->B * c->T);
     const int G = (int)(c->T / c->C);
+    const bool local = c->ablation != GAU_GLOBAL_ONLY, global = c->ablation != GAU_LOCAL_ONLY;
     for (int stage = first; stage <= last; ++stage) {
         hipError_t e = hipSuccess;
         switch (stage) {
@@ -128,10 +131,11 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
                 break;
             }
             case GAU_STAGE_STATE: {
-                e = gau::launch_chunk_state(state_params(c, L, ws), bf, st);
+                if (global) e = gau::launch_chunk_state(state_params(c, L, ws), bf, st);
                 break;
             }
             case GAU_STAGE_SCAN: {
+                if (!global) break;
                 gau::ScanParams p{ws + L.S, ws + L.P, (int)c->B, G, (int)(c->e * c->s),
                                   c->causal ? 1 : 0};
                 e = gau::launch_chunk_scan(p, bf, st);
@@ -140,17 +144,18 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
             case GAU_STAGE_SCORES: {
                 const gau::ScoresParams p{ws + L.Q_quad, ws + L.K_quad, a.relpos, ws + L.A, (int)c->B, (int)c->T,
                                           (int)c->s, (int)c->C, c->causal ? 1 : 0, c->quad_scale};
-                if (last >= GAU_STAGE_STATE) {  // both: one launch, the state stage is done with it
+                if (last >= GAU_STAGE_STATE && local && global) {  // one launch, the state stage done with it
                     e = gau::launch_chunk_scores_state(p, state_params(c, L, ws), bf, st);
                     ++stage;
-                } else {
+                } else if (local) {
                     e = gau::launch_chunk_scores(p, bf, st);
                 }
                 break;
             }
             case GAU_STAGE_ATTN: {
                 gau::AttnParams p{ws + L.A, ws + L.Q_lin, ws + L.Vt, ws + L.P, ws + L.U, ws + L.Y, (int)c->B,
-                                  (int)c->T, (int)c->e, (int)c->s, (int)c->C, c->causal ? 1 : 0};
+                                  (int)c->T, (int)c->e, (int)c->s, (int)c->C, c->causal ? 1 : 0,
+                                  local ? 1 : 0, global ? 1 : 0};
                 e = gau::launch_chunk_attn(p, bf, st);
                 break;
             }
@@ -287,7 +292,8 @@ gau_status gau_decode_step(const gau_config* cfg, int64_t t, const void* x, cons
     const gau::DecodeParams p{x, W_u, W_v, W_z, W_o, scale, offset, relpos, o,
                               (float*)(ws + D.P), ws + D.Kq, ws + D.V, ws + D.Kl,
                               (float*)(ws + D.u), (float*)(ws + D.z), ws + D.y, (int)cfg->B, (int)cfg->d, (int)cfg->e, (int)cfg->s, (int)cfg->C,
-                              (int)t, (int)(t % cfg->C), cfg->rope, cfg->quad_scale, cfg->lin_scale};
+                              (int)t, (int)(t % cfg->C), cfg->rope, cfg->quad_scale, cfg->lin_scale,
+                              cfg->ablation != GAU_GLOBAL_ONLY, cfg->ablation != GAU_LOCAL_ONLY};
     if (gau::launch_decode_step(p, cfg->dtype == GAU_BF16, (hipStream_t)stream) != hipSuccess) return GAU_ERR_HIP;
     return GAU_OK;
 }

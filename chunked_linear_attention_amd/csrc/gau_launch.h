@@ -65,6 +65,7 @@ struct AttnParams {
     void* Y;          // [M, e]
     int B, T, e, s, C;
     int causal;
+    int local, global;  // which terms enter Y (the LocalOnly / GlobalOnly variants)
 };
 
 // Output projection O = Y W_o (optionally O = residual + Y W_o in fp32).
@@ -115,6 +116,7 @@ struct DecodeParams {
     void* y;            // [B, e] element type scratch (the gated attention output)
     int B, d, e, s, C, t, j, rope;
     float qs, ls;
+    int local, global;  // which terms enter y (the LocalOnly / GlobalOnly variants)
 };
 
 hipError_t launch_decode_step(const DecodeParams& p, bool bf16_storage, hipStream_t st);

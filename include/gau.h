@@ -92,7 +92,13 @@ typedef struct {
     float lin_scale;     /* multiplies every chunk summary K_lin^T V             */
     int32_t rope;        /* 1: rotate the four heads by position (see above);
                             0: no rotation; anything else is GAU_ERR_SHAPE      */
+    int32_t ablation;    /* GAU_FULL (0): the layer as above; GAU_LOCAL_ONLY:
+                            V_lin = 0; GAU_GLOBAL_ONLY: V_quad = 0 (the
+                            LocalOnly / GlobalOnly variants, wikillm "Ablation
+                            variants"); anything else is GAU_ERR_SHAPE          */
 } gau_config;
+
+enum { GAU_FULL = 0, GAU_LOCAL_ONLY = 1, GAU_GLOBAL_ONLY = 2 };
 
 /*
  * Byte offsets, inside the workspace, of the intermediates gau_forward leaves
@@ -157,6 +163,8 @@ gau_status gau_forward(const gau_config* cfg,
  *   GAU_STAGE_SCAN   P_g = exclusive prefix over chunks (causal, eq. 8) or total (eq. 7)
  *   GAU_STAGE_ATTN   Y = U * (A_g V_g + Q_lin P_g) per chunk (wikillm "Method" steps 2-4)
  *   GAU_STAGE_OUT    O = Y W_o
+ * With GAU_LOCAL_ONLY the state and scan stages queue nothing (P is not
+ * read); with GAU_GLOBAL_ONLY the scores stage queues nothing (A is not read).
  * Arguments, checks and status codes as gau_forward (every pointer is
  * checked, also those the selected stages do not read).  A stage reads the
  * workspace regions earlier stages wrote, so a range that does not start at

@@ -20,12 +20,13 @@ def torch_dtype(dtype):
     return torch.bfloat16 if dtype == "bf16" else torch.float32
 
 
-def run_layer(inp, B, T, d, e, s, C, causal, dtype, quad_scale=None, lin_scale=None, stream=None, rope=False):
+def run_layer(inp, B, T, d, e, s, C, causal, dtype, quad_scale=None, lin_scale=None, stream=None, rope=False,
+              parts="both"):
     """Forward on the GPU; returns (O as float64 numpy, workspace tensor, cfg, layout)."""
     tdt = torch_dtype(dtype)
     dev = g.device_layer(inp, tdt)
     cfg = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32,
-                        quad_scale, lin_scale, rope)
+                        quad_scale, lin_scale, rope, parts)
     ws = torch.zeros(g.workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
     O = torch.empty((B, T, d), dtype=tdt, device="cuda")
     g.forward(cfg, dev["X"], dev["W_u"], dev["W_v"], dev["W_z"], dev["W_o"], dev["scale"],
@@ -43,10 +44,10 @@ def ws_array(ws, layout, name, shape, dtype):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def oracle_layer(inp, C, causal, quad_scale=None, lin_scale=None, intermediates=False, rope=False):
+def oracle_layer(inp, C, causal, quad_scale=None, lin_scale=None, intermediates=False, rope=False, parts="both"):
     return orc.flash_forward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"],
                              inp["beta"], inp["relpos"], C, causal, quad_scale, lin_scale,
-                             return_intermediates=intermediates, use_rope=rope)
+                             return_intermediates=intermediates, use_rope=rope, parts=parts)
 
 
 def rel_err(got, ref):

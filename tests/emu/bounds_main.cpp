@@ -92,7 +92,7 @@ static void run(const Cfg& c, const std::string& only) {
     if (c.causal) {
         for (int pos : {0, c.C - 1}) {
             DecodeParams dp{dx, Wu, Wv, Wz, Wo, sc, of, rp, dO, dP, dKq, dV, dKl, du, dz, dy,
-                            c.B, c.d, c.e, c.s, c.C, pos, pos % c.C, 1, 1.0f / c.C, 1.0f / c.C};
+                            c.B, c.d, c.e, c.s, c.C, pos, pos % c.C, 1, 1.0f / c.C, 1.0f / c.C, 1, 1};
             t(pos == 0 ? "decode_step_j0" : "decode_step_jlast",
               [&] { CHECK(launch_decode_step(dp, c.bf, nullptr)); });
         }
@@ -105,7 +105,7 @@ static void run(const Cfg& c, const std::string& only) {
     t("chunk_scores_state", [&] { CHECK(launch_chunk_scores_state(sp, stp, c.bf, nullptr)); });
     ScanParams scp{S, P, c.B, G, c.e * c.s, c.causal ? 1 : 0};
     t("chunk_scan", [&] { CHECK(launch_chunk_scan(scp, c.bf, nullptr)); });
-    AttnParams ap{A, Ql, Vt, P, U, Y, c.B, c.T, c.e, c.s, c.C, c.causal ? 1 : 0};
+    AttnParams ap{A, Ql, Vt, P, U, Y, c.B, c.T, c.e, c.s, c.C, c.causal ? 1 : 0, 1, 1};
     t("chunk_attn", [&] { CHECK(launch_chunk_attn(ap, c.bf, nullptr)); });
     OutParams op{Y, Wo, O, nullptr, (int)M, c.d, c.e};
     t("out_gemm", [&] { CHECK(launch_out_gemm(op, c.bf, nullptr)); });

@@ -68,6 +68,15 @@ def test_bad_rope_flag_rejected():
     assert g.workspace_bytes(cfg) == g.workspace_bytes(_cfg())
 
 
+def test_bad_ablation_rejected():
+    cfg = _cfg()
+    cfg.ablation = 3
+    assert g.workspace_bytes(cfg) == 0
+    for a in (g.GAU_LOCAL_ONLY, g.GAU_GLOBAL_ONLY):
+        cfg.ablation = a
+        assert g.workspace_bytes(cfg) == g.workspace_bytes(_cfg())
+
+
 def test_rope_relpos_argument_checks_without_gpu():
     lib = g.load()
     P = ctypes.c_void_p

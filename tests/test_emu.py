@@ -70,6 +70,8 @@ CASES = [
     (1, 256, 128, 1024, 256, 128, "bf16", False),   # Z formed inside the U tiles (s = 256)
     (1, 256, 128, 256, 128, 64, "f32", True, True),   # heads rotated by position (RoPE)
     (1, 256, 128, 1024, 256, 128, "bf16", True, True),
+    (1, 256, 128, 256, 128, 64, "f32", True, False, "local"),     # LocalOnly / GlobalOnly variants
+    (1, 256, 128, 1024, 256, 128, "bf16", False, False, "global"),
 ]
 
 
@@ -79,15 +81,18 @@ def _host(a, bf):
 
 
 @pytest.mark.parametrize("late", [0, 1], ids=["dma_at_issue", "dma_at_wait"])
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}{}".format(
-    *c[:7], "causal" if c[7] else "full", "_rope" if len(c) > 8 and c[8] else ""))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}{}{}".format(
+    *c[:7], "causal" if c[7] else "full", "_rope" if len(c) > 8 and c[8] else "",
+    "_" + c[9] if len(c) > 9 else ""))
 def test_emulated_kernels_match_oracle(emu, case, late):
     B, T, d, e, s, C, dtype, causal = case[:8]
     rope = len(case) > 8 and case[8]
+    parts = case[9] if len(case) > 9 else "both"
     bf = dtype == "bf16"
     emu.emu_set_mode(1, late)
     inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=B * 31 + T + C, dtype=dtype)
-    cfg = GauConfig(B, T, d, e, s, C, 1 if causal else 0, 1 if bf else 0, 1.0 / C, 1.0 / C, 1 if rope else 0)
+    cfg = GauConfig(B, T, d, e, s, C, 1 if causal else 0, 1 if bf else 0, 1.0 / C, 1.0 / C, 1 if rope else 0,
+                    {"both": 0, "local": 1, "global": 2}[parts])
     X = _host(inp["X"], bf)
     W = {k: _host(np.ascontiguousarray(inp[k].T), bf) for k in ("W_u", "W_v", "W_z", "W_o")}
     sc, of, rp = (np.ascontiguousarray(inp[k], np.float32) for k in ("gamma", "beta", "relpos"))
@@ -102,7 +107,8 @@ def test_emulated_kernels_match_oracle(emu, case, late):
     L = GauWsLayout()
     assert emu.gau_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == 0
     ref, im = orc.flash_forward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"],
-                                inp["beta"], inp["relpos"], C, causal, return_intermediates=True, use_rope=rope)
+                                inp["beta"], inp["relpos"], C, causal, return_intermediates=True, use_rope=rope,
+                                parts=parts)
     conv = inputs.bf16_bits_to_f32 if bf else (lambda a: a)
     eb = 2 if bf else 4
 
@@ -122,6 +128,8 @@ def test_emulated_kernels_match_oracle(emu, case, late):
         "Y": (region("Y", (B, T, e)), im["Y"]),
         "O": (conv(O).astype(np.float64), ref),
     }
+    if parts == "local":
+        del checks["S"]  # the state stages queue nothing
     for name, (got, want) in checks.items():
         assert np.all(np.isfinite(got)), name
         err = np.max(np.abs(got - want)) / np.max(np.abs(want))

@@ -13,10 +13,11 @@ from _gpu import assert_close, make, oracle_layer, tol_for, torch_dtype
 pytestmark = pytest.mark.gpu
 
 
-def _decode(inp, B, T, d, e, s, C, dtype, steps, rope=False, reset_twice=False):
+def _decode(inp, B, T, d, e, s, C, dtype, steps, rope=False, reset_twice=False, parts="both"):
     tdt = torch_dtype(dtype)
     dev = g.device_layer(inp, tdt)
-    cfg = g.make_config(B, T, d, e, s, C, True, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32, rope=rope)
+    cfg = g.make_config(B, T, d, e, s, C, True, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32, rope=rope,
+                        parts=parts)
     ws = torch.empty(g.decode_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
     ws.fill_(0xFF)  # the reset must clear what the state needs
     X = dev["X"]
@@ -75,3 +76,12 @@ def test_decoding_agrees_with_the_parallel_forward():
     from _gpu import run_layer
     O, *_ = run_layer(inp, B, T, d, e, s, C, True, "bf16")
     assert_close(got, O, 2e-2, "decode vs forward")
+
+
+@pytest.mark.parametrize("parts,B", [("local", 2), ("global", 2), ("global", 5)])
+def test_decoding_local_only_and_global_only(parts, B):
+    T, d, e, s, C = 192, 128, 256, 128, 64
+    inp = make(B, T, d, e, s, C, "bf16", seed=17)
+    got, = _decode(inp, B, T, d, e, s, C, "bf16", 140, parts=parts)
+    ref = oracle_layer(inp, C, True, parts=parts)[:, :140]
+    assert_close(got, ref, 2e-2, f"decoded O ({parts})")

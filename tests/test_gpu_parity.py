@@ -96,6 +96,20 @@ def test_layer_with_rope_matches_oracle(case):
     assert_close(O, ref, tol_for(dtype), "O")
 
 
+@pytest.mark.parametrize("parts", ["local", "global"])
+@pytest.mark.parametrize("case", [(2, 512, 256, 512, 128, 128, "bf16", True), (1, 256, 128, 256, 128, 64, "f32", False),
+                                  (1, 256, 128, 1024, 256, 128, "bf16", True)],
+                         ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}".format(*c[:7], "causal" if c[7] else "full"))
+def test_local_only_and_global_only_match_oracle(case, parts):
+    """The LocalOnly / GlobalOnly variants: only that term reaches Y."""
+    B, T, d, e, s, C, dtype, causal = case
+    inp = make(B, T, d, e, s, C, dtype, seed=B * 211 + T + C)
+    O, ws, cfg, L = run_layer(inp, B, T, d, e, s, C, causal, dtype, parts=parts)
+    ref, im = oracle_layer(inp, C, causal, intermediates=True, parts=parts)
+    assert_close(ws_array(ws, L, "Y", (B, T, e), dtype), im["Y"], tol_for(dtype), "Y")
+    assert_close(O, ref, tol_for(dtype), "O")
+
+
 @pytest.mark.parametrize("n", [64, 512, 1024])
 def test_rope_relpos_matches_code4_toeplitz(n):
     """The 2n-1 vector from the kernel against the oracle's Toeplitz matrix
