@@ -230,3 +230,29 @@ def test_full_size_workload(name):
         err = assert_close(O[b:b + 1], ref, 2e-2, f"{name} row {b}")
         ce = chunk_errors(O[b:b + 1], ref, C)
         print(f"{name} row {b}: global {err:.2e}, worst per-chunk {ce.max():.2e}")
+
+
+# ------------------------------------------------------------------ large sizes
+
+def test_long_sequence_checked_on_its_causal_prefix():
+    """B=1, T=131072 (512 chunks): the index arithmetic far past the benchmark
+    sizes.  Causal outputs of the first 2048 tokens depend only on those
+    tokens, so the oracle of that prefix checks them."""
+    B, T, d, e, s, C = 1, 131072, 768, 1536, 128, 256
+    inp = make(B, T, d, e, s, C, "bf16", seed=77)
+    O, *_ = run_layer(inp, B, T, d, e, s, C, True, "bf16")
+    assert np.all(np.isfinite(O))
+    P = 2048
+    ref = oracle_layer(dict(inp, X=inp["X"][:, :P]), C, True)
+    assert_close(O[:, :P], ref, 2e-2, "prefix of T=131072")
+
+
+def test_many_sequences_checked_on_first_and_last_rows():
+    """B=64, T=1024: 65536 tokens in 64 independent rows; rows 0 and 63
+    against the oracle."""
+    B, T, d, e, s, C = 64, 1024, 768, 1536, 128, 256
+    inp = make(B, T, d, e, s, C, "bf16", seed=78)
+    O, *_ = run_layer(inp, B, T, d, e, s, C, True, "bf16")
+    for b in (0, B - 1):
+        ref = oracle_layer(dict(inp, X=inp["X"][b:b + 1]), C, True)
+        assert_close(O[b:b + 1], ref, 2e-2, f"row {b} of B=64")
