@@ -335,6 +335,87 @@ def flash_forward_bruteforce(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, caus
 
 
 # --------------------------------------------------------------------------
+# gradients of the layer (the chain rule through the steps of flash_forward)
+# --------------------------------------------------------------------------
+
+def silu_grad(h):
+    """d SiLU(h) / dh = sigma(h) (1 + h (1 - sigma(h)))."""
+    sg = 1.0 / (1.0 + np.exp(-_as64(h)))
+    return sg * (1.0 + h * (1.0 - sg))
+
+
+def flash_backward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal, dO,
+                   quad_scale=None, lin_scale=None):
+    """Gradients of <dO, O> for O = flash_forward(...) (no RoPE, both parts):
+    a dict with X, W_u, W_v, W_z, W_o (pages' orientation), gamma, beta,
+    relpos.  The steps of flash_forward taken backwards, each product's
+    derivative written out:
+      O = Y W_o; Y = U * Wq (Wq = quad + lin); lin_g = Ql_g P_g;
+      P = exclusive (or full) sum of S_h = ls Kl_h^T V_h;
+      quad_g = A_g V_g with A_g = relu(Sc_g)^2 * mask, Sc_g = qs Qq Kq^T + Bias;
+      heads h_k = Z gamma_k + beta_k; U, V, Z = SiLU(X W).
+    """
+    X = _as64(X)
+    B, T, d = X.shape
+    G = T // C
+    if quad_scale is None:
+        quad_scale = 1.0 / C
+    if lin_scale is None:
+        lin_scale = 1.0 / C
+    W_u, W_v, W_z, W_o = map(_as64, (W_u, W_v, W_z, W_o))
+    gamma, beta, dO = _as64(gamma), _as64(beta), _as64(dO)
+    Hu, Hv, Hz = X @ W_u, X @ W_v, X @ W_z
+    U, V, Z = silu(Hu), silu(Hv), silu(Hz)
+    e, s = U.shape[-1], Z.shape[-1]
+    Qq, Kq, Ql, Kl = heads(Z, gamma, beta)
+    ch = lambda a: a.reshape(B, G, C, a.shape[-1])
+    Vg, Qqg, Kqg, Qlg, Klg = map(ch, (V, Qq, Kq, Ql, Kl))
+    mask = causal_mask(C) if causal else np.ones((C, C))
+    Sc = (Qqg @ Kqg.swapaxes(-1, -2)) * quad_scale + toeplitz_bias(relpos, C)
+    A = relu_squared(Sc) * mask
+    S = (Klg.swapaxes(-1, -2) @ Vg) * lin_scale
+    if causal:
+        incl = np.cumsum(S, axis=1)
+        P = np.concatenate([np.zeros_like(S[:, :1]), incl[:, :-1]], axis=1)
+    else:
+        P = np.broadcast_to(S.sum(axis=1, keepdims=True), S.shape)
+    Wq = (A @ Vg + Qlg @ P).reshape(B, T, e)
+    Y = U * Wq
+    # backwards
+    dY = dO @ W_o.T
+    dW_o = Y.reshape(-1, e).T @ dO.reshape(-1, d)
+    dU = dY * Wq
+    dWq = ch(dY * U)
+    dA = dWq @ Vg.swapaxes(-1, -2)
+    dV = A.swapaxes(-1, -2) @ dWq
+    dQl = dWq @ P.swapaxes(-1, -2)
+    dP = Qlg.swapaxes(-1, -2) @ dWq
+    if causal:   # S_h feeds P_g for every g > h
+        rev = np.cumsum(dP[:, ::-1], axis=1)[:, ::-1]
+        dS = np.concatenate([rev[:, 1:], np.zeros_like(dP[:, :1])], axis=1)
+    else:
+        dS = np.broadcast_to(dP.sum(axis=1, keepdims=True), dP.shape)
+    dKl = lin_scale * (Vg @ dS.swapaxes(-1, -2))
+    dV = dV + lin_scale * (Klg @ dS)
+    dSc = dA * 2.0 * np.maximum(Sc, 0.0) * mask
+    dQq = quad_scale * (dSc @ Kqg)
+    dKq = quad_scale * (dSc.swapaxes(-1, -2) @ Qqg)
+    i, j = np.meshgrid(np.arange(C), np.arange(C), indexing="ij")
+    drel = np.zeros(2 * C - 1)
+    np.add.at(drel, (C - 1 + j - i).ravel(), dSc.sum(axis=(0, 1)).ravel())
+    flat = lambda a: a.reshape(B, T, a.shape[-1])
+    dh = [flat(x) for x in (dQq, dKq, dQl, dKl)]
+    dZ = sum(dh[k] * gamma[k] for k in range(4))
+    dgamma = np.stack([(dh[k] * Z).sum(axis=(0, 1)) for k in range(4)])
+    dbeta = np.stack([dh[k].sum(axis=(0, 1)) for k in range(4)])
+    dHu, dHv, dHz = dU * silu_grad(Hu), flat(dV) * silu_grad(Hv), dZ * silu_grad(Hz)
+    dX = dHu @ W_u.T + dHv @ W_v.T + dHz @ W_z.T
+    Xf = X.reshape(-1, d)
+    return {"X": dX, "W_u": Xf.T @ dHu.reshape(-1, e), "W_v": Xf.T @ dHv.reshape(-1, e),
+            "W_z": Xf.T @ dHz.reshape(-1, s), "W_o": dW_o, "gamma": dgamma, "beta": dbeta, "relpos": drel}
+
+
+# --------------------------------------------------------------------------
 # incremental (token-by-token) causal decoding
 # --------------------------------------------------------------------------
 

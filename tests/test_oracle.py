@@ -407,3 +407,39 @@ def test_parts_local_and_global_match_the_ablation_by_weights(causal):
     full = _run(orc.flash_forward, p, C, causal)
     both = _run(orc.flash_forward, p, C, causal, parts="local") + _run(orc.flash_forward, p, C, causal, parts="global")
     np.testing.assert_allclose(both, full, rtol=1e-11, atol=1e-12)   # the output is linear in (quad + lin)
+
+
+# ---------------------------------------------------------------- gradients
+
+def test_silu_grad_matches_central_differences():
+    x = np.linspace(-12, 12, 97)
+    h = 1e-5
+    fd = (orc.silu(x + h) - orc.silu(x - h)) / (2 * h)
+    np.testing.assert_allclose(orc.silu_grad(x), fd, rtol=1e-8, atol=1e-10)
+
+
+@pytest.mark.parametrize("B,T,C", [(2, 8, 4), (1, 9, 3)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_matches_central_differences(B, T, C, causal):
+    """Every gradient of <dO, O> against central differences of the
+    brute-force forward (not the chunked one), entry by entry."""
+    p = _tiny(B, T, d=4, e=5, s=4, C=C, seed=B * 17 + T + C)
+    dO = np.random.default_rng(5).standard_normal((B, T, 4))
+    g = orc.flash_backward(p["X"], p["W_u"], p["W_v"], p["W_z"], p["W_o"], p["gamma"], p["beta"],
+                           p["relpos"], C, causal, dO, quad_scale=0.6, lin_scale=0.8)
+    h = 1e-6
+
+    def f(q):
+        return float(np.sum(dO * _run(orc.flash_forward_bruteforce, q, C, causal, quad_scale=0.6, lin_scale=0.8)))
+
+    names = {"X": "X", "W_u": "W_u", "W_v": "W_v", "W_z": "W_z", "W_o": "W_o", "gamma": "gamma",
+             "beta": "beta", "relpos": "relpos"}
+    for k, pk in names.items():
+        fd = np.zeros_like(p[pk])
+        for idx in np.ndindex(p[pk].shape):
+            up = {a: (b.copy() if isinstance(b, np.ndarray) else b) for a, b in p.items()}
+            dn = {a: (b.copy() if isinstance(b, np.ndarray) else b) for a, b in p.items()}
+            up[pk][idx] += h
+            dn[pk][idx] -= h
+            fd[idx] = (f(up) - f(dn)) / (2 * h)
+        np.testing.assert_allclose(g[k], fd, rtol=1e-5, atol=1e-6, err_msg=k)
