@@ -12,7 +12,7 @@ import numpy as np
 from . import inputs  # noqa: F401
 from ._lib import (  # noqa: F401
     GAU_BF16, GAU_F32, GAU_FULL, GAU_GLOBAL_ONLY, GAU_LOCAL_ONLY, STAGE_ATTN, STAGE_OUT, STAGE_PROJ, STAGE_SCAN, STAGE_SCORES, STAGE_STATE, EXPORTS,
-    GauError, decode_reset, decode_step, decode_workspace_bytes, forward, forward_stages, load, make_config,
+    GRAD_NAMES, GauError, backward, backward_workspace_bytes, decode_reset, decode_step, decode_workspace_bytes, forward, forward_stages, load, make_config,
     rope_relpos, stack_forward, stack_workspace_bytes,
     status_string, workspace_bytes, workspace_layout,
 )
@@ -69,3 +69,23 @@ def gau_forward(X, W_u, W_v, W_z, W_o, scale, offset, relpos, C, causal,
         workspace = torch.empty(max(workspace_bytes(cfg), 1), dtype=torch.uint8, device=X.device)
     forward(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, out, workspace, stream)
     return out
+
+
+def gau_backward(X, W_u, W_v, W_z, W_o, scale, offset, relpos, C, causal, dO,
+                 quad_scale=None, lin_scale=None, workspace=None, stream=None):
+    """Gradients of <dO, O> for O = gau_forward(X, ...): a dict of fp32 device
+    tensors keyed X, W_u, W_v, W_z, W_o (output-major, like the weights),
+    scale, offset, relpos.  Every step runs in libgau's kernels."""
+    torch = _torch()
+    B, T, d = X.shape
+    e = W_u.shape[0]
+    s = W_z.shape[0]
+    dt = GAU_BF16 if X.dtype == torch.bfloat16 else GAU_F32
+    cfg = make_config(B, T, d, e, s, C, causal, dt, quad_scale, lin_scale)
+    like = {"X": X, "W_u": W_u, "W_v": W_v, "W_z": W_z, "W_o": W_o, "scale": scale, "offset": offset,
+            "relpos": relpos}
+    grads = {k: torch.empty(like[k].shape, dtype=torch.float32, device=X.device) for k in GRAD_NAMES}
+    if workspace is None:
+        workspace = torch.empty(max(backward_workspace_bytes(cfg), 1), dtype=torch.uint8, device=X.device)
+    backward(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, dO, grads, workspace, stream)
+    return grads

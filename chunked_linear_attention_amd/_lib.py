@@ -27,7 +27,7 @@ STATUS = {
 EXPORTS = (
     "gau_workspace_bytes", "gau_workspace_layout", "gau_forward", "gau_forward_stages",
     "gau_stack_workspace_bytes", "gau_stack_forward", "gau_decode_workspace_bytes", "gau_decode_reset",
-    "gau_decode_step", "gau_rope_relpos", "gau_status_string",
+    "gau_decode_step", "gau_rope_relpos", "gau_backward_workspace_bytes", "gau_backward", "gau_status_string",
 )
 
 
@@ -90,6 +90,10 @@ def load():
     lib.gau_decode_step.restype = ctypes.c_int
     lib.gau_rope_relpos.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, P, P]
     lib.gau_rope_relpos.restype = ctypes.c_int
+    lib.gau_backward_workspace_bytes.argtypes = [cfgp]
+    lib.gau_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.gau_backward.argtypes = [cfgp] + [P] * 18 + [ctypes.c_size_t, P]
+    lib.gau_backward.restype = ctypes.c_int
     lib.gau_status_string.argtypes = [ctypes.c_int]
     lib.gau_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -258,3 +262,31 @@ def decode_step(cfg, t, x, W_u, W_v, W_z, W_o, scale, offset, relpos, o, workspa
         _ptr(relpos), _ptr(o), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if st != 0:
         raise GauError(st, "gau_decode_step")
+
+
+def backward_workspace_bytes(cfg):
+    return load().gau_backward_workspace_bytes(ctypes.byref(cfg))
+
+
+# gradient names, in the order gau_backward takes its outputs
+GRAD_NAMES = ("X", "W_u", "W_v", "W_z", "W_o", "scale", "offset", "relpos")
+
+
+def backward(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, dO, grads, workspace, stream=None):
+    """gau_backward on torch tensors: fills ``grads`` (a dict of fp32 device
+    tensors named as GRAD_NAMES; the weight gradients output-major like the
+    weights) with the gradients of <dO, O>."""
+    import torch
+    _check_layer(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, dO)
+    B, T, d, e, s, C = cfg.B, cfg.T, cfg.d, cfg.e, cfg.s, cfg.C
+    sizes = {"X": B * T * d, "W_u": e * d, "W_v": e * d, "W_z": s * d, "W_o": d * e, "scale": 4 * s,
+             "offset": 4 * s, "relpos": 2 * C - 1}
+    for k in GRAD_NAMES:
+        _check(grads[k], "d" + k, torch.float32, sizes[k])
+    _check(workspace, "workspace")
+    st = load().gau_backward(
+        ctypes.byref(cfg), _ptr(X), _ptr(W_u), _ptr(W_v), _ptr(W_z), _ptr(W_o), _ptr(scale), _ptr(offset),
+        _ptr(relpos), _ptr(dO), *[_ptr(grads[k]) for k in GRAD_NAMES], _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise GauError(st, "gau_backward")

@@ -172,6 +172,191 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
     return GAU_OK;
 }
 
+// Backward workspace: the forward's regions, then the backward's own.
+struct BwdLayout {
+    size_t H, ones, dY, dU, dWq, Yb, WoT, dOt, Yt, V, dA, dSc, dScE, dSct, At, Kqc, Qqc, Qlc;
+    size_t dQq, dKq, dQl, dKl, dWqc, dVl, dVg, Pt, dP, dSst, dS, Kl, rpart, hpart, dZ, dH, dHt, Xt, Wt, total;
+};
+
+void bwd_layout(const gau_config* c, BwdLayout* L) {
+    gau_ws_layout F;
+    layout(c, &F);
+    const size_t eb = elem_bytes(c->dtype);
+    const size_t M = (size_t)(c->B * c->T), d = c->d, e = c->e, s = c->s, C = c->C;
+    const size_t G = c->T / c->C, Z = (size_t)c->B * G, Gp = c->causal ? G : 1;
+    const size_t W3 = 2 * e + s;
+    size_t off = F.total;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    L->H = take(M * W3 * eb);
+    L->ones = take(M * e * eb);
+    L->dY = take(M * e * 4);
+    L->dU = take(M * e * 4);
+    L->dWq = take(M * e * eb);
+    L->Yb = take(M * e * eb);
+    L->WoT = take(e * d * eb);
+    L->dOt = take(d * M * eb);
+    L->Yt = take(e * M * eb);
+    L->V = take(M * e * eb);
+    L->dA = take(Z * C * C * 4);
+    L->dSc = take(Z * C * C * 4);
+    L->dScE = take(Z * C * C * eb);
+    L->dSct = take(Z * C * C * eb);
+    L->At = take(Z * C * C * eb);
+    L->Kqc = take(M * s * eb);
+    L->Qqc = take(M * s * eb);
+    L->Qlc = take(M * s * eb);
+    L->dQq = take(M * s * 4);
+    L->dKq = take(M * s * 4);
+    L->dQl = take(M * s * 4);
+    L->dKl = take(M * s * 4);
+    L->dWqc = take(M * e * eb);
+    L->dVl = take(M * e * 4);
+    L->dVg = take(M * e * 4);
+    L->Pt = take((size_t)c->B * Gp * e * s * eb);
+    L->dP = take(Z * e * s * 4);
+    L->dSst = take(Z * e * s * eb);
+    L->dS = take(Z * e * s * eb);
+    L->Kl = take(M * s * eb);
+    L->rpart = take(Z * (2 * C - 1) * 4);
+    L->hpart = take((M + 63) / 64 * 8 * s * 4);
+    L->dZ = take(M * s * 4);
+    L->dH = take(M * W3 * eb);
+    L->dHt = take(W3 * M * eb);
+    L->Xt = take(d * M * eb);
+    L->Wt = take(d * W3 * eb);
+    L->total = off;
+}
+
+gau::GemmNTParams nt(const void* A, int64_t a_bs, int a_rp, const void* B, int64_t b_bs, int b_rp, void* C,
+                     int64_t c_bs, int c_rp, int K, bool c_f32, float alpha = 1.f, int a_div = 1, int b_div = 1) {
+    return gau::GemmNTParams{A, B, C, a_bs, b_bs, c_bs, a_rp, b_rp, c_rp, a_div, b_div, K, c_f32 ? 1 : 0, alpha, 0, 0};
+}
+
+gau::TransposeParams tp(const void* in, int64_t in_bs, int in_rp, void* out, int64_t out_bs, int out_rp) {
+    return gau::TransposeParams{in, out, in_bs, out_bs, in_rp, out_rp, 0, 0};
+}
+
+// The backward pass: recompute the forward's intermediates, then the chain
+// rule through its steps in reverse (the launch order below).
+gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO, float* dX, float* dW_u,
+                        float* dW_v, float* dW_z, float* dW_o, float* dscale, float* doffset, float* drelpos,
+                        char* ws, hipStream_t st) {
+    gau_ws_layout F;
+    layout(c, &F);
+    BwdLayout L;
+    bwd_layout(c, &L);
+    const bool bf = c->dtype == GAU_BF16;
+    const size_t eb = elem_bytes(c->dtype);
+    const int M = (int)(c->B * c->T), d = (int)c->d, e = (int)c->e, s = (int)c->s, C = (int)c->C;
+    const int T = (int)c->T, Bn = (int)c->B, G = T / C, Z = Bn * G, W3 = 2 * e + s;
+    const int64_t CC = (int64_t)C * C, Ce = (int64_t)C * e, Cs = (int64_t)C * s, es = (int64_t)e * s;
+    auto W = [&](size_t off) { return (void*)(ws + off); };
+    hipError_t err = hipSuccess;  // the first failed launch
+    auto ok = [&](hipError_t x) {
+        if (err == hipSuccess) err = x;
+    };
+    auto gemm = [&](const gau::GemmNTParams& q, int m, int n, int nb) { ok(gau::launch_gemm_nt(q, m, n, nb, bf, st)); };
+    auto trans = [&](const gau::TransposeParams& q, int r, int cc, int nb) {
+        ok(gau::launch_transpose(q, r, cc, nb, bf, st));
+    };
+
+    // forward intermediates: heads, states, prefix, weights (tiles above the
+    // causal diagonal, which the forward leaves unwritten, cleared first)
+    if (c->causal && gau::launch_fill_zero((float*)W(F.A), (size_t)Z * CC * eb / 4, st) != hipSuccess)
+        return GAU_ERR_HIP;
+    gau_status sres = run_stages(c, GAU_STAGE_PROJ, GAU_STAGE_SCAN, a, nullptr, nullptr, ws, st);
+    if (sres != GAU_OK) return sres;
+    // Wq = A V + Q_lin P: the attention stage with a gate of ones
+    ok(gau::launch_fill_one(W(L.ones), (size_t)M * e, bf, st));
+    {
+        gau::AttnParams p{W(F.A), W(F.Q_lin), W(F.Vt), W(F.P), W(L.ones), W(F.Y), Bn, T, e, s, C,
+                          c->causal ? 1 : 0, 1, 1};
+        ok(gau::launch_chunk_attn(p, bf, st));
+    }
+    // pre-activations H = X [W_u | W_v | W_z]
+    gemm(nt(a.X, 0, d, a.W_u, 0, d, W(L.H), 0, W3, d, false), M, e, 1);
+    gemm(nt(a.X, 0, d, a.W_v, 0, d, (char*)W(L.H) + e * eb, 0, W3, d, false), M, e, 1);
+    gemm(nt(a.X, 0, d, a.W_z, 0, d, (char*)W(L.H) + 2 * e * eb, 0, W3, d, false), M, s, 1);
+
+    // O = Y W_o: dY = dO W_o^T, dW_o = Y^T dO (stored [d, e]: dO^T Y)
+    trans(tp(a.W_o, 0, e, W(L.WoT), 0, d), d, e, 1);
+    gemm(nt(dO, 0, d, W(L.WoT), 0, d, W(L.dY), 0, e, d, true), M, e, 1);
+    {
+        gau::BwdElemParams p{(const float*)W(L.dY), W(F.Y), W(F.U), (float*)W(L.dU), W(L.dWq), W(L.Yb),
+                             (size_t)M * e, C, 0};
+        ok(gau::launch_gate_bwd(p, bf, st));
+    }
+    trans(tp(dO, 0, d, W(L.dOt), 0, M), M, d, 1);
+    trans(tp(W(L.Yb), 0, e, W(L.Yt), 0, M), M, e, 1);
+    gemm(nt(W(L.dOt), 0, M, W(L.Yt), 0, M, dW_o, 0, e, M, true), d, e, 1);
+
+    // token-major V and K_lin; chunk-transposed heads, weights and dWq
+    trans(tp(W(F.Vt), (int64_t)e * T, T, W(L.V), (int64_t)T * e, e), e, T, Bn);
+    trans(tp(W(F.K_lin_t), (int64_t)s * T, T, W(L.Kl), (int64_t)T * s, s), s, T, Bn);
+    trans(tp(W(F.K_quad), Cs, s, W(L.Kqc), Cs, C), C, s, Z);
+    trans(tp(W(F.Q_quad), Cs, s, W(L.Qqc), Cs, C), C, s, Z);
+    trans(tp(W(F.Q_lin), Cs, s, W(L.Qlc), Cs, C), C, s, Z);
+    trans(tp(W(F.A), CC, C, W(L.At), CC, C), C, C, Z);
+    trans(tp(W(L.dWq), Ce, e, W(L.dWqc), Ce, C), C, e, Z);
+
+    // local part: dA = dWq V^T, dSc = dA * 2 relu(Sc) * mask, dV_local = A^T dWq,
+    // dQ_quad = qs dSc K_quad, dK_quad = qs dSc^T Q_quad, dBias
+    gemm(nt(W(L.dWq), Ce, e, W(L.V), Ce, e, W(L.dA), CC, C, e, true), C, C, Z);
+    {
+        gau::BwdElemParams p{(const float*)W(L.dA), W(F.A), nullptr, (float*)W(L.dSc), W(L.dScE), nullptr,
+                             (size_t)Z * CC, C, c->causal ? 1 : 0};
+        ok(gau::launch_scores_bwd(p, bf, st));
+    }
+    ok(gau::launch_relpos_bwd((const float*)W(L.dSc), (float*)W(L.rpart), drelpos, Z, C, st));
+    trans(tp(W(L.dScE), CC, C, W(L.dSct), CC, C), C, C, Z);
+    gemm(nt(W(L.dScE), CC, C, W(L.Kqc), Cs, C, W(L.dQq), Cs, s, C, true, c->quad_scale), C, s, Z);
+    gemm(nt(W(L.dSct), CC, C, W(L.Qqc), Cs, C, W(L.dKq), Cs, s, C, true, c->quad_scale), C, s, Z);
+    gemm(nt(W(L.At), CC, C, W(L.dWqc), Ce, C, W(L.dVl), Ce, e, C, true), C, e, Z);
+
+    // global part: dQ_lin = dWq P^T, dP = Q_lin^T dWq (per chunk, stored [e, s]),
+    // dS = reverse exclusive sum of dP (total when non-causal),
+    // dV_global = ls K_lin dS, dK_lin = ls V dS^T
+    const int Gp = c->causal ? G : 1;
+    trans(tp(W(F.P), es, s, W(L.Pt), es, e), e, s, Bn * Gp);
+    gemm(nt(W(L.dWq), Ce, e, W(L.Pt), es, e, W(L.dQl), Cs, s, e, true, 1.f, 1, c->causal ? 1 : G), C, s, Z);
+    gemm(nt(W(L.dWqc), Ce, C, W(L.Qlc), Cs, C, W(L.dP), es, s, C, true), e, s, Z);
+    {
+        gau::BwdScanParams p{(const float*)W(L.dP), W(L.dSst), Bn, G, (int)es, c->causal ? 1 : 0};
+        ok(gau::launch_scan_bwd(p, bf, st));
+    }
+    trans(tp(W(L.dSst), es, s, W(L.dS), es, e), e, s, Z);
+    gemm(nt(W(L.Kl), Cs, s, W(L.dSst), es, s, W(L.dVg), Ce, e, s, true, c->lin_scale), C, e, Z);
+    gemm(nt(W(L.V), Ce, e, W(L.dS), es, e, W(L.dKl), Cs, s, e, true, c->lin_scale), C, s, Z);
+
+    // heads h_k = Z gamma_k + beta_k: dZ, dgamma, dbeta
+    {
+        gau::BwdHeadsParams p{{(const float*)W(L.dQq), (const float*)W(L.dKq), (const float*)W(L.dQl),
+                               (const float*)W(L.dKl)},
+                              (char*)W(L.H) + 2 * e * eb, W3, a.scale, (float*)W(L.dZ), (float*)W(L.hpart), M, s};
+        ok(gau::launch_heads_bwd(p, dscale, doffset, bf, st));
+    }
+    // SiLU: dH = [dU | dV | dZ] * SiLU'(H); X W: dX = dH W^T, dW = X^T dH
+    {
+        gau::BwdSiluParams p{(const float*)W(L.dU), (const float*)W(L.dVl), (const float*)W(L.dVg),
+                             (const float*)W(L.dZ), W(L.H), W(L.dH), M, e, s};
+        ok(gau::launch_silu_bwd(p, bf, st));
+    }
+    trans(tp(a.W_u, 0, d, W(L.Wt), 0, W3), e, d, 1);
+    trans(tp(a.W_v, 0, d, (char*)W(L.Wt) + e * eb, 0, W3), e, d, 1);
+    trans(tp(a.W_z, 0, d, (char*)W(L.Wt) + 2 * e * eb, 0, W3), s, d, 1);
+    gemm(nt(W(L.dH), 0, W3, W(L.Wt), 0, W3, dX, 0, d, W3, true), M, d, 1);
+    trans(tp(W(L.dH), 0, W3, W(L.dHt), 0, M), M, W3, 1);
+    trans(tp(a.X, 0, d, W(L.Xt), 0, M), M, d, 1);
+    gemm(nt(W(L.dHt), 0, M, W(L.Xt), 0, M, dW_u, 0, d, M, true), e, d, 1);
+    gemm(nt((char*)W(L.dHt) + (size_t)e * M * eb, 0, M, W(L.Xt), 0, M, dW_v, 0, d, M, true), e, d, 1);
+    gemm(nt((char*)W(L.dHt) + (size_t)2 * e * M * eb, 0, M, W(L.Xt), 0, M, dW_z, 0, d, M, true), s, d, 1);
+    return err == hipSuccess ? GAU_OK : GAU_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,6 +434,52 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X, cons
         if ((s = run_stages(cfg, GAU_STAGE_PROJ, GAU_STAGE_OUT, a, X, X, ws, st)) != GAU_OK) return s;
     }
     return GAU_OK;
+}
+
+// What gau_backward takes beyond check_config: the plain layer, and at most
+// 2^38 pre-activation entries (one-dimensional grids of 256-thread blocks).
+gau_status check_backward(const gau_config* c) {
+    gau_status s = check_config(c);
+    if (s != GAU_OK) return s;
+    if (c->rope || c->ablation != GAU_FULL) return GAU_ERR_SHAPE;
+    if (c->B * c->T * (2 * c->e + c->s) > ((int64_t)1 << 38)) return GAU_ERR_SHAPE;
+    return GAU_OK;
+}
+
+size_t gau_backward_workspace_bytes(const gau_config* cfg) {
+    if (check_backward(cfg) != GAU_OK) return 0;
+    BwdLayout L;
+    bwd_layout(cfg, &L);
+    return L.total;
+}
+
+gau_status gau_backward(const gau_config* cfg, const void* X, const void* W_u, const void* W_v, const void* W_z,
+                        const void* W_o, const float* scale, const float* offset, const float* relpos,
+                        const void* dO, float* dX, float* dW_u, float* dW_v, float* dW_z, float* dW_o,
+                        float* dscale, float* doffset, float* drelpos, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    gau_status s = check_backward(cfg);
+    if (s != GAU_OK) return s;
+    float* outs[] = {dW_u, dW_v, dW_z, dW_o, dscale, doffset, drelpos};
+    for (float* q : outs)
+        if (!q) return GAU_ERR_NULL;
+    for (float* q : outs)
+        if (!aligned16(q)) return GAU_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    if (cfg->B * cfg->T == 0) {  // no tokens: every parameter gradient is zero
+        const size_t n[] = {(size_t)(cfg->e * cfg->d), (size_t)(cfg->e * cfg->d), (size_t)(cfg->s * cfg->d),
+                            (size_t)(cfg->d * cfg->e), (size_t)(4 * cfg->s), (size_t)(4 * cfg->s),
+                            (size_t)(2 * cfg->C - 1)};
+        for (int i = 0; i < 7; ++i)
+            if (gau::launch_fill_zero(outs[i], n[i], st) != hipSuccess) return GAU_ERR_HIP;
+        return GAU_OK;
+    }
+    const LayerPtrs a{X, W_u, W_v, W_z, W_o, scale, offset, relpos};
+    if ((s = check_layer_ptrs(a)) != GAU_OK) return s;
+    if (!dO || !dX || !workspace) return GAU_ERR_NULL;
+    if (!aligned16(dO) || !aligned16(dX) || !aligned16(workspace)) return GAU_ERR_ALIGN;
+    if (workspace_bytes < gau_backward_workspace_bytes(cfg)) return GAU_ERR_WORKSPACE;
+    return run_backward(cfg, a, dO, dX, dW_u, dW_v, dW_z, dW_o, dscale, doffset, drelpos, (char*)workspace, st);
 }
 
 size_t gau_decode_workspace_bytes(const gau_config* cfg) {

@@ -133,4 +133,83 @@ hipError_t launch_chunk_attn(const AttnParams& p, bool bf16_storage, hipStream_t
 hipError_t launch_out_gemm(const OutParams& p, bool bf16_storage, hipStream_t st);
 hipError_t launch_rms_norm(const NormParams& p, bool bf16_storage, hipStream_t st);
 
+// ---- backward pass -------------------------------------------------------
+
+// Batched C[z] = alpha * A[z] B[z]^T on the MFMA core, 64 x 64 output tiles.
+// Operand z of A is at A + (z / a_div) * a_bs elements (B likewise; C at
+// z * c_bs); rows are a_rp / b_rp / c_rp elements apart; both operands are
+// K-major (K a multiple of 64, every dimension a multiple of 64).  C is fp32
+// when c_f32, else the layer's element type.
+struct GemmNTParams {
+    const void* A;
+    const void* B;
+    void* C;
+    int64_t a_bs, b_bs, c_bs;
+    int a_rp, b_rp, c_rp;
+    int a_div, b_div;
+    int K;
+    int c_f32;
+    float alpha;
+    int tm, tn;  // row / column tiles per batch entry (set by the launcher)
+};
+
+// out[z][c][r] = in[z][r][c], element type, R and Cc multiples of 64.
+struct TransposeParams {
+    const void* in;
+    void* out;
+    int64_t in_bs, out_bs;
+    int in_rp, out_rp;
+    int tr, tc;  // row / column tiles per batch entry (set by the launcher)
+};
+
+// Elementwise steps of the gate and the scores (see backward.hip).
+struct BwdElemParams {
+    const float* f1;   // fp32 input (dY, or dA)
+    const void* b;     // element type input (Wq, or A)
+    const void* c;     // element type input (U)
+    float* f0;         // fp32 output (dU, or dSc)
+    void* o0;          // element type output (dWq, or dSc)
+    void* o1;          // element type output (Y)
+    size_t n;
+    int C, causal;
+};
+
+struct BwdScanParams {
+    const float* dP;  // [B, G, es] fp32
+    void* dS;         // [B, G, es] element type
+    int B, G, es, causal;
+};
+
+struct BwdHeadsParams {
+    const float* dh[4];  // gradients of Q_quad, K_quad, Q_lin, K_lin, [M, s] fp32
+    const void* Hz;      // pre-activation of Z: row m at Hz + m * hpitch elements
+    int hpitch;
+    const float* scale;  // [4, s]
+    float* dZ;           // [M, s]
+    float* part;         // [ceil(M / 64), 8, s] per-block sums
+    int M, s;
+};
+
+struct BwdSiluParams {
+    const float* dU;   // [M, e]
+    const float* dVl;  // [M, e] local part of dV
+    const float* dVg;  // [M, e] global part of dV
+    const float* dZ;   // [M, s]
+    const void* H;     // [M, 2e + s] pre-activations
+    void* dH;          // [M, 2e + s]
+    int M, e, s;
+};
+
+hipError_t launch_gemm_nt(const GemmNTParams& q, int M, int N, int nb, bool bf16_storage, hipStream_t st);
+hipError_t launch_transpose(const TransposeParams& q, int R, int Cc, int nb, bool bf16_storage, hipStream_t st);
+hipError_t launch_fill_one(void* x, size_t n, bool bf16_storage, hipStream_t st);
+hipError_t launch_gate_bwd(const BwdElemParams& q, bool bf16_storage, hipStream_t st);
+hipError_t launch_scores_bwd(const BwdElemParams& q, bool bf16_storage, hipStream_t st);
+// drelpos[k] = sum over chunks and over entries on diagonal k - (C-1) of dsc
+hipError_t launch_relpos_bwd(const float* dsc, float* part, float* drelpos, int nchunks, int C, hipStream_t st);
+hipError_t launch_scan_bwd(const BwdScanParams& q, bool bf16_storage, hipStream_t st);
+hipError_t launch_heads_bwd(const BwdHeadsParams& q, float* dscale, float* doffset, bool bf16_storage,
+                            hipStream_t st);
+hipError_t launch_silu_bwd(const BwdSiluParams& q, bool bf16_storage, hipStream_t st);
+
 }  // namespace gau

@@ -94,6 +94,14 @@ def make_layer_inputs(B, T, d, e, s, C, seed, dtype="bf16", **_ignored):
     return out
 
 
+def make_output_grad(B, T, d, seed, dtype="bf16"):
+    """A seeded upstream gradient dL/dO [B, T, d] (standard normal, bf16-exact
+    for dtype "bf16"), float32."""
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    g = rng.standard_normal((B, T, d), dtype=np.float32)
+    return round_bf16(g) if dtype == "bf16" else g
+
+
 def make_stack_inputs(B, T, d, e, s, C, layers, weight_seed, x_seed, dtype="bf16", **_ignored):
     """Inputs of a layer stack: X (float32, the residual stream) and a list of
     per-layer weight dicts, layer l drawn from seed weight_seed + l."""

@@ -211,6 +211,49 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Gradients of the layer (training).  Given dO = dL/dO for the outputs of
+ * gau_forward(cfg, X, ...), writes dL/dX and dL/d(every parameter): the
+ * chain rule through the forward's steps (the equations at the top of this
+ * file) taken in reverse.  The intermediates are recomputed from X inside the
+ * call (nothing is kept between gau_forward and gau_backward).  The products
+ * whose derivatives it takes, per chunk:
+ *   dY = dO W_o^T, dW_o = Y^T dO;  dU = dY * (V_quad + V_lin), dWq = dY * U
+ *   dA = dWq V^T;  dSc = dA * 2 relu(Sc) * mask  (Sc the pre-activation scores)
+ *   dQ_quad = quad_scale dSc K_quad,  dK_quad = quad_scale dSc^T Q_quad,
+ *   drelpos[C-1+j-i] += dSc[i][j]
+ *   dQ_lin = dWq P^T,  dP = Q_lin^T dWq,
+ *   dS_h = sum_{g>h} dP_g (causal) or sum_g dP_g (non-causal)
+ *   dV = A^T dWq + lin_scale K_lin dS,  dK_lin = lin_scale V dS^T
+ *   dZ = sum_h gamma_h dh_h, dgamma_h = sum Z * dh_h, dbeta_h = sum dh_h
+ *   d(pre-activations) = [dU | dV | dZ] * SiLU'(X W);  dX, dW_* from X W.
+ *
+ * cfg: as gau_forward with rope = 0 and ablation = GAU_FULL (the backward of
+ *   the rotated or partial layer is not provided: GAU_ERR_SHAPE).
+ * X .. relpos: as gau_forward.   dO [B, T, d] cfg->dtype.
+ * Outputs (fp32, written, not accumulated):
+ *   dX [B, T, d];  dW_u, dW_v [e, d], dW_z [s, d], dW_o [d, e] (the layout in
+ *   which the weights are passed: output-major);  dscale, doffset [4, s];
+ *   drelpos [2C-1].
+ * workspace: at least gau_backward_workspace_bytes(cfg) bytes (device
+ *   memory; its first gau_workspace_bytes(cfg) bytes hold the forward's
+ *   intermediates, as gau_workspace_layout describes, on return).
+ * Sums over tokens run in a fixed order: the results are bitwise
+ * reproducible for a given cfg and inputs.  B * T == 0: the parameter
+ * gradients are set to zero (X, the weights, scale, offset, relpos, dO, dX and
+ * workspace are not read and may be NULL).  Checks and
+ * status codes otherwise as gau_forward; gau_backward_workspace_bytes gives 0
+ * for a cfg gau_backward rejects.
+ */
+size_t gau_backward_workspace_bytes(const gau_config* cfg);
+
+gau_status gau_backward(const gau_config* cfg, const void* X,
+                        const void* W_u, const void* W_v, const void* W_z, const void* W_o,
+                        const float* scale, const float* offset, const float* relpos, const void* dO,
+                        float* dX, float* dW_u, float* dW_v, float* dW_z, float* dW_o,
+                        float* dscale, float* doffset, float* drelpos,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Incremental causal decoding: one new token of each of the B sequences per
  * call, with a constant-size state per sequence (the chunk-level recurrence
  * of the causal layer: wikillm, "Method" steps 2-4; Su's post, "Mixed

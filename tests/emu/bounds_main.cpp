@@ -126,6 +126,31 @@ static void run(const Cfg& c, const std::string& only) {
         }
         free(ws);
     });
+    // the backward pass through the C ABI: exact-size inputs, outputs and workspace
+    if (M <= 4096) t("gau_backward", [&] {
+        gau_config cfg{c.B, c.T, c.d, c.e, c.s, c.C, c.causal ? 1 : 0, c.bf ? GAU_BF16 : GAU_F32, 1.0f / c.C,
+                       1.0f / c.C};
+        const size_t wsb = gau_backward_workspace_bytes(&cfg);
+        void* ws = buf(wsb);
+        void* gO = buf(M * c.d * eb);
+        float* gX = (float*)buf(M * c.d * 4);
+        float* gu = (float*)buf((size_t)c.e * c.d * 4);
+        float* gv = (float*)buf((size_t)c.e * c.d * 4);
+        float* gz = (float*)buf((size_t)c.s * c.d * 4);
+        float* go = (float*)buf((size_t)c.d * c.e * 4);
+        float* gs = (float*)buf(4 * c.s * 4);
+        float* gb = (float*)buf(4 * c.s * 4);
+        float* gr = (float*)buf((2 * c.C - 1) * 4);
+        int st = gau_backward(&cfg, X, Wu, Wv, Wz, Wo, sc, of, rp, gO, gX, gu, gv, gz, go, gs, gb, gr, ws, wsb,
+                              nullptr);
+        if (st != GAU_OK) {
+            fprintf(stderr, "gau_backward status %d\n", st);
+            exit(1);
+        }
+        for (void* p : {ws, gO, (void*)gX, (void*)gu, (void*)gv, (void*)gz, (void*)go, (void*)gs, (void*)gb,
+                        (void*)gr})
+            free(p);
+    });
     for (void* p : {X, Wu, Wv, Wz, Wo, (void*)sc, (void*)of, (void*)rp, U, Vt, Qq, Kq, Ql, Klt, (void*)S, P, A, Y, O,
                     (void*)Of, (void*)ra, (void*)rb, (void*)rw, dx, dO, (void*)dP, dKq, dV, dKl, (void*)du,
                     (void*)dz, dy})

@@ -35,7 +35,7 @@ CSRC = os.environ.get("EMU_CSRC", os.path.join(ROOT, "chunked_linear_attention_a
 OUT = os.environ.get("EMU_OUT", os.path.join(HERE, "_build"))
 CXX = "/opt/rocm/llvm/bin/clang++"
 UNITS = ["proj_gemm", "chunk_attn", "chunk_scan", "chunk_scores", "chunk_state", "chunk_scores_state", "out_gemm",
-         "rope", "decode", "rms_norm", "gau_api"]
+         "rope", "decode", "backward", "rms_norm", "gau_api"]
 BOUNDS = os.path.join(OUT, "emu_bounds")
 LIB = os.path.join(OUT, "libgau_emu.so")
 

@@ -110,6 +110,30 @@ def test_decode_argument_checks_without_gpu():
     assert lib.gau_decode_reset(ctypes.byref(cfg), None, ctypes.c_size_t(ws), None) == 1
 
 
+def test_backward_argument_checks_without_gpu():
+    lib = g.load()
+    cfg = _cfg()
+    ws = g.backward_workspace_bytes(cfg)
+    assert ws > g.workspace_bytes(cfg)                      # the forward's regions come first
+    assert g.backward_workspace_bytes(_cfg(rope=True)) == 0
+    assert g.backward_workspace_bytes(_cfg(parts="local")) == 0
+    assert g.backward_workspace_bytes(_cfg(T=500)) == 0
+    good = [ctypes.c_void_p(4096 * (i + 1)) for i in range(18)]
+    call = lambda c, ptrs, n: lib.gau_backward(ctypes.byref(c), *ptrs, ctypes.c_size_t(n), None)
+    assert call(_cfg(rope=True), good, ws) == 2             # no backward of the rotated layer
+    assert call(_cfg(parts="global"), good, ws) == 2        # nor of the partial ones
+    assert call(cfg, good, ws - 1) == 5
+    assert call(cfg, [None] + good[1:], ws) == 1            # NULL X
+    assert call(cfg, good[:8] + [None] + good[9:], ws) == 1  # NULL dO
+    assert call(cfg, good[:17] + [None], ws) == 1           # NULL workspace
+    bad = list(good)
+    bad[12] = ctypes.c_void_p(4096 * 13 + 4)
+    assert call(cfg, bad, ws) == 3                          # misaligned dW_z
+    grow = g.backward_workspace_bytes(_cfg(T=1024))
+    assert grow > ws                                        # grows with the tokens
+    assert g.backward_workspace_bytes(_cfg(dtype=g.GAU_F32)) > ws
+
+
 def test_bad_dtype_rejected():
     cfg = _cfg()
     cfg.dtype = 7

@@ -170,3 +170,53 @@ def test_emulated_decoding_matches_the_causal_layer(emu, dtype, B):
                             inp["relpos"], C, True, use_rope=True)[:, :steps]
     err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
     assert err <= (2e-2 if bf else 1e-4), err
+
+
+BWD_CASES = [
+    # B, T, d, e, s, C, dtype, causal
+    (1, 256, 128, 256, 128, 64, "f32", True),
+    (1, 256, 128, 256, 128, 64, "f32", False),
+    (2, 256, 128, 256, 256, 128, "bf16", True),
+    (1, 320, 128, 512, 128, 64, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}".format(
+    *c[:7], "causal" if c[7] else "full"))
+def test_emulated_backward_matches_oracle(emu, case):
+    """gau_backward on the emulation: every gradient against the oracle's."""
+    B, T, d, e, s, C, dtype, causal = case
+    bf = dtype == "bf16"
+    emu.emu_set_mode(1, 1)
+    P = ctypes.c_void_p
+    emu.gau_backward_workspace_bytes.restype = ctypes.c_size_t
+    emu.gau_backward_workspace_bytes.argtypes = [ctypes.POINTER(GauConfig)]
+    emu.gau_backward.argtypes = [ctypes.POINTER(GauConfig)] + [P] * 18 + [ctypes.c_size_t, P]
+    emu.gau_backward.restype = ctypes.c_int
+    inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=B * 17 + T + C, dtype=dtype)
+    dO = inputs.make_output_grad(B, T, d, seed=T + C, dtype=dtype)
+    cfg = GauConfig(B, T, d, e, s, C, 1 if causal else 0, 1 if bf else 0, 1.0 / C, 1.0 / C, 0, 0)
+    X, dOh = _host(inp["X"], bf), _host(dO, bf)
+    W = {k: _host(np.ascontiguousarray(inp[k].T), bf) for k in ("W_u", "W_v", "W_z", "W_o")}
+    sc, of, rp = (np.ascontiguousarray(inp[k], np.float32) for k in ("gamma", "beta", "relpos"))
+    out = {"X": np.zeros((B, T, d), np.float32), "W_u": np.zeros((e, d), np.float32),
+           "W_v": np.zeros((e, d), np.float32), "W_z": np.zeros((s, d), np.float32),
+           "W_o": np.zeros((d, e), np.float32), "gamma": np.zeros((4, s), np.float32),
+           "beta": np.zeros((4, s), np.float32), "relpos": np.zeros(2 * C - 1, np.float32)}
+    wsb = emu.gau_backward_workspace_bytes(ctypes.byref(cfg))
+    assert wsb > 0
+    raw = np.full(wsb + 256, 0xFF, np.uint8)
+    ws = raw[(-raw.ctypes.data) % 256:][:wsb]
+    ptr = lambda a: P(a.ctypes.data)
+    st = emu.gau_backward(ctypes.byref(cfg), ptr(X), ptr(W["W_u"]), ptr(W["W_v"]), ptr(W["W_z"]), ptr(W["W_o"]),
+                          ptr(sc), ptr(of), ptr(rp), ptr(dOh), *[ptr(out[k]) for k in out], ptr(ws), wsb, None)
+    assert st == 0
+    ref = orc.flash_backward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"], inp["beta"],
+                             inp["relpos"], C, causal, dO)
+    tol = 2e-2 if bf else 1e-4
+    for k, got in out.items():
+        want = ref[k] if k != "W_o" else ref[k].T     # weights come back output-major
+        want = want.T if k in ("W_u", "W_v", "W_z") else want
+        assert np.all(np.isfinite(got)), k
+        err = np.max(np.abs(got - want)) / np.max(np.abs(want))
+        assert err <= tol, f"d{k}: {err:.3e} > {tol}"

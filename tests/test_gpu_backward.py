@@ -1,0 +1,102 @@
+"""GPU parity of the layer's gradients: gau_backward against the float64
+oracle's chain rule (oracle.flash_backward, itself pinned against central
+differences of the brute-force forward), every gradient element by element."""
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_linear_attention_amd as g
+from chunked_linear_attention_amd import inputs
+from oracle import gau_oracle as orc
+
+from _gpu import assert_close, make, tol_for, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _backward(inp, dO, B, T, d, e, s, C, causal, dtype, fill=0):
+    tdt = torch_dtype(dtype)
+    dev = g.device_layer(inp, tdt)
+    cfg = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32)
+    ws = torch.full((g.backward_workspace_bytes(cfg),), fill, dtype=torch.uint8, device="cuda")
+    dOd = g.device_tensor(dO, tdt)
+    like = {"X": (B, T, d), "W_u": (e, d), "W_v": (e, d), "W_z": (s, d), "W_o": (d, e), "scale": (4, s),
+            "offset": (4, s), "relpos": (2 * C - 1,)}
+    grads = {k: torch.full(like[k], float("nan"), dtype=torch.float32, device="cuda") for k in g.GRAD_NAMES}
+    g.backward(cfg, dev["X"], dev["W_u"], dev["W_v"], dev["W_z"], dev["W_o"], dev["scale"], dev["offset"],
+               dev["relpos"], dOd, grads, ws)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
+
+
+def _oracle(inp, dO, C, causal):
+    r = orc.flash_backward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"], inp["beta"],
+                           inp["relpos"], C, causal, dO)
+    # the library returns weight gradients output-major, like the weights it takes
+    return {"X": r["X"], "W_u": r["W_u"].T, "W_v": r["W_v"].T, "W_z": r["W_z"].T, "W_o": r["W_o"].T,
+            "scale": r["gamma"], "offset": r["beta"], "relpos": r["relpos"]}
+
+
+def _compare(got, ref, dtype):
+    for k in g.GRAD_NAMES:
+        assert np.all(np.isfinite(got[k])), f"d{k} has non-finite entries"
+        assert_close(got[k], ref[k], tol_for(dtype), f"d{k}")
+
+
+CASES = [
+    # B, T, d, e, s, C, dtype, causal
+    (1, 256, 128, 256, 128, 64, "f32", True),
+    (1, 256, 128, 256, 128, 64, "f32", False),
+    (2, 512, 256, 512, 128, 128, "bf16", True),
+    (1, 512, 256, 512, 256, 256, "bf16", False),
+    (1, 1024, 256, 512, 128, 512, "bf16", True),    # the largest chunk
+    (3, 192, 384, 768, 128, 64, "bf16", True),      # three chunks per sequence, d and e not powers of two
+    (1, 320, 128, 1024, 256, 64, "f32", False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}".format(
+    *c[:7], "causal" if c[7] else "full"))
+def test_backward_matches_oracle(case):
+    B, T, d, e, s, C, dtype, causal = case
+    print(f"backward case {case}", flush=True)
+    inp = make(B, T, d, e, s, C, dtype, seed=B * 131 + T + C)
+    dO = inputs.make_output_grad(B, T, d, seed=T + d, dtype=dtype)
+    _compare(_backward(inp, dO, B, T, d, e, s, C, causal, dtype), _oracle(inp, dO, C, causal), dtype)
+
+
+def test_backward_at_benchmark_shape():
+    """B=2, T=8192, d=768, e=1536, s=128, C=256, bf16, causal: every gradient."""
+    B, T, d, e, s, C = 2, 8192, 768, 1536, 128, 256
+    print("backward benchmark shape", flush=True)
+    inp = make(B, T, d, e, s, C, "bf16", seed=2024)
+    dO = inputs.make_output_grad(B, T, d, seed=2024, dtype="bf16")
+    _compare(_backward(inp, dO, B, T, d, e, s, C, True, "bf16"), _oracle(inp, dO, C, True), "bf16")
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_backward_is_reproducible_and_ignores_workspace_contents(causal):
+    """Bitwise equal gradients from a zeroed and from a NaN-filled workspace."""
+    B, T, d, e, s, C = 2, 256, 128, 256, 128, 64
+    inp = make(B, T, d, e, s, C, "bf16", seed=77)
+    dO = inputs.make_output_grad(B, T, d, seed=77, dtype="bf16")
+    a = _backward(inp, dO, B, T, d, e, s, C, causal, "bf16", fill=0)
+    b = _backward(inp, dO, B, T, d, e, s, C, causal, "bf16", fill=0xFF)
+    for k in g.GRAD_NAMES:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_backward_without_tokens_zeroes_the_parameter_gradients():
+    d, e, s, C = 128, 256, 128, 64
+    cfg = g.make_config(0, 256, d, e, s, C, True, g.GAU_BF16)
+    grads = {k: torch.full(sh, 5.0, device="cuda") for k, sh in
+             {"X": (0, 256, d), "W_u": (e, d), "W_v": (e, d), "W_z": (s, d), "W_o": (d, e), "scale": (4, s),
+              "offset": (4, s), "relpos": (2 * C - 1,)}.items()}
+    emp = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device="cuda")
+    f32 = lambda *sh: torch.zeros(sh, device="cuda")
+    g.backward(cfg, emp(0, 256, d), emp(e, d), emp(e, d), emp(s, d), emp(d, e), f32(4, s), f32(4, s),
+               f32(2 * C - 1), emp(0, 256, d), grads, torch.empty(1, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    for k in g.GRAD_NAMES[1:]:
+        assert torch.count_nonzero(grads[k]).item() == 0, k
