@@ -5,6 +5,7 @@ MI355X.
                     [--copy-calibration]
     python bench.py --summarize-stats STATS_CSV --command CMD --out FILE.md
     python bench.py --summarize-traffic FETCH_CSV WRITE_CSV --command CMD
+    python bench.py --decode | --backward | --sweep
 
 A step is one full forward of the layer (all six kernels) over one batch of
 seeded synthetic input, B=2 sequences of T=8192 tokens, d=768, e=1536, s=128,
@@ -149,17 +150,17 @@ def copy_calibration(torch):
 
 
 def _short(name):
-    n = name.replace("void gau::(anonymous namespace)::", "")
+    n = name.replace("void gau::(anonymous namespace)::", "").replace("gau::(anonymous namespace)::", "")
     return n.split("(")[0]
 
 
-def summarize_stats(csv_path, command, out):
+def summarize_stats(csv_path, command, out, title=None):
     """Markdown summary of a rocprofv3 --stats kernel table."""
     import csv
     rows = list(csv.DictReader(open(csv_path)))
     total = sum(float(r["TotalDurationNs"]) for r in rows)
-    lines = ["# rocprofv3 kernel statistics: FLASH layer forward, B=2 T=8192 d=768 e=1536 s=128 C=256, "
-             "bf16, causal", "", "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
+    title = title or "FLASH layer forward, B=2 T=8192 d=768 e=1536 s=128 C=256, bf16, causal"
+    lines = [f"# rocprofv3 kernel statistics: {title}", "", "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---:|---:|---:|---:|---:|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
@@ -372,6 +373,78 @@ def decode_bench(steps, warmup, batches=DECODE_BATCHES):
         torch.cuda.empty_cache()
 
 
+def summarize_backward_trace(trace_csv, command, out):
+    """Markdown table of one gau_backward call (the last complete one) from a
+    rocprofv3 --kernel-trace of `bench.py --backward`: every launch in order
+    with its grid and duration, then the totals per kernel."""
+    import csv
+    rows = list(csv.DictReader(open(trace_csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    names = [_short(r["Kernel_Name"]) for r in rows]
+    starts = [i for i, n in enumerate(names) if n.startswith("proj_kernel")]
+    a, b = starts[-2] - 1, starts[-1] - 1   # each call begins with the fill before the projection
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    total = sum(dur(rows[i]) for i in range(a, b))
+    wall = (int(rows[b - 1]["End_Timestamp"]) - int(rows[a]["Start_Timestamp"])) / 1e3
+    lines = ["# rocprofv3 kernel trace: FLASH layer backward (gau_backward), B=2 T=8192 d=768 e=1536 s=128 "
+             "C=256, bf16, causal", "", "Command (from the repository root, one MI355X):", "", "```", command,
+             "```", "", f"One call: {b - a} launches, {total:.1f} us of kernel time, {wall:.1f} us from the first "
+             "launch's start to the last one's end.", "", "| # | kernel | workgroups | us |", "|---:|---|---:|---:|"]
+    per = {}
+    for i in range(a, b):
+        r = rows[i]
+        wg = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0) // max(int(r.get("Workgroup_Size_X", 256) or 256), 1)
+        lines.append(f"| {i - a} | `{names[i]}` | {wg} | {dur(r):.1f} |")
+        per.setdefault(names[i], []).append(dur(r))
+    lines += ["", "| kernel | launches per call | us per call | share |", "|---|---:|---:|---:|"]
+    for n, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{n}` | {len(v)} | {sum(v):.1f} | {100 * sum(v) / total:.1f}% |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def backward_bench(steps, warmup):
+    """The layer's backward pass (gau_backward: the forward's intermediates
+    recomputed, then every gradient) at the headline workload: one JSON line.
+    Algorithmic FLOPs are twice the forward's (each product of the forward has
+    two gradient products); the recomputation is not counted."""
+    import torch
+    import chunked_linear_attention_amd as g
+    from chunked_linear_attention_amd import inputs
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    name = inputs.HEADLINE
+    wl, inp = inputs.workload_inputs(name)
+    B, T, d, e, s, C = (wl[k] for k in ("B", "T", "d", "e", "s", "C"))
+    dev = g.device_layer(inp, torch.bfloat16)
+    dO = g.device_tensor(inputs.make_output_grad(B, T, d, seed=wl["seed"]), torch.bfloat16)
+    cfg = g.make_config(B, T, d, e, s, C, True, g.GAU_BF16)
+    ws = torch.empty(g.backward_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    like = {"X": (B, T, d), "W_u": (e, d), "W_v": (e, d), "W_z": (s, d), "W_o": (d, e), "scale": (4, s),
+            "offset": (4, s), "relpos": (2 * C - 1,)}
+    grads = {k: torch.empty(like[k], dtype=torch.float32, device="cuda") for k in g.GRAD_NAMES}
+    w = (dev["X"], dev["W_u"], dev["W_v"], dev["W_z"], dev["W_o"], dev["scale"], dev["offset"], dev["relpos"])
+
+    def step():
+        g.backward(cfg, *w, dO, grads, ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    fl = 2.0 * sum(algorithmic_flops(B, T, d, e, s, C).values())
+    print(json.dumps({"backward": name, "steps": steps, "warmup": warmup, "ms_per_step": sec * 1e3,
+                      "tokens_per_s": B * T / sec, "workspace_bytes": ws.numel(),
+                      "roofline": {"bound": "mfma", "achieved": fl / sec / 1e12, "peak": PEAK_BF16_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": fl / sec / 1e12 / PEAK_BF16_TFLOPS,
+                                   "algorithmic_flops_per_step": fl}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -385,16 +458,23 @@ def main():
     ap.add_argument("--command", default="")
     ap.add_argument("--out")
     ap.add_argument("--summarize-decode-trace", metavar="TRACE_CSV")
+    ap.add_argument("--summarize-backward-trace", metavar="TRACE_CSV")
     ap.add_argument("--decode", action="store_true",
                     help="incremental decoding throughput per batch size (one JSON line each)")
+    ap.add_argument("--backward", action="store_true",
+                    help="the layer's backward pass at the headline workload (one JSON line)")
+    ap.add_argument("--title", help="heading of a --summarize-stats table")
     ap.add_argument("--sweep", action="store_true",
                     help="throughput of every named workload (one JSON line each) instead of the headline line")
     args = ap.parse_args()
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats, args.command, args.out)
+        summarize_stats(args.summarize_stats, args.command, args.out, args.title)
         return
     if args.summarize_decode_trace:
         summarize_decode_trace(args.summarize_decode_trace, args.command, args.out)
+        return
+    if args.summarize_backward_trace:
+        summarize_backward_trace(args.summarize_backward_trace, args.command, args.out)
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.command)
@@ -409,6 +489,9 @@ def main():
         return
     if args.decode:
         decode_bench(args.steps if args.steps != 100 else 256, args.warmup)
+        return
+    if args.backward:
+        backward_bench(args.steps if args.steps != 100 else 20, args.warmup if args.warmup != 20 else 3)
         return
 
     import torch
