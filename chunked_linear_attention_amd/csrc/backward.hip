@@ -1,13 +1,16 @@
 // Kernels of the layer's backward pass (gradients of <dO, O>): a batched NT
-// GEMM on the shared MFMA core, a batched transpose that makes every product's
-// operands K-major, and the elementwise and reduction steps of the chain rule
-// through the forward's steps (the derivative of each product written out;
-// the forward's steps as the pages give them: wikillm "Method" and the FLASH
-// block pseudocode; Su's post, "Gated Attention" and "Mixed Chunking").  The
-// order of the launches and the buffers they use are in gau_api.hip.
+// GEMM on the shared MFMA core (optionally over two K segments, with fused
+// epilogues for the gate and the SiLU derivative), a batched transpose that
+// makes every product's operands K-major, and the elementwise and reduction
+// steps of the chain rule through the forward's steps (the derivative of each
+// product written out; the forward's steps as the pages give them: wikillm
+// "Method" and the FLASH block pseudocode; Su's post, "Gated Attention" and
+// "Mixed Chunking").  The order of the launches and the buffers they use are
+// in gau_api.hip.
 //
-// Every reduction runs in a fixed order (two-stage sums, no atomics), so the
-// gradients are bitwise reproducible.
+// Every reduction runs in a fixed order (split sums written to scratch and
+// added in index order; no atomics), so the gradients are bitwise
+// reproducible.
 #include "gau_device.h"
 #include "gau_launch.h"
 #include "gemm_core.h"
@@ -31,70 +34,177 @@ __device__ __forceinline__ void st(void* p, size_t i, float v) {
     Elem<T>::put((char*)p + i * Elem<T>::kBytes, v);
 }
 
-template <int N> struct Bits;
-template <> struct Bits<2> { using type = uint16_t; };
-template <> struct Bits<4> { using type = float; };
-
-// C[z] = alpha * A[z] B[z]^T: 64 x 64 tiles, K in chunks; operand z of a
-// batch is at base + (z / div) * batch stride.
+// Eight consecutive elements at index i (a multiple of 8, 16-byte aligned).
 template <typename T>
+__device__ __forceinline__ void load8(const void* p, int64_t i, float (&v)[8]) {
+    if constexpr (Elem<T>::kBytes == 2) {
+        const u32x4_t x = *(const u32x4_t*)((const uint16_t*)p + i);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(x[k] << 16);
+            v[2 * k + 1] = __uint_as_float(x[k] & 0xFFFF0000u);
+        }
+    } else {
+        const f32x4_t a = *(const f32x4_t*)((const float*)p + i);
+        const f32x4_t b = *(const f32x4_t*)((const float*)p + i + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = a[k];
+            v[4 + k] = b[k];
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(void* p, int64_t i, const float (&v)[8]) {
+    if constexpr (Elem<T>::kBytes == 2) {
+        u32x4_t x;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = (uint32_t)f32_to_bf16(v[2 * k]) | ((uint32_t)f32_to_bf16(v[2 * k + 1]) << 16);
+        *(u32x4_t*)((uint16_t*)p + i) = x;
+    } else {
+        *(f32x4_t*)((float*)p + i) = f32x4_t{v[0], v[1], v[2], v[3]};
+        *(f32x4_t*)((float*)p + i + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+    }
+}
+
+// d SiLU(h) / dh = sigma(h) (1 + h (1 - sigma(h))), fp32 with the hardware
+// exponential and reciprocal (as the forward's SiLU).
+__device__ __forceinline__ float silu_grad(float h) {
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h));
+    return sg * (1.0f + h * (1.0f - sg));
+}
+
+// C[z] = alpha * (A[z] B[z]^T + A2[z] B2[z]^T) on BT x BT tiles, then the
+// epilogue EPI (GemmNTParams).
+template <typename T, int BT, int EPI>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmNTParams q) {
     extern __shared__ __align__(16) char lds[];
-    using G = GemmCore<T, 64, 64, 2, 2>;
+    using G = GemmCore<T, BT, BT, 2, 2>;
     constexpr int EB = Elem<T>::kBytes;
     // block -> (batch, row tile, column tile), column tiles fastest
     const int tiles = q.tm * q.tn;
     const int z = blockIdx.x / tiles, t = blockIdx.x - z * tiles;
-    const int m0 = (t / q.tn) * 64, n0 = (t % q.tn) * 64;
+    const int m0 = (t / q.tn) * BT, n0 = (t % q.tn) * BT;
+    if (q.skip_upper && n0 >= m0 + BT) return;  // wholly above the diagonal: never read
     const char* a = (const char*)q.A + ((int64_t)(z / q.a_div) * q.a_bs + (int64_t)m0 * q.a_rp) * EB;
     const char* b = (const char*)q.B + ((int64_t)(z / q.b_div) * q.b_bs + (int64_t)n0 * q.b_rp) * EB;
     f32x16_t acc[G::MB][G::NB];
     G::zero(acc);
-    G::run(acc, a, (size_t)q.a_rp * EB, 64, b, (size_t)q.b_rp * EB, 64, q.K, lds);
+    if (q.K2 > 0) {
+        const char* a2 = (const char*)q.A2 + ((int64_t)(z / q.a_div) * q.a2_bs + (int64_t)m0 * q.a2_rp) * EB;
+        const char* b2 = (const char*)q.B2 + ((int64_t)(z / q.b_div) * q.b2_bs + (int64_t)n0 * q.b2_rp) * EB;
+        G::run_segs(acc, KSeg{a, (size_t)q.a_rp * EB, q.K / G::KELEMS},
+                    KSeg{a2, (size_t)q.a2_rp * EB, q.K2 / G::KELEMS}, BT, KSeg{b, (size_t)q.b_rp * EB, q.K / G::KELEMS},
+                    KSeg{b2, (size_t)q.b2_rp * EB, q.K2 / G::KELEMS}, BT, lds);
+    } else {
+        G::run(acc, a, (size_t)q.a_rp * EB, BT, b, (size_t)q.b_rp * EB, BT, q.K, lds);
+    }
     const int64_t cb = (int64_t)z * q.c_bs + (int64_t)m0 * q.c_rp + n0;
     const float alpha = q.alpha;
-    G::for_each(acc, [&](int r, int c, float v) {
-        const int64_t i = cb + (int64_t)r * q.c_rp + c;
-        if (q.c_f32)
-            ((float*)q.C)[i] = alpha * v;
-        else
-            st<T>(q.C, i, alpha * v);
-    });
+    if constexpr (EPI == EPI_STORE) {
+        G::for_each(acc, [&](int r, int c, float v) {
+            const int64_t i = cb + (int64_t)r * q.c_rp + c;
+            if (q.c_f32)
+                ((float*)q.C)[i] = alpha * v;
+            else
+                st<T>(q.C, i, alpha * v);
+        });
+    } else {
+        // the tile (times alpha) through LDS, then 8 consecutive columns per
+        // thread: 16-byte loads of the inputs and stores of the outputs
+        float* tile = (float*)lds;
+        G::for_each(acc, [&](int r, int c, float v) { tile[r * BT + c] = alpha * v; });
+        __syncthreads();
+        constexpr int PER_ROW = BT / 8;
+#pragma unroll 2
+        for (int k = threadIdx.x; k < BT * PER_ROW; k += 256) {
+            const int r = k / PER_ROW, c = (k % PER_ROW) * 8;
+            float v[8], h[8];
+            const f32x4_t v0 = *(const f32x4_t*)(tile + r * BT + c);
+            const f32x4_t v1 = *(const f32x4_t*)(tile + r * BT + c + 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                v[u] = v0[u];
+                v[4 + u] = v1[u];
+            }
+            const int64_t i = cb + (int64_t)r * q.c_rp + c;
+            load8<T>(q.H, i, h);
+            float o[8];
+            if constexpr (EPI == EPI_SILU) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) o[u] = v[u] * silu_grad(h[u]);
+            } else {  // EPI_GATE: v = dY
+                const int64_t j = (int64_t)(m0 + r) * q.g_rp + n0 + c;
+                float w[8], g[8], a[8], y[8];
+                load8<T>(q.G0, j, w);
+                load8<T>(q.G1, j, g);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    a[u] = v[u] * g[u];
+                    y[u] = g[u] * w[u];
+                    o[u] = v[u] * w[u] * silu_grad(h[u]);
+                }
+                store8<T>(q.O0, j, a);
+                store8<T>(q.O1, j, y);
+            }
+            store8<T>(q.C, i, o);
+        }
+    }
 }
 
-// out[z][c][r] = in[z][r][c] for 64 x 64 tiles (R, Cc multiples of 64).
+// out[z][c][r] = in[z][r][c] on 64 x 64 tiles (R, Cc multiples of 64), rows
+// read and written as 16-byte vectors, the tile turned in LDS.  bf16: each
+// thread reads 8 columns of two adjacent rows and writes the 8 (even row, odd
+// row) pairs as 32-bit words to LDS, column-major, so that an output vector
+// (8 rows of one column) is one 16-byte LDS read.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeParams q) {
-    using S = typename Bits<Elem<T>::kBytes>::type;
-    constexpr int TP = 65;  // padded tile row
-    constexpr int TILE = 64 * TP;
-    __shared__ S tile[TILE];
     const int tiles = q.tr * q.tc;
     const int z = blockIdx.x / tiles, t = blockIdx.x - z * tiles;
     const int r0 = (t / q.tc) * 64, c0 = (t % q.tc) * 64;
-    const S* in = (const S*)q.in + (size_t)z * q.in_bs;
-    S* out = (S*)q.out + (size_t)z * q.out_bs;
-    for (int k = threadIdx.x; k < 64 * 64; k += 256) {
-        const int rr = k / 64, cc = k % 64;
-        tile[rr * TP + cc] = in[(size_t)(r0 + rr) * q.in_rp + c0 + cc];
+    if constexpr (Elem<T>::kBytes == 2) {
+        constexpr int WP = 36;          // LDS words per column (32 row pairs + pad)
+        constexpr int TILE = 64 * WP;
+        __shared__ uint32_t tile[TILE];
+        const uint16_t* in = (const uint16_t*)q.in + (size_t)z * q.in_bs;
+        uint16_t* out = (uint16_t*)q.out + (size_t)z * q.out_bs;
+        const int rp = threadIdx.x / 8, cg = (threadIdx.x % 8) * 8;
+        const u32x4_t a = *(const u32x4_t*)(in + (size_t)(r0 + 2 * rp) * q.in_rp + c0 + cg);
+        const u32x4_t b = *(const u32x4_t*)(in + (size_t)(r0 + 2 * rp + 1) * q.in_rp + c0 + cg);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            tile[(cg + 2 * k) * WP + rp] = (a[k] & 0xFFFFu) | (b[k] << 16);
+            tile[(cg + 2 * k + 1) * WP + rp] = (a[k] >> 16) | (b[k] & 0xFFFF0000u);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 64; p += 32) {
+            const int c = p + threadIdx.x / 8, part = threadIdx.x % 8;
+            const u32x4_t y = *(const u32x4_t*)(tile + c * WP + part * 4);
+            *(u32x4_t*)(out + (size_t)(c0 + c) * q.out_rp + r0 + part * 8) = y;
+        }
+    } else {
+        constexpr int TP = 64 + 4;  // padded LDS row (floats)
+        constexpr int TILE = 64 * TP;
+        __shared__ float tile[TILE];
+        const float* in = (const float*)q.in + (size_t)z * q.in_bs;
+        float* out = (float*)q.out + (size_t)z * q.out_bs;
+        const int vr = threadIdx.x / 16, vc = (threadIdx.x % 16) * 4;
+#pragma unroll
+        for (int p = 0; p < 64; p += 16) {
+            const f32x4_t x = *(const f32x4_t*)(in + (size_t)(r0 + p + vr) * q.in_rp + c0 + vc);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) tile[(vc + k) * TP + p + vr] = x[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 64; p += 16) {
+            const int c = p + vr;
+            const f32x4_t y = *(const f32x4_t*)(tile + c * TP + vc);
+            *(f32x4_t*)(out + (size_t)(c0 + c) * q.out_rp + r0 + vc) = y;
+        }
     }
-    __syncthreads();
-    for (int k = threadIdx.x; k < 64 * 64; k += 256) {
-        const int cc = k / 64, rr = k % 64;
-        out[(size_t)(c0 + cc) * q.out_rp + r0 + rr] = tile[rr * TP + cc];
-    }
-}
-
-// dU = dY * Wq (fp32), dWq = dY * U (element type), Y = U * Wq (element type),
-// with Wq = A V + Q_lin P the attention before the gate.
-template <typename T>
-__global__ __launch_bounds__(256) void gate_bwd_kernel(BwdElemParams q) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= q.n) return;
-    const float dy = q.f1[i], w = ld<T>(q.b, i), u = ld<T>(q.c, i);
-    q.f0[i] = dy * w;
-    st<T>(q.o0, i, dy * u);
-    st<T>(q.o1, i, u * w);
 }
 
 // dSc = 2 relu(Sc) dA * mask with relu(Sc) = sqrt(A) (A = relu(Sc)^2 as the
@@ -112,35 +222,61 @@ __global__ __launch_bounds__(256) void scores_bwd_kernel(BwdElemParams q) {
     st<T>(q.o0, i, v);
 }
 
-// Bias gradient, stage 1: per chunk, the sums of dSc along each diagonal
-// (key - query = k - (C-1)), one thread per diagonal.
+// Bias gradient, stage 1: per chunk and slab of 32 query rows, the sums of dSc
+// along each diagonal (key - query = k - (C-1)), one thread per diagonal.
 __global__ __launch_bounds__(256) void relpos_partial_kernel(const float* dsc, float* part, int C) {
     const int k = blockIdx.y * 256 + threadIdx.x;
     if (k >= 2 * C - 1) return;
-    const size_t z = blockIdx.x;
+    const int slabs = C / 32;
+    const size_t z = blockIdx.x / slabs;
+    const int i0 = (blockIdx.x % slabs) * 32;
     const float* m = dsc + z * C * C;
     const int dd = k - (C - 1);
     float acc = 0.f;
-    for (int i = 0; i < C; ++i) {
+#pragma unroll 8
+    for (int i = i0; i < i0 + 32; ++i) {
         const int j = i + dd;
         if (j >= 0 && j < C) acc += m[(size_t)i * C + j];
     }
-    part[z * (2 * C - 1) + k] = acc;
+    part[(size_t)blockIdx.x * (2 * C - 1) + k] = acc;
 }
 
-// Column sums of a [rows, cols] fp32 array whose rows are `pitch` apart, in
-// row order: out[c] = sum_r in[r * pitch + c].
-__global__ __launch_bounds__(256) void colsum_kernel(const float* in, int pitch, float* out, int rows, int cols) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= cols) return;
+// Column sums of a [rows, cols] fp32 array whose rows are `pitch` apart:
+// out[c] = sum_r in[r * pitch + c].  Block of 16 columns x 64 row groups; row
+// group g adds rows g, g+64, ... in order, then the 64 group sums are added
+// in group order.
+__global__ __launch_bounds__(1024) void colsum_kernel(const float* in, int pitch, float* out, int rows, int cols) {
+    constexpr int CW = 16, NG = 64;
+    constexpr int RED = NG * CW;
+    __shared__ float red[RED];
+    const int cl = threadIdx.x % CW, g = threadIdx.x / CW;
+    const int c = blockIdx.x * CW + cl;
     float acc = 0.f;
-    for (int r = 0; r < rows; ++r) acc += in[(size_t)r * pitch + c];
-    out[c] = acc;
+    if (c < cols)
+        for (int r = g; r < rows; r += NG) acc += in[(size_t)r * pitch + c];
+    red[g * CW + cl] = acc;
+    __syncthreads();
+    if (g == 0 && c < cols) {
+        float s = 0.f;
+        for (int k = 0; k < NG; ++k) s += red[k * CW + cl];
+        out[c] = s;
+    }
+}
+
+// out[i] = sum over z = 0..S-1 (in order) of part[z * stride + i], four
+// entries per thread (n a multiple of 4).
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* part, int64_t stride, float* out, int64_t n,
+                                                           int S) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    f32x4_t acc = *(const f32x4_t*)(part + i);
+    for (int z = 1; z < S; ++z) acc += *(const f32x4_t*)(part + z * stride + i);
+    *(f32x4_t*)(out + i) = acc;
 }
 
 // dS from dP (fp32 [B, G, s*e]): causal dS_h = sum_{g > h} dP_g (a reverse
-// exclusive sum, walked g = G-1 .. 0), non-causal dS_h = sum_g dP_g.  Element
-// type output (an MFMA operand).  One thread per state entry.
+// exclusive sum, walked g = G-1 .. 0), non-causal dS_h = sum_g dP_g; stored
+// times `scale` (lin_scale, which both of dS's products carry), element type.
 template <typename T>
 __global__ __launch_bounds__(256) void scan_bwd_kernel(BwdScanParams q) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -150,28 +286,31 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(BwdScanParams q) {
     if (q.causal) {
         float run = 0.f;
         for (int g = q.G - 1; g >= 0; --g) {
-            st<T>(q.dS, (b * q.G + g) * q.es + v, run);
+            st<T>(q.dS, (b * q.G + g) * q.es + v, q.scale * run);
             run += dp[(size_t)g * q.es];
         }
     } else {
         float tot = 0.f;
         for (int g = 0; g < q.G; ++g) tot += dp[(size_t)g * q.es];
-        for (int g = 0; g < q.G; ++g) st<T>(q.dS, (b * q.G + g) * q.es + v, tot);
+        for (int g = 0; g < q.G; ++g) st<T>(q.dS, (b * q.G + g) * q.es + v, q.scale * tot);
     }
 }
 
-// dZ = sum_k gamma_k dh_k over the four heads; per block of 64 tokens the
-// partial sums of dh_k * Z and dh_k (for gamma and beta).  Thread per feature
-// i (s threads), tokens in order.
+// dZ = sum_k gamma_k dh_k over the four heads, stored as its pre-activation
+// gradient dZ * SiLU'(H_z); per block of kHeadsBwdTokens tokens the partial sums of
+// dh_k * Z and dh_k (for gamma and beta).  Thread per feature i (s threads),
+// tokens in order.
 template <typename T>
 __global__ __launch_bounds__(256) void heads_bwd_kernel(BwdHeadsParams q) {
     const int i = threadIdx.x;
     if (i >= q.s) return;
-    const int m0 = blockIdx.x * 64;
+    const int m0 = blockIdx.x * kHeadsBwdTokens;
     float pg[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int m = m0; m < m0 + 64 && m < q.M; ++m) {
+    for (int m = m0; m < m0 + kHeadsBwdTokens && m < q.M; ++m) {
         const size_t o = (size_t)m * q.s + i;
-        const float z = silu(ld<T>(q.Hz, (size_t)m * q.hpitch + i));
+        const size_t hz = (size_t)m * q.hpitch + i;
+        const float h = ld<T>(q.Hz, hz);
+        const float z = silu(h);
         float dz = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -180,7 +319,7 @@ __global__ __launch_bounds__(256) void heads_bwd_kernel(BwdHeadsParams q) {
             pg[k] += dh * z;
             pb[k] += dh;
         }
-        q.dZ[o] = dz;
+        st<T>(q.dHz, hz, dz * silu_grad(h));
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -189,30 +328,13 @@ __global__ __launch_bounds__(256) void heads_bwd_kernel(BwdHeadsParams q) {
     }
 }
 
-// dH = [dU | dV_local + dV_lin | dZ] * SiLU'(H), element type [M, 2e+s].
+// Ones in the element type, 16 bytes per thread (n * element size a multiple of 16).
 template <typename T>
-__global__ __launch_bounds__(256) void silu_bwd_kernel(BwdSiluParams q) {
+__global__ __launch_bounds__(256) void fill_one_kernel(void* x, size_t n16) {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const int W = 2 * q.e + q.s;
-    if (i >= (size_t)q.M * W) return;
-    const size_t m = i / W;
-    const int f = (int)(i - m * W);
-    float g;
-    if (f < q.e)
-        g = q.dU[m * q.e + f];
-    else if (f < 2 * q.e)
-        g = (q.dVl ? q.dVl[m * q.e + f - q.e] : 0.f) + (q.dVg ? q.dVg[m * q.e + f - q.e] : 0.f);
-    else
-        g = q.dZ[m * q.s + f - 2 * q.e];
-    const float h = ld<T>(q.H, i);
-    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h));
-    st<T>(q.dH, i, g * sg * (1.0f + h * (1.0f - sg)));
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void fill_one_kernel(void* x, size_t n) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) st<T>(x, i, 1.0f);
+    if (i >= n16) return;
+    const uint32_t one = Elem<T>::kBytes == 2 ? 0x3F803F80u : 0x3F800000u;
+    *((u32x4_t*)x + i) = u32x4_t{one, one, one, one};
 }
 
 template <typename P>
@@ -221,23 +343,38 @@ hipError_t go(void (*k)(P), unsigned blocks, const P& p, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <typename T, int BT, int EPI>
+hipError_t gemm_go1(const GemmNTParams& q, unsigned blocks, hipStream_t st) {
+    constexpr int LDS = GemmCore<T, BT, BT, 2, 2>::LDS_BYTES;
+    const hipError_t e = allow_lds<gemm_nt_kernel<T, BT, EPI>>(LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_nt_kernel<T, BT, EPI>), dim3(blocks), dim3(256), LDS, st, q);
+    return hipGetLastError();
+}
+
+template <typename T, int BT>
+hipError_t gemm_go(const GemmNTParams& q, unsigned blocks, hipStream_t st) {
+    switch (q.epi) {
+        case EPI_STORE: return gemm_go1<T, BT, EPI_STORE>(q, blocks, st);
+        case EPI_SILU: return gemm_go1<T, BT, EPI_SILU>(q, blocks, st);
+        case EPI_GATE: return gemm_go1<T, BT, EPI_GATE>(q, blocks, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_nt(const GemmNTParams& q0, int M, int N, int nb, bool bf, hipStream_t st) {
     GemmNTParams q = q0;
-    q.tm = M / 64;
-    q.tn = N / 64;
+    // 128 x 128 tiles when they divide the output and still give every CU work
+    const bool big = M % 128 == 0 && N % 128 == 0 && (int64_t)nb * (M / 128) * (N / 128) >= 512;
+    const int bt = big ? 128 : 64;
+    q.tm = M / bt;
+    q.tn = N / bt;
     const int64_t blocks = (int64_t)nb * q.tm * q.tn;
     if (blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)blocks);
-    if (bf) {
-        constexpr int LDS = GemmCore<bf16, 64, 64, 2, 2>::LDS_BYTES;
-        hipLaunchKernelGGL(gemm_nt_kernel<bf16>, grid, dim3(256), LDS, st, q);
-    } else {
-        constexpr int LDS = GemmCore<float, 64, 64, 2, 2>::LDS_BYTES;
-        hipLaunchKernelGGL(gemm_nt_kernel<float>, grid, dim3(256), LDS, st, q);
-    }
-    return hipGetLastError();
+    if (bf) return big ? gemm_go<bf16, 128>(q, (unsigned)blocks, st) : gemm_go<bf16, 64>(q, (unsigned)blocks, st);
+    return big ? gemm_go<float, 128>(q, (unsigned)blocks, st) : gemm_go<float, 64>(q, (unsigned)blocks, st);
 }
 
 hipError_t launch_transpose(const TransposeParams& q0, int R, int Cc, int nb, bool bf, hipStream_t st) {
@@ -255,17 +392,13 @@ hipError_t launch_transpose(const TransposeParams& q0, int R, int Cc, int nb, bo
 }
 
 hipError_t launch_fill_one(void* x, size_t n, bool bf, hipStream_t st) {
-    const unsigned b = (unsigned)((n + 255) / 256);
+    const size_t n16 = n * (bf ? 2 : 4) / 16;
+    const unsigned b = (unsigned)((n16 + 255) / 256);
     if (bf)
-        hipLaunchKernelGGL(fill_one_kernel<bf16>, dim3(b), dim3(256), 0, st, x, n);
+        hipLaunchKernelGGL(fill_one_kernel<bf16>, dim3(b), dim3(256), 0, st, x, n16);
     else
-        hipLaunchKernelGGL(fill_one_kernel<float>, dim3(b), dim3(256), 0, st, x, n);
+        hipLaunchKernelGGL(fill_one_kernel<float>, dim3(b), dim3(256), 0, st, x, n16);
     return hipGetLastError();
-}
-
-hipError_t launch_gate_bwd(const BwdElemParams& q, bool bf, hipStream_t st) {
-    const unsigned b = (unsigned)((q.n + 255) / 256);
-    return bf ? go(gate_bwd_kernel<bf16>, b, q, st) : go(gate_bwd_kernel<float>, b, q, st);
 }
 
 hipError_t launch_scores_bwd(const BwdElemParams& q, bool bf, hipStream_t st) {
@@ -274,11 +407,19 @@ hipError_t launch_scores_bwd(const BwdElemParams& q, bool bf, hipStream_t st) {
 }
 
 hipError_t launch_relpos_bwd(const float* dsc, float* part, float* drelpos, int nchunks, int C, hipStream_t st) {
-    hipLaunchKernelGGL(relpos_partial_kernel, dim3(nchunks, (2 * C - 1 + 255) / 256), dim3(256), 0, st, dsc, part, C);
+    const int rows = nchunks * (C / 32);
+    hipLaunchKernelGGL(relpos_partial_kernel, dim3(rows, (2 * C - 1 + 255) / 256), dim3(256), 0, st, dsc, part, C);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(colsum_kernel, dim3((2 * C - 1 + 255) / 256), dim3(256), 0, st, part, 2 * C - 1, drelpos,
-                       nchunks, 2 * C - 1);
+    hipLaunchKernelGGL(colsum_kernel, dim3((2 * C - 1 + 15) / 16), dim3(1024), 0, st, part, 2 * C - 1, drelpos, rows,
+                       2 * C - 1);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(const float* part, int64_t stride, float* out, int64_t n, int S, hipStream_t st) {
+    if (n % 4 != 0 || stride % 4 != 0) return hipErrorInvalidValue;
+    const int64_t blocks = (n / 4 + 255) / 256;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, stride, out, n, S);
     return hipGetLastError();
 }
 
@@ -288,21 +429,16 @@ hipError_t launch_scan_bwd(const BwdScanParams& q, bool bf, hipStream_t st) {
 }
 
 hipError_t launch_heads_bwd(const BwdHeadsParams& q, float* dscale, float* doffset, bool bf, hipStream_t st) {
-    const int nblk = (q.M + 63) / 64;
+    const int nblk = (q.M + kHeadsBwdTokens - 1) / kHeadsBwdTokens;
     hipError_t e = bf ? go(heads_bwd_kernel<bf16>, (unsigned)nblk, q, st) : go(heads_bwd_kernel<float>, (unsigned)nblk, q, st);
     if (e != hipSuccess) return e;
     // part is [nblk, 8, s]: the gamma sums in rows 0..3, the beta sums in rows 4..7
-    const dim3 g((4 * q.s + 255) / 256);
-    hipLaunchKernelGGL(colsum_kernel, g, dim3(256), 0, st, q.part, 8 * q.s, dscale, nblk, 4 * q.s);
+    const dim3 g((4 * q.s + 15) / 16);
+    hipLaunchKernelGGL(colsum_kernel, g, dim3(1024), 0, st, q.part, 8 * q.s, dscale, nblk, 4 * q.s);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(colsum_kernel, g, dim3(256), 0, st, q.part + 4 * q.s, 8 * q.s, doffset, nblk, 4 * q.s);
+    hipLaunchKernelGGL(colsum_kernel, g, dim3(1024), 0, st, q.part + 4 * q.s, 8 * q.s, doffset, nblk, 4 * q.s);
     return hipGetLastError();
-}
-
-hipError_t launch_silu_bwd(const BwdSiluParams& q, bool bf, hipStream_t st) {
-    const unsigned b = (unsigned)(((size_t)q.M * (2 * q.e + q.s) + 255) / 256);
-    return bf ? go(silu_bwd_kernel<bf16>, b, q, st) : go(silu_bwd_kernel<float>, b, q, st);
 }
 
 }  // namespace gau

@@ -174,9 +174,19 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
 
 // Backward workspace: the forward's regions, then the backward's own.
 struct BwdLayout {
-    size_t H, ones, dY, dU, dWq, Yb, WoT, dOt, Yt, V, dA, dSc, dScE, dSct, At, Kqc, Qqc, Qlc;
-    size_t dQq, dKq, dQl, dKl, dWqc, dVl, dVg, Pt, dP, dSst, dS, Kl, rpart, hpart, dZ, dH, dHt, Xt, Wt, total;
+    size_t H, ones, dWq, Yb, WoT, dOt, Yt, V, dA, dSc, dScE, dSct, At, Kqc, Qqc, Qlc;
+    size_t dQq, dKq, dQl, dKl, dWqc, Pt, dP, dSst, dS, Kl, rpart, hpart, dH, dHt, Xt, Wt, wpart, total;
+    int split_o, split_w;  // K splits of the weight-gradient products
 };
+
+// Splits of a weight-gradient product (K = M tokens) with `tiles` 128 x 128
+// output tiles: doubled while the grid is small and K / splits stays a
+// multiple of 64.
+int weight_splits(int64_t M, int64_t tiles) {
+    int S = 1;
+    while (S < 8 && tiles * S < 2048 && M % (128 * S) == 0) S *= 2;
+    return S;
+}
 
 void bwd_layout(const gau_config* c, BwdLayout* L) {
     gau_ws_layout F;
@@ -185,6 +195,8 @@ void bwd_layout(const gau_config* c, BwdLayout* L) {
     const size_t M = (size_t)(c->B * c->T), d = c->d, e = c->e, s = c->s, C = c->C;
     const size_t G = c->T / c->C, Z = (size_t)c->B * G, Gp = c->causal ? G : 1;
     const size_t W3 = 2 * e + s;
+    L->split_o = weight_splits((int64_t)M, (int64_t)(d / 128) * (e / 128));
+    L->split_w = weight_splits((int64_t)M, (int64_t)((W3 + 127) / 128) * (d / 128));
     size_t off = F.total;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -193,8 +205,6 @@ void bwd_layout(const gau_config* c, BwdLayout* L) {
     };
     L->H = take(M * W3 * eb);
     L->ones = take(M * e * eb);
-    L->dY = take(M * e * 4);
-    L->dU = take(M * e * 4);
     L->dWq = take(M * e * eb);
     L->Yb = take(M * e * eb);
     L->WoT = take(e * d * eb);
@@ -214,26 +224,41 @@ void bwd_layout(const gau_config* c, BwdLayout* L) {
     L->dQl = take(M * s * 4);
     L->dKl = take(M * s * 4);
     L->dWqc = take(M * e * eb);
-    L->dVl = take(M * e * 4);
-    L->dVg = take(M * e * 4);
     L->Pt = take((size_t)c->B * Gp * e * s * eb);
     L->dP = take(Z * e * s * 4);
     L->dSst = take(Z * e * s * eb);
     L->dS = take(Z * e * s * eb);
     L->Kl = take(M * s * eb);
-    L->rpart = take(Z * (2 * C - 1) * 4);
-    L->hpart = take((M + 63) / 64 * 8 * s * 4);
-    L->dZ = take(M * s * 4);
+    L->rpart = take(M / 32 * (2 * C - 1) * 4);
+    L->hpart = take((M + gau::kHeadsBwdTokens - 1) / gau::kHeadsBwdTokens * 8 * s * 4);
     L->dH = take(M * W3 * eb);
     L->dHt = take(W3 * M * eb);
     L->Xt = take(d * M * eb);
     L->Wt = take(d * W3 * eb);
+    const size_t po = (size_t)L->split_o * d * e, pw = (size_t)L->split_w * W3 * d;
+    L->wpart = take((po > pw ? po : pw) * 4);
     L->total = off;
 }
 
 gau::GemmNTParams nt(const void* A, int64_t a_bs, int a_rp, const void* B, int64_t b_bs, int b_rp, void* C,
                      int64_t c_bs, int c_rp, int K, bool c_f32, float alpha = 1.f, int a_div = 1, int b_div = 1) {
-    return gau::GemmNTParams{A, B, C, a_bs, b_bs, c_bs, a_rp, b_rp, c_rp, a_div, b_div, K, c_f32 ? 1 : 0, alpha, 0, 0};
+    gau::GemmNTParams q{};
+    q.A = A;
+    q.B = B;
+    q.C = C;
+    q.a_bs = a_bs;
+    q.b_bs = b_bs;
+    q.c_bs = c_bs;
+    q.a_rp = a_rp;
+    q.b_rp = b_rp;
+    q.c_rp = c_rp;
+    q.a_div = a_div;
+    q.b_div = b_div;
+    q.K = K;
+    q.c_f32 = c_f32 ? 1 : 0;
+    q.alpha = alpha;
+    q.epi = gau::EPI_STORE;
+    return q;
 }
 
 gau::TransposeParams tp(const void* in, int64_t in_bs, int in_rp, void* out, int64_t out_bs, int out_rp) {
@@ -255,6 +280,7 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     const int T = (int)c->T, Bn = (int)c->B, G = T / C, Z = Bn * G, W3 = 2 * e + s;
     const int64_t CC = (int64_t)C * C, Ce = (int64_t)C * e, Cs = (int64_t)C * s, es = (int64_t)e * s;
     auto W = [&](size_t off) { return (void*)(ws + off); };
+    auto Wc = [&](size_t off, size_t elems) { return (void*)(ws + off + elems * eb); };
     hipError_t err = hipSuccess;  // the first failed launch
     auto ok = [&](hipError_t x) {
         if (err == hipSuccess) err = x;
@@ -270,7 +296,8 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         return GAU_ERR_HIP;
     gau_status sres = run_stages(c, GAU_STAGE_PROJ, GAU_STAGE_SCAN, a, nullptr, nullptr, ws, st);
     if (sres != GAU_OK) return sres;
-    // Wq = A V + Q_lin P: the attention stage with a gate of ones
+    // Wq = A V + Q_lin P (into the forward's Y region): the attention stage
+    // with a gate of ones
     ok(gau::launch_fill_one(W(L.ones), (size_t)M * e, bf, st));
     {
         gau::AttnParams p{W(F.A), W(F.Q_lin), W(F.Vt), W(F.P), W(L.ones), W(F.Y), Bn, T, e, s, C,
@@ -279,21 +306,23 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     }
     // pre-activations H = X [W_u | W_v | W_z]
     gemm(nt(a.X, 0, d, a.W_u, 0, d, W(L.H), 0, W3, d, false), M, e, 1);
-    gemm(nt(a.X, 0, d, a.W_v, 0, d, (char*)W(L.H) + e * eb, 0, W3, d, false), M, e, 1);
-    gemm(nt(a.X, 0, d, a.W_z, 0, d, (char*)W(L.H) + 2 * e * eb, 0, W3, d, false), M, s, 1);
+    gemm(nt(a.X, 0, d, a.W_v, 0, d, Wc(L.H, e), 0, W3, d, false), M, e, 1);
+    gemm(nt(a.X, 0, d, a.W_z, 0, d, Wc(L.H, 2 * e), 0, W3, d, false), M, s, 1);
 
-    // O = Y W_o: dY = dO W_o^T, dW_o = Y^T dO (stored [d, e]: dO^T Y)
+    // O = Y W_o and the gate Y = U * Wq: dY = dO W_o^T, fused with
+    // dWq = dY * U, Y, and dH_u = dY * Wq * SiLU'(H_u)
     trans(tp(a.W_o, 0, e, W(L.WoT), 0, d), d, e, 1);
-    gemm(nt(dO, 0, d, W(L.WoT), 0, d, W(L.dY), 0, e, d, true), M, e, 1);
     {
-        gau::BwdElemParams p{(const float*)W(L.dY), W(F.Y), W(F.U), (float*)W(L.dU), W(L.dWq), W(L.Yb),
-                             (size_t)M * e, C, 0};
-        ok(gau::launch_gate_bwd(p, bf, st));
+        gau::GemmNTParams q = nt(dO, 0, d, W(L.WoT), 0, d, W(L.dH), 0, W3, d, false);
+        q.epi = gau::EPI_GATE;
+        q.H = W(L.H);
+        q.G0 = W(F.Y);
+        q.G1 = W(F.U);
+        q.O0 = W(L.dWq);
+        q.O1 = W(L.Yb);
+        q.g_rp = e;
+        gemm(q, M, e, 1);
     }
-    trans(tp(dO, 0, d, W(L.dOt), 0, M), M, d, 1);
-    trans(tp(W(L.Yb), 0, e, W(L.Yt), 0, M), M, e, 1);
-    gemm(nt(W(L.dOt), 0, M, W(L.Yt), 0, M, dW_o, 0, e, M, true), d, e, 1);
-
     // token-major V and K_lin; chunk-transposed heads, weights and dWq
     trans(tp(W(F.Vt), (int64_t)e * T, T, W(L.V), (int64_t)T * e, e), e, T, Bn);
     trans(tp(W(F.K_lin_t), (int64_t)s * T, T, W(L.Kl), (int64_t)T * s, s), s, T, Bn);
@@ -303,9 +332,13 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     trans(tp(W(F.A), CC, C, W(L.At), CC, C), C, C, Z);
     trans(tp(W(L.dWq), Ce, e, W(L.dWqc), Ce, C), C, e, Z);
 
-    // local part: dA = dWq V^T, dSc = dA * 2 relu(Sc) * mask, dV_local = A^T dWq,
+    // local part: dA = dWq V^T, dSc = dA * 2 relu(Sc) * mask,
     // dQ_quad = qs dSc K_quad, dK_quad = qs dSc^T Q_quad, dBias
-    gemm(nt(W(L.dWq), Ce, e, W(L.V), Ce, e, W(L.dA), CC, C, e, true), C, C, Z);
+    {
+        gau::GemmNTParams q = nt(W(L.dWq), Ce, e, W(L.V), Ce, e, W(L.dA), CC, C, e, true);
+        q.skip_upper = c->causal ? 1 : 0;
+        gemm(q, C, C, Z);
+    }
     {
         gau::BwdElemParams p{(const float*)W(L.dA), W(F.A), nullptr, (float*)W(L.dSc), W(L.dScE), nullptr,
                              (size_t)Z * CC, C, c->causal ? 1 : 0};
@@ -315,45 +348,68 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     trans(tp(W(L.dScE), CC, C, W(L.dSct), CC, C), C, C, Z);
     gemm(nt(W(L.dScE), CC, C, W(L.Kqc), Cs, C, W(L.dQq), Cs, s, C, true, c->quad_scale), C, s, Z);
     gemm(nt(W(L.dSct), CC, C, W(L.Qqc), Cs, C, W(L.dKq), Cs, s, C, true, c->quad_scale), C, s, Z);
-    gemm(nt(W(L.At), CC, C, W(L.dWqc), Ce, C, W(L.dVl), Ce, e, C, true), C, e, Z);
 
     // global part: dQ_lin = dWq P^T, dP = Q_lin^T dWq (per chunk, stored [e, s]),
-    // dS = reverse exclusive sum of dP (total when non-causal),
-    // dV_global = ls K_lin dS, dK_lin = ls V dS^T
+    // dS = ls * (reverse exclusive sum of dP, or the total when non-causal),
+    // dK_lin = V dS^T
     const int Gp = c->causal ? G : 1;
     trans(tp(W(F.P), es, s, W(L.Pt), es, e), e, s, Bn * Gp);
     gemm(nt(W(L.dWq), Ce, e, W(L.Pt), es, e, W(L.dQl), Cs, s, e, true, 1.f, 1, c->causal ? 1 : G), C, s, Z);
     gemm(nt(W(L.dWqc), Ce, C, W(L.Qlc), Cs, C, W(L.dP), es, s, C, true), e, s, Z);
     {
-        gau::BwdScanParams p{(const float*)W(L.dP), W(L.dSst), Bn, G, (int)es, c->causal ? 1 : 0};
+        gau::BwdScanParams p{(const float*)W(L.dP), W(L.dSst), Bn, G, (int)es, c->causal ? 1 : 0, c->lin_scale};
         ok(gau::launch_scan_bwd(p, bf, st));
     }
     trans(tp(W(L.dSst), es, s, W(L.dS), es, e), e, s, Z);
-    gemm(nt(W(L.Kl), Cs, s, W(L.dSst), es, s, W(L.dVg), Ce, e, s, true, c->lin_scale), C, e, Z);
-    gemm(nt(W(L.V), Ce, e, W(L.dS), es, e, W(L.dKl), Cs, s, e, true, c->lin_scale), C, s, Z);
+    gemm(nt(W(L.V), Ce, e, W(L.dS), es, e, W(L.dKl), Cs, s, e, true), C, s, Z);
 
-    // heads h_k = Z gamma_k + beta_k: dZ, dgamma, dbeta
+    // dV = A^T dWq + K_lin dS (two K segments), stored as dH_v = dV * SiLU'(H_v)
+    {
+        gau::GemmNTParams q = nt(W(L.At), CC, C, W(L.dWqc), Ce, C, Wc(L.dH, e), (int64_t)C * W3, W3, C, false);
+        q.A2 = W(L.Kl);
+        q.a2_bs = Cs;
+        q.a2_rp = s;
+        q.B2 = W(L.dSst);
+        q.b2_bs = es;
+        q.b2_rp = s;
+        q.K2 = s;
+        q.epi = gau::EPI_SILU;
+        q.H = Wc(L.H, e);
+        gemm(q, C, e, Z);
+    }
+    // heads h_k = Z gamma_k + beta_k: dZ (stored as dH_z), dgamma, dbeta
     {
         gau::BwdHeadsParams p{{(const float*)W(L.dQq), (const float*)W(L.dKq), (const float*)W(L.dQl),
                                (const float*)W(L.dKl)},
-                              (char*)W(L.H) + 2 * e * eb, W3, a.scale, (float*)W(L.dZ), (float*)W(L.hpart), M, s};
+                              Wc(L.H, 2 * e), W3, a.scale, Wc(L.dH, 2 * e), (float*)W(L.hpart), M, s};
         ok(gau::launch_heads_bwd(p, dscale, doffset, bf, st));
     }
-    // SiLU: dH = [dU | dV | dZ] * SiLU'(H); X W: dX = dH W^T, dW = X^T dH
-    {
-        gau::BwdSiluParams p{(const float*)W(L.dU), (const float*)W(L.dVl), (const float*)W(L.dVg),
-                             (const float*)W(L.dZ), W(L.H), W(L.dH), M, e, s};
-        ok(gau::launch_silu_bwd(p, bf, st));
-    }
+    // X W: dX = dH W^T
     trans(tp(a.W_u, 0, d, W(L.Wt), 0, W3), e, d, 1);
-    trans(tp(a.W_v, 0, d, (char*)W(L.Wt) + e * eb, 0, W3), e, d, 1);
-    trans(tp(a.W_z, 0, d, (char*)W(L.Wt) + 2 * e * eb, 0, W3), s, d, 1);
+    trans(tp(a.W_v, 0, d, Wc(L.Wt, e), 0, W3), e, d, 1);
+    trans(tp(a.W_z, 0, d, Wc(L.Wt, 2 * e), 0, W3), s, d, 1);
     gemm(nt(W(L.dH), 0, W3, W(L.Wt), 0, W3, dX, 0, d, W3, true), M, d, 1);
+
+    // weight gradients, K = M split L.split_* ways into fp32 partials added in
+    // split order: dW_o (stored [d, e]) = dO^T Y, [dW_u | dW_v | dW_z] = dH^T X
+    float* wp = (float*)W(L.wpart);
+    trans(tp(dO, 0, d, W(L.dOt), 0, M), M, d, 1);
+    trans(tp(W(L.Yb), 0, e, W(L.Yt), 0, M), M, e, 1);
+    {
+        const int S = L.split_o, Ks = M / S;
+        gemm(nt(W(L.dOt), Ks, M, W(L.Yt), Ks, M, wp, (int64_t)d * e, e, Ks, true), d, e, S);
+        ok(gau::launch_split_reduce(wp, (int64_t)d * e, dW_o, (int64_t)d * e, S, st));
+    }
     trans(tp(W(L.dH), 0, W3, W(L.dHt), 0, M), M, W3, 1);
     trans(tp(a.X, 0, d, W(L.Xt), 0, M), M, d, 1);
-    gemm(nt(W(L.dHt), 0, M, W(L.Xt), 0, M, dW_u, 0, d, M, true), e, d, 1);
-    gemm(nt((char*)W(L.dHt) + (size_t)e * M * eb, 0, M, W(L.Xt), 0, M, dW_v, 0, d, M, true), e, d, 1);
-    gemm(nt((char*)W(L.dHt) + (size_t)2 * e * M * eb, 0, M, W(L.Xt), 0, M, dW_z, 0, d, M, true), s, d, 1);
+    {
+        const int S = L.split_w, Ks = M / S;
+        const int64_t stride = (int64_t)W3 * d;
+        gemm(nt(W(L.dHt), Ks, M, W(L.Xt), Ks, M, wp, stride, d, Ks, true), W3, d, S);
+        ok(gau::launch_split_reduce(wp, stride, dW_u, (int64_t)e * d, S, st));
+        ok(gau::launch_split_reduce(wp + (size_t)e * d, stride, dW_v, (int64_t)e * d, S, st));
+        ok(gau::launch_split_reduce(wp + (size_t)2 * e * d, stride, dW_z, (int64_t)s * d, S, st));
+    }
     return err == hipSuccess ? GAU_OK : GAU_ERR_HIP;
 }
 

@@ -135,11 +135,19 @@ hipError_t launch_rms_norm(const NormParams& p, bool bf16_storage, hipStream_t s
 
 // ---- backward pass -------------------------------------------------------
 
-// Batched C[z] = alpha * A[z] B[z]^T on the MFMA core, 64 x 64 output tiles.
-// Operand z of A is at A + (z / a_div) * a_bs elements (B likewise; C at
-// z * c_bs); rows are a_rp / b_rp / c_rp elements apart; both operands are
-// K-major (K a multiple of 64, every dimension a multiple of 64).  C is fp32
-// when c_f32, else the layer's element type.
+// Epilogues of the backward GEMM (value v = alpha * accumulator at (row, col),
+// i its index in C).
+enum { EPI_STORE = 0,  // C[i] = v (fp32 when c_f32, else the element type)
+       EPI_SILU = 1,   // C[i] = v * SiLU'(H[i])
+       EPI_GATE = 2 }; // v = dY at (m, n), j = m * g_rp + n: O0[j] = v * G1[j] (dWq),
+                       // O1[j] = G1[j] * G0[j] (Y), C[i] = v * G0[j] * SiLU'(H[i]) (dH_u)
+
+// Batched C[z] = alpha * (A[z] B[z]^T + A2[z] B2[z]^T) on the MFMA core, 64 x 64
+// or 128 x 128 output tiles.  Operand z of A is at A + (z / a_div) * a_bs
+// elements (B likewise with b_div; A2, B2 with the same divisors and their own
+// strides; C at z * c_bs); rows are *_rp elements apart; every operand is
+// K-major (K and K2 multiples of 64, every dimension a multiple of 64).  The
+// second segment is used when K2 > 0.
 struct GemmNTParams {
     const void* A;
     const void* B;
@@ -151,6 +159,17 @@ struct GemmNTParams {
     int c_f32;
     float alpha;
     int tm, tn;  // row / column tiles per batch entry (set by the launcher)
+    const void* A2;
+    const void* B2;
+    int64_t a2_bs, b2_bs;
+    int a2_rp, b2_rp;
+    int K2;
+    int epi;
+    const void* H;              // EPI_SILU, EPI_GATE
+    const void *G0, *G1;        // EPI_GATE inputs: Wq, U
+    void *O0, *O1;              // EPI_GATE outputs: dWq, Y
+    int g_rp;
+    int skip_upper;  // skip output tiles wholly above the diagonal (never read)
 };
 
 // out[z][c][r] = in[z][r][c], element type, R and Cc multiples of 64.
@@ -162,54 +181,47 @@ struct TransposeParams {
     int tr, tc;  // row / column tiles per batch entry (set by the launcher)
 };
 
-// Elementwise steps of the gate and the scores (see backward.hip).
+// The scores' elementwise step (see backward.hip).
 struct BwdElemParams {
-    const float* f1;   // fp32 input (dY, or dA)
-    const void* b;     // element type input (Wq, or A)
-    const void* c;     // element type input (U)
-    float* f0;         // fp32 output (dU, or dSc)
-    void* o0;          // element type output (dWq, or dSc)
-    void* o1;          // element type output (Y)
+    const float* f1;   // dA, fp32
+    const void* b;     // A, element type
+    const void* c;     // unused
+    float* f0;         // dSc, fp32
+    void* o0;          // dSc, element type
+    void* o1;          // unused
     size_t n;
     int C, causal;
 };
 
 struct BwdScanParams {
     const float* dP;  // [B, G, es] fp32
-    void* dS;         // [B, G, es] element type
+    void* dS;         // [B, G, es] element type, times scale
     int B, G, es, causal;
+    float scale;
 };
+
+constexpr int kHeadsBwdTokens = 16;  // tokens per block of the heads' backward step
 
 struct BwdHeadsParams {
     const float* dh[4];  // gradients of Q_quad, K_quad, Q_lin, K_lin, [M, s] fp32
     const void* Hz;      // pre-activation of Z: row m at Hz + m * hpitch elements
     int hpitch;
     const float* scale;  // [4, s]
-    float* dZ;           // [M, s]
-    float* part;         // [ceil(M / 64), 8, s] per-block sums
+    void* dHz;           // its gradient, same layout as Hz
+    float* part;         // [ceil(M / kHeadsBwdTokens), 8, s] per-block sums
     int M, s;
-};
-
-struct BwdSiluParams {
-    const float* dU;   // [M, e]
-    const float* dVl;  // [M, e] local part of dV
-    const float* dVg;  // [M, e] global part of dV
-    const float* dZ;   // [M, s]
-    const void* H;     // [M, 2e + s] pre-activations
-    void* dH;          // [M, 2e + s]
-    int M, e, s;
 };
 
 hipError_t launch_gemm_nt(const GemmNTParams& q, int M, int N, int nb, bool bf16_storage, hipStream_t st);
 hipError_t launch_transpose(const TransposeParams& q, int R, int Cc, int nb, bool bf16_storage, hipStream_t st);
 hipError_t launch_fill_one(void* x, size_t n, bool bf16_storage, hipStream_t st);
-hipError_t launch_gate_bwd(const BwdElemParams& q, bool bf16_storage, hipStream_t st);
 hipError_t launch_scores_bwd(const BwdElemParams& q, bool bf16_storage, hipStream_t st);
 // drelpos[k] = sum over chunks and over entries on diagonal k - (C-1) of dsc
 hipError_t launch_relpos_bwd(const float* dsc, float* part, float* drelpos, int nchunks, int C, hipStream_t st);
+// out[i] = sum_{z < S} part[z * stride + i], i < n (n, stride multiples of 4)
+hipError_t launch_split_reduce(const float* part, int64_t stride, float* out, int64_t n, int S, hipStream_t st);
 hipError_t launch_scan_bwd(const BwdScanParams& q, bool bf16_storage, hipStream_t st);
 hipError_t launch_heads_bwd(const BwdHeadsParams& q, float* dscale, float* doffset, bool bf16_storage,
                             hipStream_t st);
-hipError_t launch_silu_bwd(const BwdSiluParams& q, bool bf16_storage, hipStream_t st);
 
 }  // namespace gau

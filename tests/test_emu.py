@@ -178,6 +178,7 @@ BWD_CASES = [
     (1, 256, 128, 256, 128, 64, "f32", False),
     (2, 256, 128, 256, 256, 128, "bf16", True),
     (1, 320, 128, 512, 128, 64, "bf16", False),
+    (1, 1024, 1024, 1024, 128, 256, "bf16", True),   # 128 x 128 tiles (weight gradients, dV, dX)
 ]
 
 
