@@ -220,6 +220,61 @@ def summarize_traffic(fetch_csv, write_csv, command):
     print(json.dumps(rec))
 
 
+def summarize_counters(csvs, stats_csv, command, out):
+    """Per-kernel table from rocprofv3 --pmc runs of the headline bench: MFMA
+    utilisation (MfmaUtil: busy MFMA cycles over active cycles of all SIMDs),
+    MFMA FLOPs (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), and HBM bytes (FETCH_SIZE,
+    WRITE_SIZE scaled by the calibration copy in the same run), with rates
+    over the kernel-trace average durations of stats_csv."""
+    import csv
+    dur = {_short(r["Name"]): float(r["AverageNs"]) * 1e-9 for r in csv.DictReader(open(stats_csv))}
+    vals = {}  # (kernel, counter) -> list of per-dispatch values
+    scale = {}
+    for path in csvs:
+        rows = list(csv.DictReader(open(path)))
+        for counter in sorted({r["Counter_Name"] for r in rows}):
+            crow = _counter_rows(path, counter)
+            if counter in ("FETCH_SIZE", "WRITE_SIZE"):
+                blits = [r for r in crow if r[0] == "__amd_rocclr_copyBuffer"]
+                big = max(g for _, g, _ in blits) if blits else 0
+                copy = [v for _, g, v in blits if g == big]
+                if len(copy) != 3:
+                    raise SystemExit(f"{path}: expected 3 calibration copies")
+                scale[counter] = sum(copy) / 3 * 1024.0 / COPY_BYTES
+            for k, _, v in crow:
+                if "gau::" not in k:  # the calibration copy and torch's input set-up
+                    continue
+                vals.setdefault((_short(k), counter), []).append(v)
+    kernels = sorted({k for k, _ in vals}, key=lambda k: -dur.get(k, 0))
+    mean = lambda k, c: (sum(vals[(k, c)]) / len(vals[(k, c)])) if (k, c) in vals else None
+    lines = ["# Hardware counters per kernel: FLASH layer forward, B=2 T=8192 d=768 e=1536 s=128 C=256, bf16, causal",
+             "", "Commands (from the repository root, one MI355X; one counter group per run):", "", "```", command,
+             "```", "",
+             "MFMA util = MfmaUtil (busy MFMA cycles summed over SIMDs / (active GPU cycles x SIMDs)); MFMA "
+             "TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP / trace duration; HBM MB = FETCH_SIZE and "
+             "WRITE_SIZE per dispatch divided by each counter's reading per true byte of a 256 MiB device copy "
+             + ", ".join(f"({c}: {v:.4f})" for c, v in sorted(scale.items())) + "; GB/s over the trace duration.",
+             "", "| kernel | trace avg (us) | MFMA util | MFMA TFLOP/s | HBM read MB | HBM write MB | HBM GB/s |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for k in kernels:
+        t = dur.get(k)
+        util = mean(k, "MfmaUtil")
+        mops = mean(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        rd = mean(k, "FETCH_SIZE")
+        wr = mean(k, "WRITE_SIZE")
+        rd = rd * 1024.0 / scale["FETCH_SIZE"] if rd is not None else None
+        wr = wr * 1024.0 / scale["WRITE_SIZE"] if wr is not None else None
+        f = lambda x, fmt: (fmt % x) if x is not None else "-"
+        tf = mops * 512 / t / 1e12 if (mops is not None and t) else None
+        gbs = (rd + wr) / t / 1e9 if (rd is not None and wr is not None and t) else None
+        lines.append(f"| `{k}` | {f(t * 1e6 if t else None, '%.1f')} | {f(util, '%.1f%%')} | {f(tf, '%.0f')} | "
+                     f"{f(rd / 1e6 if rd is not None else None, '%.1f')} | "
+                     f"{f(wr / 1e6 if wr is not None else None, '%.1f')} | {f(gbs, '%.0f')} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def sweep(steps, warmup):
     """Forward throughput of every named workload (single layers causal and
     not, C = 256 and 512, the 24-layer stack), one single-call forward per
@@ -455,6 +510,9 @@ def main():
                     help="after the measurement, run the copy that calibrates the HBM counters")
     ap.add_argument("--summarize-stats", metavar="STATS_CSV")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_CSV",
+                    help="per-kernel MFMA utilisation and HBM traffic from rocprofv3 --pmc csv files (needs --stats)")
+    ap.add_argument("--stats", metavar="STATS_CSV", help="kernel statistics csv for --summarize-counters")
     ap.add_argument("--command", default="")
     ap.add_argument("--out")
     ap.add_argument("--summarize-decode-trace", metavar="TRACE_CSV")
@@ -478,6 +536,9 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.command)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.stats, args.command, args.out)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

@@ -122,7 +122,13 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >>
 // each stage after B) times the B tile, accumulated per wave into ZR x 32
 // outputs (run_with_side).  Wave (wm, wn) multiplies the side rows by its own
 // B fragment wm, so the 2 x WGN waves cover the B tile's columns once.
-template <typename T, int BM, int BN, int WGM, int WGN, int NS = 2, int ZR = 0>
+//
+// NSB > NS (only NS = 2, NSB = 3): the B operand gets a ring of its own with
+// one more stage, so two of its chunks are in flight while one is multiplied
+// (for a B operand streamed from HBM beside an A operand that stays in L2).
+// The A stages then lie at [0, NS * A_BYTES) and the B stages after them, and
+// the per-chunk barrier waits only for LDS reads and the copies it needs.
+template <typename T, int BM, int BN, int WGM, int WGN, int NS = 2, int ZR = 0, int NSB = NS>
 struct GemmCore {
     static constexpr int NW = WGM * WGN;
     static constexpr int NT = NW * kWave;
@@ -134,7 +140,9 @@ struct GemmCore {
     static constexpr int A_BYTES = BM * 128;
     static constexpr int Z_OFF = (BM + BN) * 128;  // side rows inside a stage
     static constexpr int STAGE_BYTES = (BM + BN + ZR) * 128;
-    static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+    static constexpr int B_BYTES = BN * 128;
+    static constexpr bool kAsym = NSB != NS;
+    static constexpr int LDS_BYTES = kAsym ? NS * A_BYTES + NSB * B_BYTES : NS * STAGE_BYTES;
     static constexpr int LOADS = (BM / 8) / NW + (BN / 8) / NW;  // DMA loads per wave per chunk
     static constexpr int ZMB = ZR > 0 ? ZR / 32 : 1;  // side row blocks per wave
     static constexpr int ZPIECES = ZR / 8;            // 1 KiB wave pieces of the side rows
@@ -143,6 +151,7 @@ struct GemmCore {
     static_assert(ZR == 0 || (ZR % 32 == 0 && WGM == 2 && WTN == 64 && NS == 2 && ZPIECES <= NW),
                   "side operand layout");
     static_assert(NS >= 2 && (NS - 2) * LOADS < 64, "stages / vmcnt range");
+    static_assert(!kAsym || (NS == 2 && NSB == 3 && ZR == 0), "split ring: NS = 2, NSB = 3, no side rows");
     static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "tile shape");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "tile rows");
     static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "pieces must split evenly over waves");
@@ -353,12 +362,113 @@ struct GemmCore {
         __syncthreads();  // LDS free for the epilogue
     }
 
+    // One chunk kt of the split ring.  MORE_A: chunk kt+1 exists (copy A(kt+1),
+    // then barrier and read chunk kt+1's first fragments); MORE_B: chunk kt+2
+    // exists (copy B(kt+2), which may stay in flight across the barrier).
+    template <bool MORE_A, bool MORE_B>
+    __device__ static __forceinline__ void split_chunk(f32x16_t (&acc)[MB][NB], u32x4_t (&fa)[2][MB],
+                                                       u32x4_t (&fb)[2][NB], char* la, char* lb,
+                                                       const DmaOperand<BM, NW>& da, const DmaOperand<BN, NW>& db,
+                                                       int& sa, int& sb, int kt, int wave, int fr, int fh, int oa,
+                                                       int ob) {
+        constexpr int LB = DmaOperand<BN, NW>::kLoads;
+        const char* ca = la + sa * A_BYTES + oa;
+        const char* cb = lb + sb * B_BYTES + ob;
+        const int na = sa ^ 1;                    // A stage of chunk kt+1
+        const int nb1 = sb == 2 ? 0 : sb + 1;     // B stage of chunk kt+1
+        const int nb2 = nb1 == 2 ? 0 : nb1 + 1;   // B stage of chunk kt+2
+        if constexpr (MORE_A) da.issue(la + na * A_BYTES, kt + 1, wave);
+        if constexpr (MORE_B) db.issue(lb + nb2 * B_BYTES, kt + 2, wave);
+        Side none;
+        none.on = false;
+        step<0, false, false>(acc, fa, fb, ca, cb, da, db, nullptr, 0, wave, fr, fh, none, nullptr, 0);
+        step<1, false, false>(acc, fa, fb, ca, cb, da, db, nullptr, 0, wave, fr, fh, none, nullptr, 0);
+        step<2, false, false>(acc, fa, fb, ca, cb, da, db, nullptr, 0, wave, fr, fh, none, nullptr, 0);
+        step<3, false, false>(acc, fa, fb, ca, cb, da, db, nullptr, 0, wave, fr, fh, none, nullptr, 0);
+        if constexpr (MORE_A) {
+            ring_barrier<MORE_B ? LB : 0>();
+            sa = na;
+            sb = nb1;
+            load_frags(fa[0], fb[0], la + sa * A_BYTES + oa, lb + sb * B_BYTES + ob, 0, fr, fh);
+        }
+    }
+
+    // Workgroup barrier for the split ring: waits for this wave's LDS reads
+    // (its fragments of the chunk just multiplied) and for all but the NOUT
+    // most recent vector-memory operations (its copies of the next chunk);
+    // unlike __syncthreads it does not wait for every copy in flight.  The
+    // signal fences (no instructions) keep the compiler from moving memory
+    // accesses across it.
+    template <int NOUT>
+    __device__ static __forceinline__ void ring_barrier() {
+        static_assert(NOUT >= 0 && NOUT < 64, "vmcnt out of range");
+        __builtin_amdgcn_s_waitcnt((NOUT & 0xF) | ((NOUT >> 4) << 14) | 0x70);  // lgkmcnt(0), vmcnt(NOUT)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+
+    // acc += A . B^T with the split ring (NS = 2 A stages, NSB = 3 B stages).
+    // Copy order: A(0), B(0), B(1), then iteration kt issues A(kt+1) and
+    // B(kt+2).  Vector-memory loads complete in issue order, so chunk kt+1 is
+    // complete (A(kt+1) and the earlier B(kt+1)) once at most B(kt+2)'s loads
+    // are outstanding.  A stage kt%2 and B stage kt%3 are rewritten only in
+    // iteration kt+1, after the barrier that ends iteration kt.
+    __device__ static __forceinline__ void run_split(f32x16_t (&acc)[MB][NB], const KSeg& a0, const KSeg& a1,
+                                                     int rows_a, const KSeg& b0, const KSeg& b1, int rows_b,
+                                                     char* lds) {
+        static_assert(kAsym, "split ring only");
+        constexpr int LB = DmaOperand<BN, NW>::kLoads;
+        const int tid = threadIdx.x;
+        const int wave = tid / kWave;
+        const int lane = tid % kWave;
+        const int wm = wave / WGN, wn = wave % WGN;
+        const int nk = a0.chunks + a1.chunks;
+        const int fr = lane & 31;
+        const int fh = lane >> 5;
+        char* const la = lds;                  // A stages
+        char* const lb = lds + NS * A_BYTES;   // B stages
+
+        DmaOperand<BM, NW> da;
+        DmaOperand<BN, NW> db;
+        da.init(a0, a1, rows_a, wave, lane);
+        db.init(b0, b1, rows_b, wave, lane);
+        if (nk > 0) {
+            da.issue(la, 0, wave);
+            db.issue(lb, 0, wave);
+        }
+        if (nk > 1) {
+            db.issue(lb + B_BYTES, 1, wave);
+            ring_barrier<LB>();
+        } else {
+            ring_barrier<0>();
+        }
+
+        u32x4_t fa[2][MB], fb[2][NB];
+        const int oa = (wm * WTM) * 128, ob = (wn * WTN) * 128;
+        load_frags(fa[0], fb[0], la + oa, lb + ob, 0, fr, fh);
+
+        int sa = 0, sb = 0;  // stages of chunk kt
+        int kt = 0;
+        for (; kt + 2 < nk; ++kt) split_chunk<true, true>(acc, fa, fb, la, lb, da, db, sa, sb, kt, wave, fr, fh, oa, ob);
+        if (kt + 1 < nk) {
+            split_chunk<true, false>(acc, fa, fb, la, lb, da, db, sa, sb, kt, wave, fr, fh, oa, ob);
+            ++kt;
+        }
+        if (kt < nk) split_chunk<false, false>(acc, fa, fb, la, lb, da, db, sa, sb, kt, wave, fr, fh, oa, ob);
+        __syncthreads();  // LDS free for the epilogue
+    }
+
     __device__ static __forceinline__ void run_segs(f32x16_t (&acc)[MB][NB], const KSeg& a0, const KSeg& a1,
                                                     int rows_a, const KSeg& b0, const KSeg& b1, int rows_b,
                                                     char* lds) {
-        Side none;
-        none.on = false;
-        run_impl<false>(acc, a0, a1, rows_a, b0, b1, rows_b, lds, none);
+        if constexpr (kAsym) {
+            run_split(acc, a0, a1, rows_a, b0, b1, rows_b, lds);
+        } else {
+            Side none;
+            none.on = false;
+            run_impl<false>(acc, a0, a1, rows_a, b0, b1, rows_b, lds, none);
+        }
     }
 
     // acc += A . B^T over K elements (a multiple of KELEMS), one segment each.

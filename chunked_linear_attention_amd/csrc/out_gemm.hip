@@ -19,7 +19,9 @@ constexpr int BN = 256, WGM = 2, WGN = 4;  // tokens per tile, wave grid
 
 template <typename T, int BM>
 struct OutTile {
-    using G = GemmCore<T, BM, BN, WGM, WGN>;
+    // Y (the B operand) streams from HBM: a third B stage keeps two of its
+    // chunks in flight; W_o (A) stays in L2 with two stages
+    using G = GemmCore<T, BM, BN, WGM, WGN, 2, 0, 3>;
     // staging of one pass of the epilogue in the worst case (fp32, WGN passes)
     static constexpr int STAGE = BN / WGN * (BM * 4 + 16);
     static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
