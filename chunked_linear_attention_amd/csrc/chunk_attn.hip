@@ -16,7 +16,9 @@
 // to zero).  The gate multiplies the fp32 accumulator by U in the epilogue,
 // which stores Y token-major; the block's U values are loaded into registers
 // before the main loop, so their latency overlaps the chunk copies instead of
-// adding one more round trip after them.
+// adding one more round trip after them.  Y may be U itself (the forward
+// gates in place): a block writes exactly the elements of Y whose gate values
+// it has already read, and no other block reads them.
 #include "gau_launch.h"
 #include "gemm_core.h"
 

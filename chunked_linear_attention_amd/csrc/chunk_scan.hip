@@ -13,7 +13,10 @@
 // in a fixed order (never an inclusive sum minus the own term), which keeps the
 // causal outputs independent of later chunks bit for bit.  S and P are in the
 // layer's element type (P's consumer is an MFMA operand of that type); the
-// sums are fp32.  HBM bound: it reads S once and writes P once.
+// sums are fp32.  HBM bound: it reads S once and writes P once.  In the
+// causal case P may be S itself (the forward runs the scan in place): a
+// thread reads each of its entries of S_g before it writes the same entries
+// of P_g, and no other thread touches them, so S and P are not restrict.
 #include "gau_device.h"
 #include "gau_launch.h"
 
@@ -56,8 +59,8 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanParams p) {
     const int v = idx - b * per_b;
     const size_t stride = (size_t)p.es;  // elements between consecutive chunks
     constexpr int EB = Elem<T>::kBytes;
-    const char* __restrict__ S = (const char*)p.S + ((size_t)b * p.G * stride + (size_t)v * 4) * EB;
-    char* __restrict__ P = (char*)p.P;
+    const char* S = (const char*)p.S + ((size_t)b * p.G * stride + (size_t)v * 4) * EB;
+    char* P = (char*)p.P;
     const size_t cstride = stride * EB;  // bytes between consecutive chunks
     f32x4_t run = {0.f, 0.f, 0.f, 0.f};
     if (p.causal) {

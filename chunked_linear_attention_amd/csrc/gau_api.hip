@@ -35,7 +35,15 @@ gau_status check_config(const gau_config* c) {
     return GAU_OK;
 }
 
-void layout(const gau_config* c, gau_ws_layout* L) {
+// Workspace regions.  With `shared` (the forward's layout) two regions are
+// reused in place, which keeps the layer's working set small enough to stay
+// in the 256 MB last-level cache at the benchmark size: Y overwrites U (each
+// element of Y = U * (...) is written by the block that read that element of U
+// as its gate), and in the causal case P overwrites S (each lane of the scan
+// reads an entry of S_g before it writes the same entry of P_g).  The
+// backward keeps every region separate (shared = false): it needs U, Y, S and
+// P together.
+void layout(const gau_config* c, gau_ws_layout* L, bool shared = true) {
     const size_t eb = elem_bytes(c->dtype);
     const size_t M = (size_t)(c->B * c->T);
     const size_t G = c->T / c->C;
@@ -54,9 +62,11 @@ void layout(const gau_config* c, gau_ws_layout* L) {
     L->Q_lin = take(M * c->s * eb);
     L->K_lin_t = take(M * c->s * eb);
     L->S = take((size_t)c->B * G * es * eb);
-    L->P = take((size_t)c->B * Gp * es * eb);
     L->A = take(M * (size_t)c->C * eb);
-    L->Y = take(M * c->e * eb);
+    // the regions that may be shared come last, so that every other region
+    // has the same offset in both layouts
+    L->P = (shared && c->causal) ? L->S : take((size_t)c->B * Gp * es * eb);
+    L->Y = shared ? L->U : take(M * c->e * eb);
     L->total = off;
 }
 
@@ -108,9 +118,9 @@ gau::StateParams state_params(const gau_config* c, const gau_ws_layout& L, char*
 // Stages first..last of one layer.  `residual` != nullptr makes the output
 // stage write O = residual + Y W_o in fp32.
 gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs& a, void* O, const float* residual,
-                      char* ws, hipStream_t st) {
+                      char* ws, hipStream_t st, bool shared = true) {
     gau_ws_layout L;
-    layout(c, &L);
+    layout(c, &L, shared);
     const bool bf = c->dtype == GAU_BF16;
     const int M = (int)(c->B * c->T);
     const int G = (int)(c->T / c->C);
@@ -190,7 +200,7 @@ int weight_splits(int64_t M, int64_t tiles) {
 
 void bwd_layout(const gau_config* c, BwdLayout* L) {
     gau_ws_layout F;
-    layout(c, &F);
+    layout(c, &F, false);
     const size_t eb = elem_bytes(c->dtype);
     const size_t M = (size_t)(c->B * c->T), d = c->d, e = c->e, s = c->s, C = c->C;
     const size_t G = c->T / c->C, Z = (size_t)c->B * G, Gp = c->causal ? G : 1;
@@ -271,7 +281,7 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
                         float* dW_v, float* dW_z, float* dW_o, float* dscale, float* doffset, float* drelpos,
                         char* ws, hipStream_t st) {
     gau_ws_layout F;
-    layout(c, &F);
+    layout(c, &F, false);
     BwdLayout L;
     bwd_layout(c, &L);
     const bool bf = c->dtype == GAU_BF16;
@@ -294,7 +304,7 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     // causal diagonal, which the forward leaves unwritten, cleared first)
     if (c->causal && gau::launch_fill_zero((float*)W(F.A), (size_t)Z * CC * eb / 4, st) != hipSuccess)
         return GAU_ERR_HIP;
-    gau_status sres = run_stages(c, GAU_STAGE_PROJ, GAU_STAGE_SCAN, a, nullptr, nullptr, ws, st);
+    gau_status sres = run_stages(c, GAU_STAGE_PROJ, GAU_STAGE_SCAN, a, nullptr, nullptr, ws, st, false);
     if (sres != GAU_OK) return sres;
     // Wq = A V + Q_lin P (into the forward's Y region): the attention stage
     // with a gate of ones

@@ -37,7 +37,7 @@ struct StateParams {
 // Exclusive prefix over chunks (causal) or the total (non-causal).
 struct ScanParams {
     const void* S;   // [B, G, e, s], element type of the layer
-    void* P;         // [B, G, e, s] causal, [B, 1, e, s] otherwise
+    void* P;         // [B, G, e, s] causal (may be S: scanned in place), [B, 1, e, s] otherwise
     int B, G, es;    // es = e * s
     int causal;
 };
@@ -62,7 +62,7 @@ struct AttnParams {
     const void* Vt;   // [B, e, T]
     const void* P;    // [B, G or 1, e, s]
     const void* U;    // [M, e]
-    void* Y;          // [M, e]
+    void* Y;          // [M, e]; may be U (gated in place)
     int B, T, e, s, C;
     int causal;
     int local, global;  // which terms enter Y (the LocalOnly / GlobalOnly variants)

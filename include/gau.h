@@ -118,6 +118,13 @@ enum { GAU_FULL = 0, GAU_LOCAL_ONLY = 1, GAU_GLOBAL_ONLY = 2 };
  *                               (128 wide, 64 when C = 64) are not written
  *   Y       [B*T, e]      dt    U * (V_quad + V_lin)
  *   total   bytes needed (== gau_workspace_bytes)
+ * Two regions are reused in place, so that the layer's intermediates fit the
+ * last-level cache at the benchmark sizes: Y == U (the attention stage
+ * overwrites each element of U with the gated output at the same index), and
+ * when causal P == S (the scan overwrites S_g with P_g).  After a whole
+ * forward those regions hold Y and P; U and S can be read after a
+ * gau_forward_stages range that ends before the attention stage (U) or
+ * before the scan (S).
  */
 typedef struct {
     size_t U, Vt, Q_quad, K_quad, Q_lin, K_lin_t, S, P, A, Y, total;
@@ -234,9 +241,11 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X,
  *   dX [B, T, d];  dW_u, dW_v [e, d], dW_z [s, d], dW_o [d, e] (the layout in
  *   which the weights are passed: output-major);  dscale, doffset [4, s];
  *   drelpos [2C-1].
- * workspace: at least gau_backward_workspace_bytes(cfg) bytes (device
- *   memory; its first gau_workspace_bytes(cfg) bytes hold the forward's
- *   intermediates, as gau_workspace_layout describes, on return).
+ * workspace: at least gau_backward_workspace_bytes(cfg) bytes of device
+ *   memory.  Its start holds the forward's intermediates on return, at the
+ *   offsets gau_workspace_layout gives for U, Vt, the heads, S and A; Y and
+ *   P are kept in regions of their own there (the backward needs U, Y, S and
+ *   P at once), so they are not at the offsets gau_workspace_layout gives.
  * Sums over tokens run in a fixed order: the results are bitwise
  * reproducible for a given cfg and inputs.  B * T == 0: the parameter
  * gradients are set to zero (X, the weights, scale, offset, relpos, dO, dX and

@@ -21,22 +21,40 @@ def torch_dtype(dtype):
 
 
 def run_layer(inp, B, T, d, e, s, C, causal, dtype, quad_scale=None, lin_scale=None, stream=None, rope=False,
-              parts="both"):
-    """Forward on the GPU; returns (O as float64 numpy, workspace tensor, cfg, layout)."""
+              parts="both", stagewise=False):
+    """Forward on the GPU; returns (O as float64 numpy, workspace, cfg, layout).
+
+    The forward reuses two regions in place (Y overwrites U; causal: P
+    overwrites S).  With stagewise=True the workspace returned is the pair
+    (after the full forward, after a second run of the stages up to the chunk
+    states alone), and ws_array reads U and S from the second one."""
     tdt = torch_dtype(dtype)
     dev = g.device_layer(inp, tdt)
     cfg = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32,
                         quad_scale, lin_scale, rope, parts)
     ws = torch.zeros(g.workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
     O = torch.empty((B, T, d), dtype=tdt, device="cuda")
-    g.forward(cfg, dev["X"], dev["W_u"], dev["W_v"], dev["W_z"], dev["W_o"], dev["scale"],
-              dev["offset"], dev["relpos"], O, ws, stream)
+    args = (dev["X"], dev["W_u"], dev["W_v"], dev["W_z"], dev["W_o"], dev["scale"], dev["offset"], dev["relpos"])
+    g.forward(cfg, *args, O, ws, stream)
+    if stagewise:
+        mid = torch.zeros_like(ws)
+        g.forward_stages(cfg, g.STAGE_PROJ, g.STAGE_STATE, *args, torch.empty_like(O), mid, stream=stream)
+        ws = (ws, mid)
     torch.cuda.synchronize()
     return O.float().cpu().numpy().astype(np.float64), ws, cfg, g.workspace_layout(cfg)
 
 
+# regions a later stage of the forward overwrites in place: name -> the region
+# that takes its place
+IN_PLACE = {"U": "Y", "S": "P"}
+
+
 def ws_array(ws, layout, name, shape, dtype):
-    """A workspace region as a float64 numpy array of `shape`."""
+    """A workspace region as a float64 numpy array of `shape` (from the
+    stages-up-to-the-states snapshot when the full forward overwrote it)."""
+    if isinstance(ws, tuple):
+        final, mid = ws
+        ws = mid if (name in IN_PLACE and layout[name] == layout[IN_PLACE[name]]) else final
     n = int(np.prod(shape))
     tdt, eb = torch_dtype(dtype), (2 if dtype == "bf16" else 4)
     off = layout[name]

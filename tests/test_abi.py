@@ -39,13 +39,19 @@ def test_workspace_layout_sizes():
     L = g.workspace_layout(cfg)
     M, e, s, B, G = 2 * 512, 512, 128, 2, 4
     assert L["Vt"] - L["U"] >= M * e * 2
-    assert L["P"] - L["S"] >= B * G * e * s * 2
-    assert L["Y"] - L["P"] >= B * G * e * s * 2
+    assert L["Y"] == L["U"]                             # the gate is applied in place
+    assert L["P"] == L["S"]                             # causal: the scan runs in place
+    assert L["A"] - L["S"] >= B * G * e * s * 2
+    assert L["total"] - L["A"] >= B * G * 128 * 128 * 2
     assert L["total"] == g.workspace_bytes(cfg)
     for k, v in L.items():
         assert v % 256 == 0, k
     nc = g.workspace_layout(_cfg(causal=False))
-    assert nc["Y"] - nc["P"] < L["Y"] - L["P"]          # one total per sequence
+    assert nc["Y"] == nc["U"]
+    assert nc["A"] - nc["S"] >= B * G * e * s * 2       # S kept: the totals overwrite nothing
+    assert nc["P"] - nc["A"] >= B * G * 128 * 128 * 2
+    assert nc["total"] - nc["P"] >= B * 1 * e * s * 2   # one total per sequence
+    assert nc["total"] > L["total"]
     f32 = g.workspace_layout(_cfg(dtype=g.GAU_F32))
     assert f32["total"] > L["total"]
 

@@ -36,6 +36,9 @@ def emu():
     lib.gau_workspace_layout.argtypes = [ctypes.POINTER(GauConfig), ctypes.POINTER(GauWsLayout)]
     lib.gau_forward.argtypes = [ctypes.POINTER(GauConfig)] + [P] * 9 + [P, ctypes.c_size_t, P]
     lib.gau_forward.restype = ctypes.c_int
+    lib.gau_forward_stages.argtypes = [ctypes.POINTER(GauConfig), ctypes.c_int, ctypes.c_int] + [P] * 9 + \
+        [P, ctypes.c_size_t, P]
+    lib.gau_forward_stages.restype = ctypes.c_int
     lib.emu_set_mode.argtypes = [ctypes.c_int, ctypes.c_int]
     return lib
 
@@ -101,9 +104,13 @@ def test_emulated_kernels_match_oracle(emu, case, late):
     raw = np.zeros(wsb + 256, np.uint8)
     ws = raw[(-raw.ctypes.data) % 256:][:wsb]
     ptr = lambda a: ctypes.c_void_p(a.ctypes.data)
-    st = emu.gau_forward(ctypes.byref(cfg), ptr(X), ptr(W["W_u"]), ptr(W["W_v"]), ptr(W["W_z"]), ptr(W["W_o"]),
-                         ptr(sc), ptr(of), ptr(rp), ptr(O), ptr(ws), wsb, None)
-    assert st == 0
+    # the forward in two ranges, so that U and S can be read before the
+    # attention stage gates U into Y in place and the scan turns S into P
+    args = (ptr(X), ptr(W["W_u"]), ptr(W["W_v"]), ptr(W["W_z"]), ptr(W["W_o"]), ptr(sc), ptr(of), ptr(rp), ptr(O),
+            ptr(ws), wsb, None)
+    assert emu.gau_forward_stages(ctypes.byref(cfg), 0, 2, *args) == 0
+    early = ws.copy()
+    assert emu.gau_forward_stages(ctypes.byref(cfg), 3, 5, *args) == 0
     L = GauWsLayout()
     assert emu.gau_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == 0
     ref, im = orc.flash_forward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"],
@@ -115,7 +122,8 @@ def test_emulated_kernels_match_oracle(emu, case, late):
     def region(name, shape):
         n = int(np.prod(shape))
         o = getattr(L, name)
-        return conv(ws[o:o + eb * n].view(np.uint16 if bf else np.float32).reshape(shape)).astype(np.float64)
+        src = early if name in ("U", "S") else ws
+        return conv(src[o:o + eb * n].view(np.uint16 if bf else np.float32).reshape(shape)).astype(np.float64)
 
     tol = 2e-2 if bf else 1e-4
     G = T // C

@@ -70,7 +70,7 @@ SMALL = [
 def test_layer_matches_oracle(case):
     B, T, d, e, s, C, dtype, causal = case
     inp = make(B, T, d, e, s, C, dtype, seed=B * 7919 + T + C)
-    O, ws, cfg, L = run_layer(inp, B, T, d, e, s, C, causal, dtype)
+    O, ws, cfg, L = run_layer(inp, B, T, d, e, s, C, causal, dtype, stagewise=True)
     ref, im = oracle_layer(inp, C, causal, intermediates=True)
     _stagewise(ws, L, im, B, T, e, s, C, causal, dtype)
     assert_close(O, ref, tol_for(dtype), "O")
@@ -90,7 +90,7 @@ ROPE = [
 def test_layer_with_rope_matches_oracle(case):
     B, T, d, e, s, C, dtype, causal = case
     inp = make(B, T, d, e, s, C, dtype, seed=B * 613 + T + C)
-    O, ws, cfg, L = run_layer(inp, B, T, d, e, s, C, causal, dtype, rope=True)
+    O, ws, cfg, L = run_layer(inp, B, T, d, e, s, C, causal, dtype, rope=True, stagewise=True)
     ref, im = oracle_layer(inp, C, causal, intermediates=True, rope=True)
     _stagewise(ws, L, im, B, T, e, s, C, causal, dtype)
     assert_close(O, ref, tol_for(dtype), "O")
