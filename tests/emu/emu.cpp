@@ -228,6 +228,9 @@ void run_block_full(int nt) {
         }
         if (done == nt) break;
         if (done + bar != nt) fail("scheduler: lanes neither done nor at the barrier");
+        // every wave must pass the same number of barriers: a lane that has
+        // finished while others wait at a barrier means the counts differ
+        if (done != 0) fail("barrier count mismatch: %d lanes done, %d at a barrier", done, bar);
         for (int t = 0; t < nt; ++t)
             if (g_lanes[t].state == AT_BARRIER) g_lanes[t].state = READY;
     }

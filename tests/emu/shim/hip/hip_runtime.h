@@ -75,6 +75,7 @@ using std::min;
 #define __builtin_amdgcn_s_waitcnt(imm) ::emu::s_waitcnt(imm)
 #define __builtin_amdgcn_sched_group_barrier(a, b, c) ((void)0)
 #define __builtin_amdgcn_s_barrier() ::emu::syncthreads()
+#define __builtin_amdgcn_sched_barrier(m) ((void)0)
 #define __builtin_amdgcn_rcpf(x) (1.0f / (x))
 
 #define hipFuncSetAttribute(f, attr, v) ::emu::func_set_attr((const void*)(f), attr, v)
