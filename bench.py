@@ -138,6 +138,25 @@ COPY_BYTES = 256 << 20
 PROFILE_TAG = "B2_T8192_d768_C256"
 
 
+def mfma_probe(torch, g, blocks=1024, iters=1000, reps=5):
+    """The bf16 MFMA rate the chip sustains with operands in registers
+    (gau_probe_mfma): median over reps launches, each timed with HIP events.
+    Outside the timed region; the layer is also quoted against it."""
+    out = torch.zeros(1, dtype=torch.float32, device="cuda")
+    g.probe_mfma(blocks, iters, out)  # warm-up
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        flops = g.probe_mfma(blocks, iters, out)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    t = float(np.median(times))
+    return {"tflops": flops / t / 1e12, "frac_of_published": flops / t / 1e12 / PEAK_BF16_TFLOPS,
+            "flops_per_launch": flops, "ms": t * 1e3, "blocks": blocks, "iters": iters}
+
+
 def copy_calibration(torch):
     """Three plain device-to-device copies of COPY_BYTES (torch's copy_ of a
     contiguous tensor runs the HIP runtime's copyBuffer blit kernel): the HBM
@@ -671,6 +690,10 @@ def main():
                            "each); the kernel trace gives the durations inside one forward",
         "ms_per_step_single_call": wall_plain * 1e3 / K,
     }
+    probe = mfma_probe(torch, g)
+    out["mfma_probe"] = probe
+    out["roofline"]["frac_of_probe"] = achieved / probe["tflops"]
+    out["layer_frac_of_probe"] = out["layer_tflops"] / probe["tflops"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(out), flush=True)

@@ -23,11 +23,12 @@ STATUS = {
     4: "GAU_ERR_DTYPE", 5: "GAU_ERR_WORKSPACE", 6: "GAU_ERR_HIP",
 }
 
-# Every symbol include/gau.h declares.
+# Every symbol include/gau.h and include/gau_probe.h declare.
 EXPORTS = (
     "gau_workspace_bytes", "gau_workspace_layout", "gau_forward", "gau_forward_stages",
     "gau_stack_workspace_bytes", "gau_stack_forward", "gau_decode_workspace_bytes", "gau_decode_reset",
     "gau_decode_step", "gau_rope_relpos", "gau_backward_workspace_bytes", "gau_backward", "gau_status_string",
+    "gau_probe_mfma",
 )
 
 
@@ -96,6 +97,8 @@ def load():
     lib.gau_backward.restype = ctypes.c_int
     lib.gau_status_string.argtypes = [ctypes.c_int]
     lib.gau_status_string.restype = ctypes.c_char_p
+    lib.gau_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
+    lib.gau_probe_mfma.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -222,6 +225,17 @@ def stack_forward(cfg, X, layers, workspace, stream=None):
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if st != 0:
         raise GauError(st, "gau_stack_forward")
+
+
+def probe_mfma(blocks, iters, out, stream=None):
+    """gau_probe_mfma (measurement aid, gau_probe.h): queues the register-only
+    MFMA probe; returns its FLOPs per launch.  `out` is a device fp32 tensor."""
+    import torch
+    _check(out, "out", torch.float32, 1)
+    st = load().gau_probe_mfma(int(blocks), int(iters), _ptr(out), _stream(stream))
+    if st != 0:
+        raise GauError(st, "gau_probe_mfma")
+    return float(blocks) * 4 * iters * 16 * 32768
 
 
 def rope_relpos(a, b, n, out=None, stream=None):

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    txt = open(os.path.join(ROOT, "include", "gau.h")).read()
+    inc = os.path.join(ROOT, "include")
+    txt = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(gau_[a-z_]+)\s*\(", txt)))
 
@@ -196,3 +197,13 @@ def test_status_strings():
     for code in range(7):
         assert g.status_string(code)
     assert g.status_string(99) == "unknown status"
+
+
+def test_mfma_probe_rejects_bad_arguments():
+    """The measurement probe checks its arguments before any launch."""
+    lib = g.load()
+    assert lib.gau_probe_mfma(0, 10, None, None) == 2            # GAU_ERR_SHAPE
+    assert lib.gau_probe_mfma(16, 0, None, None) == 2
+    assert lib.gau_probe_mfma(16, (1 << 20) + 1, None, None) == 2
+    assert lib.gau_probe_mfma(16, 10, None, None) == 1           # GAU_ERR_NULL
+    assert lib.gau_probe_mfma(16, 10, ctypes.c_void_p(8), None) == 3  # GAU_ERR_ALIGN
