@@ -21,9 +21,10 @@
 // in one section and its epilogue branch is uniform).  The Z blocks are
 // dispatched first and cost half a U/V tile each, so the launch is about an
 // eighth of a round longer than U and V alone instead of a second launch of
-// small, latency-bound blocks.  U/V tiles are assigned to XCDs in contiguous
-// ranges (the 2e/256 column tiles of one token tile together, so they share
-// the X tile in one L2).
+// small, latency-bound blocks.  U/V tiles are assigned to XCDs so that
+// tiles sharing operand rows share an L2: at e = 1536 each XCD takes half of
+// the column tiles for a quarter of the token tiles; otherwise contiguous
+// ranges (the 2e/256 column tiles of one token tile together).
 #include "gau_launch.h"
 #include "gemm_core.h"
 
@@ -255,10 +256,27 @@ __global__ __launch_bounds__(512) void proj_kernel(ProjParams p) {
     extern __shared__ __align__(16) char lds[];
     const int nz = ZR > 0 ? 0 : (p.s / ZF) * ((p.M + ZT - 1) / ZT);
     const int b = blockIdx.x;
-    if (b < nz)
+    if (b < nz) {
         z_tile<T>(p, b, lds);
-    else
+        return;
+    }
+    const int ntiles = 2 * (p.e / BN);
+    const int mtiles = (p.M + BM - 1) / BM;
+    if (ZR > 0 && ntiles == 12 && mtiles % 4 == 0) {
+        // XCD x (dispatch index % 8) takes half of the column tiles (each half
+        // with two of the four tiles that carry a Z slice) and a quarter of
+        // the token tiles: its six weight tiles (2.4 MB at d = 768) stay in
+        // its 4 MB L2 while its token tiles stream through, where a range of
+        // whole token tiles would cycle all twelve weight tiles through it
+        // every round (165 -> 113 MB fetched per launch at B*T = 16384).
+        constexpr int kHalf[2][6] = {{0, 1, 4, 6, 7, 8}, {2, 3, 5, 9, 10, 11}};
+        const int u = b - nz;
+        const int x = u & 7, j = u >> 3;
+        const int t = (x >> 1) * (mtiles / 4) + j / 6;
+        uv_tile<T, ZR>(p, t * ntiles + kHalf[x & 1][j % 6], lds);
+    } else {
         uv_tile<T, ZR>(p, xcd_remap(b - nz, gridDim.x - nz), lds);
+    }
 }
 
 template <typename T, int ZR>
