@@ -62,6 +62,8 @@ SMALL = [
     (1, 256, 128, 1024, 128, 64, "f32", True),     # e >= 1024: Z formed inside the U tiles
     (1, 320, 256, 1024, 256, 64, "bf16", False),   # ... with s = 256 and a ragged row tile
     (2, 256, 128, 1280, 128, 128, "bf16", True),
+    (1, 960, 128, 1536, 128, 64, "bf16", True),    # e = 1536: column halves per XCD, ragged last token tile
+    (2, 512, 128, 1536, 128, 128, "f32", True),    # e = 1536 in fp32, four token tiles
 ]
 
 
