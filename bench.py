@@ -356,10 +356,11 @@ def sweep(steps, warmup):
 
 def decode_bytes(B, d, e, s, C, eb=2):
     """Algorithmic HBM bytes of one decoding step averaged over a chunk: every
-    weight once, and per sequence the fp32 state P, the chunk cache rows read
-    so far (on average (C+1)/2 slots) and the step's own rows written."""
+    weight once, and per sequence the state P as the steps read it (its copy in
+    the element type), the chunk cache rows read so far (on average (C+1)/2
+    slots) and the step's own rows written."""
     weights = (2 * e + s) * d * eb + e * d * eb
-    per_seq = s * e * 4 + (C + 1) / 2 * (e + s) * eb + (e + 2 * s) * eb + 2 * d * eb
+    per_seq = s * e * eb + (C + 1) / 2 * (e + s) * eb + (e + 2 * s) * eb + 2 * d * eb
     return weights + B * per_seq
 
 

@@ -18,7 +18,11 @@
 // tokens the projection and output products are GEMVs that read every
 // weight once per tile of 8 tokens (one half wave per weight row); from
 // MFMA_MIN_B on they run on the shared MFMA core as GEMMs with 64-token
-// tiles.  The attention kernel reads the chunk's cached rows and P.
+// tiles.  The attention kernel reads the chunk's cached rows and P in the
+// layer's element type: the fp32 state is rounded into that copy once per
+// chunk, at its update (for bf16 this halves the state bytes every step
+// reads, the bulk of a step's traffic at large batch, and matches the
+// forward, whose prefix states are rounded to the element type too).
 #include "gau_device.h"
 #include "gau_launch.h"
 #include "gemm_core.h"
@@ -253,11 +257,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
             for (int u = 0; u < 8; ++u) quad += alpha[tau + 4 * u] * v[u];
         }
         for (; tau <= jl; tau += 4) quad += alpha[tau] * ld1<T>(V + (size_t)tau * vs);
-        const float* P = p.P + (size_t)b * p.s * p.e + f;
+        // the state in the element type (the copy rounded at each chunk end)
+        const char* P = (const char*)p.Pr + ((size_t)b * p.s * p.e + f) * EB;
         for (int i = g; i < (p.global ? p.s : 0); i += 32) {  // s is a multiple of 128
             float w[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) w[u] = P[(size_t)(i + 4 * u) * p.e];
+            for (int u = 0; u < 8; ++u) w[u] = ld1<T>(P + (size_t)(i + 4 * u) * p.e * EB);
 #pragma unroll
             for (int u = 0; u < 8; ++u) lin += ql[i + 4 * u] * w[u];
         }
@@ -339,7 +344,12 @@ __global__ __launch_bounds__(256) void decode_state_kernel(DecodeParams p) {
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
             const int f = f0 + tx + 16 * cc;
-            if (f < p.e) p.P[((size_t)b * p.s + i0 + ty + 16 * rr) * p.e + f] += p.ls * acc[rr][cc];
+            if (f < p.e) {
+                const size_t k = ((size_t)b * p.s + i0 + ty + 16 * rr) * p.e + f;
+                const float x = p.P[k] + p.ls * acc[rr][cc];
+                p.P[k] = x;
+                if constexpr (EB == 2) Elem<T>::put((char*)p.Pr + k * EB, x);  // the copy the steps read
+            }
         }
 }
 

@@ -88,7 +88,7 @@ gau_status check_layer_ptrs(const LayerPtrs& a) {
 // Decoding workspace: the state (P fp32, the chunk cache in the element type)
 // and the per-step fp32 scratch.
 struct DecodeLayout {
-    size_t P, Kq, V, Kl, u, z, y, total;
+    size_t P, Pr, Kq, V, Kl, u, z, y, total;
 };
 
 void decode_layout(const gau_config* c, DecodeLayout* D) {
@@ -101,6 +101,7 @@ void decode_layout(const gau_config* c, DecodeLayout* D) {
         return o;
     };
     D->P = take(B * s * e * 4);
+    D->Pr = eb == 4 ? D->P : take(B * s * e * eb);  // the copy the steps read
     D->Kq = take(B * C * s * eb);
     D->V = take(B * C * e * eb);
     D->Kl = take(B * C * s * eb);
@@ -568,6 +569,10 @@ gau_status gau_decode_reset(const gau_config* cfg, void* workspace, size_t works
     const size_t n = (size_t)cfg->B * cfg->s * cfg->e;
     if (gau::launch_fill_zero((float*)((char*)workspace + D.P), n, (hipStream_t)stream) != hipSuccess)
         return GAU_ERR_HIP;
+    if (D.Pr != D.P &&  // the element-type copy (2-byte elements: n / 2 words, s * e is even)
+        gau::launch_fill_zero((float*)((char*)workspace + D.Pr), n * elem_bytes(cfg->dtype) / 4,
+                              (hipStream_t)stream) != hipSuccess)
+        return GAU_ERR_HIP;
     return GAU_OK;
 }
 
@@ -587,7 +592,7 @@ gau_status gau_decode_step(const gau_config* cfg, int64_t t, const void* x, cons
     if (workspace_bytes < D.total) return GAU_ERR_WORKSPACE;
     char* ws = (char*)workspace;
     const gau::DecodeParams p{x, W_u, W_v, W_z, W_o, scale, offset, relpos, o,
-                              (float*)(ws + D.P), ws + D.Kq, ws + D.V, ws + D.Kl,
+                              (float*)(ws + D.P), ws + D.Pr, ws + D.Kq, ws + D.V, ws + D.Kl,
                               (float*)(ws + D.u), (float*)(ws + D.z), ws + D.y, (int)cfg->B, (int)cfg->d, (int)cfg->e, (int)cfg->s, (int)cfg->C,
                               (int)t, (int)(t % cfg->C), cfg->rope, cfg->quad_scale, cfg->lin_scale,
                               cfg->ablation != GAU_GLOBAL_ONLY, cfg->ablation != GAU_LOCAL_ONLY};

@@ -109,6 +109,8 @@ struct DecodeParams {
     const float* relpos;  // [2C-1]
     void* o;            // [B, d]
     float* P;           // [B, s, e] fp32 state: completed chunks' summaries
+    void* Pr;           // [B, s, e] the state in the element type, as the steps read it
+                        // (bf16: rounded from P at each chunk end; fp32: P itself)
     void* Kq;           // [B, C, s] chunk cache
     void* V;            // [B, C, e]
     void* Kl;           // [B, C, s]

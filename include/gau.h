@@ -281,8 +281,9 @@ gau_status gau_backward(const gau_config* cfg, const void* X,
  * cfg: as gau_forward with causal = 1 (else GAU_ERR_SHAPE); cfg->T bounds the
  *   positions (0 <= t < T); B is the number of sequences decoded together.
  * workspace: at least gau_decode_workspace_bytes(cfg) bytes of device memory
- *   holding the state (P as [B, s, e] fp32; the chunk's K_quad and K_lin rows
- *   [B, C, s] and V rows [B, C, e] in cfg->dtype) and per-step scratch.  It
+ *   holding the state (P as [B, s, e] fp32, and for bf16 its copy rounded to
+ *   bf16 at each chunk end, which the steps read; the chunk's K_quad and K_lin
+ *   rows [B, C, s] and V rows [B, C, e] in cfg->dtype) and per-step scratch.  It
  *   must be reset (gau_decode_reset) before t = 0, and each call must follow
  *   the call for t - 1 on the same workspace (not checked: the library keeps
  *   no position).

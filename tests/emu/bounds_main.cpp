@@ -83,6 +83,7 @@ static void run(const Cfg& c, const std::string& only) {
     void* dx = buf((size_t)c.B * c.d * eb);
     void* dO = buf((size_t)c.B * c.d * eb);
     float* dP = (float*)buf((size_t)c.B * c.s * c.e * 4);
+    void* dPr = c.bf ? buf((size_t)c.B * c.s * c.e * eb) : (void*)dP;  // the copy the steps read
     void* dKq = buf((size_t)c.B * c.C * c.s * eb);
     void* dV = buf((size_t)c.B * c.C * c.e * eb);
     void* dKl = buf((size_t)c.B * c.C * c.s * eb);
@@ -91,7 +92,7 @@ static void run(const Cfg& c, const std::string& only) {
     void* dy = buf((size_t)c.B * c.e * eb);
     if (c.causal) {
         for (int pos : {0, c.C - 1}) {
-            DecodeParams dp{dx, Wu, Wv, Wz, Wo, sc, of, rp, dO, dP, dKq, dV, dKl, du, dz, dy,
+            DecodeParams dp{dx, Wu, Wv, Wz, Wo, sc, of, rp, dO, dP, dPr, dKq, dV, dKl, du, dz, dy,
                             c.B, c.d, c.e, c.s, c.C, pos, pos % c.C, 1, 1.0f / c.C, 1.0f / c.C, 1, 1};
             t(pos == 0 ? "decode_step_j0" : "decode_step_jlast",
               [&] { CHECK(launch_decode_step(dp, c.bf, nullptr)); });
