@@ -59,6 +59,43 @@ __device__ __forceinline__ float ld1<float>(const char* p) {
     return *(const float*)p;
 }
 
+// Eight consecutive elements (16-byte aligned) as floats, and back (bf16:
+// round to nearest even, as Elem<bf16>::put).
+template <typename T>
+__device__ __forceinline__ void ld8(const char* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void ld8<bf16>(const char* p, float (&v)[8]) {
+    const u32x4_t w = *(const u32x4_t*)p;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __uint_as_float(w[k] << 16);
+        v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void ld8<float>(const char* p, float (&v)[8]) {
+    const f32x4_t a = *(const f32x4_t*)p, c = *(const f32x4_t*)(p + 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        v[k] = a[k];
+        v[4 + k] = c[k];
+    }
+}
+template <typename T>
+__device__ __forceinline__ void st8(char* p, const float (&v)[8]);
+template <>
+__device__ __forceinline__ void st8<bf16>(char* p, const float (&v)[8]) {
+    u32x4_t w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
+    *(u32x4_t*)p = w;
+}
+template <>
+__device__ __forceinline__ void st8<float>(char* p, const float (&v)[8]) {
+    *(f32x4_t*)p = f32x4_t{v[0], v[1], v[2], v[3]};
+    *(f32x4_t*)(p + 16) = f32x4_t{v[4], v[5], v[6], v[7]};
+}
+
 // Four consecutive elements as floats.
 template <typename T>
 __device__ __forceinline__ void ld4(const char* p, float (&v)[4]) {
@@ -163,17 +200,44 @@ __device__ __forceinline__ float as_stored<float>(float x) {
     return x;
 }
 
-// The token's four heads, and y = u * (quad + q_lin P) for 64 of its
+// FV consecutive elements as floats, and back.
+template <typename T, int FV>
+__device__ __forceinline__ void ldn(const char* p, float (&v)[FV]) {
+    if constexpr (FV == 8) {
+        ld8<T>(p, v);
+    } else {
+        static_assert(FV == 1, "1 or 8 features per thread");
+        v[0] = ld1<T>(p);
+    }
+}
+template <typename T, int FV>
+__device__ __forceinline__ void stn(char* p, const float (&v)[FV]) {
+    if constexpr (FV == 8) {
+        st8<T>(p, v);
+    } else {
+#pragma unroll
+        for (int k = 0; k < FV; ++k) Elem<T>::put(p + k * Elem<T>::kBytes, v[k]);
+    }
+}
+
+// The token's four heads, and y = u * (quad + q_lin P) for 64 * FV of its
 // features.  Every block of the token forms the heads from z (s/2 pairs,
 // turned by position t with RoPE on) into LDS, uses its own K_quad for the
 // score of slot j, and the first block writes K_quad and K_lin into the
-// cache slot.  The 256 threads then form 4 groups that split the sums over
-// the chunk slots and the state rows.
-template <typename T>
+// cache slot.  The 256 threads then form 4 groups of 64 that split the sums
+// over the chunk slots and the state rows; a thread owns FV consecutive
+// features, read as one vector per slot or state row.  More features per
+// block (FV = 8: 16-byte loads, e/512 blocks per token) cut the score work,
+// which every block of a token repeats, and the load instructions; fewer
+// (FV = 1: e/64 blocks per token) spread a small batch over more CUs.
+// Measured per step at d=768, e=1536, C=256, bf16 (FV = 1 / 8): B=1 21.8 /
+// 24.3 us, B=32 37.1 / 38.9, B=128 67.5 / 48.9.
+template <typename T, int FV>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
     constexpr int EB = Elem<T>::kBytes;
-    constexpr int FT = 64;
-    constexpr int PARTS = 2 * 4 * FT;  // [quad | lin][group][feature]
+    constexpr int FT = 64 * FV;            // features per block
+    constexpr int RIF = FV == 1 ? 8 : 4;   // rows in flight per thread
+    constexpr int PARTS = 2 * 4 * FT;      // [quad | lin][group][feature]
     __shared__ float alpha[512];
     __shared__ float qq[256];
     __shared__ float ql[256];
@@ -241,43 +305,60 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
         alpha[tau] = x > 0.f ? x * x : 0.f;
     }
     __syncthreads();
-    const int g = tid / FT, fl = tid % FT;
-    const int f = f0 + fl;
-    float quad = 0.f, lin = 0.f;
+    const int g = tid / 64, fl = tid % 64;  // group, thread inside the group
+    const int f = f0 + fl * FV;             // first of this thread's 8 features
+    float quad[FV] = {}, lin[FV] = {};
     if (f < p.e) {
         const char* V = (const char*)p.V + ((size_t)b * p.C * p.e + f) * EB;
         const size_t vs = (size_t)p.e * EB;
         const int jl = p.local ? j : -1;  // last slot of the local term
         int tau = g;
-        for (; tau + 28 <= jl; tau += 32) {  // eight independent loads in flight
-            float v[8];
+        for (; tau + 4 * (RIF - 1) <= jl; tau += 4 * RIF) {  // RIF rows in flight
+            float v[RIF][FV];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = ld1<T>(V + (size_t)(tau + 4 * u) * vs);
+            for (int u = 0; u < RIF; ++u) ldn<T, FV>(V + (size_t)(tau + 4 * u) * vs, v[u]);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) quad += alpha[tau + 4 * u] * v[u];
+            for (int u = 0; u < RIF; ++u)
+#pragma unroll
+                for (int k = 0; k < FV; ++k) quad[k] += alpha[tau + 4 * u] * v[u][k];
         }
-        for (; tau <= jl; tau += 4) quad += alpha[tau] * ld1<T>(V + (size_t)tau * vs);
+        for (; tau <= jl; tau += 4) {
+            float v[FV];
+            ldn<T, FV>(V + (size_t)tau * vs, v);
+#pragma unroll
+            for (int k = 0; k < FV; ++k) quad[k] += alpha[tau] * v[k];
+        }
         // the state in the element type (the copy rounded at each chunk end)
         const char* P = (const char*)p.Pr + ((size_t)b * p.s * p.e + f) * EB;
-        for (int i = g; i < (p.global ? p.s : 0); i += 32) {  // s is a multiple of 128
-            float w[8];
+        for (int i = g; i < (p.global ? p.s : 0); i += 4 * RIF) {  // s is a multiple of 128
+            float w[RIF][FV];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) w[u] = ld1<T>(P + (size_t)(i + 4 * u) * p.e * EB);
+            for (int u = 0; u < RIF; ++u) ldn<T, FV>(P + (size_t)(i + 4 * u) * p.e * EB, w[u]);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) lin += ql[i + 4 * u] * w[u];
+            for (int u = 0; u < RIF; ++u)
+#pragma unroll
+                for (int k = 0; k < FV; ++k) lin[k] += ql[i + 4 * u] * w[u][k];
         }
     }
-    part[g * FT + fl] = quad;
-    part[4 * FT + g * FT + fl] = lin;
+#pragma unroll
+    for (int k = 0; k < FV; ++k) {
+        part[g * FT + fl * FV + k] = quad[k];
+        part[4 * FT + g * FT + fl * FV + k] = lin[k];
+    }
     __syncthreads();
     if (g == 0 && f < p.e) {
-        float q = 0.f, l = 0.f;
+        float y[FV];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {  // fixed order: 0, 1, 2, 3
-            q += part[k * FT + fl];
-            l += part[4 * FT + k * FT + fl];
+        for (int k = 0; k < FV; ++k) {
+            float q = 0.f, l = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {  // fixed order: 0, 1, 2, 3
+                q += part[gg * FT + fl * FV + k];
+                l += part[4 * FT + gg * FT + fl * FV + k];
+            }
+            y[k] = p.u[(size_t)b * p.e + f + k] * (q + l);
         }
-        Elem<T>::put((char*)p.y + ((size_t)b * p.e + f) * EB, p.u[(size_t)b * p.e + f] * (q + l));
+        stn<T, FV>((char*)p.y + ((size_t)b * p.e + f) * EB, y);
     }
 }
 
@@ -410,6 +491,10 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* x, size_t n) {
     if (k < n) x[k] = 0.f;
 }
 
+// 8 features per thread in the attention kernel once that grid (B * e / 512
+// blocks) still gives every one of the 256 CUs a block.
+bool attn_wide(int B, int e) { return (long)B * ((e + 511) / 512) >= 256; }
+
 template <typename T>
 hipError_t step(const DecodeParams& p, hipStream_t st) {
     const bool mfma = p.B >= MFMA_MIN_B;
@@ -423,7 +508,12 @@ hipError_t step(const DecodeParams& p, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_attn_kernel<T>, dim3((unsigned)(p.B * ((p.e + 63) / 64))), dim3(256), 0, st, p);
+    if (attn_wide(p.B, p.e))
+        hipLaunchKernelGGL((decode_attn_kernel<T, 8>), dim3((unsigned)(p.B * ((p.e + 511) / 512))), dim3(256), 0, st,
+                           p);
+    else
+        hipLaunchKernelGGL((decode_attn_kernel<T, 1>), dim3((unsigned)(p.B * ((p.e + 63) / 64))), dim3(256), 0, st,
+                           p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (mfma) {
         constexpr int LDS = GemmCore<T, 32, 64, 1, 2>::LDS_BYTES;

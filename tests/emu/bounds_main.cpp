@@ -65,7 +65,7 @@ static void run(const Cfg& c, const std::string& only) {
     void* O = buf(M * c.d * eb);
     float* Of = (float*)buf(M * c.d * 4);
     auto t = [&](const char* name, auto fn) {
-        if (!only.empty() && only != name) return;
+        if (!only.empty() && std::string(name).compare(0, only.size(), only) != 0) return;  // prefix match
         double t0 = now();
         fn();
         fprintf(stderr, "  %-12s ok (%.1f s)\n", name, now() - t0);
@@ -174,6 +174,11 @@ int main(int argc, char** argv) {
         // batches that decode on the MFMA core (one ragged and two token tiles)
         {17, 64, 128, 256, 128, 64, true, true},     {70, 64, 128, 512, 256, 64, false, true},
     };
+    // batches whose decoding attention takes 8 features per thread (decoding
+    // launches only)
+    std::vector<Cfg> decode_wide = {
+        {96, 64, 128, 1536, 128, 64, false, true}, {176, 64, 128, 1536, 128, 64, true, true},
+    };
     std::vector<Cfg> full = {
         {8, 1024, 768, 1536, 128, 256, true, true}, {4, 4096, 768, 1536, 128, 256, true, true},
         {4, 4096, 768, 1536, 128, 256, true, false}, {2, 8192, 768, 1536, 128, 512, true, true},
@@ -181,8 +186,11 @@ int main(int argc, char** argv) {
     };
     const std::string which = argc > 1 ? argv[1] : "small";
     const std::string only = argc > 2 ? argv[2] : "";
-    if (which == "small" || which == "all")
+    if (which == "small" || which == "all") {
         for (auto& c : small) run(c, only);
+        if (only.empty() || only.compare(0, 6, "decode") == 0)
+            for (auto& c : decode_wide) run(c, only.empty() ? "decode" : only);
+    }
     if (which == "full" || which == "all")
         for (auto& c : full) run(c, only);
     if (which == "headline") run(full.back(), only);

@@ -45,6 +45,8 @@ CASES = [
     (9, 128, 128, 256, 128, 64, "f32", 128, True),     # B > 8: two token tiles per weight row
     (20, 128, 128, 256, 128, 64, "bf16", 128, False),  # B >= 3: the products on the MFMA core
     (70, 128, 256, 512, 256, 64, "f32", 70, True),     # ... two token tiles, the second ragged
+    (96, 128, 128, 1536, 128, 64, "f32", 128, False),   # attention with 8 features per thread
+    (176, 128, 128, 1536, 128, 64, "bf16", 128, True),  # ... bf16 (16-byte loads), RoPE
 ]
 
 
