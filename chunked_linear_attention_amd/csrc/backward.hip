@@ -68,13 +68,6 @@ __device__ __forceinline__ void store8(void* p, int64_t i, const float (&v)[8]) 
     }
 }
 
-// d SiLU(h) / dh = sigma(h) (1 + h (1 - sigma(h))), fp32 with the hardware
-// exponential and reciprocal (as the forward's SiLU).
-__device__ __forceinline__ float silu_grad(float h) {
-    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h));
-    return sg * (1.0f + h * (1.0f - sg));
-}
-
 // C[z] = alpha * (A[z] B[z]^T + A2[z] B2[z]^T) on BT x BT tiles, then the
 // epilogue EPI (GemmNTParams).
 template <typename T, int BT, int EPI>
@@ -131,23 +124,9 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmNTParams q) {
             const int64_t i = cb + (int64_t)r * q.c_rp + c;
             load8<T>(q.H, i, h);
             float o[8];
-            if constexpr (EPI == EPI_SILU) {
+            static_assert(EPI == EPI_SILU, "epilogues: store, SiLU derivative");
 #pragma unroll
-                for (int u = 0; u < 8; ++u) o[u] = v[u] * silu_grad(h[u]);
-            } else {  // EPI_GATE: v = dY
-                const int64_t j = (int64_t)(m0 + r) * q.g_rp + n0 + c;
-                float w[8], g[8], a[8], y[8];
-                load8<T>(q.G0, j, w);
-                load8<T>(q.G1, j, g);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    a[u] = v[u] * g[u];
-                    y[u] = g[u] * w[u];
-                    o[u] = v[u] * w[u] * silu_grad(h[u]);
-                }
-                store8<T>(q.O0, j, a);
-                store8<T>(q.O1, j, y);
-            }
+            for (int u = 0; u < 8; ++u) o[u] = v[u] * silu_grad(h[u]);
             store8<T>(q.C, i, o);
         }
     }
@@ -357,7 +336,6 @@ hipError_t gemm_go(const GemmNTParams& q, unsigned blocks, hipStream_t st) {
     switch (q.epi) {
         case EPI_STORE: return gemm_go1<T, BT, EPI_STORE>(q, blocks, st);
         case EPI_SILU: return gemm_go1<T, BT, EPI_SILU>(q, blocks, st);
-        case EPI_GATE: return gemm_go1<T, BT, EPI_GATE>(q, blocks, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -171,7 +171,8 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
                 break;
             }
             case GAU_STAGE_OUT: {
-                gau::OutParams p{ws + L.Y, a.W_o, O, residual, M, (int)c->d, (int)c->e};
+                gau::OutParams p{ws + L.Y, a.W_o, O, residual, M, (int)c->d, (int)c->e, 0, 0,
+                                 nullptr, nullptr, nullptr, nullptr, nullptr, 0};
                 e = gau::launch_out_gemm(p, bf, st);
                 break;
             }
@@ -316,24 +317,23 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         ok(gau::launch_chunk_attn(p, bf, st));
     }
     // pre-activations H = X [W_u | W_v | W_z]
-    gemm(nt(a.X, 0, d, a.W_u, 0, d, W(L.H), 0, W3, d, false), M, e, 1);
-    gemm(nt(a.X, 0, d, a.W_v, 0, d, Wc(L.H, e), 0, W3, d, false), M, e, 1);
+    // (U and V on the output GEMM's tiles: rows of X times rows of W_u, W_v, K = d)
+    ok(gau::launch_out_gemm(
+        gau::OutParams{a.X, a.W_u, W(L.H), nullptr, M, e, d, 0, W3, nullptr, nullptr, nullptr, nullptr, nullptr, 0}, bf,
+        st));
+    ok(gau::launch_out_gemm(
+        gau::OutParams{a.X, a.W_v, Wc(L.H, e), nullptr, M, e, d, 0, W3, nullptr, nullptr, nullptr, nullptr, nullptr, 0},
+        bf, st));
     gemm(nt(a.X, 0, d, a.W_z, 0, d, Wc(L.H, 2 * e), 0, W3, d, false), M, s, 1);
 
     // O = Y W_o and the gate Y = U * Wq: dY = dO W_o^T, fused with
     // dWq = dY * U, Y, and dH_u = dY * Wq * SiLU'(H_u)
     trans(tp(a.W_o, 0, e, W(L.WoT), 0, d), d, e, 1);
-    {
-        gau::GemmNTParams q = nt(dO, 0, d, W(L.WoT), 0, d, W(L.dH), 0, W3, d, false);
-        q.epi = gau::EPI_GATE;
-        q.H = W(L.H);
-        q.G0 = W(F.Y);
-        q.G1 = W(F.U);
-        q.O0 = W(L.dWq);
-        q.O1 = W(L.Yb);
-        q.g_rp = e;
-        gemm(q, M, e, 1);
-    }
+    // (on the output GEMM's tiles: rows of dO times rows of W_o, K = d, with
+    // the gate epilogue)
+    ok(gau::launch_out_gemm(gau::OutParams{dO, W(L.WoT), W(L.dH), nullptr, M, e, d, 0, W3, W(L.H), W(F.Y), W(F.U),
+                                           W(L.dWq), W(L.Yb), e},
+                            bf, st));
     // token-major V and K_lin; chunk-transposed heads, weights and dWq
     trans(tp(W(F.Vt), (int64_t)e * T, T, W(L.V), (int64_t)T * e, e), e, T, Bn);
     trans(tp(W(F.K_lin_t), (int64_t)s * T, T, W(L.Kl), (int64_t)T * s, s), s, T, Bn);
@@ -399,7 +399,10 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     trans(tp(a.W_u, 0, d, W(L.Wt), 0, W3), e, d, 1);
     trans(tp(a.W_v, 0, d, Wc(L.Wt, e), 0, W3), e, d, 1);
     trans(tp(a.W_z, 0, d, Wc(L.Wt, 2 * e), 0, W3), s, d, 1);
-    gemm(nt(W(L.dH), 0, W3, W(L.Wt), 0, W3, dX, 0, d, W3, true), M, d, 1);
+    // (the output GEMM's form: rows of dH times rows of W^T, K = 2e + s)
+    ok(gau::launch_out_gemm(gau::OutParams{W(L.dH), W(L.Wt), dX, nullptr, M, d, W3, 1, 0, nullptr, nullptr, nullptr,
+                                           nullptr, nullptr, 0},
+                            bf, st));
 
     // weight gradients, K = M split L.split_* ways into fp32 partials added in
     // split order: dW_o (stored [d, e]) = dO^T Y, [dW_u | dW_v | dW_z] = dH^T X

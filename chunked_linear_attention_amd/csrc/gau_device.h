@@ -55,6 +55,13 @@ template <> struct Elem<float> {
 // x * 0 = -0, the correctly rounded limit.
 __device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
+// d SiLU(h) / dh = sigma(h) (1 + h (1 - sigma(h))), fp32 with the hardware
+// exponential and reciprocal (as SiLU).
+__device__ __forceinline__ float silu_grad(float h) {
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h));
+    return sg * (1.0f + h * (1.0f - sg));
+}
+
 // Rotary frequency of pair i of a head of width 2 * half: 10000^(-i / half),
 // in fp64 (angles t * theta reach about 10^4 rad).
 __device__ __forceinline__ double rope_theta(int i, int half) { return pow(10000.0, -(double)i / (double)half); }

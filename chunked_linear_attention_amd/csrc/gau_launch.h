@@ -72,9 +72,20 @@ struct AttnParams {
 struct OutParams {
     const void* Y;     // [M, e]
     const void* W_o;   // [d, e]  (W_o transposed)
-    void* O;           // [M, d]  element type of the layer, or fp32 when residual
+    void* O;           // [M, d]  element type of the layer, or fp32 when residual or f32_out
     const float* residual;  // [M, d] fp32 or nullptr
     int M, d, e;
+    int f32_out;       // O in fp32 without a residual (the backward's dX = dH W^T)
+    int o_rp;          // elements between rows of O (and of residual); 0: d
+    // gate epilogue of the backward (when gU != nullptr), with v = the product
+    // (dY) in fp32, per element at row m, column n (gate index j = m g_rp + n):
+    //   gDWq[j] = v U, gY[j] = U Wq, O[m, n] = v Wq SiLU'(gH[m, n]), element type
+    const void* gH;    // pre-activations, pitch o_rp
+    const void* gW;    // Wq (ungated attention output)
+    const void* gU;    // U
+    void* gDWq;
+    void* gY;
+    int g_rp;
 };
 
 // Row RMS normalisation for the layer stack: Xn = bf16(x / sqrt(mean(x^2) + eps)).
@@ -140,9 +151,7 @@ hipError_t launch_rms_norm(const NormParams& p, bool bf16_storage, hipStream_t s
 // Epilogues of the backward GEMM (value v = alpha * accumulator at (row, col),
 // i its index in C).
 enum { EPI_STORE = 0,  // C[i] = v (fp32 when c_f32, else the element type)
-       EPI_SILU = 1,   // C[i] = v * SiLU'(H[i])
-       EPI_GATE = 2 }; // v = dY at (m, n), j = m * g_rp + n: O0[j] = v * G1[j] (dWq),
-                       // O1[j] = G1[j] * G0[j] (Y), C[i] = v * G0[j] * SiLU'(H[i]) (dH_u)
+       EPI_SILU = 1 }; // C[i] = v * SiLU'(H[i])
 
 // Batched C[z] = alpha * (A[z] B[z]^T + A2[z] B2[z]^T) on the MFMA core, 64 x 64
 // or 128 x 128 output tiles.  Operand z of A is at A + (z / a_div) * a_bs
@@ -167,10 +176,7 @@ struct GemmNTParams {
     int a2_rp, b2_rp;
     int K2;
     int epi;
-    const void* H;              // EPI_SILU, EPI_GATE
-    const void *G0, *G1;        // EPI_GATE inputs: Wq, U
-    void *O0, *O1;              // EPI_GATE outputs: dWq, Y
-    int g_rp;
+    const void* H;              // EPI_SILU
     int skip_upper;  // skip output tiles wholly above the diagonal (never read)
 };
 

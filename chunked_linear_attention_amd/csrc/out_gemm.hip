@@ -15,6 +15,31 @@
 namespace gau {
 namespace {
 
+// Four consecutive elements (aligned to four) as floats, and back.
+template <typename T>
+__device__ __forceinline__ void get4(const char* p, float (&v)[4]) {
+    if constexpr (Elem<T>::kBytes == 2) {
+        const u32x2_t w = *(const u32x2_t*)p;
+        v[0] = __uint_as_float(w.x << 16);
+        v[1] = __uint_as_float(w.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(w.y << 16);
+        v[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    } else {
+        const f32x4_t w = *(const f32x4_t*)p;
+        v[0] = w.x;
+        v[1] = w.y;
+        v[2] = w.z;
+        v[3] = w.w;
+    }
+}
+template <typename T>
+__device__ __forceinline__ void put4(char* p, const float (&v)[4]) {
+    if constexpr (Elem<T>::kBytes == 2)
+        *(u32x2_t*)p = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    else
+        *(f32x4_t*)p = f32x4_t{v[0], v[1], v[2], v[3]};
+}
+
 constexpr int BN = 256, WGM = 2, WGN = 4;  // tokens per tile, wave grid
 
 template <typename T, int BM>
@@ -50,12 +75,51 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
 
     constexpr int LDS = OutTile<T, BM>::LDS;
     const int M = p.M, d = p.d;
+    const size_t orp = p.o_rp > 0 ? (size_t)p.o_rp : (size_t)d;  // output row pitch
     auto ident = [](int, int, float v) { return v; };
-    if (p.residual == nullptr) {
+    if (p.gU != nullptr) {
+        // gate epilogue: the product staged in fp32; each 16-byte staged vector
+        // is four columns n..n+3 of row m.  The staging address handed to the
+        // emitter is O + 4 (m o_rp + n) (a position code, never dereferenced
+        // as fp32): O holds element-type values.
+        const char* code0 = (const char*)p.O;
+        const size_t grp = (size_t)p.g_rp;
+        G::template store_packed<float>(
+            acc, lds, LDS, ident,
+            [&](int tok, int feat) -> char* {
+                const int m = m0 + tok, n = n0 + feat;
+                return (m < M && n < d) ? (char*)code0 + 4 * ((size_t)m * orp + n) : nullptr;
+            },
+            [&](char* dp, const u32x4_t& v) {
+                const size_t idx = (size_t)(dp - code0) / 4, m = idx / orp, n = idx - m * orp;
+                const size_t j = m * grp + n;
+                float h[4], w[4], u[4], a[4], y[4], o[4];
+                get4<T>((const char*)p.gH + idx * EB, h);
+                get4<T>((const char*)p.gW + j * EB, w);
+                get4<T>((const char*)p.gU + j * EB, u);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float dy = __uint_as_float(v[k]);
+                    a[k] = dy * u[k];
+                    y[k] = u[k] * w[k];
+                    o[k] = dy * w[k] * silu_grad(h[k]);
+                }
+                put4<T>((char*)p.gDWq + j * EB, a);
+                put4<T>((char*)p.gY + j * EB, y);
+                put4<T>((char*)p.O + idx * EB, o);
+            });
+    } else if (p.residual == nullptr && !p.f32_out) {
         char* O = (char*)p.O;
         G::template store_packed<T>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
             const int m = m0 + tok, n = n0 + feat;
-            return (m < M && n < d) ? O + ((size_t)m * d + n) * EB : nullptr;
+            return (m < M && n < d) ? O + ((size_t)m * orp + n) * EB : nullptr;
+        });
+    } else if (p.residual == nullptr) {
+        // fp32 O = Y W_o
+        float* O = (float*)p.O;
+        G::template store_packed<float>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
+            const int m = m0 + tok, n = n0 + feat;
+            return (m < M && n < d) ? (char*)(O + (size_t)m * orp + n) : nullptr;
         });
     } else {
         // O = residual + Y W_o (fp32): stage the product, then add the residual
@@ -66,7 +130,7 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
             acc, lds, LDS, ident,
             [&](int tok, int feat) -> char* {
                 const int m = m0 + tok, n = n0 + feat;
-                return (m < M && n < d) ? (char*)(O + (size_t)m * d + n) : nullptr;
+                return (m < M && n < d) ? (char*)(O + (size_t)m * orp + n) : nullptr;
             },
             [&](char* dp, const u32x4_t& v) {
                 const size_t off = (size_t)((float*)dp - O);
