@@ -269,11 +269,15 @@ __global__ __launch_bounds__(512) void proj_kernel(ProjParams p) {
         // its 4 MB L2 while its token tiles stream through, where a range of
         // whole token tiles would cycle all twelve weight tiles through it
         // every round (165 -> 113 MB fetched per launch at B*T = 16384).
-        constexpr int kHalf[2][6] = {{0, 1, 4, 6, 7, 8}, {2, 3, 5, 9, 10, 11}};
+        // Inside an XCD the Z-carrying tiles (the slower ones) are dispatched
+        // first, so the last round holds only plain tiles.
+        constexpr int kHost[2][2] = {{0, 1}, {2, 3}}, kRest[2][4] = {{4, 6, 7, 8}, {5, 9, 10, 11}};
         const int u = b - nz;
-        const int x = u & 7, j = u >> 3;
-        const int t = (x >> 1) * (mtiles / 4) + j / 6;
-        uv_tile<T, ZR>(p, t * ntiles + kHalf[x & 1][j % 6], lds);
+        const int x = u & 7, j = u >> 3, h = x & 1;
+        const int tq = mtiles / 4, nh = 2 * tq;  // token tiles and Z-carrying tiles per XCD
+        const int t = (x >> 1) * tq + (j < nh ? j / 2 : (j - nh) / 4);
+        const int col = j < nh ? kHost[h][j % 2] : kRest[h][(j - nh) % 4];
+        uv_tile<T, ZR>(p, t * ntiles + col, lds);
     } else {
         uv_tile<T, ZR>(p, xcd_remap(b - nz, gridDim.x - nz), lds);
     }
