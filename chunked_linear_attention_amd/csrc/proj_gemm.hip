@@ -278,6 +278,16 @@ __global__ __launch_bounds__(512) void proj_kernel(ProjParams p) {
         const int t = (x >> 1) * tq + (j < nh ? j / 2 : (j - nh) / 4);
         const int col = j < nh ? kHost[h][j % 2] : kRest[h][(j - nh) % 4];
         uv_tile<T, ZR>(p, t * ntiles + col, lds);
+    } else if (ZR > 0 && ntiles == 16 && mtiles % 2 == 0) {
+        // e = 2048: XCD x takes a quarter of the column tiles (g, g+4, g+8,
+        // g+12 with g = x % 4: one Z-carrying tile each) for half of the token
+        // tiles (its weight tiles: 2 MB at d = 1024), the Z-carrying tiles first
+        const int u = b - nz;
+        const int x = u & 7, j = u >> 3, gq = x & 3;
+        const int th = mtiles / 2;  // token tiles per XCD (= its Z-carrying tiles)
+        const int t = (x >> 2) * th + (j < th ? j : (j - th) / 3);
+        const int col = j < th ? gq : gq + 4 * (1 + (j - th) % 3);
+        uv_tile<T, ZR>(p, t * ntiles + col, lds);
     } else {
         uv_tile<T, ZR>(p, xcd_remap(b - nz, gridDim.x - nz), lds);
     }

@@ -72,6 +72,7 @@ CASES = [
     (1, 256, 128, 1024, 128, 64, "f32", True),      # Z formed inside the U tiles (s = 128)
     (1, 256, 128, 1024, 256, 128, "bf16", False),   # Z formed inside the U tiles (s = 256)
     (1, 1024, 128, 1536, 128, 256, "bf16", True),   # e = 1536: tiles spread over the XCDs by column halves
+    (1, 512, 128, 2048, 128, 128, "bf16", True),    # e = 2048: column quarters per XCD
     (1, 256, 128, 256, 128, 64, "f32", True, True),   # heads rotated by position (RoPE)
     (1, 256, 128, 1024, 256, 128, "bf16", True, True),
     (1, 256, 128, 256, 128, 64, "f32", True, False, "local"),     # LocalOnly / GlobalOnly variants

@@ -64,6 +64,8 @@ SMALL = [
     (2, 256, 128, 1280, 128, 128, "bf16", True),
     (1, 960, 128, 1536, 128, 64, "bf16", True),    # e = 1536: column halves per XCD, ragged last token tile
     (2, 512, 128, 1536, 128, 128, "f32", True),    # e = 1536 in fp32, four token tiles
+    (1, 512, 256, 2048, 128, 128, "bf16", True),   # e = 2048: column quarters per XCD, two token tiles
+    (1, 768, 128, 2048, 128, 128, "f32", False),   # e = 2048, three token tiles (the generic order)
 ]
 
 
