@@ -23,8 +23,9 @@
 // eighth of a round longer than U and V alone instead of a second launch of
 // small, latency-bound blocks.  U/V tiles are assigned to XCDs so that
 // tiles sharing operand rows share an L2: at e = 1536 each XCD takes half of
-// the column tiles for a quarter of the token tiles; otherwise contiguous
-// ranges (the 2e/256 column tiles of one token tile together).
+// the column tiles for a quarter of the token tiles, at e = 2048 a quarter of
+// them for half of the token tiles; otherwise contiguous ranges (the 2e/256
+// column tiles of one token tile together).
 #include "gau_launch.h"
 #include "gemm_core.h"
 
