@@ -5,7 +5,7 @@ MI355X.
                     [--copy-calibration]
     python bench.py --summarize-stats STATS_CSV --command CMD --out FILE.md
     python bench.py --summarize-traffic FETCH_CSV WRITE_CSV --command CMD
-    python bench.py --decode | --backward | --sweep
+    python bench.py --decode | --backward | --sweep | --vendor-gemm
 
 A step is one full forward of the layer (all six kernels) over one batch of
 seeded synthetic input, B=2 sequences of T=8192 tokens, d=768, e=1536, s=128,
@@ -155,6 +155,40 @@ def mfma_probe(torch, g, blocks=1024, iters=1000, reps=5):
     t = float(np.median(times))
     return {"tflops": flops / t / 1e12, "frac_of_published": flops / t / 1e12 / PEAK_BF16_TFLOPS,
             "flops_per_launch": flops, "ms": t * 1e3, "blocks": blocks, "iters": iters}
+
+
+def vendor_gemm():
+    """The plain bf16 GEMMs of the layer's two dense contractions through
+    torch (its vendor BLAS), no epilogue: a yardstick for the projection and
+    output kernels, which also apply SiLU, the heads, the transposed V store
+    or the residual.  One JSON line per shape; not part of the layer path."""
+    import torch
+
+    torch.manual_seed(0)
+    shapes = [("proj d768 e1536 (X [W_u|W_v|W_z])", 16384, 3200, 768),
+              ("proj without W_z", 16384, 3072, 768),
+              ("out d768 e1536 (Y W_o)", 16384, 768, 1536),
+              ("proj d1024 e2048", 16384, 4224, 1024),
+              ("out d1024 e2048", 16384, 1024, 2048)]
+    for name, M, N, K in shapes:
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+        for _ in range(10):
+            c = a @ b.t()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(50):
+                c = a @ b.t()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / 50)
+        us = float(np.median(times))
+        print(json.dumps({"vendor_gemm": name, "M": M, "N": N, "K": K, "us": us,
+                          "tflops": 2.0 * M * N * K / us / 1e6}), flush=True)
+        del a, b, c
 
 
 def copy_calibration(torch):
@@ -542,6 +576,8 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="the layer's backward pass at the headline workload (one JSON line)")
     ap.add_argument("--title", help="heading of a --summarize-stats table")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time torch's plain bf16 GEMMs of the layer's dense shapes (a yardstick, one JSON line each)")
     ap.add_argument("--sweep", action="store_true",
                     help="throughput of every named workload (one JSON line each) instead of the headline line")
     args = ap.parse_args()
@@ -567,6 +603,9 @@ def main():
 
     if args.sweep:
         sweep(args.steps, args.warmup)
+        return
+    if args.vendor_gemm:
+        vendor_gemm()
         return
     if args.decode:
         decode_bench(args.steps if args.steps != 100 else 256, args.warmup)
