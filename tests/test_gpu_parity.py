@@ -66,6 +66,8 @@ SMALL = [
     (2, 512, 128, 1536, 128, 128, "f32", True),    # e = 1536 in fp32, four token tiles
     (1, 512, 256, 2048, 128, 128, "bf16", True),   # e = 2048: column quarters per XCD, two token tiles
     (1, 768, 128, 2048, 128, 128, "f32", False),   # e = 2048, three token tiles (the generic order)
+    (1, 256, 2048, 4096, 128, 64, "bf16", True),   # wide layer: K = 2048 projection, 256-feature output tiles
+    (1, 128, 1024, 3072, 256, 64, "f32", False),   # wide fp32 layer, s = 256, one token tile
 ]
 
 
