@@ -307,15 +307,6 @@ __global__ __launch_bounds__(256) void heads_bwd_kernel(BwdHeadsParams q) {
     }
 }
 
-// Ones in the element type, 16 bytes per thread (n * element size a multiple of 16).
-template <typename T>
-__global__ __launch_bounds__(256) void fill_one_kernel(void* x, size_t n16) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n16) return;
-    const uint32_t one = Elem<T>::kBytes == 2 ? 0x3F803F80u : 0x3F800000u;
-    *((u32x4_t*)x + i) = u32x4_t{one, one, one, one};
-}
-
 template <typename P>
 hipError_t go(void (*k)(P), unsigned blocks, const P& p, hipStream_t st) {
     hipLaunchKernelGGL(k, dim3(blocks), dim3(256), 0, st, p);
@@ -366,16 +357,6 @@ hipError_t launch_transpose(const TransposeParams& q0, int R, int Cc, int nb, bo
         hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, st, q);
     else
         hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st, q);
-    return hipGetLastError();
-}
-
-hipError_t launch_fill_one(void* x, size_t n, bool bf, hipStream_t st) {
-    const size_t n16 = n * (bf ? 2 : 4) / 16;
-    const unsigned b = (unsigned)((n16 + 255) / 256);
-    if (bf)
-        hipLaunchKernelGGL(fill_one_kernel<bf16>, dim3(b), dim3(256), 0, st, x, n16);
-    else
-        hipLaunchKernelGGL(fill_one_kernel<float>, dim3(b), dim3(256), 0, st, x, n16);
     return hipGetLastError();
 }
 

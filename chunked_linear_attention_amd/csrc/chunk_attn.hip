@@ -78,11 +78,13 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void chunk_attn_kernel(AttnParam
     // gate: acc rows are features f0 + row, columns are queries q0 + col; the
     // four rows a lane holds are four consecutive features of one token of U
     // (the accumulator layout of the MFMA core, as in transform4)
+    // (U == nullptr: no gate, Y = the attention output itself)
+    const bool gated = p.U != nullptr;
     const char* U = (const char*)p.U + ((tok0 + q0) * p.e + f0) * EB;
     const size_t pitch_e = (size_t)p.e * EB;
     using GV = typename GateVec<T>::type;
     GV gate[G::MB][G::NB][4];
-    {
+    if (gated) {
         const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
         const int wm = wave / WGN, wn = wave % WGN;
         const int c = lane & 31, h = lane >> 5;
@@ -102,6 +104,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void chunk_attn_kernel(AttnParam
     G::zero(acc);
     G::run_segs(acc, a0, a1, BF, b0, b1, BQ, lds);
 
+    if (gated)
 #pragma unroll
     for (int i = 0; i < G::MB; ++i)
 #pragma unroll

@@ -186,7 +186,7 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
 
 // Backward workspace: the forward's regions, then the backward's own.
 struct BwdLayout {
-    size_t H, ones, dWq, Yb, WoT, dOt, Yt, V, dA, dSc, dScE, dSct, At, Kqc, Qqc, Qlc;
+    size_t H, dWq, Yb, WoT, dOt, Yt, V, dA, dSc, dScE, dSct, At, Kqc, Qqc, Qlc;
     size_t dQq, dKq, dQl, dKl, dWqc, Pt, dP, dSst, dS, Kl, rpart, hpart, dH, dHt, Xt, Wt, wpart, total;
     int split_o, split_w;  // K splits of the weight-gradient products
 };
@@ -216,7 +216,6 @@ void bwd_layout(const gau_config* c, BwdLayout* L) {
         return o;
     };
     L->H = take(M * W3 * eb);
-    L->ones = take(M * e * eb);
     L->dWq = take(M * e * eb);
     L->Yb = take(M * e * eb);
     L->WoT = take(e * d * eb);
@@ -309,10 +308,9 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     gau_status sres = run_stages(c, GAU_STAGE_PROJ, GAU_STAGE_SCAN, a, nullptr, nullptr, ws, st, false);
     if (sres != GAU_OK) return sres;
     // Wq = A V + Q_lin P (into the forward's Y region): the attention stage
-    // with a gate of ones
-    ok(gau::launch_fill_one(W(L.ones), (size_t)M * e, bf, st));
+    // without the gate
     {
-        gau::AttnParams p{W(F.A), W(F.Q_lin), W(F.Vt), W(F.P), W(L.ones), W(F.Y), Bn, T, e, s, C,
+        gau::AttnParams p{W(F.A), W(F.Q_lin), W(F.Vt), W(F.P), nullptr, W(F.Y), Bn, T, e, s, C,
                           c->causal ? 1 : 0, 1, 1};
         ok(gau::launch_chunk_attn(p, bf, st));
     }

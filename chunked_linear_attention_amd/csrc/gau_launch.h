@@ -61,7 +61,7 @@ struct AttnParams {
     const void* Ql;   // [M, s]
     const void* Vt;   // [B, e, T]
     const void* P;    // [B, G or 1, e, s]
-    const void* U;    // [M, e]
+    const void* U;    // [M, e], or nullptr: no gate (Y = A_g V_g + Q_lin P_g)
     void* Y;          // [M, e]; may be U (gated in place)
     int B, T, e, s, C;
     int causal;
@@ -222,7 +222,6 @@ struct BwdHeadsParams {
 
 hipError_t launch_gemm_nt(const GemmNTParams& q, int M, int N, int nb, bool bf16_storage, hipStream_t st);
 hipError_t launch_transpose(const TransposeParams& q, int R, int Cc, int nb, bool bf16_storage, hipStream_t st);
-hipError_t launch_fill_one(void* x, size_t n, bool bf16_storage, hipStream_t st);
 hipError_t launch_scores_bwd(const BwdElemParams& q, bool bf16_storage, hipStream_t st);
 // drelpos[k] = sum over chunks and over entries on diagonal k - (C-1) of dsc
 hipError_t launch_relpos_bwd(const float* dsc, float* part, float* drelpos, int nchunks, int C, hipStream_t st);

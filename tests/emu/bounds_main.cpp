@@ -108,6 +108,9 @@ static void run(const Cfg& c, const std::string& only) {
     t("chunk_scan", [&] { CHECK(launch_chunk_scan(scp, c.bf, nullptr)); });
     AttnParams ap{A, Ql, Vt, P, U, Y, c.B, c.T, c.e, c.s, c.C, c.causal ? 1 : 0, 1, 1};
     t("chunk_attn", [&] { CHECK(launch_chunk_attn(ap, c.bf, nullptr)); });
+    AttnParams apu = ap;
+    apu.U = nullptr;  // no gate (the backward's recompute of the attention output)
+    t("chunk_attn_ungated", [&] { CHECK(launch_chunk_attn(apu, c.bf, nullptr)); });
     OutParams op{Y, Wo, O, nullptr, (int)M, c.d, c.e};
     t("out_gemm", [&] { CHECK(launch_out_gemm(op, c.bf, nullptr)); });
     OutParams opr{Y, Wo, Of, Of, (int)M, c.d, c.e};
