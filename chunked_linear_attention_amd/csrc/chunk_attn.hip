@@ -49,7 +49,7 @@ struct GateVec<float> {
     using type = f32x4_t;
 };
 
-template <typename T, int BQ>
+template <typename T, int BQ, bool GATED>
 __global__ __launch_bounds__(WGM * WGN * kWave) void chunk_attn_kernel(AttnParams p) {
     extern __shared__ __align__(16) char lds[];
     using G = typename AttnTile<T, BQ>::G;
@@ -78,13 +78,13 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void chunk_attn_kernel(AttnParam
     // gate: acc rows are features f0 + row, columns are queries q0 + col; the
     // four rows a lane holds are four consecutive features of one token of U
     // (the accumulator layout of the MFMA core, as in transform4)
-    // (U == nullptr: no gate, Y = the attention output itself)
-    const bool gated = p.U != nullptr;
+    // (GATED false: U == nullptr, Y = the attention output itself; a template
+    // parameter so that the gated kernel's code is that of the gate alone)
     const char* U = (const char*)p.U + ((tok0 + q0) * p.e + f0) * EB;
     const size_t pitch_e = (size_t)p.e * EB;
     using GV = typename GateVec<T>::type;
     GV gate[G::MB][G::NB][4];
-    if (gated) {
+    if constexpr (GATED) {
         const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
         const int wm = wave / WGN, wn = wave % WGN;
         const int c = lane & 31, h = lane >> 5;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void chunk_attn_kernel(AttnParam
     G::zero(acc);
     G::run_segs(acc, a0, a1, BF, b0, b1, BQ, lds);
 
-    if (gated)
+    if constexpr (GATED)
 #pragma unroll
     for (int i = 0; i < G::MB; ++i)
 #pragma unroll
@@ -131,22 +131,27 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void chunk_attn_kernel(AttnParam
                                 [&](int q, int f) -> char* { return Y + (size_t)q * pitch_e + (size_t)f * EB; });
 }
 
-template <typename T, int BQ>
+template <typename T, int BQ, bool GATED>
 hipError_t launch_t(const AttnParams& p, hipStream_t st) {
     constexpr int LDS = AttnTile<T, BQ>::LDS;
     static_assert(LDS <= 160 * 1024, "chunk kernel LDS over budget");
     const int blocks = (p.e / BF) * (p.C / BQ) * p.B * (p.T / p.C);
-    hipError_t e = allow_lds<chunk_attn_kernel<T, BQ>>(LDS);
+    hipError_t e = allow_lds<chunk_attn_kernel<T, BQ, GATED>>(LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_attn_kernel<T, BQ>), dim3(blocks), dim3(WGM * WGN * kWave), LDS, st, p);
+    hipLaunchKernelGGL((chunk_attn_kernel<T, BQ, GATED>), dim3(blocks), dim3(WGM * WGN * kWave), LDS, st, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_chunk_attn(const AttnParams& p, bool bf16_storage, hipStream_t st) {
-    if (bf16_storage) return p.C >= 128 ? launch_t<bf16, 128>(p, st) : launch_t<bf16, 64>(p, st);
-    return p.C >= 128 ? launch_t<float, 128>(p, st) : launch_t<float, 64>(p, st);
+    const bool g = p.U != nullptr;
+    if (bf16_storage) {
+        if (p.C >= 128) return g ? launch_t<bf16, 128, true>(p, st) : launch_t<bf16, 128, false>(p, st);
+        return g ? launch_t<bf16, 64, true>(p, st) : launch_t<bf16, 64, false>(p, st);
+    }
+    if (p.C >= 128) return g ? launch_t<float, 128, true>(p, st) : launch_t<float, 128, false>(p, st);
+    return g ? launch_t<float, 64, true>(p, st) : launch_t<float, 64, false>(p, st);
 }
 
 }  // namespace gau
