@@ -12,11 +12,12 @@ seeded synthetic input, B=2 sequences of T=8192 tokens, d=768, e=1536, s=128,
 chunk C=256, bf16 storage with fp32 accumulation, causal.  Inputs are resident
 in HBM before the timed region starts.  Prints one JSON line.
 
-Inside the timed region the dominant kernel (the projection GEMM) is
-bracketed by HIP events on the stream the kernels run on; the roofline object
-is its algorithmic FLOPs per launch divided by that average duration, against
-the dense bf16 MFMA peak.  Per-stage times (kernels_us) come from a separate
-pass with events around every stage, outside the timed region.
+The timed region is K plain gau_forward calls between two synchronisations.
+Just before it, a pass of whole forwards brackets the dominant kernel (the
+projection GEMM) with HIP events on the stream the kernels run on; the
+roofline object is its algorithmic FLOPs per launch divided by that average
+duration, against the dense bf16 MFMA peak.  Per-stage times (kernels_us)
+come from another pass with events around every stage.
 """
 
 import argparse
@@ -37,7 +38,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "GAU/FLASH layer fwd tokens/sec at d=768 T=8192 C=256; % bf16 MFMA peak"
 STAGES = ["proj", "chunk_scores", "chunk_state", "chunk_scan", "chunk_attn", "out_gemm"]
 DOMINANT = "proj"
-EVENT_EVERY = 5  # steps between event-bracketed launches of the dominant kernel
+DOM_MIN_SAMPLES = 50  # event-bracketed launches of the dominant kernel, at least
 
 
 def algorithmic_flops(B, T, d, e, s, C, causal=True):
@@ -113,6 +114,20 @@ def blas_threads():
     return len(os.sched_getaffinity(0))
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo) and its logical CPU count."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{name} ({os.cpu_count()} logical CPUs, {len(os.sched_getaffinity(0))} usable)"
+
+
 def cpu_baseline(cfg, inp, min_s=12.0, max_passes=100):
     """The float64 oracle, as it stands, on the host cores: whole sequences of
     the timed workload, one after another, repeated until at least min_s of
@@ -128,7 +143,7 @@ def cpu_baseline(cfg, inp, min_s=12.0, max_passes=100):
         if (dt >= min_s and done % cfg["B"] == 0) or done >= max_passes * cfg["B"]:
             break
     return {"value": done * cfg["T"] / dt, "unit": "tokens/s", "cores": blas_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{done} sequences of T={cfg['T']} ({done // cfg['B']} passes over the B={cfg['B']} "
                       f"timed workload), float64 numpy, {dt:.1f} s"}
 
@@ -633,12 +648,13 @@ def main():
 
     dom = STAGES.index(DOMINANT)
 
-    def step(ev=None):
-        """One forward.  With ev = (start, end) events, the dominant kernel's
-        stage is bracketed by them (the forward is split into three calls)."""
-        if ev is None:
-            g.forward(gc, *args_l, stream=stream)
-            return
+    def step():
+        """One forward: one gau_forward call (six kernels) on the stream."""
+        g.forward(gc, *args_l, stream=stream)
+
+    def step_bracketed(ev):
+        """The same forward as three calls, with the dominant kernel's stage
+        alone between the two events ev = (start, end)."""
         if dom > 0:
             g.forward_stages(gc, 0, dom - 1, *args_l, stream=stream)
         ev[0].record(stream)
@@ -647,27 +663,26 @@ def main():
         if dom + 1 < len(STAGES):
             g.forward_stages(gc, dom + 1, len(STAGES) - 1, *args_l, stream=stream)
 
+    K = args.steps
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps; on every EVENT_EVERY-th step the dominant kernel
-    # is bracketed by HIP events on the stream it runs on (a pair of timing
-    # events costs the GPU about 6 us, so bracketing every step would slow the
-    # steps it measures)
-    K = args.steps
-    sampled = list(range(0, K, EVENT_EVERY))
-    events = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in sampled}
+    # Diagnostics before the timed region (they also settle the clocks):
+    # (1) the dominant kernel's launches bracketed by HIP events on the
+    # stream the kernels run on, inside whole forwards (its neighbours run as
+    # they do in a forward), K of them; the roofline's `achieved` uses their
+    # average.  (2) every stage alone between events, and scores + states as
+    # the forward runs them (one launch).
+    dom_n = max(K, DOM_MIN_SAMPLES)
+    dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(dom_n)]
+    t_split = time.perf_counter()
+    for ev in dom_ev:
+        step_bracketed(ev)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        step(events.get(k))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in events.values()]))
+    split_ms_per_step = (time.perf_counter() - t_split) * 1e3 / dom_n
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dom_ev]))
 
-    # diagnostics outside the timed region: every stage bracketed by events,
-    # and the plain single-call forward
     stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(K)]
     for k in range(K):
         for i in range(len(STAGES)):
@@ -677,7 +692,6 @@ def main():
     torch.cuda.synchronize()
     per_stage = {n: float(np.mean([stage_ev[k][i].elapsed_time(stage_ev[k][i + 1]) for k in range(K)]))
                  for i, n in enumerate(STAGES)}  # ms
-    # scores and states as the forward runs them: one launch for both
     i_sc = STAGES.index("chunk_scores")
     pair_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for a, b in pair_ev:
@@ -686,11 +700,23 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     pair_ms = float(np.mean([a.elapsed_time(b) for a, b in pair_ev]))
+    for _ in range(args.warmup):
+        step()
+
+    # timed region: exactly K plain forwards, a synchronisation on each side
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # the same loop once more (a repeat of the timed region, reported beside it)
     t1 = time.perf_counter()
     for _ in range(K):
         step()
     torch.cuda.synchronize()
-    wall_plain = time.perf_counter() - t1
+    wall_repeat = time.perf_counter() - t1
 
     tokens = B * T
     ms_per_step = wall * 1e3 / K
@@ -721,14 +747,17 @@ def main():
         "roofline": {"bound": "mfma", "kernel": DOMINANT, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "algorithmic_flops_per_launch": flops[DOMINANT], "avg_launch_us": dom_ms * 1e3,
-                     "event_samples": len(sampled)},
+                     "event_samples": dom_n,
+                     "event_note": "the kernel's launches inside whole forwards, each between two HIP events "
+                                   "on the launch stream, in a pass of their own just before the timed region"},
         "kernels_us": {n: per_stage[n] * 1e3 for n in STAGES},
         "kernels_gbs": {n: bytes_[n] / (per_stage[n] * 1e-3) / 1e9 for n in STAGES},
         "kernels_tflops": {n: flops[n] / (per_stage[n] * 1e-3) / 1e12 for n in STAGES},
         "kernels_us_combined": {"chunk_scores+chunk_state": pair_ms * 1e3},
         "kernels_us_note": "each stage launched alone between two timing events (about 3 us of GPU time "
                            "each); the kernel trace gives the durations inside one forward",
-        "ms_per_step_single_call": wall_plain * 1e3 / K,
+        "ms_per_step_repeat": wall_repeat * 1e3 / K,
+        "ms_per_step_split_calls": split_ms_per_step,
     }
     probe = mfma_probe(torch, g)
     out["mfma_probe"] = probe

@@ -52,11 +52,13 @@ __device__ __forceinline__ void put4<bf16>(void* dst, const f32x4_t& v) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanParams p) {
-    const int per_b = p.es / 4;
-    const int idx = blockIdx.x * 256 + threadIdx.x;
+    // 64-bit lane index: B * e * s / 4 lanes may exceed 2^31 (check_config
+    // bounds it below 2^31 so that the grid fits, but no product here wraps)
+    const int64_t per_b = p.es / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= per_b * p.B) return;
-    const int b = idx / per_b;
-    const int v = idx - b * per_b;
+    const int64_t b = idx / per_b;
+    const int64_t v = idx - b * per_b;
     const size_t stride = (size_t)p.es;  // elements between consecutive chunks
     constexpr int EB = Elem<T>::kBytes;
     const char* S = (const char*)p.S + ((size_t)b * p.G * stride + (size_t)v * 4) * EB;
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanParams p) {
 
 template <typename T>
 hipError_t launch(const ScanParams& p, hipStream_t st) {
-    const long threads = (long)p.B * (p.es / 4);
+    const int64_t threads = (int64_t)p.B * (p.es / 4);
     const int blocks = (int)((threads + 255) / 256);
     hipLaunchKernelGGL(chunk_scan_kernel<T>, dim3(blocks), dim3(256), 0, st, p);
     return hipGetLastError();

@@ -32,6 +32,9 @@ gau_status check_config(const gau_config* c) {
     const int64_t M = c->B * c->T;
     if (M > (int64_t)1 << 30 || c->d > 65536 || c->e > 65536) return GAU_ERR_SHAPE;
     if (M * (c->e > c->d ? c->e : c->d) > ((int64_t)1 << 40)) return GAU_ERR_SHAPE;
+    // the chunk scan's grid: one lane per four of the B * e * s state
+    // entries, fewer than 2^31 lanes
+    if (c->B * c->e * c->s >= ((int64_t)1 << 33)) return GAU_ERR_SHAPE;
     return GAU_OK;
 }
 

@@ -39,6 +39,9 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* out) 
 
 extern "C" gau_status gau_probe_mfma(int blocks, int iters, float* out, void* stream) {
     if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20)) return GAU_ERR_SHAPE;
+    // at most 2^22 block-iterations (about 4.4 PFLOP, a few seconds of the
+    // whole chip), so that no call queues an effectively endless kernel
+    if ((int64_t)blocks * iters > ((int64_t)1 << 22)) return GAU_ERR_SHAPE;
     if (!out) return GAU_ERR_NULL;
     if (((uintptr_t)out & 15) != 0) return GAU_ERR_ALIGN;
     hipLaunchKernelGGL(gau::mfma_probe_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);

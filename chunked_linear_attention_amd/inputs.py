@@ -16,6 +16,12 @@ Distributions (one seeded PCG64 stream per layer, drawn in this order):
 All are drawn in float32.  For bf16 workloads X and the four weight matrices
 are rounded to bf16 (round to nearest, ties to even); gamma, beta and relpos
 stay float32, which is the precision the library takes them in.
+
+With heads="wide" (parity tests only) gamma and beta are redrawn after the
+rest, from a stream of their own (seed + 104729), as
+  gamma ~ N(1, 0.5^2), beta ~ N(0, 0.3^2)
+so that every offset moves the output and a mix-up of two heads' scales is
+far outside the bf16 tolerance; the other tensors keep their values.
 """
 
 import numpy as np
@@ -78,14 +84,28 @@ def _draw_weights(rng, d, e, s, C):
     return dict(W_u=W_u, W_v=W_v, W_z=W_z, W_o=W_o, gamma=gamma, beta=beta, relpos=relpos)
 
 
-def make_layer_inputs(B, T, d, e, s, C, seed, dtype="bf16", **_ignored):
+def wide_heads(s, seed):
+    """gamma ~ N(1, 0.5^2) and beta ~ N(0, 0.3^2), both (4, s) float32, from a
+    stream of their own (seed + 104729)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    gamma = np.float32(1.0) + np.float32(0.5) * rng.standard_normal((4, s), dtype=np.float32)
+    beta = np.float32(0.3) * rng.standard_normal((4, s), dtype=np.float32)
+    return gamma, beta
+
+
+def make_layer_inputs(B, T, d, e, s, C, seed, dtype="bf16", heads="workload", **_ignored):
     """All inputs of one layer as float32 numpy arrays in the pages' orientation
     (W_u is d x e, etc.).  For dtype "bf16" the matrices hold bf16-exact values.
+    heads="wide" replaces gamma and beta by wide_heads(s, seed).
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     X = rng.standard_normal((B, T, d), dtype=np.float32)
     out = dict(X=X)
     out.update(_draw_weights(rng, d, e, s, C))
+    if heads == "wide":
+        out["gamma"], out["beta"] = wide_heads(s, seed)
+    elif heads != "workload":
+        raise ValueError("heads must be 'workload' or 'wide'")
     if dtype == "bf16":
         for k in ("X", "W_u", "W_v", "W_z", "W_o"):
             out[k] = round_bf16(out[k])
@@ -102,14 +122,20 @@ def make_output_grad(B, T, d, seed, dtype="bf16"):
     return round_bf16(g) if dtype == "bf16" else g
 
 
-def make_stack_inputs(B, T, d, e, s, C, layers, weight_seed, x_seed, dtype="bf16", **_ignored):
+def make_stack_inputs(B, T, d, e, s, C, layers, weight_seed, x_seed, dtype="bf16", heads="workload",
+                      **_ignored):
     """Inputs of a layer stack: X (float32, the residual stream) and a list of
-    per-layer weight dicts, layer l drawn from seed weight_seed + l."""
+    per-layer weight dicts, layer l drawn from seed weight_seed + l (with
+    heads="wide", its gamma and beta from wide_heads(s, weight_seed + l))."""
     rng = np.random.Generator(np.random.PCG64(x_seed))
     X = rng.standard_normal((B, T, d), dtype=np.float32)
     Ls = []
     for l in range(layers):
         w = _draw_weights(np.random.Generator(np.random.PCG64(weight_seed + l)), d, e, s, C)
+        if heads == "wide":
+            w["gamma"], w["beta"] = wide_heads(s, weight_seed + l)
+        elif heads != "workload":
+            raise ValueError("heads must be 'workload' or 'wide'")
         if dtype == "bf16":
             for k in ("W_u", "W_v", "W_z", "W_o"):
                 w[k] = round_bf16(w[k])

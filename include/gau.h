@@ -79,8 +79,9 @@ typedef enum {
  *   s shared (attention) width, C chunk length; G = T / C.
  * Supported: B, T >= 0 (B*T == 0 is a no-op); T % C == 0 (the chunking splits
  *   the sequence into whole chunks, wikillm "Method", papercache 3.2);
- *   C in {64, 128, 256, 512}; d % 128 == 0; e % 256 == 0; s in {128, 256}.
- *   Otherwise GAU_ERR_SHAPE.
+ *   C in {64, 128, 256, 512}; d % 128 == 0; e % 256 == 0; s in {128, 256};
+ *   B*T <= 2^30, d, e <= 65536, B*T*max(d, e) <= 2^40 and B*e*s < 2^33 (the
+ *   kernels' grids and index arithmetic).  Otherwise GAU_ERR_SHAPE.
  */
 typedef struct {
     int64_t B, T, d, e, s, C;

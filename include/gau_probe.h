@@ -24,8 +24,10 @@ extern "C" {
  * blocks * 4 * iters * 16 * 32768.  `out` (device, one float) is written only
  * if the accumulators sum to a sentinel they cannot reach, which keeps the
  * compiler from dropping the work; it may be any 16-byte aligned device
- * pointer.  GAU_ERR_SHAPE if blocks or iters is not in 1 .. 2^20,
- * GAU_ERR_NULL / GAU_ERR_ALIGN for `out`, GAU_ERR_HIP if the launch fails.
+ * pointer.  GAU_ERR_SHAPE if blocks or iters is not in 1 .. 2^20 or
+ * blocks * iters > 2^22 (a cap on one call's work: about 4.4 PFLOP, seconds
+ * of the whole chip), GAU_ERR_NULL / GAU_ERR_ALIGN for `out`, GAU_ERR_HIP if
+ * the launch fails.  Nothing is queued unless the status is GAU_OK.
  */
 gau_status gau_probe_mfma(int blocks, int iters, float* out, void* stream);
 

@@ -88,6 +88,7 @@ def chunk_errors(got, ref, C):
     return e / np.maximum(r, 1e-300)
 
 
-def make(B, T, d, e, s, C, dtype, seed):
-    """Seeded inputs with the workloads' recipe at a given shape."""
-    return inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=seed, dtype=dtype)
+def make(B, T, d, e, s, C, dtype, seed, heads="workload"):
+    """Seeded inputs with the workloads' recipe at a given shape (heads="wide":
+    gamma ~ N(1, 0.5^2) and beta ~ N(0, 0.3^2), so the offsets count)."""
+    return inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=seed, dtype=dtype, heads=heads)

@@ -58,7 +58,9 @@ def test_workspace_layout_sizes():
 
 
 @pytest.mark.parametrize("bad", [dict(T=500), dict(C=32), dict(C=96), dict(d=200), dict(e=384),
-                                 dict(s=64), dict(s=192), dict(B=-1)])
+                                 dict(s=64), dict(s=192), dict(B=-1),
+                                 # B * e * s = 2^33: the chunk scan's lanes would reach 2^31
+                                 dict(B=8192, T=128, C=128, d=128, e=8192, s=128)])
 def test_bad_shapes_rejected(bad):
     cfg = _cfg(**bad)
     assert g.workspace_bytes(cfg) == 0
@@ -193,6 +195,13 @@ def test_stack_argument_checks():
     assert lib.gau_stack_forward(ctypes.byref(cfg), 0, None, *[pp] * 7, None, 0, None) == 0
 
 
+def test_largest_scan_grid_accepted():
+    """Just under the bound: B * e * s = 2^33 - 2^22 (the scan's lanes stay
+    below 2^31) is a valid shape."""
+    cfg = _cfg(B=8191, T=128, C=128, d=128, e=8192, s=128)
+    assert g.workspace_bytes(cfg) > 0
+
+
 def test_status_strings():
     for code in range(7):
         assert g.status_string(code)
@@ -205,5 +214,7 @@ def test_mfma_probe_rejects_bad_arguments():
     assert lib.gau_probe_mfma(0, 10, None, None) == 2            # GAU_ERR_SHAPE
     assert lib.gau_probe_mfma(16, 0, None, None) == 2
     assert lib.gau_probe_mfma(16, (1 << 20) + 1, None, None) == 2
+    assert lib.gau_probe_mfma(1 << 12, (1 << 10) + 1, None, None) == 2   # blocks * iters > 2^22
+    assert lib.gau_probe_mfma(1 << 20, 1 << 20, None, None) == 2
     assert lib.gau_probe_mfma(16, 10, None, None) == 1           # GAU_ERR_NULL
     assert lib.gau_probe_mfma(16, 10, ctypes.c_void_p(8), None) == 3  # GAU_ERR_ALIGN

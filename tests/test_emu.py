@@ -77,6 +77,11 @@ CASES = [
     (1, 256, 128, 1024, 256, 128, "bf16", True, True),
     (1, 256, 128, 256, 128, 64, "f32", True, False, "local"),     # LocalOnly / GlobalOnly variants
     (1, 256, 128, 1024, 256, 128, "bf16", False, False, "global"),
+    # gamma ~ N(1, 0.5^2), beta ~ N(0, 0.3^2): the offsets count (Z tiles and Z in U tiles, s = 128 and 256)
+    (1, 256, 128, 256, 128, 64, "f32", True, False, "both", "wide"),
+    (1, 256, 128, 256, 256, 128, "bf16", False, False, "both", "wide"),
+    (1, 256, 128, 1024, 128, 64, "bf16", True, False, "both", "wide"),
+    (1, 256, 128, 1024, 256, 128, "f32", False, True, "both", "wide"),
 ]
 
 
@@ -86,16 +91,17 @@ def _host(a, bf):
 
 
 @pytest.mark.parametrize("late", [0, 1], ids=["dma_at_issue", "dma_at_wait"])
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}{}{}".format(
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}{}{}{}".format(
     *c[:7], "causal" if c[7] else "full", "_rope" if len(c) > 8 and c[8] else "",
-    "_" + c[9] if len(c) > 9 else ""))
+    "_" + c[9] if len(c) > 9 else "", "_wide" if len(c) > 10 else ""))
 def test_emulated_kernels_match_oracle(emu, case, late):
     B, T, d, e, s, C, dtype, causal = case[:8]
     rope = len(case) > 8 and case[8]
     parts = case[9] if len(case) > 9 else "both"
+    heads = case[10] if len(case) > 10 else "workload"
     bf = dtype == "bf16"
     emu.emu_set_mode(1, late)
-    inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=B * 31 + T + C, dtype=dtype)
+    inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=B * 31 + T + C, dtype=dtype, heads=heads)
     cfg = GauConfig(B, T, d, e, s, C, 1 if causal else 0, 1 if bf else 0, 1.0 / C, 1.0 / C, 1 if rope else 0,
                     {"both": 0, "local": 1, "global": 2}[parts])
     X = _host(inp["X"], bf)
@@ -133,6 +139,8 @@ def test_emulated_kernels_match_oracle(emu, case, late):
         "U": (region("U", (B, T, e)), im["U"]),
         "Vt": (region("Vt", (B, e, T)), im["V"].transpose(0, 2, 1)),
         "Q_quad": (region("Q_quad", (B, T, s)), im["Q_quad"]),
+        "K_quad": (region("K_quad", (B, T, s)), im["K_quad"]),
+        "Q_lin": (region("Q_lin", (B, T, s)), im["Q_lin"]),
         "K_lin_t": (region("K_lin_t", (B, s, T)), im["K_lin"].transpose(0, 2, 1)),
         "S": (region("S", (B, G, e, s)), im["S"].transpose(0, 1, 3, 2)),
         "Y": (region("Y", (B, T, e)), im["Y"]),
@@ -146,10 +154,12 @@ def test_emulated_kernels_match_oracle(emu, case, late):
         assert err <= tol, f"{name}: {err:.3e} > {tol}"
 
 
-@pytest.mark.parametrize("dtype,B", [("f32", 2), ("bf16", 2), ("bf16", 18)])
-def test_emulated_decoding_matches_the_causal_layer(emu, dtype, B):
+@pytest.mark.parametrize("dtype,B,heads", [("f32", 2, "workload"), ("bf16", 2, "workload"), ("bf16", 18, "workload"),
+                                           ("f32", 2, "wide"), ("bf16", 18, "wide")])
+def test_emulated_decoding_matches_the_causal_layer(emu, dtype, B, heads):
     """gau_decode_step on the emulation for 66 tokens (one chunk end, C = 64)
-    against the oracle's causal layer; B = 18 takes the MFMA products (from B = 3 on)."""
+    against the oracle's causal layer; B = 18 takes the MFMA products (from B = 3 on);
+    "wide": gamma ~ N(1, 0.5^2), beta ~ N(0, 0.3^2)."""
     T, d, e, s, C = 128, 128, 256, 128, 64
     steps = 66
     bf = dtype == "bf16"
@@ -159,7 +169,7 @@ def test_emulated_decoding_matches_the_causal_layer(emu, dtype, B):
     emu.gau_decode_workspace_bytes.argtypes = [ctypes.POINTER(GauConfig)]
     emu.gau_decode_reset.argtypes = [ctypes.POINTER(GauConfig), P, ctypes.c_size_t, P]
     emu.gau_decode_step.argtypes = [ctypes.POINTER(GauConfig), ctypes.c_int64] + [P] * 10 + [ctypes.c_size_t, P]
-    inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=41, dtype=dtype)
+    inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=41, dtype=dtype, heads=heads)
     cfg = GauConfig(B, T, d, e, s, C, 1, 1 if bf else 0, 1.0 / C, 1.0 / C, 1)
     W = {k: _host(np.ascontiguousarray(inp[k].T), bf) for k in ("W_u", "W_v", "W_z", "W_o")}
     sc, of, rp = (np.ascontiguousarray(inp[k], np.float32) for k in ("gamma", "beta", "relpos"))
@@ -189,14 +199,16 @@ BWD_CASES = [
     (2, 256, 128, 256, 256, 128, "bf16", True),
     (1, 320, 128, 512, 128, 64, "bf16", False),
     (1, 1024, 1024, 1024, 128, 256, "bf16", True),   # 128 x 128 tiles (weight gradients, dV, dX)
+    (1, 256, 128, 256, 128, 64, "f32", True, "wide"),  # gamma ~ N(1, 0.5^2), beta ~ N(0, 0.3^2)
 ]
 
 
-@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}".format(
-    *c[:7], "causal" if c[7] else "full"))
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}{}".format(
+    *c[:7], "causal" if c[7] else "full", "_wide" if len(c) > 8 else ""))
 def test_emulated_backward_matches_oracle(emu, case):
     """gau_backward on the emulation: every gradient against the oracle's."""
-    B, T, d, e, s, C, dtype, causal = case
+    B, T, d, e, s, C, dtype, causal = case[:8]
+    heads = case[8] if len(case) > 8 else "workload"
     bf = dtype == "bf16"
     emu.emu_set_mode(1, 1)
     P = ctypes.c_void_p
@@ -204,7 +216,7 @@ def test_emulated_backward_matches_oracle(emu, case):
     emu.gau_backward_workspace_bytes.argtypes = [ctypes.POINTER(GauConfig)]
     emu.gau_backward.argtypes = [ctypes.POINTER(GauConfig)] + [P] * 18 + [ctypes.c_size_t, P]
     emu.gau_backward.restype = ctypes.c_int
-    inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=B * 17 + T + C, dtype=dtype)
+    inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=B * 17 + T + C, dtype=dtype, heads=heads)
     dO = inputs.make_output_grad(B, T, d, seed=T + C, dtype=dtype)
     cfg = GauConfig(B, T, d, e, s, C, 1 if causal else 0, 1 if bf else 0, 1.0 / C, 1.0 / C, 0, 0)
     X, dOh = _host(inp["X"], bf), _host(dO, bf)

@@ -53,15 +53,20 @@ CASES = [
     (1, 1024, 256, 512, 128, 512, "bf16", True),    # the largest chunk
     (3, 192, 384, 768, 128, 64, "bf16", True),      # three chunks per sequence, d and e not powers of two
     (1, 320, 128, 1024, 256, 64, "f32", False),
+    # gamma ~ N(1, 0.5^2), beta ~ N(0, 0.3^2): the heads' offsets count
+    (1, 256, 128, 256, 128, 64, "f32", True, "wide"),
+    (2, 512, 256, 512, 128, 128, "bf16", False, "wide"),
+    (1, 320, 128, 1024, 256, 64, "bf16", True, "wide"),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}".format(
-    *c[:7], "causal" if c[7] else "full"))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}{}".format(
+    *c[:7], "causal" if c[7] else "full", "_wide" if len(c) > 8 else ""))
 def test_backward_matches_oracle(case):
-    B, T, d, e, s, C, dtype, causal = case
+    B, T, d, e, s, C, dtype, causal = case[:8]
+    heads = case[8] if len(case) > 8 else "workload"
     print(f"backward case {case}", flush=True)
-    inp = make(B, T, d, e, s, C, dtype, seed=B * 131 + T + C)
+    inp = make(B, T, d, e, s, C, dtype, seed=B * 131 + T + C, heads=heads)
     dO = inputs.make_output_grad(B, T, d, seed=T + d, dtype=dtype)
     _compare(_backward(inp, dO, B, T, d, e, s, C, causal, dtype), _oracle(inp, dO, C, causal), dtype)
 

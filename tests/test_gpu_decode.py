@@ -47,14 +47,20 @@ CASES = [
     (70, 128, 256, 512, 256, 64, "f32", 70, True),     # ... two token tiles, the second ragged
     (96, 128, 128, 1536, 128, 64, "f32", 128, False),   # attention with 8 features per thread
     (176, 128, 128, 1536, 128, 64, "bf16", 128, True),  # ... bf16 (16-byte loads), RoPE
+    # gamma ~ N(1, 0.5^2), beta ~ N(0, 0.3^2): the heads' offsets count
+    (2, 192, 128, 256, 128, 64, "f32", 192, False, "wide"),
+    (2, 384, 256, 512, 128, 128, "bf16", 384, True, "wide"),
+    (20, 128, 128, 256, 256, 64, "bf16", 128, False, "wide"),
+    (96, 128, 128, 1536, 128, 64, "f32", 128, True, "wide"),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}steps{}".format(
-    *c[:7], c[7], "_rope" if c[8] else ""))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}steps{}{}".format(
+    *c[:7], c[7], "_rope" if c[8] else "", "_wide" if len(c) > 9 else ""))
 def test_decoding_matches_the_causal_layer(case):
-    B, T, d, e, s, C, dtype, steps, rope = case
-    inp = make(B, T, d, e, s, C, dtype, seed=B * 389 + T + C)
+    B, T, d, e, s, C, dtype, steps, rope = case[:9]
+    heads = case[9] if len(case) > 9 else "workload"
+    inp = make(B, T, d, e, s, C, dtype, seed=B * 389 + T + C, heads=heads)
     got, = _decode(inp, B, T, d, e, s, C, dtype, steps, rope)
     ref = oracle_layer(inp, C, True, rope=rope)[:, :steps]
     assert_close(got, ref, tol_for(dtype), "decoded O")

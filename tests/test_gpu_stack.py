@@ -9,7 +9,7 @@ import chunked_linear_attention_amd as g
 from chunked_linear_attention_amd import inputs
 from oracle import gau_oracle as orc
 
-from _gpu import assert_close, torch_dtype
+from _gpu import assert_close, chunk_errors, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -25,27 +25,37 @@ def _run_stack(X, layers, B, T, d, e, s, C, dtype, causal=True):
     return x.cpu().numpy().astype(np.float64)
 
 
+@pytest.mark.parametrize("heads", ["workload", "wide"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_small_stack_matches_oracle(dtype):
+def test_small_stack_matches_oracle(dtype, heads):
     B, T, d, e, s, C, nl = 2, 512, 256, 512, 128, 128, 3
-    X, layers = inputs.make_stack_inputs(B, T, d, e, s, C, nl, weight_seed=300, x_seed=301, dtype=dtype)
+    X, layers = inputs.make_stack_inputs(B, T, d, e, s, C, nl, weight_seed=300, x_seed=301, dtype=dtype,
+                                         heads=heads)
     got = _run_stack(X, layers, B, T, d, e, s, C, dtype)
     ref = orc.flash_stack_forward(X, layers, C, True)
-    assert_close(got, ref, 1e-4 if dtype == "f32" else 2e-2, "stack")
-    # the layers changed the residual stream (the check is not vacuous)
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    assert_close(got, ref, tol, "stack")
+    # the tolerance applied to what the layers added to the residual stream
+    # (X is exact on both sides), and that contribution is not small
+    assert_close(got - X, ref - X, tol, "stack minus its input")
     assert np.max(np.abs(ref - X)) > 0.1 * np.max(np.abs(X))
 
 
-def test_full_stack_workload_on_causal_prefix():
-    """24 layers at d=1024, B=2, T=8192: the GPU output on the first 512
-    tokens of each sequence must match the oracle run on those tokens alone
-    (every layer is causal and the norm is per token)."""
+def test_full_stack_workload():
+    """24 layers at d=1024, B=2, T=8192, C=256: every token of both
+    sequences against the oracle, the output and the layers' contribution
+    (output minus input) each under the bf16 gate, and every chunk of that
+    contribution under the gate relative to its own largest value."""
     cfg = inputs.WORKLOADS["stack24_bf16_B2_T8192_d1024_C256"]
     B, T, d, e, s, C, nl = (cfg[k] for k in ("B", "T", "d", "e", "s", "C", "layers"))
     X, layers = inputs.make_stack_inputs(**cfg)
+    print("stack24 B=2 T=8192 d=1024: GPU run", flush=True)
     got = _run_stack(X, layers, B, T, d, e, s, C, "bf16")
     assert np.all(np.isfinite(got))
-    P = 512
-    for b in range(B):
-        ref = orc.flash_stack_forward(X[b:b + 1, :P], layers, C, True)
-        assert_close(got[b:b + 1, :P], ref, 2e-2, f"stack prefix row {b}")
+    print("stack24: oracle", flush=True)
+    ref = orc.flash_stack_forward(X, layers, C, True)
+    assert_close(got, ref, 2e-2, "stack24")
+    err = assert_close(got - X, ref - X, 2e-2, "stack24 minus its input")
+    ce = chunk_errors(got - X, ref - X, C)
+    print(f"stack24: delta {err:.2e}, worst per-chunk {ce.max():.2e} (chunk {int(ce.argmax())})", flush=True)
+    assert ce.max() <= 2e-2, f"chunk {int(ce.argmax())}: {ce.max():.3e}"

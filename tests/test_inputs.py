@@ -45,3 +45,19 @@ def test_bf16_workload_values_are_bf16_exact():
     for k in ("X", "W_u", "W_v", "W_z", "W_o"):
         np.testing.assert_array_equal(inputs.round_bf16(a[k]), a[k])
     assert a["relpos"].dtype == np.float32
+
+
+def test_wide_heads_change_only_gamma_and_beta():
+    kw = dict(B=1, T=128, d=128, e=256, s=128, C=64, seed=7, dtype="bf16")
+    a = inputs.make_layer_inputs(**kw)
+    b = inputs.make_layer_inputs(heads="wide", **kw)
+    for k in ("X", "W_u", "W_v", "W_z", "W_o", "relpos"):
+        np.testing.assert_array_equal(a[k], b[k])
+    assert b["beta"].shape == (4, 128) and b["gamma"].shape == (4, 128)
+    assert 0.2 < float(b["beta"].std()) < 0.4 and abs(float(b["beta"].mean())) < 0.05
+    assert 0.4 < float(b["gamma"].std()) < 0.6 and abs(float(b["gamma"].mean()) - 1.0) < 0.1
+    # every head has its own scales and offsets
+    for h in range(4):
+        for k in range(h):
+            assert np.max(np.abs(b["gamma"][h] - b["gamma"][k])) > 0.5
+            assert np.max(np.abs(b["beta"][h] - b["beta"][k])) > 0.3

@@ -275,6 +275,51 @@ def test_stack_first_layer_matches_single_layer():
     np.testing.assert_allclose(out2, ref2, rtol=1e-13, atol=1e-13)
 
 
+def _stack_layers(n, C, d=6, e=8, s=4, seed=60):
+    return [{k: v for k, v in _tiny(1, 8, d, e, s, C, seed=seed + l).items() if k != "X"} for l in range(n)]
+
+
+def test_stack_with_zero_output_weights_is_the_identity():
+    """W_o = 0 in every layer: each block adds exactly zero, so the stack
+    returns its input bit for bit (a dropped shortcut, or a norm applied to
+    the residual stream itself, would not)."""
+    C = 4
+    layers = _stack_layers(3, C)
+    for L in layers:
+        L["W_o"] = np.zeros_like(L["W_o"])
+    X = 3.0 * np.random.default_rng(6).standard_normal((2, 8, 6))
+    np.testing.assert_array_equal(orc.flash_stack_forward(X, layers, C, True), X)
+
+
+@pytest.mark.parametrize("c", [0.5, 7.0])
+def test_stack_layer_sees_a_scale_free_input(c):
+    """Pre-norm: one block adds f(norm(x)) to x, and the RMS norm removes a
+    positive scale, so stack(cX) - cX equals stack(X) - X up to the norm's
+    eps (a post-norm, or a residual taken after the norm, would scale).  X
+    has mean square ~100, so eps = 1e-6 moves the normalised rows by ~1e-8."""
+    C = 4
+    layers = _stack_layers(1, C)
+    X = 10.0 * np.random.default_rng(7).standard_normal((1, 8, 6))
+    a = orc.flash_stack_forward(X, layers, C, True) - X
+    b = orc.flash_stack_forward(c * X, layers, C, True) - c * X
+    np.testing.assert_allclose(b, a, rtol=1e-5, atol=1e-7 * np.max(np.abs(a)))
+    assert np.max(np.abs(a)) > 1e-2
+
+
+def test_stack_is_causal_bitwise():
+    """A causal stack with a per-token norm: outputs before position t do not
+    depend on tokens after t, bit for bit, through every layer."""
+    C = 4
+    layers = _stack_layers(3, C)
+    X = np.random.default_rng(8).standard_normal((1, 8, 6))
+    a = orc.flash_stack_forward(X, layers, C, True)
+    Y = X.copy()
+    Y[:, 5:] = np.random.default_rng(9).standard_normal(Y[:, 5:].shape)
+    b = orc.flash_stack_forward(Y, layers, C, True)
+    np.testing.assert_array_equal(a[:, :5], b[:, :5])
+    assert np.max(np.abs(a[:, 5:] - b[:, 5:])) > 0
+
+
 # ---------------------------------------------------------------- RoPE
 
 def test_rope_frequencies_match_the_printed_sinusoid_helper():
