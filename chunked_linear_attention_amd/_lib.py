@@ -28,8 +28,11 @@ EXPORTS = (
     "gau_workspace_bytes", "gau_workspace_layout", "gau_forward", "gau_forward_stages",
     "gau_stack_workspace_bytes", "gau_stack_forward", "gau_decode_workspace_bytes", "gau_decode_reset",
     "gau_decode_step", "gau_rope_relpos", "gau_backward_workspace_bytes", "gau_backward", "gau_status_string",
-    "gau_probe_mfma",
+    "gau_probe_mfma", "gau_forward_noalloc",
 )
+
+# include/gau.h: the size of gau_forward_noalloc's device scratch array
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class GauConfig(ctypes.Structure):
@@ -78,6 +81,8 @@ def load():
     lib.gau_forward.restype = ctypes.c_int
     lib.gau_forward_stages.argtypes = [cfgp, ctypes.c_int, ctypes.c_int] + layer
     lib.gau_forward_stages.restype = ctypes.c_int
+    lib.gau_forward_noalloc.argtypes = [cfgp] + [P] * 5 + [P] * 3 + [P, P]
+    lib.gau_forward_noalloc.restype = ctypes.c_int
     lib.gau_stack_workspace_bytes.argtypes = [cfgp]
     lib.gau_stack_workspace_bytes.restype = ctypes.c_size_t
     PP = ctypes.POINTER(ctypes.c_void_p)
@@ -200,6 +205,18 @@ def forward(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O, workspace, str
         workspace.numel() * workspace.element_size(), _stream(stream))
     if st != 0:
         raise GauError(st, "gau_forward")
+
+
+def forward_noalloc(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O, stream=None):
+    """gau_forward_noalloc: gau_forward with the workspace in the library's
+    device scratch array (no allocation; gau_workspace_bytes(cfg) must not
+    exceed NOALLOC_SCRATCH_BYTES)."""
+    _check_layer(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O)
+    st = load().gau_forward_noalloc(
+        ctypes.byref(cfg), _ptr(X), _ptr(W_u), _ptr(W_v), _ptr(W_z), _ptr(W_o),
+        _ptr(scale), _ptr(offset), _ptr(relpos), _ptr(O), _stream(stream))
+    if st != 0:
+        raise GauError(st, "gau_forward_noalloc")
 
 
 def stack_forward(cfg, X, layers, workspace, stream=None):

@@ -3,8 +3,18 @@
 // are in include/gau.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/gau.h"
 #include "gau_launch.h"
+
+// Scratch of gau_forward_noalloc: the forward's workspace, at most
+// GAU_NOALLOC_SCRATCH_BYTES, in a device array of this library.  Each device
+// the library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not the device copy: its device
+// address is taken once per device with hipGetSymbolAddress (noalloc_scratch
+// below), and only that address is passed to kernels.
+static __device__ __align__(256) char scratch[GAU_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -611,6 +621,52 @@ gau_status gau_rope_relpos(const float* a, const float* b, int64_t n, int64_t di
     if (gau::launch_rope_relpos(a, b, (int)n, (int)dim, relpos, (hipStream_t)stream) != hipSuccess)
         return GAU_ERR_HIP;
     return GAU_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up on the
+// first call for that device (with it current) and kept for later calls.
+gau_status noalloc_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GAU_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GAU_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GAU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gau_status gau_forward_noalloc(const gau_config* cfg, const void* X, const void* W_u, const void* W_v,
+                               const void* W_z, const void* W_o, const float* scale, const float* offset,
+                               const float* relpos, void* O, void* stream) {
+    gau_status s = check_config(cfg);
+    if (s != GAU_OK) return s;
+    if (cfg->B * cfg->T == 0) return GAU_OK;
+    const LayerPtrs a{X, W_u, W_v, W_z, W_o, scale, offset, relpos};
+    if ((s = check_layer_ptrs(a)) != GAU_OK) return s;
+    if (!O) return GAU_ERR_NULL;
+    if (!aligned16(O)) return GAU_ERR_ALIGN;
+    const size_t need = gau_workspace_bytes(cfg);
+    if (need > (size_t)GAU_NOALLOC_SCRATCH_BYTES) return GAU_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((s = noalloc_scratch(&ws)) != GAU_OK) return s;
+    // the forward writes every workspace entry it reads (nothing needs to
+    // start at zero), so the previous call's contents do not matter
+    return run_stages(cfg, GAU_STAGE_PROJ, GAU_STAGE_OUT, a, O, nullptr, (char*)ws, (hipStream_t)stream);
 }
 
 const char* gau_status_string(int status) {

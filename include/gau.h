@@ -36,8 +36,10 @@
  *
  * Conventions for every entry point:
  *  - Every pointer is caller-owned device memory (HBM of the current HIP
- *    device) unless stated otherwise.  The library allocates nothing, keeps no
- *    global state and may be called from several host threads at once.
+ *    device) unless stated otherwise.  The library allocates nothing and may
+ *    be called from several host threads at once; its only global state is
+ *    the scratch array of gau_forward_noalloc (below) and that array's
+ *    address per device.
  *  - Work is queued on `stream` (a hipStream_t; NULL is the default stream)
  *    and the call returns without synchronising.
  *  - Arguments are checked before anything is queued.  A non-OK status means
@@ -157,6 +159,31 @@ gau_status gau_forward(const gau_config* cfg,
                        const void* W_z, const void* W_o,
                        const float* scale, const float* offset, const float* relpos,
                        void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gau_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace lives in a device array of the
+ * library of GAU_NOALLOC_SCRATCH_BYTES bytes (64 MiB; every device the library
+ * runs on holds one until the process ends); the call itself allocates
+ * nothing.  Arguments, outputs and results as gau_forward (the same kernels in
+ * the same order: O is bitwise equal to gau_forward's).
+ *   GAU_ERR_WORKSPACE if gau_workspace_bytes(cfg) > GAU_NOALLOC_SCRATCH_BYTES
+ *   (at d = 768, e = 1536, s = 128, C = 256, bf16: B*T up to 7168 tokens),
+ *   nothing queued.  GAU_ERR_HIP if the array's device address cannot be
+ *   looked up (done once per device, on the first call with it current).
+ * All calls on one device share its array, which keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on one
+ * device (other streams, other host threads) race and give undefined results;
+ * calls queued in order on one stream do not.
+ */
+#define GAU_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+gau_status gau_forward_noalloc(const gau_config* cfg,
+                               const void* X, const void* W_u, const void* W_v,
+                               const void* W_z, const void* W_o,
+                               const float* scale, const float* offset, const float* relpos,
+                               void* O, void* stream);
 
 /*
  * The six kernels gau_forward queues, in order.  gau_forward_stages runs a

@@ -202,6 +202,21 @@ def test_largest_scan_grid_accepted():
     assert g.workspace_bytes(cfg) > 0
 
 
+def test_noalloc_forward_argument_checks_without_gpu():
+    """gau_forward_noalloc rejects NULL pointers and configurations whose
+    workspace exceeds its 64 MiB scratch before anything touches a GPU."""
+    lib = g.load()
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: rejected first
+    cfg = _cfg()
+    assert lib.gau_forward_noalloc(ctypes.byref(cfg), *([None] * 8), None, None) == 1      # GAU_ERR_NULL
+    big = _cfg(B=1, T=8192, d=768, e=1536, s=128, C=256)
+    assert g.workspace_bytes(big) > g.NOALLOC_SCRATCH_BYTES
+    assert lib.gau_forward_noalloc(ctypes.byref(big), *([fake] * 8), fake, None) == 5       # GAU_ERR_WORKSPACE
+    assert lib.gau_forward_noalloc(ctypes.byref(_cfg(T=500)), *([fake] * 8), fake, None) == 2
+    empty = _cfg(B=0)
+    assert lib.gau_forward_noalloc(ctypes.byref(empty), *([None] * 8), None, None) == 0     # no tokens: no-op
+
+
 def test_status_strings():
     for code in range(7):
         assert g.status_string(code)
