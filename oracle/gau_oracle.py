@@ -43,7 +43,7 @@ design notes):
 * Bias index: b[i, j] = w[C - 1 + j - i] (key position minus query position),
   obtained by carrying out Code 4's pad / tile / slice / reshape / slice steps.
 * The causal mask keeps j <= i (diagonal included) and is applied after relu^2.
-* SiLU on U, V and Z.  No dense-layer biases, no segment masks.  RoPE is
+* SiLU on U, V and Z.  No dense-layer biases.  RoPE is
   optional (off in the layer's plain form, which has no RoPE argument).
 * RoPE itself is not printed on the pages.  ``rope`` rotates the pairs
   (x_i, x_{i+s/2}) by t * theta_i with theta_i = 10000^(-i/(s/2)): the
@@ -53,6 +53,19 @@ design notes):
   the pins fix the rotation's defining properties, not which pairing the
   authors' hidden helper used.
 * Non-causal: every chunk (its own included) feeds the linear term.
+* Segment masks for packed sequences (optional ``chunk_segments``).  The
+  listing's Code 7 builds a chunk-level mask and divides each of its rows by
+  the row's sum (divide_no_nan: an all-zero row stays zero); Code 8 applies it
+  to the chunk summaries only, so the linear term becomes the average of the
+  visible summaries; the local part has no segment mask (wikillm, "Paper vs
+  code" and "Pitfalls", segment masks).  Code 7 itself is not on the pages.
+  Reading taken here: one segment id per chunk (documents packed along the
+  sequence start on chunk boundaries); a segment is a maximal run of
+  consecutive chunks with equal ids; chunk h is visible from chunk g when both
+  lie in one segment and, causal, h < g (non-causal: every chunk of the
+  segment, g included).  Without ``chunk_segments`` the layer is the plain
+  sum of equations 7 and 8.  parity unpinned for the reading itself (which
+  chunks Code 7 counts as visible is not printed); its arithmetic is pinned.
 
 parity pinned: every function here is checked in tests/test_oracle.py against
 brute force, closed forms or invariants that do not reuse its code.
@@ -169,6 +182,24 @@ def rope_relpos(a, b, n):
     return np.concatenate([t[::-1, 0][:-1], t[0, :]])
 
 
+def segment_chunk_mask(chunk_segments, causal):
+    """The row-normalised chunk mask M[b, g, h] of Code 7 as described on the
+    wikillm page ("Paper vs code", segment masks): 1 where chunk h is visible
+    from chunk g, each row divided by its sum (divide_no_nan: rows with no
+    visible chunk stay 0).  A segment is a maximal run of consecutive chunks
+    with equal ids; visible = same segment and, when causal, h < g."""
+    seg = np.asarray(chunk_segments)
+    B, G = seg.shape
+    run = np.zeros((B, G), dtype=np.int64)          # run index of each chunk
+    run[:, 1:] = np.cumsum(seg[:, 1:] != seg[:, :-1], axis=1)
+    same = run[:, :, None] == run[:, None, :]
+    if causal:
+        same = same & (np.arange(G)[None, :, None] > np.arange(G)[None, None, :])
+    M = same.astype(np.float64)
+    n = M.sum(axis=-1, keepdims=True)
+    return np.divide(M, n, out=np.zeros_like(M), where=n > 0)
+
+
 def heads(Z, gamma, beta):
     """The four heads Q_quad, K_quad, Q_lin, K_lin from Z.
 
@@ -182,7 +213,7 @@ def heads(Z, gamma, beta):
 
 def flash_forward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
                   quad_scale=None, lin_scale=None, return_intermediates=False, use_rope=False,
-                  parts="both"):
+                  parts="both", chunk_segments=None):
     """Forward pass of one FLASH layer (GAU with mixed chunk attention).
 
     X: (B, T, d).  W_u, W_v: (d, e).  W_z: (d, s).  W_o: (e, d).
@@ -194,6 +225,9 @@ def flash_forward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
     the linear cross-chunk term (the LocalOnly / GlobalOnly ablation
     variants: wikillm, "Ablation variants"; Su's post reports both fall well
     short of the full model).
+    chunk_segments (B, G) ints: packed sequences; the linear term of chunk g
+    becomes the average of the summaries of the chunks visible from it
+    (segment_chunk_mask), the local part is unchanged.
 
     Steps, in the order of the FLASH block (wikillm pseudocode; blog "Mixed
     Chunking"; papercache 3.2):
@@ -239,8 +273,14 @@ def flash_forward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
     # step 4: one s x e summary per chunk
     S = (Klg.swapaxes(-1, -2) @ Vg) * lin_scale
 
-    # step 5: chunk-level sum, exclusive prefix when causal
-    if causal:
+    # step 5: chunk-level sum, exclusive prefix when causal; with segments,
+    # the row-normalised chunk mask applied to the summaries
+    if chunk_segments is not None:
+        if np.shape(chunk_segments) != (B, G):
+            raise ValueError("chunk_segments must have shape (B, T / C)")
+        M = segment_chunk_mask(chunk_segments, causal)
+        P = np.einsum("bgh,bhse->bgse", M, S)
+    elif causal:
         incl = np.cumsum(S, axis=1)
         P = np.concatenate([np.zeros_like(S[:, :1]), incl[:, :-1]], axis=1)
     else:
@@ -271,7 +311,7 @@ def flash_forward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
 # --------------------------------------------------------------------------
 
 def flash_forward_bruteforce(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal,
-                             quad_scale=None, lin_scale=None, use_rope=False):
+                             quad_scale=None, lin_scale=None, use_rope=False, chunk_segments=None):
     """The layer as O = (U * (A V)) W_o with the full T x T matrix A.
 
     A per-token double loop builds A[t, tau] (blog, "Gated Attention" GAU
@@ -283,6 +323,9 @@ def flash_forward_bruteforce(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, caus
         (causal), or for every tau (non-causal, own chunk included).
     With use_rope, each head vector of token t is rotated pair by pair,
     (h_i, h_{i+s/2}) by the angle t * 10000^(-i/(s/2)), written out here.
+    With chunk_segments, the linear entry is kept only when chunk(tau) is in
+    the same segment (run of equal consecutive ids) as chunk(t), and divided
+    by the number of chunks visible from chunk(t), counted here by a loop.
     Every product is written out per token; nothing is shared with
     ``flash_forward`` beyond the SiLU definition.  Pure Python loops: keep
     T small.
@@ -319,6 +362,22 @@ def flash_forward_bruteforce(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, caus
                         x0, x1 = hv[i], hv[i + half]
                         hv[i] = x0 * np.cos(ang) - x1 * np.sin(ang)
                         hv[i + half] = x1 * np.cos(ang) + x0 * np.sin(ang)
+        G = T // C
+        if chunk_segments is not None:
+            ids = [int(x) for x in np.asarray(chunk_segments)[b]]
+            first = [0] * G                      # first chunk of each chunk's segment
+            for g in range(1, G):
+                first[g] = first[g - 1] if ids[g] == ids[g - 1] else g
+            last = [G - 1] * G                   # last chunk of each chunk's segment
+            for g in range(G - 2, -1, -1):
+                last[g] = last[g + 1] if ids[g] == ids[g + 1] else g
+
+        def visible(g, h):
+            if chunk_segments is not None and not (first[g] <= h <= last[g]):
+                return False
+            return h < g if causal else True
+
+        nvis = [sum(1 for h in range(G) if visible(g, h)) for g in range(G)]
         A = np.zeros((T, T))
         for t in range(T):
             for tau in range(T):
@@ -327,8 +386,9 @@ def flash_forward_bruteforce(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, caus
                 if same and (tau <= t or not causal):
                     sc = float(np.dot(qq[t], kq[tau])) * quad_scale + w[C - 1 + (tau % C) - (t % C)]
                     a += max(sc, 0.0) ** 2
-                if (not causal) or (tau // C) < (t // C):
-                    a += float(np.dot(ql[t], kl[tau])) * lin_scale
+                if visible(t // C, tau // C):
+                    lin = float(np.dot(ql[t], kl[tau])) * lin_scale
+                    a += lin / nvis[t // C] if chunk_segments is not None else lin
                 A[t, tau] = a
         out[b] = (u * (A @ v)) @ W_o
     return out

@@ -488,3 +488,81 @@ def test_backward_matches_central_differences(B, T, C, causal):
             dn[pk][idx] -= h
             fd[idx] = (f(up) - f(dn)) / (2 * h)
         np.testing.assert_allclose(g[k], fd, rtol=1e-5, atol=1e-6, err_msg=k)
+
+
+# ---------------------------------------------------------------- segment masks
+
+SEGMENTS = [
+    # B, T, C, causal, per-row chunk ids
+    (1, 24, 4, True, [[0, 0, 1, 1, 1, 2]]),
+    (2, 24, 4, False, [[3, 3, 3, 8, 8, 8], [1, 2, 3, 4, 5, 6]]),
+    (1, 16, 2, True, [[0, 1, 0, 0, 2, 2, 2, 2]]),   # an id that comes back starts a new segment
+    (2, 12, 3, True, [[7, 7, 7, 7], [0, 1, 1, 1]]),
+    (1, 12, 4, False, [[0, 0, 0]]),
+]
+
+
+@pytest.mark.parametrize("case", SEGMENTS, ids=lambda c: f"B{c[0]}_T{c[1]}_C{c[2]}_{'causal' if c[3] else 'full'}")
+def test_segmented_chunked_equals_bruteforce(case):
+    B, T, C, causal, seg = case
+    p = _tiny(B, T, 5, 6, 4, C, seed=T + C + B)
+    seg = np.array(seg)
+    got = _run(orc.flash_forward, p, C, causal, chunk_segments=seg)
+    ref = _run(orc.flash_forward_bruteforce, p, C, causal, chunk_segments=seg)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+    # the segments matter: the unsegmented layer differs
+    assert np.max(np.abs(_run(orc.flash_forward, p, C, causal) - ref)) > 1e-3 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_one_segment_averages_the_visible_summaries(causal):
+    """One segment per row: the linear term of chunk g is the plain layer's
+    with its summaries divided by the number of visible chunks (g when
+    causal, G otherwise), i.e. the plain layer with lin_scale / n, chunk by
+    chunk; chunk 0 of a causal row sees nothing (divide_no_nan) and equals
+    the plain layer's chunk 0."""
+    B, T, C = 2, 20, 4
+    G = T // C
+    p = _tiny(B, T, 5, 6, 4, C, seed=71)
+    seg = np.zeros((B, G), dtype=int)
+    got = _run(orc.flash_forward, p, C, causal, chunk_segments=seg)
+    for g in range(G):
+        n = g if causal else G
+        ls = (1.0 / C) / n if n > 0 else 1.0 / C
+        ref = _run(orc.flash_forward, p, C, causal, lin_scale=ls)
+        np.testing.assert_allclose(got[:, g * C:(g + 1) * C], ref[:, g * C:(g + 1) * C], rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_packed_sequences_equal_separate_runs(causal):
+    """Two sequences packed into one row, each a segment starting on a chunk
+    boundary: the packed output is the two rows run on their own, each as one
+    segment (the local part never crosses a chunk, and the mask keeps the
+    linear part inside each segment)."""
+    C, T1, T2 = 4, 12, 8
+    p = _tiny(1, T1 + T2, 5, 6, 4, C, seed=72)
+    seg = np.array([[4] * (T1 // C) + [9] * (T2 // C)])
+    packed = _run(orc.flash_forward, p, C, causal, chunk_segments=seg)
+    for lo, hi in ((0, T1), (T1, T1 + T2)):
+        q = dict(p, X=p["X"][:, lo:hi])
+        alone = _run(orc.flash_forward, q, C, causal, chunk_segments=np.zeros((1, (hi - lo) // C), int))
+        np.testing.assert_allclose(packed[:, lo:hi], alone, rtol=1e-11, atol=1e-13)
+
+
+def test_segment_ids_matter_only_through_runs():
+    """Relabelling the ids, run for run, changes nothing (bitwise)."""
+    C, T = 4, 24
+    p = _tiny(1, T, 5, 6, 4, C, seed=73)
+    a = _run(orc.flash_forward, p, C, True, chunk_segments=np.array([[0, 0, 1, 1, 1, 2]]))
+    b = _run(orc.flash_forward, p, C, True, chunk_segments=np.array([[-5, -5, 40, 40, 40, 7]]))
+    np.testing.assert_array_equal(a, b)
+
+
+def test_segment_mask_rows():
+    """The mask's rows: each sums to 1 or is all zero (divide_no_nan); the
+    first chunk of a causal segment sees nothing."""
+    M = orc.segment_chunk_mask(np.array([[0, 0, 1, 1, 1, 0]]), True)[0]
+    np.testing.assert_array_equal(M.sum(axis=1), [0, 1, 0, 1, 1, 0])
+    assert M[4, 2] == M[4, 3] == 0.5 and M[3, 2] == 1.0 and M[1, 0] == 1.0
+    N = orc.segment_chunk_mask(np.array([[0, 0, 1]]), False)[0]
+    np.testing.assert_array_equal(N, [[0.5, 0.5, 0], [0.5, 0.5, 0], [0, 0, 1]])
