@@ -12,7 +12,7 @@ import numpy as np
 from . import inputs  # noqa: F401
 from ._lib import (  # noqa: F401
     GAU_BF16, GAU_F32, GAU_FULL, GAU_GLOBAL_ONLY, GAU_LOCAL_ONLY, STAGE_ATTN, STAGE_OUT, STAGE_PROJ, STAGE_SCAN, STAGE_SCORES, STAGE_STATE, EXPORTS,
-    GRAD_NAMES, NOALLOC_SCRATCH_BYTES, GauError, backward, backward_workspace_bytes, decode_reset, decode_step, decode_workspace_bytes, forward, forward_noalloc, forward_stages, load, make_config,
+    GRAD_NAMES, NOALLOC_SCRATCH_BYTES, GauError, backward, backward_workspace_bytes, decode_reset, decode_step, decode_workspace_bytes, forward, forward_noalloc, forward_segmented, forward_stages, load, make_config,
     probe_mfma, rope_relpos, stack_forward, stack_workspace_bytes,
     status_string, workspace_bytes, workspace_layout,
 )

@@ -28,7 +28,7 @@ EXPORTS = (
     "gau_workspace_bytes", "gau_workspace_layout", "gau_forward", "gau_forward_stages",
     "gau_stack_workspace_bytes", "gau_stack_forward", "gau_decode_workspace_bytes", "gau_decode_reset",
     "gau_decode_step", "gau_rope_relpos", "gau_backward_workspace_bytes", "gau_backward", "gau_status_string",
-    "gau_probe_mfma", "gau_forward_noalloc",
+    "gau_probe_mfma", "gau_forward_noalloc", "gau_forward_segmented",
 )
 
 # include/gau.h: the size of gau_forward_noalloc's device scratch array
@@ -83,6 +83,8 @@ def load():
     lib.gau_forward_stages.restype = ctypes.c_int
     lib.gau_forward_noalloc.argtypes = [cfgp] + [P] * 5 + [P] * 3 + [P, P]
     lib.gau_forward_noalloc.restype = ctypes.c_int
+    lib.gau_forward_segmented.argtypes = [cfgp, P] + layer
+    lib.gau_forward_segmented.restype = ctypes.c_int
     lib.gau_stack_workspace_bytes.argtypes = [cfgp]
     lib.gau_stack_workspace_bytes.restype = ctypes.c_size_t
     PP = ctypes.POINTER(ctypes.c_void_p)
@@ -205,6 +207,22 @@ def forward(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O, workspace, str
         workspace.numel() * workspace.element_size(), _stream(stream))
     if st != 0:
         raise GauError(st, "gau_forward")
+
+
+def forward_segmented(cfg, chunk_segments, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O, workspace,
+                      stream=None):
+    """gau_forward_segmented: the layer over packed sequences; chunk_segments
+    is an int32 device tensor [B, T / C] of per-chunk segment ids."""
+    import torch
+    _check_layer(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O)
+    _check(chunk_segments, "chunk_segments", torch.int32, cfg.B * (cfg.T // cfg.C))
+    _check(workspace, "workspace")
+    st = load().gau_forward_segmented(
+        ctypes.byref(cfg), _ptr(chunk_segments), _ptr(X), _ptr(W_u), _ptr(W_v), _ptr(W_z), _ptr(W_o),
+        _ptr(scale), _ptr(offset), _ptr(relpos), _ptr(O), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise GauError(st, "gau_forward_segmented")
 
 
 def forward_noalloc(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O, stream=None):

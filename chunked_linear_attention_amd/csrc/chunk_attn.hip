@@ -66,7 +66,7 @@ __global__ __launch_bounds__(WGM * WGN * kWave) void chunk_attn_kernel(AttnParam
     const int f0 = ft * BF, q0 = qt * BQ;
     const size_t tok0 = (size_t)b * p.T + (size_t)g * p.C;
     const int keys = p.causal ? q0 + BQ : p.C;
-    const size_t pidx = p.causal ? (size_t)chunk : (size_t)b;
+    const size_t pidx = (p.causal || p.p_chunked) ? (size_t)chunk : (size_t)b;
 
     const KSeg a0{(const char*)p.Vt + (((size_t)b * p.e + f0) * p.T + (size_t)g * p.C) * EB, (size_t)p.T * EB,
                   p.local ? keys / KELEMS : 0};

@@ -17,6 +17,15 @@
 // causal case P may be S itself (the forward runs the scan in place): a
 // thread reads each of its entries of S_g before it writes the same entries
 // of P_g, and no other thread touches them, so S and P are not restrict.
+//
+// With segment ids (packed sequences; wikillm "Paper vs code" and
+// "Pitfalls", segment masks: the listing's chunk mask, each row divided by
+// its sum, applied to the summaries) a segment is a run of consecutive
+// chunks with equal ids, and P_g is the average of the summaries visible
+// from chunk g: causal, S_h for the h < g of g's segment (0 when there is
+// none); non-causal, every S_h of the segment.  One state per chunk in
+// both cases; the non-causal pass reads a whole segment's S before it writes
+// its P, so it too may run in place.
 #include "gau_device.h"
 #include "gau_launch.h"
 
@@ -65,7 +74,33 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanParams p) {
     char* P = (char*)p.P;
     const size_t cstride = stride * EB;  // bytes between consecutive chunks
     f32x4_t run = {0.f, 0.f, 0.f, 0.f};
-    if (p.causal) {
+    if (p.seg) {
+        const int32_t* sg = p.seg + b * p.G;
+        char* out = P + ((size_t)b * p.G * stride + (size_t)v * 4) * EB;
+        if (p.causal) {
+            int start = 0;  // first chunk of the current segment
+            for (int g = 0; g < p.G; ++g) {
+                if (g > 0 && sg[g] != sg[g - 1]) {
+                    run = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    start = g;
+                }
+                const f32x4_t s0 = get4<T>(S + (size_t)g * cstride);
+                const int n = g - start;  // chunks visible from g
+                put4<T>(out + (size_t)g * cstride, n > 0 ? run * (1.0f / (float)n) : run);
+                run += s0;
+            }
+        } else {
+            for (int a = 0; a < p.G;) {
+                int z = a + 1;  // the segment is chunks a .. z-1
+                while (z < p.G && sg[z] == sg[a]) ++z;
+                for (int g = a; g < z; ++g) run += get4<T>(S + (size_t)g * cstride);
+                const f32x4_t avg = run * (1.0f / (float)(z - a));
+                for (int g = a; g < z; ++g) put4<T>(out + (size_t)g * cstride, avg);
+                run = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                a = z;
+            }
+        }
+    } else if (p.causal) {
         char* out = P + ((size_t)b * p.G * stride + (size_t)v * 4) * EB;
         int g = 0;
         for (; g + 4 <= p.G; g += 4) {

@@ -130,11 +130,14 @@ gau::StateParams state_params(const gau_config* c, const gau_ws_layout& L, char*
 }
 
 // Stages first..last of one layer.  `residual` != nullptr makes the output
-// stage write O = residual + Y W_o in fp32.
+// stage write O = residual + Y W_o in fp32.  `seg` != nullptr ([B, G] chunk
+// segment ids): the scan forms one averaged state per chunk, in place over S
+// (also when non-causal), and the attention stage reads it per chunk.
 gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs& a, void* O, const float* residual,
-                      char* ws, hipStream_t st, bool shared = true) {
+                      char* ws, hipStream_t st, bool shared = true, const int32_t* seg = nullptr) {
     gau_ws_layout L;
     layout(c, &L, shared);
+    if (seg) L.P = L.S;
     const bool bf = c->dtype == GAU_BF16;
     const int M = (int)(c->B * c->T);
     const int G = (int)(c->T / c->C);
@@ -161,7 +164,7 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
             case GAU_STAGE_SCAN: {
                 if (!global) break;
                 gau::ScanParams p{ws + L.S, ws + L.P, (int)c->B, G, (int)(c->e * c->s),
-                                  c->causal ? 1 : 0};
+                                  c->causal ? 1 : 0, seg};
                 e = gau::launch_chunk_scan(p, bf, st);
                 break;
             }
@@ -179,7 +182,7 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
             case GAU_STAGE_ATTN: {
                 gau::AttnParams p{ws + L.A, ws + L.Q_lin, ws + L.Vt, ws + L.P, ws + L.U, ws + L.Y, (int)c->B,
                                   (int)c->T, (int)c->e, (int)c->s, (int)c->C, c->causal ? 1 : 0,
-                                  local ? 1 : 0, global ? 1 : 0};
+                                  local ? 1 : 0, global ? 1 : 0, seg ? 1 : 0};
                 e = gau::launch_chunk_attn(p, bf, st);
                 break;
             }
@@ -478,6 +481,22 @@ gau_status gau_forward(const gau_config* cfg, const void* X, const void* W_u, co
                        void* workspace, size_t workspace_bytes, void* stream) {
     return gau_forward_stages(cfg, GAU_STAGE_PROJ, GAU_STAGE_OUT, X, W_u, W_v, W_z, W_o, scale, offset, relpos, O,
                               workspace, workspace_bytes, stream);
+}
+
+gau_status gau_forward_segmented(const gau_config* cfg, const int32_t* chunk_segments, const void* X,
+                                 const void* W_u, const void* W_v, const void* W_z, const void* W_o,
+                                 const float* scale, const float* offset, const float* relpos, void* O,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    gau_status s = check_config(cfg);
+    if (s != GAU_OK) return s;
+    if (cfg->B * cfg->T == 0) return GAU_OK;
+    const LayerPtrs a{X, W_u, W_v, W_z, W_o, scale, offset, relpos};
+    if ((s = check_layer_ptrs(a)) != GAU_OK) return s;
+    if (!chunk_segments || !O || !workspace) return GAU_ERR_NULL;
+    if (!aligned16(chunk_segments) || !aligned16(O) || !aligned16(workspace)) return GAU_ERR_ALIGN;
+    if (workspace_bytes < gau_workspace_bytes(cfg)) return GAU_ERR_WORKSPACE;
+    return run_stages(cfg, GAU_STAGE_PROJ, GAU_STAGE_OUT, a, O, nullptr, (char*)workspace, (hipStream_t)stream,
+                      true, chunk_segments);
 }
 
 size_t gau_stack_workspace_bytes(const gau_config* cfg) {

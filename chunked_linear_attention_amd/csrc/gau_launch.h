@@ -34,12 +34,14 @@ struct StateParams {
     float lin_scale;
 };
 
-// Exclusive prefix over chunks (causal) or the total (non-causal).
+// Exclusive prefix over chunks (causal) or the total (non-causal); with
+// segment ids, the average over the chunks visible in the chunk's segment.
 struct ScanParams {
     const void* S;   // [B, G, e, s], element type of the layer
-    void* P;         // [B, G, e, s] causal (may be S: scanned in place), [B, 1, e, s] otherwise
+    void* P;         // [B, G, e, s] causal or segmented (may be S: scanned in place), [B, 1, e, s] otherwise
     int B, G, es;    // es = e * s
     int causal;
+    const int32_t* seg;  // [B, G] chunk segment ids, or nullptr (no segments)
 };
 
 // Per-chunk attention weights A_g = relu^2(quad_scale Q_quad K_quad^T + Bias),
@@ -66,6 +68,7 @@ struct AttnParams {
     int B, T, e, s, C;
     int causal;
     int local, global;  // which terms enter Y (the LocalOnly / GlobalOnly variants)
+    int p_chunked;      // P holds one state per chunk also when non-causal (segments)
 };
 
 // Output projection O = Y W_o (optionally O = residual + Y W_o in fp32).

@@ -161,6 +161,32 @@ gau_status gau_forward(const gau_config* cfg,
                        void* O, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The layer over packed sequences: gau_forward with a segment mask on the
+ * linear (cross-chunk) term.  The listing's Code 7 builds a chunk-level mask
+ * and divides each row by its sum (divide_no_nan), and Code 8 applies it to
+ * the chunk summaries, so the linear term becomes an average over the visible
+ * chunks; the local (in-chunk) part has no segment mask (wikillm, "Paper vs
+ * code" and "Pitfalls", segment masks).  Here:
+ *   chunk_segments [B, G] int32 device array, one id per chunk (documents
+ *     packed along a sequence start on chunk boundaries).  A segment is a run
+ *     of consecutive chunks with equal ids (an id that comes back after
+ *     another starts a new segment).  Chunk h is visible from chunk g when
+ *     both lie in one segment and, causal, h < g (non-causal: every chunk of
+ *     the segment, g included).
+ *   V_lin_g = Q_lin_g P_g with P_g = (1/n_g) sum of the visible S_h (n_g of
+ *     them; P_g = 0 when n_g = 0, e.g. the first chunk of a causal segment).
+ * Everything else (arguments, checks, status codes, the workspace size) as
+ * gau_forward; chunk_segments must be non-NULL and 16-byte aligned.  In the
+ * workspace, the P region is S's (the states are averaged in place, one per
+ * chunk, also when non-causal).
+ */
+gau_status gau_forward_segmented(const gau_config* cfg, const int32_t* chunk_segments,
+                                 const void* X, const void* W_u, const void* W_v,
+                                 const void* W_z, const void* W_o,
+                                 const float* scale, const float* offset, const float* relpos,
+                                 void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gau_forward without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  The workspace lives in a device array of the

@@ -62,10 +62,12 @@ def ws_array(ws, layout, name, shape, dtype):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def oracle_layer(inp, C, causal, quad_scale=None, lin_scale=None, intermediates=False, rope=False, parts="both"):
+def oracle_layer(inp, C, causal, quad_scale=None, lin_scale=None, intermediates=False, rope=False, parts="both",
+                 chunk_segments=None):
     return orc.flash_forward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"],
                              inp["beta"], inp["relpos"], C, causal, quad_scale, lin_scale,
-                             return_intermediates=intermediates, use_rope=rope, parts=parts)
+                             return_intermediates=intermediates, use_rope=rope, parts=parts,
+                             chunk_segments=chunk_segments)
 
 
 def rel_err(got, ref):

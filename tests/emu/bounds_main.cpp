@@ -104,9 +104,16 @@ static void run(const Cfg& c, const std::string& only) {
     StateParams stp{Vt, Klt, S, c.B, c.T, c.e, c.s, c.C, 1.0f / c.C};
     t("chunk_state", [&] { CHECK(launch_chunk_state(stp, c.bf, nullptr)); });
     t("chunk_scores_state", [&] { CHECK(launch_chunk_scores_state(sp, stp, c.bf, nullptr)); });
-    ScanParams scp{S, P, c.B, G, c.e * c.s, c.causal ? 1 : 0};
+    ScanParams scp{S, P, c.B, G, c.e * c.s, c.causal ? 1 : 0, nullptr};
     t("chunk_scan", [&] { CHECK(launch_chunk_scan(scp, c.bf, nullptr)); });
-    AttnParams ap{A, Ql, Vt, P, U, Y, c.B, c.T, c.e, c.s, c.C, c.causal ? 1 : 0, 1, 1};
+    // segmented: one state per chunk (in place over S), ids in an exact-size array
+    int32_t* seg = (int32_t*)buf((size_t)c.B * G * 4);
+    for (int i = 0; i < c.B * G; ++i) seg[i] = (i / 2) % 3;
+    ScanParams scs{S, S, c.B, G, c.e * c.s, c.causal ? 1 : 0, seg};
+    t("chunk_scan_segmented", [&] { CHECK(launch_chunk_scan(scs, c.bf, nullptr)); });
+    AttnParams aps{A, Ql, Vt, S, U, Y, c.B, c.T, c.e, c.s, c.C, c.causal ? 1 : 0, 1, 1, 1};
+    t("chunk_attn_segmented", [&] { CHECK(launch_chunk_attn(aps, c.bf, nullptr)); });
+    AttnParams ap{A, Ql, Vt, P, U, Y, c.B, c.T, c.e, c.s, c.C, c.causal ? 1 : 0, 1, 1, 0};
     t("chunk_attn", [&] { CHECK(launch_chunk_attn(ap, c.bf, nullptr)); });
     AttnParams apu = ap;
     apu.U = nullptr;  // no gate (the backward's recompute of the attention output)
@@ -126,6 +133,18 @@ static void run(const Cfg& c, const std::string& only) {
         int st = gau_forward(&cfg, X, Wu, Wv, Wz, Wo, sc, of, rp, O, ws, wsb, nullptr);
         if (st != GAU_OK) {
             fprintf(stderr, "gau_forward status %d\n", st);
+            exit(1);
+        }
+        free(ws);
+    });
+    t("gau_forward_segmented", [&] {
+        gau_config cfg{c.B, c.T, c.d, c.e, c.s, c.C, c.causal ? 1 : 0, c.bf ? GAU_BF16 : GAU_F32, 1.0f / c.C,
+                       1.0f / c.C};
+        const size_t wsb = gau_workspace_bytes(&cfg);
+        void* ws = buf(wsb);
+        int st = gau_forward_segmented(&cfg, seg, X, Wu, Wv, Wz, Wo, sc, of, rp, O, ws, wsb, nullptr);
+        if (st != GAU_OK) {
+            fprintf(stderr, "gau_forward_segmented status %d\n", st);
             exit(1);
         }
         free(ws);
@@ -157,7 +176,7 @@ static void run(const Cfg& c, const std::string& only) {
     });
     for (void* p : {X, Wu, Wv, Wz, Wo, (void*)sc, (void*)of, (void*)rp, U, Vt, Qq, Kq, Ql, Klt, (void*)S, P, A, Y, O,
                     (void*)Of, (void*)ra, (void*)rb, (void*)rw, dx, dO, (void*)dP, dKq, dV, dKl, (void*)du,
-                    (void*)dz, dy})
+                    (void*)dz, dy, (void*)seg})
         free(p);
 }
 

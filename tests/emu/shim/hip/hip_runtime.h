@@ -82,3 +82,15 @@ using std::min;
 #define hipGetLastError() ::emu::last_error()
 #define hipLaunchKernelGGL(kernel, grid, block, lds, stream, ...) \
     ::emu::launch(#kernel, (const void*)(kernel), [=]() { kernel(__VA_ARGS__); }, dim3(grid), dim3(block), (lds), (stream))
+
+// Device symbols: on the host emulation a __device__ array is an ordinary
+// host array, so its "device address" is its address; one device (0).
+#define HIP_SYMBOL(x) ((const void*)&(x))
+inline hipError_t hipGetDevice(int* dev) {
+    *dev = 0;
+    return hipSuccess;
+}
+inline hipError_t hipGetSymbolAddress(void** p, const void* sym) {
+    *p = const_cast<void*>(sym);
+    return hipSuccess;
+}

@@ -154,6 +154,60 @@ def test_emulated_kernels_match_oracle(emu, case, late):
         assert err <= tol, f"{name}: {err:.3e} > {tol}"
 
 
+SEG_CASES = [
+    # B, T, d, e, s, C, dtype, causal, per-row chunk ids
+    (1, 512, 128, 256, 128, 64, "f32", True, [[0, 0, 0, 1, 1, 2, 2, 2]]),
+    (2, 512, 128, 256, 128, 128, "bf16", False, [[5, 5, 6, 6], [1, 2, 2, 1]]),
+    (1, 1024, 128, 1024, 128, 128, "bf16", True, [[0, 1, 1, 1, 0, 0, 3, 3]]),
+    (2, 256, 128, 256, 256, 64, "f32", False, [[0, 0, 0, 0], [0, 1, 2, 3]]),
+]
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}".format(
+    *c[:7], "causal" if c[7] else "full"))
+def test_emulated_segmented_layer_matches_oracle(emu, case):
+    """gau_forward_segmented on the emulation (copies landing at their waits)
+    against the oracle's segment-masked layer: the output and the averaged
+    per-chunk states it leaves in the S region."""
+    B, T, d, e, s, C, dtype, causal, seg = case
+    bf = dtype == "bf16"
+    emu.emu_set_mode(1, 1)
+    P = ctypes.c_void_p
+    emu.gau_forward_segmented.argtypes = [ctypes.POINTER(GauConfig), P] + [P] * 9 + [P, ctypes.c_size_t, P]
+    emu.gau_forward_segmented.restype = ctypes.c_int
+    inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=B * 53 + T + C, dtype=dtype, heads="wide")
+    cfg = GauConfig(B, T, d, e, s, C, 1 if causal else 0, 1 if bf else 0, 1.0 / C, 1.0 / C, 0, 0)
+    X = _host(inp["X"], bf)
+    W = {k: _host(np.ascontiguousarray(inp[k].T), bf) for k in ("W_u", "W_v", "W_z", "W_o")}
+    sc, of, rp = (np.ascontiguousarray(inp[k], np.float32) for k in ("gamma", "beta", "relpos"))
+    segr = np.zeros(len(seg) * len(seg[0]) + 4, np.int32)
+    sega = segr[(-segr.ctypes.data) % 16 // 4:][:B * (T // C)].reshape(B, T // C)
+    sega[:] = np.array(seg, np.int32)
+    O = np.zeros((B, T, d), np.uint16 if bf else np.float32)
+    wsb = emu.gau_workspace_bytes(ctypes.byref(cfg))
+    raw = np.full(wsb + 256, 0xFF, np.uint8)
+    ws = raw[(-raw.ctypes.data) % 256:][:wsb]
+    ptr = lambda a: P(a.ctypes.data)
+    assert emu.gau_forward_segmented(ctypes.byref(cfg), ptr(sega), ptr(X), ptr(W["W_u"]), ptr(W["W_v"]),
+                                     ptr(W["W_z"]), ptr(W["W_o"]), ptr(sc), ptr(of), ptr(rp), ptr(O), ptr(ws),
+                                     wsb, None) == 0
+    L = GauWsLayout()
+    assert emu.gau_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)) == 0
+    ref, im = orc.flash_forward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"],
+                                inp["beta"], inp["relpos"], C, causal, return_intermediates=True,
+                                chunk_segments=np.array(seg))
+    conv = inputs.bf16_bits_to_f32 if bf else (lambda a: a)
+    eb = 2 if bf else 4
+    G = T // C
+    n = B * G * e * s
+    Pg = conv(ws[L.S:L.S + eb * n].view(np.uint16 if bf else np.float32).reshape(B, G, e, s)).astype(np.float64)
+    tol = 2e-2 if bf else 1e-4
+    for name, got, want in (("P", Pg, im["P"].transpose(0, 1, 3, 2)), ("O", conv(O).astype(np.float64), ref)):
+        assert np.all(np.isfinite(got)), name
+        err = np.max(np.abs(got - want)) / np.max(np.abs(want))
+        assert err <= tol, f"{name}: {err:.3e} > {tol}"
+
+
 @pytest.mark.parametrize("dtype,B,heads", [("f32", 2, "workload"), ("bf16", 2, "workload"), ("bf16", 18, "workload"),
                                            ("f32", 2, "wide"), ("bf16", 18, "wide")])
 def test_emulated_decoding_matches_the_causal_layer(emu, dtype, B, heads):
