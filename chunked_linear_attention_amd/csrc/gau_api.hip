@@ -148,13 +148,8 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
             case GAU_STAGE_PROJ: {
                 gau::ProjParams p{a.X, a.W_u, a.W_v, a.W_z, a.scale, a.offset, ws + L.U, ws + L.Vt,
                                   ws + L.Q_quad, ws + L.K_quad, ws + L.Q_lin, ws + L.K_lin_t,
-                                  M, (int)c->T, (int)c->d, (int)c->e, (int)c->s};
+                                  M, (int)c->T, (int)c->d, (int)c->e, (int)c->s, c->rope};
                 e = gau::launch_proj(p, bf, st);
-                if (e == hipSuccess && c->rope) {
-                    const gau::RopeParams r{ws + L.Q_quad, ws + L.K_quad, ws + L.Q_lin, ws + L.K_lin_t, (int)c->B,
-                                            (int)c->T, M, (int)c->s};
-                    e = gau::launch_rope_heads(r, bf, st);
-                }
                 break;
             }
             case GAU_STAGE_STATE: {

@@ -66,6 +66,16 @@ __device__ __forceinline__ float silu_grad(float h) {
 // in fp64 (angles t * theta reach about 10^4 rad).
 __device__ __forceinline__ double rope_theta(int i, int half) { return pow(10000.0, -(double)i / (double)half); }
 
+// cos and sin of the rotary angle t * theta: the angle is formed in fp64 and
+// reduced to [-pi, pi] there (at t ~ 10^5 an fp32 product would be off by
+// 10^-2 rad); only the reduced angle's cosine and sine are fp32 (about 1 ulp).
+__device__ __forceinline__ void rope_cos_sin(double t, double theta, float& c, float& s) {
+    constexpr double kTwoPi = 6.283185307179586476925287;
+    const double a = t * theta;
+    const float r = (float)(a - kTwoPi * rint(a / kTwoPi));
+    sincosf(r, &s, &c);
+}
+
 // Allow kernel `Kernel` more than the default dynamic LDS (the attribute is set
 // once per kernel).
 template <auto Kernel>

@@ -22,6 +22,7 @@ struct ProjParams {
     void* Ql;   // [M, s]
     void* Klt;  // [B, s, T]
     int M, T, d, e, s;
+    int rope;   // 1: the four heads rotated by position t = m mod T (in the epilogue)
 };
 
 // Per-chunk state S_g^T = lin_scale * V_g^T K_lin_g, [B, G, e, s] in the
@@ -99,17 +100,7 @@ struct NormParams {
     float eps;
 };
 
-hipError_t launch_proj(const ProjParams& p, bool bf16_storage, hipStream_t st);  // U, Vt, Z heads
-// Rotary position embedding of the four heads, in place.
-struct RopeParams {
-    void* Qq;   // [M, s]
-    void* Kq;   // [M, s]
-    void* Ql;   // [M, s]
-    void* Klt;  // [B, s, T]
-    int B, T, M, s;
-};
-
-hipError_t launch_rope_heads(const RopeParams& p, bool bf16_storage, hipStream_t st);
+hipError_t launch_proj(const ProjParams& p, bool bf16_storage, hipStream_t st);  // U, Vt, Z heads (+ RoPE)
 
 // One incremental decoding step (causal): token t, chunk slot j = t mod C.
 struct DecodeParams {

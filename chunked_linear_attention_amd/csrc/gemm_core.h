@@ -479,14 +479,16 @@ struct GemmCore {
                  rows_b, lds);
     }
 
-    // As run(), plus (when `on`, block-uniform) the side product of the ZR rows
-    // at z (K-major, rows z_pitch bytes apart, all present) with the B tile:
+    // As run(), plus (when `on`, block-uniform) the side product of ZR rows
+    // (K-major, rows z_pitch bytes apart, all present) with the B tile: side
+    // row r < zsplit is row r at z, side row r >= zsplit is row r - zsplit at
+    // z2 (zsplit a multiple of 8, so each 8-row copy piece lies in one part).
     // sd.acc[i] (16 floats per lane) holds side rows i*32 + 8*(r/4) + 4*(l/32)
     // + r%4 (lane l, register r) times B-tile column wn*64 + wm*32 + l%32.
     __device__ static __forceinline__ void run_with_side(f32x16_t (&acc)[MB][NB], Side& sd, const char* a,
                                                          size_t pitch_a, int rows_a, const char* b, size_t pitch_b,
-                                                         int rows_b, int K, const char* z, size_t z_pitch, bool on,
-                                                         char* lds) {
+                                                         int rows_b, int K, const char* z, const char* z2,
+                                                         int zsplit, size_t z_pitch, bool on, char* lds) {
         static_assert(ZR > 0, "core without side rows");
         const int nk = K / KELEMS;
         const int wave = threadIdx.x / kWave;
@@ -500,7 +502,8 @@ struct GemmCore {
         // lane's 16-byte piece: row 8*wave + lane/8 (waves below ZPIECES),
         // physical piece lane % 8, logical piece (lane % 8) ^ perm(row)
         const int row = (wave < ZPIECES ? wave : 0) * 8 + (lane >> 3);
-        sd.src = z + (size_t)row * z_pitch + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
+        const char* zrow = row < zsplit ? z + (size_t)row * z_pitch : z2 + (size_t)(row - zsplit) * z_pitch;
+        sd.src = zrow + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
         run_impl<true>(acc, KSeg{a, pitch_a, nk}, KSeg{a, pitch_a, 0}, rows_a, KSeg{b, pitch_b, nk},
                        KSeg{b, pitch_b, 0}, rows_b, lds, sd);
     }

@@ -70,10 +70,11 @@ static void run(const Cfg& c, const std::string& only) {
         fn();
         fprintf(stderr, "  %-12s ok (%.1f s)\n", name, now() - t0);
     };
-    ProjParams pp{X, Wu, Wv, Wz, sc, of, U, Vt, Qq, Kq, Ql, Klt, (int)M, c.T, c.d, c.e, c.s};
+    ProjParams pp{X, Wu, Wv, Wz, sc, of, U, Vt, Qq, Kq, Ql, Klt, (int)M, c.T, c.d, c.e, c.s, 0};
     t("proj", [&] { CHECK(launch_proj(pp, c.bf, nullptr)); });
-    RopeParams rop{Qq, Kq, Ql, Klt, c.B, c.T, (int)M, c.s};
-    t("rope_heads", [&] { CHECK(launch_rope_heads(rop, c.bf, nullptr)); });
+    ProjParams ppr = pp;
+    ppr.rope = 1;  // the heads rotated in the epilogue
+    t("proj_rope", [&] { CHECK(launch_proj(ppr, c.bf, nullptr)); });
     float* ra = (float*)buf(128 * 4);
     float* rb = (float*)buf(128 * 4);
     float* rw = (float*)buf((2 * c.C - 1) * 4);

@@ -82,6 +82,7 @@ CASES = [
     (1, 256, 128, 256, 256, 128, "bf16", False, False, "both", "wide"),
     (1, 256, 128, 1024, 128, 64, "bf16", True, False, "both", "wide"),
     (1, 256, 128, 1024, 256, 128, "f32", False, True, "both", "wide"),
+    (1, 320, 128, 256, 256, 64, "bf16", True, True, "both", "wide"),   # Z tile with s = 256, rotated, ragged
 ]
 
 

@@ -120,6 +120,8 @@ ROPE = [
     (2, 256, 128, 1024, 128, 64, "bf16", True),
     (1, 320, 256, 1024, 256, 64, "bf16", False),
     (1, 1024, 256, 512, 128, 512, "bf16", True),
+    (1, 512, 256, 512, 256, 128, "f32", True),     # Z tile with s = 256
+    (1, 960, 128, 1536, 128, 64, "bf16", False),   # e = 1536 mapping, ragged last token tile
 ]
 
 
