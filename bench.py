@@ -13,10 +13,11 @@ chunk C=256, bf16 storage with fp32 accumulation, causal.  Inputs are resident
 in HBM before the timed region starts.  Prints one JSON line.
 
 The timed region is K plain gau_forward calls between two synchronisations.
-Just before it, a pass of whole forwards brackets the dominant kernel (the
-projection GEMM) with HIP events on the stream the kernels run on; the
-roofline object is its algorithmic FLOPs per launch divided by that average
-duration, against the dense bf16 MFMA peak.  Per-stage times (kernels_us)
+Just before it, loops of whole forwards and of forwards without the dominant
+kernel (the projection GEMM), each loop between two HIP events on the stream
+the kernels run on, give that kernel's average duration inside a forward; the
+roofline object is its algorithmic FLOPs per launch divided by that duration,
+against the dense bf16 MFMA peak.  Per-stage times (kernels_us)
 come from another pass with events around every stage.
 """
 
@@ -38,7 +39,8 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "GAU/FLASH layer fwd tokens/sec at d=768 T=8192 C=256; % bf16 MFMA peak"
 STAGES = ["proj", "chunk_scores", "chunk_state", "chunk_scan", "chunk_attn", "out_gemm"]
 DOMINANT = "proj"
-DOM_MIN_SAMPLES = 50  # event-bracketed launches of the dominant kernel, at least
+DOM_BATCH = 20  # back-to-back launches of the dominant kernel between two events
+DOM_REPS = 5    # loops per measurement of the dominant kernel (median)
 
 
 def algorithmic_flops(B, T, d, e, s, C, causal=True):
@@ -234,6 +236,41 @@ def summarize_stats(csv_path, command, out, title=None):
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+FORWARD_KERNELS = ["proj_kernel", "chunk_scores_state_kernel", "chunk_scan_kernel", "chunk_attn_kernel",
+                   "out_gemm_kernel"]
+
+
+def summarize_forward_trace(trace_csv, command, out, title=None):
+    """Markdown summary of the plain forwards in a rocprofv3 kernel trace: the
+    runs of the forward's five launches in order, per-kernel duration
+    statistics over them and the forward's span (first start to last end)."""
+    import csv
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+
+    def kind(name):
+        for k in FORWARD_KERNELS:
+            if k in name:
+                return k
+        return None
+
+    kinds = [kind(r["Kernel_Name"]) for r in rows]
+    fwd = [rows[i:i + 5] for i in range(len(rows) - 4) if kinds[i:i + 5] == FORWARD_KERNELS]
+    title = title or "FLASH layer forward, B=2 T=8192 d=768 e=1536 s=128 C=256, bf16, causal"
+    span = [(int(f[-1]["End_Timestamp"]) - int(f[0]["Start_Timestamp"])) / 1e3 for f in fwd]
+    lines = [f"# rocprofv3 kernel trace, whole forwards: {title}", "", "Command (from the repository root, one MI355X):",
+             "", "```", command, "```", "",
+             f"{len(fwd)} forwards found (five launches in order); durations from each launch's start to its end.",
+             f"Forward span, first start to last end: median {np.median(span):.1f} us, mean {np.mean(span):.1f} us.",
+             "", "| kernel | launches | median (us) | mean (us) | min (us) | max (us) | share of span |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for k, name in enumerate(FORWARD_KERNELS):
+        d = np.array([(int(f[k]["End_Timestamp"]) - int(f[k]["Start_Timestamp"])) / 1e3 for f in fwd])
+        lines.append(f"| `{name}` | {len(d)} | {np.median(d):.1f} | {d.mean():.1f} | {d.min():.1f} | {d.max():.1f} | "
+                     f"{100 * np.median(d) / np.median(span):.1f}% |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -578,6 +615,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, run the copy that calibrates the HBM counters")
     ap.add_argument("--summarize-stats", metavar="STATS_CSV")
+    ap.add_argument("--summarize-forward-trace", metavar="TRACE_CSV",
+                    help="per-kernel durations over the plain forwards of a rocprofv3 kernel trace")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_CSV",
                     help="per-kernel MFMA utilisation and HBM traffic from rocprofv3 --pmc csv files (needs --stats)")
@@ -598,6 +637,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.command, args.out, args.title)
+        return
+    if args.summarize_forward_trace:
+        summarize_forward_trace(args.summarize_forward_trace, args.command, args.out, args.title)
         return
     if args.summarize_decode_trace:
         summarize_decode_trace(args.summarize_decode_trace, args.command, args.out)
@@ -669,19 +711,39 @@ def main():
     torch.cuda.synchronize()
 
     # Diagnostics before the timed region (they also settle the clocks):
-    # (1) the dominant kernel's launches bracketed by HIP events on the
-    # stream the kernels run on, inside whole forwards (its neighbours run as
-    # they do in a forward), K of them; the roofline's `achieved` uses their
-    # average.  (2) every stage alone between events, and scores + states as
-    # the forward runs them (one launch).
-    dom_n = max(K, DOM_MIN_SAMPLES)
-    dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(dom_n)]
+    # (1) the dominant kernel's duration inside forwards, from HIP events on
+    # the stream the kernels run on, one pair around each loop: K whole
+    # forwards, then K forwards without the dominant stage (the later stages
+    # read the workspace it left), DOM_REPS times each, interleaved; the
+    # difference of the medians per forward is that stage's cost in a forward
+    # (no event sits between its launch and its neighbours').  (2) the same
+    # kernel in batches of DOM_BATCH back-to-back launches between two events
+    # (median of DOM_REPS).  (3) the forward split into three calls with
+    # events around the dominant kernel, K of them.  (4) every stage alone
+    # between events, and scores + states as the forward runs them.
+    def loop_ms(first, last, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            g.forward_stages(gc, first, last, *args_l, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    full_ms, rest_ms = [], []
+    for _ in range(DOM_REPS):
+        full_ms.append(loop_ms(0, len(STAGES) - 1, K))
+        rest_ms.append(loop_ms(dom + 1, len(STAGES) - 1, K) if dom == 0 else loop_ms(0, len(STAGES) - 1, K))
+    dom_ms = float(np.median(full_ms) - np.median(rest_ms))
+    batch_ms = [loop_ms(dom, dom, DOM_BATCH) for _ in range(DOM_REPS)]
+    dom_batch_ms = float(np.median(batch_ms))
+    dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     t_split = time.perf_counter()
     for ev in dom_ev:
         step_bracketed(ev)
     torch.cuda.synchronize()
-    split_ms_per_step = (time.perf_counter() - t_split) * 1e3 / dom_n
-    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dom_ev]))
+    split_ms_per_step = (time.perf_counter() - t_split) * 1e3 / K
+    dom_in_forward_ms = float(np.mean([a.elapsed_time(b) for a, b in dom_ev]))
 
     stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(K)]
     for k in range(K):
@@ -747,9 +809,13 @@ def main():
         "roofline": {"bound": "mfma", "kernel": DOMINANT, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "algorithmic_flops_per_launch": flops[DOMINANT], "avg_launch_us": dom_ms * 1e3,
-                     "event_samples": dom_n,
-                     "event_note": "the kernel's launches inside whole forwards, each between two HIP events "
-                                   "on the launch stream, in a pass of their own just before the timed region"},
+                     "event_samples": 2 * DOM_REPS * K,
+                     "event_note": f"the kernel's cost inside forwards: median per-forward time of {K} whole "
+                                   f"forwards minus that of {K} forwards without its stage, {DOM_REPS} loops each, "
+                                   "one pair of HIP events on the launch stream around each loop, just before "
+                                   "the timed region",
+                     "avg_launch_us_back_to_back": dom_batch_ms * 1e3,
+                     "avg_launch_us_in_forward_with_events": dom_in_forward_ms * 1e3},
         "kernels_us": {n: per_stage[n] * 1e3 for n in STAGES},
         "kernels_gbs": {n: bytes_[n] / (per_stage[n] * 1e-3) / 1e9 for n in STAGES},
         "kernels_tflops": {n: flops[n] / (per_stage[n] * 1e-3) / 1e12 for n in STAGES},
