@@ -134,7 +134,8 @@ gau::StateParams state_params(const gau_config* c, const gau_ws_layout& L, char*
 // segment ids): the scan forms one averaged state per chunk, in place over S
 // (also when non-causal), and the attention stage reads it per chunk.
 gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs& a, void* O, const float* residual,
-                      char* ws, hipStream_t st, bool shared = true, const int32_t* seg = nullptr) {
+                      char* ws, hipStream_t st, bool shared = true, const int32_t* seg = nullptr,
+                      void* preact = nullptr) {
     gau_ws_layout L;
     layout(c, &L, shared);
     if (seg) L.P = L.S;
@@ -148,7 +149,7 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
             case GAU_STAGE_PROJ: {
                 gau::ProjParams p{a.X, a.W_u, a.W_v, a.W_z, a.scale, a.offset, ws + L.U, ws + L.Vt,
                                   ws + L.Q_quad, ws + L.K_quad, ws + L.Q_lin, ws + L.K_lin_t,
-                                  M, (int)c->T, (int)c->d, (int)c->e, (int)c->s, c->rope};
+                                  M, (int)c->T, (int)c->d, (int)c->e, (int)c->s, c->rope, preact};
                 e = gau::launch_proj(p, bf, st);
                 break;
             }
@@ -316,7 +317,10 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     // causal diagonal, which the forward leaves unwritten, cleared first)
     if (c->causal && gau::launch_fill_zero((float*)W(F.A), (size_t)Z * CC * eb / 4, st) != hipSuccess)
         return GAU_ERR_HIP;
-    gau_status sres = run_stages(c, GAU_STAGE_PROJ, GAU_STAGE_SCAN, a, nullptr, nullptr, ws, st, false);
+    // (the projection also stores the pre-activations H = X [W_u | W_v | W_z],
+    // which the SiLU derivatives below read)
+    gau_status sres = run_stages(c, GAU_STAGE_PROJ, GAU_STAGE_SCAN, a, nullptr, nullptr, ws, st, false, nullptr,
+                                 W(L.H));
     if (sres != GAU_OK) return sres;
     // Wq = A V + Q_lin P (into the forward's Y region): the attention stage
     // without the gate
@@ -325,16 +329,6 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
                           c->causal ? 1 : 0, 1, 1};
         ok(gau::launch_chunk_attn(p, bf, st));
     }
-    // pre-activations H = X [W_u | W_v | W_z]
-    // (U and V on the output GEMM's tiles: rows of X times rows of W_u, W_v, K = d)
-    ok(gau::launch_out_gemm(
-        gau::OutParams{a.X, a.W_u, W(L.H), nullptr, M, e, d, 0, W3, nullptr, nullptr, nullptr, nullptr, nullptr, 0}, bf,
-        st));
-    ok(gau::launch_out_gemm(
-        gau::OutParams{a.X, a.W_v, Wc(L.H, e), nullptr, M, e, d, 0, W3, nullptr, nullptr, nullptr, nullptr, nullptr, 0},
-        bf, st));
-    gemm(nt(a.X, 0, d, a.W_z, 0, d, Wc(L.H, 2 * e), 0, W3, d, false), M, s, 1);
-
     // O = Y W_o and the gate Y = U * Wq: dY = dO W_o^T, fused with
     // dWq = dY * U, Y, and dH_u = dY * Wq * SiLU'(H_u)
     trans(tp(a.W_o, 0, e, W(L.WoT), 0, d), d, e, 1);

@@ -23,6 +23,8 @@ struct ProjParams {
     void* Klt;  // [B, s, T]
     int M, T, d, e, s;
     int rope;   // 1: the four heads rotated by position t = m mod T (in the epilogue)
+    void* H;    // [M, 2e+s] token-major pre-activations X [W_u | W_v | W_z] (row pitch 2e+s),
+                // written besides the activated outputs when non-null (the backward's recompute)
 };
 
 // Per-chunk state S_g^T = lin_scale * V_g^T K_lin_g, [B, G, e, s] in the

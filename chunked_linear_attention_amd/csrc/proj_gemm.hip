@@ -9,6 +9,10 @@
 // four heads, quadratic and linear Q/K (wikillm "Method", mixed chunk
 // attention; papercache 3.2 "Preparation").
 //
+// With H non-null (the backward's recompute) the pre-activations X W_u,
+// X W_v, X W_z are also stored, token-major with row pitch 2e + s, before
+// the epilogue applies SiLU.
+//
 // Layout written (see the workspace layout in gau.h):
 //   U [M, e] row-major; Vt [B, e, T] (V transposed per sequence, so the chunk
 //   kernels read tokens contiguously); Q_quad, K_quad, Q_lin [M, s] row-major;
@@ -101,6 +105,32 @@ __device__ __forceinline__ void z_side_epilogue(const ProjParams& p, Side& sd, i
     const int M = p.M, T_ = p.T, s = p.s, half = p.s / 2;
     const bool one_pass = 3 * HEAD_T + ZR * FP <= lds_bytes;
     auto feat = [&](int zr) { return zr < ZH ? hb + zr : half + hb + (zr - ZH); };
+    if (p.H) {  // the slice's pre-activations, token-major at column 2e + feature
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < ZMB; ++i)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                char* q = lds + tok * TP + (i * 32 + 8 * g4 + 4 * h) * EB;
+                const float x[4] = {sd.acc[i][4 * g4], sd.acc[i][4 * g4 + 1], sd.acc[i][4 * g4 + 2],
+                                    sd.acc[i][4 * g4 + 3]};
+                if constexpr (EB == 2) {
+                    *(u32x2_t*)q = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+                } else {
+                    *(f32x4_t*)q = f32x4_t{x[0], x[1], x[2], x[3]};
+                }
+            }
+        __syncthreads();
+        constexpr int VPR = ZR * EB / 16;
+        const size_t hrp = (size_t)(2 * p.e + s);
+        for (int idx = threadIdx.x; idx < BN * VPR; idx += NT) {
+            const int t = idx / VPR, v = idx - t * VPR;
+            const int m = m0 + t;
+            if (m < M)
+                *(u32x4_t*)((char*)p.H + ((size_t)m * hrp + 2 * p.e + feat(v * (16 / EB))) * EB) =
+                    *(const u32x4_t*)(lds + t * TP + v * 16);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < ZMB; ++i)
 #pragma unroll
@@ -251,11 +281,25 @@ __device__ __forceinline__ void uv_tile(const ProjParams& p, int bid, char* lds,
     }
     if (!ran)
         G::run(acc, is_v ? xt : wt, pitch, is_v ? rows_x : BN, is_v ? wt : xt, pitch, is_v ? BN : rows_x, p.d, lds);
-    G::transform(acc, [](int, int, float v) { return silu(v); });
 
     constexpr int LDS = ProjTile<T, ZR>::LDS;
     const int M = p.M, T_ = p.T;
     auto ident = [](int, int, float v) { return v; };
+    if (p.H) {  // pre-activations, token-major, columns c0.. of the U or V section
+        char* Hb = (char*)p.H + (size_t)((is_v ? p.e : 0) + c0) * EB;
+        const size_t hrp = (size_t)(2 * p.e + p.s);
+        if (!is_v)  // acc rows = features, columns = tokens
+            G::template store_packed<T>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
+                const int m = m0 + tok;
+                return m < M ? Hb + ((size_t)m * hrp + feat) * EB : nullptr;
+            });
+        else  // acc rows = tokens, columns = features
+            G::template store<T, false>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
+                const int m = m0 + tok;
+                return m < M ? Hb + ((size_t)m * hrp + feat) * EB : nullptr;
+            });
+    }
+    G::transform(acc, [](int, int, float v) { return silu(v); });
     if (!is_v) {
         // acc rows = features, columns = tokens
         char* U = (char*)p.U;
@@ -300,12 +344,30 @@ __device__ __forceinline__ void z_tile(const ProjParams& p, int zb, char* lds, c
     f32x16_t acc[MB][1];
     G::zero(acc);
     G::run(acc, (const char*)p.W_z, pitch, ZF, (const char*)p.X + (size_t)m0 * pitch, pitch, rows_x, p.d, lds);
-    G::transform(acc, [](int, int, float v) { return silu(v); });
-
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int c = lane & 31, h = lane >> 5;
     const int m = m0 + wave * 32 + c;  // this lane's token
     if (m >= p.M) return;              // (no barrier follows)
+    if (p.H) {  // pre-activations X W_z, token-major at column 2e
+        char* row = (char*)p.H + ((size_t)m * (2 * p.e + p.s) + 2 * p.e) * EB;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                char* q = row + (size_t)(i * 32 + 8 * g4 + 4 * h) * EB;
+                const float x[4] = {acc[i][0][4 * g4], acc[i][0][4 * g4 + 1], acc[i][0][4 * g4 + 2],
+                                    acc[i][0][4 * g4 + 3]};
+                if constexpr (EB == 2) {
+                    *(u32x2_t*)q = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+                } else {
+                    *(f32x4_t*)q = f32x4_t{x[0], x[1], x[2], x[3]};
+                }
+            }
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][0][r] = silu(acc[i][0][r]);
     const int T_ = p.T, s = p.s, half = p.s / 2;
     const int b = m / T_, t = m - b * T_;
     char* Klt = (char*)p.Klt + ((size_t)b * s * T_ + t) * EB;

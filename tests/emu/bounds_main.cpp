@@ -70,11 +70,16 @@ static void run(const Cfg& c, const std::string& only) {
         fn();
         fprintf(stderr, "  %-12s ok (%.1f s)\n", name, now() - t0);
     };
-    ProjParams pp{X, Wu, Wv, Wz, sc, of, U, Vt, Qq, Kq, Ql, Klt, (int)M, c.T, c.d, c.e, c.s, 0};
+    ProjParams pp{X, Wu, Wv, Wz, sc, of, U, Vt, Qq, Kq, Ql, Klt, (int)M, c.T, c.d, c.e, c.s, 0, nullptr};
     t("proj", [&] { CHECK(launch_proj(pp, c.bf, nullptr)); });
     ProjParams ppr = pp;
     ppr.rope = 1;  // the heads rotated in the epilogue
     t("proj_rope", [&] { CHECK(launch_proj(ppr, c.bf, nullptr)); });
+    void* Hpre = buf(M * (2 * c.e + c.s) * eb);
+    ProjParams pph = pp;
+    pph.H = Hpre;  // the pre-activations stored too (the backward's recompute)
+    t("proj_preact", [&] { CHECK(launch_proj(pph, c.bf, nullptr)); });
+    free(Hpre);
     float* ra = (float*)buf(128 * 4);
     float* rb = (float*)buf(128 * 4);
     float* rw = (float*)buf((2 * c.C - 1) * 4);
