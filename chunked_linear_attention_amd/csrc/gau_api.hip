@@ -203,12 +203,13 @@ struct BwdLayout {
     int split_o, split_w;  // K splits of the weight-gradient products
 };
 
-// Splits of a weight-gradient product (K = M tokens) with `tiles` 128 x 128
-// output tiles: doubled while the grid is small and K / splits stays a
-// multiple of 64.
-int weight_splits(int64_t M, int64_t tiles) {
-    int S = 1;
-    while (S < 8 && tiles * S < 2048 && M % (128 * S) == 0) S *= 2;
+// K splits of a weight-gradient product (K = M tokens, 64 per chunk) on the
+// output GEMM's 256 x 256 tiles: as many as fill one round of the 256 CUs,
+// at most one per chunk.
+int weight_splits(int64_t M, int tiles) {
+    int S = tiles >= 256 ? 1 : 256 / tiles;
+    const int64_t chunks = M / 64;
+    if (S > chunks) S = (int)(chunks > 0 ? chunks : 1);
     return S;
 }
 
@@ -219,8 +220,9 @@ void bwd_layout(const gau_config* c, BwdLayout* L) {
     const size_t M = (size_t)(c->B * c->T), d = c->d, e = c->e, s = c->s, C = c->C;
     const size_t G = c->T / c->C, Z = (size_t)c->B * G, Gp = c->causal ? G : 1;
     const size_t W3 = 2 * e + s;
-    L->split_o = weight_splits((int64_t)M, (int64_t)(d / 128) * (e / 128));
-    L->split_w = weight_splits((int64_t)M, (int64_t)((W3 + 127) / 128) * (d / 128));
+    // dW_o: feature tiles over e, token tiles over d; [dW_u|dW_v|dW_z]: over d and 2e + s
+    L->split_o = weight_splits((int64_t)M, gau::out_gemm_tiles((int)e, (int)d, 256));
+    L->split_w = weight_splits((int64_t)M, gau::out_gemm_tiles((int)d, (int)W3, 256));
     size_t off = F.total;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -412,17 +414,25 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     float* wp = (float*)W(L.wpart);
     trans(tp(dO, 0, d, W(L.dOt), 0, M), M, d, 1);
     trans(tp(W(L.Yb), 0, e, W(L.Yt), 0, M), M, e, 1);
+    // (the output GEMM's tiles, split over K: rows of Yt (e) as the feature
+    // side and rows of dOt (d) as the token side, so the product is [d, e])
     {
-        const int S = L.split_o, Ks = M / S;
-        gemm(nt(W(L.dOt), Ks, M, W(L.Yt), Ks, M, wp, (int64_t)d * e, e, Ks, true), d, e, S);
+        const int S = L.split_o;
+        gau::OutParams q{W(L.dOt), W(L.Yt), wp, nullptr, d, e, M, 1, e, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         0, S, (int64_t)d * e, M, 256};
+        ok(gau::launch_out_gemm(q, bf, st));
         ok(gau::launch_split_reduce(wp, (int64_t)d * e, dW_o, (int64_t)d * e, S, st));
     }
     trans(tp(W(L.dH), 0, W3, W(L.dHt), 0, M), M, W3, 1);
     trans(tp(a.X, 0, d, W(L.Xt), 0, M), M, d, 1);
+    // (rows of Xt (d) as the feature side, rows of dHt (2e + s) as the token
+    // side: the product is [2e + s, d])
     {
-        const int S = L.split_w, Ks = M / S;
+        const int S = L.split_w;
         const int64_t stride = (int64_t)W3 * d;
-        gemm(nt(W(L.dHt), Ks, M, W(L.Xt), Ks, M, wp, stride, d, Ks, true), W3, d, S);
+        gau::OutParams q{W(L.dHt), W(L.Xt), wp, nullptr, W3, d, M, 1, d, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         0, S, stride, M, 256};
+        ok(gau::launch_out_gemm(q, bf, st));
         ok(gau::launch_split_reduce(wp, stride, dW_u, (int64_t)e * d, S, st));
         ok(gau::launch_split_reduce(wp + (size_t)e * d, stride, dW_v, (int64_t)e * d, S, st));
         ok(gau::launch_split_reduce(wp + (size_t)2 * e * d, stride, dW_z, (int64_t)s * d, S, st));

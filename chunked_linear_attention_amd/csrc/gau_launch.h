@@ -92,7 +92,17 @@ struct OutParams {
     void* gDWq;
     void* gY;
     int g_rp;
+    // split-K (fp32 output without residual or gate only): block z of ksplit
+    // takes K chunks [z*(nk/ksplit) + min(z, nk%ksplit), ...) of the nk = e/64
+    // (bf16) and writes its partial product at O + z * o_bs elements
+    int ksplit;        // 0 or 1: one K range
+    int64_t o_bs;
+    int k_rp;          // elements between rows of W_o and Y (their K pitch); 0: e
+    int bm;            // feature-tile width (256, 192 or 128); 0: chosen from d and M
 };
+
+// Blocks of a split-K output GEMM of d x M outputs with feature tiles of bm.
+int out_gemm_tiles(int d, int M, int bm);
 
 // Row RMS normalisation for the layer stack: Xn = bf16(x / sqrt(mean(x^2) + eps)).
 struct NormParams {

@@ -58,20 +58,26 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     using G = typename OutTile<T, BM>::G;
     constexpr int EB = Elem<T>::kBytes;
     const int ntiles = (p.d + BM - 1) / BM;  // feature tiles (acc rows)
+    const int tiles = ntiles * ((p.M + BN - 1) / BN);
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int nt = bid % ntiles;
-    const int mt = bid / ntiles;
+    const int z = bid / tiles, tt = bid - z * tiles;  // K split, tile
+    const int nt = tt % ntiles;
+    const int mt = tt / ntiles;
     const int m0 = mt * BN, n0 = nt * BM;  // token offset, feature offset
-    const size_t pitch = (size_t)p.e * EB;
+    const size_t pitch = (size_t)(p.k_rp > 0 ? p.k_rp : p.e) * EB;
     const int rows_y = min(BN, p.M - m0);
     const int rows_w = min(BM, p.d - n0);
+    // this block's K chunks (one range unless split)
+    const int S = p.ksplit > 1 ? p.ksplit : 1;
+    const int nk = p.e / G::KELEMS, kbase = nk / S, krem = nk % S;
+    const int kc0 = z * kbase + min(z, krem), nkz = kbase + (z < krem ? 1 : 0);
 
     // acc = tile^T: rows = output features (W_o^T rows), columns = tokens, so
     // the packed epilogue writes run along the token-major rows of O.
     f32x16_t acc[G::MB][G::NB];
     G::zero(acc);
-    G::run(acc, (const char*)p.W_o + (size_t)n0 * pitch, pitch, rows_w, (const char*)p.Y + (size_t)m0 * pitch, pitch,
-           rows_y, p.e, lds);
+    G::run(acc, (const char*)p.W_o + (size_t)n0 * pitch + (size_t)kc0 * 128, pitch, rows_w,
+           (const char*)p.Y + (size_t)m0 * pitch + (size_t)kc0 * 128, pitch, rows_y, nkz * G::KELEMS, lds);
 
     constexpr int LDS = OutTile<T, BM>::LDS;
     const int M = p.M, d = p.d;
@@ -115,8 +121,8 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
             return (m < M && n < d) ? O + ((size_t)m * orp + n) * EB : nullptr;
         });
     } else if (p.residual == nullptr) {
-        // fp32 O = Y W_o
-        float* O = (float*)p.O;
+        // fp32 O = Y W_o (split z: its partial product at O + z * o_bs)
+        float* O = (float*)p.O + (size_t)z * p.o_bs;
         G::template store_packed<float>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
             const int m = m0 + tok, n = n0 + feat;
             return (m < M && n < d) ? (char*)(O + (size_t)m * orp + n) : nullptr;
@@ -145,7 +151,10 @@ template <typename T, int BM>
 hipError_t launch(const OutParams& p, hipStream_t st) {
     constexpr int LDS = OutTile<T, BM>::LDS;
     static_assert(LDS <= 160 * 1024, "output GEMM LDS over budget");
-    const int blocks = ((p.d + BM - 1) / BM) * ((p.M + BN - 1) / BN);
+    const int S = p.ksplit > 1 ? p.ksplit : 1;
+    if (S > 1 && (p.residual != nullptr || p.gU != nullptr || !p.f32_out)) return hipErrorInvalidValue;
+    if (S > p.e / OutTile<T, BM>::G::KELEMS) return hipErrorInvalidValue;
+    const int blocks = ((p.d + BM - 1) / BM) * ((p.M + BN - 1) / BN) * S;
     hipError_t e = allow_lds<out_gemm_kernel<T, BM>>(LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((out_gemm_kernel<T, BM>), dim3(blocks), dim3(512), LDS, st, p);
@@ -173,7 +182,7 @@ int feature_tile(int d, int M) {
 
 template <typename T>
 hipError_t dispatch(const OutParams& p, hipStream_t st) {
-    switch (feature_tile(p.d, p.M)) {
+    switch (p.bm > 0 ? p.bm : feature_tile(p.d, p.M)) {
         case 256: return launch<T, 256>(p, st);
         case 192: return launch<T, 192>(p, st);
         default: return launch<T, 128>(p, st);
@@ -181,6 +190,11 @@ hipError_t dispatch(const OutParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+int out_gemm_tiles(int d, int M, int bm) {
+    const int b = bm > 0 ? bm : feature_tile(d, M);
+    return ((d + b - 1) / b) * ((M + BN - 1) / BN);
+}
 
 hipError_t launch_out_gemm(const OutParams& p, bool bf16_storage, hipStream_t st) {
     return bf16_storage ? dispatch<bf16>(p, st) : dispatch<float>(p, st);
