@@ -138,9 +138,9 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmNTParams q) {
 // row) pairs as 32-bit words to LDS, column-major, so that an output vector
 // (8 rows of one column) is one 16-byte LDS read.
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(TransposeParams q) {
+__device__ __forceinline__ void transpose_block(const TransposeParams& q, int bid) {
     const int tiles = q.tr * q.tc;
-    const int z = blockIdx.x / tiles, t = blockIdx.x - z * tiles;
+    const int z = bid / tiles, t = bid - z * tiles;
     const int r0 = (t / q.tc) * 64, c0 = (t % q.tc) * 64;
     if constexpr (Elem<T>::kBytes == 2) {
         constexpr int WP = 36;          // LDS words per column (32 row pairs + pad)
@@ -184,6 +184,21 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeParams q) {
             *(f32x4_t*)(out + (size_t)(c0 + c) * q.out_rp + r0 + vc) = y;
         }
     }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeParams q) {
+    transpose_block<T>(q, blockIdx.x);
+}
+
+// Several independent transposes in one launch: block b runs job j with
+// start[j] <= b < start[j+1] (their tiles are small; apart they cost a launch
+// ramp each).
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_batch_kernel(TransposeBatch b) {
+    int j = 0;
+    while (j + 1 < b.n && (int)blockIdx.x >= b.start[j + 1]) ++j;
+    transpose_block<T>(b.job[j], (int)blockIdx.x - b.start[j]);
 }
 
 // dSc = 2 relu(Sc) dA * mask with relu(Sc) = sqrt(A) (A = relu(Sc)^2 as the
@@ -344,6 +359,29 @@ hipError_t launch_gemm_nt(const GemmNTParams& q0, int M, int N, int nb, bool bf,
     if (blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
     if (bf) return big ? gemm_go<bf16, 128>(q, (unsigned)blocks, st) : gemm_go<bf16, 64>(q, (unsigned)blocks, st);
     return big ? gemm_go<float, 128>(q, (unsigned)blocks, st) : gemm_go<float, 64>(q, (unsigned)blocks, st);
+}
+
+hipError_t launch_transpose_batch(const TransposeParams* jobs, const int* R, const int* Cc, const int* nb, int n,
+                                  bool bf, hipStream_t st) {
+    if (n < 1 || n > kTransposeBatch) return hipErrorInvalidValue;
+    TransposeBatch b{};
+    b.n = n;
+    int64_t total = 0;
+    for (int j = 0; j < n; ++j) {
+        b.job[j] = jobs[j];
+        b.job[j].tr = R[j] / 64;
+        b.job[j].tc = Cc[j] / 64;
+        b.start[j] = (int)total;
+        total += (int64_t)nb[j] * b.job[j].tr * b.job[j].tc;
+        if (total > INT32_MAX) return hipErrorInvalidValue;
+    }
+    b.start[n] = (int)total;
+    if (total <= 0) return hipErrorInvalidValue;
+    if (bf)
+        hipLaunchKernelGGL(transpose_batch_kernel<bf16>, dim3((unsigned)total), dim3(256), 0, st, b);
+    else
+        hipLaunchKernelGGL(transpose_batch_kernel<float>, dim3((unsigned)total), dim3(256), 0, st, b);
+    return hipGetLastError();
 }
 
 hipError_t launch_transpose(const TransposeParams& q0, int R, int Cc, int nb, bool bf, hipStream_t st) {

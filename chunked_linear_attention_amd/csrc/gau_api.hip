@@ -314,6 +314,23 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     auto trans = [&](const gau::TransposeParams& q, int r, int cc, int nb) {
         ok(gau::launch_transpose(q, r, cc, nb, bf, st));
     };
+    // independent transposes queued together and run as one launch
+    struct Batch {
+        gau::TransposeParams q[gau::kTransposeBatch];
+        int r[gau::kTransposeBatch], cc[gau::kTransposeBatch], nb[gau::kTransposeBatch];
+        int n = 0;
+    } batch;
+    auto add = [&](const gau::TransposeParams& q, int r, int cc, int nb) {
+        batch.q[batch.n] = q;
+        batch.r[batch.n] = r;
+        batch.cc[batch.n] = cc;
+        batch.nb[batch.n] = nb;
+        ++batch.n;
+    };
+    auto flush = [&]() {
+        if (batch.n) ok(gau::launch_transpose_batch(batch.q, batch.r, batch.cc, batch.nb, batch.n, bf, st));
+        batch.n = 0;
+    };
 
     // forward intermediates: heads, states, prefix, weights (tiles above the
     // causal diagonal, which the forward leaves unwritten, cleared first)
@@ -331,22 +348,35 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
                           c->causal ? 1 : 0, 1, 1};
         ok(gau::launch_chunk_attn(p, bf, st));
     }
+    // every transpose whose input is ready now, in one launch: W_o^T;
+    // token-major V and K_lin; chunk-transposed heads and weights; P^T per
+    // chunk; the weights for dX; dO and X for the weight gradients
+    const int Gp = c->causal ? G : 1;
+    add(tp(a.W_o, 0, e, W(L.WoT), 0, d), d, e, 1);
+    add(tp(W(F.Vt), (int64_t)e * T, T, W(L.V), (int64_t)T * e, e), e, T, Bn);
+    add(tp(W(F.K_lin_t), (int64_t)s * T, T, W(L.Kl), (int64_t)T * s, s), s, T, Bn);
+    add(tp(W(F.K_quad), Cs, s, W(L.Kqc), Cs, C), C, s, Z);
+    add(tp(W(F.Q_quad), Cs, s, W(L.Qqc), Cs, C), C, s, Z);
+    add(tp(W(F.Q_lin), Cs, s, W(L.Qlc), Cs, C), C, s, Z);
+    add(tp(W(F.A), CC, C, W(L.At), CC, C), C, C, Z);
+    add(tp(W(F.P), es, s, W(L.Pt), es, e), e, s, Bn * Gp);
+    add(tp(a.W_u, 0, d, W(L.Wt), 0, W3), e, d, 1);
+    add(tp(a.W_v, 0, d, Wc(L.Wt, e), 0, W3), e, d, 1);
+    add(tp(a.W_z, 0, d, Wc(L.Wt, 2 * e), 0, W3), s, d, 1);
+    add(tp(dO, 0, d, W(L.dOt), 0, M), M, d, 1);
+    add(tp(a.X, 0, d, W(L.Xt), 0, M), M, d, 1);
+    flush();
     // O = Y W_o and the gate Y = U * Wq: dY = dO W_o^T, fused with
     // dWq = dY * U, Y, and dH_u = dY * Wq * SiLU'(H_u)
-    trans(tp(a.W_o, 0, e, W(L.WoT), 0, d), d, e, 1);
     // (on the output GEMM's tiles: rows of dO times rows of W_o, K = d, with
     // the gate epilogue)
     ok(gau::launch_out_gemm(gau::OutParams{dO, W(L.WoT), W(L.dH), nullptr, M, e, d, 0, W3, W(L.H), W(F.Y), W(F.U),
                                            W(L.dWq), W(L.Yb), e},
                             bf, st));
-    // token-major V and K_lin; chunk-transposed heads, weights and dWq
-    trans(tp(W(F.Vt), (int64_t)e * T, T, W(L.V), (int64_t)T * e, e), e, T, Bn);
-    trans(tp(W(F.K_lin_t), (int64_t)s * T, T, W(L.Kl), (int64_t)T * s, s), s, T, Bn);
-    trans(tp(W(F.K_quad), Cs, s, W(L.Kqc), Cs, C), C, s, Z);
-    trans(tp(W(F.Q_quad), Cs, s, W(L.Qqc), Cs, C), C, s, Z);
-    trans(tp(W(F.Q_lin), Cs, s, W(L.Qlc), Cs, C), C, s, Z);
-    trans(tp(W(F.A), CC, C, W(L.At), CC, C), C, C, Z);
-    trans(tp(W(L.dWq), Ce, e, W(L.dWqc), Ce, C), C, e, Z);
+    // chunk-transposed dWq, and Y^T for dW_o
+    add(tp(W(L.dWq), Ce, e, W(L.dWqc), Ce, C), C, e, Z);
+    add(tp(W(L.Yb), 0, e, W(L.Yt), 0, M), M, e, 1);
+    flush();
 
     // local part: dA = dWq V^T, dSc = dA * 2 relu(Sc) * mask,
     // dQ_quad = qs dSc K_quad, dK_quad = qs dSc^T Q_quad, dBias
@@ -368,8 +398,6 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     // global part: dQ_lin = dWq P^T, dP = Q_lin^T dWq (per chunk, stored [e, s]),
     // dS = ls * (reverse exclusive sum of dP, or the total when non-causal),
     // dK_lin = V dS^T
-    const int Gp = c->causal ? G : 1;
-    trans(tp(W(F.P), es, s, W(L.Pt), es, e), e, s, Bn * Gp);
     gemm(nt(W(L.dWq), Ce, e, W(L.Pt), es, e, W(L.dQl), Cs, s, e, true, 1.f, 1, c->causal ? 1 : G), C, s, Z);
     gemm(nt(W(L.dWqc), Ce, C, W(L.Qlc), Cs, C, W(L.dP), es, s, C, true), e, s, Z);
     {
@@ -401,9 +429,6 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         ok(gau::launch_heads_bwd(p, dscale, doffset, bf, st));
     }
     // X W: dX = dH W^T
-    trans(tp(a.W_u, 0, d, W(L.Wt), 0, W3), e, d, 1);
-    trans(tp(a.W_v, 0, d, Wc(L.Wt, e), 0, W3), e, d, 1);
-    trans(tp(a.W_z, 0, d, Wc(L.Wt, 2 * e), 0, W3), s, d, 1);
     // (the output GEMM's form: rows of dH times rows of W^T, K = 2e + s)
     ok(gau::launch_out_gemm(gau::OutParams{W(L.dH), W(L.Wt), dX, nullptr, M, d, W3, 1, 0, nullptr, nullptr, nullptr,
                                            nullptr, nullptr, 0},
@@ -412,8 +437,6 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     // weight gradients, K = M split L.split_* ways into fp32 partials added in
     // split order: dW_o (stored [d, e]) = dO^T Y, [dW_u | dW_v | dW_z] = dH^T X
     float* wp = (float*)W(L.wpart);
-    trans(tp(dO, 0, d, W(L.dOt), 0, M), M, d, 1);
-    trans(tp(W(L.Yb), 0, e, W(L.Yt), 0, M), M, e, 1);
     // (the output GEMM's tiles, split over K: rows of Yt (e) as the feature
     // side and rows of dOt (d) as the token side, so the product is [d, e])
     {
@@ -424,7 +447,6 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         ok(gau::launch_split_reduce(wp, (int64_t)d * e, dW_o, (int64_t)d * e, S, st));
     }
     trans(tp(W(L.dH), 0, W3, W(L.dHt), 0, M), M, W3, 1);
-    trans(tp(a.X, 0, d, W(L.Xt), 0, M), M, d, 1);
     // (rows of Xt (d) as the feature side, rows of dHt (2e + s) as the token
     // side: the product is [2e + s, d])
     {

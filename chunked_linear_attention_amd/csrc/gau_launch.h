@@ -228,6 +228,17 @@ struct BwdHeadsParams {
 
 hipError_t launch_gemm_nt(const GemmNTParams& q, int M, int N, int nb, bool bf16_storage, hipStream_t st);
 hipError_t launch_transpose(const TransposeParams& q, int R, int Cc, int nb, bool bf16_storage, hipStream_t st);
+
+// Up to kTransposeBatch independent transposes (job j: R[j] x Cc[j], nb[j]
+// batch entries) in one launch.
+constexpr int kTransposeBatch = 16;
+struct TransposeBatch {
+    TransposeParams job[kTransposeBatch];
+    int start[kTransposeBatch + 1];
+    int n;
+};
+hipError_t launch_transpose_batch(const TransposeParams* jobs, const int* R, const int* Cc, const int* nb, int n,
+                                  bool bf16_storage, hipStream_t st);
 hipError_t launch_scores_bwd(const BwdElemParams& q, bool bf16_storage, hipStream_t st);
 // drelpos[k] = sum over chunks and over entries on diagonal k - (C-1) of dsc
 hipError_t launch_relpos_bwd(const float* dsc, float* part, float* drelpos, int nchunks, int C, hipStream_t st);
