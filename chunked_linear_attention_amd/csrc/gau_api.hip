@@ -184,7 +184,7 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
             }
             case GAU_STAGE_OUT: {
                 gau::OutParams p{ws + L.Y, a.W_o, O, residual, M, (int)c->d, (int)c->e, 0, 0,
-                                 nullptr, nullptr, nullptr, nullptr, nullptr, 0};
+                                 nullptr, nullptr, nullptr, nullptr, 0};
                 e = gau::launch_out_gemm(p, bf, st);
                 break;
             }
@@ -370,7 +370,7 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     // dWq = dY * U, Y, and dH_u = dY * Wq * SiLU'(H_u)
     // (on the output GEMM's tiles: rows of dO times rows of W_o, K = d, with
     // the gate epilogue)
-    ok(gau::launch_out_gemm(gau::OutParams{dO, W(L.WoT), W(L.dH), nullptr, M, e, d, 0, W3, W(L.H), W(F.Y), W(F.U),
+    ok(gau::launch_out_gemm(gau::OutParams{dO, W(L.WoT), W(L.dH), nullptr, M, e, d, 0, W3, W(L.H), W(F.Y),
                                            W(L.dWq), W(L.Yb), e},
                             bf, st));
     // chunk-transposed dWq, and Y^T for dW_o
@@ -430,7 +430,7 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     }
     // X W: dX = dH W^T
     // (the output GEMM's form: rows of dH times rows of W^T, K = 2e + s)
-    ok(gau::launch_out_gemm(gau::OutParams{W(L.dH), W(L.Wt), dX, nullptr, M, d, W3, 1, 0, nullptr, nullptr, nullptr,
+    ok(gau::launch_out_gemm(gau::OutParams{W(L.dH), W(L.Wt), dX, nullptr, M, d, W3, 1, 0, nullptr, nullptr,
                                            nullptr, nullptr, 0},
                             bf, st));
 
@@ -441,7 +441,7 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     // side and rows of dOt (d) as the token side, so the product is [d, e])
     {
         const int S = L.split_o;
-        gau::OutParams q{W(L.dOt), W(L.Yt), wp, nullptr, d, e, M, 1, e, nullptr, nullptr, nullptr, nullptr, nullptr,
+        gau::OutParams q{W(L.dOt), W(L.Yt), wp, nullptr, d, e, M, 1, e, nullptr, nullptr, nullptr, nullptr,
                          0, S, (int64_t)d * e, M, 256};
         ok(gau::launch_out_gemm(q, bf, st));
         ok(gau::launch_split_reduce(wp, (int64_t)d * e, dW_o, (int64_t)d * e, S, st));
@@ -452,7 +452,7 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     {
         const int S = L.split_w;
         const int64_t stride = (int64_t)W3 * d;
-        gau::OutParams q{W(L.dHt), W(L.Xt), wp, nullptr, W3, d, M, 1, d, nullptr, nullptr, nullptr, nullptr, nullptr,
+        gau::OutParams q{W(L.dHt), W(L.Xt), wp, nullptr, W3, d, M, 1, d, nullptr, nullptr, nullptr, nullptr,
                          0, S, stride, M, 256};
         ok(gau::launch_out_gemm(q, bf, st));
         ok(gau::launch_split_reduce(wp, stride, dW_u, (int64_t)e * d, S, st));

@@ -24,7 +24,8 @@ struct ProjParams {
     int M, T, d, e, s;
     int rope;   // 1: the four heads rotated by position t = m mod T (in the epilogue)
     void* H;    // [M, 2e+s] token-major pre-activations X [W_u | W_v | W_z] (row pitch 2e+s),
-                // written besides the activated outputs when non-null (the backward's recompute)
+                // written when non-null (the backward's recompute), instead of U and besides
+                // the other activated outputs
 };
 
 // Per-chunk state S_g^T = lin_scale * V_g^T K_lin_g, [B, G, e, s] in the
@@ -83,12 +84,13 @@ struct OutParams {
     int M, d, e;
     int f32_out;       // O in fp32 without a residual (the backward's dX = dH W^T)
     int o_rp;          // elements between rows of O (and of residual); 0: d
-    // gate epilogue of the backward (when gU != nullptr), with v = the product
-    // (dY) in fp32, per element at row m, column n (gate index j = m g_rp + n):
-    //   gDWq[j] = v U, gY[j] = U Wq, O[m, n] = v Wq SiLU'(gH[m, n]), element type
-    const void* gH;    // pre-activations, pitch o_rp
+    // gate epilogue of the backward (when gH != nullptr), with v = the product
+    // (dY) in fp32, h = gH[m, n] and U = SiLU(h) (formed from h, with the
+    // sigmoid SiLU' needs), per element at row m, column n (gate index
+    // j = m g_rp + n):
+    //   gDWq[j] = v U, gY[j] = U Wq, O[m, n] = v Wq SiLU'(h), element type
+    const void* gH;    // pre-activations X W_u, pitch o_rp
     const void* gW;    // Wq (ungated attention output)
-    const void* gU;    // U
     void* gDWq;
     void* gY;
     int g_rp;

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     const int M = p.M, d = p.d;
     const size_t orp = p.o_rp > 0 ? (size_t)p.o_rp : (size_t)d;  // output row pitch
     auto ident = [](int, int, float v) { return v; };
-    if (p.gU != nullptr) {
+    if (p.gH != nullptr) {
         // gate epilogue: the product staged in fp32; each 16-byte staged vector
         // is four columns n..n+3 of row m.  The staging address handed to the
         // emitter is O + 4 (m o_rp + n) (a position code, never dereferenced
@@ -99,16 +99,18 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
             [&](char* dp, const u32x4_t& v) {
                 const size_t idx = (size_t)(dp - code0) / 4, m = idx / orp, n = idx - m * orp;
                 const size_t j = m * grp + n;
-                float h[4], w[4], u[4], a[4], y[4], o[4];
+                float h[4], w[4], a[4], y[4], o[4];
                 get4<T>((const char*)p.gH + idx * EB, h);
                 get4<T>((const char*)p.gW + j * EB, w);
-                get4<T>((const char*)p.gU + j * EB, u);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const float dy = __uint_as_float(v[k]);
-                    a[k] = dy * u[k];
-                    y[k] = u[k] * w[k];
-                    o[k] = dy * w[k] * silu_grad(h[k]);
+                    // U = h sigma(h); SiLU'(h) = sigma(h) (1 + h (1 - sigma(h)))
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h[k]));
+                    const float u = h[k] * sg;
+                    a[k] = dy * u;
+                    y[k] = u * w[k];
+                    o[k] = dy * w[k] * (sg * (1.0f + h[k] * (1.0f - sg)));
                 }
                 put4<T>((char*)p.gDWq + j * EB, a);
                 put4<T>((char*)p.gY + j * EB, y);
@@ -152,7 +154,7 @@ hipError_t launch(const OutParams& p, hipStream_t st) {
     constexpr int LDS = OutTile<T, BM>::LDS;
     static_assert(LDS <= 160 * 1024, "output GEMM LDS over budget");
     const int S = p.ksplit > 1 ? p.ksplit : 1;
-    if (S > 1 && (p.residual != nullptr || p.gU != nullptr || !p.f32_out)) return hipErrorInvalidValue;
+    if (S > 1 && (p.residual != nullptr || p.gH != nullptr || !p.f32_out)) return hipErrorInvalidValue;
     if (S > p.e / OutTile<T, BM>::G::KELEMS) return hipErrorInvalidValue;
     const int blocks = ((p.d + BM - 1) / BM) * ((p.M + BN - 1) / BN) * S;
     hipError_t e = allow_lds<out_gemm_kernel<T, BM>>(LDS);

@@ -301,12 +301,14 @@ __device__ __forceinline__ void uv_tile(const ProjParams& p, int bid, char* lds,
     }
     G::transform(acc, [](int, int, float v) { return silu(v); });
     if (!is_v) {
-        // acc rows = features, columns = tokens
+        // acc rows = features, columns = tokens (U is not stored when the
+        // pre-activations are: the backward forms U = SiLU(X W_u) from them)
         char* U = (char*)p.U;
-        G::template store_packed<T>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
-            const int m = m0 + tok;
-            return m < M ? U + ((size_t)m * p.e + c0 + feat) * EB : nullptr;
-        });
+        if (!p.H)
+            G::template store_packed<T>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
+                const int m = m0 + tok;
+                return m < M ? U + ((size_t)m * p.e + c0 + feat) * EB : nullptr;
+            });
         if constexpr (ZR > 0) {
             if (side) z_side_epilogue<T, ZR, ROPE>(p, sd, m0, nt * (ZR / 2), lds, LDS, theta);
         }

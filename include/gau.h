@@ -297,9 +297,10 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X,
  *   drelpos [2C-1].
  * workspace: at least gau_backward_workspace_bytes(cfg) bytes of device
  *   memory.  Its start holds the forward's intermediates on return, at the
- *   offsets gau_workspace_layout gives for U, Vt, the heads, S and A; Y and
- *   P are kept in regions of their own there (the backward needs U, Y, S and
- *   P at once), so they are not at the offsets gau_workspace_layout gives.
+ *   offsets gau_workspace_layout gives for Vt, the heads, S and A (U is not
+ *   stored: the backward forms SiLU(X W_u) from the pre-activations); Y and
+ *   P are kept in regions of their own there (the backward needs Y, S and P
+ *   at once), so they are not at the offsets gau_workspace_layout gives.
  * Sums over tokens run in a fixed order: the results are bitwise
  * reproducible for a given cfg and inputs.  B * T == 0: the parameter
  * gradients are set to zero (X, the weights, scale, offset, relpos, dO, dX and
