@@ -359,8 +359,13 @@ def summarize_counters(csvs, stats_csv, command, out):
              "TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP / trace duration; HBM MB = FETCH_SIZE and "
              "WRITE_SIZE per dispatch divided by each counter's reading per true byte of a 256 MiB device copy "
              + ", ".join(f"({c}: {v:.4f})" for c, v in sorted(scale.items())) + "; GB/s over the trace duration.",
-             "", "| kernel | trace avg (us) | MFMA util | MFMA TFLOP/s | HBM read MB | HBM write MB | HBM GB/s |",
-             "|---|---:|---:|---:|---:|---:|---:|"]
+             "LDS read B/clk/CU = SQ_INSTS_LDS_LOAD_BANDWIDTH x 64 B / (GRBM_GUI_ACTIVE / 8 x 256 CUs) (the "
+             "reported GRBM_GUI_ACTIVE is the sum over the 8 XCDs); bank conflict = SQ_LDS_BANK_CONFLICT / "
+             "SQ_LDS_IDX_ACTIVE (share of the LDS's busy cycles stalled by bank conflicts); LDS busy = "
+             "SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / 8 x 256 CUs).",
+             "", "| kernel | trace avg (us) | MFMA util | MFMA TFLOP/s | HBM read MB | HBM write MB | HBM GB/s | "
+             "LDS read B/clk/CU | LDS bank conflict | LDS busy |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for k in kernels:
         t = dur.get(k)
         util = mean(k, "MfmaUtil")
@@ -372,9 +377,17 @@ def summarize_counters(csvs, stats_csv, command, out):
         f = lambda x, fmt: (fmt % x) if x is not None else "-"
         tf = mops * 512 / t / 1e12 if (mops is not None and t) else None
         gbs = (rd + wr) / t / 1e9 if (rd is not None and wr is not None and t) else None
+        gui, idx = mean(k, "GRBM_GUI_ACTIVE"), mean(k, "SQ_LDS_IDX_ACTIVE")
+        ldsb, conf = mean(k, "SQ_INSTS_LDS_LOAD_BANDWIDTH"), mean(k, "SQ_LDS_BANK_CONFLICT")
+        cu_clk = gui / 8 * 256 if gui else None
+        ld_rate = ldsb * 64 / cu_clk if (ldsb is not None and cu_clk) else None
+        cshare = conf / idx if (conf is not None and idx) else None
+        busy = idx / cu_clk if (idx is not None and cu_clk) else None
         lines.append(f"| `{k}` | {f(t * 1e6 if t else None, '%.1f')} | {f(util, '%.1f%%')} | {f(tf, '%.0f')} | "
                      f"{f(rd / 1e6 if rd is not None else None, '%.1f')} | "
-                     f"{f(wr / 1e6 if wr is not None else None, '%.1f')} | {f(gbs, '%.0f')} |")
+                     f"{f(wr / 1e6 if wr is not None else None, '%.1f')} | {f(gbs, '%.0f')} | "
+                     f"{f(ld_rate, '%.1f')} | {f(100 * cshare if cshare is not None else None, '%.1f%%')} | "
+                     f"{f(100 * busy if busy is not None else None, '%.1f%%')} |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
