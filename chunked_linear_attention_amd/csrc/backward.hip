@@ -69,30 +69,32 @@ __device__ __forceinline__ void store8(void* p, int64_t i, const float (&v)[8]) 
 }
 
 // C[z] = alpha * (A[z] B[z]^T + A2[z] B2[z]^T) on BT x BT tiles, then the
-// epilogue EPI (GemmNTParams).
-template <typename T, int BT, int EPI>
+// epilogue EPI (GemmNTParams).  TA, TB: MN-major A, B in the first segment;
+// TA2, TB2 in the second (its own K loop into the same accumulators).
+template <typename T, int BT, int EPI, bool TA, bool TB, bool TA2, bool TB2>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmNTParams q) {
     extern __shared__ __align__(16) char lds[];
-    using G = GemmCore<T, BT, BT, 2, 2>;
+    using G = GemmCore<T, BT, BT, 2, 2, 2, 0, 2, TA, TB>;
+    using G2 = GemmCore<T, BT, BT, 2, 2, 2, 0, 2, TA2, TB2>;
     constexpr int EB = Elem<T>::kBytes;
     // block -> (batch, row tile, column tile), column tiles fastest
     const int tiles = q.tm * q.tn;
     const int z = blockIdx.x / tiles, t = blockIdx.x - z * tiles;
     const int m0 = (t / q.tn) * BT, n0 = (t % q.tn) * BT;
     if (q.skip_upper && n0 >= m0 + BT) return;  // wholly above the diagonal: never read
-    const char* a = (const char*)q.A + ((int64_t)(z / q.a_div) * q.a_bs + (int64_t)m0 * q.a_rp) * EB;
-    const char* b = (const char*)q.B + ((int64_t)(z / q.b_div) * q.b_bs + (int64_t)n0 * q.b_rp) * EB;
+    const int64_t zs = z / q.zg, zc = z - zs * q.zg;
+    // first element of an operand's tile: row r0 of a K-major operand, column
+    // r0 of an MN-major one
+    auto tile = [&](const void* base, int64_t bsq, int64_t bs, int rp, bool mn_major, int r0) {
+        return (const char*)base + (zs * bsq + zc * bs + (mn_major ? (int64_t)r0 : (int64_t)r0 * rp)) * EB;
+    };
     f32x16_t acc[G::MB][G::NB];
     G::zero(acc);
-    if (q.K2 > 0) {
-        const char* a2 = (const char*)q.A2 + ((int64_t)(z / q.a_div) * q.a2_bs + (int64_t)m0 * q.a2_rp) * EB;
-        const char* b2 = (const char*)q.B2 + ((int64_t)(z / q.b_div) * q.b2_bs + (int64_t)n0 * q.b2_rp) * EB;
-        G::run_segs(acc, KSeg{a, (size_t)q.a_rp * EB, q.K / G::KELEMS},
-                    KSeg{a2, (size_t)q.a2_rp * EB, q.K2 / G::KELEMS}, BT, KSeg{b, (size_t)q.b_rp * EB, q.K / G::KELEMS},
-                    KSeg{b2, (size_t)q.b2_rp * EB, q.K2 / G::KELEMS}, BT, lds);
-    } else {
-        G::run(acc, a, (size_t)q.a_rp * EB, BT, b, (size_t)q.b_rp * EB, BT, q.K, lds);
-    }
+    G::run(acc, tile(q.A, q.a_bsq, q.a_bs, q.a_rp, TA, m0), (size_t)q.a_rp * EB, BT,
+           tile(q.B, q.b_bsq, q.b_bs, q.b_rp, TB, n0), (size_t)q.b_rp * EB, BT, q.K, lds);
+    if (q.K2 > 0)
+        G2::run(acc, tile(q.A2, q.a2_bsq, q.a2_bs, q.a2_rp, TA2, m0), (size_t)q.a2_rp * EB, BT,
+                tile(q.B2, q.b2_bsq, q.b2_bs, q.b2_rp, TB2, n0), (size_t)q.b2_rp * EB, BT, q.K2, lds);
     const int64_t cb = (int64_t)z * q.c_bs + (int64_t)m0 * q.c_rp + n0;
     const float alpha = q.alpha;
     if constexpr (EPI == EPI_STORE) {
@@ -328,22 +330,36 @@ hipError_t go(void (*k)(P), unsigned blocks, const P& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename T, int BT, int EPI>
+template <typename T, int BT, int EPI, bool TA, bool TB, bool TA2, bool TB2>
 hipError_t gemm_go1(const GemmNTParams& q, unsigned blocks, hipStream_t st) {
-    constexpr int LDS = GemmCore<T, BT, BT, 2, 2>::LDS_BYTES;
-    const hipError_t e = allow_lds<gemm_nt_kernel<T, BT, EPI>>(LDS);
+    constexpr int LDS = GemmCore<T, BT, BT, 2, 2>::LDS_BYTES;  // the same for every operand layout
+    const hipError_t e = allow_lds<gemm_nt_kernel<T, BT, EPI, TA, TB, TA2, TB2>>(LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_nt_kernel<T, BT, EPI>), dim3(blocks), dim3(256), LDS, st, q);
+    hipLaunchKernelGGL((gemm_nt_kernel<T, BT, EPI, TA, TB, TA2, TB2>), dim3(blocks), dim3(256), LDS, st, q);
     return hipGetLastError();
 }
 
 template <typename T, int BT>
 hipError_t gemm_go(const GemmNTParams& q, unsigned blocks, hipStream_t st) {
-    switch (q.epi) {
-        case EPI_STORE: return gemm_go1<T, BT, EPI_STORE>(q, blocks, st);
-        case EPI_SILU: return gemm_go1<T, BT, EPI_SILU>(q, blocks, st);
-        default: return hipErrorInvalidValue;
+    const bool two = q.K2 > 0;
+    const int a2 = two ? q.a2_t : q.a_t, b2 = two ? q.b2_t : q.b_t;
+    const int key = (q.a_t ? 8 : 0) | (q.b_t ? 4 : 0) | (a2 ? 2 : 0) | (b2 ? 1 : 0);
+    if (q.epi == EPI_STORE) {
+        switch (key) {
+            case 0x0: return gemm_go1<T, BT, EPI_STORE, false, false, false, false>(q, blocks, st);
+            case 0x5: return gemm_go1<T, BT, EPI_STORE, false, true, false, true>(q, blocks, st);
+            case 0xF: return gemm_go1<T, BT, EPI_STORE, true, true, true, true>(q, blocks, st);
+            default: return hipErrorInvalidValue;
+        }
     }
+    if (q.epi == EPI_SILU) {
+        switch (key) {
+            case 0x0: return gemm_go1<T, BT, EPI_SILU, false, false, false, false>(q, blocks, st);
+            case 0xC: return gemm_go1<T, BT, EPI_SILU, true, true, false, false>(q, blocks, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace

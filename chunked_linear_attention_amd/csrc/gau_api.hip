@@ -198,8 +198,8 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
 
 // Backward workspace: the forward's regions, then the backward's own.
 struct BwdLayout {
-    size_t H, dWq, Yb, WoT, dOt, Yt, V, dA, dSc, dScE, dSct, At, Kqc, Qqc, Qlc;
-    size_t dQq, dKq, dQl, dKl, dWqc, Pt, dP, dSst, dS, Kl, rpart, hpart, dH, dHt, Xt, Wt, wpart, total;
+    size_t H, dWq, Yb, WoT, dA, dSc, dScE;
+    size_t dQq, dKq, dQl, dKl, dP, dSst, Kl, rpart, hpart, dH, Wt, wpart, total;
     int split_o, split_w;  // K splits of the weight-gradient products
 };
 
@@ -218,7 +218,7 @@ void bwd_layout(const gau_config* c, BwdLayout* L) {
     layout(c, &F, false);
     const size_t eb = elem_bytes(c->dtype);
     const size_t M = (size_t)(c->B * c->T), d = c->d, e = c->e, s = c->s, C = c->C;
-    const size_t G = c->T / c->C, Z = (size_t)c->B * G, Gp = c->causal ? G : 1;
+    const size_t G = c->T / c->C, Z = (size_t)c->B * G;
     const size_t W3 = 2 * e + s;
     // dW_o: feature tiles over e, token tiles over d; [dW_u|dW_v|dW_z]: over d and 2e + s
     L->split_o = weight_splits((int64_t)M, gau::out_gemm_tiles((int)e, (int)d, 256));
@@ -233,52 +233,55 @@ void bwd_layout(const gau_config* c, BwdLayout* L) {
     L->dWq = take(M * e * eb);
     L->Yb = take(M * e * eb);
     L->WoT = take(e * d * eb);
-    L->dOt = take(d * M * eb);
-    L->Yt = take(e * M * eb);
-    L->V = take(M * e * eb);
     L->dA = take(Z * C * C * 4);
     L->dSc = take(Z * C * C * 4);
     L->dScE = take(Z * C * C * eb);
-    L->dSct = take(Z * C * C * eb);
-    L->At = take(Z * C * C * eb);
-    L->Kqc = take(M * s * eb);
-    L->Qqc = take(M * s * eb);
-    L->Qlc = take(M * s * eb);
     L->dQq = take(M * s * 4);
     L->dKq = take(M * s * 4);
     L->dQl = take(M * s * 4);
     L->dKl = take(M * s * 4);
-    L->dWqc = take(M * e * eb);
-    L->Pt = take((size_t)c->B * Gp * e * s * eb);
     L->dP = take(Z * e * s * 4);
     L->dSst = take(Z * e * s * eb);
-    L->dS = take(Z * e * s * eb);
     L->Kl = take(M * s * eb);
     L->rpart = take(M / 32 * (2 * C - 1) * 4);
     L->hpart = take((M + gau::kHeadsBwdTokens - 1) / gau::kHeadsBwdTokens * 8 * s * 4);
     L->dH = take(M * W3 * eb);
-    L->dHt = take(W3 * M * eb);
-    L->Xt = take(d * M * eb);
     L->Wt = take(d * W3 * eb);
     const size_t po = (size_t)L->split_o * d * e, pw = (size_t)L->split_w * W3 * d;
     L->wpart = take((po > pw ? po : pw) * 4);
     L->total = off;
 }
 
-gau::GemmNTParams nt(const void* A, int64_t a_bs, int a_rp, const void* B, int64_t b_bs, int b_rp, void* C,
-                     int64_t c_bs, int c_rp, int K, bool c_f32, float alpha = 1.f, int a_div = 1, int b_div = 1) {
+// One operand of a batched NT product (GemmNTParams): entry z (chunk z % zg
+// of sequence z / zg) at (z / zg) * bsq + (z % zg) * bs elements.
+struct NtOp {
+    const void* p;
+    int64_t bs, bsq;
+    int rp;
+    int mn_major;
+};
+// K-major, rows rp elements apart, entries bs elements apart throughout
+NtOp kmaj(const void* p, int64_t bs, int rp, int zg) { return NtOp{p, bs, bs * zg, rp, 0}; }
+// MN-major, K rows rp elements apart, chunks bs and sequences bsq apart
+NtOp mnmaj(const void* p, int64_t bs, int64_t bsq, int rp) { return NtOp{p, bs, bsq, rp, 1}; }
+
+gau::GemmNTParams nt(const NtOp& a, const NtOp& b, void* C, int64_t c_bs, int c_rp, int K, bool c_f32, int zg,
+                     float alpha = 1.f) {
     gau::GemmNTParams q{};
-    q.A = A;
-    q.B = B;
+    q.A = a.p;
+    q.B = b.p;
     q.C = C;
-    q.a_bs = a_bs;
-    q.b_bs = b_bs;
+    q.a_bs = a.bs;
+    q.a_bsq = a.bsq;
+    q.a_rp = a.rp;
+    q.a_t = a.mn_major;
+    q.b_bs = b.bs;
+    q.b_bsq = b.bsq;
+    q.b_rp = b.rp;
+    q.b_t = b.mn_major;
     q.c_bs = c_bs;
-    q.a_rp = a_rp;
-    q.b_rp = b_rp;
     q.c_rp = c_rp;
-    q.a_div = a_div;
-    q.b_div = b_div;
+    q.zg = zg;
     q.K = K;
     q.c_f32 = c_f32 ? 1 : 0;
     q.alpha = alpha;
@@ -311,9 +314,6 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         if (err == hipSuccess) err = x;
     };
     auto gemm = [&](const gau::GemmNTParams& q, int m, int n, int nb) { ok(gau::launch_gemm_nt(q, m, n, nb, bf, st)); };
-    auto trans = [&](const gau::TransposeParams& q, int r, int cc, int nb) {
-        ok(gau::launch_transpose(q, r, cc, nb, bf, st));
-    };
     // independent transposes queued together and run as one launch
     struct Batch {
         gau::TransposeParams q[gau::kTransposeBatch];
@@ -348,23 +348,14 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
                           c->causal ? 1 : 0, 1, 1};
         ok(gau::launch_chunk_attn(p, bf, st));
     }
-    // every transpose whose input is ready now, in one launch: W_o^T;
-    // token-major V and K_lin; chunk-transposed heads and weights; P^T per
-    // chunk; the weights for dX; dO and X for the weight gradients
-    const int Gp = c->causal ? G : 1;
+    // the transposes left, in one launch: W_o^T (dY), the weights (dX) and
+    // token-major K_lin (dV); every other product reads its operands where
+    // they lie, K-major or MN-major
     add(tp(a.W_o, 0, e, W(L.WoT), 0, d), d, e, 1);
-    add(tp(W(F.Vt), (int64_t)e * T, T, W(L.V), (int64_t)T * e, e), e, T, Bn);
     add(tp(W(F.K_lin_t), (int64_t)s * T, T, W(L.Kl), (int64_t)T * s, s), s, T, Bn);
-    add(tp(W(F.K_quad), Cs, s, W(L.Kqc), Cs, C), C, s, Z);
-    add(tp(W(F.Q_quad), Cs, s, W(L.Qqc), Cs, C), C, s, Z);
-    add(tp(W(F.Q_lin), Cs, s, W(L.Qlc), Cs, C), C, s, Z);
-    add(tp(W(F.A), CC, C, W(L.At), CC, C), C, C, Z);
-    add(tp(W(F.P), es, s, W(L.Pt), es, e), e, s, Bn * Gp);
     add(tp(a.W_u, 0, d, W(L.Wt), 0, W3), e, d, 1);
     add(tp(a.W_v, 0, d, Wc(L.Wt, e), 0, W3), e, d, 1);
     add(tp(a.W_z, 0, d, Wc(L.Wt, 2 * e), 0, W3), s, d, 1);
-    add(tp(dO, 0, d, W(L.dOt), 0, M), M, d, 1);
-    add(tp(a.X, 0, d, W(L.Xt), 0, M), M, d, 1);
     flush();
     // O = Y W_o and the gate Y = U * Wq: dY = dO W_o^T, fused with
     // dWq = dY * U, Y, and dH_u = dY * Wq * SiLU'(H_u)
@@ -373,15 +364,20 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     ok(gau::launch_out_gemm(gau::OutParams{dO, W(L.WoT), W(L.dH), nullptr, M, e, d, 0, W3, W(L.H), W(F.Y),
                                            W(L.dWq), W(L.Yb), e},
                             bf, st));
-    // chunk-transposed dWq, and Y^T for dW_o
-    add(tp(W(L.dWq), Ce, e, W(L.dWqc), Ce, C), C, e, Z);
-    add(tp(W(L.Yb), 0, e, W(L.Yt), 0, M), M, e, 1);
-    flush();
+
+    // operands per chunk z (chunk z % G of sequence z / G): dWq, the heads
+    // and A token-major ([C, e], [C, s], [C, C]); V from Vt and P, dS as
+    // [e, s] (feature-major)
+    const NtOp dWq_k = kmaj(W(L.dWq), Ce, e, G);                       // rows q, K = f
+    const NtOp dWq_m = mnmaj(W(L.dWq), Ce, (int64_t)G * Ce, e);        // K = q, MN = f
+    const NtOp V_m = mnmaj(W(F.Vt), C, (int64_t)e * T, T);             // K = f, MN = keys
+    const NtOp dS_m = mnmaj(W(L.dSst), es, (int64_t)G * es, s);        // K = f, MN = j
+    auto heads_m = [&](size_t off) { return mnmaj(W(off), Cs, (int64_t)G * Cs, s); };  // K = tokens, MN = j
 
     // local part: dA = dWq V^T, dSc = dA * 2 relu(Sc) * mask,
     // dQ_quad = qs dSc K_quad, dK_quad = qs dSc^T Q_quad, dBias
     {
-        gau::GemmNTParams q = nt(W(L.dWq), Ce, e, W(L.V), Ce, e, W(L.dA), CC, C, e, true);
+        gau::GemmNTParams q = nt(dWq_k, V_m, W(L.dA), CC, C, e, true, G);
         q.skip_upper = c->causal ? 1 : 0;
         gemm(q, C, C, Z);
     }
@@ -391,31 +387,38 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         ok(gau::launch_scores_bwd(p, bf, st));
     }
     ok(gau::launch_relpos_bwd((const float*)W(L.dSc), (float*)W(L.rpart), drelpos, Z, C, st));
-    trans(tp(W(L.dScE), CC, C, W(L.dSct), CC, C), C, C, Z);
-    gemm(nt(W(L.dScE), CC, C, W(L.Kqc), Cs, C, W(L.dQq), Cs, s, C, true, c->quad_scale), C, s, Z);
-    gemm(nt(W(L.dSct), CC, C, W(L.Qqc), Cs, C, W(L.dKq), Cs, s, C, true, c->quad_scale), C, s, Z);
+    gemm(nt(kmaj(W(L.dScE), CC, C, G), heads_m(F.K_quad), W(L.dQq), Cs, s, C, true, G, c->quad_scale), C, s, Z);
+    gemm(nt(mnmaj(W(L.dScE), CC, (int64_t)G * CC, C), heads_m(F.Q_quad), W(L.dKq), Cs, s, C, true, G,
+            c->quad_scale),
+         C, s, Z);
 
     // global part: dQ_lin = dWq P^T, dP = Q_lin^T dWq (per chunk, stored [e, s]),
     // dS = ls * (reverse exclusive sum of dP, or the total when non-causal),
     // dK_lin = V dS^T
-    gemm(nt(W(L.dWq), Ce, e, W(L.Pt), es, e, W(L.dQl), Cs, s, e, true, 1.f, 1, c->causal ? 1 : G), C, s, Z);
-    gemm(nt(W(L.dWqc), Ce, C, W(L.Qlc), Cs, C, W(L.dP), es, s, C, true), e, s, Z);
+    {
+        const NtOp P_m = c->causal ? mnmaj(W(F.P), es, (int64_t)G * es, s) : mnmaj(W(F.P), 0, es, s);
+        gemm(nt(dWq_k, P_m, W(L.dQl), Cs, s, e, true, G), C, s, Z);
+    }
+    gemm(nt(dWq_m, heads_m(F.Q_lin), W(L.dP), es, s, C, true, G), e, s, Z);
     {
         gau::BwdScanParams p{(const float*)W(L.dP), W(L.dSst), Bn, G, (int)es, c->causal ? 1 : 0, c->lin_scale};
         ok(gau::launch_scan_bwd(p, bf, st));
     }
-    trans(tp(W(L.dSst), es, s, W(L.dS), es, e), e, s, Z);
-    gemm(nt(W(L.V), Ce, e, W(L.dS), es, e, W(L.dKl), Cs, s, e, true), C, s, Z);
+    gemm(nt(V_m, dS_m, W(L.dKl), Cs, s, e, true, G), C, s, Z);
 
     // dV = A^T dWq + K_lin dS (two K segments), stored as dH_v = dV * SiLU'(H_v)
     {
-        gau::GemmNTParams q = nt(W(L.At), CC, C, W(L.dWqc), Ce, C, Wc(L.dH, e), (int64_t)C * W3, W3, C, false);
-        q.A2 = W(L.Kl);
-        q.a2_bs = Cs;
-        q.a2_rp = s;
-        q.B2 = W(L.dSst);
-        q.b2_bs = es;
-        q.b2_rp = s;
+        gau::GemmNTParams q = nt(mnmaj(W(F.A), CC, (int64_t)G * CC, C), dWq_m, Wc(L.dH, e), (int64_t)C * W3, W3, C,
+                                 false, G);
+        const NtOp Kl_k = kmaj(W(L.Kl), Cs, s, G), dS_k = kmaj(W(L.dSst), es, s, G);
+        q.A2 = Kl_k.p;
+        q.a2_bs = Kl_k.bs;
+        q.a2_bsq = Kl_k.bsq;
+        q.a2_rp = Kl_k.rp;
+        q.B2 = dS_k.p;
+        q.b2_bs = dS_k.bs;
+        q.b2_bsq = dS_k.bsq;
+        q.b2_rp = dS_k.rp;
         q.K2 = s;
         q.epi = gau::EPI_SILU;
         q.H = Wc(L.H, e);
@@ -435,25 +438,26 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
                             bf, st));
 
     // weight gradients, K = M split L.split_* ways into fp32 partials added in
-    // split order: dW_o (stored [d, e]) = dO^T Y, [dW_u | dW_v | dW_z] = dH^T X
+    // split order: dW_o (stored [d, e]) = dO^T Y, [dW_u | dW_v | dW_z] = dH^T X,
+    // on the output GEMM's 256 x 256 tiles with MN-major operands (the
+    // token-major tensors as they lie: K = tokens)
     float* wp = (float*)W(L.wpart);
-    // (the output GEMM's tiles, split over K: rows of Yt (e) as the feature
-    // side and rows of dOt (d) as the token side, so the product is [d, e])
+    // (Y's e features as the feature side, dO's d as the token side: the
+    // product is [d, e])
     {
         const int S = L.split_o;
-        gau::OutParams q{W(L.dOt), W(L.Yt), wp, nullptr, d, e, M, 1, e, nullptr, nullptr, nullptr, nullptr,
-                         0, S, (int64_t)d * e, M, 256};
+        gau::OutParams q{dO, W(L.Yb), wp, nullptr, d, e, M, 1, e, nullptr, nullptr, nullptr, nullptr,
+                         0, S, (int64_t)d * e, d, 256, 1, e};
         ok(gau::launch_out_gemm(q, bf, st));
         ok(gau::launch_split_reduce(wp, (int64_t)d * e, dW_o, (int64_t)d * e, S, st));
     }
-    trans(tp(W(L.dH), 0, W3, W(L.dHt), 0, M), M, W3, 1);
-    // (rows of Xt (d) as the feature side, rows of dHt (2e + s) as the token
-    // side: the product is [2e + s, d])
+    // (X's d features as the feature side, dH's 2e + s as the token side: the
+    // product is [2e + s, d])
     {
         const int S = L.split_w;
         const int64_t stride = (int64_t)W3 * d;
-        gau::OutParams q{W(L.dHt), W(L.Xt), wp, nullptr, W3, d, M, 1, d, nullptr, nullptr, nullptr, nullptr,
-                         0, S, stride, M, 256};
+        gau::OutParams q{W(L.dH), a.X, wp, nullptr, W3, d, M, 1, d, nullptr, nullptr, nullptr, nullptr,
+                         0, S, stride, W3, 256, 1, d};
         ok(gau::launch_out_gemm(q, bf, st));
         ok(gau::launch_split_reduce(wp, stride, dW_u, (int64_t)e * d, S, st));
         ok(gau::launch_split_reduce(wp + (size_t)e * d, stride, dW_v, (int64_t)e * d, S, st));

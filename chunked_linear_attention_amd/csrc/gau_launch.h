@@ -101,6 +101,11 @@ struct OutParams {
     int64_t o_bs;
     int k_rp;          // elements between rows of W_o and Y (their K pitch); 0: e
     int bm;            // feature-tile width (256, 192 or 128); 0: chosen from d and M
+    // MN-major operands (tn = 1; 256-feature tiles, fp32 output without
+    // residual or gate only): K row k of Y holds its M elements contiguously
+    // from Y + k * k_rp, K row k of W_o its d elements from W_o + k * w_rp
+    int tn;
+    int w_rp;
 };
 
 // Blocks of a split-K output GEMM of d x M outputs with feature tiles of bm.
@@ -162,30 +167,36 @@ enum { EPI_STORE = 0,  // C[i] = v (fp32 when c_f32, else the element type)
        EPI_SILU = 1 }; // C[i] = v * SiLU'(H[i])
 
 // Batched C[z] = alpha * (A[z] B[z]^T + A2[z] B2[z]^T) on the MFMA core, 64 x 64
-// or 128 x 128 output tiles.  Operand z of A is at A + (z / a_div) * a_bs
-// elements (B likewise with b_div; A2, B2 with the same divisors and their own
-// strides; C at z * c_bs); rows are *_rp elements apart; every operand is
-// K-major (K and K2 multiples of 64, every dimension a multiple of 64).  The
-// second segment is used when K2 > 0.
+// or 128 x 128 output tiles.  Each operand is K-major (*_t = 0: row r of its
+// M or N axis holds its K elements contiguously, rows *_rp elements apart) or
+// MN-major (*_t = 1: K index k holds its M or N elements contiguously, K rows
+// *_rp elements apart).  Batch entry z is chunk z % zg of sequence z / zg; an
+// operand's entry starts at (z / zg) * *_bsq + (z % zg) * *_bs elements, C's
+// at z * c_bs, C's rows c_rp elements apart.  K and K2 are multiples of 64,
+// every dimension a multiple of 64.  The second segment is used when K2 > 0.
+// Layouts implemented: (a_t, b_t) = (0, 0), (0, 1), (1, 1); with a second
+// segment and the SiLU epilogue (1, 1) then (a2_t, b2_t) = (0, 0).
 struct GemmNTParams {
     const void* A;
     const void* B;
     void* C;
     int64_t a_bs, b_bs, c_bs;
+    int64_t a_bsq, b_bsq;
     int a_rp, b_rp, c_rp;
-    int a_div, b_div;
+    int zg;
     int K;
     int c_f32;
     float alpha;
     int tm, tn;  // row / column tiles per batch entry (set by the launcher)
     const void* A2;
     const void* B2;
-    int64_t a2_bs, b2_bs;
+    int64_t a2_bs, b2_bs, a2_bsq, b2_bsq;
     int a2_rp, b2_rp;
     int K2;
     int epi;
     const void* H;              // EPI_SILU
     int skip_upper;  // skip output tiles wholly above the diagonal (never read)
+    int a_t, b_t, a2_t, b2_t;
 };
 
 // out[z][c][r] = in[z][r][c], element type, R and Cc multiples of 64.

@@ -104,6 +104,84 @@ struct DmaOperand {
     }
 };
 
+// Piece permutation of an MN-major operand tile in LDS (one row per K index,
+// PPR 16-byte pieces of consecutive MN elements per row): logical piece c of
+// row k sits at c ^ tsw<PPR>(k).  It spreads the transposed fragment reads
+// over the banks: a bf16 read touches K rows k0..k0+3 (32 bytes of each per
+// 16 lanes) in both halves of the wave; fp32 reads touch row k in one half of
+// the wave and k + 4 in the other.  With PPR >= 16 (a row covers every bank)
+// 4 (k & 3) separates the four rows and 8 ((k >> 2) & 1) the fp32 halves;
+// with PPR = 8 consecutive rows already alternate between the two halves of
+// the banks and 4 ((k >> 1) & 1) separates the pairs.
+template <int PPR>
+__device__ __forceinline__ int tsw(int k) {
+    if constexpr (PPR >= 16)
+        return (4 * (k & 3)) ^ (8 * ((k >> 2) & 1));
+    else
+        return 4 * ((k >> 1) & 1);
+}
+
+// Direct global -> LDS copy of one K chunk (KE = 128 / EB K indices) of an
+// MN-major operand tile: the segment's K rows are `pitch` bytes apart and hold
+// the tile's ROWS MN elements contiguously from `base`.  In LDS row k of the
+// chunk lies at k * RB bytes (RB = ROWS * EB), its pieces permuted by tsw;
+// each 1 KiB wave copy moves 1024 / RB whole rows, so a chunk is ROWS / 8
+// copies as for a K-major tile.  Pieces past the rows_valid MN elements
+// (rows_valid a multiple of 16 / EB) read the last valid piece instead.
+template <int ROWS, int NW, int EB>
+struct DmaOperandT {
+    static constexpr int RB = ROWS * EB;
+    static constexpr int PPR = RB / 16;
+    static constexpr int KE = 128 / EB;
+    static constexpr int kLoads = ROWS / 8 / NW;
+    static_assert(ROWS % (8 * NW) == 0 && PPR >= 8 && 64 % PPR == 0, "MN-major tile shape");
+    const char* src0[kLoads];
+    const char* src1[kLoads];
+    size_t step0, step1;  // bytes per chunk (KE rows) in each segment
+    int n0;
+
+    __device__ __forceinline__ void init(const KSeg& s0, const KSeg& s1, int rows_valid, int wave, int lane) {
+        n0 = s0.chunks;
+        step0 = (size_t)KE * s0.pitch;
+        step1 = (size_t)KE * s1.pitch;
+        const int last = rows_valid * EB / 16 - 1;
+#pragma unroll
+        for (int jj = 0; jj < kLoads; ++jj) {
+            const int pc = (wave + jj * NW) * 64 + lane;  // LDS piece of the chunk this lane fills
+            const int k = pc / PPR;
+            int c = (pc % PPR) ^ tsw<PPR>(k);  // logical piece held there
+            c = c <= last ? c : last;
+            src0[jj] = s0.base + (size_t)k * s0.pitch + c * 16;
+            src1[jj] = s1.base + (size_t)k * s1.pitch + c * 16;
+        }
+    }
+    // Issue the copy of K chunk `kc` into `lds_tile`.
+    __device__ __forceinline__ void issue(char* lds_tile, int kc, int wave) const {
+        const bool first = kc < n0;
+        const size_t off = first ? (size_t)kc * step0 : (size_t)(kc - n0) * step1;
+#pragma unroll
+        for (int jj = 0; jj < kLoads; ++jj)
+            __builtin_amdgcn_global_load_lds((glb_ptr_t)((first ? src0[jj] : src1[jj]) + off),
+                                             (lds_ptr_t)(lds_tile + (wave + jj * NW) * 1024), 16, 0, 0);
+    }
+};
+
+// Transposed LDS read of 16-bit elements (ds_read_b64_tr_b16, gfx950).  In
+// each group of 16 lanes, lane 4j + r passes the address of four consecutive
+// elements; lane i of the group receives, as its element jj, element i % 4 of
+// the four that lane 4jj + i / 4 addressed (measured on gfx950).  So when
+// lanes 4j .. 4j+3 address 16 consecutive MN elements of K row j, lane i
+// receives MN element i of K rows 0..3.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const char* p) {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)p);
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
+template <bool C, typename X, typename Y> struct PickT { using type = X; };
+template <typename X, typename Y> struct PickT<false, X, Y> { using type = Y; };
+
 // The hardware dispatches workgroup b to XCD b % 8, and each XCD has its own
 // L2.  xcd_remap turns the dispatch index into a logical tile index such that
 // each XCD receives a contiguous range of logical tiles (so neighbouring tiles,
@@ -128,7 +206,8 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >>
 // (for a B operand streamed from HBM beside an A operand that stays in L2).
 // The A stages then lie at [0, NS * A_BYTES) and the B stages after them, and
 // the per-chunk barrier waits only for LDS reads and the copies it needs.
-template <typename T, int BM, int BN, int WGM, int WGN, int NS = 2, int ZR = 0, int NSB = NS>
+template <typename T, int BM, int BN, int WGM, int WGN, int NS = 2, int ZR = 0, int NSB = NS, bool TA = false,
+          bool TB = false>
 struct GemmCore {
     static constexpr int NW = WGM * WGN;
     static constexpr int NT = NW * kWave;
@@ -152,6 +231,10 @@ struct GemmCore {
                   "side operand layout");
     static_assert(NS >= 2 && (NS - 2) * LOADS < 64, "stages / vmcnt range");
     static_assert(!kAsym || (NS == 2 && NSB == 3 && ZR == 0), "split ring: NS = 2, NSB = 3, no side rows");
+    static_assert(!(TA || TB) || (!kAsym && ZR == 0), "MN-major operands: plain ring, no side rows");
+    // copy engines of the two operands (K-major or MN-major tiles)
+    using DA = typename PickT<TA, DmaOperandT<BM, NW, Elem<T>::kBytes>, DmaOperand<BM, NW>>::type;
+    using DB = typename PickT<TB, DmaOperandT<BN, NW, Elem<T>::kBytes>, DmaOperand<BN, NW>>::type;
     static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "tile shape");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "tile rows");
     static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "pieces must split evenly over waves");
@@ -165,13 +248,55 @@ struct GemmCore {
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     }
 
+    // Fragment of the 32 MN rows mn .. mn+31 of an MN-major tile of ROWS
+    // rows for K step ks: the same lane layout as a K-major fragment (lane
+    // l: row l % 32, K indices 8 (l / 32) .. +7 for bf16; 4 (l / 32) + t for
+    // fp32's four K=2 steps).  bf16: two transposed reads of four K rows each;
+    // fp32: four 4-byte reads (32 consecutive MN elements per half wave).
+    template <int ROWS>
+    __device__ static __forceinline__ u32x4_t frag_t(const char* tile, int mn, int ks) {
+        constexpr int EB = Elem<T>::kBytes, RB = ROWS * EB, PPR = RB / 16;
+        const int lane = threadIdx.x % kWave;
+        if constexpr (EB == 2) {
+            const int g = lane & 15, q = lane >> 4, j = g >> 2, r = g & 3;
+            const int m = mn + 16 * (q & 1) + 4 * r;
+            const int k0 = 16 * ks + 8 * (q >> 1) + j;
+            const u32x2_t lo = lds_read_tr16(tile + k0 * RB + (((m >> 3) ^ tsw<PPR>(k0)) << 4) + 8 * (r & 1));
+            const int k1 = k0 + 4;
+            const u32x2_t hi = lds_read_tr16(tile + k1 * RB + (((m >> 3) ^ tsw<PPR>(k1)) << 4) + 8 * (r & 1));
+            return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        } else {
+            const int h = lane >> 5, m = mn + (lane & 31);
+            u32x4_t v;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int k = 8 * ks + 4 * h + t;
+                v[t] = *(const uint32_t*)(tile + k * RB + (((m >> 2) ^ tsw<PPR>(k)) << 4) + 4 * (m & 3));
+            }
+            return v;
+        }
+    }
+
     // Fragments of one 32-byte K step (ks = 0..3 inside a 128-byte chunk).
+    // K-major operands: ta / tb point at the wave's first row of the tile;
+    // MN-major operands: at the tile (the wave's rows are found here).
     __device__ static __forceinline__ void load_frags(u32x4_t (&fa)[MB], u32x4_t (&fb)[NB], const char* ta,
                                                       const char* tb, int ks, int fr, int fh) {
+        const int wave = threadIdx.x / kWave;
+        if constexpr (TA) {
 #pragma unroll
-        for (int i = 0; i < MB; ++i) fa[i] = *(const u32x4_t*)(ta + swz(i * 32 + fr, 2 * ks + fh));
+            for (int i = 0; i < MB; ++i) fa[i] = frag_t<BM>(ta, (wave / WGN) * WTM + i * 32, ks);
+        } else {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) fb[j] = *(const u32x4_t*)(tb + swz(j * 32 + fr, 2 * ks + fh));
+            for (int i = 0; i < MB; ++i) fa[i] = *(const u32x4_t*)(ta + swz(i * 32 + fr, 2 * ks + fh));
+        }
+        if constexpr (TB) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) fb[j] = frag_t<BN>(tb, (wave % WGN) * WTN + j * 32, ks);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) fb[j] = *(const u32x4_t*)(tb + swz(j * 32 + fr, 2 * ks + fh));
+        }
     }
 
     __device__ static __forceinline__ void mma_step(f32x16_t (&acc)[MB][NB], const u32x4_t (&fa)[MB],
@@ -227,10 +352,9 @@ struct GemmCore {
     template <int KS, bool ISSUE, bool SIDE>
     __device__ static __forceinline__ void step(f32x16_t (&acc)[MB][NB], u32x4_t (&fa)[2][MB],
                                                 u32x4_t (&fb)[2][NB], const char* ta, const char* tb,
-                                                const DmaOperand<BM, NW>& da, const DmaOperand<BN, NW>& db,
-                                                char* nxt, int kc_next, int wave, int fr, int fh, Side& sd,
-                                                const char* tz, int lane) {
-        constexpr int NL = DmaOperand<BM, NW>::kLoads + DmaOperand<BN, NW>::kLoads;
+                                                const DA& da, const DB& db, char* nxt, int kc_next, int wave,
+                                                int fr, int fh, Side& sd, const char* tz, int lane) {
+        constexpr int NL = DA::kLoads + DB::kLoads;
         if constexpr (KS < 3) load_frags(fa[(KS + 1) & 1], fb[(KS + 1) & 1], ta, tb, KS + 1, fr, fh);
         if constexpr (SIDE && KS < 3) {
             if (sd.on) load_side(sd, (KS + 1) & 1, tz, KS + 1, fr, fh);
@@ -259,9 +383,8 @@ struct GemmCore {
     template <bool ISSUE, bool SIDE>
     __device__ static __forceinline__ void chunk(f32x16_t (&acc)[MB][NB], u32x4_t (&fa)[2][MB],
                                                  u32x4_t (&fb)[2][NB], const char* ta, const char* tb,
-                                                 const DmaOperand<BM, NW>& da, const DmaOperand<BN, NW>& db,
-                                                 char* nxt, int kc_next, int wave, int fr, int fh, Side& sd,
-                                                 const char* tz, int lane) {
+                                                 const DA& da, const DB& db, char* nxt, int kc_next, int wave,
+                                                 int fr, int fh, Side& sd, const char* tz, int lane) {
         step<0, ISSUE, SIDE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh, sd, tz, lane);
         step<1, ISSUE, SIDE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh, sd, tz, lane);
         step<2, ISSUE, SIDE>(acc, fa, fb, ta, tb, da, db, nxt, kc_next, wave, fr, fh, sd, tz, lane);
@@ -303,8 +426,8 @@ struct GemmCore {
         const int fr = lane & 31;  // fragment row
         const int fh = lane >> 5;  // fragment K half
 
-        DmaOperand<BM, NW> da;
-        DmaOperand<BN, NW> db;
+        DA da;
+        DB db;
         da.init(a0, a1, rows_a, wave, lane);
         db.init(b0, b1, rows_b, wave, lane);
 #pragma unroll
@@ -320,7 +443,7 @@ struct GemmCore {
         __syncthreads();
 
         u32x4_t fa[2][MB], fb[2][NB];
-        const int oa = (wm * WTM) * 128, ob = A_BYTES + (wn * WTN) * 128;
+        const int oa = TA ? 0 : (wm * WTM) * 128, ob = A_BYTES + (TB ? 0 : (wn * WTN) * 128);
         load_frags(fa[0], fb[0], lds + oa, lds + ob, 0, fr, fh);
         if constexpr (SIDE) {
             if (sd.on) load_side(sd, 0, lds + Z_OFF, 0, fr, fh);

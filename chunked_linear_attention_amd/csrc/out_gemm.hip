@@ -42,20 +42,22 @@ __device__ __forceinline__ void put4(char* p, const float (&v)[4]) {
 
 constexpr int BN = 256, WGM = 2, WGN = 4;  // tokens per tile, wave grid
 
-template <typename T, int BM>
+template <typename T, int BM, bool TN = false>
 struct OutTile {
     // Y (the B operand) streams from HBM: a third B stage keeps two of its
-    // chunks in flight; W_o (A) stays in L2 with two stages
-    using G = GemmCore<T, BM, BN, WGM, WGN, 2, 0, 3>;
+    // chunks in flight; W_o (A) stays in L2 with two stages.  MN-major
+    // operands (TN) take the plain two-stage ring.
+    using G = typename PickT<TN, GemmCore<T, BM, BN, WGM, WGN, 2, 0, 2, true, true>,
+                             GemmCore<T, BM, BN, WGM, WGN, 2, 0, 3>>::type;
     // staging of one pass of the epilogue in the worst case (fp32, WGN passes)
     static constexpr int STAGE = BN / WGN * (BM * 4 + 16);
     static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
 };
 
-template <typename T, int BM>
+template <typename T, int BM, bool TN>
 __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     extern __shared__ __align__(16) char lds[];
-    using G = typename OutTile<T, BM>::G;
+    using G = typename OutTile<T, BM, TN>::G;
     constexpr int EB = Elem<T>::kBytes;
     const int ntiles = (p.d + BM - 1) / BM;  // feature tiles (acc rows)
     const int tiles = ntiles * ((p.M + BN - 1) / BN);
@@ -76,14 +78,28 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     // the packed epilogue writes run along the token-major rows of O.
     f32x16_t acc[G::MB][G::NB];
     G::zero(acc);
-    G::run(acc, (const char*)p.W_o + (size_t)n0 * pitch + (size_t)kc0 * 128, pitch, rows_w,
-           (const char*)p.Y + (size_t)m0 * pitch + (size_t)kc0 * 128, pitch, rows_y, nkz * G::KELEMS, lds);
+    if constexpr (TN) {
+        // tiles start at column n0 (m0) of their first K row
+        const size_t wp = (size_t)p.w_rp * EB, yp = (size_t)p.k_rp * EB;
+        G::run(acc, (const char*)p.W_o + (size_t)n0 * EB + (size_t)kc0 * G::KELEMS * wp, wp, rows_w,
+               (const char*)p.Y + (size_t)m0 * EB + (size_t)kc0 * G::KELEMS * yp, yp, rows_y, nkz * G::KELEMS, lds);
+    } else {
+        G::run(acc, (const char*)p.W_o + (size_t)n0 * pitch + (size_t)kc0 * 128, pitch, rows_w,
+               (const char*)p.Y + (size_t)m0 * pitch + (size_t)kc0 * 128, pitch, rows_y, nkz * G::KELEMS, lds);
+    }
 
-    constexpr int LDS = OutTile<T, BM>::LDS;
+    constexpr int LDS = OutTile<T, BM, TN>::LDS;
     const int M = p.M, d = p.d;
     const size_t orp = p.o_rp > 0 ? (size_t)p.o_rp : (size_t)d;  // output row pitch
     auto ident = [](int, int, float v) { return v; };
-    if (p.gH != nullptr) {
+    if constexpr (TN) {
+        // fp32 O = Y W_o (split z: its partial product at O + z * o_bs)
+        float* O = (float*)p.O + (size_t)z * p.o_bs;
+        G::template store_packed<float>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
+            const int m = m0 + tok, n = n0 + feat;
+            return (m < M && n < d) ? (char*)(O + (size_t)m * orp + n) : nullptr;
+        });
+    } else if (p.gH != nullptr) {
         // gate epilogue: the product staged in fp32; each 16-byte staged vector
         // is four columns n..n+3 of row m.  The staging address handed to the
         // emitter is O + 4 (m o_rp + n) (a position code, never dereferenced
@@ -149,17 +165,19 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     }
 }
 
-template <typename T, int BM>
+template <typename T, int BM, bool TN = false>
 hipError_t launch(const OutParams& p, hipStream_t st) {
-    constexpr int LDS = OutTile<T, BM>::LDS;
+    constexpr int LDS = OutTile<T, BM, TN>::LDS;
     static_assert(LDS <= 160 * 1024, "output GEMM LDS over budget");
     const int S = p.ksplit > 1 ? p.ksplit : 1;
     if (S > 1 && (p.residual != nullptr || p.gH != nullptr || !p.f32_out)) return hipErrorInvalidValue;
-    if (S > p.e / OutTile<T, BM>::G::KELEMS) return hipErrorInvalidValue;
+    if (TN && (p.residual != nullptr || p.gH != nullptr || !p.f32_out || p.M % 64 != 0 || p.d % 64 != 0))
+        return hipErrorInvalidValue;
+    if (S > p.e / OutTile<T, BM, TN>::G::KELEMS) return hipErrorInvalidValue;
     const int blocks = ((p.d + BM - 1) / BM) * ((p.M + BN - 1) / BN) * S;
-    hipError_t e = allow_lds<out_gemm_kernel<T, BM>>(LDS);
+    hipError_t e = allow_lds<out_gemm_kernel<T, BM, TN>>(LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((out_gemm_kernel<T, BM>), dim3(blocks), dim3(512), LDS, st, p);
+    hipLaunchKernelGGL((out_gemm_kernel<T, BM, TN>), dim3(blocks), dim3(512), LDS, st, p);
     return hipGetLastError();
 }
 
@@ -184,6 +202,7 @@ int feature_tile(int d, int M) {
 
 template <typename T>
 hipError_t dispatch(const OutParams& p, hipStream_t st) {
+    if (p.tn) return p.bm == 256 ? launch<T, 256, true>(p, st) : hipErrorInvalidValue;
     switch (p.bm > 0 ? p.bm : feature_tile(p.d, p.M)) {
         case 256: return launch<T, 256>(p, st);
         case 192: return launch<T, 192>(p, st);

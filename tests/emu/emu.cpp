@@ -52,7 +52,7 @@ namespace emu {
 namespace {
 
 enum State { READY, AT_BARRIER, AT_WAVE, DONE };
-enum WaveOp { OP_NONE, OP_M32_BF16, OP_M32_F32, OP_M16_BF16, OP_M16_F32, OP_SHFL };
+enum WaveOp { OP_NONE, OP_M32_BF16, OP_M32_F32, OP_M16_BF16, OP_M16_F32, OP_SHFL, OP_TR16 };
 
 struct DmaEntry {
     char* dst;
@@ -70,6 +70,8 @@ struct Lane {
     WaveOp op = OP_NONE;
     int op_arg = 0;
     float a[8], b[8], c[16], r[16];
+    const char* tr_ptr = nullptr;  // OP_TR16: this lane's LDS address
+    uint16_t tr_out[4];
 };
 
 struct Wave {
@@ -160,6 +162,24 @@ void run_wave_op(int w, int first, int n) {
     const int arg = L[0].op_arg;
     for (int i = 0; i < n; ++i)
         if (L[i].op != op || L[i].op_arg != arg) fail("wave %d: lanes wait at different wave ops", w);
+    if (op == OP_TR16) {
+        // ds_read_b64_tr_b16: per group of 16 lanes, lane i receives as its
+        // element jj element i % 4 of the 8 bytes lane 4 jj + i / 4 addressed
+        if (n != 64) fail("transposed LDS read in a partial wave");
+        for (int i = 0; i < n; ++i) {
+            const char* q = L[i].tr_ptr;
+            if (q < g_lds || q + 8 > g_lds + g_lds_bytes)
+                fail("transposed read of LDS [%td, %td) outside the %zu-byte allocation", q - g_lds, q + 8 - g_lds,
+                     g_lds_bytes);
+            if (((q - g_lds) & 7) != 0) fail("transposed read address not 8-byte aligned");
+        }
+        for (int l = 0; l < 64; ++l) {
+            const int g = l % 16, base = l - g;
+            for (int jj = 0; jj < 4; ++jj)
+                memcpy(&L[l].tr_out[jj], L[base + 4 * jj + g / 4].tr_ptr + 2 * (g % 4), 2);
+        }
+        return;
+    }
     if (op == OP_SHFL) {
         for (int i = 0; i < n; ++i) {
             const int src = i ^ arg;
@@ -347,6 +367,24 @@ f32x4_t mfma_16x16x4_f32(float a, float b, f32x4_t c) {
     f32x4_t d;
     for (int r = 0; r < 4; ++r) d[r] = g_cur->r[r];
     return d;
+}
+
+s16x4_t ds_read_tr16(const void* p) {
+    const char* q = (const char*)p;
+    s16x4_t out;
+    if (!g_full) {
+        // addresses only: the lane's own 8 bytes (in bounds, aligned)
+        if (q < g_lds || q + 8 > g_lds + g_lds_bytes)
+            fail("transposed read of LDS [%td, %td) outside the %zu-byte allocation", q - g_lds, q + 8 - g_lds,
+                 g_lds_bytes);
+        if (((q - g_lds) & 7) != 0) fail("transposed read address not 8-byte aligned");
+        memcpy(&out, q, 8);
+        return out;
+    }
+    g_cur->tr_ptr = q;
+    wave_op(OP_TR16, 0);
+    memcpy(&out, g_cur->tr_out, 8);
+    return out;
 }
 
 float shfl_xor(float v, int mask) {

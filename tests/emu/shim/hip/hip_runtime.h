@@ -30,6 +30,7 @@ namespace emu {
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 const dim3& thread_idx();
 const dim3& block_idx();
 const dim3& grid_dim();
@@ -44,6 +45,7 @@ f32x16_t mfma_32x32x2_f32(float a, float b, f32x16_t c);
 f32x4_t mfma_16x16x32_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c);
 f32x4_t mfma_16x16x4_f32(float a, float b, f32x4_t c);
 float shfl_xor(float v, int mask);
+s16x4_t ds_read_tr16(const void* p);
 hipError_t func_set_attr(const void* f, int attr, int value);
 void launch_impl(const char* name, const void* fn, void (*tramp)(void*), void* ctx, dim3 grid, dim3 block,
                  size_t lds, hipStream_t st);
@@ -73,6 +75,7 @@ using std::min;
 #define __builtin_amdgcn_global_load_lds(g, l, sz, off, aux) \
     ::emu::global_load_lds((const void*)(g), (void*)(l), sz, off, aux)
 #define __builtin_amdgcn_s_waitcnt(imm) ::emu::s_waitcnt(imm)
+#define __builtin_amdgcn_ds_read_tr16_b64_v4i16(p) ::emu::ds_read_tr16((const void*)(p))
 #define __builtin_amdgcn_sched_group_barrier(a, b, c) ((void)0)
 #define __builtin_amdgcn_s_barrier() ::emu::syncthreads()
 #define __builtin_amdgcn_sched_barrier(m) ((void)0)
