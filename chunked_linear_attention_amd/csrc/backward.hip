@@ -238,36 +238,63 @@ __global__ __launch_bounds__(256) void relpos_partial_kernel(const float* dsc, f
 }
 
 // Column sums of a [rows, cols] fp32 array whose rows are `pitch` apart:
-// out[c] = sum_r in[r * pitch + c].  Block of 16 columns x 64 row groups; row
-// group g adds rows g, g+64, ... in order, then the 64 group sums are added
-// in group order.
-__global__ __launch_bounds__(1024) void colsum_kernel(const float* in, int pitch, float* out, int rows, int cols) {
-    constexpr int CW = 16, NG = 64;
+// column c < split goes to out0[c], column c >= split to out1[c - split].
+// Block of 16 columns x 64 row groups; row group g adds rows g, g+64, ... in
+// order (eight loads in flight), then the 64 group sums are added in group
+// order.
+__global__ __launch_bounds__(1024) void colsum_kernel(const float* in, int pitch, float* out0, float* out1, int split,
+                                                      int rows, int cols) {
+    constexpr int CW = 16, NG = 64, NL = 8;
     constexpr int RED = NG * CW;
     __shared__ float red[RED];
     const int cl = threadIdx.x % CW, g = threadIdx.x / CW;
     const int c = blockIdx.x * CW + cl;
     float acc = 0.f;
-    if (c < cols)
-        for (int r = g; r < rows; r += NG) acc += in[(size_t)r * pitch + c];
+    if (c < cols) {
+        int r = g;
+        for (; r + (NL - 1) * NG < rows; r += NL * NG) {
+            float v[NL];
+#pragma unroll
+            for (int k = 0; k < NL; ++k) v[k] = in[(size_t)(r + k * NG) * pitch + c];
+#pragma unroll
+            for (int k = 0; k < NL; ++k) acc += v[k];
+        }
+        for (; r < rows; r += NG) acc += in[(size_t)r * pitch + c];
+    }
     red[g * CW + cl] = acc;
     __syncthreads();
     if (g == 0 && c < cols) {
         float s = 0.f;
         for (int k = 0; k < NG; ++k) s += red[k * CW + cl];
-        out[c] = s;
+        if (c < split)
+            out0[c] = s;
+        else
+            out1[c - split] = s;
     }
 }
 
 // out[i] = sum over z = 0..S-1 (in order) of part[z * stride + i], four
-// entries per thread (n a multiple of 4).
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* part, int64_t stride, float* out, int64_t n,
-                                                           int S) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= n) return;
+// entries per thread (n a multiple of 4), for up to kSplitJobs jobs: job j
+// takes blocks start[j] .. start[j+1]-1.
+constexpr int kSplitJobs = 4;
+struct SplitJobs {
+    const float* part[kSplitJobs];
+    float* out[kSplitJobs];
+    int64_t n[kSplitJobs];
+    int start[kSplitJobs + 1];
+    int64_t stride;
+    int S, jobs;
+};
+
+__global__ __launch_bounds__(256) void split_reduce_kernel(SplitJobs q) {
+    int j = 0;
+    while (j + 1 < q.jobs && (int)blockIdx.x >= q.start[j + 1]) ++j;
+    const int64_t i = ((int64_t)(blockIdx.x - q.start[j]) * 256 + threadIdx.x) * 4;
+    if (i >= q.n[j]) return;
+    const float* part = q.part[j];
     f32x4_t acc = *(const f32x4_t*)(part + i);
-    for (int z = 1; z < S; ++z) acc += *(const f32x4_t*)(part + z * stride + i);
-    *(f32x4_t*)(out + i) = acc;
+    for (int z = 1; z < q.S; ++z) acc += *(const f32x4_t*)(part + z * q.stride + i);
+    *(f32x4_t*)(q.out[j] + i) = acc;
 }
 
 // dS from dP (fp32 [B, G, s*e]): causal dS_h = sum_{g > h} dP_g (a reverse
@@ -367,7 +394,8 @@ hipError_t gemm_go(const GemmNTParams& q, unsigned blocks, hipStream_t st) {
 hipError_t launch_gemm_nt(const GemmNTParams& q0, int M, int N, int nb, bool bf, hipStream_t st) {
     GemmNTParams q = q0;
     // 128 x 128 tiles when they divide the output and still give every CU work
-    const bool big = M % 128 == 0 && N % 128 == 0 && (int64_t)nb * (M / 128) * (N / 128) >= 512;
+    if (q.bt != 0 && q.bt != 64 && !(q.bt == 128 && M % 128 == 0 && N % 128 == 0)) return hipErrorInvalidValue;
+    const bool big = q.bt ? q.bt == 128 : M % 128 == 0 && N % 128 == 0 && (int64_t)nb * (M / 128) * (N / 128) >= 512;
     const int bt = big ? 128 : 64;
     q.tm = M / bt;
     q.tn = N / bt;
@@ -424,15 +452,31 @@ hipError_t launch_relpos_bwd(const float* dsc, float* part, float* drelpos, int 
     hipLaunchKernelGGL(relpos_partial_kernel, dim3(rows, (2 * C - 1 + 255) / 256), dim3(256), 0, st, dsc, part, C);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(colsum_kernel, dim3((2 * C - 1 + 15) / 16), dim3(1024), 0, st, part, 2 * C - 1, drelpos, rows,
-                       2 * C - 1);
+    hipLaunchKernelGGL(colsum_kernel, dim3((2 * C - 1 + 15) / 16), dim3(1024), 0, st, part, 2 * C - 1, drelpos,
+                       drelpos, 2 * C - 1, rows, 2 * C - 1);
     return hipGetLastError();
 }
 
-hipError_t launch_split_reduce(const float* part, int64_t stride, float* out, int64_t n, int S, hipStream_t st) {
-    if (n % 4 != 0 || stride % 4 != 0) return hipErrorInvalidValue;
-    const int64_t blocks = (n / 4 + 255) / 256;
-    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, stride, out, n, S);
+hipError_t launch_split_reduce(const float* const* parts, float* const* outs, const int64_t* ns, int jobs,
+                               int64_t stride, int S, hipStream_t st) {
+    if (jobs < 1 || jobs > kSplitJobs || stride % 4 != 0 || S < 1) return hipErrorInvalidValue;
+    SplitJobs q{};
+    q.stride = stride;
+    q.S = S;
+    q.jobs = jobs;
+    int64_t blocks = 0;
+    for (int j = 0; j < jobs; ++j) {
+        if (ns[j] % 4 != 0 || ns[j] > stride) return hipErrorInvalidValue;
+        q.part[j] = parts[j];
+        q.out[j] = outs[j];
+        q.n[j] = ns[j];
+        q.start[j] = (int)blocks;
+        blocks += (ns[j] / 4 + 255) / 256;
+        if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    }
+    q.start[jobs] = (int)blocks;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, q);
     return hipGetLastError();
 }
 
@@ -445,12 +489,10 @@ hipError_t launch_heads_bwd(const BwdHeadsParams& q, float* dscale, float* doffs
     const int nblk = (q.M + kHeadsBwdTokens - 1) / kHeadsBwdTokens;
     hipError_t e = bf ? go(heads_bwd_kernel<bf16>, (unsigned)nblk, q, st) : go(heads_bwd_kernel<float>, (unsigned)nblk, q, st);
     if (e != hipSuccess) return e;
-    // part is [nblk, 8, s]: the gamma sums in rows 0..3, the beta sums in rows 4..7
-    const dim3 g((4 * q.s + 15) / 16);
-    hipLaunchKernelGGL(colsum_kernel, g, dim3(1024), 0, st, q.part, 8 * q.s, dscale, nblk, 4 * q.s);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(colsum_kernel, g, dim3(1024), 0, st, q.part + 4 * q.s, 8 * q.s, doffset, nblk, 4 * q.s);
+    // part is [nblk, 8, s]: the gamma sums in rows 0..3, the beta sums in rows
+    // 4..7, i.e. columns [0, 4s) and [4s, 8s) of an [nblk, 8s] array
+    hipLaunchKernelGGL(colsum_kernel, dim3((8 * q.s + 15) / 16), dim3(1024), 0, st, q.part, 8 * q.s, dscale, doffset,
+                       4 * q.s, nblk, 8 * q.s);
     return hipGetLastError();
 }
 

@@ -379,6 +379,7 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     {
         gau::GemmNTParams q = nt(dWq_k, V_m, W(L.dA), CC, C, e, true, G);
         q.skip_upper = c->causal ? 1 : 0;
+        q.bt = C % 128 == 0 ? 128 : 64;  // K = e is long: the larger tile's operand reuse pays
         gemm(q, C, C, Z);
     }
     {
@@ -449,7 +450,10 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         gau::OutParams q{dO, W(L.Yb), wp, nullptr, d, e, M, 1, e, nullptr, nullptr, nullptr, nullptr,
                          0, S, (int64_t)d * e, d, 256, 1, e};
         ok(gau::launch_out_gemm(q, bf, st));
-        ok(gau::launch_split_reduce(wp, (int64_t)d * e, dW_o, (int64_t)d * e, S, st));
+        const float* parts[1] = {wp};
+        float* outs[1] = {dW_o};
+        const int64_t ns[1] = {(int64_t)d * e};
+        ok(gau::launch_split_reduce(parts, outs, ns, 1, (int64_t)d * e, S, st));
     }
     // (X's d features as the feature side, dH's 2e + s as the token side: the
     // product is [2e + s, d])
@@ -459,9 +463,10 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         gau::OutParams q{W(L.dH), a.X, wp, nullptr, W3, d, M, 1, d, nullptr, nullptr, nullptr, nullptr,
                          0, S, stride, W3, 256, 1, d};
         ok(gau::launch_out_gemm(q, bf, st));
-        ok(gau::launch_split_reduce(wp, stride, dW_u, (int64_t)e * d, S, st));
-        ok(gau::launch_split_reduce(wp + (size_t)e * d, stride, dW_v, (int64_t)e * d, S, st));
-        ok(gau::launch_split_reduce(wp + (size_t)2 * e * d, stride, dW_z, (int64_t)s * d, S, st));
+        const float* parts[3] = {wp, wp + (size_t)e * d, wp + (size_t)2 * e * d};
+        float* outs[3] = {dW_u, dW_v, dW_z};
+        const int64_t ns[3] = {(int64_t)e * d, (int64_t)e * d, (int64_t)s * d};
+        ok(gau::launch_split_reduce(parts, outs, ns, 3, stride, S, st));
     }
     return err == hipSuccess ? GAU_OK : GAU_ERR_HIP;
 }

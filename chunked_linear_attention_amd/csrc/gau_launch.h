@@ -197,6 +197,7 @@ struct GemmNTParams {
     const void* H;              // EPI_SILU
     int skip_upper;  // skip output tiles wholly above the diagonal (never read)
     int a_t, b_t, a2_t, b2_t;
+    int bt;          // tile size 64 or 128; 0: 128 when it divides M and N and gives >= 512 blocks
 };
 
 // out[z][c][r] = in[z][r][c], element type, R and Cc multiples of 64.
@@ -255,8 +256,11 @@ hipError_t launch_transpose_batch(const TransposeParams* jobs, const int* R, con
 hipError_t launch_scores_bwd(const BwdElemParams& q, bool bf16_storage, hipStream_t st);
 // drelpos[k] = sum over chunks and over entries on diagonal k - (C-1) of dsc
 hipError_t launch_relpos_bwd(const float* dsc, float* part, float* drelpos, int nchunks, int C, hipStream_t st);
-// out[i] = sum_{z < S} part[z * stride + i], i < n (n, stride multiples of 4)
-hipError_t launch_split_reduce(const float* part, int64_t stride, float* out, int64_t n, int S, hipStream_t st);
+// For each job j < jobs (at most 4), in one launch:
+// outs[j][i] = sum_{z < S} parts[j][z * stride + i], i < ns[j]
+// (ns[j] <= stride, both multiples of 4)
+hipError_t launch_split_reduce(const float* const* parts, float* const* outs, const int64_t* ns, int jobs,
+                               int64_t stride, int S, hipStream_t st);
 hipError_t launch_scan_bwd(const BwdScanParams& q, bool bf16_storage, hipStream_t st);
 hipError_t launch_heads_bwd(const BwdHeadsParams& q, float* dscale, float* doffset, bool bf16_storage,
                             hipStream_t st);
