@@ -90,8 +90,12 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmNTParams q) {
     };
     f32x16_t acc[G::MB][G::NB];
     G::zero(acc);
-    G::run(acc, tile(q.A, q.a_bsq, q.a_bs, q.a_rp, TA, m0), (size_t)q.a_rp * EB, BT,
-           tile(q.B, q.b_bsq, q.b_bs, q.b_rp, TB, n0), (size_t)q.b_rp * EB, BT, q.K, lds);
+    // first K index of segment 1 (a K row of an MN-major operand, an element
+    // of a K-major one's rows)
+    const int k0 = q.k_from_row ? m0 : 0;
+    G::run(acc, tile(q.A, q.a_bsq, q.a_bs, q.a_rp, TA, m0) + (TA ? (int64_t)k0 * q.a_rp : k0) * EB,
+           (size_t)q.a_rp * EB, BT, tile(q.B, q.b_bsq, q.b_bs, q.b_rp, TB, n0) + (TB ? (int64_t)k0 * q.b_rp : k0) * EB,
+           (size_t)q.b_rp * EB, BT, q.K - k0, lds);
     if (q.K2 > 0)
         G2::run(acc, tile(q.A2, q.a2_bsq, q.a2_bs, q.a2_rp, TA2, m0), (size_t)q.a2_rp * EB, BT,
                 tile(q.B2, q.b2_bsq, q.b2_bs, q.b2_rp, TB2, n0), (size_t)q.b2_rp * EB, BT, q.K2, lds);
@@ -204,37 +208,46 @@ __global__ __launch_bounds__(256) void transpose_batch_kernel(TransposeBatch b) 
 }
 
 // dSc = 2 relu(Sc) dA * mask with relu(Sc) = sqrt(A) (A = relu(Sc)^2 as the
-// forward stored it); fp32 copy for the bias gradient, element type for the
-// products.  One thread per entry of the [B*G, C, C] scores.
+// forward stored it), stored in the element type for the products, and the
+// bias gradient's first stage: per chunk and slab of 32 query rows, the sums
+// of dSc along each diagonal (key - query = k - (C-1)), rows in order.  One
+// block per slab: its 32 x C entries (eight consecutive ones per thread and
+// step) are kept in LDS in fp32 for the diagonal sums, one thread per
+// diagonal.
 template <typename T>
-__global__ __launch_bounds__(256) void scores_bwd_kernel(BwdElemParams q) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= q.n) return;
-    const int C = q.C;
-    const int r = (int)((i / C) % C), c = (int)(i % C);  // query, key
-    float v = 0.f;
-    if (!q.causal || c <= r) v = 2.f * sqrtf(fmaxf(ld<T>(q.b, i), 0.f)) * q.f1[i];
-    q.f0[i] = v;
-    st<T>(q.o0, i, v);
-}
-
-// Bias gradient, stage 1: per chunk and slab of 32 query rows, the sums of dSc
-// along each diagonal (key - query = k - (C-1)), one thread per diagonal.
-__global__ __launch_bounds__(256) void relpos_partial_kernel(const float* dsc, float* part, int C) {
-    const int k = blockIdx.y * 256 + threadIdx.x;
-    if (k >= 2 * C - 1) return;
-    const int slabs = C / 32;
+__global__ __launch_bounds__(256) void scores_bwd_kernel(BwdElemParams q, float* part) {
+    extern __shared__ __align__(16) char lds[];
+    float* slab = (float*)lds;  // [32, C]
+    const int C = q.C, slabs = C / 32;
     const size_t z = blockIdx.x / slabs;
     const int i0 = (blockIdx.x % slabs) * 32;
-    const float* m = dsc + z * C * C;
-    const int dd = k - (C - 1);
-    float acc = 0.f;
-#pragma unroll 8
-    for (int i = i0; i < i0 + 32; ++i) {
-        const int j = i + dd;
-        if (j >= 0 && j < C) acc += m[(size_t)i * C + j];
+#pragma unroll 4
+    for (int t8 = threadIdx.x; t8 < 4 * C; t8 += 256) {
+        const int t = 8 * t8, r = i0 + t / C, c = t % C;  // query, first key of eight
+        const size_t i = (z * C + r) * C + c;
+        float a[8], v[8];
+        load8<T>(q.b, (int64_t)i, a);
+        const f32x4_t d0 = *(const f32x4_t*)(q.f1 + i), d1 = *(const f32x4_t*)(q.f1 + i + 4);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float dk = k < 4 ? d0[k] : d1[k - 4];
+            v[k] = (!q.causal || c + k <= r) ? 2.f * sqrtf(fmaxf(a[k], 0.f)) * dk : 0.f;
+        }
+        store8<T>(q.o0, (int64_t)i, v);
+        *(f32x4_t*)(slab + t) = f32x4_t{v[0], v[1], v[2], v[3]};
+        *(f32x4_t*)(slab + t + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
     }
-    part[(size_t)blockIdx.x * (2 * C - 1) + k] = acc;
+    __syncthreads();
+    for (int k = threadIdx.x; k < 2 * C - 1; k += 256) {
+        const int dd = k - (C - 1);
+        float acc = 0.f;
+#pragma unroll 8
+        for (int ii = 0; ii < 32; ++ii) {
+            const int j = i0 + ii + dd;
+            if (j >= 0 && j < C) acc += slab[ii * C + j];
+        }
+        part[(size_t)blockIdx.x * (2 * C - 1) + k] = acc;
+    }
 }
 
 // Column sums of a [rows, cols] fp32 array whose rows are `pitch` apart:
@@ -395,6 +408,7 @@ hipError_t launch_gemm_nt(const GemmNTParams& q0, int M, int N, int nb, bool bf,
     GemmNTParams q = q0;
     // 128 x 128 tiles when they divide the output and still give every CU work
     if (q.bt != 0 && q.bt != 64 && !(q.bt == 128 && M % 128 == 0 && N % 128 == 0)) return hipErrorInvalidValue;
+    if (q.k_from_row && (M > q.K || q.K % 64 != 0)) return hipErrorInvalidValue;
     const bool big = q.bt ? q.bt == 128 : M % 128 == 0 && N % 128 == 0 && (int64_t)nb * (M / 128) * (N / 128) >= 512;
     const int bt = big ? 128 : 64;
     q.tm = M / bt;
@@ -442,15 +456,18 @@ hipError_t launch_transpose(const TransposeParams& q0, int R, int Cc, int nb, bo
     return hipGetLastError();
 }
 
-hipError_t launch_scores_bwd(const BwdElemParams& q, bool bf, hipStream_t st) {
-    const unsigned b = (unsigned)((q.n + 255) / 256);
-    return bf ? go(scores_bwd_kernel<bf16>, b, q, st) : go(scores_bwd_kernel<float>, b, q, st);
-}
-
-hipError_t launch_relpos_bwd(const float* dsc, float* part, float* drelpos, int nchunks, int C, hipStream_t st) {
-    const int rows = nchunks * (C / 32);
-    hipLaunchKernelGGL(relpos_partial_kernel, dim3(rows, (2 * C - 1 + 255) / 256), dim3(256), 0, st, dsc, part, C);
-    hipError_t e = hipGetLastError();
+hipError_t launch_scores_bwd(const BwdElemParams& q, float* part, float* drelpos, bool bf, hipStream_t st) {
+    const int C = q.C;
+    if (C % 32 != 0 || q.n % ((size_t)C * C) != 0) return hipErrorInvalidValue;
+    const int nchunks = (int)(q.n / ((size_t)C * C)), rows = nchunks * (C / 32);
+    const int lds = 32 * C * 4;
+    hipError_t e = bf ? allow_lds<scores_bwd_kernel<bf16>>(lds) : allow_lds<scores_bwd_kernel<float>>(lds);
+    if (e != hipSuccess) return e;
+    if (bf)
+        hipLaunchKernelGGL(scores_bwd_kernel<bf16>, dim3(rows), dim3(256), lds, st, q, part);
+    else
+        hipLaunchKernelGGL(scores_bwd_kernel<float>, dim3(rows), dim3(256), lds, st, q, part);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(colsum_kernel, dim3((2 * C - 1 + 15) / 16), dim3(1024), 0, st, part, 2 * C - 1, drelpos,
                        drelpos, 2 * C - 1, rows, 2 * C - 1);

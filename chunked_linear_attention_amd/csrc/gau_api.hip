@@ -198,7 +198,7 @@ gau_status run_stages(const gau_config* c, int first, int last, const LayerPtrs&
 
 // Backward workspace: the forward's regions, then the backward's own.
 struct BwdLayout {
-    size_t H, dWq, Yb, WoT, dA, dSc, dScE;
+    size_t H, dWq, Yb, WoT, dA, dScE;
     size_t dQq, dKq, dQl, dKl, dP, dSst, Kl, rpart, hpart, dH, Wt, wpart, total;
     int split_o, split_w;  // K splits of the weight-gradient products
 };
@@ -234,7 +234,6 @@ void bwd_layout(const gau_config* c, BwdLayout* L) {
     L->Yb = take(M * e * eb);
     L->WoT = take(e * d * eb);
     L->dA = take(Z * C * C * 4);
-    L->dSc = take(Z * C * C * 4);
     L->dScE = take(Z * C * C * eb);
     L->dQq = take(M * s * 4);
     L->dKq = take(M * s * 4);
@@ -383,11 +382,9 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         gemm(q, C, C, Z);
     }
     {
-        gau::BwdElemParams p{(const float*)W(L.dA), W(F.A), nullptr, (float*)W(L.dSc), W(L.dScE), nullptr,
-                             (size_t)Z * CC, C, c->causal ? 1 : 0};
-        ok(gau::launch_scores_bwd(p, bf, st));
+        gau::BwdElemParams p{(const float*)W(L.dA), W(F.A), W(L.dScE), (size_t)Z * CC, C, c->causal ? 1 : 0};
+        ok(gau::launch_scores_bwd(p, (float*)W(L.rpart), drelpos, bf, st));
     }
-    ok(gau::launch_relpos_bwd((const float*)W(L.dSc), (float*)W(L.rpart), drelpos, Z, C, st));
     gemm(nt(kmaj(W(L.dScE), CC, C, G), heads_m(F.K_quad), W(L.dQq), Cs, s, C, true, G, c->quad_scale), C, s, Z);
     gemm(nt(mnmaj(W(L.dScE), CC, (int64_t)G * CC, C), heads_m(F.Q_quad), W(L.dKq), Cs, s, C, true, G,
             c->quad_scale),
@@ -421,6 +418,7 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         q.b2_bsq = dS_k.bsq;
         q.b2_rp = dS_k.rp;
         q.K2 = s;
+        q.k_from_row = c->causal ? 1 : 0;  // A[q][k] = 0 for queries q < k
         q.epi = gau::EPI_SILU;
         q.H = Wc(L.H, e);
         gemm(q, C, e, Z);

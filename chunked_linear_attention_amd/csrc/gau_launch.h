@@ -198,6 +198,8 @@ struct GemmNTParams {
     int skip_upper;  // skip output tiles wholly above the diagonal (never read)
     int a_t, b_t, a2_t, b2_t;
     int bt;          // tile size 64 or 128; 0: 128 when it divides M and N and gives >= 512 blocks
+    int k_from_row;  // the first segment's K range starts at the tile's first row m0 (A[z][r][k]
+                     // = 0 for k < r, e.g. the transposed causal scores)
 };
 
 // out[z][c][r] = in[z][r][c], element type, R and Cc multiples of 64.
@@ -213,11 +215,8 @@ struct TransposeParams {
 struct BwdElemParams {
     const float* f1;   // dA, fp32
     const void* b;     // A, element type
-    const void* c;     // unused
-    float* f0;         // dSc, fp32
     void* o0;          // dSc, element type
-    void* o1;          // unused
-    size_t n;
+    size_t n;          // entries: chunks * C * C
     int C, causal;
 };
 
@@ -253,9 +252,10 @@ struct TransposeBatch {
 };
 hipError_t launch_transpose_batch(const TransposeParams* jobs, const int* R, const int* Cc, const int* nb, int n,
                                   bool bf16_storage, hipStream_t st);
-hipError_t launch_scores_bwd(const BwdElemParams& q, bool bf16_storage, hipStream_t st);
-// drelpos[k] = sum over chunks and over entries on diagonal k - (C-1) of dsc
-hipError_t launch_relpos_bwd(const float* dsc, float* part, float* drelpos, int nchunks, int C, hipStream_t st);
+// dSc from dA (element type) and the bias gradient: per chunk and 32-row slab
+// the diagonal sums into part [chunks * C / 32, 2C-1], then their column sums
+// into drelpos [2C-1].
+hipError_t launch_scores_bwd(const BwdElemParams& q, float* part, float* drelpos, bool bf, hipStream_t st);
 // For each job j < jobs (at most 4), in one launch:
 // outs[j][i] = sum_{z < S} parts[j][z * stride + i], i < ns[j]
 // (ns[j] <= stride, both multiples of 4)
