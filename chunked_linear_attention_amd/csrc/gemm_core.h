@@ -730,13 +730,52 @@ struct GemmCore {
         }
     }
 
+    // The LDS writes of one pass of store_packed: staged element (col - pass
+    // prows, row) = val(row, col, acc) for the waves of wave column `pass`
+    // (all waves when npass == 1), rows BM * EB + 16 bytes apart.  Each lane
+    // holds four consecutive accumulator rows of one column, so every write is
+    // one packed 4-element store (8 bytes for bf16).
+    template <typename OutT, typename V>
+    __device__ static __forceinline__ void stage_packed(const f32x16_t (&acc)[MB][NB], char* lds, int pass, int prows,
+                                                        int npass, V&& val) {
+        constexpr int EB = Elem<OutT>::kBytes;
+        constexpr int PITCH = BM * EB + 16;
+        const int wave = threadIdx.x / kWave;
+        const int lane = threadIdx.x % kWave;
+        const int wm = wave / WGN, wn = wave % WGN;
+        const int c = lane & 31;
+        const int h = lane >> 5;
+        if (npass == 1 || wn == pass) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int row0 = wm * WTM + i * 32 + 8 * g4 + 4 * h;
+                        const int col = wn * WTN + j * 32 + c;
+                        float x[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) x[t] = val(row0 + t, col, acc[i][j][4 * g4 + t]);
+                        char* q = lds + (col - pass * prows) * PITCH + row0 * EB;
+                        if constexpr (EB == 2) {
+                            u32x2_t w;
+                            w.x = pack_bf16x2(x[0], x[1]);
+                            w.y = pack_bf16x2(x[2], x[3]);
+                            *(u32x2_t*)q = w;
+                        } else {
+                            *(f32x4_t*)q = f32x4_t{x[0], x[1], x[2], x[3]};
+                        }
+                    }
+        }
+    }
+
     // Store the block tile through LDS with the accumulator's column index as
-    // the staged row: staged element (col, row) = val(row, col, acc).  Each
-    // lane holds four consecutive accumulator rows of one column, so every LDS
-    // write is one packed 4-element store (8 bytes for bf16).  dst(srow, scol)
-    // gives the global address of staged elements (srow, scol..scol+V-1) or
-    // nullptr; the caller picks the operand order so that the staged rows are
-    // the rows of the global layout.  Passes as in store().
+    // the staged row: staged element (col, row) = val(row, col, acc) (written
+    // by stage_packed).  dst(srow, scol) gives the global address of staged
+    // elements (srow, scol..scol+V-1) or nullptr; the caller picks the operand
+    // order so that the staged rows are the rows of the global layout.
+    // Passes as in store().
     template <typename OutT, typename V, typename D, typename E = PlainEmit>
     __device__ static __forceinline__ void store_packed(const f32x16_t (&acc)[MB][NB], char* lds, int lds_bytes,
                                                         V&& val, D&& dst, E&& emit = E()) {
@@ -745,37 +784,10 @@ struct GemmCore {
         constexpr int PITCH = SCOLS * EB + 16;
         const int npass = SROWS * PITCH <= lds_bytes ? 1 : WGN;
         const int prows = SROWS / npass;
-        const int wave = threadIdx.x / kWave;
-        const int lane = threadIdx.x % kWave;
-        const int wm = wave / WGN, wn = wave % WGN;
-        const int c = lane & 31;
-        const int h = lane >> 5;
         constexpr int VPR = SCOLS * EB / 16;
         for (int pass = 0; pass < npass; ++pass) {
             __syncthreads();
-            if (npass == 1 || wn == pass) {
-#pragma unroll
-                for (int i = 0; i < MB; ++i)
-#pragma unroll
-                    for (int j = 0; j < NB; ++j)
-#pragma unroll
-                        for (int g4 = 0; g4 < 4; ++g4) {
-                            const int row0 = wm * WTM + i * 32 + 8 * g4 + 4 * h;
-                            const int col = wn * WTN + j * 32 + c;
-                            float x[4];
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) x[t] = val(row0 + t, col, acc[i][j][4 * g4 + t]);
-                            char* q = lds + (col - pass * prows) * PITCH + row0 * EB;
-                            if constexpr (EB == 2) {
-                                u32x2_t w;
-                                w.x = pack_bf16x2(x[0], x[1]);
-                                w.y = pack_bf16x2(x[2], x[3]);
-                                *(u32x2_t*)q = w;
-                            } else {
-                                *(f32x4_t*)q = f32x4_t{x[0], x[1], x[2], x[3]};
-                            }
-                        }
-            }
+            stage_packed<OutT>(acc, lds, pass, prows, npass, val);
             __syncthreads();
             for (int idx = threadIdx.x; idx < prows * VPR; idx += NT) {
                 const int srow = idx / VPR;

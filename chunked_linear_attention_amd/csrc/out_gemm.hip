@@ -15,22 +15,21 @@
 namespace gau {
 namespace {
 
-// Four consecutive elements (aligned to four) as floats, and back.
-template <typename T>
-__device__ __forceinline__ void get4(const char* p, float (&v)[4]) {
-    if constexpr (Elem<T>::kBytes == 2) {
-        const u32x2_t w = *(const u32x2_t*)p;
-        v[0] = __uint_as_float(w.x << 16);
-        v[1] = __uint_as_float(w.x & 0xFFFF0000u);
-        v[2] = __uint_as_float(w.y << 16);
-        v[3] = __uint_as_float(w.y & 0xFFFF0000u);
-    } else {
-        const f32x4_t w = *(const f32x4_t*)p;
-        v[0] = w.x;
-        v[1] = w.y;
-        v[2] = w.z;
-        v[3] = w.w;
-    }
+// Four consecutive elements (aligned to four) as loaded, as floats, and back.
+template <typename T> struct Raw4 { using type = f32x4_t; };
+template <> struct Raw4<bf16> { using type = u32x2_t; };
+
+__device__ __forceinline__ void unpack4(const u32x2_t& w, float (&v)[4]) {
+    v[0] = __uint_as_float(w.x << 16);
+    v[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(w.y << 16);
+    v[3] = __uint_as_float(w.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ void unpack4(const f32x4_t& w, float (&v)[4]) {
+    v[0] = w.x;
+    v[1] = w.y;
+    v[2] = w.z;
+    v[3] = w.w;
 }
 template <typename T>
 __device__ __forceinline__ void put4(char* p, const float (&v)[4]) {
@@ -100,38 +99,62 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
             return (m < M && n < d) ? (char*)(O + (size_t)m * orp + n) : nullptr;
         });
     } else if (p.gH != nullptr) {
-        // gate epilogue: the product staged in fp32; each 16-byte staged vector
-        // is four columns n..n+3 of row m.  The staging address handed to the
-        // emitter is O + 4 (m o_rp + n) (a position code, never dereferenced
-        // as fp32): O holds element-type values.
-        const char* code0 = (const char*)p.O;
+        // gate epilogue (the OutParams gate fields), in NPASS passes of PROWS
+        // tokens: the product staged in fp32 (staged rows = tokens); each
+        // thread takes NV 16-byte staged vectors (features n..n+3 of token m)
+        // whose pre-activations and Wq it loaded at the end of the previous
+        // pass (before the staging of this one).
+        constexpr int NPASS = WGN, PROWS = BN / NPASS;
+        constexpr int PITCH = BM * 4 + 16;       // fp32 staging row
+        constexpr int VPR = BM / 4;              // 16-byte vectors per staged row
+        constexpr int NV = PROWS * VPR / G::NT;  // vectors per thread per pass
+        static_assert(PROWS * VPR % G::NT == 0 && PROWS * PITCH <= LDS, "gate epilogue passes");
+        using Raw = typename Raw4<T>::type;
         const size_t grp = (size_t)p.g_rp;
-        G::template store_packed<float>(
-            acc, lds, LDS, ident,
-            [&](int tok, int feat) -> char* {
-                const int m = m0 + tok, n = n0 + feat;
-                return (m < M && n < d) ? (char*)code0 + 4 * ((size_t)m * orp + n) : nullptr;
-            },
-            [&](char* dp, const u32x4_t& v) {
-                const size_t idx = (size_t)(dp - code0) / 4, m = idx / orp, n = idx - m * orp;
-                const size_t j = m * grp + n;
-                float h[4], w[4], a[4], y[4], o[4];
-                get4<T>((const char*)p.gH + idx * EB, h);
-                get4<T>((const char*)p.gW + j * EB, w);
+        Raw hb[NV], wb[NV];
+        auto load = [&](int pass) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int idx = threadIdx.x + i * G::NT;
+                const int m = m0 + pass * PROWS + idx / VPR, n = n0 + (idx % VPR) * 4;
+                if (m < M && n < d) {
+                    hb[i] = *(const Raw*)((const char*)p.gH + ((size_t)m * orp + n) * EB);
+                    wb[i] = *(const Raw*)((const char*)p.gW + ((size_t)m * grp + n) * EB);
+                }
+            }
+        };
+        load(0);
+        for (int pass = 0; pass < NPASS; ++pass) {
+            __syncthreads();
+            G::template stage_packed<float>(acc, lds, pass, PROWS, NPASS, ident);
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int idx = threadIdx.x + i * G::NT;
+                const int srow = idx / VPR, n = n0 + (idx % VPR) * 4;
+                const size_t m = (size_t)(m0 + pass * PROWS + srow);
+                if ((int)m >= M || n >= d) continue;
+                const u32x4_t v = *(const u32x4_t*)(lds + srow * PITCH + (idx % VPR) * 16);
+                float hv[4], wv[4], a[4], y[4], o[4];
+                unpack4(hb[i], hv);
+                unpack4(wb[i], wv);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const float dy = __uint_as_float(v[k]);
+                    const float dy = __uint_as_float(v[k]), h = hv[k], w = wv[k];
                     // U = h sigma(h); SiLU'(h) = sigma(h) (1 + h (1 - sigma(h)))
-                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h[k]));
-                    const float u = h[k] * sg;
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h));
+                    const float u = h * sg;
                     a[k] = dy * u;
-                    y[k] = u * w[k];
-                    o[k] = dy * w[k] * (sg * (1.0f + h[k] * (1.0f - sg)));
+                    y[k] = u * w;
+                    o[k] = dy * w * (sg * (1.0f + h * (1.0f - sg)));
                 }
+                const size_t j = m * grp + n;
                 put4<T>((char*)p.gDWq + j * EB, a);
                 put4<T>((char*)p.gY + j * EB, y);
-                put4<T>((char*)p.O + idx * EB, o);
-            });
+                put4<T>((char*)p.O + (m * orp + n) * EB, o);
+            }
+            if (pass + 1 < NPASS) load(pass + 1);  // in flight across the next pass's staging
+        }
     } else if (p.residual == nullptr && !p.f32_out) {
         char* O = (char*)p.O;
         G::template store_packed<T>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
