@@ -405,15 +405,19 @@ def silu_grad(h):
 
 
 def flash_backward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal, dO,
-                   quad_scale=None, lin_scale=None):
-    """Gradients of <dO, O> for O = flash_forward(...) (no RoPE, both parts):
-    a dict with X, W_u, W_v, W_z, W_o (pages' orientation), gamma, beta,
-    relpos.  The steps of flash_forward taken backwards, each product's
-    derivative written out:
+                   quad_scale=None, lin_scale=None, use_rope=False):
+    """Gradients of <dO, O> for O = flash_forward(...) (both parts): a dict
+    with X, W_u, W_v, W_z, W_o (pages' orientation), gamma, beta, relpos.  The
+    steps of flash_forward taken backwards, each product's derivative written
+    out:
       O = Y W_o; Y = U * Wq (Wq = quad + lin); lin_g = Ql_g P_g;
       P = exclusive (or full) sum of S_h = ls Kl_h^T V_h;
       quad_g = A_g V_g with A_g = relu(Sc_g)^2 * mask, Sc_g = qs Qq Kq^T + Bias;
-      heads h_k = Z gamma_k + beta_k; U, V, Z = SiLU(X W).
+      heads h_k = Z gamma_k + beta_k (rotated by rope at their positions when
+      use_rope); U, V, Z = SiLU(X W).
+    A rotation's transpose is the rotation by the opposite angle, so the
+    gradients of the rotated heads go back through rope at the negated
+    positions.
     """
     X = _as64(X)
     B, T, d = X.shape
@@ -428,6 +432,9 @@ def flash_backward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal, dO,
     U, V, Z = silu(Hu), silu(Hv), silu(Hz)
     e, s = U.shape[-1], Z.shape[-1]
     Qq, Kq, Ql, Kl = heads(Z, gamma, beta)
+    pos = np.arange(T)
+    if use_rope:
+        Qq, Kq, Ql, Kl = (rope(h, pos) for h in (Qq, Kq, Ql, Kl))
     ch = lambda a: a.reshape(B, G, C, a.shape[-1])
     Vg, Qqg, Kqg, Qlg, Klg = map(ch, (V, Qq, Kq, Ql, Kl))
     mask = causal_mask(C) if causal else np.ones((C, C))
@@ -465,6 +472,8 @@ def flash_backward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal, dO,
     np.add.at(drel, (C - 1 + j - i).ravel(), dSc.sum(axis=(0, 1)).ravel())
     flat = lambda a: a.reshape(B, T, a.shape[-1])
     dh = [flat(x) for x in (dQq, dKq, dQl, dKl)]
+    if use_rope:
+        dh = [rope(x, -pos) for x in dh]
     dZ = sum(dh[k] * gamma[k] for k in range(4))
     dgamma = np.stack([(dh[k] * Z).sum(axis=(0, 1)) for k in range(4)])
     dbeta = np.stack([dh[k].sum(axis=(0, 1)) for k in range(4)])

@@ -463,19 +463,21 @@ def test_silu_grad_matches_central_differences():
     np.testing.assert_allclose(orc.silu_grad(x), fd, rtol=1e-8, atol=1e-10)
 
 
-@pytest.mark.parametrize("B,T,C", [(2, 8, 4), (1, 9, 3)])
+@pytest.mark.parametrize("B,T,C,rope", [(2, 8, 4, False), (1, 9, 3, False), (2, 8, 4, True)])
 @pytest.mark.parametrize("causal", [True, False])
-def test_backward_matches_central_differences(B, T, C, causal):
+def test_backward_matches_central_differences(B, T, C, rope, causal):
     """Every gradient of <dO, O> against central differences of the
-    brute-force forward (not the chunked one), entry by entry."""
+    brute-force forward (not the chunked one), entry by entry; with RoPE the
+    brute force rotates each head vector by its own position."""
     p = _tiny(B, T, d=4, e=5, s=4, C=C, seed=B * 17 + T + C)
     dO = np.random.default_rng(5).standard_normal((B, T, 4))
     g = orc.flash_backward(p["X"], p["W_u"], p["W_v"], p["W_z"], p["W_o"], p["gamma"], p["beta"],
-                           p["relpos"], C, causal, dO, quad_scale=0.6, lin_scale=0.8)
+                           p["relpos"], C, causal, dO, quad_scale=0.6, lin_scale=0.8, use_rope=rope)
     h = 1e-6
 
     def f(q):
-        return float(np.sum(dO * _run(orc.flash_forward_bruteforce, q, C, causal, quad_scale=0.6, lin_scale=0.8)))
+        return float(np.sum(dO * _run(orc.flash_forward_bruteforce, q, C, causal, quad_scale=0.6, lin_scale=0.8,
+                                      use_rope=rope)))
 
     names = {"X": "X", "W_u": "W_u", "W_v": "W_v", "W_z": "W_z", "W_o": "W_o", "gamma": "gamma",
              "beta": "beta", "relpos": "relpos"}
