@@ -335,11 +335,17 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(BwdScanParams q) {
 // dZ = sum_k gamma_k dh_k over the four heads, stored as its pre-activation
 // gradient dZ * SiLU'(H_z); per block of kHeadsBwdTokens tokens the partial sums of
 // dh_k * Z and dh_k (for gamma and beta).  Thread per feature i (s threads),
-// tokens in order.
+// tokens in order.  With rope the dh_k given are those of the rotated heads:
+// each goes back through the transposed rotation of its pair (i, i +- s/2)
+// at the token's position (dlo = dlo' c + dhi' sin, dhi = dhi' c - dlo' sin).
 template <typename T>
 __global__ __launch_bounds__(256) void heads_bwd_kernel(BwdHeadsParams q) {
     const int i = threadIdx.x;
     if (i >= q.s) return;
+    const int half = q.s / 2;
+    const bool lo = i < half;
+    const int partner = lo ? i + half : i - half;
+    const double theta = q.rope ? rope_theta(lo ? i : partner, half) : 0.0;
     const int m0 = blockIdx.x * kHeadsBwdTokens;
     float pg[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
     for (int m = m0; m < m0 + kHeadsBwdTokens && m < q.M; ++m) {
@@ -347,10 +353,23 @@ __global__ __launch_bounds__(256) void heads_bwd_kernel(BwdHeadsParams q) {
         const size_t hz = (size_t)m * q.hpitch + i;
         const float h = ld<T>(q.Hz, hz);
         const float z = silu(h);
+        float dhk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dhk[k] = q.dh[k][o];
+        if (q.rope) {
+            float c, sn;
+            rope_cos_sin((double)(m % q.T), theta, c, sn);
+            const size_t op = (size_t)m * q.s + partner;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float pk = q.dh[k][op];
+                dhk[k] = lo ? dhk[k] * c + pk * sn : dhk[k] * c - pk * sn;
+            }
+        }
         float dz = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float dh = q.dh[k][o];
+            const float dh = dhk[k];
             dz += q.scale[k * q.s + i] * dh;
             pg[k] += dh * z;
             pb[k] += dh;

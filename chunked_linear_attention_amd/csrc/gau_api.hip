@@ -427,7 +427,8 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     {
         gau::BwdHeadsParams p{{(const float*)W(L.dQq), (const float*)W(L.dKq), (const float*)W(L.dQl),
                                (const float*)W(L.dKl)},
-                              Wc(L.H, 2 * e), W3, a.scale, Wc(L.dH, 2 * e), (float*)W(L.hpart), M, s};
+                              Wc(L.H, 2 * e), W3, a.scale, Wc(L.dH, 2 * e), (float*)W(L.hpart), M, s,
+                              c->rope ? 1 : 0, T};
         ok(gau::launch_heads_bwd(p, dscale, doffset, bf, st));
     }
     // X W: dX = dH W^T
@@ -564,12 +565,13 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X, cons
     return GAU_OK;
 }
 
-// What gau_backward takes beyond check_config: the plain layer, and at most
-// 2^38 pre-activation entries (one-dimensional grids of 256-thread blocks).
+// What gau_backward takes beyond check_config: both parts of the layer (with
+// or without RoPE), and at most 2^38 pre-activation entries (one-dimensional
+// grids of 256-thread blocks).
 gau_status check_backward(const gau_config* c) {
     gau_status s = check_config(c);
     if (s != GAU_OK) return s;
-    if (c->rope || c->ablation != GAU_FULL) return GAU_ERR_SHAPE;
+    if (c->ablation != GAU_FULL) return GAU_ERR_SHAPE;
     if (c->B * c->T * (2 * c->e + c->s) > ((int64_t)1 << 38)) return GAU_ERR_SHAPE;
     return GAU_OK;
 }

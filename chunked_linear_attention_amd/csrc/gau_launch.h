@@ -237,6 +237,7 @@ struct BwdHeadsParams {
     void* dHz;           // its gradient, same layout as Hz
     float* part;         // [ceil(M / kHeadsBwdTokens), 8, s] per-block sums
     int M, s;
+    int rope, T;         // rope: the heads were rotated by position m mod T
 };
 
 hipError_t launch_gemm_nt(const GemmNTParams& q, int M, int N, int nb, bool bf16_storage, hipStream_t st);

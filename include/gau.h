@@ -285,11 +285,16 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X,
  *   dQ_lin = dWq P^T,  dP = Q_lin^T dWq,
  *   dS_h = sum_{g>h} dP_g (causal) or sum_g dP_g (non-causal)
  *   dV = A^T dWq + lin_scale K_lin dS,  dK_lin = lin_scale V dS^T
+ *   with rope = 1 the dh_h of the rotated heads first go back through the
+ *   transposed rotation (the rotation by the opposite angle) at each token's
+ *   position;
  *   dZ = sum_h gamma_h dh_h, dgamma_h = sum Z * dh_h, dbeta_h = sum dh_h
  *   d(pre-activations) = [dU | dV | dZ] * SiLU'(X W);  dX, dW_* from X W.
  *
- * cfg: as gau_forward with rope = 0 and ablation = GAU_FULL (the backward of
- *   the rotated or partial layer is not provided: GAU_ERR_SHAPE).
+ * cfg: as gau_forward with ablation = GAU_FULL, rope 0 or 1 (the backward of
+ *   the partial layers is not provided: GAU_ERR_SHAPE).  With rope, drelpos is
+ *   the gradient with respect to the relpos vector passed in (for a bias built
+ *   by gau_rope_relpos, the caller chains it to a and b).
  * X .. relpos: as gau_forward.   dO [B, T, d] cfg->dtype.
  * Outputs (fp32, written, not accumulated):
  *   dX [B, T, d];  dW_u, dW_v [e, d], dW_z [s, d], dW_o [d, e] (the layout in

@@ -15,10 +15,10 @@ from _gpu import assert_close, make, tol_for, torch_dtype
 pytestmark = pytest.mark.gpu
 
 
-def _backward(inp, dO, B, T, d, e, s, C, causal, dtype, fill=0):
+def _backward(inp, dO, B, T, d, e, s, C, causal, dtype, fill=0, rope=False):
     tdt = torch_dtype(dtype)
     dev = g.device_layer(inp, tdt)
-    cfg = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32)
+    cfg = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32, rope=rope)
     ws = torch.full((g.backward_workspace_bytes(cfg),), fill, dtype=torch.uint8, device="cuda")
     dOd = g.device_tensor(dO, tdt)
     like = {"X": (B, T, d), "W_u": (e, d), "W_v": (e, d), "W_z": (s, d), "W_o": (d, e), "scale": (4, s),
@@ -30,9 +30,9 @@ def _backward(inp, dO, B, T, d, e, s, C, causal, dtype, fill=0):
     return {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
 
 
-def _oracle(inp, dO, C, causal):
+def _oracle(inp, dO, C, causal, rope=False):
     r = orc.flash_backward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"], inp["beta"],
-                           inp["relpos"], C, causal, dO)
+                           inp["relpos"], C, causal, dO, use_rope=rope)
     # the library returns weight gradients output-major, like the weights it takes
     return {"X": r["X"], "W_u": r["W_u"].T, "W_v": r["W_v"].T, "W_z": r["W_z"].T, "W_o": r["W_o"].T,
             "scale": r["gamma"], "offset": r["beta"], "relpos": r["relpos"]}
@@ -69,6 +69,36 @@ def test_backward_matches_oracle(case):
     inp = make(B, T, d, e, s, C, dtype, seed=B * 131 + T + C, heads=heads)
     dO = inputs.make_output_grad(B, T, d, seed=T + d, dtype=dtype)
     _compare(_backward(inp, dO, B, T, d, e, s, C, causal, dtype), _oracle(inp, dO, C, causal), dtype)
+
+
+ROPE_CASES = [
+    # B, T, d, e, s, C, dtype, causal, heads: the four heads rotated by position
+    (1, 256, 128, 256, 128, 64, "f32", True, "wide"),
+    (2, 512, 256, 512, 128, 128, "bf16", False, "wide"),
+    (1, 512, 256, 512, 256, 256, "f32", True, "wide"),     # s = 256
+    (1, 960, 128, 1536, 128, 64, "bf16", True, "wide"),    # e >= 1024: heads formed inside the U tiles
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}_rope".format(
+    *c[:7], "causal" if c[7] else "full"))
+def test_backward_with_rope_matches_oracle(case):
+    B, T, d, e, s, C, dtype, causal, heads = case
+    print(f"backward rope case {case}", flush=True)
+    inp = make(B, T, d, e, s, C, dtype, seed=B * 97 + T + C, heads=heads)
+    dO = inputs.make_output_grad(B, T, d, seed=T + 3 * d, dtype=dtype)
+    _compare(_backward(inp, dO, B, T, d, e, s, C, causal, dtype, rope=True), _oracle(inp, dO, C, causal, rope=True),
+             dtype)
+
+
+def test_backward_with_rope_at_benchmark_shape():
+    """B=2, T=8192 (angles up to 8191 rad), d=768, e=1536, bf16, causal, RoPE."""
+    B, T, d, e, s, C = 2, 8192, 768, 1536, 128, 256
+    print("backward rope benchmark shape", flush=True)
+    inp = make(B, T, d, e, s, C, "bf16", seed=2025, heads="wide")
+    dO = inputs.make_output_grad(B, T, d, seed=2025, dtype="bf16")
+    _compare(_backward(inp, dO, B, T, d, e, s, C, True, "bf16", rope=True), _oracle(inp, dO, C, True, rope=True),
+             "bf16")
 
 
 def test_backward_at_benchmark_shape():
