@@ -405,11 +405,12 @@ def silu_grad(h):
 
 
 def flash_backward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal, dO,
-                   quad_scale=None, lin_scale=None, use_rope=False):
-    """Gradients of <dO, O> for O = flash_forward(...) (both parts): a dict
-    with X, W_u, W_v, W_z, W_o (pages' orientation), gamma, beta, relpos.  The
-    steps of flash_forward taken backwards, each product's derivative written
-    out:
+                   quad_scale=None, lin_scale=None, use_rope=False, parts="both"):
+    """Gradients of <dO, O> for O = flash_forward(...): a dict with X, W_u,
+    W_v, W_z, W_o (pages' orientation), gamma, beta, relpos.  parts as in
+    flash_forward: "local" drops the linear term (and everything that only
+    feeds it gets a zero gradient), "global" the quadratic one.  The steps of
+    flash_forward taken backwards, each product's derivative written out:
       O = Y W_o; Y = U * Wq (Wq = quad + lin); lin_g = Ql_g P_g;
       P = exclusive (or full) sum of S_h = ls Kl_h^T V_h;
       quad_g = A_g V_g with A_g = relu(Sc_g)^2 * mask, Sc_g = qs Qq Kq^T + Bias;
@@ -446,17 +447,21 @@ def flash_backward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal, dO,
         P = np.concatenate([np.zeros_like(S[:, :1]), incl[:, :-1]], axis=1)
     else:
         P = np.broadcast_to(S.sum(axis=1, keepdims=True), S.shape)
-    Wq = (A @ Vg + Qlg @ P).reshape(B, T, e)
+    if parts not in ("both", "local", "global"):
+        raise ValueError("parts must be 'both', 'local' or 'global'")
+    keep_quad, keep_lin = parts != "global", parts != "local"
+    Wq = ((A @ Vg) * keep_quad + (Qlg @ P) * keep_lin).reshape(B, T, e)
     Y = U * Wq
     # backwards
     dY = dO @ W_o.T
     dW_o = Y.reshape(-1, e).T @ dO.reshape(-1, d)
     dU = dY * Wq
     dWq = ch(dY * U)
-    dA = dWq @ Vg.swapaxes(-1, -2)
-    dV = A.swapaxes(-1, -2) @ dWq
-    dQl = dWq @ P.swapaxes(-1, -2)
-    dP = Qlg.swapaxes(-1, -2) @ dWq
+    dWq_quad, dWq_lin = dWq * keep_quad, dWq * keep_lin   # the parts that reach O
+    dA = dWq_quad @ Vg.swapaxes(-1, -2)
+    dV = A.swapaxes(-1, -2) @ dWq_quad
+    dQl = dWq_lin @ P.swapaxes(-1, -2)
+    dP = Qlg.swapaxes(-1, -2) @ dWq_lin
     if causal:   # S_h feeds P_g for every g > h
         rev = np.cumsum(dP[:, ::-1], axis=1)[:, ::-1]
         dS = np.concatenate([rev[:, 1:], np.zeros_like(dP[:, :1])], axis=1)

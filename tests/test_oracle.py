@@ -492,6 +492,38 @@ def test_backward_matches_central_differences(B, T, C, rope, causal):
         np.testing.assert_allclose(g[k], fd, rtol=1e-5, atol=1e-6, err_msg=k)
 
 
+@pytest.mark.parametrize("parts", ["local", "global"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_of_one_part_matches_central_differences(parts, causal):
+    """LocalOnly / GlobalOnly: every gradient against central differences of
+    the chunked forward with that part alone (pinned above by the weight
+    ablations it equals)."""
+    B, T, C = 2, 8, 4
+    p = _tiny(B, T, d=4, e=5, s=4, C=C, seed=41)
+    dO = np.random.default_rng(6).standard_normal((B, T, 4))
+    g = orc.flash_backward(p["X"], p["W_u"], p["W_v"], p["W_z"], p["W_o"], p["gamma"], p["beta"],
+                           p["relpos"], C, causal, dO, quad_scale=0.6, lin_scale=0.8, parts=parts)
+    h = 1e-6
+
+    def f(q):
+        return float(np.sum(dO * _run(orc.flash_forward, q, C, causal, quad_scale=0.6, lin_scale=0.8, parts=parts)))
+
+    for k in ("X", "W_u", "W_v", "W_z", "W_o", "gamma", "beta", "relpos"):
+        fd = np.zeros_like(p[k])
+        for idx in np.ndindex(p[k].shape):
+            up = {a: (b.copy() if isinstance(b, np.ndarray) else b) for a, b in p.items()}
+            dn = {a: (b.copy() if isinstance(b, np.ndarray) else b) for a, b in p.items()}
+            up[k][idx] += h
+            dn[k][idx] -= h
+            fd[idx] = (f(up) - f(dn)) / (2 * h)
+        np.testing.assert_allclose(g[k], fd, rtol=1e-5, atol=1e-6, err_msg=k)
+    # what only feeds the dropped part gets nothing
+    if parts == "local":
+        assert np.all(g["gamma"][2:] == 0) and np.all(g["beta"][2:] == 0)
+    else:
+        assert np.all(g["gamma"][:2] == 0) and np.all(g["relpos"] == 0)
+
+
 # ---------------------------------------------------------------- segment masks
 
 SEGMENTS = [
