@@ -415,6 +415,7 @@ hipError_t gemm_go(const GemmNTParams& q, unsigned blocks, hipStream_t st) {
         switch (key) {
             case 0x0: return gemm_go1<T, BT, EPI_SILU, false, false, false, false>(q, blocks, st);
             case 0xC: return gemm_go1<T, BT, EPI_SILU, true, true, false, false>(q, blocks, st);
+            case 0xF: return gemm_go1<T, BT, EPI_SILU, true, true, true, true>(q, blocks, st);
             default: return hipErrorInvalidValue;
         }
     }

@@ -331,20 +331,22 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         batch.n = 0;
     };
 
+    // which terms reach Y (the LocalOnly / GlobalOnly layers keep one)
+    const bool local = c->ablation != GAU_GLOBAL_ONLY, global = c->ablation != GAU_LOCAL_ONLY;
     // forward intermediates: heads, states, prefix, weights (tiles above the
     // causal diagonal, which the forward leaves unwritten, cleared first)
-    if (c->causal && gau::launch_fill_zero((float*)W(F.A), (size_t)Z * CC * eb / 4, st) != hipSuccess)
+    if (local && c->causal && gau::launch_fill_zero((float*)W(F.A), (size_t)Z * CC * eb / 4, st) != hipSuccess)
         return GAU_ERR_HIP;
     // (the projection also stores the pre-activations H = X [W_u | W_v | W_z],
     // which the SiLU derivatives below read)
     gau_status sres = run_stages(c, GAU_STAGE_PROJ, GAU_STAGE_SCAN, a, nullptr, nullptr, ws, st, false, nullptr,
                                  W(L.H));
     if (sres != GAU_OK) return sres;
-    // Wq = A V + Q_lin P (into the forward's Y region): the attention stage
-    // without the gate
+    // Wq = A V + Q_lin P, or the kept term (into the forward's Y region): the
+    // attention stage without the gate
     {
         gau::AttnParams p{W(F.A), W(F.Q_lin), W(F.Vt), W(F.P), nullptr, W(F.Y), Bn, T, e, s, C,
-                          c->causal ? 1 : 0, 1, 1};
+                          c->causal ? 1 : 0, local ? 1 : 0, global ? 1 : 0};
         ok(gau::launch_chunk_attn(p, bf, st));
     }
     // the transposes left, in one launch: W_o^T (dY), the weights (dX) and
@@ -373,52 +375,73 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     const NtOp dS_m = mnmaj(W(L.dSst), es, (int64_t)G * es, s);        // K = f, MN = j
     auto heads_m = [&](size_t off) { return mnmaj(W(off), Cs, (int64_t)G * Cs, s); };  // K = tokens, MN = j
 
+    // a term the layer drops: its head gradients (and the bias's) are zero
+    auto zero = [&](float* x, size_t n) { ok(gau::launch_fill_zero(x, n, st)); };
+    if (!local) {
+        zero((float*)W(L.dQq), (size_t)M * s);
+        zero((float*)W(L.dKq), (size_t)M * s);
+        zero(drelpos, (size_t)(2 * C - 1));
+    }
+    if (!global) {
+        zero((float*)W(L.dQl), (size_t)M * s);
+        zero((float*)W(L.dKl), (size_t)M * s);
+    }
+
     // local part: dA = dWq V^T, dSc = dA * 2 relu(Sc) * mask,
     // dQ_quad = qs dSc K_quad, dK_quad = qs dSc^T Q_quad, dBias
-    {
-        gau::GemmNTParams q = nt(dWq_k, V_m, W(L.dA), CC, C, e, true, G);
-        q.skip_upper = c->causal ? 1 : 0;
-        q.bt = C % 128 == 0 ? 128 : 64;  // K = e is long: the larger tile's operand reuse pays
-        gemm(q, C, C, Z);
+    if (local) {
+        {
+            gau::GemmNTParams q = nt(dWq_k, V_m, W(L.dA), CC, C, e, true, G);
+            q.skip_upper = c->causal ? 1 : 0;
+            q.bt = C % 128 == 0 ? 128 : 64;  // K = e is long: the larger tile's operand reuse pays
+            gemm(q, C, C, Z);
+        }
+        {
+            gau::BwdElemParams p{(const float*)W(L.dA), W(F.A), W(L.dScE), (size_t)Z * CC, C, c->causal ? 1 : 0};
+            ok(gau::launch_scores_bwd(p, (float*)W(L.rpart), drelpos, bf, st));
+        }
+        gemm(nt(kmaj(W(L.dScE), CC, C, G), heads_m(F.K_quad), W(L.dQq), Cs, s, C, true, G, c->quad_scale), C, s, Z);
+        gemm(nt(mnmaj(W(L.dScE), CC, (int64_t)G * CC, C), heads_m(F.Q_quad), W(L.dKq), Cs, s, C, true, G,
+                c->quad_scale),
+             C, s, Z);
     }
-    {
-        gau::BwdElemParams p{(const float*)W(L.dA), W(F.A), W(L.dScE), (size_t)Z * CC, C, c->causal ? 1 : 0};
-        ok(gau::launch_scores_bwd(p, (float*)W(L.rpart), drelpos, bf, st));
-    }
-    gemm(nt(kmaj(W(L.dScE), CC, C, G), heads_m(F.K_quad), W(L.dQq), Cs, s, C, true, G, c->quad_scale), C, s, Z);
-    gemm(nt(mnmaj(W(L.dScE), CC, (int64_t)G * CC, C), heads_m(F.Q_quad), W(L.dKq), Cs, s, C, true, G,
-            c->quad_scale),
-         C, s, Z);
 
     // global part: dQ_lin = dWq P^T, dP = Q_lin^T dWq (per chunk, stored [e, s]),
     // dS = ls * (reverse exclusive sum of dP, or the total when non-causal),
     // dK_lin = V dS^T
-    {
-        const NtOp P_m = c->causal ? mnmaj(W(F.P), es, (int64_t)G * es, s) : mnmaj(W(F.P), 0, es, s);
-        gemm(nt(dWq_k, P_m, W(L.dQl), Cs, s, e, true, G), C, s, Z);
+    if (global) {
+        {
+            const NtOp P_m = c->causal ? mnmaj(W(F.P), es, (int64_t)G * es, s) : mnmaj(W(F.P), 0, es, s);
+            gemm(nt(dWq_k, P_m, W(L.dQl), Cs, s, e, true, G), C, s, Z);
+        }
+        gemm(nt(dWq_m, heads_m(F.Q_lin), W(L.dP), es, s, C, true, G), e, s, Z);
+        {
+            gau::BwdScanParams p{(const float*)W(L.dP), W(L.dSst), Bn, G, (int)es, c->causal ? 1 : 0,
+                                 c->lin_scale};
+            ok(gau::launch_scan_bwd(p, bf, st));
+        }
+        gemm(nt(V_m, dS_m, W(L.dKl), Cs, s, e, true, G), C, s, Z);
     }
-    gemm(nt(dWq_m, heads_m(F.Q_lin), W(L.dP), es, s, C, true, G), e, s, Z);
-    {
-        gau::BwdScanParams p{(const float*)W(L.dP), W(L.dSst), Bn, G, (int)es, c->causal ? 1 : 0, c->lin_scale};
-        ok(gau::launch_scan_bwd(p, bf, st));
-    }
-    gemm(nt(V_m, dS_m, W(L.dKl), Cs, s, e, true, G), C, s, Z);
 
-    // dV = A^T dWq + K_lin dS (two K segments), stored as dH_v = dV * SiLU'(H_v)
+    // dV = A^T dWq + K_lin dS (two K segments; one when the layer keeps one
+    // term), stored as dH_v = dV * SiLU'(H_v)
     {
-        gau::GemmNTParams q = nt(mnmaj(W(F.A), CC, (int64_t)G * CC, C), dWq_m, Wc(L.dH, e), (int64_t)C * W3, W3, C,
-                                 false, G);
         const NtOp Kl_k = kmaj(W(L.Kl), Cs, s, G), dS_k = kmaj(W(L.dSst), es, s, G);
-        q.A2 = Kl_k.p;
-        q.a2_bs = Kl_k.bs;
-        q.a2_bsq = Kl_k.bsq;
-        q.a2_rp = Kl_k.rp;
-        q.B2 = dS_k.p;
-        q.b2_bs = dS_k.bs;
-        q.b2_bsq = dS_k.bsq;
-        q.b2_rp = dS_k.rp;
-        q.K2 = s;
-        q.k_from_row = c->causal ? 1 : 0;  // A[q][k] = 0 for queries q < k
+        gau::GemmNTParams q = local ? nt(mnmaj(W(F.A), CC, (int64_t)G * CC, C), dWq_m, Wc(L.dH, e), (int64_t)C * W3,
+                                         W3, C, false, G)
+                                    : nt(Kl_k, dS_k, Wc(L.dH, e), (int64_t)C * W3, W3, s, false, G);
+        if (local && global) {
+            q.A2 = Kl_k.p;
+            q.a2_bs = Kl_k.bs;
+            q.a2_bsq = Kl_k.bsq;
+            q.a2_rp = Kl_k.rp;
+            q.B2 = dS_k.p;
+            q.b2_bs = dS_k.bs;
+            q.b2_bsq = dS_k.bsq;
+            q.b2_rp = dS_k.rp;
+            q.K2 = s;
+        }
+        q.k_from_row = local && c->causal ? 1 : 0;  // A[q][k] = 0 for queries q < k
         q.epi = gau::EPI_SILU;
         q.H = Wc(L.H, e);
         gemm(q, C, e, Z);
@@ -565,13 +588,11 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X, cons
     return GAU_OK;
 }
 
-// What gau_backward takes beyond check_config: both parts of the layer (with
-// or without RoPE), and at most 2^38 pre-activation entries (one-dimensional
-// grids of 256-thread blocks).
+// What gau_backward takes beyond check_config: at most 2^38 pre-activation
+// entries (one-dimensional grids of 256-thread blocks).
 gau_status check_backward(const gau_config* c) {
     gau_status s = check_config(c);
     if (s != GAU_OK) return s;
-    if (c->ablation != GAU_FULL) return GAU_ERR_SHAPE;
     if (c->B * c->T * (2 * c->e + c->s) > ((int64_t)1 << 38)) return GAU_ERR_SHAPE;
     return GAU_OK;
 }

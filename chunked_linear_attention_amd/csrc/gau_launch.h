@@ -174,8 +174,9 @@ enum { EPI_STORE = 0,  // C[i] = v (fp32 when c_f32, else the element type)
 // operand's entry starts at (z / zg) * *_bsq + (z % zg) * *_bs elements, C's
 // at z * c_bs, C's rows c_rp elements apart.  K and K2 are multiples of 64,
 // every dimension a multiple of 64.  The second segment is used when K2 > 0.
-// Layouts implemented: (a_t, b_t) = (0, 0), (0, 1), (1, 1); with a second
-// segment and the SiLU epilogue (1, 1) then (a2_t, b2_t) = (0, 0).
+// Layouts implemented: (a_t, b_t) = (0, 0), (0, 1), (1, 1) (the SiLU epilogue:
+// (0, 0), (1, 1)); with a second segment and the SiLU epilogue (1, 1) then
+// (a2_t, b2_t) = (0, 0).
 struct GemmNTParams {
     const void* A;
     const void* B;

@@ -291,10 +291,11 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X,
  *   dZ = sum_h gamma_h dh_h, dgamma_h = sum Z * dh_h, dbeta_h = sum dh_h
  *   d(pre-activations) = [dU | dV | dZ] * SiLU'(X W);  dX, dW_* from X W.
  *
- * cfg: as gau_forward with ablation = GAU_FULL, rope 0 or 1 (the backward of
- *   the partial layers is not provided: GAU_ERR_SHAPE).  With rope, drelpos is
- *   the gradient with respect to the relpos vector passed in (for a bias built
- *   by gau_rope_relpos, the caller chains it to a and b).
+ * cfg: as gau_forward (rope 0 or 1, any ablation: with GAU_LOCAL_ONLY the
+ *   gradients of the Q_lin and K_lin heads' scale and offset are zero, with
+ *   GAU_GLOBAL_ONLY those of Q_quad, K_quad and drelpos).  With rope, drelpos
+ *   is the gradient with respect to the relpos vector passed in (for a bias
+ *   built by gau_rope_relpos, the caller chains it to a and b).
  * X .. relpos: as gau_forward.   dO [B, T, d] cfg->dtype.
  * Outputs (fp32, written, not accumulated):
  *   dX [B, T, d];  dW_u, dW_v [e, d], dW_z [s, d], dW_o [d, e] (the layout in

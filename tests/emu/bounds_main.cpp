@@ -155,10 +155,14 @@ static void run(const Cfg& c, const std::string& only) {
         }
         free(ws);
     });
-    // the backward pass through the C ABI: exact-size inputs, outputs and workspace
-    if (M <= 4096) t("gau_backward", [&] {
+    // the backward pass through the C ABI: exact-size inputs, outputs and
+    // workspace, for the full layer, with RoPE and for each partial layer
+    for (int variant = 0; variant < 4; ++variant)
+    if (M <= 4096) t(variant == 0 ? "gau_backward" : variant == 1 ? "gau_backward_rope"
+                     : variant == 2 ? "gau_backward_local" : "gau_backward_global", [&] {
         gau_config cfg{c.B, c.T, c.d, c.e, c.s, c.C, c.causal ? 1 : 0, c.bf ? GAU_BF16 : GAU_F32, 1.0f / c.C,
-                       1.0f / c.C};
+                       1.0f / c.C, variant == 1 ? 1 : 0,
+                       variant == 2 ? GAU_LOCAL_ONLY : variant == 3 ? GAU_GLOBAL_ONLY : GAU_FULL};
         const size_t wsb = gau_backward_workspace_bytes(&cfg);
         void* ws = buf(wsb);
         void* gO = buf(M * c.d * eb);

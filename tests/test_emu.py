@@ -257,16 +257,20 @@ BWD_CASES = [
     (1, 256, 128, 256, 128, 64, "f32", True, "wide"),  # gamma ~ N(1, 0.5^2), beta ~ N(0, 0.3^2)
     (1, 256, 128, 256, 128, 64, "f32", True, "wide", True),    # RoPE
     (2, 256, 128, 256, 256, 128, "bf16", False, "wide", True),  # RoPE, s = 256
+    (1, 256, 128, 256, 128, 64, "f32", True, "wide", False, "local"),   # LocalOnly
+    (1, 256, 128, 256, 128, 64, "bf16", False, "wide", False, "global"),  # GlobalOnly
 ]
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}{}{}".format(
-    *c[:7], "causal" if c[7] else "full", "_wide" if len(c) > 8 else "", "_rope" if len(c) > 9 else ""))
+    *c[:7], "causal" if c[7] else "full", "_wide" if len(c) > 8 else "", "_rope" if len(c) > 9 and c[9] else "")
+    + ("_" + c[10] if len(c) > 10 else ""))
 def test_emulated_backward_matches_oracle(emu, case):
     """gau_backward on the emulation: every gradient against the oracle's."""
     B, T, d, e, s, C, dtype, causal = case[:8]
     heads = case[8] if len(case) > 8 else "workload"
     rope = len(case) > 9 and case[9]
+    parts = case[10] if len(case) > 10 else "both"
     bf = dtype == "bf16"
     emu.emu_set_mode(1, 1)
     P = ctypes.c_void_p
@@ -276,7 +280,8 @@ def test_emulated_backward_matches_oracle(emu, case):
     emu.gau_backward.restype = ctypes.c_int
     inp = inputs.make_layer_inputs(B=B, T=T, d=d, e=e, s=s, C=C, seed=B * 17 + T + C, dtype=dtype, heads=heads)
     dO = inputs.make_output_grad(B, T, d, seed=T + C, dtype=dtype)
-    cfg = GauConfig(B, T, d, e, s, C, 1 if causal else 0, 1 if bf else 0, 1.0 / C, 1.0 / C, 1 if rope else 0, 0)
+    cfg = GauConfig(B, T, d, e, s, C, 1 if causal else 0, 1 if bf else 0, 1.0 / C, 1.0 / C, 1 if rope else 0,
+                    {"both": 0, "local": 1, "global": 2}[parts])
     X, dOh = _host(inp["X"], bf), _host(dO, bf)
     W = {k: _host(np.ascontiguousarray(inp[k].T), bf) for k in ("W_u", "W_v", "W_z", "W_o")}
     sc, of, rp = (np.ascontiguousarray(inp[k], np.float32) for k in ("gamma", "beta", "relpos"))
@@ -293,11 +298,14 @@ def test_emulated_backward_matches_oracle(emu, case):
                           ptr(sc), ptr(of), ptr(rp), ptr(dOh), *[ptr(out[k]) for k in out], ptr(ws), wsb, None)
     assert st == 0
     ref = orc.flash_backward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"], inp["beta"],
-                             inp["relpos"], C, causal, dO, use_rope=rope)
+                             inp["relpos"], C, causal, dO, use_rope=rope, parts=parts)
     tol = 2e-2 if bf else 1e-4
     for k, got in out.items():
         want = ref[k] if k != "W_o" else ref[k].T     # weights come back output-major
         want = want.T if k in ("W_u", "W_v", "W_z") else want
         assert np.all(np.isfinite(got)), k
+        if not np.any(want):   # carried by the dropped term alone
+            assert not np.any(got), k
+            continue
         err = np.max(np.abs(got - want)) / np.max(np.abs(want))
         assert err <= tol, f"d{k}: {err:.3e} > {tol}"

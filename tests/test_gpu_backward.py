@@ -15,10 +15,11 @@ from _gpu import assert_close, make, tol_for, torch_dtype
 pytestmark = pytest.mark.gpu
 
 
-def _backward(inp, dO, B, T, d, e, s, C, causal, dtype, fill=0, rope=False):
+def _backward(inp, dO, B, T, d, e, s, C, causal, dtype, fill=0, rope=False, parts="both"):
     tdt = torch_dtype(dtype)
     dev = g.device_layer(inp, tdt)
-    cfg = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32, rope=rope)
+    cfg = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32, rope=rope,
+                        parts=parts)
     ws = torch.full((g.backward_workspace_bytes(cfg),), fill, dtype=torch.uint8, device="cuda")
     dOd = g.device_tensor(dO, tdt)
     like = {"X": (B, T, d), "W_u": (e, d), "W_v": (e, d), "W_z": (s, d), "W_o": (d, e), "scale": (4, s),
@@ -30,9 +31,9 @@ def _backward(inp, dO, B, T, d, e, s, C, causal, dtype, fill=0, rope=False):
     return {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
 
 
-def _oracle(inp, dO, C, causal, rope=False):
+def _oracle(inp, dO, C, causal, rope=False, parts="both"):
     r = orc.flash_backward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"], inp["beta"],
-                           inp["relpos"], C, causal, dO, use_rope=rope)
+                           inp["relpos"], C, causal, dO, use_rope=rope, parts=parts)
     # the library returns weight gradients output-major, like the weights it takes
     return {"X": r["X"], "W_u": r["W_u"].T, "W_v": r["W_v"].T, "W_z": r["W_z"].T, "W_o": r["W_o"].T,
             "scale": r["gamma"], "offset": r["beta"], "relpos": r["relpos"]}
@@ -41,6 +42,9 @@ def _oracle(inp, dO, C, causal, rope=False):
 def _compare(got, ref, dtype):
     for k in g.GRAD_NAMES:
         assert np.all(np.isfinite(got[k])), f"d{k} has non-finite entries"
+        if not np.any(ref[k]):   # a gradient the layer's dropped term alone would carry
+            assert not np.any(got[k]), f"d{k} should be zero"
+            continue
         assert_close(got[k], ref[k], tol_for(dtype), f"d{k}")
 
 
@@ -99,6 +103,28 @@ def test_backward_with_rope_at_benchmark_shape():
     dO = inputs.make_output_grad(B, T, d, seed=2025, dtype="bf16")
     _compare(_backward(inp, dO, B, T, d, e, s, C, True, "bf16", rope=True), _oracle(inp, dO, C, True, rope=True),
              "bf16")
+
+
+PARTS_CASES = [
+    # B, T, d, e, s, C, dtype, causal
+    (1, 256, 128, 256, 128, 64, "f32", True),
+    (2, 512, 256, 512, 128, 128, "bf16", False),
+    (1, 960, 128, 1536, 128, 64, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("parts", ["local", "global"])
+@pytest.mark.parametrize("case", PARTS_CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}".format(
+    *c[:7], "causal" if c[7] else "full"))
+def test_backward_of_one_part_matches_oracle(case, parts):
+    """LocalOnly / GlobalOnly: the kept term's gradients, and exact zeros for
+    the parameters only the dropped term uses."""
+    B, T, d, e, s, C, dtype, causal = case
+    print(f"backward {parts} case {case}", flush=True)
+    inp = make(B, T, d, e, s, C, dtype, seed=B * 61 + T + C, heads="wide")
+    dO = inputs.make_output_grad(B, T, d, seed=T + 5 * d, dtype=dtype)
+    _compare(_backward(inp, dO, B, T, d, e, s, C, causal, dtype, parts=parts),
+             _oracle(inp, dO, C, causal, parts=parts), dtype)
 
 
 def test_backward_at_benchmark_shape():
