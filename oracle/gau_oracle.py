@@ -405,7 +405,7 @@ def silu_grad(h):
 
 
 def flash_backward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal, dO,
-                   quad_scale=None, lin_scale=None, use_rope=False, parts="both"):
+                   quad_scale=None, lin_scale=None, use_rope=False, parts="both", chunk_segments=None):
     """Gradients of <dO, O> for O = flash_forward(...): a dict with X, W_u,
     W_v, W_z, W_o (pages' orientation), gamma, beta, relpos.  parts as in
     flash_forward: "local" drops the linear term (and everything that only
@@ -418,7 +418,9 @@ def flash_backward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal, dO,
       use_rope); U, V, Z = SiLU(X W).
     A rotation's transpose is the rotation by the opposite angle, so the
     gradients of the rotated heads go back through rope at the negated
-    positions.
+    positions.  With chunk_segments the summaries reach P through the
+    row-normalised chunk mask M (P_g = sum_h M[g, h] S_h), so dS_h =
+    sum_g M[g, h] dP_g.
     """
     X = _as64(X)
     B, T, d = X.shape
@@ -442,7 +444,12 @@ def flash_backward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal, dO,
     Sc = (Qqg @ Kqg.swapaxes(-1, -2)) * quad_scale + toeplitz_bias(relpos, C)
     A = relu_squared(Sc) * mask
     S = (Klg.swapaxes(-1, -2) @ Vg) * lin_scale
-    if causal:
+    if chunk_segments is not None:
+        if np.shape(chunk_segments) != (B, G):
+            raise ValueError("chunk_segments must have shape (B, T / C)")
+        Mseg = segment_chunk_mask(chunk_segments, causal)
+        P = np.einsum("bgh,bhse->bgse", Mseg, S)
+    elif causal:
         incl = np.cumsum(S, axis=1)
         P = np.concatenate([np.zeros_like(S[:, :1]), incl[:, :-1]], axis=1)
     else:
@@ -462,7 +469,9 @@ def flash_backward(X, W_u, W_v, W_z, W_o, gamma, beta, relpos, C, causal, dO,
     dV = A.swapaxes(-1, -2) @ dWq_quad
     dQl = dWq_lin @ P.swapaxes(-1, -2)
     dP = Qlg.swapaxes(-1, -2) @ dWq_lin
-    if causal:   # S_h feeds P_g for every g > h
+    if chunk_segments is not None:   # S_h feeds P_g with weight M[g, h]
+        dS = np.einsum("bgh,bgse->bhse", Mseg, dP)
+    elif causal:   # S_h feeds P_g for every g > h
         rev = np.cumsum(dP[:, ::-1], axis=1)[:, ::-1]
         dS = np.concatenate([rev[:, 1:], np.zeros_like(dP[:, :1])], axis=1)
     else:

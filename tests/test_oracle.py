@@ -524,6 +524,33 @@ def test_backward_of_one_part_matches_central_differences(parts, causal):
         assert np.all(g["gamma"][:2] == 0) and np.all(g["relpos"] == 0)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_with_segments_matches_central_differences(causal):
+    """Packed sequences: every gradient against central differences of the
+    brute-force forward with the same chunk segments."""
+    B, T, C = 2, 12, 2
+    seg = [[0, 0, 1, 1, 1, 5], [3, 4, 4, 4, 4, 4]]
+    p = _tiny(B, T, d=4, e=5, s=4, C=C, seed=43)
+    dO = np.random.default_rng(7).standard_normal((B, T, 4))
+    g = orc.flash_backward(p["X"], p["W_u"], p["W_v"], p["W_z"], p["W_o"], p["gamma"], p["beta"],
+                           p["relpos"], C, causal, dO, quad_scale=0.6, lin_scale=0.8, chunk_segments=seg)
+    h = 1e-6
+
+    def f(q):
+        return float(np.sum(dO * _run(orc.flash_forward_bruteforce, q, C, causal, quad_scale=0.6, lin_scale=0.8,
+                                      chunk_segments=seg)))
+
+    for k in ("X", "W_u", "W_v", "W_z", "W_o", "gamma", "beta", "relpos"):
+        fd = np.zeros_like(p[k])
+        for idx in np.ndindex(p[k].shape):
+            up = {a: (b.copy() if isinstance(b, np.ndarray) else b) for a, b in p.items()}
+            dn = {a: (b.copy() if isinstance(b, np.ndarray) else b) for a, b in p.items()}
+            up[k][idx] += h
+            dn[k][idx] -= h
+            fd[idx] = (f(up) - f(dn)) / (2 * h)
+        np.testing.assert_allclose(g[k], fd, rtol=1e-5, atol=1e-6, err_msg=k)
+
+
 # ---------------------------------------------------------------- segment masks
 
 SEGMENTS = [
