@@ -28,7 +28,7 @@ EXPORTS = (
     "gau_workspace_bytes", "gau_workspace_layout", "gau_forward", "gau_forward_stages",
     "gau_stack_workspace_bytes", "gau_stack_forward", "gau_decode_workspace_bytes", "gau_decode_reset",
     "gau_decode_step", "gau_rope_relpos", "gau_backward_workspace_bytes", "gau_backward", "gau_status_string",
-    "gau_probe_mfma", "gau_forward_noalloc", "gau_forward_segmented",
+    "gau_probe_mfma", "gau_forward_noalloc", "gau_forward_segmented", "gau_backward_segmented",
 )
 
 # include/gau.h: the size of gau_forward_noalloc's device scratch array
@@ -102,6 +102,8 @@ def load():
     lib.gau_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.gau_backward.argtypes = [cfgp] + [P] * 18 + [ctypes.c_size_t, P]
     lib.gau_backward.restype = ctypes.c_int
+    lib.gau_backward_segmented.argtypes = [cfgp] + [P] * 19 + [ctypes.c_size_t, P]
+    lib.gau_backward_segmented.restype = ctypes.c_int
     lib.gau_status_string.argtypes = [ctypes.c_int]
     lib.gau_status_string.restype = ctypes.c_char_p
     lib.gau_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
@@ -321,10 +323,13 @@ def backward_workspace_bytes(cfg):
 GRAD_NAMES = ("X", "W_u", "W_v", "W_z", "W_o", "scale", "offset", "relpos")
 
 
-def backward(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, dO, grads, workspace, stream=None):
+def backward(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, dO, grads, workspace, stream=None,
+             chunk_segments=None):
     """gau_backward on torch tensors: fills ``grads`` (a dict of fp32 device
     tensors named as GRAD_NAMES; the weight gradients output-major like the
-    weights) with the gradients of <dO, O>."""
+    weights) with the gradients of <dO, O>.  With chunk_segments (an int32
+    device tensor [B, T / C]) gau_backward_segmented, the backward of
+    gau_forward_segmented."""
     import torch
     _check_layer(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, dO)
     B, T, d, e, s, C = cfg.B, cfg.T, cfg.d, cfg.e, cfg.s, cfg.C
@@ -333,9 +338,15 @@ def backward(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, dO, grads, works
     for k in GRAD_NAMES:
         _check(grads[k], "d" + k, torch.float32, sizes[k])
     _check(workspace, "workspace")
-    st = load().gau_backward(
-        ctypes.byref(cfg), _ptr(X), _ptr(W_u), _ptr(W_v), _ptr(W_z), _ptr(W_o), _ptr(scale), _ptr(offset),
-        _ptr(relpos), _ptr(dO), *[_ptr(grads[k]) for k in GRAD_NAMES], _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream))
+    tail = (_ptr(X), _ptr(W_u), _ptr(W_v), _ptr(W_z), _ptr(W_o), _ptr(scale), _ptr(offset), _ptr(relpos),
+            _ptr(dO), *[_ptr(grads[k]) for k in GRAD_NAMES], _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if chunk_segments is None:
+        st = load().gau_backward(ctypes.byref(cfg), *tail)
+        name = "gau_backward"
+    else:
+        _check(chunk_segments, "chunk_segments", torch.int32, B * (T // C))
+        st = load().gau_backward_segmented(ctypes.byref(cfg), _ptr(chunk_segments), *tail)
+        name = "gau_backward_segmented"
     if st != 0:
-        raise GauError(st, "gau_backward")
+        raise GauError(st, name)

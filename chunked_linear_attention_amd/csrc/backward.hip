@@ -313,13 +313,35 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(SplitJobs q) {
 // dS from dP (fp32 [B, G, s*e]): causal dS_h = sum_{g > h} dP_g (a reverse
 // exclusive sum, walked g = G-1 .. 0), non-causal dS_h = sum_g dP_g; stored
 // times `scale` (lin_scale, which both of dS's products carry), element type.
+// With segment ids (runs of equal consecutive ids, chunks a .. z-1) the
+// transpose of the forward's averaging: causal dS_h = sum_{h < g < z}
+// dP_g / (g - a), non-causal dS_h = sum_{a <= g < z} dP_g / (z - a).
 template <typename T>
 __global__ __launch_bounds__(256) void scan_bwd_kernel(BwdScanParams q) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)q.B * q.es) return;
     const size_t b = idx / q.es, v = idx - b * q.es;
     const float* dp = q.dP + b * q.G * q.es + v;
-    if (q.causal) {
+    if (q.seg) {
+        const int32_t* sg = q.seg + b * q.G;
+        for (int z = q.G; z > 0;) {
+            int a = z - 1;  // the segment is chunks a .. z-1
+            while (a > 0 && sg[a - 1] == sg[z - 1]) --a;
+            if (q.causal) {
+                float run = 0.f;
+                for (int g = z - 1; g >= a; --g) {
+                    st<T>(q.dS, (b * q.G + g) * q.es + v, q.scale * run);
+                    if (g > a) run += dp[(size_t)g * q.es] * (1.0f / (float)(g - a));
+                }
+            } else {
+                float tot = 0.f;
+                for (int g = a; g < z; ++g) tot += dp[(size_t)g * q.es];
+                const float avg = tot * (1.0f / (float)(z - a));
+                for (int g = a; g < z; ++g) st<T>(q.dS, (b * q.G + g) * q.es + v, q.scale * avg);
+            }
+            z = a;
+        }
+    } else if (q.causal) {
         float run = 0.f;
         for (int g = q.G - 1; g >= 0; --g) {
             st<T>(q.dS, (b * q.G + g) * q.es + v, q.scale * run);

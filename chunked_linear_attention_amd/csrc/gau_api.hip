@@ -296,7 +296,7 @@ gau::TransposeParams tp(const void* in, int64_t in_bs, int in_rp, void* out, int
 // rule through its steps in reverse (the launch order below).
 gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO, float* dX, float* dW_u,
                         float* dW_v, float* dW_z, float* dW_o, float* dscale, float* doffset, float* drelpos,
-                        char* ws, hipStream_t st) {
+                        char* ws, hipStream_t st, const int32_t* seg = nullptr) {
     gau_ws_layout F;
     layout(c, &F, false);
     BwdLayout L;
@@ -339,14 +339,17 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
         return GAU_ERR_HIP;
     // (the projection also stores the pre-activations H = X [W_u | W_v | W_z],
     // which the SiLU derivatives below read)
-    gau_status sres = run_stages(c, GAU_STAGE_PROJ, GAU_STAGE_SCAN, a, nullptr, nullptr, ws, st, false, nullptr,
+    // (with segments the scan leaves one averaged state per chunk in place
+    // of S)
+    gau_status sres = run_stages(c, GAU_STAGE_PROJ, GAU_STAGE_SCAN, a, nullptr, nullptr, ws, st, false, seg,
                                  W(L.H));
+    const size_t Poff = seg ? F.S : F.P;
     if (sres != GAU_OK) return sres;
     // Wq = A V + Q_lin P, or the kept term (into the forward's Y region): the
     // attention stage without the gate
     {
-        gau::AttnParams p{W(F.A), W(F.Q_lin), W(F.Vt), W(F.P), nullptr, W(F.Y), Bn, T, e, s, C,
-                          c->causal ? 1 : 0, local ? 1 : 0, global ? 1 : 0};
+        gau::AttnParams p{W(F.A), W(F.Q_lin), W(F.Vt), W(Poff), nullptr, W(F.Y), Bn, T, e, s, C,
+                          c->causal ? 1 : 0, local ? 1 : 0, global ? 1 : 0, seg ? 1 : 0};
         ok(gau::launch_chunk_attn(p, bf, st));
     }
     // the transposes left, in one launch: W_o^T (dY), the weights (dX) and
@@ -411,13 +414,13 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
     // dK_lin = V dS^T
     if (global) {
         {
-            const NtOp P_m = c->causal ? mnmaj(W(F.P), es, (int64_t)G * es, s) : mnmaj(W(F.P), 0, es, s);
+            const NtOp P_m = (c->causal || seg) ? mnmaj(W(Poff), es, (int64_t)G * es, s) : mnmaj(W(Poff), 0, es, s);
             gemm(nt(dWq_k, P_m, W(L.dQl), Cs, s, e, true, G), C, s, Z);
         }
         gemm(nt(dWq_m, heads_m(F.Q_lin), W(L.dP), es, s, C, true, G), e, s, Z);
         {
             gau::BwdScanParams p{(const float*)W(L.dP), W(L.dSst), Bn, G, (int)es, c->causal ? 1 : 0,
-                                 c->lin_scale};
+                                 c->lin_scale, seg};
             ok(gau::launch_scan_bwd(p, bf, st));
         }
         gemm(nt(V_m, dS_m, W(L.dKl), Cs, s, e, true, G), C, s, Z);
@@ -590,7 +593,7 @@ gau_status gau_stack_forward(const gau_config* cfg, int n_layers, float* X, cons
 
 // What gau_backward takes beyond check_config: at most 2^38 pre-activation
 // entries (one-dimensional grids of 256-thread blocks).
-gau_status check_backward(const gau_config* c) {
+static gau_status check_backward(const gau_config* c) {
     gau_status s = check_config(c);
     if (s != GAU_OK) return s;
     if (c->B * c->T * (2 * c->e + c->s) > ((int64_t)1 << 38)) return GAU_ERR_SHAPE;
@@ -604,11 +607,15 @@ size_t gau_backward_workspace_bytes(const gau_config* cfg) {
     return L.total;
 }
 
-gau_status gau_backward(const gau_config* cfg, const void* X, const void* W_u, const void* W_v, const void* W_z,
-                        const void* W_o, const float* scale, const float* offset, const float* relpos,
-                        const void* dO, float* dX, float* dW_u, float* dW_v, float* dW_z, float* dW_o,
-                        float* dscale, float* doffset, float* drelpos, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+}  // extern "C"
+
+namespace {
+
+gau_status backward_entry(const gau_config* cfg, const int32_t* seg, bool segmented, const void* X,
+                          const void* W_u, const void* W_v, const void* W_z, const void* W_o, const float* scale,
+                          const float* offset, const float* relpos, const void* dO, float* dX, float* dW_u,
+                          float* dW_v, float* dW_z, float* dW_o, float* dscale, float* doffset, float* drelpos,
+                          void* workspace, size_t workspace_bytes, void* stream) {
     gau_status s = check_backward(cfg);
     if (s != GAU_OK) return s;
     float* outs[] = {dW_u, dW_v, dW_z, dW_o, dscale, doffset, drelpos};
@@ -627,10 +634,35 @@ gau_status gau_backward(const gau_config* cfg, const void* X, const void* W_u, c
     }
     const LayerPtrs a{X, W_u, W_v, W_z, W_o, scale, offset, relpos};
     if ((s = check_layer_ptrs(a)) != GAU_OK) return s;
-    if (!dO || !dX || !workspace) return GAU_ERR_NULL;
-    if (!aligned16(dO) || !aligned16(dX) || !aligned16(workspace)) return GAU_ERR_ALIGN;
+    if (!dO || !dX || !workspace || (segmented && !seg)) return GAU_ERR_NULL;
+    if (!aligned16(dO) || !aligned16(dX) || !aligned16(workspace) || (segmented && !aligned16(seg)))
+        return GAU_ERR_ALIGN;
     if (workspace_bytes < gau_backward_workspace_bytes(cfg)) return GAU_ERR_WORKSPACE;
-    return run_backward(cfg, a, dO, dX, dW_u, dW_v, dW_z, dW_o, dscale, doffset, drelpos, (char*)workspace, st);
+    return run_backward(cfg, a, dO, dX, dW_u, dW_v, dW_z, dW_o, dscale, doffset, drelpos, (char*)workspace, st,
+                        segmented ? seg : nullptr);
+}
+
+}  // namespace
+
+extern "C" {
+
+gau_status gau_backward(const gau_config* cfg, const void* X, const void* W_u, const void* W_v, const void* W_z,
+                        const void* W_o, const float* scale, const float* offset, const float* relpos,
+                        const void* dO, float* dX, float* dW_u, float* dW_v, float* dW_z, float* dW_o,
+                        float* dscale, float* doffset, float* drelpos, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    return backward_entry(cfg, nullptr, false, X, W_u, W_v, W_z, W_o, scale, offset, relpos, dO, dX, dW_u, dW_v,
+                          dW_z, dW_o, dscale, doffset, drelpos, workspace, workspace_bytes, stream);
+}
+
+gau_status gau_backward_segmented(const gau_config* cfg, const int32_t* chunk_segments, const void* X,
+                                  const void* W_u, const void* W_v, const void* W_z, const void* W_o,
+                                  const float* scale, const float* offset, const float* relpos, const void* dO,
+                                  float* dX, float* dW_u, float* dW_v, float* dW_z, float* dW_o, float* dscale,
+                                  float* doffset, float* drelpos, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    return backward_entry(cfg, chunk_segments, true, X, W_u, W_v, W_z, W_o, scale, offset, relpos, dO, dX, dW_u,
+                          dW_v, dW_z, dW_o, dscale, doffset, drelpos, workspace, workspace_bytes, stream);
 }
 
 size_t gau_decode_workspace_bytes(const gau_config* cfg) {

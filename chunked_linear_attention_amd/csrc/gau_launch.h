@@ -226,6 +226,7 @@ struct BwdScanParams {
     void* dS;         // [B, G, es] element type, times scale
     int B, G, es, causal;
     float scale;
+    const int32_t* seg;  // [B, G] chunk segment ids, or nullptr (no segments)
 };
 
 constexpr int kHeadsBwdTokens = 16;  // tokens per block of the heads' backward step

@@ -324,6 +324,25 @@ gau_status gau_backward(const gau_config* cfg, const void* X,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gau_backward for the segment-masked layer of gau_forward_segmented (packed
+ * sequences; wikillm "Paper vs code" and "Pitfalls", segment masks): the same
+ * arguments plus chunk_segments [B, T/C] int32 (16-byte aligned), the ids
+ * gau_forward_segmented took.  The summaries reach P through the
+ * row-normalised chunk mask M (P_g = sum_h M[g][h] S_h), so the reverse sum
+ * becomes dS_h = sum_g M[g][h] dP_g: causal, sum over the later chunks g of
+ * h's segment of dP_g / (chunks visible from g); non-causal, the segment's
+ * sum of dP_g over its length.  Any rope and ablation.  Checks and status
+ * codes as gau_backward (NULL chunk_segments: GAU_ERR_NULL); the workspace
+ * is gau_backward_workspace_bytes(cfg).
+ */
+gau_status gau_backward_segmented(const gau_config* cfg, const int32_t* chunk_segments, const void* X,
+                                  const void* W_u, const void* W_v, const void* W_z, const void* W_o,
+                                  const float* scale, const float* offset, const float* relpos, const void* dO,
+                                  float* dX, float* dW_u, float* dW_v, float* dW_z, float* dW_o,
+                                  float* dscale, float* doffset, float* drelpos,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Incremental causal decoding: one new token of each of the B sequences per
  * call, with a constant-size state per sequence (the chunk-level recurrence
  * of the causal layer: wikillm, "Method" steps 2-4; Su's post, "Mixed

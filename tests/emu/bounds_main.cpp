@@ -156,10 +156,12 @@ static void run(const Cfg& c, const std::string& only) {
         free(ws);
     });
     // the backward pass through the C ABI: exact-size inputs, outputs and
-    // workspace, for the full layer, with RoPE and for each partial layer
-    for (int variant = 0; variant < 4; ++variant)
+    // workspace, for the full layer, with RoPE, for each partial layer and
+    // with segment ids
+    for (int variant = 0; variant < 5; ++variant)
     if (M <= 4096) t(variant == 0 ? "gau_backward" : variant == 1 ? "gau_backward_rope"
-                     : variant == 2 ? "gau_backward_local" : "gau_backward_global", [&] {
+                     : variant == 2 ? "gau_backward_local" : variant == 3 ? "gau_backward_global"
+                     : "gau_backward_segmented", [&] {
         gau_config cfg{c.B, c.T, c.d, c.e, c.s, c.C, c.causal ? 1 : 0, c.bf ? GAU_BF16 : GAU_F32, 1.0f / c.C,
                        1.0f / c.C, variant == 1 ? 1 : 0,
                        variant == 2 ? GAU_LOCAL_ONLY : variant == 3 ? GAU_GLOBAL_ONLY : GAU_FULL};
@@ -174,8 +176,10 @@ static void run(const Cfg& c, const std::string& only) {
         float* gs = (float*)buf(4 * c.s * 4);
         float* gb = (float*)buf(4 * c.s * 4);
         float* gr = (float*)buf((2 * c.C - 1) * 4);
-        int st = gau_backward(&cfg, X, Wu, Wv, Wz, Wo, sc, of, rp, gO, gX, gu, gv, gz, go, gs, gb, gr, ws, wsb,
-                              nullptr);
+        int st = variant == 4 ? gau_backward_segmented(&cfg, seg, X, Wu, Wv, Wz, Wo, sc, of, rp, gO, gX, gu, gv, gz,
+                                                       go, gs, gb, gr, ws, wsb, nullptr)
+                              : gau_backward(&cfg, X, Wu, Wv, Wz, Wo, sc, of, rp, gO, gX, gu, gv, gz, go, gs, gb, gr,
+                                             ws, wsb, nullptr);
         if (st != GAU_OK) {
             fprintf(stderr, "gau_backward status %d\n", st);
             exit(1);

@@ -136,6 +136,12 @@ def test_backward_argument_checks_without_gpu():
     bad = list(good)
     bad[12] = ctypes.c_void_p(4096 * 13 + 4)
     assert call(cfg, bad, ws) == 3                          # misaligned dW_z
+    # the segment-masked backward: the same checks plus its segment ids
+    seg = lambda c, sg, ptrs, n: lib.gau_backward_segmented(ctypes.byref(c), sg, *ptrs, ctypes.c_size_t(n), None)
+    assert seg(cfg, None, good, ws) == 1                    # NULL chunk_segments
+    assert seg(cfg, ctypes.c_void_p(4096 * 40 + 4), good, ws) == 3  # misaligned chunk_segments
+    assert seg(cfg, ctypes.c_void_p(4096 * 40), good, ws - 1) == 5
+    assert seg(cfg, ctypes.c_void_p(4096 * 40), [None] + good[1:], ws) == 1
     grow = g.backward_workspace_bytes(_cfg(T=1024))
     assert grow > ws                                        # grows with the tokens
     assert g.backward_workspace_bytes(_cfg(dtype=g.GAU_F32)) > ws

@@ -267,6 +267,17 @@ BWD_CASES = [
     + ("_" + c[10] if len(c) > 10 else ""))
 def test_emulated_backward_matches_oracle(emu, case):
     """gau_backward on the emulation: every gradient against the oracle's."""
+    _emulated_backward(emu, case)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_emulated_segmented_backward_matches_oracle(emu, causal):
+    """gau_backward_segmented on the emulation (packed runs of 1..3 chunks)."""
+    seg = np.array([[0, 0, 0, 1, 2, 2], [4, 5, 5, 5, 6, 6]], np.int32)
+    _emulated_backward(emu, (2, 384, 128, 256, 128, 64, "f32", causal, "wide"), seg=seg)
+
+
+def _emulated_backward(emu, case, seg=None):
     B, T, d, e, s, C, dtype, causal = case[:8]
     heads = case[8] if len(case) > 8 else "workload"
     rope = len(case) > 9 and case[9]
@@ -294,11 +305,20 @@ def test_emulated_backward_matches_oracle(emu, case):
     raw = np.full(wsb + 256, 0xFF, np.uint8)
     ws = raw[(-raw.ctypes.data) % 256:][:wsb]
     ptr = lambda a: P(a.ctypes.data)
-    st = emu.gau_backward(ctypes.byref(cfg), ptr(X), ptr(W["W_u"]), ptr(W["W_v"]), ptr(W["W_z"]), ptr(W["W_o"]),
-                          ptr(sc), ptr(of), ptr(rp), ptr(dOh), *[ptr(out[k]) for k in out], ptr(ws), wsb, None)
+    args = (ptr(X), ptr(W["W_u"]), ptr(W["W_v"]), ptr(W["W_z"]), ptr(W["W_o"]), ptr(sc), ptr(of), ptr(rp), ptr(dOh),
+            *[ptr(out[k]) for k in out], ptr(ws), wsb, None)
+    if seg is None:
+        st = emu.gau_backward(ctypes.byref(cfg), *args)
+    else:
+        emu.gau_backward_segmented.argtypes = [ctypes.POINTER(GauConfig)] + [P] * 19 + [ctypes.c_size_t, P]
+        emu.gau_backward_segmented.restype = ctypes.c_int
+        segr = np.zeros(seg.size + 4, np.int32)
+        sega = segr[(-segr.ctypes.data) % 16 // 4:][:seg.size]
+        sega[:] = seg.ravel()
+        st = emu.gau_backward_segmented(ctypes.byref(cfg), ptr(sega), *args)
     assert st == 0
     ref = orc.flash_backward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"], inp["beta"],
-                             inp["relpos"], C, causal, dO, use_rope=rope, parts=parts)
+                             inp["relpos"], C, causal, dO, use_rope=rope, parts=parts, chunk_segments=seg)
     tol = 2e-2 if bf else 1e-4
     for k, got in out.items():
         want = ref[k] if k != "W_o" else ref[k].T     # weights come back output-major

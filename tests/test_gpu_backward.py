@@ -15,7 +15,7 @@ from _gpu import assert_close, make, tol_for, torch_dtype
 pytestmark = pytest.mark.gpu
 
 
-def _backward(inp, dO, B, T, d, e, s, C, causal, dtype, fill=0, rope=False, parts="both"):
+def _backward(inp, dO, B, T, d, e, s, C, causal, dtype, fill=0, rope=False, parts="both", seg=None):
     tdt = torch_dtype(dtype)
     dev = g.device_layer(inp, tdt)
     cfg = g.make_config(B, T, d, e, s, C, causal, g.GAU_BF16 if dtype == "bf16" else g.GAU_F32, rope=rope,
@@ -25,15 +25,16 @@ def _backward(inp, dO, B, T, d, e, s, C, causal, dtype, fill=0, rope=False, part
     like = {"X": (B, T, d), "W_u": (e, d), "W_v": (e, d), "W_z": (s, d), "W_o": (d, e), "scale": (4, s),
             "offset": (4, s), "relpos": (2 * C - 1,)}
     grads = {k: torch.full(like[k], float("nan"), dtype=torch.float32, device="cuda") for k in g.GRAD_NAMES}
+    sg = None if seg is None else torch.from_numpy(np.ascontiguousarray(seg, dtype=np.int32)).cuda()
     g.backward(cfg, dev["X"], dev["W_u"], dev["W_v"], dev["W_z"], dev["W_o"], dev["scale"], dev["offset"],
-               dev["relpos"], dOd, grads, ws)
+               dev["relpos"], dOd, grads, ws, chunk_segments=sg)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
 
 
-def _oracle(inp, dO, C, causal, rope=False, parts="both"):
+def _oracle(inp, dO, C, causal, rope=False, parts="both", seg=None):
     r = orc.flash_backward(inp["X"], inp["W_u"], inp["W_v"], inp["W_z"], inp["W_o"], inp["gamma"], inp["beta"],
-                           inp["relpos"], C, causal, dO, use_rope=rope, parts=parts)
+                           inp["relpos"], C, causal, dO, use_rope=rope, parts=parts, chunk_segments=seg)
     # the library returns weight gradients output-major, like the weights it takes
     return {"X": r["X"], "W_u": r["W_u"].T, "W_v": r["W_v"].T, "W_z": r["W_z"].T, "W_o": r["W_o"].T,
             "scale": r["gamma"], "offset": r["beta"], "relpos": r["relpos"]}
@@ -125,6 +126,50 @@ def test_backward_of_one_part_matches_oracle(case, parts):
     dO = inputs.make_output_grad(B, T, d, seed=T + 5 * d, dtype=dtype)
     _compare(_backward(inp, dO, B, T, d, e, s, C, causal, dtype, parts=parts),
              _oracle(inp, dO, C, causal, parts=parts), dtype)
+
+
+SEG_CASES = [
+    # B, T, d, e, s, C, dtype, causal, longest segment (chunks)
+    (1, 512, 128, 256, 128, 64, "f32", True, 3),
+    (2, 512, 128, 256, 128, 64, "f32", False, 3),
+    (2, 1024, 256, 512, 128, 128, "bf16", True, 2),
+    (1, 960, 128, 1536, 128, 64, "bf16", False, 4),
+]
+
+
+def _runs(rng, B, G, max_run):
+    """Per-row chunk ids: runs of 1..max_run chunks, ids increasing."""
+    seg = np.zeros((B, G), np.int32)
+    for b in range(B):
+        g0, sid = 0, 0
+        while g0 < G:
+            n = int(rng.integers(1, max_run + 1))
+            seg[b, g0:g0 + n] = sid
+            g0, sid = g0 + n, sid + 1
+    return seg
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_{}_{}_seg{}".format(
+    *c[:7], "causal" if c[7] else "full", c[8]))
+def test_backward_with_segments_matches_oracle(case):
+    """gau_backward_segmented: packed sequences, every gradient."""
+    B, T, d, e, s, C, dtype, causal, max_run = case
+    print(f"backward segments case {case}", flush=True)
+    seg = _runs(np.random.default_rng(T + C + max_run), B, T // C, max_run)
+    inp = make(B, T, d, e, s, C, dtype, seed=B * 53 + T + C, heads="wide")
+    dO = inputs.make_output_grad(B, T, d, seed=T + 7 * d, dtype=dtype)
+    _compare(_backward(inp, dO, B, T, d, e, s, C, causal, dtype, seg=seg), _oracle(inp, dO, C, causal, seg=seg),
+             dtype)
+
+
+def test_backward_with_segments_at_benchmark_shape():
+    """B=2, T=8192 packed with documents of 1..8 chunks, bf16, causal."""
+    B, T, d, e, s, C = 2, 8192, 768, 1536, 128, 256
+    print("backward segments benchmark shape", flush=True)
+    seg = _runs(np.random.default_rng(11), B, T // C, 8)
+    inp = make(B, T, d, e, s, C, "bf16", seed=2026)
+    dO = inputs.make_output_grad(B, T, d, seed=2026, dtype="bf16")
+    _compare(_backward(inp, dO, B, T, d, e, s, C, True, "bf16", seg=seg), _oracle(inp, dO, C, True, seg=seg), "bf16")
 
 
 def test_backward_at_benchmark_shape():
