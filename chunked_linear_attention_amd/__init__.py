@@ -1,5 +1,6 @@
-"""MI355X-native forward pass of the FLASH gated attention unit with mixed
-chunk attention ("Transformer Quality in Linear Time").
+"""MI355X-native FLASH gated attention unit with mixed chunk attention
+("Transformer Quality in Linear Time"): the layer's forward pass, its
+gradients, incremental decoding and the layer stack.
 
 The computation lives in libgau.so: hand-written HIP kernels for gfx950 behind
 the C ABI declared in include/gau.h.  This package is the thin Python binding
@@ -72,20 +73,24 @@ def gau_forward(X, W_u, W_v, W_z, W_o, scale, offset, relpos, C, causal,
 
 
 def gau_backward(X, W_u, W_v, W_z, W_o, scale, offset, relpos, C, causal, dO,
-                 quad_scale=None, lin_scale=None, workspace=None, stream=None):
-    """Gradients of <dO, O> for O = gau_forward(X, ...): a dict of fp32 device
-    tensors keyed X, W_u, W_v, W_z, W_o (output-major, like the weights),
-    scale, offset, relpos.  Every step runs in libgau's kernels."""
+                 quad_scale=None, lin_scale=None, workspace=None, stream=None, rope=False, parts="both",
+                 chunk_segments=None):
+    """Gradients of <dO, O> for O = gau_forward(X, ...) with the same rope and
+    parts (with chunk_segments, an int32 device tensor [B, T / C], the
+    segment-masked layer of forward_segmented): a dict of fp32 device tensors
+    keyed X, W_u, W_v, W_z, W_o (output-major, like the weights), scale,
+    offset, relpos.  Every step runs in libgau's kernels."""
     torch = _torch()
     B, T, d = X.shape
     e = W_u.shape[0]
     s = W_z.shape[0]
     dt = GAU_BF16 if X.dtype == torch.bfloat16 else GAU_F32
-    cfg = make_config(B, T, d, e, s, C, causal, dt, quad_scale, lin_scale)
+    cfg = make_config(B, T, d, e, s, C, causal, dt, quad_scale, lin_scale, rope, parts)
     like = {"X": X, "W_u": W_u, "W_v": W_v, "W_z": W_z, "W_o": W_o, "scale": scale, "offset": offset,
             "relpos": relpos}
     grads = {k: torch.empty(like[k].shape, dtype=torch.float32, device=X.device) for k in GRAD_NAMES}
     if workspace is None:
         workspace = torch.empty(max(backward_workspace_bytes(cfg), 1), dtype=torch.uint8, device=X.device)
-    backward(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, dO, grads, workspace, stream)
+    backward(cfg, X, W_u, W_v, W_z, W_o, scale, offset, relpos, dO, grads, workspace, stream,
+             chunk_segments=chunk_segments)
     return grads
