@@ -172,6 +172,17 @@ def test_backward_with_segments_at_benchmark_shape():
     _compare(_backward(inp, dO, B, T, d, e, s, C, True, "bf16", seg=seg), _oracle(inp, dO, C, True, seg=seg), "bf16")
 
 
+@pytest.mark.parametrize("B,T,causal", [(4, 4096, False), (8, 1024, True)], ids=["B4_T4096_full", "B8_T1024_causal"])
+def test_backward_at_other_full_shapes(B, T, causal):
+    """The layer's other full-size shapes (d=768, e=1536, s=128, C=256, bf16):
+    B=4 T=4096 non-causal, B=8 T=1024 causal; every gradient."""
+    d, e, s, C = 768, 1536, 128, 256
+    print(f"backward full shape B{B} T{T} causal={causal}", flush=True)
+    inp = make(B, T, d, e, s, C, "bf16", seed=3000 + B, heads="wide")
+    dO = inputs.make_output_grad(B, T, d, seed=3000 + T, dtype="bf16")
+    _compare(_backward(inp, dO, B, T, d, e, s, C, causal, "bf16"), _oracle(inp, dO, C, causal), "bf16")
+
+
 def test_backward_at_benchmark_shape():
     """B=2, T=8192, d=768, e=1536, s=128, C=256, bf16, causal: every gradient."""
     B, T, d, e, s, C = 2, 8192, 768, 1536, 128, 256
