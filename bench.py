@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -82,13 +83,19 @@ def algorithmic_bytes(B, T, d, e, s, C, causal=True, eb=2):
 SOURCES = {"proj": "proj_gemm"}
 
 
+_COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def source_hash(name):
-    """Hash of a kernel's source file and the device headers it includes."""
+    """Hash of the code (comments and blank lines dropped) of a kernel's
+    source file and the device headers it includes."""
     csrc = os.path.join(ROOT, "chunked_linear_attention_amd", "csrc")
     h = hashlib.sha256()
     for f in (SOURCES.get(name, name) + ".hip", "gemm_core.h", "gau_device.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            code = _COMMENTS.sub("", fh.read())
+        h.update("\n".join(l.rstrip() for l in code.splitlines() if l.strip()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

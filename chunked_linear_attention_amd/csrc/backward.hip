@@ -1,7 +1,8 @@
 // Kernels of the layer's backward pass (gradients of <dO, O>): a batched NT
-// GEMM on the shared MFMA core (optionally over two K segments, with fused
-// epilogues for the gate and the SiLU derivative), a batched transpose that
-// makes every product's operands K-major, and the elementwise and reduction
+// GEMM on the shared MFMA core (its operands K-major or MN-major, optionally
+// over two K segments, with a fused SiLU-derivative epilogue), a batched
+// transpose for the few small tensors still made K-major, and the
+// elementwise and reduction
 // steps of the chain rule through the forward's steps (the derivative of each
 // product written out; the forward's steps as the pages give them: wikillm
 // "Method" and the FLASH block pseudocode; Su's post, "Gated Attention" and
@@ -190,11 +191,6 @@ __device__ __forceinline__ void transpose_block(const TransposeParams& q, int bi
             *(f32x4_t*)(out + (size_t)(c0 + c) * q.out_rp + r0 + vc) = y;
         }
     }
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(TransposeParams q) {
-    transpose_block<T>(q, blockIdx.x);
 }
 
 // Several independent transposes in one launch: block b runs job j with
@@ -481,20 +477,6 @@ hipError_t launch_transpose_batch(const TransposeParams* jobs, const int* R, con
         hipLaunchKernelGGL(transpose_batch_kernel<bf16>, dim3((unsigned)total), dim3(256), 0, st, b);
     else
         hipLaunchKernelGGL(transpose_batch_kernel<float>, dim3((unsigned)total), dim3(256), 0, st, b);
-    return hipGetLastError();
-}
-
-hipError_t launch_transpose(const TransposeParams& q0, int R, int Cc, int nb, bool bf, hipStream_t st) {
-    TransposeParams q = q0;
-    q.tr = R / 64;
-    q.tc = Cc / 64;
-    const int64_t blocks = (int64_t)nb * q.tr * q.tc;
-    if (blocks <= 0 || blocks > INT32_MAX) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)blocks);
-    if (bf)
-        hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, st, q);
-    else
-        hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st, q);
     return hipGetLastError();
 }
 

@@ -243,7 +243,6 @@ struct BwdHeadsParams {
 };
 
 hipError_t launch_gemm_nt(const GemmNTParams& q, int M, int N, int nb, bool bf16_storage, hipStream_t st);
-hipError_t launch_transpose(const TransposeParams& q, int R, int Cc, int nb, bool bf16_storage, hipStream_t st);
 
 // Up to kTransposeBatch independent transposes (job j: R[j] x Cc[j], nb[j]
 // batch entries) in one launch.

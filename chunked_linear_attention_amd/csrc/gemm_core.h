@@ -1,6 +1,7 @@
 // Block-level NT GEMM core for gfx950:  C[BM x BN] += A[BM x K] . B[BN x K]^T
-// with A and B row-major and K contiguous.  Used by the projection and output
-// GEMMs of the layer.
+// with A and B K-major (row-major, K contiguous), or either one MN-major (K
+// rows of contiguous M or N elements: TA, TB; see DmaOperandT and frag_t).
+// Used by the layer's GEMM-shaped kernels, forward and backward.
 //
 // Design (MI355X / CDNA4):
 //  * 32x32x16 bf16 MFMA (v_mfma_f32_32x32x16_bf16; fp32: four
