@@ -799,6 +799,62 @@ struct GemmCore {
         }
     }
 
+    // store_packed with an elementwise f applied on the way, in NB passes of
+    // one accumulator block column each (every wave's block column j: the
+    // staged rows wn * WTN + j * 32 + c, WGN * 32 of them).  Pass j applies f
+    // to acc[.][j], stages the result and stores it; the passes alternate
+    // between two LDS buffers, so one barrier per pass suffices and the
+    // global stores of pass j are in flight while pass j + 1 computes.  Needs
+    // two buffers of WGN * 32 staged rows in lds_bytes (else f, then
+    // store_packed).  Begins with a barrier.
+    template <typename OutT, typename F, typename D>
+    __device__ static __forceinline__ void store_packed_cols(f32x16_t (&acc)[MB][NB], char* lds, int lds_bytes,
+                                                             F&& f, D&& dst) {
+        constexpr int EB = Elem<OutT>::kBytes;
+        constexpr int PITCH = BM * EB + 16;
+        constexpr int SROWS = WGN * 32;  // staged rows per pass
+        constexpr int BUF = SROWS * PITCH;
+        constexpr int VPR = BM * EB / 16;
+        if (2 * BUF > lds_bytes) {
+            transform(acc, f);
+            store_packed<OutT>(acc, lds, lds_bytes, [](int, int, float v) { return v; }, dst);
+            return;
+        }
+        const int wave = threadIdx.x / kWave;
+        const int lane = threadIdx.x % kWave;
+        const int wm = wave / WGN, wn = wave % WGN;
+        const int c = lane & 31;
+        const int h = lane >> 5;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            char* buf = lds + (j & 1) * BUF;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int row0 = wm * WTM + i * 32 + 8 * g4 + 4 * h;
+                    const int col = wn * WTN + j * 32 + c;
+                    float x[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) x[t] = f(row0 + t, col, acc[i][j][4 * g4 + t]);
+                    char* q = buf + (wn * 32 + c) * PITCH + row0 * EB;
+                    if constexpr (EB == 2) {
+                        *(u32x2_t*)q = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+                    } else {
+                        *(f32x4_t*)q = f32x4_t{x[0], x[1], x[2], x[3]};
+                    }
+                }
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < SROWS * VPR; idx += NT) {
+                const int srow = idx / VPR;
+                const int v = idx % VPR;
+                char* d = dst((srow >> 5) * WTN + j * 32 + (srow & 31), v * (16 / EB));
+                if (d) *(u32x4_t*)d = *(const u32x4_t*)(buf + srow * PITCH + v * 16);
+            }
+        }
+    }
+
     // f(row, col, value) for every accumulator element; row/col relative to
     // the block tile.
     template <typename F>

@@ -299,13 +299,13 @@ __device__ __forceinline__ void uv_tile(const ProjParams& p, int bid, char* lds,
                 return m < M ? Hb + ((size_t)m * hrp + feat) * EB : nullptr;
             });
     }
-    G::transform(acc, [](int, int, float v) { return silu(v); });
+    auto act = [](int, int, float v) { return silu(v); };
     if (!is_v) {
         // acc rows = features, columns = tokens (U is not stored when the
         // pre-activations are: the backward forms U = SiLU(X W_u) from them)
         char* U = (char*)p.U;
         if (!p.H)
-            G::template store_packed<T>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
+            G::template store_packed_cols<T>(acc, lds, LDS, act, [&](int tok, int feat) -> char* {
                 const int m = m0 + tok;
                 return m < M ? U + ((size_t)m * p.e + c0 + feat) * EB : nullptr;
             });
@@ -315,7 +315,7 @@ __device__ __forceinline__ void uv_tile(const ProjParams& p, int bid, char* lds,
     } else {
         // acc rows = tokens, columns = features
         char* Vt = (char*)p.Vt;
-        G::template store_packed<T>(acc, lds, LDS, ident, [&](int feat, int tok) -> char* {
+        G::template store_packed_cols<T>(acc, lds, LDS, act, [&](int feat, int tok) -> char* {
             const int m = m0 + tok;
             if (m >= M) return nullptr;
             const int b = m / T_, t = m - b * T_;
