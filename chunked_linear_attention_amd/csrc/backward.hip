@@ -78,9 +78,12 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmNTParams q) {
     using G = GemmCore<T, BT, BT, 2, 2, 2, 0, 2, TA, TB>;
     using G2 = GemmCore<T, BT, BT, 2, 2, 2, 0, 2, TA2, TB2>;
     constexpr int EB = Elem<T>::kBytes;
-    // block -> (batch, row tile, column tile), column tiles fastest
+    // block -> (batch, row tile, column tile), column tiles fastest, the
+    // logical order spread over the XCDs in contiguous ranges (the tiles of
+    // one batch entry share their operands in one L2)
     const int tiles = q.tm * q.tn;
-    const int z = blockIdx.x / tiles, t = blockIdx.x - z * tiles;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int z = bid / tiles, t = bid - z * tiles;
     const int m0 = (t / q.tn) * BT, n0 = (t % q.tn) * BT;
     if (q.skip_upper && n0 >= m0 + BT) return;  // wholly above the diagonal: never read
     const int64_t zs = z / q.zg, zc = z - zs * q.zg;
