@@ -128,6 +128,21 @@ static void run(const Cfg& c, const std::string& only) {
     t("out_gemm", [&] { CHECK(launch_out_gemm(op, c.bf, nullptr)); });
     OutParams opr{Y, Wo, Of, Of, (int)M, c.d, c.e};
     t("out_residual", [&] { CHECK(launch_out_gemm(opr, c.bf, nullptr)); });
+    // the backward's dY product with its gate epilogue (K = d, e outputs per
+    // token)
+    t("out_gate", [&] {
+        const int W3 = 2 * c.e + c.s;
+        void* WoT = buf((size_t)c.e * c.d * eb);
+        void* gO = buf(M * c.d * eb);
+        void* dH = buf(M * W3 * eb);
+        void* gH = buf(M * W3 * eb);
+        void* gW = buf(M * c.e * eb);
+        void* gD = buf(M * c.e * eb);
+        void* gY = buf(M * c.e * eb);
+        OutParams og{gO, WoT, dH, nullptr, (int)M, c.e, c.d, 0, W3, gH, gW, gD, gY, c.e};
+        CHECK(launch_out_gemm(og, c.bf, nullptr));
+        for (void* q : {WoT, gO, dH, gH, gW, gD, gY}) free(q);
+    });
     NormParams np{Of, X, (int)M, c.d, 1e-6f};
     t("rms_norm", [&] { CHECK(launch_rms_norm(np, c.bf, nullptr)); });
     // the whole layer through the C ABI, one workspace
