@@ -53,7 +53,9 @@ struct OutTile {
     static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
 };
 
-template <typename T, int BM, bool TN>
+// GATE: the backward's gate epilogue (p.gH set), a kernel of its own so that
+// the others carry none of its prefetch registers.
+template <typename T, int BM, bool TN, bool GATE>
 __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     extern __shared__ __align__(16) char lds[];
     using G = typename OutTile<T, BM, TN>::G;
@@ -73,6 +75,38 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     const int nk = p.e / G::KELEMS, kbase = nk / S, krem = nk % S;
     const int kc0 = z * kbase + min(z, krem), nkz = kbase + (z < krem ? 1 : 0);
 
+    const int M = p.M, d = p.d;
+    const size_t orp = p.o_rp > 0 ? (size_t)p.o_rp : (size_t)d;  // output row pitch
+
+    // Inputs of the gate epilogue (the OutParams gate fields), processed in
+    // NPASS passes of PROWS tokens; each thread takes NV 4-element vectors
+    // (features n..n+3 of token m) per pass.  bf16: the first pass's
+    // pre-activations and Wq are loaded before the K loop, so that their
+    // memory latency overlaps it, each later pass's at the start of the pass
+    // before it (two register buffers).  fp32 (vectors twice as wide, no
+    // registers to spare in the K loop): one buffer, the first pass's loaded
+    // after the K loop, each later pass's at the end of the pass before it.
+    constexpr int NPASS = WGN, PROWS = BN / NPASS;
+    constexpr int VPR = BM / 4;              // 4-element vectors per token row of the tile
+    constexpr int NV = PROWS * VPR / G::NT;  // vectors per thread per pass
+    using Raw = typename Raw4<T>::type;
+    constexpr int NBUF = EB == 2 ? 2 : 1;
+    Raw hb[NBUF][NV], wb[NBUF][NV];
+    constexpr bool gate = !TN && GATE;
+    const size_t grp = (size_t)p.g_rp;
+    auto gload = [&](int pass, Raw (&h)[NV], Raw (&w)[NV]) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + i * G::NT;
+            const int m = m0 + pass * PROWS + idx / VPR, n = n0 + (idx % VPR) * 4;
+            if (m < M && n < d) {
+                h[i] = *(const Raw*)((const char*)p.gH + ((size_t)m * orp + n) * EB);
+                w[i] = *(const Raw*)((const char*)p.gW + ((size_t)m * grp + n) * EB);
+            }
+        }
+    };
+    if constexpr (NBUF == 2 && gate) gload(0, hb[0], wb[0]);
+
     // acc = tile^T: rows = output features (W_o^T rows), columns = tokens, so
     // the packed epilogue writes run along the token-major rows of O.
     f32x16_t acc[G::MB][G::NB];
@@ -88,8 +122,6 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     }
 
     constexpr int LDS = OutTile<T, BM, TN>::LDS;
-    const int M = p.M, d = p.d;
-    const size_t orp = p.o_rp > 0 ? (size_t)p.o_rp : (size_t)d;  // output row pitch
     auto ident = [](int, int, float v) { return v; };
     if constexpr (TN) {
         // fp32 O = Y W_o (split z: its partial product at O + z * o_bs)
@@ -98,33 +130,18 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
             const int m = m0 + tok, n = n0 + feat;
             return (m < M && n < d) ? (char*)(O + (size_t)m * orp + n) : nullptr;
         });
-    } else if (p.gH != nullptr) {
-        // gate epilogue (the OutParams gate fields), in NPASS passes of PROWS
-        // tokens: the product staged in fp32 (staged rows = tokens); each
-        // thread takes NV 16-byte staged vectors (features n..n+3 of token m)
-        // whose pre-activations and Wq it loaded at the end of the previous
-        // pass (before the staging of this one).
-        constexpr int NPASS = WGN, PROWS = BN / NPASS;
-        constexpr int PITCH = BM * 4 + 16;       // fp32 staging row
-        constexpr int VPR = BM / 4;              // 16-byte vectors per staged row
-        constexpr int NV = PROWS * VPR / G::NT;  // vectors per thread per pass
+    } else if constexpr (gate) {
+        // gate epilogue: the product staged in fp32 (staged rows = tokens),
+        // one pass at a time; the pass's inputs were loaded one pass ahead
+        constexpr int PITCH = BM * 4 + 16;  // fp32 staging row
         static_assert(PROWS * VPR % G::NT == 0 && PROWS * PITCH <= LDS, "gate epilogue passes");
-        using Raw = typename Raw4<T>::type;
-        const size_t grp = (size_t)p.g_rp;
-        Raw hb[NV], wb[NV];
-        auto load = [&](int pass) {
+        if constexpr (NBUF == 1) gload(0, hb[0], wb[0]);
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int idx = threadIdx.x + i * G::NT;
-                const int m = m0 + pass * PROWS + idx / VPR, n = n0 + (idx % VPR) * 4;
-                if (m < M && n < d) {
-                    hb[i] = *(const Raw*)((const char*)p.gH + ((size_t)m * orp + n) * EB);
-                    wb[i] = *(const Raw*)((const char*)p.gW + ((size_t)m * grp + n) * EB);
-                }
-            }
-        };
-        load(0);
         for (int pass = 0; pass < NPASS; ++pass) {
+            const int cur = NBUF == 2 ? (pass & 1) : 0;
+            if constexpr (NBUF == 2) {
+                if (pass + 1 < NPASS) gload(pass + 1, hb[cur ^ 1], wb[cur ^ 1]);  // in flight across this pass
+            }
             __syncthreads();
             G::template stage_packed<float>(acc, lds, pass, PROWS, NPASS, ident);
             __syncthreads();
@@ -136,8 +153,8 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
                 if ((int)m >= M || n >= d) continue;
                 const u32x4_t v = *(const u32x4_t*)(lds + srow * PITCH + (idx % VPR) * 16);
                 float hv[4], wv[4], a[4], y[4], o[4];
-                unpack4(hb[i], hv);
-                unpack4(wb[i], wv);
+                unpack4(hb[cur][i], hv);
+                unpack4(wb[cur][i], wv);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const float dy = __uint_as_float(v[k]), h = hv[k], w = wv[k];
@@ -153,7 +170,9 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
                 put4<T>((char*)p.gY + j * EB, y);
                 put4<T>((char*)p.O + (m * orp + n) * EB, o);
             }
-            if (pass + 1 < NPASS) load(pass + 1);  // in flight across the next pass's staging
+            if constexpr (NBUF == 1) {
+                if (pass + 1 < NPASS) gload(pass + 1, hb[0], wb[0]);  // in flight across the next pass's staging
+            }
         }
     } else if (p.residual == nullptr && !p.f32_out) {
         char* O = (char*)p.O;
@@ -188,7 +207,7 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     }
 }
 
-template <typename T, int BM, bool TN = false>
+template <typename T, int BM, bool TN = false, bool GATE = false>
 hipError_t launch(const OutParams& p, hipStream_t st) {
     constexpr int LDS = OutTile<T, BM, TN>::LDS;
     static_assert(LDS <= 160 * 1024, "output GEMM LDS over budget");
@@ -198,9 +217,10 @@ hipError_t launch(const OutParams& p, hipStream_t st) {
         return hipErrorInvalidValue;
     if (S > p.e / OutTile<T, BM, TN>::G::KELEMS) return hipErrorInvalidValue;
     const int blocks = ((p.d + BM - 1) / BM) * ((p.M + BN - 1) / BN) * S;
-    hipError_t e = allow_lds<out_gemm_kernel<T, BM, TN>>(LDS);
+    if (GATE != (p.gH != nullptr)) return hipErrorInvalidValue;
+    hipError_t e = allow_lds<out_gemm_kernel<T, BM, TN, GATE>>(LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((out_gemm_kernel<T, BM, TN>), dim3(blocks), dim3(512), LDS, st, p);
+    hipLaunchKernelGGL((out_gemm_kernel<T, BM, TN, GATE>), dim3(blocks), dim3(512), LDS, st, p);
     return hipGetLastError();
 }
 
@@ -227,9 +247,9 @@ template <typename T>
 hipError_t dispatch(const OutParams& p, hipStream_t st) {
     if (p.tn) return p.bm == 256 ? launch<T, 256, true>(p, st) : hipErrorInvalidValue;
     switch (p.bm > 0 ? p.bm : feature_tile(p.d, p.M)) {
-        case 256: return launch<T, 256>(p, st);
-        case 192: return launch<T, 192>(p, st);
-        default: return launch<T, 128>(p, st);
+        case 256: return p.gH ? launch<T, 256, false, true>(p, st) : launch<T, 256>(p, st);
+        case 192: return p.gH ? launch<T, 192, false, true>(p, st) : launch<T, 192>(p, st);
+        default: return p.gH ? launch<T, 128, false, true>(p, st) : launch<T, 128>(p, st);
     }
 }
 
