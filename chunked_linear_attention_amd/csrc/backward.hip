@@ -56,6 +56,36 @@ __device__ __forceinline__ void load8(const void* p, int64_t i, float (&v)[8]) {
     }
 }
 
+// Eight consecutive elements as loaded (one 16-byte vector for bf16, two for
+// fp32), and as floats.
+template <typename T> struct Raw8 { u32x4_t x; };
+template <> struct Raw8<float> { f32x4_t a, b; };
+template <typename T>
+__device__ __forceinline__ void load8raw(const void* p, int64_t i, Raw8<T>& r) {
+    if constexpr (Elem<T>::kBytes == 2) {
+        r.x = *(const u32x4_t*)((const uint16_t*)p + i);
+    } else {
+        r.a = *(const f32x4_t*)((const float*)p + i);
+        r.b = *(const f32x4_t*)((const float*)p + i + 4);
+    }
+}
+template <typename T>
+__device__ __forceinline__ void unpack8(const Raw8<T>& r, float (&v)[8]) {
+    if constexpr (Elem<T>::kBytes == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(r.x[k] << 16);
+            v[2 * k + 1] = __uint_as_float(r.x[k] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = r.a[k];
+            v[4 + k] = r.b[k];
+        }
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ void store8(void* p, int64_t i, const float (&v)[8]) {
     if constexpr (Elem<T>::kBytes == 2) {
@@ -92,6 +122,19 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmNTParams q) {
     auto tile = [&](const void* base, int64_t bsq, int64_t bs, int rp, bool mn_major, int r0) {
         return (const char*)base + (zs * bsq + zc * bs + (mn_major ? (int64_t)r0 : (int64_t)r0 * rp)) * EB;
     };
+    const int64_t cb = (int64_t)z * q.c_bs + (int64_t)m0 * q.c_rp + n0;
+    // SiLU-derivative epilogue: each thread takes ITERS runs of 8 consecutive
+    // columns; their pre-activations are loaded before the K loop, so that
+    // the memory latency overlaps it
+    constexpr int PER_ROW = BT / 8, ITERS = BT * PER_ROW / 256;
+    Raw8<T> hr[EPI == EPI_SILU ? ITERS : 1];
+    if constexpr (EPI == EPI_SILU) {
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const int k = threadIdx.x + it * 256, r = k / PER_ROW, c = (k % PER_ROW) * 8;
+            load8raw<T>(q.H, cb + (int64_t)r * q.c_rp + c, hr[it]);
+        }
+    }
     f32x16_t acc[G::MB][G::NB];
     G::zero(acc);
     // first K index of segment 1 (a K row of an MN-major operand, an element
@@ -103,7 +146,6 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmNTParams q) {
     if (q.K2 > 0)
         G2::run(acc, tile(q.A2, q.a2_bsq, q.a2_bs, q.a2_rp, TA2, m0), (size_t)q.a2_rp * EB, BT,
                 tile(q.B2, q.b2_bsq, q.b2_bs, q.b2_rp, TB2, n0), (size_t)q.b2_rp * EB, BT, q.K2, lds);
-    const int64_t cb = (int64_t)z * q.c_bs + (int64_t)m0 * q.c_rp + n0;
     const float alpha = q.alpha;
     if constexpr (EPI == EPI_STORE) {
         G::for_each(acc, [&](int r, int c, float v) {
@@ -119,10 +161,10 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmNTParams q) {
         float* tile = (float*)lds;
         G::for_each(acc, [&](int r, int c, float v) { tile[r * BT + c] = alpha * v; });
         __syncthreads();
-        constexpr int PER_ROW = BT / 8;
-#pragma unroll 2
-        for (int k = threadIdx.x; k < BT * PER_ROW; k += 256) {
-            const int r = k / PER_ROW, c = (k % PER_ROW) * 8;
+        static_assert(BT * PER_ROW % 256 == 0, "whole runs per thread");
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const int k = threadIdx.x + it * 256, r = k / PER_ROW, c = (k % PER_ROW) * 8;
             float v[8], h[8];
             const f32x4_t v0 = *(const f32x4_t*)(tile + r * BT + c);
             const f32x4_t v1 = *(const f32x4_t*)(tile + r * BT + c + 4);
@@ -132,7 +174,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmNTParams q) {
                 v[4 + u] = v1[u];
             }
             const int64_t i = cb + (int64_t)r * q.c_rp + c;
-            load8<T>(q.H, i, h);
+            unpack8<T>(hr[it], h);
             float o[8];
             static_assert(EPI == EPI_SILU, "epilogues: store, SiLU derivative");
 #pragma unroll
