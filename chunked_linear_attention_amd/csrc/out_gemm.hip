@@ -53,9 +53,12 @@ struct OutTile {
     static constexpr int LDS = G::LDS_BYTES > STAGE ? G::LDS_BYTES : STAGE;
 };
 
-// GATE: the backward's gate epilogue (p.gH set), a kernel of its own so that
-// the others carry none of its prefetch registers.
-template <typename T, int BM, bool TN, bool GATE>
+// Epilogue kinds, each a kernel of its own so that the others carry none of
+// its prefetch registers: plain stores, the backward's gate (p.gH set), the
+// residual add (p.residual set).
+enum { kEpPlain = 0, kEpGate = 1, kEpResid = 2 };
+
+template <typename T, int BM, bool TN, int EP>
 __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     extern __shared__ __align__(16) char lds[];
     using G = typename OutTile<T, BM, TN>::G;
@@ -78,10 +81,10 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     const int M = p.M, d = p.d;
     const size_t orp = p.o_rp > 0 ? (size_t)p.o_rp : (size_t)d;  // output row pitch
 
-    // Inputs of the gate epilogue (the OutParams gate fields), processed in
-    // NPASS passes of PROWS tokens; each thread takes NV 4-element vectors
-    // (features n..n+3 of token m) per pass.  bf16: the first pass's
-    // pre-activations and Wq are loaded before the K loop, so that their
+    // Inputs of the gate epilogue (the OutParams gate fields) and of the
+    // residual add, processed in NPASS passes of PROWS tokens; each thread
+    // takes NV 4-element vectors (features n..n+3 of token m) per pass.  bf16:
+    // the first pass's inputs are loaded before the K loop, so that their
     // memory latency overlaps it, each later pass's at the start of the pass
     // before it (two register buffers).  fp32 (vectors twice as wide, no
     // registers to spare in the K loop): one buffer, the first pass's loaded
@@ -91,8 +94,9 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
     constexpr int NV = PROWS * VPR / G::NT;  // vectors per thread per pass
     using Raw = typename Raw4<T>::type;
     constexpr int NBUF = EB == 2 ? 2 : 1;
-    Raw hb[NBUF][NV], wb[NBUF][NV];
-    constexpr bool gate = !TN && GATE;
+    constexpr bool gate = !TN && EP == kEpGate, resid = !TN && EP == kEpResid;
+    Raw hb[gate ? NBUF : 1][NV], wb[gate ? NBUF : 1][NV];
+    f32x4_t rb[resid ? NBUF : 1][NV];
     const size_t grp = (size_t)p.g_rp;
     auto gload = [&](int pass, Raw (&h)[NV], Raw (&w)[NV]) {
 #pragma unroll
@@ -105,7 +109,16 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
             }
         }
     };
+    auto rload = [&](int pass, f32x4_t (&r)[NV]) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + i * G::NT;
+            const int m = m0 + pass * PROWS + idx / VPR, n = n0 + (idx % VPR) * 4;
+            if (m < M && n < d) r[i] = *(const f32x4_t*)(p.residual + (size_t)m * orp + n);
+        }
+    };
     if constexpr (NBUF == 2 && gate) gload(0, hb[0], wb[0]);
+    if constexpr (NBUF == 2 && resid) rload(0, rb[0]);
 
     // acc = tile^T: rows = output features (W_o^T rows), columns = tokens, so
     // the packed epilogue writes run along the token-major rows of O.
@@ -174,40 +187,53 @@ __global__ __launch_bounds__(512) void out_gemm_kernel(OutParams p) {
                 if (pass + 1 < NPASS) gload(pass + 1, hb[0], wb[0]);  // in flight across the next pass's staging
             }
         }
+    } else if constexpr (resid) {
+        // O = residual + Y W_o (fp32), in place allowed: each output vector is
+        // read from the residual and written by the same thread
+        constexpr int PITCH = BM * 4 + 16;  // fp32 staging row
+        static_assert(PROWS * VPR % G::NT == 0 && PROWS * PITCH <= LDS, "residual epilogue passes");
+        float* O = (float*)p.O;
+        if constexpr (NBUF == 1) rload(0, rb[0]);
+#pragma unroll
+        for (int pass = 0; pass < NPASS; ++pass) {
+            const int cur = NBUF == 2 ? (pass & 1) : 0;
+            if constexpr (NBUF == 2) {
+                if (pass + 1 < NPASS) rload(pass + 1, rb[cur ^ 1]);  // in flight across this pass
+            }
+            __syncthreads();
+            G::template stage_packed<float>(acc, lds, pass, PROWS, NPASS, ident);
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int idx = threadIdx.x + i * G::NT;
+                const int srow = idx / VPR, n = n0 + (idx % VPR) * 4;
+                const int m = m0 + pass * PROWS + srow;
+                if (m >= M || n >= d) continue;
+                f32x4_t x = *(const f32x4_t*)(lds + srow * PITCH + (idx % VPR) * 16);
+                x += rb[cur][i];
+                *(f32x4_t*)(O + (size_t)m * orp + n) = x;
+            }
+            if constexpr (NBUF == 1) {
+                if (pass + 1 < NPASS) rload(pass + 1, rb[0]);  // in flight across the next pass's staging
+            }
+        }
     } else if (p.residual == nullptr && !p.f32_out) {
         char* O = (char*)p.O;
         G::template store_packed<T>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
             const int m = m0 + tok, n = n0 + feat;
             return (m < M && n < d) ? O + ((size_t)m * orp + n) * EB : nullptr;
         });
-    } else if (p.residual == nullptr) {
+    } else {
         // fp32 O = Y W_o (split z: its partial product at O + z * o_bs)
         float* O = (float*)p.O + (size_t)z * p.o_bs;
         G::template store_packed<float>(acc, lds, LDS, ident, [&](int tok, int feat) -> char* {
             const int m = m0 + tok, n = n0 + feat;
             return (m < M && n < d) ? (char*)(O + (size_t)m * orp + n) : nullptr;
         });
-    } else {
-        // O = residual + Y W_o (fp32): stage the product, then add the residual
-        // while storing (each 16-byte vector is read and written by one thread).
-        float* O = (float*)p.O;
-        const float* R = p.residual;
-        G::template store_packed<float>(
-            acc, lds, LDS, ident,
-            [&](int tok, int feat) -> char* {
-                const int m = m0 + tok, n = n0 + feat;
-                return (m < M && n < d) ? (char*)(O + (size_t)m * orp + n) : nullptr;
-            },
-            [&](char* dp, const u32x4_t& v) {
-                const size_t off = (size_t)((float*)dp - O);
-                f32x4_t x = *(const f32x4_t*)(R + off);
-                x += __builtin_bit_cast(f32x4_t, v);
-                *(f32x4_t*)dp = x;
-            });
     }
 }
 
-template <typename T, int BM, bool TN = false, bool GATE = false>
+template <typename T, int BM, bool TN = false, int EP = kEpPlain>
 hipError_t launch(const OutParams& p, hipStream_t st) {
     constexpr int LDS = OutTile<T, BM, TN>::LDS;
     static_assert(LDS <= 160 * 1024, "output GEMM LDS over budget");
@@ -217,10 +243,11 @@ hipError_t launch(const OutParams& p, hipStream_t st) {
         return hipErrorInvalidValue;
     if (S > p.e / OutTile<T, BM, TN>::G::KELEMS) return hipErrorInvalidValue;
     const int blocks = ((p.d + BM - 1) / BM) * ((p.M + BN - 1) / BN) * S;
-    if (GATE != (p.gH != nullptr)) return hipErrorInvalidValue;
-    hipError_t e = allow_lds<out_gemm_kernel<T, BM, TN, GATE>>(LDS);
+    if ((EP == kEpGate) != (p.gH != nullptr) || (EP == kEpResid) != (p.residual != nullptr))
+        return hipErrorInvalidValue;
+    hipError_t e = allow_lds<out_gemm_kernel<T, BM, TN, EP>>(LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((out_gemm_kernel<T, BM, TN, GATE>), dim3(blocks), dim3(512), LDS, st, p);
+    hipLaunchKernelGGL((out_gemm_kernel<T, BM, TN, EP>), dim3(blocks), dim3(512), LDS, st, p);
     return hipGetLastError();
 }
 
@@ -243,13 +270,20 @@ int feature_tile(int d, int M) {
     return best;
 }
 
+template <typename T, int BM>
+hipError_t launch_ep(const OutParams& p, hipStream_t st) {
+    if (p.gH != nullptr) return launch<T, BM, false, kEpGate>(p, st);
+    if (p.residual != nullptr) return launch<T, BM, false, kEpResid>(p, st);
+    return launch<T, BM>(p, st);
+}
+
 template <typename T>
 hipError_t dispatch(const OutParams& p, hipStream_t st) {
     if (p.tn) return p.bm == 256 ? launch<T, 256, true>(p, st) : hipErrorInvalidValue;
     switch (p.bm > 0 ? p.bm : feature_tile(p.d, p.M)) {
-        case 256: return p.gH ? launch<T, 256, false, true>(p, st) : launch<T, 256>(p, st);
-        case 192: return p.gH ? launch<T, 192, false, true>(p, st) : launch<T, 192>(p, st);
-        default: return p.gH ? launch<T, 128, false, true>(p, st) : launch<T, 128>(p, st);
+        case 256: return launch_ep<T, 256>(p, st);
+        case 192: return launch_ep<T, 192>(p, st);
+        default: return launch_ep<T, 128>(p, st);
     }
 }
 
