@@ -401,43 +401,63 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(BwdScanParams q) {
 // tokens in order.  With rope the dh_k given are those of the rotated heads:
 // each goes back through the transposed rotation of its pair (i, i +- s/2)
 // at the token's position (dlo = dlo' c + dhi' sin, dhi = dhi' c - dlo' sin).
-template <typename T>
+template <typename T, bool ROPE>
 __global__ __launch_bounds__(256) void heads_bwd_kernel(BwdHeadsParams q) {
     const int i = threadIdx.x;
     if (i >= q.s) return;
     const int half = q.s / 2;
     const bool lo = i < half;
     const int partner = lo ? i + half : i - half;
-    const double theta = q.rope ? rope_theta(lo ? i : partner, half) : 0.0;
+    const double theta = ROPE ? rope_theta(lo ? i : partner, half) : 0.0;
     const int m0 = blockIdx.x * kHeadsBwdTokens;
     float pg[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int m = m0; m < m0 + kHeadsBwdTokens && m < q.M; ++m) {
-        const size_t o = (size_t)m * q.s + i;
-        const size_t hz = (size_t)m * q.hpitch + i;
-        const float h = ld<T>(q.Hz, hz);
-        const float z = silu(h);
-        float dhk[4];
+    float gk[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) dhk[k] = q.dh[k][o];
-        if (q.rope) {
-            float c, sn;
-            rope_cos_sin((double)(m % q.T), theta, c, sn);
-            const size_t op = (size_t)m * q.s + partner;
+    for (int k = 0; k < 4; ++k) gk[k] = q.scale[k * q.s + i];
+    // groups of U tokens: every load of a group in flight together, then the
+    // arithmetic in token order (the sums keep that order)
+    constexpr int U = 4;
+    static_assert(kHeadsBwdTokens % U == 0, "whole groups");
+    for (int m1 = m0; m1 < m0 + kHeadsBwdTokens; m1 += U) {
+        float hv[U], dv[U][4], pv[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int m = min(m1 + u, q.M - 1);  // (a token past the end is loaded, not used)
+            hv[u] = ld<T>(q.Hz, (size_t)m * q.hpitch + i);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float pk = q.dh[k][op];
-                dhk[k] = lo ? dhk[k] * c + pk * sn : dhk[k] * c - pk * sn;
+                dv[u][k] = q.dh[k][(size_t)m * q.s + i];
+                if constexpr (ROPE) pv[u][k] = q.dh[k][(size_t)m * q.s + partner];
             }
         }
-        float dz = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float dh = dhk[k];
-            dz += q.scale[k * q.s + i] * dh;
-            pg[k] += dh * z;
-            pb[k] += dh;
+        for (int u = 0; u < U; ++u) {
+            const int m = m1 + u;
+            if (m >= q.M) break;
+            const float h = hv[u];
+            const float z = silu(h);
+            float dhk[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dhk[k] = dv[u][k];
+            if constexpr (ROPE) {
+                float c, sn;
+                rope_cos_sin((double)(m % q.T), theta, c, sn);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float pk = pv[u][k];
+                    dhk[k] = lo ? dhk[k] * c + pk * sn : dhk[k] * c - pk * sn;
+                }
+            }
+            float dz = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float dh = dhk[k];
+                dz += gk[k] * dh;
+                pg[k] += dh * z;
+                pb[k] += dh;
+            }
+            st<T>(q.dHz, (size_t)m * q.hpitch + i, dz * silu_grad(h));
         }
-        st<T>(q.dHz, hz, dz * silu_grad(h));
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -573,7 +593,10 @@ hipError_t launch_scan_bwd(const BwdScanParams& q, bool bf, hipStream_t st) {
 
 hipError_t launch_heads_bwd(const BwdHeadsParams& q, float* dscale, float* doffset, bool bf, hipStream_t st) {
     const int nblk = (q.M + kHeadsBwdTokens - 1) / kHeadsBwdTokens;
-    hipError_t e = bf ? go(heads_bwd_kernel<bf16>, (unsigned)nblk, q, st) : go(heads_bwd_kernel<float>, (unsigned)nblk, q, st);
+    hipError_t e = bf ? (q.rope ? go(heads_bwd_kernel<bf16, true>, (unsigned)nblk, q, st)
+                                : go(heads_bwd_kernel<bf16, false>, (unsigned)nblk, q, st))
+                      : (q.rope ? go(heads_bwd_kernel<float, true>, (unsigned)nblk, q, st)
+                                : go(heads_bwd_kernel<float, false>, (unsigned)nblk, q, st));
     if (e != hipSuccess) return e;
     // part is [nblk, 8, s]: the gamma sums in rows 0..3, the beta sums in rows
     // 4..7, i.e. columns [0, 4s) and [4s, 8s) of an [nblk, 8s] array
