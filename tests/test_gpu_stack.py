@@ -25,10 +25,18 @@ def _run_stack(X, layers, B, T, d, e, s, C, dtype, causal=True):
     return x.cpu().numpy().astype(np.float64)
 
 
+STACK_SHAPES = [
+    # B, T, d, e, s, C, layers
+    (2, 512, 256, 512, 128, 128, 3),
+    (3, 192, 384, 768, 128, 64, 2),   # B*T = 576: the output tiles' last token tile ragged, d not a power of two
+]
+
+
+@pytest.mark.parametrize("shape", STACK_SHAPES, ids=lambda c: "B{}_T{}_d{}_e{}_s{}_C{}_L{}".format(*c))
 @pytest.mark.parametrize("heads", ["workload", "wide"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_small_stack_matches_oracle(dtype, heads):
-    B, T, d, e, s, C, nl = 2, 512, 256, 512, 128, 128, 3
+def test_small_stack_matches_oracle(dtype, heads, shape):
+    B, T, d, e, s, C, nl = shape
     X, layers = inputs.make_stack_inputs(B, T, d, e, s, C, nl, weight_seed=300, x_seed=301, dtype=dtype,
                                          heads=heads)
     got = _run_stack(X, layers, B, T, d, e, s, C, dtype)
