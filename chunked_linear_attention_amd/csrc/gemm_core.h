@@ -71,37 +71,62 @@ struct KSeg {
 // Direct global -> LDS copy of one 128-byte K chunk of a ROWS-row operand
 // tile whose K axis is the concatenation of two segments (the second may be
 // empty).  The tile is moved as 1 KiB wave pieces (8 rows); wave w of NW takes
-// pieces w, w + NW, ...  Each lane's source pointers (row clamped to the rows
-// that exist, piece XOR-permuted by the row) are computed once; a chunk only
-// adds its K offset.
-template <int ROWS, int NW>
+// pieces w, w + NW, ...  Each lane's source (row clamped to the rows that
+// exist, piece XOR-permuted by the row) is computed once; a chunk only adds
+// its K offset.
+//   BUF = false: 64-bit source pointers per lane, global_load_lds_dwordx4.
+//   BUF = true: a raw buffer resource per segment (its tile base, in SGPRs;
+//     no range limit) and 32-bit byte offsets per lane, the chunk's K offset
+//     as the scalar offset: buffer_load_dwordx4 ... lds.  Fewer address
+//     registers and instructions per copy (the bf16 operands: projection -1.2
+//     us, output GEMM -1.1 us).  A segment's rows must lie within 2 GiB of its
+//     base (the tiles here span at most 256 rows of a few KiB).
+template <int ROWS, int NW, bool BUF = false>
 struct DmaOperand {
     static constexpr int kLoads = ROWS / 8 / NW;
     static_assert(ROWS % (8 * NW) == 0, "pieces must split evenly over the waves");
-    const char* src0[kLoads];
-    const char* src1[kLoads];
+    const char* src0[BUF ? 1 : kLoads];
+    const char* src1[BUF ? 1 : kLoads];
+    __amdgpu_buffer_rsrc_t r0, r1;
+    int off0[BUF ? kLoads : 1];
+    int off1[BUF ? kLoads : 1];
     int n0;
 
     __device__ __forceinline__ void init(const KSeg& s0, const KSeg& s1, int rows_valid, int wave, int lane) {
         const int sub = lane >> 3;  // row inside the 8-row piece
         n0 = s0.chunks;
+        if constexpr (BUF) {
+            // raw buffers (stride 0), no range limit; word 3 as for untyped dword loads
+            r0 = __builtin_amdgcn_make_buffer_rsrc((void*)s0.base, (short)0, -1, 0x00020000);
+            r1 = __builtin_amdgcn_make_buffer_rsrc((void*)s1.base, (short)0, -1, 0x00020000);
+        }
 #pragma unroll
         for (int jj = 0; jj < kLoads; ++jj) {
             const int row = (wave + jj * NW) * 8 + sub;
             const int piece = (lane & 7) ^ ((row >> 1) & 7);  // logical 16-byte piece this lane fetches
             const int r = row < rows_valid ? row : rows_valid - 1;
-            src0[jj] = s0.base + (size_t)r * s0.pitch + piece * 16;
-            src1[jj] = s1.base + (size_t)r * s1.pitch + piece * 16;
+            if constexpr (BUF) {
+                off0[jj] = r * (int)s0.pitch + piece * 16;
+                off1[jj] = r * (int)s1.pitch + piece * 16;
+            } else {
+                src0[jj] = s0.base + (size_t)r * s0.pitch + piece * 16;
+                src1[jj] = s1.base + (size_t)r * s1.pitch + piece * 16;
+            }
         }
     }
     // Issue the copy of K chunk `kc` into `lds_tile`.
     __device__ __forceinline__ void issue(char* lds_tile, int kc, int wave) const {
         const bool first = kc < n0;
-        const size_t off = (size_t)(first ? kc : kc - n0) * 128;
+        const int kb = (first ? kc : kc - n0) * 128;
 #pragma unroll
-        for (int jj = 0; jj < kLoads; ++jj)
-            __builtin_amdgcn_global_load_lds((glb_ptr_t)((first ? src0[jj] : src1[jj]) + off),
-                                             (lds_ptr_t)(lds_tile + (wave + jj * NW) * 1024), 16, 0, 0);
+        for (int jj = 0; jj < kLoads; ++jj) {
+            lds_ptr_t dst = (lds_ptr_t)(lds_tile + (wave + jj * NW) * 1024);
+            if constexpr (BUF)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(first ? r0 : r1, dst, 16, first ? off0[jj] : off1[jj], kb, 0,
+                                                         0);
+            else
+                __builtin_amdgcn_global_load_lds((glb_ptr_t)((first ? src0[jj] : src1[jj]) + kb), dst, 16, 0, 0);
+        }
     }
 };
 
@@ -234,8 +259,14 @@ struct GemmCore {
     static_assert(!kAsym || (NS == 2 && NSB == 3 && ZR == 0), "split ring: NS = 2, NSB = 3, no side rows");
     static_assert(!(TA || TB) || (!kAsym && ZR == 0), "MN-major operands: plain ring, no side rows");
     // copy engines of the two operands (K-major or MN-major tiles)
-    using DA = typename PickT<TA, DmaOperandT<BM, NW, Elem<T>::kBytes>, DmaOperand<BM, NW>>::type;
-    using DB = typename PickT<TB, DmaOperandT<BN, NW, Elem<T>::kBytes>, DmaOperand<BN, NW>>::type;
+    // K-major copies through buffer resources for bf16 (for fp32 the global
+    // form: the compiler's register allocation of the fp32 kernels fares
+    // worse with the resources)
+    static constexpr bool kBuf = Elem<T>::kBytes == 2;
+    using DKA = DmaOperand<BM, NW, kBuf>;
+    using DKB = DmaOperand<BN, NW, kBuf>;
+    using DA = typename PickT<TA, DmaOperandT<BM, NW, Elem<T>::kBytes>, DKA>::type;
+    using DB = typename PickT<TB, DmaOperandT<BN, NW, Elem<T>::kBytes>, DKB>::type;
     static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "tile shape");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "tile rows");
     static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "pieces must split evenly over waves");
@@ -492,10 +523,10 @@ struct GemmCore {
     template <bool MORE_A, bool MORE_B>
     __device__ static __forceinline__ void split_chunk(f32x16_t (&acc)[MB][NB], u32x4_t (&fa)[2][MB],
                                                        u32x4_t (&fb)[2][NB], char* la, char* lb,
-                                                       const DmaOperand<BM, NW>& da, const DmaOperand<BN, NW>& db,
+                                                       const DKA& da, const DKB& db,
                                                        int& sa, int& sb, int kt, int wave, int fr, int fh, int oa,
                                                        int ob) {
-        constexpr int LB = DmaOperand<BN, NW>::kLoads;
+        constexpr int LB = DKB::kLoads;
         const char* ca = la + sa * A_BYTES + oa;
         const char* cb = lb + sb * B_BYTES + ob;
         const int na = sa ^ 1;                    // A stage of chunk kt+1
@@ -542,7 +573,7 @@ struct GemmCore {
                                                      int rows_a, const KSeg& b0, const KSeg& b1, int rows_b,
                                                      char* lds) {
         static_assert(kAsym, "split ring only");
-        constexpr int LB = DmaOperand<BN, NW>::kLoads;
+        constexpr int LB = DKB::kLoads;
         const int tid = threadIdx.x;
         const int wave = tid / kWave;
         const int lane = tid % kWave;
@@ -553,8 +584,8 @@ struct GemmCore {
         char* const la = lds;                  // A stages
         char* const lb = lds + NS * A_BYTES;   // B stages
 
-        DmaOperand<BM, NW> da;
-        DmaOperand<BN, NW> db;
+        DKA da;
+        DKB db;
         da.init(a0, a1, rows_a, wave, lane);
         db.init(b0, b1, rows_b, wave, lane);
         if (nk > 0) {
@@ -799,27 +830,26 @@ struct GemmCore {
         }
     }
 
+    // Whether store_packed_cols fits (two buffers of WGN * 32 staged rows of
+    // OutT in LDS_BYTES).
+    template <typename OutT, int LDS_BYTES>
+    static constexpr bool kColsFit = 2 * WGN * 32 * (BM * Elem<OutT>::kBytes + 16) <= LDS_BYTES;
+
     // store_packed with an elementwise f applied on the way, in NB passes of
     // one accumulator block column each (every wave's block column j: the
     // staged rows wn * WTN + j * 32 + c, WGN * 32 of them).  Pass j applies f
     // to acc[.][j], stages the result and stores it; the passes alternate
     // between two LDS buffers, so one barrier per pass suffices and the
-    // global stores of pass j are in flight while pass j + 1 computes.  Needs
-    // two buffers of WGN * 32 staged rows in lds_bytes (else f, then
-    // store_packed).  Begins with a barrier.
-    template <typename OutT, typename F, typename D>
-    __device__ static __forceinline__ void store_packed_cols(f32x16_t (&acc)[MB][NB], char* lds, int lds_bytes,
-                                                             F&& f, D&& dst) {
+    // global stores of pass j are in flight while pass j + 1 computes.
+    // Requires kColsFit.  Begins with a barrier.
+    template <typename OutT, int LDS_BYTES, typename F, typename D>
+    __device__ static __forceinline__ void store_packed_cols(f32x16_t (&acc)[MB][NB], char* lds, F&& f, D&& dst) {
         constexpr int EB = Elem<OutT>::kBytes;
         constexpr int PITCH = BM * EB + 16;
         constexpr int SROWS = WGN * 32;  // staged rows per pass
         constexpr int BUF = SROWS * PITCH;
         constexpr int VPR = BM * EB / 16;
-        if (2 * BUF > lds_bytes) {
-            transform(acc, f);
-            store_packed<OutT>(acc, lds, lds_bytes, [](int, int, float v) { return v; }, dst);
-            return;
-        }
+        static_assert(kColsFit<OutT, LDS_BYTES>, "two column-pass buffers must fit");
         const int wave = threadIdx.x / kWave;
         const int lane = threadIdx.x % kWave;
         const int wm = wave / WGN, wn = wave % WGN;

@@ -299,13 +299,24 @@ __device__ __forceinline__ void uv_tile(const ProjParams& p, int bid, char* lds,
                 return m < M ? Hb + ((size_t)m * hrp + feat) * EB : nullptr;
             });
     }
+    // SiLU, then the stores: in two column passes over two LDS buffers
+    // (store_packed_cols: the first pass's stores overlap the second's SiLU)
+    // when they fit, else SiLU on the whole tile and one store_packed
     auto act = [](int, int, float v) { return silu(v); };
+    constexpr bool cols = G::template kColsFit<T, LDS>;
+    if constexpr (!cols) G::transform(acc, act);
+    auto store_act = [&](auto&& dst) {
+        if constexpr (cols)
+            G::template store_packed_cols<T, LDS>(acc, lds, act, dst);
+        else
+            G::template store_packed<T>(acc, lds, LDS, ident, dst);
+    };
     if (!is_v) {
         // acc rows = features, columns = tokens (U is not stored when the
         // pre-activations are: the backward forms U = SiLU(X W_u) from them)
         char* U = (char*)p.U;
         if (!p.H)
-            G::template store_packed_cols<T>(acc, lds, LDS, act, [&](int tok, int feat) -> char* {
+            store_act([&](int tok, int feat) -> char* {
                 const int m = m0 + tok;
                 return m < M ? U + ((size_t)m * p.e + c0 + feat) * EB : nullptr;
             });
@@ -315,7 +326,7 @@ __device__ __forceinline__ void uv_tile(const ProjParams& p, int bid, char* lds,
     } else {
         // acc rows = tokens, columns = features
         char* Vt = (char*)p.Vt;
-        G::template store_packed_cols<T>(acc, lds, LDS, act, [&](int feat, int tok) -> char* {
+        store_act([&](int feat, int tok) -> char* {
             const int m = m0 + tok;
             if (m >= M) return nullptr;
             const int b = m / T_, t = m - b * T_;

@@ -310,6 +310,26 @@ void global_load_lds(const void* g, void* l, int size, int offset, int aux) {
     }
 }
 
+BufRsrc make_buffer_rsrc(const void* base, int stride, int num_records, int flags) {
+    if (stride != 0 || flags != 0x00020000) fail("buffer resource form not emulated");
+    return BufRsrc{(const char*)base, (uint32_t)num_records};
+}
+
+// buffer_load_dwordx4 ... lds (offen): the lane's bytes at base + voffset +
+// soffset + offset; an offset at or past num_records reads zeros (the raw
+// buffer's range check), otherwise the same copy as global_load_lds.
+void buffer_load_lds(const BufRsrc& r, void* l, int size, int voffset, int soffset, int offset, int aux) {
+    if (size != 16 || offset != 0 || aux != 0) fail("buffer_load_lds form not emulated");
+    if (voffset < 0 || soffset < 0) fail("negative buffer offset (%d, %d)", voffset, soffset);
+    const uint64_t off = (uint64_t)voffset + (uint64_t)soffset;
+    if (off + 16 > r.num_records) {
+        alignas(16) static const char zeros[16] = {};
+        global_load_lds(zeros, l, 16, 0, 0);
+        return;
+    }
+    global_load_lds(r.base + off, l, 16, 0, 0);
+}
+
 void s_waitcnt(int imm) {
     const int vm = (imm & 0xF) | (((imm >> 14) & 3) << 4);
     flush(g_cur, (size_t)vm);

@@ -39,6 +39,14 @@ void syncthreads();
 char* lds_base();
 void* static_shared(int key, size_t bytes);
 void global_load_lds(const void* g, void* l, int size, int offset, int aux);
+// A raw buffer resource (stride 0): its base and the byte count past which
+// loads read zeros.
+struct BufRsrc {
+    const char* base;
+    uint32_t num_records;
+};
+BufRsrc make_buffer_rsrc(const void* base, int stride, int num_records, int flags);
+void buffer_load_lds(const BufRsrc& r, void* l, int size, int voffset, int soffset, int offset, int aux);
 void s_waitcnt(int imm);
 f32x16_t mfma_32x32x16_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c);
 f32x16_t mfma_32x32x2_f32(float a, float b, f32x16_t c);
@@ -74,6 +82,10 @@ using std::min;
 #define __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, x, y, z) ::emu::mfma_16x16x4_f32(a, b, c)
 #define __builtin_amdgcn_global_load_lds(g, l, sz, off, aux) \
     ::emu::global_load_lds((const void*)(g), (void*)(l), sz, off, aux)
+typedef ::emu::BufRsrc __amdgpu_buffer_rsrc_t;
+#define __builtin_amdgcn_make_buffer_rsrc(p, stride, n, flags) ::emu::make_buffer_rsrc((const void*)(p), stride, n, flags)
+#define __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, sz, voff, soff, off, aux) \
+    ::emu::buffer_load_lds(r, (void*)(l), sz, voff, soff, off, aux)
 #define __builtin_amdgcn_s_waitcnt(imm) ::emu::s_waitcnt(imm)
 #define __builtin_amdgcn_ds_read_tr16_b64_v4i16(p) ::emu::ds_read_tr16((const void*)(p))
 #define __builtin_amdgcn_sched_group_barrier(a, b, c) ((void)0)
