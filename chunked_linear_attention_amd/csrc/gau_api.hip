@@ -333,10 +333,10 @@ gau_status run_backward(const gau_config* c, const LayerPtrs& a, const void* dO,
 
     // which terms reach Y (the LocalOnly / GlobalOnly layers keep one)
     const bool local = c->ablation != GAU_GLOBAL_ONLY, global = c->ablation != GAU_LOCAL_ONLY;
-    // forward intermediates: heads, states, prefix, weights (tiles above the
-    // causal diagonal, which the forward leaves unwritten, cleared first)
-    if (local && c->causal && gau::launch_fill_zero((float*)W(F.A), (size_t)Z * CC * eb / 4, st) != hipSuccess)
-        return GAU_ERR_HIP;
+    // forward intermediates: heads, states, prefix, weights (the causal
+    // weight tiles above the diagonal stay unwritten: the attention and dV
+    // products never read them, and the scores' derivative selects zero
+    // there without using what it loaded)
     // (the projection also stores the pre-activations H = X [W_u | W_v | W_z],
     // which the SiLU derivatives below read)
     // (with segments the scan leaves one averaged state per chunk in place

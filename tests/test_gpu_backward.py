@@ -192,10 +192,14 @@ def test_backward_at_benchmark_shape():
     _compare(_backward(inp, dO, B, T, d, e, s, C, True, "bf16"), _oracle(inp, dO, C, True), "bf16")
 
 
+@pytest.mark.parametrize("shape", [(2, 256, 128, 256, 128, 64), (1, 1024, 256, 1536, 128, 256)],
+                         ids=["C64", "C256"])
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
-def test_backward_is_reproducible_and_ignores_workspace_contents(causal):
-    """Bitwise equal gradients from a zeroed and from a NaN-filled workspace."""
-    B, T, d, e, s, C = 2, 256, 128, 256, 128, 64
+def test_backward_is_reproducible_and_ignores_workspace_contents(causal, shape):
+    """Bitwise equal gradients from a zeroed and from a NaN-filled workspace
+    (at C = 256 the causal score tiles above the diagonal are never written:
+    nothing may read them unmasked)."""
+    B, T, d, e, s, C = shape
     inp = make(B, T, d, e, s, C, "bf16", seed=77)
     dO = inputs.make_output_grad(B, T, d, seed=77, dtype="bf16")
     a = _backward(inp, dO, B, T, d, e, s, C, causal, "bf16", fill=0)
