@@ -563,7 +563,7 @@ def summarize_backward_trace(trace_csv, command, out):
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     names = [_short(r["Kernel_Name"]) for r in rows]
     starts = [i for i, n in enumerate(names) if n.startswith("proj_kernel")]
-    a, b = starts[-2] - 1, starts[-1] - 1   # each call begins with the fill before the projection
+    a, b = starts[-2], starts[-1]   # each call begins with the recompute's projection
     dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
     total = sum(dur(rows[i]) for i in range(a, b))
     wall = (int(rows[b - 1]["End_Timestamp"]) - int(rows[a]["Start_Timestamp"])) / 1e3
