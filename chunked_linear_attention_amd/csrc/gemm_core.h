@@ -8,8 +8,9 @@
 //    v_mfma_f32_32x32x2_f32 per 16-byte fragment), fp32 accumulation.  Each of
 //    the WGM x WGN waves owns a (BM/WGM) x (BN/WGN) sub-tile.
 //  * K advances in chunks of 128 bytes (64 bf16 / 32 fp32).  Global memory is
-//    copied straight into LDS with global_load_lds_dwordx4 (no VGPR staging),
-//    through a ring of NS stages (NS = 2 for the large tiles, more for small
+//    copied straight into LDS (no VGPR staging: buffer_load_dwordx4 ... lds
+//    for bf16 K-major operands, global_load_lds_dwordx4 otherwise; see
+//    DmaOperand), through a ring of NS stages (NS = 2 for the large tiles, more for small
 //    tiles whose blocks would otherwise wait on one copy at a time): the
 //    copies of the next NS-1 chunks are in flight while one chunk is
 //    multiplied, and one barrier per chunk separates them.
