@@ -324,3 +324,36 @@ def test_many_sequences_checked_on_first_and_last_rows():
     for b in (0, B - 1):
         ref = oracle_layer(dict(inp, X=inp["X"][b:b + 1]), C, True)
         assert_close(O[b:b + 1], ref, 2e-2, f"row {b} of B=64")
+
+
+def _random_configs(n, seed):
+    """n layer configurations drawn from the ABI's valid ranges (sizes kept
+    small enough for the oracle): batch, chunk, chunks per sequence, widths,
+    storage type, mask, RoPE, ablation and head parameters all vary."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(n):
+        C = int(rng.choice([64, 128, 256, 512]))
+        G = int(rng.integers(1, 5 if C <= 128 else 3))
+        out.append(dict(B=int(rng.integers(1, 4)), T=C * G, d=128 * int(rng.integers(1, 5)),
+                        e=256 * int(rng.integers(1, 9)), s=int(rng.choice([128, 256])), C=C,
+                        dtype=str(rng.choice(["f32", "bf16"])), causal=bool(rng.integers(0, 2)),
+                        rope=bool(rng.integers(0, 2)), parts=str(rng.choice(["both", "local", "global"])),
+                        heads=str(rng.choice(["workload", "wide"]))))
+    return out
+
+
+RANDOM = _random_configs(16, seed=4242)
+
+
+@pytest.mark.parametrize("k", range(len(RANDOM)), ids=lambda k: "B{B}_T{T}_d{d}_e{e}_s{s}_C{C}_{dtype}_{causal}_"
+                         "rope{rope}_{parts}_{heads}".format(**RANDOM[k]))
+def test_random_configurations_match_oracle(k):
+    """Seeded random configurations across every option the layer has,
+    output against the oracle under the storage type's gate."""
+    c = RANDOM[k]
+    B, T, d, e, s, C, dtype, causal = (c[x] for x in ("B", "T", "d", "e", "s", "C", "dtype", "causal"))
+    inp = make(B, T, d, e, s, C, dtype, seed=9000 + k, heads=c["heads"])
+    O, _, _, _ = run_layer(inp, B, T, d, e, s, C, causal, dtype, rope=c["rope"], parts=c["parts"])
+    ref = oracle_layer(inp, C, causal, rope=c["rope"], parts=c["parts"])
+    assert_close(O, ref, tol_for(dtype), "O")
