@@ -221,3 +221,33 @@ def test_backward_without_tokens_zeroes_the_parameter_gradients():
     torch.cuda.synchronize()
     for k in g.GRAD_NAMES[1:]:
         assert torch.count_nonzero(grads[k]).item() == 0, k
+
+
+def _random_backward_configs(n, seed):
+    """n configurations drawn from the valid ranges (sizes kept small enough
+    for the oracle's chain rule): every option of the layer varies."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(n):
+        C = int(rng.choice([64, 128, 256]))
+        out.append(dict(B=int(rng.integers(1, 3)), T=C * int(rng.integers(1, 4)), d=128 * int(rng.integers(1, 3)),
+                        e=256 * int(rng.integers(1, 7)), s=int(rng.choice([128, 256])), C=C,
+                        dtype=str(rng.choice(["f32", "bf16"])), causal=bool(rng.integers(0, 2)),
+                        rope=bool(rng.integers(0, 2)), parts=str(rng.choice(["both", "local", "global"])),
+                        heads=str(rng.choice(["workload", "wide"]))))
+    return out
+
+
+RANDOM = _random_backward_configs(10, seed=5151)
+
+
+@pytest.mark.parametrize("k", range(len(RANDOM)), ids=lambda k: "B{B}_T{T}_d{d}_e{e}_s{s}_C{C}_{dtype}_{causal}_"
+                         "rope{rope}_{parts}_{heads}".format(**RANDOM[k]))
+def test_random_configurations_backward_matches_oracle(k):
+    """Seeded random configurations: every gradient against the oracle's."""
+    c = RANDOM[k]
+    B, T, d, e, s, C, dtype, causal = (c[x] for x in ("B", "T", "d", "e", "s", "C", "dtype", "causal"))
+    inp = make(B, T, d, e, s, C, dtype, seed=9500 + k, heads=c["heads"])
+    dO = inputs.make_output_grad(B, T, d, seed=9500 + k, dtype=dtype)
+    got = _backward(inp, dO, B, T, d, e, s, C, causal, dtype, rope=c["rope"], parts=c["parts"])
+    _compare(got, _oracle(inp, dO, C, causal, rope=c["rope"], parts=c["parts"]), dtype)
