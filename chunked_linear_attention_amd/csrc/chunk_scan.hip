@@ -103,19 +103,19 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanParams p) {
     } else if (p.causal) {
         char* out = P + ((size_t)b * p.G * stride + (size_t)v * 4) * EB;
         int g = 0;
-        for (; g + 4 <= p.G; g += 4) {
-            const f32x4_t s0 = get4<T>(S + (size_t)(g + 0) * cstride);
-            const f32x4_t s1 = get4<T>(S + (size_t)(g + 1) * cstride);
-            const f32x4_t s2 = get4<T>(S + (size_t)(g + 2) * cstride);
-            const f32x4_t s3 = get4<T>(S + (size_t)(g + 3) * cstride);
-            put4<T>(out + (size_t)(g + 0) * cstride, run);
-            run += s0;
-            put4<T>(out + (size_t)(g + 1) * cstride, run);
-            run += s1;
-            put4<T>(out + (size_t)(g + 2) * cstride, run);
-            run += s2;
-            put4<T>(out + (size_t)(g + 3) * cstride, run);
-            run += s3;
+        // U chunks' loads in flight at once (a long sequence has few lanes
+        // per chunk step and many steps: its loads must overlap), then their
+        // stores and sums in chunk order
+        constexpr int U = 16;
+        for (; g + U <= p.G; g += U) {
+            f32x4_t sv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) sv[u] = get4<T>(S + (size_t)(g + u) * cstride);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                put4<T>(out + (size_t)(g + u) * cstride, run);
+                run += sv[u];
+            }
         }
         for (; g < p.G; ++g) {
             const f32x4_t s0 = get4<T>(S + (size_t)g * cstride);

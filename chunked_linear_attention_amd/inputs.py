@@ -43,6 +43,12 @@ WORKLOADS = {
                                           dtype="bf16", causal=True, seed=1003),
     "layer_bf16_B2_T8192_d768_C256_rope": dict(B=2, T=8192, d=768, e=1536, s=128, C=256,
                                                dtype="bf16", causal=True, seed=1003, rope=True),
+    # the same number of tokens as one long sequence and as many short ones
+    # (cost linear in T: the two take the same time per token)
+    "layer_bf16_B1_T131072_d768_C256": dict(B=1, T=131072, d=768, e=1536, s=128, C=256,
+                                            dtype="bf16", causal=True, seed=1004),
+    "layer_bf16_B16_T8192_d768_C256": dict(B=16, T=8192, d=768, e=1536, s=128, C=256,
+                                           dtype="bf16", causal=True, seed=1004),
     "stack24_bf16_B2_T8192_d1024_C256": dict(B=2, T=8192, d=1024, e=2048, s=128, C=256,
                                              dtype="bf16", causal=True, layers=24,
                                              weight_seed=2000, x_seed=2100),
