@@ -494,7 +494,7 @@ def summarize_decode_trace(trace_csv, command, out, steps=256, warmup=20):
     kernels = ["decode_proj", "decode_attn", "decode_out", "decode_state"]
     lines = ["# rocprofv3 kernel trace: incremental decoding, d=768 e=1536 s=128 C=256, bf16", "",
              "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
-             "Average duration per launch (us) by batch size B (from B = 3 the projection and output "
+             "Average duration per launch (us) by batch size B (from B = 9 the projection and output "
              "products are the `_mfma` kernels); decode_state runs once per chunk "
              f"({steps} steps per batch size, {warmup} warm-up steps before them).", "",
              "| B | " + " | ".join(f"`{k}`" for k in kernels) + " |",

@@ -16,7 +16,7 @@
 //
 // Three launches per step (a fourth at a chunk's end).  Up to MFMA_MIN_B - 1
 // tokens the projection and output products are GEMVs that read every
-// weight once per tile of 8 tokens (one half wave per weight row); from
+// weight once (one half wave per weight row, 16-byte loads); from
 // MFMA_MIN_B on they run on the shared MFMA core as GEMMs with 64-token
 // tiles.  The attention kernel reads the chunk's cached rows and P in the
 // layer's element type: the fp32 state is rounded into that copy once per
@@ -31,22 +31,7 @@ namespace gau {
 namespace {
 
 constexpr int BT = 8;           // tokens per pass over a weight row (GEMV)
-constexpr int MFMA_MIN_B = 3;   // batch from which the products use the MFMA core (measured)
-
-template <typename T>
-__device__ __forceinline__ void ld2(const char* p, float& a, float& b);
-template <>
-__device__ __forceinline__ void ld2<bf16>(const char* p, float& a, float& b) {
-    const uint32_t w = *(const uint32_t*)p;
-    a = __uint_as_float(w << 16);
-    b = __uint_as_float(w & 0xFFFF0000u);
-}
-template <>
-__device__ __forceinline__ void ld2<float>(const char* p, float& a, float& b) {
-    const u32x2_t v = *(const u32x2_t*)p;
-    a = __uint_as_float(v.x);
-    b = __uint_as_float(v.y);
-}
+constexpr int MFMA_MIN_B = 9;   // batch from which the products use the MFMA core (measured)
 
 template <typename T>
 __device__ __forceinline__ float ld1(const char* p);
@@ -96,15 +81,6 @@ __device__ __forceinline__ void st8<float>(char* p, const float (&v)[8]) {
     *(f32x4_t*)(p + 16) = f32x4_t{v[4], v[5], v[6], v[7]};
 }
 
-// Four consecutive elements as floats.
-template <typename T>
-__device__ __forceinline__ void ld4(const char* p, float (&v)[4]) {
-    float a, b, c, d;
-    ld2<T>(p, a, b);
-    ld2<T>(p + 2 * Elem<T>::kBytes, c, d);
-    v[0] = a, v[1] = b, v[2] = c, v[3] = d;
-}
-
 // Sum over the 32 lanes of a half wave.
 __device__ __forceinline__ float half_sum(float v) {
 #pragma unroll
@@ -114,40 +90,59 @@ __device__ __forceinline__ float half_sum(float v) {
 
 constexpr int RL = 32;  // lanes per weight row
 
-// acc[bb] = row . x[b0 + bb] for the tokens of one tile.  row: K elements of
-// type WT; x: B rows of K elements of type XT.  The row is read in 4-element
-// groups strided over the RL lanes of its half wave (up to 8 groups per lane
-// in flight), each multiplied with the same group of every token's x.
-template <typename WT, typename XT>
+// The elements of one 16-byte vector as floats (8 for bf16, 4 for fp32).
+template <typename T>
+__device__ __forceinline__ void unpack16(const u32x4_t& w, float (&v)[16 / Elem<T>::kBytes]) {
+    if constexpr (Elem<T>::kBytes == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = __uint_as_float(w[k]);
+    }
+}
+
+// acc[bb] = row . x[b0 + bb] for the tokens of one tile.  row: K elements,
+// x: B rows of K elements, both of type T, 16-byte aligned (K is a multiple
+// of 64).  The row is read in 16-byte vectors strided over the RL lanes of
+// its half wave, up to U vectors per lane in flight (one pass for K <= 2048
+// in bf16), each multiplied with the same vector of every token's x.
+template <typename T>
 __device__ __forceinline__ void row_dots(const char* row, const char* x, int K, int B, int b0, int rl,
                                          float (&acc)[BT]) {
-    constexpr int WB = Elem<WT>::kBytes, XB = Elem<XT>::kBytes;
+    constexpr int EB = Elem<T>::kBytes, VE = 16 / EB;
     constexpr int U = 8;
 #pragma unroll
     for (int bb = 0; bb < BT; ++bb) acc[bb] = 0.f;
-    const int groups = K / 4;
-    for (int g0 = rl; g0 < groups; g0 += RL * U) {
-        float w[U][4];
+    const int nv = K / VE;
+    for (int v0 = rl; v0 < nv; v0 += RL * U) {
+        u32x4_t w[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int gi = g0 + u * RL;
-            if (gi < groups) {
-                ld4<WT>(row + (size_t)gi * 4 * WB, w[u]);
-            } else {
-                w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0.f;
-            }
+            const int vi = v0 + u * RL;
+            w[u] = vi < nv ? *(const u32x4_t*)(row + (size_t)vi * 16) : u32x4_t{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int bb = 0; bb < BT; ++bb) {
             if (b0 + bb >= B) break;
-            const char* xb = x + (size_t)(b0 + bb) * K * XB;
+            const char* xb = x + (size_t)(b0 + bb) * K * EB;
+            u32x4_t xv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int gi = g0 + u * RL;
-                if (gi < groups) {
-                    float xv[4];
-                    ld4<XT>(xb + (size_t)gi * 4 * XB, xv);
-                    acc[bb] += w[u][0] * xv[0] + w[u][1] * xv[1] + w[u][2] * xv[2] + w[u][3] * xv[3];
+                const int vi = v0 + u * RL;
+                xv[u] = vi < nv ? *(const u32x4_t*)(xb + (size_t)vi * 16) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (v0 + u * RL < nv) {
+                    float a[VE], c[VE];
+                    unpack16<T>(w[u], a);
+                    unpack16<T>(xv[u], c);
+#pragma unroll
+                    for (int k = 0; k < VE; ++k) acc[bb] += a[k] * c[k];
                 }
             }
         }
@@ -170,7 +165,7 @@ __global__ __launch_bounds__(256) void decode_proj_kernel(DecodeParams p) {
                                     : (const char*)p.W_z + (size_t)(f - 2 * p.e) * pitch;
     for (int b0 = 0; b0 < p.B; b0 += BT) {
         float acc[BT];
-        row_dots<T, T>(row, (const char*)p.x, p.d, p.B, b0, lane, acc);
+        row_dots<T>(row, (const char*)p.x, p.d, p.B, b0, lane, acc);
         if (lane != 0) continue;
 #pragma unroll
         for (int bb = 0; bb < BT; ++bb) {
@@ -372,7 +367,7 @@ __global__ __launch_bounds__(256) void decode_out_kernel(DecodeParams p) {
     const char* row = (const char*)p.W_o + (size_t)n * p.e * EB;
     for (int b0 = 0; b0 < p.B; b0 += BT) {
         float acc[BT];
-        row_dots<T, T>(row, (const char*)p.y, p.e, p.B, b0, lane, acc);
+        row_dots<T>(row, (const char*)p.y, p.e, p.B, b0, lane, acc);
         if (lane != 0) continue;
 #pragma unroll
         for (int bb = 0; bb < BT; ++bb) {

@@ -213,7 +213,7 @@ def test_emulated_segmented_layer_matches_oracle(emu, case):
                                            ("f32", 2, "wide"), ("bf16", 18, "wide")])
 def test_emulated_decoding_matches_the_causal_layer(emu, dtype, B, heads):
     """gau_decode_step on the emulation for 66 tokens (one chunk end, C = 64)
-    against the oracle's causal layer; B = 18 takes the MFMA products (from B = 3 on);
+    against the oracle's causal layer; B = 18 takes the MFMA products (from B = 9 on);
     "wide": gamma ~ N(1, 0.5^2), beta ~ N(0, 0.3^2)."""
     T, d, e, s, C = 128, 128, 256, 128, 64
     steps = 66

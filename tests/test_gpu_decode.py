@@ -42,8 +42,9 @@ CASES = [
     (2, 384, 256, 512, 128, 128, "bf16", 384, False),
     (1, 256, 128, 1024, 256, 128, "bf16", 256, True),  # s = 256, RoPE
     (3, 192, 128, 256, 128, 64, "bf16", 130, False),   # stop inside a chunk
-    (9, 128, 128, 256, 128, 64, "f32", 128, True),     # B > 8: two token tiles per weight row
-    (20, 128, 128, 256, 128, 64, "bf16", 128, False),  # B >= 3: the products on the MFMA core
+    (8, 128, 128, 256, 128, 64, "f32", 128, True),     # the largest batch of the GEMV products
+    (9, 128, 128, 256, 128, 64, "f32", 128, True),     # B >= 9: the products on the MFMA core
+    (20, 128, 128, 256, 128, 64, "bf16", 128, False),
     (70, 128, 256, 512, 256, 64, "f32", 70, True),     # ... two token tiles, the second ragged
     (96, 128, 128, 1536, 128, 64, "f32", 128, False),   # attention with 8 features per thread
     (176, 128, 128, 1536, 128, 64, "bf16", 128, True),  # ... bf16 (16-byte loads), RoPE
