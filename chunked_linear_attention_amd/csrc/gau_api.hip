@@ -45,6 +45,12 @@ gau_status check_config(const gau_config* c) {
     // the chunk scan's grid: one lane per four of the B * e * s state
     // entries, fewer than 2^31 lanes
     if (c->B * c->e * c->s >= ((int64_t)1 << 33)) return GAU_ERR_SHAPE;
+    // bf16: the MFMA core copies K-major operand tiles through buffer
+    // resources with 32-bit signed row offsets (up to 255 rows of the
+    // operand's pitch); the token-major operands (V and K_lin transposed per
+    // sequence) have a pitch of T elements, so 255 * 2 T bytes must stay
+    // below 2^31
+    if (c->dtype == GAU_BF16 && c->T > ((int64_t)1 << 22)) return GAU_ERR_SHAPE;
     return GAU_OK;
 }
 

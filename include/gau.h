@@ -83,7 +83,9 @@ typedef enum {
  *   the sequence into whole chunks, wikillm "Method", papercache 3.2);
  *   C in {64, 128, 256, 512}; d % 128 == 0; e % 256 == 0; s in {128, 256};
  *   B*T <= 2^30, d, e <= 65536, B*T*max(d, e) <= 2^40 and B*e*s < 2^33 (the
- *   kernels' grids and index arithmetic).  Otherwise GAU_ERR_SHAPE.
+ *   kernels' grids and index arithmetic); in bf16 also T <= 2^22 (32-bit
+ *   offsets of the operand tiles the matrix cores copy, whose rows are
+ *   T-element token runs).  Otherwise GAU_ERR_SHAPE.
  */
 typedef struct {
     int64_t B, T, d, e, s, C;

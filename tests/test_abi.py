@@ -199,6 +199,20 @@ def test_stack_argument_checks():
     assert lib.gau_stack_forward(ctypes.byref(cfg), 0, None, *[pp] * 7, None, 0, None) == 0
 
 
+def test_longest_bf16_sequence():
+    """bf16 takes T up to 2^22 tokens per sequence (the matrix cores' 32-bit
+    tile offsets over T-element rows); fp32, copied with 64-bit addresses,
+    takes longer ones."""
+    ok = _cfg(B=1, T=1 << 22, C=256, d=128, e=256, s=128)
+    assert g.workspace_bytes(ok) > 0
+    bad = _cfg(B=1, T=(1 << 22) + 256, C=256, d=128, e=256, s=128)
+    assert g.workspace_bytes(bad) == 0
+    with pytest.raises(g.GauError) as ei:
+        g.workspace_layout(bad)
+    assert ei.value.status == 2
+    assert g.workspace_bytes(_cfg(B=1, T=(1 << 22) + 256, C=256, d=128, e=256, s=128, dtype=g.GAU_F32)) > 0
+
+
 def test_largest_scan_grid_accepted():
     """Just under the bound: B * e * s = 2^33 - 2^22 (the scan's lanes stay
     below 2^31) is a valid shape."""
