@@ -268,9 +268,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
     }
     __syncthreads();
     // scores of the chunk's slots 0 .. j (slot j from this block's own K_quad):
-    // one thread per slot, its K_quad row read as 16-byte vectors all in flight
+    // one thread per slot, its K_quad row read as 16-byte vectors all in
+    // flight, each batch's query values read from LDS as 16-byte vectors
+    // before its products (one wait per batch instead of one per vector)
     for (int tau = tid; tau <= (p.local ? j : -1); tau += 256) {
         float acc = 0.f;
+        const float rpos = p.relpos[p.C - 1 + tau - j];
         if (tau == j) {
             for (int i = 0; i < p.s; ++i) acc += qq[i] * kq[i];
         } else {
@@ -280,23 +283,29 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeParams p) {
                 u32x4_t w[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) w[u] = *(const u32x4_t*)(k + (size_t)(i0 + u * VE) * EB);
+                float qv[8 * VE];
+#pragma unroll
+                for (int x = 0; x < 2 * VE; ++x) {
+                    const f32x4_t q4 = *(const f32x4_t*)(qq + i0 + 4 * x);
+                    qv[4 * x] = q4.x, qv[4 * x + 1] = q4.y, qv[4 * x + 2] = q4.z, qv[4 * x + 3] = q4.w;
+                }
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const int i = i0 + u * VE;
+                    const int i = u * VE;
                     if constexpr (EB == 2) {
                         const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            acc += qq[i + 2 * q] * __uint_as_float(ww[q] << 16) +
-                                   qq[i + 2 * q + 1] * __uint_as_float(ww[q] & 0xFFFF0000u);
+                            acc += qv[i + 2 * q] * __uint_as_float(ww[q] << 16) +
+                                   qv[i + 2 * q + 1] * __uint_as_float(ww[q] & 0xFFFF0000u);
                     } else {
-                        acc += qq[i] * __uint_as_float(w[u].x) + qq[i + 1] * __uint_as_float(w[u].y) +
-                               qq[i + 2] * __uint_as_float(w[u].z) + qq[i + 3] * __uint_as_float(w[u].w);
+                        acc += qv[i] * __uint_as_float(w[u].x) + qv[i + 1] * __uint_as_float(w[u].y) +
+                               qv[i + 2] * __uint_as_float(w[u].z) + qv[i + 3] * __uint_as_float(w[u].w);
                     }
                 }
             }
         }
-        const float x = acc * p.qs + p.relpos[p.C - 1 + tau - j];
+        const float x = acc * p.qs + rpos;
         alpha[tau] = x > 0.f ? x * x : 0.f;
     }
     __syncthreads();
