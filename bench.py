@@ -674,7 +674,7 @@ def main():
         summarize_counters(args.summarize_counters, args.stats, args.command, args.out)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
