@@ -315,6 +315,57 @@ def test_long_sequence():
     assert ce.max() <= 2e-2, f"chunk {int(ce.argmax())}: {ce.max():.3e}"
 
 
+def test_longest_bf16_sequence():
+    """T = 2^22 tokens, the longest sequence bf16 takes (the matrix cores'
+    buffer copies address up to 255 rows of T-element token runs with 32-bit
+    offsets: 255 * 2^23 bytes at the farthest).  No oracle pass over 4M tokens;
+    instead properties that hold at any length, compared bitwise between GPU
+    runs: LocalOnly, a chunk's output depends on its own tokens only, so the
+    first and last chunks equal forwards of those chunks alone; the full
+    layer's first two chunks equal a forward of those two chunks (causality).
+    The short forwards are checked against the oracle, and every output of the
+    long ones is finite."""
+    B, T, d, e, s, C = 1, 1 << 22, 128, 256, 128, 256
+    inp = make(B, C, d, e, s, C, "bf16", seed=91)  # the weights (and one chunk of X, unused)
+    dev = g.device_layer(inp, torch.bfloat16)
+    W = [dev[k] for k in ("W_u", "W_v", "W_z", "W_o", "scale", "offset", "relpos")]
+    # X ~ N(0, 1) drawn on the device (seeded; 2^29 draws take minutes on the
+    # host), rounded to bf16 to nearest even; the oracle takes the same values
+    gen = torch.Generator(device="cuda").manual_seed(91)
+    X = torch.randn((B, T, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    def forward(t0, n, parts):
+        cfg = g.make_config(B, n, d, e, s, C, True, g.GAU_BF16, parts=parts)
+        ws = torch.empty(g.workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+        O = torch.empty((B, n, d), dtype=torch.bfloat16, device="cuda")
+        g.forward(cfg, X[:, t0:t0 + n].contiguous(), *W, O, ws)
+        torch.cuda.synchronize()
+        del ws
+        return O
+
+    def short_ref(t0, n, parts):
+        one = dict(inp, X=X[:, t0:t0 + n].float().cpu().numpy().astype(np.float64))
+        return oracle_layer(one, C, True, parts=parts)
+
+    print("T=2^22 LocalOnly: GPU run", flush=True)
+    O = forward(0, T, "local")
+    assert bool(torch.isfinite(O).all())
+    for t0 in (0, T - C):
+        Oc = forward(t0, C, "local")
+        assert torch.equal(O[:, t0:t0 + C], Oc), f"LocalOnly chunk at {t0}"
+        assert_close(Oc.float().cpu().numpy().astype(np.float64), short_ref(t0, C, "local"), 2e-2,
+                     f"LocalOnly chunk at {t0}")
+    del O
+    torch.cuda.empty_cache()
+    print("T=2^22 full layer: GPU run", flush=True)
+    O = forward(0, T, "both")
+    assert bool(torch.isfinite(O).all())
+    O2 = forward(0, 2 * C, "both")
+    assert torch.equal(O[:, :2 * C], O2), "the first two chunks"
+    assert_close(O2.float().cpu().numpy().astype(np.float64), short_ref(0, 2 * C, "both"), 2e-2,
+                 "the first two chunks")
+
+
 def test_many_sequences_checked_on_first_and_last_rows():
     """B=64, T=1024: 65536 tokens in 64 independent rows; rows 0 and 63
     against the oracle."""
