@@ -120,6 +120,17 @@ def make_layer_inputs(B, T, d, e, s, C, seed, dtype="bf16", heads="workload", **
     return out
 
 
+def device_normal_bf16(shape, seed):
+    """X ~ N(0, 1) of `shape` drawn on the GPU by torch's seeded generator and
+    rounded to bf16 (to nearest even), for sequences too long to draw on the
+    host in a test's time (2^29 host draws take minutes).  Callers that check
+    against the oracle hand it these same values."""
+    import torch
+
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    return torch.randn(tuple(shape), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
 def make_output_grad(B, T, d, seed, dtype="bf16"):
     """A seeded upstream gradient dL/dO [B, T, d] (standard normal, bf16-exact
     for dtype "bf16"), float32."""

@@ -329,10 +329,8 @@ def test_longest_bf16_sequence():
     inp = make(B, C, d, e, s, C, "bf16", seed=91)  # the weights (and one chunk of X, unused)
     dev = g.device_layer(inp, torch.bfloat16)
     W = [dev[k] for k in ("W_u", "W_v", "W_z", "W_o", "scale", "offset", "relpos")]
-    # X ~ N(0, 1) drawn on the device (seeded; 2^29 draws take minutes on the
-    # host), rounded to bf16 to nearest even; the oracle takes the same values
-    gen = torch.Generator(device="cuda").manual_seed(91)
-    X = torch.randn((B, T, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    # X ~ N(0, 1) drawn on the device; the oracle takes the same values
+    X = inputs.device_normal_bf16((B, T, d), seed=91)
 
     def forward(t0, n, parts):
         cfg = g.make_config(B, n, d, e, s, C, True, g.GAU_BF16, parts=parts)
